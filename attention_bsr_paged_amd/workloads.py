@@ -1,0 +1,281 @@
+"""Seeded synthetic inputs for paged block-sparse-row (BSR) attention.
+
+This module draws request lengths, page pools and N(0, 1) values and rounds them
+to the storage type. It holds none of the attention arithmetic. Both the HIP
+path (through the binding) and the fp64 oracle are fed from here; neither of
+those imports the other.
+
+Storage convention: every fp16 / bf16 tensor is a numpy ``uint16`` array of bit
+patterns. ``to_torch`` reinterprets it as the matching torch dtype.
+
+The KV cache of a batch is a block-sparse-row matrix (FlashInfer paper summary,
+"图谱动态｜学苑周刊 NO.266", section 统一的 KV 缓存存储格式): request b owns
+pages ``kv_indices[kv_indptr[b]:kv_indptr[b+1]]`` in logical order, each page
+holds ``page_size`` token slots, and only the first ``kv_last_page_len[b]``
+slots of its last page are valid. K and V are separate pools of shape
+``[num_pages, page_size, num_kv_heads, head_dim]`` (NHD inside a page).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional
+
+import numpy as np
+
+BF16 = "bf16"
+FP16 = "fp16"
+
+
+# ----------------------------------------------------------------------------
+# rounding fp32 -> storage bits (input generation only)
+# ----------------------------------------------------------------------------
+def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (round to nearest, ties to even).
+
+    Finite inputs only (the generators draw N(0, 1)).
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = (u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def round_to_fp16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to IEEE binary16 (numpy rounds to nearest even)."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def round_bits(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == BF16:
+        return round_to_bf16_bits(x)
+    if dtype == FP16:
+        return round_to_fp16_bits(x)
+    raise ValueError(f"unknown storage dtype {dtype!r}")
+
+
+def normal_bits(rng: np.random.Generator, shape, dtype: str, chunk: int = 1 << 24) -> np.ndarray:
+    """N(0, 1) draws in float32, rounded to ``dtype``; generated in chunks to bound memory."""
+    n = int(np.prod(shape)) if len(shape) else 1
+    out = np.empty(n, dtype=np.uint16)
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        out[s:e] = round_bits(rng.standard_normal(e - s, dtype=np.float32), dtype)
+    return out.reshape(shape)
+
+
+def to_torch(bits: np.ndarray, dtype: str, device=None):
+    """Reinterpret uint16 storage bits as a torch fp16 / bf16 tensor."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    t = t.view(torch.bfloat16 if dtype == BF16 else torch.float16)
+    return t.to(device) if device is not None else t
+
+
+# ----------------------------------------------------------------------------
+# paged KV cache
+# ----------------------------------------------------------------------------
+@dataclass
+class PagedKV:
+    """One BSR-paged KV cache (a batch of requests sharing one page pool)."""
+
+    page_size: int
+    num_kv_heads: int
+    head_dim: int
+    dtype: str
+    kv_len: np.ndarray            # int64 [B], the drawn lengths
+    kv_indptr: np.ndarray         # int32 [B+1]
+    kv_indices: np.ndarray        # int32 [nnz_pages]
+    kv_last_page_len: np.ndarray  # int32 [B]
+    k_pages: np.ndarray           # uint16 [num_pages, P, Hkv, d]
+    v_pages: np.ndarray           # uint16 [num_pages, P, Hkv, d]
+
+    @property
+    def batch(self) -> int:
+        return int(self.kv_len.shape[0])
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.k_pages.shape[0])
+
+
+def page_table(kv_len: np.ndarray, page_size: int, pool: np.ndarray):
+    """indptr / indices / last_page_len for lengths ``kv_len``.
+
+    Pages are handed out to the requests in order from ``pool`` (drawing without
+    replacement when ``pool`` is a shuffled permutation). A request with no
+    tokens owns no page; its last_page_len is 0 (never read).
+    """
+    kv_len = np.asarray(kv_len, dtype=np.int64)
+    npages = (kv_len + page_size - 1) // page_size
+    indptr = np.zeros(len(kv_len) + 1, dtype=np.int64)
+    indptr[1:] = np.cumsum(npages)
+    if indptr[-1] > len(pool):
+        raise ValueError("page pool too small")
+    indices = np.asarray(pool[: indptr[-1]], dtype=np.int32)
+    lpl = np.where(npages > 0, kv_len - (npages - 1) * page_size, 0)
+    return indptr.astype(np.int32), indices, lpl.astype(np.int32)
+
+
+def make_paged_kv(rng: np.random.Generator, kv_len, page_size: int, num_kv_heads: int,
+                  head_dim: int, dtype: str, extra_pages: int = 0, shuffle: bool = True) -> PagedKV:
+    """Draw a paged KV cache holding ``kv_len[b]`` tokens for each request.
+
+    The pool holds exactly the pages needed (plus ``extra_pages`` unused ones),
+    shuffled with ``rng.permutation`` so logical and physical order differ.
+    """
+    kv_len = np.asarray(kv_len, dtype=np.int64)
+    need = int(((kv_len + page_size - 1) // page_size).sum())
+    num_pages = need + int(extra_pages)
+    pool = rng.permutation(num_pages) if shuffle else np.arange(num_pages)
+    indptr, indices, lpl = page_table(kv_len, page_size, pool)
+    shape = (num_pages, page_size, num_kv_heads, head_dim)
+    k = normal_bits(rng, shape, dtype)
+    v = normal_bits(rng, shape, dtype)
+    return PagedKV(page_size, num_kv_heads, head_dim, dtype, kv_len, indptr, indices, lpl, k, v)
+
+
+# ----------------------------------------------------------------------------
+# the five named workloads
+# ----------------------------------------------------------------------------
+@dataclass
+class Workload:
+    name: str
+    kind: str                      # "decode" | "append" | "cascade"
+    seed: int
+    dtype: str
+    num_qo_heads: int
+    num_kv_heads: int
+    head_dim: int
+    kv: PagedKV                    # the (suffix) KV cache
+    q: np.ndarray                  # uint16 [B, Hq, d] (decode) or [sum qo, Hq, d] (append)
+    qo_indptr: Optional[np.ndarray] = None   # int32 [B+1], append only
+    causal: bool = False
+    rope_theta: float = 0.0        # 0 -> no RoPE
+    q_pos: Optional[np.ndarray] = None       # int32, per query token
+    kv_pos_offset: Optional[np.ndarray] = None  # int32 [B]
+    prefix: Optional[PagedKV] = None         # cascade: the shared prefix (one "request")
+    meta: Dict[str, object] = field(default_factory=dict)
+
+    @property
+    def batch(self) -> int:
+        return self.kv.batch
+
+    @property
+    def sm_scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.head_dim))
+
+
+def single_decode_mha(seed: int = 1001) -> Workload:
+    """Single-request decode: 32 qo = 32 kv heads, d 128, fp16, kv_len 2048 in 128
+    pages of 16 in random physical order."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    Hq = Hkv = 32
+    d, P, L = 128, 16, 2048
+    kv_len = np.array([L])
+    pool = rng.permutation(L // P)
+    indptr, indices, lpl = page_table(kv_len, P, pool)
+    q = normal_bits(rng, (1, Hq, d), FP16)
+    k = normal_bits(rng, (L // P, P, Hkv, d), FP16)
+    v = normal_bits(rng, (L // P, P, Hkv, d), FP16)
+    kv = PagedKV(P, Hkv, d, FP16, kv_len, indptr, indices, lpl, k, v)
+    return Workload("single_decode_mha32_d128_fp16_kv2048_p16", "decode", seed, FP16, Hq, Hkv, d, kv, q)
+
+
+def batch_decode_gqa(seed: int = 1002, batch: int = 64, lo: int = 512, hi: int = 4096) -> Workload:
+    """Batch paged decode: 64 requests, GQA 32/8, d 128, page 16, bf16,
+    kv_len uniform on the integers [512, 4096]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    Hq, Hkv, d, P = 32, 8, 128, 16
+    kv_len = rng.integers(lo, hi, size=batch, endpoint=True)
+    q = normal_bits(rng, (batch, Hq, d), BF16)
+    kv = make_paged_kv(rng, kv_len, P, Hkv, d, BF16)
+    return Workload(f"batch_decode_b{batch}_gqa32x8_d128_bf16_p16_kv{lo}-{hi}", "decode", seed,
+                    BF16, Hq, Hkv, d, kv, q)
+
+
+def skewed_decode_gqa(seed: int = 1003, batch: int = 128) -> Workload:
+    """Skewed-length decode: 128 requests, GQA 32/8, d 128, page 16, bf16; one
+    request of 32768 tokens, the rest lognormal(ln 512, 1) rounded and clipped
+    to [16, 16384]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    Hq, Hkv, d, P = 32, 8, 128, 16
+    rest = np.clip(np.rint(np.exp(rng.normal(np.log(512.0), 1.0, size=batch - 1))), 16, 16384)
+    kv_len = np.concatenate([[32768], rest]).astype(np.int64)
+    q = normal_bits(rng, (batch, Hq, d), BF16)
+    kv = make_paged_kv(rng, kv_len, P, Hkv, d, BF16)
+    return Workload(f"skewed_decode_b{batch}_gqa32x8_d128_bf16_p16_long32768", "decode", seed,
+                    BF16, Hq, Hkv, d, kv, q)
+
+
+def ragged_append_causal(seed: int = 1004, batch: int = 16) -> Workload:
+    """Ragged causal append: 16 requests each appending qo_len ~ U{128..1024} new
+    tokens onto an existing kv_len ~ U{1024..8192}; the page table holds
+    existing + qo_len tokens (the new K/V are already cached); GQA 32/8, d 128,
+    page 16, bf16."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    Hq, Hkv, d, P = 32, 8, 128, 16
+    qo_len = rng.integers(128, 1024, size=batch, endpoint=True)
+    existing = rng.integers(1024, 8192, size=batch, endpoint=True)
+    kv_len = existing + qo_len
+    qo_indptr = np.zeros(batch + 1, dtype=np.int32)
+    qo_indptr[1:] = np.cumsum(qo_len)
+    q = normal_bits(rng, (int(qo_indptr[-1]), Hq, d), BF16)
+    kv = make_paged_kv(rng, kv_len, P, Hkv, d, BF16)
+    w = Workload(f"ragged_append_causal_{batch}req_gqa32x8_d128_bf16_p16", "append", seed, BF16,
+                 Hq, Hkv, d, kv, q, qo_indptr=qo_indptr, causal=True)
+    w.meta["existing"] = existing
+    return w
+
+
+def cascade_rope(seed: int = 1005, batch: int = 64, prefix_len: int = 8192) -> Workload:
+    """Cascade (composable formats) decode with fused RoPE: 64 decode requests
+    sharing one 8192-token prefix stored in pages of 256, plus unique suffixes of
+    U{256..1024} tokens in pages of 16; GQA 32/8, d 128, bf16; LLaMA RoPE with
+    theta 500000 on q and k from per-token positions (prefix token t at t,
+    suffix token t at prefix_len + t, the query at the last suffix position)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    Hq, Hkv, d = 32, 8, 128
+    prefix = make_paged_kv(rng, np.array([prefix_len]), 256, Hkv, d, BF16)
+    suffix_len = rng.integers(256, 1024, size=batch, endpoint=True)
+    kv = make_paged_kv(rng, suffix_len, 16, Hkv, d, BF16)
+    q = normal_bits(rng, (batch, Hq, d), BF16)
+    q_pos = (prefix_len + suffix_len - 1).astype(np.int32)
+    kv_pos_offset = np.full(batch, prefix_len, dtype=np.int32)
+    return Workload(f"cascade_rope_{batch}req_prefix{prefix_len}p256_suffix256-1024p16_gqa32x8_bf16",
+                    "cascade", seed, BF16, Hq, Hkv, d, kv, q, rope_theta=500000.0,
+                    q_pos=q_pos, kv_pos_offset=kv_pos_offset, prefix=prefix)
+
+
+WORKLOADS = {
+    "single_decode": single_decode_mha,
+    "batch_decode": batch_decode_gqa,
+    "skewed_decode": skewed_decode_gqa,
+    "ragged_append": ragged_append_causal,
+    "cascade_rope": cascade_rope,
+}
+
+
+def small_decode(seed: int, kv_lens: List[int], page_size: int, num_qo_heads: int, num_kv_heads: int,
+                 head_dim: int = 128, dtype: str = BF16, extra_pages: int = 3) -> Workload:
+    """A small decode batch for parity tests (arbitrary lengths, including 0)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    kv = make_paged_kv(rng, np.asarray(kv_lens), page_size, num_kv_heads, head_dim, dtype,
+                       extra_pages=extra_pages)
+    q = normal_bits(rng, (len(kv_lens), num_qo_heads, head_dim), dtype)
+    return Workload(f"small_decode_s{seed}", "decode", seed, dtype, num_qo_heads, num_kv_heads,
+                    head_dim, kv, q)
+
+
+def small_append(seed: int, qo_lens: List[int], kv_lens: List[int], page_size: int,
+                 num_qo_heads: int, num_kv_heads: int, head_dim: int = 128, dtype: str = BF16,
+                 causal: bool = True, extra_pages: int = 3) -> Workload:
+    """A small ragged append batch for parity tests."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    kv = make_paged_kv(rng, np.asarray(kv_lens), page_size, num_kv_heads, head_dim, dtype,
+                       extra_pages=extra_pages)
+    qo_indptr = np.zeros(len(qo_lens) + 1, dtype=np.int32)
+    qo_indptr[1:] = np.cumsum(qo_lens)
+    q = normal_bits(rng, (int(qo_indptr[-1]), num_qo_heads, head_dim), dtype)
+    return Workload(f"small_append_s{seed}", "append", seed, dtype, num_qo_heads, num_kv_heads,
+                    head_dim, kv, q, qo_indptr=qo_indptr, causal=causal)

@@ -1,0 +1,169 @@
+"""Reference work-unit planner (pure Python, integers only).
+
+TEST INFRASTRUCTURE: only ``tests/`` may use it. The library's own C++ planner
+must reproduce every array returned here bit for bit.
+
+The paper summary ("图谱动态｜学苑周刊 NO.266", section 动态负载均衡调度)
+states the scheme only in words: attention is cut into work units that are
+spread over the compute units to minimise imbalance, in the spirit of Stream-K;
+a plan is made on the CPU from the length distribution and the GPU kernel, a
+persistent kernel with a fixed grid and a preallocated workspace, follows it.
+The concrete rule below is the plainest Stream-K reading of that passage:
+
+1. Validate. kv_len_b = (n_b - 1) * page_size + last_page_len_b when request b
+   owns n_b > 0 pages (last_page_len_b in [1, page_size]), else 0; indptr must
+   be non-decreasing and start at 0; a causal append needs qo_len_b <= kv_len_b.
+2. Tiles, in order: request b, then kv head h, then query tile qt. Decode has one
+   tile per (b, h) (its rows are the qo-head group of h). Append has
+   ceil(qo_len_b / tile_q) query tiles per (b, h). A tile's extent is the number
+   of keys its last row may see: kv_len_b - qo_len_b + min((qt + 1) * tile_q,
+   qo_len_b) when causal, else kv_len_b. It costs nblk = max(1,
+   ceil(extent / tile_kv)) blocks (an empty tile still writes its (0, -inf)).
+3. Partition. N = sum of nblk; quota = ceil(N / W); worker w owns the global
+   block range [w * quota, min((w + 1) * quota, N)).
+4. Segments are the intersections of a worker's range with one tile's blocks, in
+   increasing global order: (tile, kv_begin, kv_end, worker), kv_begin =
+   first local block * tile_kv, kv_end = min((last local block + 1) * tile_kv,
+   extent).
+5. A tile covered by one segment writes its output directly (partial = -1).
+   Otherwise its segments get consecutive partial slots in global order (so in
+   kv order) and the tile enters the merge list, in tile order.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+KIND_DECODE = 0
+KIND_APPEND = 1
+
+
+class PlanError(ValueError):
+    pass
+
+
+def _ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def kv_lengths(kv_indptr: Sequence[int], kv_last_page_len: Sequence[int], page_size: int,
+               batch: int):
+    if page_size < 1:
+        raise PlanError("page_size must be >= 1")
+    if len(kv_indptr) < batch + 1 or int(kv_indptr[0]) != 0:
+        raise PlanError("kv_indptr must have batch+1 entries starting at 0")
+    out = []
+    for b in range(batch):
+        n = int(kv_indptr[b + 1]) - int(kv_indptr[b])
+        if n < 0:
+            raise PlanError("kv_indptr must be non-decreasing")
+        if n == 0:
+            out.append(0)
+            continue
+        lpl = int(kv_last_page_len[b])
+        if lpl < 1 or lpl > page_size:
+            raise PlanError("kv_last_page_len must lie in [1, page_size]")
+        out.append((n - 1) * page_size + lpl)
+    return out
+
+
+def plan_ref(kind: int, batch: int, kv_indptr, kv_last_page_len, page_size: int,
+             num_kv_heads: int, num_workers: int, tile_kv: int, qo_indptr=None,
+             tile_q: int = 1, causal: bool = False) -> Dict[str, np.ndarray]:
+    """Return the plan as int32 arrays (see the module docstring for the rule)."""
+    if num_workers < 1 or tile_kv < 1 or tile_q < 1 or num_kv_heads < 1 or batch < 0:
+        raise PlanError("bad sizes")
+    kv_len = kv_lengths(kv_indptr, kv_last_page_len, page_size, batch)
+    if kind == KIND_DECODE:
+        qo_len = [1] * batch
+        n_qt = [1] * batch
+        causal = False
+    else:
+        if qo_indptr is None or int(qo_indptr[0]) != 0:
+            raise PlanError("qo_indptr must start at 0")
+        qo_len = []
+        for b in range(batch):
+            n = int(qo_indptr[b + 1]) - int(qo_indptr[b])
+            if n < 0:
+                raise PlanError("qo_indptr must be non-decreasing")
+            if causal and n > kv_len[b]:
+                raise PlanError("causal append needs qo_len <= kv_len")
+            qo_len.append(n)
+        n_qt = [_ceil_div(n, tile_q) for n in qo_len]
+
+    tile_b, tile_h, tile_qt, extent, nblk = [], [], [], [], []
+    for b in range(batch):
+        for h in range(num_kv_heads):
+            for qt in range(n_qt[b]):
+                if causal:
+                    e = kv_len[b] - qo_len[b] + min((qt + 1) * tile_q, qo_len[b])
+                else:
+                    e = kv_len[b]
+                tile_b.append(b)
+                tile_h.append(h)
+                tile_qt.append(qt)
+                extent.append(e)
+                nblk.append(max(1, _ceil_div(e, tile_kv)))
+    T = len(tile_b)
+    N = sum(nblk)
+    quota = _ceil_div(N, num_workers) if N else 1
+
+    seg_tile, seg_begin, seg_end, seg_worker = [], [], [], []
+    g0 = 0
+    for t in range(T):
+        g1 = g0 + nblk[t]
+        w = g0 // quota
+        while w * quota < g1:
+            lo = max(g0, w * quota)
+            hi = min(g1, (w + 1) * quota)
+            seg_tile.append(t)
+            seg_begin.append((lo - g0) * tile_kv)
+            seg_end.append(min((hi - g0) * tile_kv, extent[t]))
+            seg_worker.append(w)
+            w += 1
+        g0 = g1
+    S = len(seg_tile)
+
+    nseg = [0] * T
+    for t in seg_tile:
+        nseg[t] += 1
+    seg_partial = []
+    first_partial = [-1] * T
+    num_partials = [0] * T
+    slot = 0
+    for s in range(S):
+        t = seg_tile[s]
+        if nseg[t] == 1:
+            seg_partial.append(-1)
+        else:
+            if first_partial[t] < 0:
+                first_partial[t] = slot
+                num_partials[t] = nseg[t]
+            seg_partial.append(slot)
+            slot += 1
+    merge_list = [t for t in range(T) if nseg[t] > 1]
+
+    worker_seg_indptr = [0] * (num_workers + 1)
+    for w in seg_worker:
+        worker_seg_indptr[w + 1] += 1
+    for w in range(num_workers):
+        worker_seg_indptr[w + 1] += worker_seg_indptr[w]
+
+    i32 = lambda x: np.asarray(x, dtype=np.int32)
+    return {
+        "num_blocks": i32([N]),
+        "quota": i32([quota]),
+        "num_partials": i32([slot]),
+        "worker_seg_indptr": i32(worker_seg_indptr),
+        "seg_tile": i32(seg_tile),
+        "seg_kv_begin": i32(seg_begin),
+        "seg_kv_end": i32(seg_end),
+        "seg_partial": i32(seg_partial),
+        "tile_b": i32(tile_b),
+        "tile_h": i32(tile_h),
+        "tile_qt": i32(tile_qt),
+        "tile_first_partial": i32(first_partial),
+        "tile_num_partials": i32(num_partials),
+        "merge_list": i32(merge_list),
+    }

@@ -1,0 +1,126 @@
+"""Pins of the reference planner: hand-derived plans and the Stream-K invariants (CPU)."""
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+from oracle.plan_ref import KIND_APPEND, KIND_DECODE, PlanError, plan_ref
+
+
+def test_decode_hand_example():
+    # page 4; request 0 owns 3 pages with 2 valid slots in the last (10 tokens),
+    # request 1 owns 1 full page (4 tokens). tile_kv 4: tile 0 costs 3 blocks, tile 1
+    # costs 1; N = 4, W = 3 -> quota 2. Worker 0: blocks 0-1 = tile 0 keys [0, 8).
+    # Worker 1: block 2 = tile 0 keys [8, 10), block 3 = tile 1 keys [0, 4). Worker 2: none.
+    p = plan_ref(KIND_DECODE, 2, [0, 3, 4], [2, 4], 4, 1, 3, 4)
+    assert p["quota"].tolist() == [2]
+    assert p["worker_seg_indptr"].tolist() == [0, 1, 3, 3]
+    assert p["seg_tile"].tolist() == [0, 0, 1]
+    assert p["seg_kv_begin"].tolist() == [0, 8, 0]
+    assert p["seg_kv_end"].tolist() == [8, 10, 4]
+    assert p["seg_partial"].tolist() == [0, 1, -1]
+    assert p["tile_first_partial"].tolist() == [0, -1]
+    assert p["tile_num_partials"].tolist() == [2, 0]
+    assert p["merge_list"].tolist() == [0]
+
+
+def test_append_causal_hand_example():
+    # one request, 20 keys (2 pages of 16, 4 valid in the last), 5 queries, 2 kv heads,
+    # tile_q 2, tile_kv 8, causal. Query tiles see 15+2=17, 15+4=19, 15+5=20 keys ->
+    # 3 blocks each; 6 tiles (h0: qt0..2, h1: qt0..2) = 18 blocks; W 4 -> quota 5.
+    p = plan_ref(KIND_APPEND, 1, [0, 2], [4], 16, 2, 4, 8, qo_indptr=[0, 5], tile_q=2, causal=True)
+    assert p["tile_h"].tolist() == [0, 0, 0, 1, 1, 1]
+    assert p["tile_qt"].tolist() == [0, 1, 2, 0, 1, 2]
+    assert p["worker_seg_indptr"].tolist() == [0, 2, 5, 7, 8]
+    assert p["seg_tile"].tolist() == [0, 1, 1, 2, 3, 3, 4, 5]
+    assert p["seg_kv_begin"].tolist() == [0, 0, 16, 0, 0, 8, 0, 0]
+    assert p["seg_kv_end"].tolist() == [17, 16, 19, 20, 8, 17, 19, 20]
+    assert p["seg_partial"].tolist() == [-1, 0, 1, -1, 2, 3, -1, -1]
+    assert p["merge_list"].tolist() == [1, 3]
+    assert p["tile_first_partial"].tolist() == [-1, 0, -1, 2, -1, -1]
+
+
+def test_empty_request_still_gets_a_block():
+    p = plan_ref(KIND_DECODE, 3, [0, 0, 2, 2], [0, 3, 0], 4, 1, 8, 64)
+    assert p["num_blocks"].tolist() == [3]
+    assert p["seg_kv_begin"].tolist() == [0, 0, 0]
+    assert p["seg_kv_end"].tolist() == [0, 7, 0]
+
+
+@pytest.mark.parametrize("args", [
+    dict(kv_indptr=[0, 2, 1], lpl=[1, 1]),      # decreasing indptr
+    dict(kv_indptr=[1, 2, 3], lpl=[1, 1]),      # indptr not starting at 0
+    dict(kv_indptr=[0, 1, 2], lpl=[0, 1]),      # last_page_len 0 with pages
+    dict(kv_indptr=[0, 1, 2], lpl=[1, 5]),      # last_page_len > page size
+])
+def test_validation(args):
+    with pytest.raises(PlanError):
+        plan_ref(KIND_DECODE, 2, args["kv_indptr"], args["lpl"], 4, 1, 4, 16)
+
+
+def test_causal_needs_qo_not_above_kv():
+    with pytest.raises(PlanError):
+        plan_ref(KIND_APPEND, 1, [0, 1], [3], 4, 1, 4, 16, qo_indptr=[0, 4], tile_q=2, causal=True)
+    plan_ref(KIND_APPEND, 1, [0, 1], [3], 4, 1, 4, 16, qo_indptr=[0, 4], tile_q=2, causal=False)
+
+
+def check_invariants(p, W, Tk, extents):
+    T = len(extents)
+    S = len(p["seg_tile"])
+    quota = int(p["quota"][0])
+    ind = p["worker_seg_indptr"]
+    assert ind[0] == 0 and ind[-1] == S and np.all(np.diff(ind) >= 0)
+    assert S <= T + W - 1
+    # exact cover of every tile's blocks, in kv order
+    for t in range(T):
+        segs = np.nonzero(p["seg_tile"] == t)[0]
+        assert len(segs) >= 1 and np.all(np.diff(segs) == 1)
+        b = p["seg_kv_begin"][segs]
+        e = p["seg_kv_end"][segs]
+        assert b[0] == 0 and e[-1] == extents[t]
+        assert np.all(b[1:] == e[:-1]) and np.all(b % Tk == 0)
+        if len(segs) == 1:
+            assert p["seg_partial"][segs[0]] == -1 and p["tile_first_partial"][t] == -1
+        else:
+            slots = p["seg_partial"][segs]
+            assert np.all(np.diff(slots) == 1) and slots[0] == p["tile_first_partial"][t]
+            assert p["tile_num_partials"][t] == len(segs)
+    # worker loads stay within the quota
+    for w in range(W):
+        blocks = 0
+        for s in range(ind[w], ind[w + 1]):
+            blocks += max(1, -(-(int(p["seg_kv_end"][s]) - int(p["seg_kv_begin"][s])) // Tk))
+        assert blocks <= quota
+    used = p["seg_partial"][p["seg_partial"] >= 0]
+    assert np.array_equal(np.sort(used), np.arange(len(used)))
+    assert p["merge_list"].tolist() == [t for t in range(T) if p["tile_num_partials"][t] > 1]
+
+
+@settings(max_examples=150, deadline=None)
+@given(st.data())
+def test_invariants_random(data):
+    B = data.draw(st.integers(0, 9))
+    P = data.draw(st.sampled_from([1, 3, 16, 256]))
+    Hkv = data.draw(st.integers(1, 3))
+    W = data.draw(st.integers(1, 40))
+    Tk = data.draw(st.sampled_from([1, 16, 64]))
+    kv_len = data.draw(st.lists(st.integers(0, 700), min_size=B, max_size=B))
+    npg = [-(-n // P) for n in kv_len]
+    indptr = np.concatenate([[0], np.cumsum(npg)]).astype(int)
+    lpl = [n - (k - 1) * P if k else 0 for n, k in zip(kv_len, npg)]
+    append = data.draw(st.booleans())
+    if not append:
+        p = plan_ref(KIND_DECODE, B, indptr, lpl, P, Hkv, W, Tk)
+        ext = [n for n in kv_len for _ in range(Hkv)]
+    else:
+        causal = data.draw(st.booleans())
+        Tq = data.draw(st.sampled_from([1, 4, 32]))
+        qo = [data.draw(st.integers(0, n if causal else 90)) for n in kv_len]
+        qo_indptr = np.concatenate([[0], np.cumsum(qo)]).astype(int)
+        p = plan_ref(KIND_APPEND, B, indptr, lpl, P, Hkv, W, Tk, qo_indptr=qo_indptr,
+                     tile_q=Tq, causal=causal)
+        ext = []
+        for n, m in zip(kv_len, qo):
+            for _ in range(Hkv):
+                for qt in range(-(-m // Tq)):
+                    ext.append(n - m + min((qt + 1) * Tq, m) if causal else n)
+    check_invariants(p, W, Tk, ext)
