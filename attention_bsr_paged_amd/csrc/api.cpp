@@ -1,0 +1,382 @@
+// C ABI of libabp: validation, plan upload and kernel launches.
+//
+// Every entry point returns an abp_status and records a message in a
+// thread-local string; no C++ exception crosses the boundary. Nothing here
+// allocates device or pinned memory: the caller owns all buffers.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+
+#include "../../include/abp.h"
+#include "kernels.h"
+#include "plan.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int status, const std::string& msg) {
+  g_err = msg;
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  g_err = std::string(what) + ": " + hipGetErrorString(e);
+  return ABP_ERR_HIP;
+}
+
+std::mutex g_cu_mutex;
+int32_t g_cu_count[64] = {0};
+
+int num_cus(int device, int32_t* out) {
+  if (device < 0 || device >= 64) return fail(ABP_ERR_INVALID_ARG, "device out of range");
+  std::lock_guard<std::mutex> lock(g_cu_mutex);
+  if (g_cu_count[device] == 0) {
+    int v = 0;
+    hipError_t e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, device);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    g_cu_count[device] = v;
+  }
+  *out = g_cu_count[device];
+  return ABP_OK;
+}
+
+int default_workers(int kind, int32_t* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  int32_t cus = 0;
+  int st = num_cus(dev, &cus);
+  if (st != ABP_OK) return st;
+  *out = kind == ABP_KIND_DECODE ? 2 * cus : cus;
+  return ABP_OK;
+}
+
+// Layout of a plan from its capacity fields (what *_run can reconstruct).
+int layout_of_plan(const abp::Config& cfg, const abp_plan* plan, abp::Layout* L, std::string* err) {
+  int st = abp::make_layout_caps(cfg, plan->max_tiles, plan->num_workers, L, err);
+  if (st != ABP_OK) return st;
+  if (L->max_segs != plan->max_segments || L->max_partials != plan->max_partials) {
+    *err = "plan capacities are inconsistent";
+    return ABP_ERR_PLAN_MISMATCH;
+  }
+  return ABP_OK;
+}
+
+int resolve_layout(int kind, const abp_params* params, int32_t max_batch, int32_t max_qo,
+                   int32_t workers, abp::Config* cfg, abp::Layout* L) {
+  std::string err;
+  int st = abp::check_params(kind, params, cfg, &err);
+  if (st != ABP_OK) return fail(st, err);
+  if (kind == ABP_KIND_DECODE && cfg->group > 8)
+    return fail(ABP_ERR_UNSUPPORTED, "decode supports group sizes 1, 2, 4 and 8");
+  if (workers <= 0) {
+    st = default_workers(kind, &workers);
+    if (st != ABP_OK) return st;
+  }
+  st = abp::make_layout(*cfg, max_batch, max_qo, workers, L, &err);
+  if (st != ABP_OK) return fail(st, err);
+  return ABP_OK;
+}
+
+int do_plan(int kind, const abp_params* params, int32_t batch, const int32_t* qo_indptr_h,
+            const int32_t* kv_indptr_h, const int32_t* lpl_h, int32_t max_batch, int32_t max_qo,
+            int32_t workers, void* host_ws, size_t host_bytes, abp_plan* plan,
+            abp::Config* cfg_out, abp::Layout* lay_out) {
+  if (!plan) return fail(ABP_ERR_INVALID_ARG, "plan is NULL");
+  if (!host_ws) return fail(ABP_ERR_INVALID_ARG, "host workspace is NULL");
+  if (batch > max_batch) return fail(ABP_ERR_WORKSPACE_TOO_SMALL, "batch > max_batch");
+  abp::Config cfg;
+  abp::Layout L;
+  int st = resolve_layout(kind, params, max_batch, max_qo, workers, &cfg, &L);
+  if (st != ABP_OK) return st;
+  if (host_bytes < L.plan_bytes)
+    return fail(ABP_ERR_WORKSPACE_TOO_SMALL, "host workspace smaller than abp_workspace_size");
+  if (kind == ABP_KIND_APPEND && qo_indptr_h && batch >= 0 && qo_indptr_h[batch] > max_qo)
+    return fail(ABP_ERR_WORKSPACE_TOO_SMALL, "total query tokens > max_qo_tokens");
+  std::string err;
+  st = abp::plan_compute(cfg, L, batch, qo_indptr_h, kv_indptr_h, lpl_h,
+                         static_cast<int32_t*>(host_ws), plan, &err);
+  if (st != ABP_OK) return fail(st, err);
+  if (cfg_out) *cfg_out = cfg;
+  if (lay_out) *lay_out = L;
+  return ABP_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+int prepare_run(int kind, const abp_plan* plan, const abp_params* params, void* dev_ws,
+                size_t dev_bytes, abp::Config* cfg, abp::Layout* L) {
+  if (!plan || !params) return fail(ABP_ERR_INVALID_ARG, "plan or params is NULL");
+  if (plan->kind != kind) return fail(ABP_ERR_PLAN_MISMATCH, "plan was made for the other kind");
+  std::string err;
+  int st = abp::check_params(kind, params, cfg, &err);
+  if (st != ABP_OK) return fail(st, err);
+  if (kind == ABP_KIND_DECODE && cfg->group > 8)
+    return fail(ABP_ERR_UNSUPPORTED, "decode supports group sizes 1, 2, 4 and 8");
+  if (plan->num_workers < 1) return fail(ABP_ERR_PLAN_MISMATCH, "plan has no workers");
+  st = layout_of_plan(*cfg, plan, L, &err);
+  if (st != ABP_OK) return fail(st, err);
+  if (abp::fingerprint(*cfg, *L) != plan->fingerprint)
+    return fail(ABP_ERR_PLAN_MISMATCH, "params or capacities differ from the planned ones");
+  if (!dev_ws) return fail(ABP_ERR_INVALID_ARG, "device workspace is NULL");
+  if (dev_bytes < L->dev_bytes)
+    return fail(ABP_ERR_WORKSPACE_TOO_SMALL, "device workspace smaller than abp_workspace_size");
+  if (!aligned16(dev_ws)) return fail(ABP_ERR_INVALID_ARG, "device workspace must be 16-byte aligned");
+  return ABP_OK;
+}
+
+void fill_args(const abp::Config& cfg, const abp::Layout& L, const abp_plan* plan, void* dev_ws,
+               abp::AttnArgs* a) {
+  a->num_qo_heads = cfg.hq;
+  a->num_kv_heads = cfg.hkv;
+  a->page_size = cfg.page_size;
+  int shift = -1;
+  if ((cfg.page_size & (cfg.page_size - 1)) == 0) {
+    shift = 0;
+    while ((1 << shift) < cfg.page_size) ++shift;
+  }
+  a->page_shift = shift;
+  a->token_stride = cfg.hkv * cfg.head_dim;
+  a->page_stride = int64_t(cfg.page_size) * a->token_stride;
+  a->out_dtype = cfg.out_dtype;
+  a->sm_scale = cfg.sm_scale;
+  a->sm_scale_log2 = cfg.sm_scale * 1.4426950408889634f;
+  a->workers = plan->num_workers;
+  char* ws = static_cast<char*>(dev_ws);
+  a->plan = reinterpret_cast<const int32_t*>(ws);
+  a->o_part = reinterpret_cast<float*>(ws + L.partial_offset);
+  a->lse_part = a->o_part + int64_t(L.max_partials) * L.rows * cfg.head_dim;
+}
+
+int merge_grid(const abp_plan* plan) { return plan->num_workers; }
+
+}  // namespace
+
+extern "C" {
+
+const char* abp_status_string(int status) {
+  switch (status) {
+    case ABP_OK: return "ok";
+    case ABP_ERR_INVALID_ARG: return "invalid argument";
+    case ABP_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ABP_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case ABP_ERR_PLAN_MISMATCH: return "plan does not match the run arguments";
+    case ABP_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* abp_last_error(void) { return g_err.c_str(); }
+
+int abp_device_num_cus(int device, int32_t* out) {
+  try {
+    if (!out) return fail(ABP_ERR_INVALID_ARG, "num_cus is NULL");
+    return num_cus(device, out);
+  } catch (...) {
+    return fail(ABP_ERR_HIP, "exception");
+  }
+}
+
+int abp_workspace_size(int kind, const abp_params* params, int32_t max_batch,
+                       int32_t max_qo_tokens, int32_t num_workers, size_t* host_bytes,
+                       size_t* dev_bytes) {
+  try {
+    if (!host_bytes || !dev_bytes) return fail(ABP_ERR_INVALID_ARG, "NULL size pointer");
+    abp::Config cfg;
+    abp::Layout L;
+    int st = resolve_layout(kind, params, max_batch, max_qo_tokens, num_workers, &cfg, &L);
+    if (st != ABP_OK) return st;
+    *host_bytes = L.plan_bytes;
+    *dev_bytes = L.dev_bytes;
+    return ABP_OK;
+  } catch (...) {
+    return fail(ABP_ERR_INVALID_ARG, "exception");
+  }
+}
+
+int abp_plan_host(int kind, const abp_params* params, int32_t batch, const int32_t* qo_indptr_h,
+                  const int32_t* kv_indptr_h, const int32_t* kv_last_page_len_h,
+                  int32_t max_batch, int32_t max_qo_tokens, int32_t num_workers, void* host_ws,
+                  size_t host_bytes, abp_plan* plan) {
+  try {
+    if (num_workers <= 0) return fail(ABP_ERR_INVALID_ARG, "abp_plan_host needs num_workers > 0");
+    return do_plan(kind, params, batch, qo_indptr_h, kv_indptr_h, kv_last_page_len_h, max_batch,
+                   max_qo_tokens, num_workers, host_ws, host_bytes, plan, nullptr, nullptr);
+  } catch (...) {
+    return fail(ABP_ERR_INVALID_ARG, "exception");
+  }
+}
+
+static int plan_and_upload(int kind, const abp_params* params, int32_t batch,
+                           const int32_t* qo_indptr_h, const int32_t* kv_indptr_h,
+                           const int32_t* lpl_h, int32_t max_batch, int32_t max_qo,
+                           int32_t workers, void* host_ws, size_t host_bytes, void* dev_ws,
+                           size_t dev_bytes, abp_stream_t stream, abp_plan* plan) {
+  abp::Config cfg;
+  abp::Layout L;
+  int st = do_plan(kind, params, batch, qo_indptr_h, kv_indptr_h, lpl_h, max_batch, max_qo,
+                   workers, host_ws, host_bytes, plan, &cfg, &L);
+  if (st != ABP_OK) return st;
+  if (!dev_ws) return fail(ABP_ERR_INVALID_ARG, "device workspace is NULL");
+  if (dev_bytes < L.dev_bytes)
+    return fail(ABP_ERR_WORKSPACE_TOO_SMALL, "device workspace smaller than abp_workspace_size");
+  hipError_t e = hipMemcpyAsync(dev_ws, host_ws, L.plan_bytes, hipMemcpyHostToDevice,
+                                reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(plan)");
+  return ABP_OK;
+}
+
+int abp_decode_plan(const abp_params* params, int32_t batch, const int32_t* kv_indptr_h,
+                    const int32_t* kv_last_page_len_h, int32_t max_batch, int32_t num_workers,
+                    void* host_ws, size_t host_bytes, void* dev_ws, size_t dev_bytes,
+                    abp_stream_t stream, abp_plan* plan) {
+  try {
+    return plan_and_upload(ABP_KIND_DECODE, params, batch, nullptr, kv_indptr_h,
+                           kv_last_page_len_h, max_batch, 0, num_workers, host_ws, host_bytes,
+                           dev_ws, dev_bytes, stream, plan);
+  } catch (...) {
+    return fail(ABP_ERR_INVALID_ARG, "exception");
+  }
+}
+
+int abp_append_plan(const abp_params* params, int32_t batch, const int32_t* qo_indptr_h,
+                    const int32_t* kv_indptr_h, const int32_t* kv_last_page_len_h,
+                    int32_t max_batch, int32_t max_qo_tokens, int32_t num_workers,
+                    void* host_ws, size_t host_bytes, void* dev_ws, size_t dev_bytes,
+                    abp_stream_t stream, abp_plan* plan) {
+  try {
+    if (!qo_indptr_h) return fail(ABP_ERR_INVALID_ARG, "qo_indptr is NULL");
+    return plan_and_upload(ABP_KIND_APPEND, params, batch, qo_indptr_h, kv_indptr_h,
+                           kv_last_page_len_h, max_batch, max_qo_tokens, num_workers, host_ws,
+                           host_bytes, dev_ws, dev_bytes, stream, plan);
+  } catch (...) {
+    return fail(ABP_ERR_INVALID_ARG, "exception");
+  }
+}
+
+int abp_decode_run(const abp_plan* plan, const abp_params* params, const void* q,
+                   const void* k_pages, const void* v_pages, const int32_t* kv_indptr_d,
+                   const int32_t* kv_indices_d, const int32_t* kv_last_page_len_d,
+                   const int32_t* q_pos_d, const int32_t* kv_pos_offset_d, void* o, float* lse,
+                   void* dev_ws, size_t dev_bytes, abp_stream_t stream) {
+  try {
+    abp::Config cfg;
+    abp::Layout L;
+    int st = prepare_run(ABP_KIND_DECODE, plan, params, dev_ws, dev_bytes, &cfg, &L);
+    if (st != ABP_OK) return st;
+    if (plan->batch > 0 && (!q || !k_pages || !v_pages || !kv_indptr_d || !kv_indices_d ||
+                            !kv_last_page_len_d || !o))
+      return fail(ABP_ERR_INVALID_ARG, "NULL tensor pointer");
+    if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o))
+      return fail(ABP_ERR_INVALID_ARG, "q, k_pages, v_pages and o must be 16-byte aligned");
+    abp::AttnArgs a = {};
+    a.q = q;
+    a.k_pages = k_pages;
+    a.v_pages = v_pages;
+    a.kv_indptr = kv_indptr_d;
+    a.kv_indices = kv_indices_d;
+    a.kv_last_page_len = kv_last_page_len_d;
+    a.q_pos = q_pos_d;
+    a.kv_pos_offset = kv_pos_offset_d;
+    a.o = o;
+    a.lse = lse;
+    fill_args(cfg, L, plan, dev_ws, &a);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = abp::launch_decode(cfg, a, s);
+    if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
+    e = abp::launch_plan_merge(cfg, a, merge_grid(plan), s);
+    if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+    return ABP_OK;
+  } catch (...) {
+    return fail(ABP_ERR_HIP, "exception");
+  }
+}
+
+int abp_append_run(const abp_plan* plan, const abp_params* params, const void* q,
+                   const void* k_pages, const void* v_pages, const int32_t* qo_indptr_d,
+                   const int32_t* kv_indptr_d, const int32_t* kv_indices_d,
+                   const int32_t* kv_last_page_len_d, const int32_t* q_pos_d,
+                   const int32_t* kv_pos_offset_d, void* o, float* lse, void* dev_ws,
+                   size_t dev_bytes, abp_stream_t stream) {
+  try {
+    abp::Config cfg;
+    abp::Layout L;
+    int st = prepare_run(ABP_KIND_APPEND, plan, params, dev_ws, dev_bytes, &cfg, &L);
+    if (st != ABP_OK) return st;
+    if (plan->batch > 0 && (!q || !k_pages || !v_pages || !qo_indptr_d || !kv_indptr_d ||
+                            !kv_indices_d || !kv_last_page_len_d || !o))
+      return fail(ABP_ERR_INVALID_ARG, "NULL tensor pointer");
+    if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o))
+      return fail(ABP_ERR_INVALID_ARG, "q, k_pages, v_pages and o must be 16-byte aligned");
+    abp::AttnArgs a = {};
+    a.q = q;
+    a.k_pages = k_pages;
+    a.v_pages = v_pages;
+    a.qo_indptr = qo_indptr_d;
+    a.kv_indptr = kv_indptr_d;
+    a.kv_indices = kv_indices_d;
+    a.kv_last_page_len = kv_last_page_len_d;
+    a.q_pos = q_pos_d;
+    a.kv_pos_offset = kv_pos_offset_d;
+    a.o = o;
+    a.lse = lse;
+    fill_args(cfg, L, plan, dev_ws, &a);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = abp::launch_append(cfg, a, s);
+    if (e != hipSuccess) return hip_fail(e, "append kernel launch");
+    e = abp::launch_plan_merge(cfg, a, merge_grid(plan), s);
+    if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+    return ABP_OK;
+  } catch (...) {
+    return fail(ABP_ERR_HIP, "exception");
+  }
+}
+
+int abp_merge_state(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
+                    void* o_out, float* lse_out, int64_t num_rows, int32_t head_dim,
+                    int in_dtype, int out_dtype, abp_stream_t stream) {
+  try {
+    if (head_dim != 128) return fail(ABP_ERR_UNSUPPORTED, "only head_dim 128 is built");
+    if (num_rows < 0) return fail(ABP_ERR_INVALID_ARG, "num_rows < 0");
+    if (in_dtype < ABP_F16 || in_dtype > ABP_F32 || out_dtype < ABP_F16 || out_dtype > ABP_F32)
+      return fail(ABP_ERR_UNSUPPORTED, "dtype must be ABP_F16, ABP_BF16 or ABP_F32");
+    if (num_rows > 0 && (!o_a || !lse_a || !o_b || !lse_b || !o_out))
+      return fail(ABP_ERR_INVALID_ARG, "NULL pointer");
+    if (!aligned16(o_a) || !aligned16(o_b) || !aligned16(o_out))
+      return fail(ABP_ERR_INVALID_ARG, "o pointers must be 16-byte aligned");
+    hipError_t e = abp::launch_merge_two(o_a, lse_a, o_b, lse_b, o_out, lse_out, num_rows,
+                                         in_dtype, out_dtype, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "merge_state launch");
+    return ABP_OK;
+  } catch (...) {
+    return fail(ABP_ERR_HIP, "exception");
+  }
+}
+
+int abp_merge_states(const void* o_in, const float* lse_in, int32_t num_states, int64_t num_rows,
+                     int32_t head_dim, int in_dtype, int out_dtype, void* o_out, float* lse_out,
+                     abp_stream_t stream) {
+  try {
+    if (head_dim != 128) return fail(ABP_ERR_UNSUPPORTED, "only head_dim 128 is built");
+    if (num_rows < 0 || num_states < 0) return fail(ABP_ERR_INVALID_ARG, "negative size");
+    if (in_dtype < ABP_F16 || in_dtype > ABP_F32 || out_dtype < ABP_F16 || out_dtype > ABP_F32)
+      return fail(ABP_ERR_UNSUPPORTED, "dtype must be ABP_F16, ABP_BF16 or ABP_F32");
+    if (num_rows > 0 && (!o_out || (num_states > 0 && (!o_in || !lse_in))))
+      return fail(ABP_ERR_INVALID_ARG, "NULL pointer");
+    if (!aligned16(o_in) || !aligned16(o_out))
+      return fail(ABP_ERR_INVALID_ARG, "o pointers must be 16-byte aligned");
+    hipError_t e = abp::launch_merge_states(o_in, lse_in, num_states, num_rows, in_dtype,
+                                            out_dtype, o_out, lse_out,
+                                            reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "merge_states launch");
+    return ABP_OK;
+  } catch (...) {
+    return fail(ABP_ERR_HIP, "exception");
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,51 @@
+// Kernel argument blocks and host-side launchers (defined in the .hip files).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "plan.h"
+
+namespace abp {
+
+// Paged attention (decode and append share this argument block).
+struct AttnArgs {
+  const void* q;
+  const void* k_pages;
+  const void* v_pages;
+  const int32_t* qo_indptr;      // append only
+  const int32_t* kv_indptr;
+  const int32_t* kv_indices;
+  const int32_t* kv_last_page_len;
+  const int32_t* q_pos;          // RoPE only, may be NULL
+  const int32_t* kv_pos_offset;  // RoPE only, may be NULL
+  void* o;
+  float* lse;                    // may be NULL
+  const int32_t* plan;           // plan blob in device memory
+  float* o_part;                 // [max_partials, rows, head_dim]
+  float* lse_part;               // [max_partials, rows]
+  int32_t num_qo_heads;
+  int32_t num_kv_heads;
+  int32_t page_size;
+  int32_t page_shift;            // log2(page_size) if a power of two, else -1
+  int64_t page_stride;           // elements per page = page_size * Hkv * head_dim
+  int32_t token_stride;          // elements per token inside a page = Hkv * head_dim
+  int32_t out_dtype;
+  float sm_scale;
+  float sm_scale_log2;           // sm_scale * log2(e)
+  int32_t workers;
+};
+
+hipError_t launch_decode(const Config& cfg, const AttnArgs& a, hipStream_t stream);
+hipError_t launch_append(const Config& cfg, const AttnArgs& a, hipStream_t stream);
+// merges the split tiles of a plan into o / lse (fixed grid, reads counts from the plan)
+hipError_t launch_plan_merge(const Config& cfg, const AttnArgs& a, int32_t grid,
+                             hipStream_t stream);
+
+hipError_t launch_merge_two(const void* o_a, const float* lse_a, const void* o_b,
+                            const float* lse_b, void* o_out, float* lse_out, int64_t rows,
+                            int in_dtype, int out_dtype, hipStream_t stream);
+hipError_t launch_merge_states(const void* o_in, const float* lse_in, int32_t num_states,
+                               int64_t rows, int in_dtype, int out_dtype, void* o_out,
+                               float* lse_out, hipStream_t stream);
+
+}  // namespace abp

@@ -1,0 +1,75 @@
+// Plan blob layout shared by the host planner and the GPU kernels.
+//
+// The blob is an int32 array written on the host and copied once to the start
+// of the device workspace. Every offset depends only on capacities fixed by
+// (kind, params, max_batch, max_qo_tokens, num_workers), never on the lengths
+// of one batch, so kernels captured in a graph stay valid after a re-plan:
+// they read the counts of the current plan from the header at run time.
+#pragma once
+#include <stdint.h>
+
+namespace abp {
+
+enum Header : int {
+  H_MAGIC = 0,
+  H_KIND,
+  H_BATCH,
+  H_WORKERS,
+  H_NUM_TILES,
+  H_NUM_SEGS,
+  H_NUM_PARTIALS,
+  H_NUM_MERGES,
+  H_TILE_Q,
+  H_TILE_KV,
+  H_ROWS,        // rows per tile = tile_q * group
+  H_GROUP,       // qo heads per kv head
+  H_NUM_KV_HEADS,
+  H_PAGE_SIZE,
+  H_NUM_BLOCKS,
+  H_QUOTA,
+  H_OFF_WSEG,    // int32 offsets of the arrays below
+  H_OFF_SEG,
+  H_OFF_TILE,
+  H_OFF_MERGE,
+  H_OFF_ROPE,
+  H_MAX_TILES,
+  H_MAX_SEGS,
+  H_MAX_PARTIALS,
+  H_CAUSAL,
+  HEADER_INTS = 32
+};
+
+constexpr int32_t kMagic = 0x41425031;  // "ABP1"
+constexpr int kMaxRopePairs = 64;        // head_dim 128
+
+// Records (int32 x 4 each, 16-byte aligned in the blob):
+//   seg   {tile, kv_begin, kv_end, partial_slot or -1}
+//   tile  {b, kv_head, q_tile, first_partial or -1}
+//   merge {tile, first_partial, num_partials, 0}
+// worker_seg_indptr has num_workers + 1 entries.
+// rope: kMaxRopePairs x {hi, lo} float32 bit patterns of theta^(-2j/d) / (2 pi)
+//       (revolutions per position), split so hi + lo carries ~48 bits.
+
+struct Layout {
+  int32_t workers = 0;
+  int32_t max_tiles = 0;
+  int32_t max_segs = 0;
+  int32_t max_partials = 0;
+  int32_t max_merges = 0;
+  int32_t tile_q = 1;
+  int32_t tile_kv = 64;
+  int32_t rows = 1;
+  int64_t off_wseg = 0, off_seg = 0, off_tile = 0, off_merge = 0, off_rope = 0;
+  int64_t plan_ints = 0;       // total int32 of the blob
+  uint64_t plan_bytes = 0;
+  uint64_t partial_offset = 0; // bytes, 256-aligned
+  uint64_t partial_bytes = 0;
+  uint64_t dev_bytes = 0;
+};
+
+// Tile sizes of the kernels.
+constexpr int kDecodeTileKv = 64;   // keys per work block (decode)
+constexpr int kAppendRows = 128;    // MFMA rows per append tile = tile_q * group
+constexpr int kAppendTileKv = 64;   // keys per work block (append)
+
+}  // namespace abp

@@ -1,0 +1,204 @@
+// Merging of attention states (o, lse) computed over disjoint key sets.
+//
+// Attention split over key ranges is recombined exactly through the natural-log
+// sum of exponentials of the scaled logits: with M = max_i lse_i,
+//   lse = M + ln sum_i exp(lse_i - M),   o = sum_i exp(lse_i - lse) o_i,
+// and all-(-inf) inputs give (0, -inf). This is what lets the planner cut one
+// request's keys over several workers (paper summary "图谱动态｜学苑周刊 NO.266",
+// section 动态负载均衡调度) and what combines a shared prefix with per-request
+// suffixes (section 统一的 KV 缓存存储格式: several formats in one attention).
+//
+// Layout: 16 lanes per row of 128, 8 consecutive elements per lane (one
+// 16-byte load of bf16/fp16, two of fp32); 16 rows per 256-thread block. The
+// merge order is fixed (slot 0, 1, ...), so results are bit-reproducible.
+#include "common.h"
+#include "kernels.h"
+#include "layout.h"
+
+namespace abp {
+
+namespace {
+
+template <int IN_DT, int OUT_DT>
+__global__ __launch_bounds__(256) void merge_states_kernel(const void* o_in, const float* lse_in,
+                                                           int32_t n, int64_t rows, void* o_out,
+                                                           float* lse_out) {
+  const int64_t row = int64_t(blockIdx.x) * 16 + (threadIdx.x >> 4);
+  const int e0 = (threadIdx.x & 15) * 8;
+  if (row >= rows) return;
+  float M = kNegInf;
+  for (int i = 0; i < n; ++i) M = __builtin_fmaxf(M, lse_in[int64_t(i) * rows + row]);
+  float out[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) out[e] = 0.f;
+  float lse = kNegInf;
+  if (M != kNegInf) {
+    float tot = 0.f;
+    for (int i = 0; i < n; ++i) tot += fast_exp2((lse_in[int64_t(i) * rows + row] - M) * kLog2e);
+    lse = M + fast_log2(tot) * kLn2;
+    for (int i = 0; i < n; ++i) {
+      const int64_t sr = int64_t(i) * rows + row;
+      const float w = fast_exp2((lse_in[sr] - lse) * kLog2e);
+      float v[8];
+      load8<IN_DT>(o_in, sr * 128 + e0, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out[e] = __builtin_fmaf(w, v[e], out[e]);
+    }
+  }
+  store8<OUT_DT>(o_out, row * 128 + e0, out);
+  if (lse_out && e0 == 0) lse_out[row] = lse;
+}
+
+template <int IN_DT, int OUT_DT>
+__global__ __launch_bounds__(256) void merge_two_kernel(const void* o_a, const float* lse_a,
+                                                        const void* o_b, const float* lse_b,
+                                                        int64_t rows, void* o_out,
+                                                        float* lse_out) {
+  const int64_t row = int64_t(blockIdx.x) * 16 + (threadIdx.x >> 4);
+  const int e0 = (threadIdx.x & 15) * 8;
+  if (row >= rows) return;
+  const float la = lse_a[row], lb = lse_b[row];
+  const float M = __builtin_fmaxf(la, lb);
+  float out[8];
+  float lse = kNegInf;
+  if (M == kNegInf) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = 0.f;
+  } else {
+    const float ea = fast_exp2((la - M) * kLog2e), eb = fast_exp2((lb - M) * kLog2e);
+    lse = M + fast_log2(ea + eb) * kLn2;
+    const float wa = fast_exp2((la - lse) * kLog2e), wb = fast_exp2((lb - lse) * kLog2e);
+    float va[8], vb[8];
+    load8<IN_DT>(o_a, row * 128 + e0, va);
+    load8<IN_DT>(o_b, row * 128 + e0, vb);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = __builtin_fmaf(wa, va[e], wb * vb[e]);
+  }
+  store8<OUT_DT>(o_out, row * 128 + e0, out);
+  if (lse_out && e0 == 0) lse_out[row] = lse;
+}
+
+// Merge the split tiles of a plan. Grid is fixed; work items are
+// (merge entry, block of 16 tile rows), read from the plan header at run time.
+template <int OUT_DT>
+__global__ __launch_bounds__(256) void plan_merge_kernel(AttnArgs a) {
+  const int32_t* plan = a.plan;
+  const int kind = plan[H_KIND];
+  const int rows = plan[H_ROWS];
+  const int G = plan[H_GROUP];
+  const int Tq = plan[H_TILE_Q];
+  const int num_merges = plan[H_NUM_MERGES];
+  const int4* tiles = reinterpret_cast<const int4*>(plan + plan[H_OFF_TILE]);
+  const int4* merges = reinterpret_cast<const int4*>(plan + plan[H_OFF_MERGE]);
+  const int row_blocks = (rows + 15) / 16;
+  const int items = num_merges * row_blocks;
+  const int e0 = (threadIdx.x & 15) * 8;
+  for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    const int m = item / row_blocks;
+    const int r = (item % row_blocks) * 16 + (threadIdx.x >> 4);
+    if (r >= rows) continue;
+    const int4 mr = merges[m];
+    const int4 tl = tiles[mr.x];
+    int64_t token;
+    int head;
+    if (kind == ABP_KIND_DECODE) {
+      token = tl.x;
+      head = tl.y * G + r;
+    } else {
+      const int q0 = a.qo_indptr[tl.x];
+      const int qo_len = a.qo_indptr[tl.x + 1] - q0;
+      const int tloc = tl.z * Tq + r / G;
+      if (tloc >= qo_len) continue;
+      token = q0 + tloc;
+      head = tl.y * G + (r % G);
+    }
+    const int n = mr.z;
+    float M = kNegInf;
+    for (int i = 0; i < n; ++i) M = __builtin_fmaxf(M, a.lse_part[int64_t(mr.y + i) * rows + r]);
+    float out[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = 0.f;
+    float lse = kNegInf;
+    if (M != kNegInf) {
+      float tot = 0.f;
+      for (int i = 0; i < n; ++i)
+        tot += fast_exp2((a.lse_part[int64_t(mr.y + i) * rows + r] - M) * kLog2e);
+      lse = M + fast_log2(tot) * kLn2;
+      for (int i = 0; i < n; ++i) {
+        const int64_t sr = int64_t(mr.y + i) * rows + r;
+        const float w = fast_exp2((a.lse_part[sr] - lse) * kLog2e);
+        float v[8];
+        load8<ABP_F32>(a.o_part, sr * 128 + e0, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) out[e] = __builtin_fmaf(w, v[e], out[e]);
+      }
+    }
+    const int64_t orow = token * a.num_qo_heads + head;
+    store8<OUT_DT>(a.o, orow * 128 + e0, out);
+    if (a.lse && e0 == 0) a.lse[orow] = lse;
+  }
+}
+
+template <int IN_DT>
+hipError_t merge_two_out(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
+                         void* o_out, float* lse_out, int64_t rows, int out_dtype,
+                         hipStream_t s) {
+  const dim3 grid((unsigned)((rows + 15) / 16));
+  if (out_dtype == ABP_F32)
+    merge_two_kernel<IN_DT, ABP_F32><<<grid, 256, 0, s>>>(o_a, lse_a, o_b, lse_b, rows, o_out, lse_out);
+  else if (out_dtype == ABP_BF16)
+    merge_two_kernel<IN_DT, ABP_BF16><<<grid, 256, 0, s>>>(o_a, lse_a, o_b, lse_b, rows, o_out, lse_out);
+  else
+    merge_two_kernel<IN_DT, ABP_F16><<<grid, 256, 0, s>>>(o_a, lse_a, o_b, lse_b, rows, o_out, lse_out);
+  return hipGetLastError();
+}
+
+template <int IN_DT>
+hipError_t merge_states_out(const void* o_in, const float* lse_in, int32_t n, int64_t rows,
+                            int out_dtype, void* o_out, float* lse_out, hipStream_t s) {
+  const dim3 grid((unsigned)((rows + 15) / 16));
+  if (out_dtype == ABP_F32)
+    merge_states_kernel<IN_DT, ABP_F32><<<grid, 256, 0, s>>>(o_in, lse_in, n, rows, o_out, lse_out);
+  else if (out_dtype == ABP_BF16)
+    merge_states_kernel<IN_DT, ABP_BF16><<<grid, 256, 0, s>>>(o_in, lse_in, n, rows, o_out, lse_out);
+  else
+    merge_states_kernel<IN_DT, ABP_F16><<<grid, 256, 0, s>>>(o_in, lse_in, n, rows, o_out, lse_out);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+
+hipError_t launch_merge_two(const void* o_a, const float* lse_a, const void* o_b,
+                            const float* lse_b, void* o_out, float* lse_out, int64_t rows,
+                            int in_dtype, int out_dtype, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  if (in_dtype == ABP_F32)
+    return merge_two_out<ABP_F32>(o_a, lse_a, o_b, lse_b, o_out, lse_out, rows, out_dtype, s);
+  if (in_dtype == ABP_BF16)
+    return merge_two_out<ABP_BF16>(o_a, lse_a, o_b, lse_b, o_out, lse_out, rows, out_dtype, s);
+  return merge_two_out<ABP_F16>(o_a, lse_a, o_b, lse_b, o_out, lse_out, rows, out_dtype, s);
+}
+
+hipError_t launch_merge_states(const void* o_in, const float* lse_in, int32_t n, int64_t rows,
+                               int in_dtype, int out_dtype, void* o_out, float* lse_out,
+                               hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  if (in_dtype == ABP_F32)
+    return merge_states_out<ABP_F32>(o_in, lse_in, n, rows, out_dtype, o_out, lse_out, s);
+  if (in_dtype == ABP_BF16)
+    return merge_states_out<ABP_BF16>(o_in, lse_in, n, rows, out_dtype, o_out, lse_out, s);
+  return merge_states_out<ABP_F16>(o_in, lse_in, n, rows, out_dtype, o_out, lse_out, s);
+}
+
+hipError_t launch_plan_merge(const Config& cfg, const AttnArgs& a, int32_t grid, hipStream_t s) {
+  if (cfg.out_dtype == ABP_F32)
+    plan_merge_kernel<ABP_F32><<<grid, 256, 0, s>>>(a);
+  else if (cfg.out_dtype == ABP_BF16)
+    plan_merge_kernel<ABP_BF16><<<grid, 256, 0, s>>>(a);
+  else
+    plan_merge_kernel<ABP_F16><<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace abp

@@ -1,0 +1,363 @@
+// Host work-unit planner (pure C++, no HIP runtime calls).
+//
+// The paper summary (FlashInfer, "图谱动态｜学苑周刊 NO.266", section
+// 动态负载均衡调度) describes a two-phase scheduler in the spirit of Stream-K:
+// on the CPU, cut attention into work units from the length distribution and
+// spread them over the compute units; on the GPU, a persistent kernel with a
+// fixed grid follows the plan. The rule implemented here:
+//
+//  * tiles in order (request, kv head, query tile); a tile's extent is the
+//    number of keys its last row may see, and it costs max(1, ceil(extent /
+//    tile_kv)) blocks;
+//  * the N blocks are split into equal contiguous ranges of quota = ceil(N / W)
+//    blocks, one per worker;
+//  * a segment is one tile's share of one worker's range; a tile cut into
+//    several segments writes fp32 partial states to consecutive slots (in key
+//    order) and is merged afterwards.
+//
+// The planner writes straight into the caller's host workspace and allocates
+// nothing.
+#include "plan.h"
+
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+
+namespace abp {
+
+namespace {
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+inline int64_t align4(int64_t x) { return (x + 3) & ~int64_t(3); }
+
+constexpr int32_t kMaxKvLen = 1 << 24;
+
+}  // namespace
+
+int check_params(int kind, const abp_params* p, Config* cfg, std::string* err) {
+  if (!p || !cfg) {
+    *err = "params is NULL";
+    return ABP_ERR_INVALID_ARG;
+  }
+  if (kind != ABP_KIND_DECODE && kind != ABP_KIND_APPEND) {
+    *err = "kind must be ABP_KIND_DECODE or ABP_KIND_APPEND";
+    return ABP_ERR_INVALID_ARG;
+  }
+  if (p->num_qo_heads < 1 || p->num_kv_heads < 1) {
+    *err = "head counts must be >= 1";
+    return ABP_ERR_INVALID_ARG;
+  }
+  if (p->num_qo_heads % p->num_kv_heads != 0) {
+    *err = "num_qo_heads must be a multiple of num_kv_heads";
+    return ABP_ERR_INVALID_ARG;
+  }
+  const int32_t g = p->num_qo_heads / p->num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16) {
+    *err = "group size num_qo_heads/num_kv_heads must be 1, 2, 4, 8 or 16";
+    return ABP_ERR_UNSUPPORTED;
+  }
+  if (p->head_dim != 128) {
+    *err = "only head_dim 128 is built";
+    return ABP_ERR_UNSUPPORTED;
+  }
+  if (p->page_size < 1) {
+    *err = "page_size must be >= 1";
+    return ABP_ERR_INVALID_ARG;
+  }
+  if (p->qkv_dtype != ABP_F16 && p->qkv_dtype != ABP_BF16) {
+    *err = "qkv_dtype must be ABP_F16 or ABP_BF16";
+    return ABP_ERR_UNSUPPORTED;
+  }
+  if (p->out_dtype != ABP_F16 && p->out_dtype != ABP_BF16 && p->out_dtype != ABP_F32) {
+    *err = "out_dtype must be ABP_F16, ABP_BF16 or ABP_F32";
+    return ABP_ERR_UNSUPPORTED;
+  }
+  if (p->rope != 0 && p->rope != 1) {
+    *err = "rope must be 0 or 1";
+    return ABP_ERR_INVALID_ARG;
+  }
+  if (p->rope == 1 && !(p->rope_theta > 1.f)) {
+    *err = "rope_theta must be > 1";
+    return ABP_ERR_INVALID_ARG;
+  }
+  if (p->causal != 0 && p->causal != 1) {
+    *err = "causal must be 0 or 1";
+    return ABP_ERR_INVALID_ARG;
+  }
+  cfg->kind = kind;
+  cfg->hq = p->num_qo_heads;
+  cfg->hkv = p->num_kv_heads;
+  cfg->group = g;
+  cfg->head_dim = p->head_dim;
+  cfg->page_size = p->page_size;
+  cfg->qkv_dtype = p->qkv_dtype;
+  cfg->out_dtype = p->out_dtype;
+  cfg->sm_scale = p->sm_scale > 0.f ? p->sm_scale : (float)(1.0 / sqrt((double)p->head_dim));
+  cfg->causal = kind == ABP_KIND_APPEND ? p->causal : 0;
+  cfg->rope = p->rope;
+  cfg->rope_theta = p->rope_theta;
+  return ABP_OK;
+}
+
+int make_layout_caps(const Config& cfg, int64_t max_tiles, int32_t workers, Layout* out,
+                     std::string* err) {
+  if (max_tiles < 0 || workers < 1) {
+    *err = "capacities must be >= 0 and num_workers >= 1";
+    return ABP_ERR_INVALID_ARG;
+  }
+  Layout L;
+  L.workers = workers;
+  if (cfg.kind == ABP_KIND_DECODE) {
+    L.tile_q = 1;
+    L.tile_kv = kDecodeTileKv;
+    L.rows = cfg.group;
+  } else {
+    L.tile_q = kAppendRows / cfg.group;
+    L.tile_kv = kAppendTileKv;
+    L.rows = kAppendRows;
+  }
+  const int64_t max_segs = max_tiles + workers - 1;
+  // a tile cut k >= 2 times uses k slots and k - 1 of the W - 1 inner worker boundaries
+  const int64_t max_partials = std::min<int64_t>(max_segs, 2 * int64_t(workers - 1));
+  const int64_t max_merges = std::min<int64_t>(max_tiles, workers - 1);
+  if (max_segs > (int64_t(1) << 28)) {
+    *err = "capacities too large";
+    return ABP_ERR_INVALID_ARG;
+  }
+  L.max_tiles = (int32_t)max_tiles;
+  L.max_segs = (int32_t)max_segs;
+  L.max_partials = (int32_t)max_partials;
+  L.max_merges = (int32_t)max_merges;
+  int64_t off = HEADER_INTS;
+  L.off_wseg = off;
+  off += align4(workers + 1);
+  L.off_seg = off;
+  off += 4 * max_segs;
+  L.off_tile = off;
+  off += 4 * max_tiles;
+  L.off_merge = off;
+  off += 4 * max_merges;
+  L.off_rope = off;
+  off += 2 * kMaxRopePairs;
+  L.plan_ints = off;
+  L.plan_bytes = uint64_t(off) * 4;
+  L.partial_offset = (L.plan_bytes + 255) & ~uint64_t(255);
+  L.partial_bytes = uint64_t(max_partials) * L.rows * (cfg.head_dim + 1) * 4;
+  L.dev_bytes = L.partial_offset + ((L.partial_bytes + 255) & ~uint64_t(255));
+  *out = L;
+  return ABP_OK;
+}
+
+int make_layout(const Config& cfg, int32_t max_batch, int32_t max_qo_tokens, int32_t workers,
+                Layout* out, std::string* err) {
+  if (max_batch < 0 || workers < 1 || (cfg.kind == ABP_KIND_APPEND && max_qo_tokens < 0)) {
+    *err = "max_batch and max_qo_tokens must be >= 0 and num_workers >= 1";
+    return ABP_ERR_INVALID_ARG;
+  }
+  int64_t max_tiles;
+  if (cfg.kind == ABP_KIND_DECODE) {
+    max_tiles = int64_t(max_batch) * cfg.hkv;
+  } else {
+    // sum_b ceil(qo_b / tile_q) <= sum_qo / tile_q + batch
+    const int64_t tile_q = kAppendRows / cfg.group;
+    max_tiles = (ceil_div(max_qo_tokens, tile_q) + max_batch) * int64_t(cfg.hkv);
+  }
+  return make_layout_caps(cfg, max_tiles, workers, out, err);
+}
+
+uint64_t fingerprint(const Config& c, const Layout& L) {
+  uint64_t h = 1469598103934665603ull;
+  auto mix = [&h](uint64_t v) {
+    for (int i = 0; i < 8; ++i) {
+      h ^= (v >> (8 * i)) & 0xff;
+      h *= 1099511628211ull;
+    }
+  };
+  uint32_t scale_bits, theta_bits;
+  memcpy(&scale_bits, &c.sm_scale, 4);
+  memcpy(&theta_bits, &c.rope_theta, 4);
+  const int64_t vals[] = {c.kind,      c.hq,          c.hkv,          c.head_dim,   c.page_size,
+                          c.qkv_dtype, c.out_dtype,   scale_bits,     c.causal,     c.rope,
+                          theta_bits,  L.workers,     L.max_tiles,    L.max_segs,   L.max_partials,
+                          L.max_merges, L.tile_q,     L.tile_kv,      L.rows,       L.plan_ints,
+                          (int64_t)L.partial_offset};
+  for (int64_t v : vals) mix((uint64_t)v);
+  return h;
+}
+
+int plan_compute(const Config& cfg, const Layout& L, int32_t batch, const int32_t* qo_indptr,
+                 const int32_t* kv_indptr, const int32_t* lpl, int32_t* blob, abp_plan* plan,
+                 std::string* err) {
+  const bool append = cfg.kind == ABP_KIND_APPEND;
+  if (batch < 0) {
+    *err = "batch must be >= 0";
+    return ABP_ERR_INVALID_ARG;
+  }
+  if (!blob || !plan || (batch > 0 && (!kv_indptr || !lpl)) || (append && !qo_indptr)) {
+    *err = "NULL array";
+    return ABP_ERR_INVALID_ARG;
+  }
+  if (!kv_indptr || kv_indptr[0] != 0) {
+    *err = "kv_indptr[0] must be 0";
+    return ABP_ERR_INVALID_ARG;
+  }
+  if (append && qo_indptr[0] != 0) {
+    *err = "qo_indptr[0] must be 0";
+    return ABP_ERR_INVALID_ARG;
+  }
+  const int32_t P = cfg.page_size;
+  const int32_t Tq = L.tile_q, Tk = L.tile_kv, W = L.workers;
+
+  // validation and the block count N (pass 1)
+  int64_t N = 0, T = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t n = int64_t(kv_indptr[b + 1]) - kv_indptr[b];
+    if (n < 0) {
+      *err = "kv_indptr must be non-decreasing";
+      return ABP_ERR_INVALID_ARG;
+    }
+    int64_t kv_len = 0;
+    if (n > 0) {
+      if (lpl[b] < 1 || lpl[b] > P) {
+        *err = "kv_last_page_len must lie in [1, page_size] for a request with pages";
+        return ABP_ERR_INVALID_ARG;
+      }
+      kv_len = (n - 1) * P + lpl[b];
+    }
+    if (kv_len >= kMaxKvLen) {
+      *err = "kv_len must be < 2^24";
+      return ABP_ERR_INVALID_ARG;
+    }
+    int64_t qo_len = 1, nqt = 1;
+    if (append) {
+      qo_len = int64_t(qo_indptr[b + 1]) - qo_indptr[b];
+      if (qo_len < 0) {
+        *err = "qo_indptr must be non-decreasing";
+        return ABP_ERR_INVALID_ARG;
+      }
+      if (cfg.causal && qo_len > kv_len) {
+        *err = "causal append needs qo_len <= kv_len for every request";
+        return ABP_ERR_INVALID_ARG;
+      }
+      nqt = ceil_div(qo_len, Tq);
+    }
+    for (int64_t qt = 0; qt < nqt; ++qt) {
+      const int64_t e = cfg.causal ? kv_len - qo_len + std::min((qt + 1) * Tq, qo_len) : kv_len;
+      N += int64_t(cfg.hkv) * std::max<int64_t>(1, ceil_div(e, Tk));
+    }
+    T += nqt * cfg.hkv;
+  }
+  if (T > L.max_tiles) {
+    *err = "batch exceeds the workspace capacities (max_batch / max_qo_tokens)";
+    return ABP_ERR_WORKSPACE_TOO_SMALL;
+  }
+  const int64_t quota = N > 0 ? ceil_div(N, W) : 1;
+
+  memset(blob, 0, sizeof(int32_t) * size_t(L.plan_ints));
+  int32_t* wseg = blob + L.off_wseg;
+  int32_t* seg = blob + L.off_seg;
+  int32_t* tile = blob + L.off_tile;
+  int32_t* mrg = blob + L.off_merge;
+
+  // tiles, segments, partial slots, merge list (pass 2)
+  int64_t t = 0, s = 0, g0 = 0, slot = 0, m = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t n = int64_t(kv_indptr[b + 1]) - kv_indptr[b];
+    const int64_t kv_len = n > 0 ? (n - 1) * P + lpl[b] : 0;
+    const int64_t qo_len = append ? int64_t(qo_indptr[b + 1]) - qo_indptr[b] : 1;
+    const int64_t nqt = append ? ceil_div(qo_len, Tq) : 1;
+    for (int32_t h = 0; h < cfg.hkv; ++h) {
+      for (int64_t qt = 0; qt < nqt; ++qt, ++t) {
+        const int64_t e = cfg.causal ? kv_len - qo_len + std::min((qt + 1) * Tq, qo_len) : kv_len;
+        const int64_t g1 = g0 + std::max<int64_t>(1, ceil_div(e, Tk));
+        const int64_t w_first = g0 / quota, w_last = (g1 - 1) / quota;
+        const int64_t nseg = w_last - w_first + 1;
+        int32_t* tr = tile + 4 * t;
+        tr[0] = b;
+        tr[1] = h;
+        tr[2] = (int32_t)qt;
+        tr[3] = nseg > 1 ? (int32_t)slot : -1;
+        if (nseg > 1) {
+          int32_t* mr = mrg + 4 * m++;
+          mr[0] = (int32_t)t;
+          mr[1] = (int32_t)slot;
+          mr[2] = (int32_t)nseg;
+          mr[3] = 0;
+        }
+        for (int64_t w = w_first; w <= w_last; ++w, ++s) {
+          const int64_t lo = std::max(g0, w * quota), hi = std::min(g1, (w + 1) * quota);
+          int32_t* sr = seg + 4 * s;
+          sr[0] = (int32_t)t;
+          sr[1] = (int32_t)((lo - g0) * Tk);
+          sr[2] = (int32_t)std::min((hi - g0) * Tk, e);
+          sr[3] = nseg > 1 ? (int32_t)slot++ : -1;
+          wseg[w + 1] += 1;
+        }
+        g0 = g1;
+      }
+    }
+  }
+  for (int32_t w = 0; w < W; ++w) wseg[w + 1] += wseg[w];
+
+  // RoPE frequencies in revolutions per position, as fp32 hi + lo
+  float* rope = reinterpret_cast<float*>(blob + L.off_rope);
+  const int half = cfg.head_dim / 2;
+  for (int j = 0; j < kMaxRopePairs; ++j) {
+    double f = 0.0;
+    if (cfg.rope && j < half)
+      f = pow((double)cfg.rope_theta, -2.0 * j / cfg.head_dim) / (2.0 * M_PI);
+    const float hi = (float)f;
+    rope[2 * j] = hi;
+    rope[2 * j + 1] = (float)(f - (double)hi);
+  }
+
+  blob[H_MAGIC] = kMagic;
+  blob[H_KIND] = cfg.kind;
+  blob[H_BATCH] = batch;
+  blob[H_WORKERS] = W;
+  blob[H_NUM_TILES] = (int32_t)T;
+  blob[H_NUM_SEGS] = (int32_t)s;
+  blob[H_NUM_PARTIALS] = (int32_t)slot;
+  blob[H_NUM_MERGES] = (int32_t)m;
+  blob[H_TILE_Q] = Tq;
+  blob[H_TILE_KV] = Tk;
+  blob[H_ROWS] = L.rows;
+  blob[H_GROUP] = cfg.group;
+  blob[H_NUM_KV_HEADS] = cfg.hkv;
+  blob[H_PAGE_SIZE] = P;
+  blob[H_NUM_BLOCKS] = (int32_t)std::min<int64_t>(N, INT32_MAX);
+  blob[H_QUOTA] = (int32_t)std::min<int64_t>(quota, INT32_MAX);
+  blob[H_OFF_WSEG] = (int32_t)L.off_wseg;
+  blob[H_OFF_SEG] = (int32_t)L.off_seg;
+  blob[H_OFF_TILE] = (int32_t)L.off_tile;
+  blob[H_OFF_MERGE] = (int32_t)L.off_merge;
+  blob[H_OFF_ROPE] = (int32_t)L.off_rope;
+  blob[H_MAX_TILES] = L.max_tiles;
+  blob[H_MAX_SEGS] = L.max_segs;
+  blob[H_MAX_PARTIALS] = L.max_partials;
+  blob[H_CAUSAL] = cfg.causal;
+
+  plan->kind = cfg.kind;
+  plan->batch = batch;
+  plan->num_workers = W;
+  plan->tile_q = Tq;
+  plan->tile_kv = Tk;
+  plan->rows_per_tile = L.rows;
+  plan->num_tiles = (int32_t)T;
+  plan->num_segments = (int32_t)s;
+  plan->num_partials = (int32_t)slot;
+  plan->num_merges = (int32_t)m;
+  plan->max_tiles = L.max_tiles;
+  plan->max_segments = L.max_segs;
+  plan->max_partials = L.max_partials;
+  plan->reserved = 0;
+  plan->fingerprint = fingerprint(cfg, L);
+  plan->plan_bytes = L.plan_bytes;
+  plan->partial_offset = L.partial_offset;
+  plan->dev_bytes = L.dev_bytes;
+  return ABP_OK;
+}
+
+}  // namespace abp

@@ -1,0 +1,218 @@
+/*
+ * abp.h -- C ABI of libabp: attention over a paged block-sparse-row (BSR) KV
+ * cache on AMD Instinct MI355X (gfx950).
+ *
+ * Operations and where they are defined
+ * -------------------------------------
+ *  - The KV cache is a block-sparse-row matrix with a configurable block (page)
+ *    size; one kernel serves contiguous and paged layouts (FlashInfer paper
+ *    summary, "图谱动态｜学苑周刊 NO.266", section 统一的 KV 缓存存储格式).
+ *  - Work is planned on the CPU from the length distribution and then run on
+ *    the GPU by a persistent kernel with a fixed grid and a preallocated
+ *    workspace, so the run can be captured in a graph (same page, section
+ *    动态负载均衡调度).
+ *  - Decode, append and prefill over paged and ragged caches, cascade attention
+ *    for shared prefixes, and RoPE fused into attention (README translation on
+ *    gittoolsai.com, section 核心功能 / 注意力机制内核; paper summary, section
+ *    可定制的注意力模板 and 高级功能).
+ *  - The single-request decode call of the README example (section 基本用法)
+ *    is abp_decode_* with batch 1: q [num_qo_heads, head_dim], K/V
+ *    [kv_len, num_kv_heads, head_dim] as one page of size kv_len.
+ *
+ * Attention computed (exactly, up to float rounding):
+ *     s_t = sm_scale * <q, k_t>,  lse = ln sum_t exp(s_t),  o = sum_t exp(s_t - lse) v_t
+ * over the keys t a query may see; with no visible key, o = 0 and lse = -inf.
+ * lse is the natural log of the scaled logits.
+ *
+ * Layouts (all row-major, "NHD" inside a page)
+ * --------------------------------------------
+ *  q (decode)     [batch, num_qo_heads, head_dim]           qkv_dtype
+ *  q (append)     [total_qo_tokens, num_qo_heads, head_dim] qkv_dtype, ragged by qo_indptr
+ *  k_pages,
+ *  v_pages        [num_pages, page_size, num_kv_heads, head_dim] qkv_dtype (two pools)
+ *  kv_indptr      int32 [batch + 1]; request b owns page slots [kv_indptr[b], kv_indptr[b+1])
+ *  kv_indices     int32 [kv_indptr[batch]]; physical page id of each slot, in logical order
+ *  kv_last_page_len int32 [batch]; valid tokens in the last page, in [1, page_size]
+ *                 (ignored for a request with no pages, whose kv_len is 0)
+ *  kv_len[b] = (kv_indptr[b+1] - kv_indptr[b] - 1) * page_size + kv_last_page_len[b]
+ *  o              same shape as q, out_dtype; lse float32 [rows of q, num_qo_heads]
+ *  GQA: qo head h reads kv head h / (num_qo_heads / num_kv_heads).
+ *  Causal append: query i (0-based) of a request with qo_len queries sees keys
+ *  t <= kv_len - qo_len + i (aligned to the end of the KV).
+ *  RoPE (params.rope = 1): LLaMA rotate-half; pair (j, j + head_dim/2) of q and k
+ *  is turned by pos * rope_theta^(-2j/head_dim). Key t of request b sits at
+ *  kv_pos_offset[b] + t (default 0). A decode query sits at q_pos[b] (default
+ *  kv_len - 1); append query i at q_pos[token] (default kv_len - qo_len + i).
+ *  K is stored un-rotated; v is never rotated.
+ *
+ * Supported: head_dim 128; fp16 or bf16 q/k/v; num_qo_heads / num_kv_heads in
+ * {1, 2, 4, 8, 16}; page_size >= 1; kv_len < 2^24; batch >= 0.
+ *
+ * Ownership and lifetime
+ * ----------------------
+ * The caller owns every buffer: tensors, index arrays, the host workspace (use
+ * pinned memory for an asynchronous upload), the device workspace and the
+ * abp_plan struct. The library allocates no memory in any call; its only state
+ * is a per-device compute-unit count and a thread-local error string.
+ * *_plan enqueues one host->device copy of the plan on `stream`; the host
+ * workspace must not be modified until that copy has completed.
+ *
+ * Errors
+ * ------
+ * Every entry point returns an abp_status (0 = ABP_OK); no C++ exception
+ * crosses this boundary. abp_last_error() gives a message for the calling
+ * thread's last failure. *_plan validates the host index arrays fully; *_run
+ * checks that its params match the plan (fingerprint) and that the device
+ * workspace is large enough. Device-side index arrays are trusted: a page id
+ * outside the pools is undefined behaviour.
+ *
+ * Graphs
+ * ------
+ * *_run and abp_merge_state(s) only enqueue kernels on `stream` (fixed grids,
+ * no allocation, no copies), so they can be captured in a hipGraph and
+ * replayed after a re-plan with the same capacities and worker count. *_plan
+ * must not be called during capture.
+ */
+#ifndef ABP_H_
+#define ABP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* abp_stream_t; /* a hipStream_t; NULL = default stream */
+
+typedef enum abp_status {
+  ABP_OK = 0,
+  ABP_ERR_INVALID_ARG = -1,         /* bad pointer, size or index array */
+  ABP_ERR_UNSUPPORTED = -2,         /* head_dim, dtype or group size not built */
+  ABP_ERR_WORKSPACE_TOO_SMALL = -3, /* host or device workspace below the query */
+  ABP_ERR_PLAN_MISMATCH = -4,       /* run params differ from the planned ones */
+  ABP_ERR_HIP = -5                  /* a HIP runtime call failed (e.g. no device) */
+} abp_status;
+
+typedef enum abp_dtype { ABP_F16 = 0, ABP_BF16 = 1, ABP_F32 = 2 } abp_dtype;
+typedef enum abp_kind { ABP_KIND_DECODE = 0, ABP_KIND_APPEND = 1 } abp_kind;
+
+typedef struct abp_params {
+  int32_t num_qo_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;   /* 128 */
+  int32_t page_size;  /* >= 1 */
+  int32_t qkv_dtype;  /* ABP_F16 or ABP_BF16 */
+  int32_t out_dtype;  /* ABP_F16, ABP_BF16 or ABP_F32 */
+  float sm_scale;     /* <= 0 selects 1/sqrt(head_dim) */
+  int32_t causal;     /* append only: 1 = causal mask aligned to the end of the KV */
+  int32_t rope;       /* 0 = none, 1 = LLaMA rotate-half RoPE on q and k at load */
+  float rope_theta;   /* RoPE base, e.g. 500000 */
+} abp_params;
+
+/* Result of a plan: plain data, copied by value. Fields are informative; only
+ * the library interprets them. */
+typedef struct abp_plan {
+  int32_t kind;          /* abp_kind */
+  int32_t batch;
+  int32_t num_workers;   /* grid size of the persistent kernel */
+  int32_t tile_q;        /* query tokens per tile (1 for decode) */
+  int32_t tile_kv;       /* keys per work block */
+  int32_t rows_per_tile; /* tile_q * group */
+  int32_t num_tiles;
+  int32_t num_segments;
+  int32_t num_partials;  /* partial (o, lse) slots used by split tiles */
+  int32_t num_merges;    /* tiles merged after the main kernel */
+  int32_t max_tiles;     /* capacities fixed by (max_batch, max_qo_tokens, workers) */
+  int32_t max_segments;
+  int32_t max_partials;
+  int32_t reserved;
+  uint64_t fingerprint;  /* hash of kind, params, capacities and tiling */
+  uint64_t plan_bytes;   /* bytes uploaded from the host workspace */
+  uint64_t partial_offset; /* byte offset of the partial-state region in dev_ws */
+  uint64_t dev_bytes;    /* device workspace bytes this layout needs */
+} abp_plan;
+
+/* Static text for a status code. */
+const char* abp_status_string(int status);
+
+/* Message of the calling thread's last failing call ("" if none). */
+const char* abp_last_error(void);
+
+/* Number of compute units of HIP device `device` (cached). */
+int abp_device_num_cus(int device, int32_t* num_cus);
+
+/* Workspace sizes for plans of `kind` with at most `max_batch` requests,
+ * `max_qo_tokens` query tokens (append; ignored for decode) and `num_workers`
+ * workers (<= 0: 2 per compute unit of the current device for decode, 1 for
+ * append). Pure host code except the compute-unit query for num_workers <= 0. */
+int abp_workspace_size(int kind, const abp_params* params, int32_t max_batch,
+                       int32_t max_qo_tokens, int32_t num_workers, size_t* host_bytes,
+                       size_t* dev_bytes);
+
+/* The planner alone (host only, no HIP call): validate the index arrays and
+ * write the plan into `host_ws` (>= host_bytes of abp_workspace_size).
+ * qo_indptr_h is read for ABP_KIND_APPEND only. num_workers must be > 0.
+ * Work is cut into blocks of tile_kv keys and spread over the workers in equal
+ * contiguous ranges (Stream-K), paper summary section 动态负载均衡调度. */
+int abp_plan_host(int kind, const abp_params* params, int32_t batch, const int32_t* qo_indptr_h,
+                  const int32_t* kv_indptr_h, const int32_t* kv_last_page_len_h,
+                  int32_t max_batch, int32_t max_qo_tokens, int32_t num_workers, void* host_ws,
+                  size_t host_bytes, abp_plan* plan);
+
+/* Decode plan: abp_plan_host for ABP_KIND_DECODE, then one hipMemcpyAsync of the
+ * plan from host_ws to dev_ws on `stream`. */
+int abp_decode_plan(const abp_params* params, int32_t batch, const int32_t* kv_indptr_h,
+                    const int32_t* kv_last_page_len_h, int32_t max_batch, int32_t num_workers,
+                    void* host_ws, size_t host_bytes, void* dev_ws, size_t dev_bytes,
+                    abp_stream_t stream, abp_plan* plan);
+
+/* Batch decode over the paged cache (one query token per request).
+ * q [batch, Hq, d]; o [batch, Hq, d] (out_dtype); lse [batch, Hq] float32 or NULL.
+ * q_pos_d [batch] and kv_pos_offset_d [batch] are read only with RoPE (NULL =
+ * defaults). Launches the persistent decode kernel (grid = num_workers) and the
+ * merge of split tiles. */
+int abp_decode_run(const abp_plan* plan, const abp_params* params, const void* q,
+                   const void* k_pages, const void* v_pages, const int32_t* kv_indptr_d,
+                   const int32_t* kv_indices_d, const int32_t* kv_last_page_len_d,
+                   const int32_t* q_pos_d, const int32_t* kv_pos_offset_d, void* o, float* lse,
+                   void* dev_ws, size_t dev_bytes, abp_stream_t stream);
+
+/* Append / prefill plan for ragged queries (qo_indptr_h [batch + 1]). */
+int abp_append_plan(const abp_params* params, int32_t batch, const int32_t* qo_indptr_h,
+                    const int32_t* kv_indptr_h, const int32_t* kv_last_page_len_h,
+                    int32_t max_batch, int32_t max_qo_tokens, int32_t num_workers,
+                    void* host_ws, size_t host_bytes, void* dev_ws, size_t dev_bytes,
+                    abp_stream_t stream, abp_plan* plan);
+
+/* Append / prefill attention (MFMA): q [total_qo, Hq, d] ragged by qo_indptr_d;
+ * o [total_qo, Hq, d]; lse [total_qo, Hq] or NULL. Causal per params.causal.
+ * q_pos_d [total_qo] and kv_pos_offset_d [batch] are read only with RoPE. */
+int abp_append_run(const abp_plan* plan, const abp_params* params, const void* q,
+                   const void* k_pages, const void* v_pages, const int32_t* qo_indptr_d,
+                   const int32_t* kv_indptr_d, const int32_t* kv_indices_d,
+                   const int32_t* kv_last_page_len_d, const int32_t* q_pos_d,
+                   const int32_t* kv_pos_offset_d, void* o, float* lse, void* dev_ws,
+                   size_t dev_bytes, abp_stream_t stream);
+
+/* Merge two attention states over disjoint key sets (cascade: prefix and suffix).
+ * o_a, o_b [num_rows, head_dim] in in_dtype; lse_a, lse_b [num_rows] float32;
+ * writes o_out [num_rows, head_dim] in out_dtype and lse_out (may be NULL).
+ * lse = ln(e^lse_a + e^lse_b); o = e^(lse_a - lse) o_a + e^(lse_b - lse) o_b;
+ * two -inf states give (0, -inf). num_rows counts (token, head) pairs. */
+int abp_merge_state(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
+                    void* o_out, float* lse_out, int64_t num_rows, int32_t head_dim,
+                    int in_dtype, int out_dtype, abp_stream_t stream);
+
+/* Merge `num_states` states stacked on a leading axis: o_in [num_states,
+ * num_rows, head_dim] (in_dtype), lse_in [num_states, num_rows] float32 ->
+ * o_out [num_rows, head_dim] (out_dtype), lse_out [num_rows] (may be NULL). */
+int abp_merge_states(const void* o_in, const float* lse_in, int32_t num_states,
+                     int64_t num_rows, int32_t head_dim, int in_dtype, int out_dtype,
+                     void* o_out, float* lse_out, abp_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ABP_H_ */

@@ -1,0 +1,167 @@
+"""C-ABI checks that need no GPU: exports, status codes, validation, and the
+C++ planner against the reference planner (bit-exact)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import attention_bsr_paged_amd as abp
+from oracle.plan_ref import KIND_APPEND, KIND_DECODE, plan_ref
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "abp.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(abp_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in abp.h but not exported"
+    assert set(names) == set(abp.EXPORTED_SYMBOLS)
+
+
+def test_status_strings(lib):
+    assert abp.abp_status_string(0) == "ok"
+    for s in (-1, -2, -3, -4, -5):
+        assert abp.abp_status_string(s) not in ("ok", "unknown status")
+    assert abp.abp_status_string(42) == "unknown status"
+
+
+def P(**kw):
+    base = dict(num_qo_heads=32, num_kv_heads=8, head_dim=128, page_size=16, dtype="bf16")
+    base.update(kw)
+    return abp.make_params(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=64), abp.ABP_ERR_UNSUPPORTED),
+    (dict(num_qo_heads=30), abp.ABP_ERR_INVALID_ARG),
+    (dict(num_qo_heads=24), abp.ABP_ERR_UNSUPPORTED),      # group 3
+    (dict(page_size=0), abp.ABP_ERR_INVALID_ARG),
+    (dict(num_qo_heads=32, num_kv_heads=2), abp.ABP_ERR_UNSUPPORTED),  # decode group 16
+])
+def test_param_validation(lib, kw, status):
+    with pytest.raises(abp.AbpError) as e:
+        abp.abp_workspace_size(abp.ABP_KIND_DECODE, P(**kw), 4, 0, 8)
+    assert e.value.status == status
+
+
+def test_bad_dtype(lib):
+    p = P()
+    p.qkv_dtype = abp.ABP_F32
+    with pytest.raises(abp.AbpError) as e:
+        abp.abp_workspace_size(abp.ABP_KIND_DECODE, p, 4, 0, 8)
+    assert e.value.status == abp.ABP_ERR_UNSUPPORTED
+
+
+def _ws(kind, p, max_batch, max_qo, W):
+    h, _ = abp.abp_workspace_size(kind, p, max_batch, max_qo, W)
+    return np.zeros(h, np.uint8)
+
+
+@pytest.mark.parametrize("indptr,lpl,status", [
+    ([0, 2, 1], [1, 1], abp.ABP_ERR_INVALID_ARG),
+    ([1, 2, 3], [1, 1], abp.ABP_ERR_INVALID_ARG),
+    ([0, 1, 2], [0, 1], abp.ABP_ERR_INVALID_ARG),
+    ([0, 1, 2], [1, 17], abp.ABP_ERR_INVALID_ARG),
+])
+def test_index_validation(lib, indptr, lpl, status):
+    p = P()
+    with pytest.raises(abp.AbpError) as e:
+        abp.abp_plan_host(abp.ABP_KIND_DECODE, p, 2, None, indptr, lpl, 2, 0, 8,
+                          _ws(0, p, 2, 0, 8))
+    assert e.value.status == status
+
+
+def test_workspace_and_capacity_errors(lib):
+    p = P()
+    ws = _ws(0, p, 2, 0, 8)
+    with pytest.raises(abp.AbpError) as e:        # batch above max_batch
+        abp.abp_plan_host(0, p, 3, None, [0, 1, 2, 3], [1, 1, 1], 2, 0, 8, ws)
+    assert e.value.status == abp.ABP_ERR_WORKSPACE_TOO_SMALL
+    with pytest.raises(abp.AbpError) as e:        # host workspace too small
+        abp.abp_plan_host(0, p, 2, None, [0, 1, 2], [1, 1], 2, 0, 8, ws[:64])
+    assert e.value.status == abp.ABP_ERR_WORKSPACE_TOO_SMALL
+    pa = P(causal=True)
+    wa = _ws(1, pa, 1, 8, 8)
+    with pytest.raises(abp.AbpError) as e:        # causal with qo_len > kv_len
+        abp.abp_plan_host(1, pa, 1, [0, 8], [0, 1], [4], 1, 8, 8, wa)
+    assert e.value.status == abp.ABP_ERR_INVALID_ARG
+    with pytest.raises(abp.AbpError) as e:        # more query tokens than planned for
+        abp.abp_plan_host(1, pa, 1, [0, 9], [0, 1], [16], 1, 8, 8, wa)
+    assert e.value.status == abp.ABP_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_run_rejects_mismatched_params_before_any_launch(lib):
+    """The fingerprint check fails on the host, so no device is touched."""
+    p = P()
+    ws = _ws(0, p, 2, 0, 8)
+    plan = abp.abp_plan_host(0, p, 2, None, [0, 1, 2], [3, 4], 2, 0, 8, ws)
+    other = P(page_size=32)
+    st_ = lib.abp_decode_run(ctypes.byref(plan), ctypes.byref(other), *([None] * 10), None, 0, None)
+    assert st_ == abp.ABP_ERR_PLAN_MISMATCH
+    plan.kind = abp.ABP_KIND_APPEND
+    st_ = lib.abp_decode_run(ctypes.byref(plan), ctypes.byref(p), *([None] * 10), None, 0, None)
+    assert st_ == abp.ABP_ERR_PLAN_MISMATCH
+
+
+def _compare(kind, p, B, qo_indptr, kv_indptr, lpl, W, G, max_qo=0):
+    ws = _ws(kind, p, B, max_qo, W)
+    plan = abp.abp_plan_host(kind, p, B, qo_indptr, kv_indptr, lpl, B, max_qo, W, ws)
+    got = abp.decode_plan_arrays(ws, plan)
+    if kind == KIND_DECODE:
+        ref = plan_ref(KIND_DECODE, B, kv_indptr, lpl, p.page_size, p.num_kv_heads, W, 64)
+    else:
+        ref = plan_ref(KIND_APPEND, B, kv_indptr, lpl, p.page_size, p.num_kv_heads, W, 64,
+                       qo_indptr=qo_indptr, tile_q=128 // G, causal=bool(p.causal))
+    for k, v in ref.items():
+        assert np.array_equal(got[k], v), k
+    assert plan.num_segments == len(ref["seg_tile"])
+    assert plan.num_merges == len(ref["merge_list"])
+
+
+@settings(max_examples=120, deadline=None)
+@given(st.data())
+def test_cpp_planner_matches_reference(data):
+    abp.load_library()
+    B = data.draw(st.integers(0, 12))
+    page = data.draw(st.sampled_from([1, 3, 16, 256]))
+    G = data.draw(st.sampled_from([1, 2, 4, 8]))
+    hkv = data.draw(st.integers(1, 3))
+    W = data.draw(st.integers(1, 70))
+    kv_len = data.draw(st.lists(st.integers(0, 3000), min_size=B, max_size=B))
+    npg = [-(-n // page) for n in kv_len]
+    indptr = np.concatenate([[0], np.cumsum(npg)]).astype(np.int32)
+    lpl = np.array([n - (k - 1) * page if k else 0 for n, k in zip(kv_len, npg)], np.int32)
+    if data.draw(st.booleans()):
+        p = P(num_qo_heads=hkv * G, num_kv_heads=hkv, page_size=page)
+        _compare(KIND_DECODE, p, B, None, indptr, lpl, W, G)
+    else:
+        causal = data.draw(st.booleans())
+        qo = [data.draw(st.integers(0, min(n, 300) if causal else 300)) for n in kv_len]
+        qo_indptr = np.concatenate([[0], np.cumsum(qo)]).astype(np.int32)
+        p = P(num_qo_heads=hkv * G, num_kv_heads=hkv, page_size=page, causal=causal)
+        _compare(KIND_APPEND, p, B, qo_indptr, indptr, lpl, W, G, max_qo=int(qo_indptr[-1]))
+
+
+@pytest.mark.parametrize("name", ["batch_decode", "skewed_decode"])
+def test_planner_on_named_decode_workloads(lib, name):
+    """The planner on the named workloads' page tables (lengths only, no values)."""
+    from attention_bsr_paged_amd import workloads as wl
+    rng = np.random.Generator(np.random.PCG64(1002 if name == "batch_decode" else 1003))
+    if name == "batch_decode":
+        kv_len = rng.integers(512, 4096, size=64, endpoint=True)
+    else:
+        rest = np.clip(np.rint(np.exp(rng.normal(np.log(512.0), 1.0, size=127))), 16, 16384)
+        kv_len = np.concatenate([[32768], rest]).astype(np.int64)
+    indptr, _, lpl = wl.page_table(kv_len, 16, np.arange(10 ** 6))
+    for W in (256, 512, 1024):
+        _compare(KIND_DECODE, P(), len(kv_len), None, indptr, lpl, W, 4)
