@@ -279,12 +279,10 @@ class _Planned:
         self.device = torch.device("cuda", torch.cuda.current_device()) if device is None \
             else torch.device(device)
         with torch.cuda.device(self.device):
-            if num_workers <= 0:
-                num_workers = (2 if self.kind == ABP_KIND_DECODE else 1) * \
-                    abp_device_num_cus(self.device.index or 0)
-            self.num_workers = int(num_workers)
+            # num_workers <= 0: the library picks one worker per resident workgroup slot
             hb, db = abp_workspace_size(self.kind, params, self.max_batch, self.max_qo_tokens,
-                                        self.num_workers)
+                                        num_workers)
+            self.num_workers = int(num_workers)
             self.host_ws = torch.empty(max(hb, 16), dtype=torch.uint8, pin_memory=True)
             self.dev_ws = torch.empty(max(db, 256), dtype=torch.uint8, device=self.device)
         self.plan_struct = None

@@ -44,14 +44,18 @@ int num_cus(int device, int32_t* out) {
   return ABP_OK;
 }
 
-int default_workers(int kind, int32_t* out) {
+// One worker per resident workgroup slot of the current device: compute units
+// times the workgroups of the chosen kernel that fit on one compute unit.
+int default_workers(const abp::Config& cfg, int32_t* out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   int32_t cus = 0;
   int st = num_cus(dev, &cus);
   if (st != ABP_OK) return st;
-  *out = kind == ABP_KIND_DECODE ? 2 * cus : cus;
+  int per_cu = cfg.kind == ABP_KIND_DECODE ? abp::decode_blocks_per_cu(cfg)
+                                           : abp::append_blocks_per_cu(cfg);
+  *out = cus * (per_cu > 0 ? per_cu : 1);
   return ABP_OK;
 }
 
@@ -74,7 +78,7 @@ int resolve_layout(int kind, const abp_params* params, int32_t max_batch, int32_
   if (kind == ABP_KIND_DECODE && cfg->group > 8)
     return fail(ABP_ERR_UNSUPPORTED, "decode supports group sizes 1, 2, 4 and 8");
   if (workers <= 0) {
-    st = default_workers(kind, &workers);
+    st = default_workers(*cfg, &workers);
     if (st != ABP_OK) return st;
   }
   st = abp::make_layout(*cfg, max_batch, max_qo, workers, L, &err);

@@ -8,4 +8,6 @@ hipError_t launch_append(const Config&, const AttnArgs&, hipStream_t) {
   return hipErrorNotSupported;
 }
 
+int append_blocks_per_cu(const Config&) { return 1; }
+
 }  // namespace abp

@@ -17,6 +17,14 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
+// Read-only arrays whose loads at wave-uniform addresses should go through the
+// scalar unit (plan records, page tables). Only loads are done through it.
+#define ABP_CONST_AS __attribute__((address_space(4)))
+template <typename T>
+__device__ __forceinline__ const ABP_CONST_AS T* const_as(const T* p) {
+  return (const ABP_CONST_AS T*)(p);
+}
+
 struct BF16 {};  // storage tags
 struct F16 {};
 
@@ -100,13 +108,16 @@ enum Dpp : int {
   kDppRor8 = 0x128,       // lane i <- (i + 8) mod 16  (= xor 8)
 };
 
+// Every lane of the patterns used here has a valid source lane, so the "old"
+// operand is never selected (mov_dpp leaves it undefined, which lets the
+// compiler fold the move into the consuming add as a DPP operand).
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, true));
 }
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xf, 0xf, false);
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xf, 0xf, true);
 }
 
 // sum over the 16 lanes of a row; every lane of the row gets the total

@@ -5,7 +5,8 @@
 // (paper summary "图谱动态｜学苑周刊 NO.266", section 统一的 KV 缓存存储格式;
 // single and batch decode kernels of "FlashInfer 源码级解读"). Decode reads
 // every K/V byte once and does ~4 flop per byte at a GQA group of 4, so it is
-// bound by HBM bandwidth; the design goal is to keep enough bytes in flight.
+// bound by HBM bandwidth; the design goal is to keep enough bytes in flight
+// while spending few instructions per byte.
 //
 // Work split: the host planner cuts the (request, kv head) tiles into segments
 // of whole 64-key blocks spread evenly over a fixed grid of workers (section
@@ -15,18 +16,24 @@
 // Inside a segment the 4 waves take 16-token chunks round-robin. In a chunk,
 // lane (grp = lane / 16, sub = lane % 16) holds head-dim elements
 // [8 sub, 8 sub + 8) of tokens c + 4 i + grp for i = 0..3: each load
-// instruction reads 4 contiguous 256-byte head rows (coalesced 128-bit
-// lanes). All G query rows of the kv head (the GQA group) are kept in every
-// lane, so one K/V read serves the whole group:
-//   * q.k uses dot2 (bf16/fp16 pairs, fp32 accumulate) and a 16-lane DPP sum;
+// instruction reads 4 whole 256-byte head rows (coalesced 128-bit lanes). All
+// G query rows of the kv head (the GQA group) are kept in every lane, so one
+// K/V read serves the whole group:
+//   * q.k uses dot2 (bf16/fp16 pairs, fp32 accumulate) and 16-lane DPP sums,
+//     done step by step over all 4 G values so no DPP hazard stalls remain;
 //   * online softmax in fp32 with base-2 exponentials, one running max per
-//     (row, token group);
+//     (row, token group), rescaled lazily: the reference max only moves when a
+//     score exceeds it by more than 2^8 in probability, so most chunks skip the
+//     rescale of o (exact: the final normalisation uses the same reference);
 //   * p.v uses dot2 over token pairs: p of tokens (i, i+1) packed as a pair
 //     against V elements of the same two tokens repacked with v_perm.
-// Chunks are double-buffered in registers so the next chunk's loads are in
-// flight while the current one is computed. At the end of a segment the
-// states of the 4 token groups and 4 waves are merged, and the tile's rows
-// are written either as the final o / lse or as an fp32 partial state.
+// When the page size is a power of two and a multiple of 16, a 16-token chunk
+// never straddles a page: its page id is one scalar load (issued a chunk
+// ahead) and all K/V addresses are a uniform page base plus fixed per-lane
+// offsets. Other page sizes translate every token.
+// Chunks are double-buffered in registers. At the end of a segment the states
+// of the 4 token groups and 4 waves are merged, and the tile's rows are written
+// either as the final o / lse or as an fp32 partial state.
 #include "common.h"
 #include "kernels.h"
 #include "layout.h"
@@ -37,12 +44,13 @@ namespace {
 
 constexpr int kD = 128;
 constexpr int kWaves = 4;
-constexpr int kChunk = 16;           // tokens per wave step
-constexpr int kStep = kWaves * kChunk;
+constexpr int kSub = 16;             // tokens per sub-chunk (4 load instructions)
+constexpr float kRescaleLog2 = 8.f;  // lazy rescale threshold (log2 of the max p)
 
-struct KVRegs {
-  uint4 k[4];
-  uint4 v[4];
+template <int S>
+struct KVRegs {  // S sub-chunks of 16 tokens
+  uint4 k[4 * S];
+  uint4 v[4 * S];
 };
 
 __device__ __forceinline__ uint32_t word(const uint4& u, int j) {
@@ -85,25 +93,43 @@ __device__ __forceinline__ void store8_dt(void* base, int64_t off, const float v
   else store8<ABP_F16>(base, off, v);
 }
 
-template <typename T, int G, bool ROPE>
+template <int N>
+__device__ __forceinline__ void row16_sum_all(float* x) {
+#pragma unroll
+  for (int n = 0; n < N; ++n) x[n] += dpp<kDppXor1>(x[n]);
+#pragma unroll
+  for (int n = 0; n < N; ++n) x[n] += dpp<kDppXor2>(x[n]);
+#pragma unroll
+  for (int n = 0; n < N; ++n) x[n] += dpp<kDppHalfMirror>(x[n]);
+#pragma unroll
+  for (int n = 0; n < N; ++n) x[n] += dpp<kDppMirror>(x[n]);
+}
+
+template <typename T, int G, bool ROPE, bool FASTPAGE, int S>
 __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
-  const int32_t* plan = a.plan;
-  const int32_t* wseg = plan + plan[H_OFF_WSEG];
-  const int4* segs = reinterpret_cast<const int4*>(plan + plan[H_OFF_SEG]);
-  const int4* tiles = reinterpret_cast<const int4*>(plan + plan[H_OFF_TILE]);
+  constexpr int kChunk = kSub * S;       // tokens per wave per buffered chunk
+  constexpr int kStep = kWaves * kChunk;  // tokens per workgroup step
+  const ABP_CONST_AS int32_t* plan = const_as(a.plan);
+  const ABP_CONST_AS int32_t* wseg = plan + plan[H_OFF_WSEG];
+  const ABP_CONST_AS int32_t* segs = plan + plan[H_OFF_SEG];    // 4 ints per record
+  const ABP_CONST_AS int32_t* tiles = plan + plan[H_OFF_TILE];
+  const ABP_CONST_AS int32_t* kv_indptr = const_as(a.kv_indptr);
+  const ABP_CONST_AS int32_t* kv_indices = const_as(a.kv_indices);
   const int s_begin = wseg[blockIdx.x], s_end = wseg[blockIdx.x + 1];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = lane >> 4;
   const int sub = lane & 15;
   const bool hi_half = sub >= 8;
   const float cl2 = a.sm_scale_log2;
+  const float thr = kRescaleLog2 / cl2;  // threshold in raw score units
 
   const uint16_t* __restrict__ kp = static_cast<const uint16_t*>(a.k_pages);
   const uint16_t* __restrict__ vp = static_cast<const uint16_t*>(a.v_pages);
   const int P = a.page_size;
   const int shift = a.page_shift;
+  const int tstride = a.token_stride;
 
   __shared__ float s_o[kWaves][G][kD];
   __shared__ float s_m[kWaves][G];
@@ -111,7 +137,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
 
   float fhi[8], flo[8];
   if constexpr (ROPE) {
-    const float* rope = reinterpret_cast<const float*>(plan + plan[H_OFF_ROPE]);
+    const ABP_CONST_AS float* rope = (const ABP_CONST_AS float*)(plan + plan[H_OFF_ROPE]);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int j = (sub & 7) * 8 + e;
@@ -121,12 +147,11 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
   }
 
   for (int s = s_begin; s < s_end; ++s) {
-    const int4 sg = segs[s];
-    const int4 tl = tiles[sg.x];
-    const int b = tl.x, h = tl.y;
-    const int kv_begin = sg.y, kv_end = sg.z, slot = sg.w;
-    const int ip0 = a.kv_indptr[b];
-    const int64_t head_off = int64_t(h) * kD + sub * 8;
+    const int tile = segs[4 * s];
+    const int kv_begin = segs[4 * s + 1], kv_end = segs[4 * s + 2], slot = segs[4 * s + 3];
+    const int b = tiles[4 * tile], h = tiles[4 * tile + 1];
+    const int ip0 = kv_indptr[b];
+    const int head_off = h * kD + sub * 8;
 
     // ---- q of the G rows of this kv head: words of elements [8 sub, 8 sub + 8)
     uint4 qv[G];
@@ -135,10 +160,15 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
                            (int64_t(b) * a.num_qo_heads + int64_t(h) * G) * kD + sub * 8;
 #pragma unroll
       for (int g = 0; g < G; ++g) qv[g] = *reinterpret_cast<const uint4*>(qb + g * kD);
+      // Consume q here so its load is waited for before the chunk loop; else the
+      // loop's first use of q waits for every load in flight (the next chunk too).
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        asm volatile("" : "+v"(qv[g].x), "+v"(qv[g].y), "+v"(qv[g].z), "+v"(qv[g].w));
     }
     float kv_pos0 = 0.f;
     if constexpr (ROPE) {
-      const int n = a.kv_indptr[b + 1] - ip0;
+      const int n = kv_indptr[b + 1] - ip0;
       const int kv_len = n > 0 ? (n - 1) * P + a.kv_last_page_len[b] : 0;
       const int qpos = a.q_pos ? a.q_pos[b] : kv_len - 1;
       kv_pos0 = a.kv_pos_offset ? (float)a.kv_pos_offset[b] : 0.f;
@@ -155,65 +185,111 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
       for (int e = 0; e < 8; ++e) o[g][e] = 0.f;
     }
 
-    auto load_chunk = [&](KVRegs& X, int c) {
+    // per-lane byte offsets of the 4 token rows of a sub-chunk (fast path)
+    uint32_t lane_off[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = min(c + 4 * i + grp, kv_end - 1);
-        int page, off;
-        if (shift >= 0) {
-          page = tok >> shift;
-          off = tok & (P - 1);
-        } else {
-          page = tok / P;
-          off = tok - page * P;
-        }
-        const int64_t pid = a.kv_indices[ip0 + page];
-        const int64_t base = pid * a.page_stride + int64_t(off) * a.token_stride + head_off;
-        X.k[i] = *reinterpret_cast<const uint4*>(kp + base);
-        X.v[i] = *reinterpret_cast<const uint4*>(vp + base);
+    for (int i = 0; i < 4; ++i) lane_off[i] = uint32_t((4 * i + grp) * tstride + head_off) * 2u;
+
+    // fast path: one scalar page-table load per sub-chunk, issued a chunk ahead
+    // of its use. A sub-chunk that starts past kv_end re-reads the chunk's
+    // first sub-chunk (in bounds, cached, fully masked).
+    auto chunk_pids = [&](int c, int* pid) {
+#pragma unroll
+      for (int u = 0; u < S; ++u) {
+        const int cu = c + kSub * u < kv_end ? c + kSub * u : c;
+        pid[u] = kv_indices[ip0 + (cu >> shift)];
       }
     };
 
-    auto compute_chunk = [&](KVRegs& X, int c) {
+    auto load_chunk = [&](KVRegs<S>& X, int c, const int* pid) {
+#pragma unroll
+      for (int u = 0; u < S; ++u) {
+        if constexpr (FASTPAGE) {
+          const int cu = c + kSub * u < kv_end ? c + kSub * u : c;
+          const int64_t base = int64_t(pid[u]) * a.page_stride + int64_t(cu & (P - 1)) * tstride;
+          const char* kb = reinterpret_cast<const char*>(kp + base);
+          const char* vb = reinterpret_cast<const char*>(vp + base);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            X.k[4 * u + i] = *reinterpret_cast<const uint4*>(kb + lane_off[i]);
+            X.v[4 * u + i] = *reinterpret_cast<const uint4*>(vb + lane_off[i]);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int tok = min(c + kSub * u + 4 * i + grp, kv_end - 1);
+            int page, off;
+            if (shift >= 0) {
+              page = tok >> shift;
+              off = tok & (P - 1);
+            } else {
+              page = tok / P;
+              off = tok - page * P;
+            }
+            const int64_t pg = a.kv_indices[ip0 + page];  // per-lane (vector) load
+            const int64_t at = pg * a.page_stride + int64_t(off) * tstride + head_off;
+            X.k[4 * u + i] = *reinterpret_cast<const uint4*>(kp + at);
+            X.v[4 * u + i] = *reinterpret_cast<const uint4*>(vp + at);
+          }
+        }
+      }
+    };
+
+    // one 16-token sub-chunk starting at token c (registers k4[4], v4[4])
+    auto compute_sub = [&](uint4* k4, const uint4* v4, int c) {
       if constexpr (ROPE) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          rope_rotate8<T>(X.k[i], kv_pos0 + (float)(c + 4 * i + grp), fhi, flo, hi_half);
+          rope_rotate8<T>(k4[i], kv_pos0 + (float)(c + 4 * i + grp), fhi, flo, hi_half);
       }
       // scores of 4 tokens x G rows, summed over the 16 lanes of the token's row
-      float sc[4][G];
+      float sc[4 * G];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-          float acc = dot2<T>(qv[g].x, X.k[i].x, 0.f);
-          acc = dot2<T>(qv[g].y, X.k[i].y, acc);
-          acc = dot2<T>(qv[g].z, X.k[i].z, acc);
-          acc = dot2<T>(qv[g].w, X.k[i].w, acc);
-          sc[i][g] = row16_sum(acc);
-        }
-        if (c + 4 * i + grp >= kv_end) {
-#pragma unroll
-          for (int g = 0; g < G; ++g) sc[i][g] = kNegInf;
+          float acc = dot2<T>(qv[g].x, k4[i].x, 0.f);
+          acc = dot2<T>(qv[g].y, k4[i].y, acc);
+          acc = dot2<T>(qv[g].z, k4[i].z, acc);
+          sc[i * G + g] = dot2<T>(qv[g].w, k4[i].w, acc);
         }
       }
-      // online softmax (per row, per token group) and p packed as token pairs
+      row16_sum_all<4 * G>(sc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (c + 4 * i + grp >= kv_end) {
+#pragma unroll
+          for (int g = 0; g < G; ++g) sc[i * G + g] = kNegInf;
+        }
+      }
+      // lazy online softmax: move the reference max only when it is exceeded by thr
+      float mx[G];
+      bool need = false;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        mx[g] = __builtin_fmaxf(__builtin_fmaxf(sc[g], sc[G + g]),
+                                __builtin_fmaxf(sc[2 * G + g], sc[3 * G + g]));
+        need |= mx[g] > m[g] + thr;
+      }
+      if (__builtin_amdgcn_ballot_w64(need)) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float mn = __builtin_fmaxf(m[g], mx[g]);
+          const float alpha = mn == kNegInf ? 1.f : fast_exp2((m[g] - mn) * cl2);
+          l[g] *= alpha;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[g][e] *= alpha;
+          m[g] = mn;
+        }
+      }
       uint32_t pp[2][G];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const float mx = __builtin_fmaxf(__builtin_fmaxf(sc[0][g], sc[1][g]),
-                                         __builtin_fmaxf(sc[2][g], sc[3][g]));
-        const float mn = __builtin_fmaxf(m[g], mx);
-        const float mu = mn == kNegInf ? 0.f : mn;
-        const float alpha = fast_exp2((m[g] - mu) * cl2);
-        const float mc = mu * cl2;
+        const float mc = (m[g] == kNegInf ? 0.f : m[g]) * cl2;
         float p[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p[i] = fast_exp2(__builtin_fmaf(sc[i][g], cl2, -mc));
-        l[g] = __builtin_fmaf(l[g], alpha, (p[0] + p[1]) + (p[2] + p[3]));
-        m[g] = mn;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[g][e] *= alpha;
+        for (int i = 0; i < 4; ++i) p[i] = fast_exp2(__builtin_fmaf(sc[i * G + g], cl2, -mc));
+        l[g] += (p[0] + p[1]) + (p[2] + p[3]);
         pp[0][g] = pack2<T>(p[0], p[1]);
         pp[1][g] = pack2<T>(p[2], p[3]);
       }
@@ -222,7 +298,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
       for (int pr = 0; pr < 2; ++pr) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const uint32_t va = word(X.v[2 * pr], j), vb = word(X.v[2 * pr + 1], j);
+          const uint32_t va = word(v4[2 * pr], j), vb = word(v4[2 * pr + 1], j);
           const uint32_t vlo = pair_lo(va, vb);  // element 2j of both tokens
           const uint32_t vhi = pair_hi(va, vb);  // element 2j + 1
 #pragma unroll
@@ -234,19 +310,46 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
       }
     };
 
-    // ---- main loop: double-buffered chunks, this wave's chunks every kStep keys
+    auto compute_chunk = [&](KVRegs<S>& X, int c) {
+#pragma unroll
+      for (int u = 0; u < S; ++u) {
+        if (u == 0 || c + kSub * u < kv_end) compute_sub(&X.k[4 * u], &X.v[4 * u], c + kSub * u);
+      }
+    };
+
+    // ---- main loop: double-buffered chunks, this wave's chunks every kStep keys.
+    // The steady-state body issues its loads unconditionally (the last one or
+    // two chunks are peeled), so each compute waits only for its own chunk.
     {
-      KVRegs A, B;
-      int c = kv_begin + wave * kChunk;
-      if (c < kv_end) load_chunk(A, c);
-      while (c < kv_end) {
-        if (c + kStep < kv_end) load_chunk(B, c + kStep);
-        compute_chunk(A, c);
-        c += kStep;
-        if (c >= kv_end) break;
-        if (c + kStep < kv_end) load_chunk(A, c + kStep);
-        compute_chunk(B, c);
-        c += kStep;
+      KVRegs<S> A, B;
+      const int c0 = kv_begin + wave * kChunk;
+      const int n = c0 < kv_end ? (kv_end - c0 + kStep - 1) / kStep : 0;
+      auto cpos = [&](int i) { return c0 + i * kStep; };
+      if (n > 0) {
+        int pidA[S] = {}, pidB[S] = {};
+        if constexpr (FASTPAGE) {
+          chunk_pids(cpos(0), pidA);
+          if (n > 1) chunk_pids(cpos(1), pidB);
+        }
+        load_chunk(A, cpos(0), pidA);
+        int i = 0;
+        for (; i + 2 < n; i += 2) {
+          load_chunk(B, cpos(i + 1), pidB);
+          if constexpr (FASTPAGE) chunk_pids(cpos(i + 2), pidA);
+          compute_chunk(A, cpos(i));
+          load_chunk(A, cpos(i + 2), pidA);
+          if constexpr (FASTPAGE) {
+            if (i + 3 < n) chunk_pids(cpos(i + 3), pidB);
+          }
+          compute_chunk(B, cpos(i + 1));
+        }
+        if (i + 1 < n) {
+          load_chunk(B, cpos(i + 1), pidB);
+          compute_chunk(A, cpos(i));
+          compute_chunk(B, cpos(i + 1));
+        } else {
+          compute_chunk(A, cpos(i));
+        }
       }
     }
 
@@ -255,8 +358,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
     for (int g = 0; g < G; ++g) {
       float M = __builtin_fmaxf(m[g], __shfl_xor(m[g], 16));
       M = __builtin_fmaxf(M, __shfl_xor(M, 32));
-      const float Mu = M == kNegInf ? 0.f : M;
-      const float f = fast_exp2((m[g] - Mu) * cl2);
+      const float f = M == kNegInf ? 0.f : fast_exp2((m[g] - M) * cl2);
       float lg = l[g] * f;
       lg += __shfl_xor(lg, 16);
       lg += __shfl_xor(lg, 32);
@@ -298,7 +400,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
         float L = 0.f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-          const float f = fast_exp2((s_m[w][g] - M) * cl2);
+          const float f = s_m[w][g] == kNegInf ? 0.f : fast_exp2((s_m[w][g] - M) * cl2);
           L = __builtin_fmaf(f, s_l[w][g], L);
 #pragma unroll
           for (int e = 0; e < 8; ++e) out[e] = __builtin_fmaf(f, s_o[w][g][e0 + e], out[e]);
@@ -322,13 +424,27 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
   }
 }
 
+// Sub-chunks per buffered chunk on the page-aligned path: 2 (32 tokens, 16 KB
+// of K/V in flight per wave) where the registers allow it (G <= 4, no RoPE),
+// else 1. The per-token path always uses 1.
+template <int G, bool ROPE>
+constexpr int sub_fast() {
+  return (G <= 4 && !ROPE) ? 2 : 1;
+}
+
+template <typename T, int G, bool ROPE>
+hipError_t launch_r(const AttnArgs& a, hipStream_t s) {
+  const bool fast = a.page_shift >= 4;  // power of two and a multiple of 16
+  if (fast)
+    decode_kernel<T, G, ROPE, true, sub_fast<G, ROPE>()><<<a.workers, 256, 0, s>>>(a);
+  else
+    decode_kernel<T, G, ROPE, false, 1><<<a.workers, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
 template <typename T, int G>
 hipError_t launch_g(const Config& cfg, const AttnArgs& a, hipStream_t s) {
-  if (cfg.rope)
-    decode_kernel<T, G, true><<<a.workers, 256, 0, s>>>(a);
-  else
-    decode_kernel<T, G, false><<<a.workers, 256, 0, s>>>(a);
-  return hipGetLastError();
+  return cfg.rope ? launch_r<T, G, true>(a, s) : launch_r<T, G, false>(a, s);
 }
 
 template <typename T>
@@ -342,11 +458,45 @@ hipError_t launch_t(const Config& cfg, const AttnArgs& a, hipStream_t s) {
   }
 }
 
+template <typename T, int G>
+int occupancy_g(const Config& cfg, bool fast) {
+  int n = 0;
+  hipError_t e;
+  if (cfg.rope)
+    e = fast ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                   &n, decode_kernel<T, G, true, true, sub_fast<G, true>()>, 256, 0)
+             : hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                   &n, decode_kernel<T, G, true, false, 1>, 256, 0);
+  else
+    e = fast ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                   &n, decode_kernel<T, G, false, true, sub_fast<G, false>()>, 256, 0)
+             : hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                   &n, decode_kernel<T, G, false, false, 1>, 256, 0);
+  return e == hipSuccess ? n : 0;
+}
+
+template <typename T>
+int occupancy_t(const Config& cfg, bool fast) {
+  switch (cfg.group) {
+    case 1: return occupancy_g<T, 1>(cfg, fast);
+    case 2: return occupancy_g<T, 2>(cfg, fast);
+    case 4: return occupancy_g<T, 4>(cfg, fast);
+    case 8: return occupancy_g<T, 8>(cfg, fast);
+    default: return 0;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_decode(const Config& cfg, const AttnArgs& a, hipStream_t s) {
   if (cfg.qkv_dtype == ABP_BF16) return launch_t<BF16>(cfg, a, s);
   return launch_t<F16>(cfg, a, s);
+}
+
+int decode_blocks_per_cu(const Config& cfg) {
+  const bool pow2 = (cfg.page_size & (cfg.page_size - 1)) == 0;
+  const bool fast = pow2 && cfg.page_size >= 16;
+  return cfg.qkv_dtype == ABP_BF16 ? occupancy_t<BF16>(cfg, fast) : occupancy_t<F16>(cfg, fast);
 }
 
 }  // namespace abp

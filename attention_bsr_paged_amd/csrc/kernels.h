@@ -36,6 +36,9 @@ struct AttnArgs {
 };
 
 hipError_t launch_decode(const Config& cfg, const AttnArgs& a, hipStream_t stream);
+// resident 256-thread workgroups per compute unit of the kernel chosen for cfg
+int decode_blocks_per_cu(const Config& cfg);
+int append_blocks_per_cu(const Config& cfg);
 hipError_t launch_append(const Config& cfg, const AttnArgs& a, hipStream_t stream);
 // merges the split tiles of a plan into o / lse (fixed grid, reads counts from the plan)
 hipError_t launch_plan_merge(const Config& cfg, const AttnArgs& a, int32_t grid,

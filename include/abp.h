@@ -144,8 +144,9 @@ int abp_device_num_cus(int device, int32_t* num_cus);
 
 /* Workspace sizes for plans of `kind` with at most `max_batch` requests,
  * `max_qo_tokens` query tokens (append; ignored for decode) and `num_workers`
- * workers (<= 0: 2 per compute unit of the current device for decode, 1 for
- * append). Pure host code except the compute-unit query for num_workers <= 0. */
+ * workers (<= 0: one per resident workgroup slot of the current device, i.e.
+ * compute units times the workgroups of the selected kernel that fit on one).
+ * Pure host code except the device query for num_workers <= 0. */
 int abp_workspace_size(int kind, const abp_params* params, int32_t max_batch,
                        int32_t max_qo_tokens, int32_t num_workers, size_t* host_bytes,
                        size_t* dev_bytes);
