@@ -1,13 +1,504 @@
-// Append / prefill attention (MFMA): not built yet in this revision.
+// Persistent append / prefill attention over a paged block-sparse-row KV cache
+// on gfx950 matrix cores.
+//
+// What it computes: for ragged query tokens (qo_indptr) of each request, exact
+// softmax attention over the request's paged keys, optionally causal with the
+// mask aligned to the end of the KV (query i sees keys t <= kv_len - qo_len + i).
+// Prefill / append over paged and ragged caches are core kernels of the README
+// (gittoolsai.com, section 核心功能 / 注意力机制内核); the block-sparse-row
+// addressing is the paper summary's ("图谱动态｜学苑周刊 NO.266", section
+// 统一的 KV 缓存存储格式), and the work split follows its load-balancing
+// section (动态负载均衡调度). Unlike decode, each K/V element is reused by up
+// to 128 query rows, so this path is bound by matrix-core throughput.
+//
+// Tiles: 128 rows = tile_q tokens x G qo heads of one kv head (row r is token
+// r / G, head r % G), against blocks of 64 keys. A 256-thread workgroup is one
+// worker; wave w owns rows [32 w, 32 w + 32) (two 16-row column blocks).
+//
+//   S^T = K Q^T    v_mfma_f32_16x16x32 with A = K rows (LDS, row-major,
+//                  padded) and B = Q^T (registers). The accumulator gives each
+//                  lane one query row and 16 of the block's keys, so softmax
+//                  statistics are lane-local except a 4-lane max.
+//   softmax        fp32, base-2 exponentials, running max per row; P is
+//                  rounded to the storage type for the next product.
+//   O^T += V^T P^T v_mfma with A = V^T (LDS, transposed when staged: key pairs
+//                  packed with v_perm) and B = P^T taken directly from the S
+//                  registers: the K-slot order of the product is chosen to be
+//                  the order in which S holds the keys, so no lane exchange.
+//
+// The next block's K/V are loaded into registers while the current block is
+// computed, then stored to LDS. With a power-of-two page size >= 16, a block's
+// page ids are scalar loads (one per 16-key group). Workers are mapped to
+// workgroup ids XCD-major, so consecutive workers (which usually share the
+// same request and kv head) run on the same XCD and share its L2.
 #include "common.h"
 #include "kernels.h"
+#include "layout.h"
 
 namespace abp {
 
-hipError_t launch_append(const Config&, const AttnArgs&, hipStream_t) {
-  return hipErrorNotSupported;
+namespace {
+
+constexpr int kD = 128;
+constexpr int kRows = kAppendRows;   // 128
+constexpr int kTk = kAppendTileKv;   // 64
+constexpr int kKStride = 136;        // sK row stride (uint16): 128 + 8 pad
+constexpr int kVStride = 68;         // sVt row stride (uint16): 64 + 4 pad
+
+template <typename T>
+__device__ __forceinline__ f32x4_t mfma(const uint4& a, const uint4& b, f32x4_t c);
+template <>
+__device__ __forceinline__ f32x4_t mfma<BF16>(const uint4& a, const uint4& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x4_t mfma<F16>(const uint4& a, const uint4& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
-int append_blocks_per_cu(const Config&) { return 1; }
+__device__ __forceinline__ uint32_t word(const uint4& u, int j) {
+  return j == 0 ? u.x : j == 1 ? u.y : j == 2 ? u.z : u.w;
+}
+
+// Split fp32 values into a 16-bit high part and the 16-bit rounding of the
+// remainder, so that hi + lo carries ~16 significant bits: products of rotated
+// operands keep fp32-level accuracy with three 16-bit matrix products.
+template <typename T>
+__device__ __forceinline__ void split8(const float v[8], uint4& hi, uint4& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    h[w] = pack2<T>(v[2 * w], v[2 * w + 1]);
+    l[w] = pack2<T>(v[2 * w] - lo_f32<T>(h[w]), v[2 * w + 1] - hi_f32<T>(h[w]));
+  }
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+// Rotate q: `lo` holds elements j0..j0+7 (j0 < 64) and `hi` their partners
+// j0+64..; results are split into (hi, lo) 16-bit parts for both halves.
+template <typename T>
+__device__ __forceinline__ void rope_pair(uint4& lo, uint4& hi, uint4& lo_r, uint4& hi_r,
+                                          float pos, int j0, const ABP_CONST_AS float* rope) {
+  float a[8], b[8];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    a[2 * w] = lo_f32<T>(word(lo, w));
+    a[2 * w + 1] = hi_f32<T>(word(lo, w));
+    b[2 * w] = lo_f32<T>(word(hi, w));
+    b[2 * w + 1] = hi_f32<T>(word(hi, w));
+  }
+  float ra[8], rb[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float sn, cs;
+    rope_sincos(pos, rope[2 * (j0 + e)], rope[2 * (j0 + e) + 1], &sn, &cs);
+    ra[e] = __builtin_fmaf(a[e], cs, -b[e] * sn);
+    rb[e] = __builtin_fmaf(b[e], cs, a[e] * sn);
+  }
+  split8<T>(ra, lo, lo_r);
+  split8<T>(rb, hi, hi_r);
+}
+
+// Rotate a K row chunk (elements 8c..8c+7) held by lane t; its partner chunk
+// (c ^ 8) is held by lane t ^ 8 of the same 16-lane row. Wave-uniform call.
+template <typename T>
+__device__ __forceinline__ void rope_k(const uint4& u, float pos, int c,
+                                       const ABP_CONST_AS float* rope, float out[8]) {
+  uint32_t w[4], pw[4];
+  w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) pw[j] = dpp_u<kDppRor8>(w[j]);
+  const bool hi = c >= 8;
+  const int j0 = (c & 7) * 8;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float own = (e & 1) ? hi_f32<T>(w[e >> 1]) : lo_f32<T>(w[e >> 1]);
+    const float par = (e & 1) ? hi_f32<T>(pw[e >> 1]) : lo_f32<T>(pw[e >> 1]);
+    float sn, cs;
+    rope_sincos(pos, rope[2 * (j0 + e)], rope[2 * (j0 + e) + 1], &sn, &cs);
+    out[e] = __builtin_fmaf(par, hi ? sn : -sn, own * cs);
+  }
+}
+
+// RoPE variants carry hi/lo parts of q and k and run one workgroup per CU.
+template <bool ROPE>
+constexpr int append_wg_per_cu() {
+  return ROPE ? 1 : 2;
+}
+
+template <typename T, int G, bool CAUSAL, bool ROPE, bool FASTPAGE>
+__global__ __launch_bounds__(256, append_wg_per_cu<ROPE>()) void append_kernel(AttnArgs a) {
+  constexpr int TQ = kRows / G;
+  __shared__ __align__(16) uint16_t sK[kTk * kKStride];
+  __shared__ __align__(16) uint16_t sKlo[ROPE ? kTk * kKStride : 8];  // RoPE: low parts of K
+  __shared__ __align__(16) uint16_t sVt[kD * kVStride];
+
+  const ABP_CONST_AS int32_t* plan = const_as(a.plan);
+  const ABP_CONST_AS int32_t* wseg = plan + plan[H_OFF_WSEG];
+  const ABP_CONST_AS int32_t* segs = plan + plan[H_OFF_SEG];
+  const ABP_CONST_AS int32_t* tiles = plan + plan[H_OFF_TILE];
+  const ABP_CONST_AS float* rope = (const ABP_CONST_AS float*)(plan + plan[H_OFF_ROPE]);
+  const ABP_CONST_AS int32_t* kv_indptr = const_as(a.kv_indptr);
+  const ABP_CONST_AS int32_t* kv_indices = const_as(a.kv_indices);
+  const ABP_CONST_AS int32_t* qo_indptr = const_as(a.qo_indptr);
+
+  // XCD-major worker id: workgroup i runs on XCD i % 8
+  const int W = a.workers;
+  const int worker = (W % 8 == 0) ? (blockIdx.x % 8) * (W / 8) + blockIdx.x / 8 : blockIdx.x;
+  const int s_begin = wseg[worker], s_end = wseg[worker + 1];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g16 = lane >> 4;   // lane group 0..3
+  const int l16 = lane & 15;
+  const float cl2 = a.sm_scale_log2;
+  const int P = a.page_size;
+  const int shift = a.page_shift;
+  const int tstride = a.token_stride;
+  const uint16_t* __restrict__ kp = static_cast<const uint16_t*>(a.k_pages);
+  const uint16_t* __restrict__ vp = static_cast<const uint16_t*>(a.v_pages);
+
+  // staging thread mappings
+  const int kc_chunk = tid & 15;      // K: 16-byte chunk of head_dim
+  const int k_row = tid >> 4;         // K: keys k_row + 16 i
+  const int v_kg = tid & 15;          // V: keys 4 v_kg .. 4 v_kg + 3
+  const int v_chunk = tid >> 4;       // V: 16-byte chunk of head_dim
+
+  for (int s = s_begin; s < s_end; ++s) {
+    const int tile = segs[4 * s];
+    const int kv_begin = segs[4 * s + 1], kv_end = segs[4 * s + 2], slot = segs[4 * s + 3];
+    const int b = tiles[4 * tile], h = tiles[4 * tile + 1], qt = tiles[4 * tile + 2];
+    const int q0 = qo_indptr[b];
+    const int qo_len = qo_indptr[b + 1] - q0;
+    const int ip0 = kv_indptr[b];
+    const int npg = kv_indptr[b + 1] - ip0;
+    const int kv_len = npg > 0 ? (npg - 1) * P + a.kv_last_page_len[b] : 0;
+    const int kv_pos0 = (ROPE && a.kv_pos_offset) ? a.kv_pos_offset[b] : 0;
+
+    // ---- Q fragments (B operand of S^T = K Q^T) for this wave's 32 rows
+    uint4 qf[2][4];
+    uint4 qfl[ROPE ? 2 : 1][4];  // RoPE: low parts of the rotated q
+    int lim[2];
+    int tloc_r[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int r = wave * 32 + nb * 16 + l16;
+      const int tloc = qt * TQ + r / G;
+      const int tl = min(tloc, qo_len - 1);
+      tloc_r[nb] = tloc;
+      lim[nb] = kv_len - qo_len + tl;
+      const uint16_t* qptr = static_cast<const uint16_t*>(a.q) +
+                             ((int64_t)(q0 + tl) * a.num_qo_heads + h * G + (r % G)) * kD + g16 * 8;
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) qf[nb][kc] = *reinterpret_cast<const uint4*>(qptr + kc * 32);
+      if constexpr (ROPE) {
+        const float qpos = a.q_pos ? (float)a.q_pos[q0 + tl] : (float)lim[nb];
+        rope_pair<T>(qf[nb][0], qf[nb][2], qfl[nb][0], qfl[nb][2], qpos, g16 * 8, rope);
+        rope_pair<T>(qf[nb][1], qf[nb][3], qfl[nb][1], qfl[nb][3], qpos, 32 + g16 * 8, rope);
+      }
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc)
+        asm volatile("" : "+v"(qf[nb][kc].x), "+v"(qf[nb][kc].y), "+v"(qf[nb][kc].z),
+                     "+v"(qf[nb][kc].w));
+    }
+    // first row of the tile sees the fewest keys
+    const int tile_min_lim = kv_len - qo_len + qt * TQ;
+
+    float m[2] = {kNegInf, kNegInf};
+    float lsum[2] = {0.f, 0.f};
+    f32x4_t O[8][2];
+#pragma unroll
+    for (int md = 0; md < 8; ++md)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) O[md][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // ---- staging: global -> registers (next block) and registers -> LDS
+    uint4 kreg[4], vreg[4];
+    auto gload = [&](int kb) {
+      if constexpr (FASTPAGE) {
+        // one page id per 16-key group (scalar), clamped to the last valid group
+        const int last16 = (kv_end - 1) & ~15;
+        int pid[4], kk[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          kk[i] = min(kb + 16 * i, last16);
+          pid[i] = kv_indices[ip0 + (kk[i] >> shift)];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t at = (int64_t)pid[i] * a.page_stride +
+                             (int64_t)((kk[i] & (P - 1)) + k_row) * tstride + h * kD + kc_chunk * 8;
+          kreg[i] = *reinterpret_cast<const uint4*>(kp + at);
+        }
+        const int gi = v_kg >> 2;  // 16-key group of this thread's V keys
+        const int vpid = gi == 0 ? pid[0] : gi == 1 ? pid[1] : gi == 2 ? pid[2] : pid[3];
+        const int vkk = gi == 0 ? kk[0] : gi == 1 ? kk[1] : gi == 2 ? kk[2] : kk[3];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t at = (int64_t)vpid * a.page_stride +
+                             (int64_t)((vkk & (P - 1)) + (4 * v_kg & 15) + i) * tstride + h * kD +
+                             v_chunk * 8;
+          vreg[i] = *reinterpret_cast<const uint4*>(vp + at);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = min(kb + k_row + 16 * i, kv_end - 1);
+          int page, off;
+          if (shift >= 0) {
+            page = key >> shift;
+            off = key & (P - 1);
+          } else {
+            page = key / P;
+            off = key - page * P;
+          }
+          const int64_t pg = a.kv_indices[ip0 + page];
+          kreg[i] = *reinterpret_cast<const uint4*>(kp + pg * a.page_stride +
+                                                    (int64_t)off * tstride + h * kD + kc_chunk * 8);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = min(kb + 4 * v_kg + i, kv_end - 1);
+          int page, off;
+          if (shift >= 0) {
+            page = key >> shift;
+            off = key & (P - 1);
+          } else {
+            page = key / P;
+            off = key - page * P;
+          }
+          const int64_t pg = a.kv_indices[ip0 + page];
+          vreg[i] = *reinterpret_cast<const uint4*>(vp + pg * a.page_stride +
+                                                    (int64_t)off * tstride + h * kD + v_chunk * 8);
+        }
+      }
+    };
+    auto swrite = [&](int kb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int at = (k_row + 16 * i) * kKStride + kc_chunk * 8;
+        if constexpr (ROPE) {
+          float kr[8];
+          rope_k<T>(kreg[i], (float)(kv_pos0 + kb + k_row + 16 * i), kc_chunk, rope, kr);
+          uint4 hi, lo;
+          split8<T>(kr, hi, lo);
+          *reinterpret_cast<uint4*>(&sK[at]) = hi;
+          *reinterpret_cast<uint4*>(&sKlo[at]) = lo;
+        } else {
+          *reinterpret_cast<uint4*>(&sK[at]) = kreg[i];
+        }
+      }
+      // V^T: element e of the 4 keys 4 v_kg .. 4 v_kg + 3 as one 8-byte row piece
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w0 = word(vreg[0], j), w1 = word(vreg[1], j);
+        const uint32_t w2 = word(vreg[2], j), w3 = word(vreg[3], j);
+        uint2 lo, hi;
+        lo.x = pair_lo(w0, w1);
+        lo.y = pair_lo(w2, w3);
+        hi.x = pair_hi(w0, w1);
+        hi.y = pair_hi(w2, w3);
+        const int d = v_chunk * 8 + 2 * j;
+        *reinterpret_cast<uint2*>(&sVt[d * kVStride + 4 * v_kg]) = lo;
+        *reinterpret_cast<uint2*>(&sVt[(d + 1) * kVStride + 4 * v_kg]) = hi;
+      }
+    };
+
+    if (kv_begin < kv_end) {
+      gload(kv_begin);
+      swrite(kv_begin);
+      __syncthreads();
+    }
+    for (int kb = kv_begin; kb < kv_end; kb += kTk) {
+      const bool has_next = kb + kTk < kv_end;
+      if (has_next) gload(kb + kTk);
+
+      // ---- S^T = K Q^T: S[mb][nb] holds keys kb + 16 mb + 4 g16 + j, row nb*16 + l16
+      f32x4_t S[4][2];
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        S[mb][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        S[mb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+          const int at = (mb * 16 + l16) * kKStride + kc * 32 + g16 * 8;
+          const uint4 ka = *reinterpret_cast<const uint4*>(&sK[at]);
+          S[mb][0] = mfma<T>(ka, qf[0][kc], S[mb][0]);
+          S[mb][1] = mfma<T>(ka, qf[1][kc], S[mb][1]);
+          if constexpr (ROPE) {  // + Kh Ql + Kl Qh
+            const uint4 kl = *reinterpret_cast<const uint4*>(&sKlo[at]);
+            S[mb][0] = mfma<T>(ka, qfl[0][kc], S[mb][0]);
+            S[mb][1] = mfma<T>(ka, qfl[1][kc], S[mb][1]);
+            S[mb][0] = mfma<T>(kl, qf[0][kc], S[mb][0]);
+            S[mb][1] = mfma<T>(kl, qf[1][kc], S[mb][1]);
+          }
+        }
+      }
+      // ---- masks: keys past the segment end, causal limit per row
+      const bool edge = (kb + kTk > kv_end) || (CAUSAL && kb + kTk - 1 > tile_min_lim);
+      if (edge) {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int key = kb + mb * 16 + g16 * 4 + j;
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+              const bool dead = key >= kv_end || (CAUSAL && key > lim[nb]);
+              if (dead) S[mb][nb][j] = kNegInf;
+            }
+          }
+      }
+      // ---- online softmax per row; P packed as the B operand of the PV product
+      uint4 pB[2][2];  // [kc2][nb]
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        float mx = kNegInf;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+          mx = __builtin_fmaxf(mx, __builtin_fmaxf(__builtin_fmaxf(S[mb][nb][0], S[mb][nb][1]),
+                                                   __builtin_fmaxf(S[mb][nb][2], S[mb][nb][3])));
+        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16));
+        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
+        const float mn = __builtin_fmaxf(m[nb], mx);
+        const float mu = mn == kNegInf ? 0.f : mn;
+        const float alpha = fast_exp2((m[nb] - mu) * cl2);
+        m[nb] = mn;
+        lsum[nb] *= alpha;
+#pragma unroll
+        for (int md = 0; md < 8; ++md) O[md][nb] *= alpha;
+        const float mc = mu * cl2;
+        float p[4][4];
+        float ps = 0.f;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            p[mb][j] = fast_exp2(__builtin_fmaf(S[mb][nb][j], cl2, -mc));
+            ps += p[mb][j];
+          }
+        lsum[nb] += ps;
+#pragma unroll
+        for (int kc2 = 0; kc2 < 2; ++kc2) {
+          pB[kc2][nb] = make_uint4(pack2<T>(p[2 * kc2][0], p[2 * kc2][1]),
+                                   pack2<T>(p[2 * kc2][2], p[2 * kc2][3]),
+                                   pack2<T>(p[2 * kc2 + 1][0], p[2 * kc2 + 1][1]),
+                                   pack2<T>(p[2 * kc2 + 1][2], p[2 * kc2 + 1][3]));
+        }
+      }
+      // ---- O^T += V^T P^T: K-slots of lane group g16 are keys 4 g16..+3 and 16 + 4 g16..+3
+#pragma unroll
+      for (int md = 0; md < 8; ++md) {
+#pragma unroll
+        for (int kc2 = 0; kc2 < 2; ++kc2) {
+          const uint16_t* vrow = &sVt[(md * 16 + l16) * kVStride + kc2 * 32 + g16 * 4];
+          const uint2 v0 = *reinterpret_cast<const uint2*>(vrow);
+          const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 16);
+          const uint4 va = make_uint4(v0.x, v0.y, v1.x, v1.y);
+          O[md][0] = mfma<T>(va, pB[kc2][0], O[md][0]);
+          O[md][1] = mfma<T>(va, pB[kc2][1], O[md][1]);
+        }
+      }
+      __syncthreads();  // all waves are done with this block's LDS tiles
+      if (has_next) {
+        swrite(kb + kTk);
+        __syncthreads();
+      }
+    }
+
+    // ---- finalize rows: o = O / l, lse = m * scale + ln l
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      float L = lsum[nb];
+      L += __shfl_xor(L, 16);
+      L += __shfl_xor(L, 32);
+      const int r = wave * 32 + nb * 16 + l16;
+      const bool valid = tloc_r[nb] < qo_len;
+      const bool empty = !(L > 0.f);
+      const float inv = empty ? 0.f : 1.f / L;
+      const float lse = empty ? kNegInf : m[nb] * a.sm_scale + fast_log2(L) * kLn2;
+      if (valid) {
+        if (slot < 0) {
+          const int64_t orow = (int64_t)(q0 + tloc_r[nb]) * a.num_qo_heads + h * G + (r % G);
+#pragma unroll
+          for (int md = 0; md < 8; ++md) {
+            const int64_t off = orow * kD + md * 16 + g16 * 4;
+            const f32x4_t v = O[md][nb] * inv;
+            if (a.out_dtype == ABP_F32) {
+              *reinterpret_cast<float4*>(static_cast<float*>(a.o) + off) =
+                  make_float4(v[0], v[1], v[2], v[3]);
+            } else if (a.out_dtype == ABP_BF16) {
+              *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.o) + off) =
+                  make_uint2(pack2<BF16>(v[0], v[1]), pack2<BF16>(v[2], v[3]));
+            } else {
+              *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.o) + off) =
+                  make_uint2(pack2<F16>(v[0], v[1]), pack2<F16>(v[2], v[3]));
+            }
+          }
+          if (a.lse && g16 == 0) a.lse[orow] = lse;
+        } else {
+          const int64_t prow = (int64_t)slot * kRows + r;
+#pragma unroll
+          for (int md = 0; md < 8; ++md) {
+            const f32x4_t v = O[md][nb] * inv;
+            *reinterpret_cast<float4*>(a.o_part + prow * kD + md * 16 + g16 * 4) =
+                make_float4(v[0], v[1], v[2], v[3]);
+          }
+          if (g16 == 0) a.lse_part[prow] = lse;
+        }
+      }
+    }
+  }
+}
+
+template <typename T, int G, bool CAUSAL, bool ROPE>
+hipError_t launch_f(const AttnArgs& a, hipStream_t s) {
+  if (a.page_shift >= 4)
+    append_kernel<T, G, CAUSAL, ROPE, true><<<a.workers, 256, 0, s>>>(a);
+  else
+    append_kernel<T, G, CAUSAL, ROPE, false><<<a.workers, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+template <typename T, int G>
+hipError_t launch_g(const Config& cfg, const AttnArgs& a, hipStream_t s) {
+  if (cfg.causal)
+    return cfg.rope ? launch_f<T, G, true, true>(a, s) : launch_f<T, G, true, false>(a, s);
+  return cfg.rope ? launch_f<T, G, false, true>(a, s) : launch_f<T, G, false, false>(a, s);
+}
+
+template <typename T>
+hipError_t launch_t(const Config& cfg, const AttnArgs& a, hipStream_t s) {
+  switch (cfg.group) {
+    case 1: return launch_g<T, 1>(cfg, a, s);
+    case 2: return launch_g<T, 2>(cfg, a, s);
+    case 4: return launch_g<T, 4>(cfg, a, s);
+    case 8: return launch_g<T, 8>(cfg, a, s);
+    case 16: return launch_g<T, 16>(cfg, a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_append(const Config& cfg, const AttnArgs& a, hipStream_t s) {
+  if (cfg.qkv_dtype == ABP_BF16) return launch_t<BF16>(cfg, a, s);
+  return launch_t<F16>(cfg, a, s);
+}
+
+int append_blocks_per_cu(const Config& cfg) {
+  int n = 0;
+  // the tile shape is shared by all variants; RoPE ones are built for one per CU
+  hipError_t e =
+      cfg.rope ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                     &n, append_kernel<BF16, 4, true, true, true>, 256, 0)
+               : hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                     &n, append_kernel<BF16, 4, true, false, true>, 256, 0);
+  return e == hipSuccess && n > 0 ? n : 1;
+}
 
 }  // namespace abp

@@ -64,17 +64,19 @@ __device__ __forceinline__ void set_word(uint4& u, int j, uint32_t v) {
 }
 
 // Rotate this lane's 8 elements (pairs (j, j + 64) split across lanes sub and
-// sub ^ 8) at position `pos`. All lanes of the wave must call it together.
+// sub ^ 8) at position `pos`, into fp32. All lanes of the wave must call it
+// together. The rotated values stay in fp32: rounding them back to 16 bits
+// would put ~1e-3 of noise on every logit, which short key ranges do not
+// average out.
 template <typename T>
-__device__ __forceinline__ void rope_rotate8(uint4& u, float pos, const float* fhi,
-                                             const float* flo, bool hi_half) {
+__device__ __forceinline__ void rope_rotate8(const uint4& u, float pos, const float* fhi,
+                                             const float* flo, bool hi_half, float out[8]) {
   uint32_t w[4], pw[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     w[j] = word(u, j);
     pw[j] = dpp_u<kDppRor8>(w[j]);
   }
-  float out[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const float own = (e & 1) ? hi_f32<T>(w[e >> 1]) : lo_f32<T>(w[e >> 1]);
@@ -83,8 +85,6 @@ __device__ __forceinline__ void rope_rotate8(uint4& u, float pos, const float* f
     rope_sincos(pos, fhi[e], flo[e], &sn, &cs);
     out[e] = __builtin_fmaf(par, hi_half ? sn : -sn, own * cs);
   }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) set_word(u, j, pack2<T>(out[2 * j], out[2 * j + 1]));
 }
 
 __device__ __forceinline__ void store8_dt(void* base, int64_t off, const float v[8], int dt) {
@@ -167,13 +167,14 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
         asm volatile("" : "+v"(qv[g].x), "+v"(qv[g].y), "+v"(qv[g].z), "+v"(qv[g].w));
     }
     float kv_pos0 = 0.f;
+    float qr[ROPE ? G : 1][8];  // rotated q in fp32 (RoPE only)
     if constexpr (ROPE) {
       const int n = kv_indptr[b + 1] - ip0;
       const int kv_len = n > 0 ? (n - 1) * P + a.kv_last_page_len[b] : 0;
       const int qpos = a.q_pos ? a.q_pos[b] : kv_len - 1;
       kv_pos0 = a.kv_pos_offset ? (float)a.kv_pos_offset[b] : 0.f;
 #pragma unroll
-      for (int g = 0; g < G; ++g) rope_rotate8<T>(qv[g], (float)qpos, fhi, flo, hi_half);
+      for (int g = 0; g < G; ++g) rope_rotate8<T>(qv[g], (float)qpos, fhi, flo, hi_half, qr[g]);
     }
 
     float m[G], l[G], o[G][8];
@@ -236,22 +237,29 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
     };
 
     // one 16-token sub-chunk starting at token c (registers k4[4], v4[4])
-    auto compute_sub = [&](uint4* k4, const uint4* v4, int c) {
-      if constexpr (ROPE) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          rope_rotate8<T>(k4[i], kv_pos0 + (float)(c + 4 * i + grp), fhi, flo, hi_half);
-      }
+    auto compute_sub = [&](const uint4* k4, const uint4* v4, int c) {
       // scores of 4 tokens x G rows, summed over the 16 lanes of the token's row
       float sc[4 * G];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        if constexpr (ROPE) {
+          float kr[8];
+          rope_rotate8<T>(k4[i], kv_pos0 + (float)(c + 4 * i + grp), fhi, flo, hi_half, kr);
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float acc = dot2<T>(qv[g].x, k4[i].x, 0.f);
-          acc = dot2<T>(qv[g].y, k4[i].y, acc);
-          acc = dot2<T>(qv[g].z, k4[i].z, acc);
-          sc[i * G + g] = dot2<T>(qv[g].w, k4[i].w, acc);
+          for (int g = 0; g < G; ++g) {
+            float acc = qr[g][0] * kr[0];
+#pragma unroll
+            for (int e = 1; e < 8; ++e) acc = __builtin_fmaf(qr[g][e], kr[e], acc);
+            sc[i * G + g] = acc;
+          }
+        } else {
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            float acc = dot2<T>(qv[g].x, k4[i].x, 0.f);
+            acc = dot2<T>(qv[g].y, k4[i].y, acc);
+            acc = dot2<T>(qv[g].z, k4[i].z, acc);
+            sc[i * G + g] = dot2<T>(qv[g].w, k4[i].w, acc);
+          }
         }
       }
       row16_sum_all<4 * G>(sc);

@@ -1,0 +1,169 @@
+"""GPU parity of the append / prefill (MFMA) path, fused RoPE and the cascade
+(composable formats) path against the fp64 oracle."""
+import numpy as np
+import pytest
+
+import attention_bsr_paged_amd as abp
+from attention_bsr_paged_amd import workloads as wl
+from oracle import attention as ora
+
+from gpu_helpers import assert_parity, i32, run_append, run_decode, say, upload_kv
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _cuda():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    abp.load_library()
+
+
+QO = [1, 5, 31, 32, 33, 64, 130, 300]
+KV_EXTRA = [0, 3, 64, 1, 200, 17, 1000, 65]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("P", [1, 3, 16, 256])
+@pytest.mark.parametrize("G", [1, 4, 8])
+def test_small_append_parity(causal, P, G):
+    say(f"[case] small append causal={causal} P={P} G={G}")
+    kv = [q + e for q, e in zip(QO, KV_EXTRA)]
+    w = wl.small_append(200 + P + G, QO, kv, P, 2 * G, 2, dtype="bf16", causal=causal)
+    o_ref, l_ref = ora.append_workload(w)
+    for W in (1, 9, 0):
+        o, l = run_append(w, num_workers=W)
+        assert_parity(o, l, o_ref, l_ref, "bf16", what=f"append c{int(causal)} P{P} G{G} W{W}")
+
+
+@pytest.mark.parametrize("G", [2, 16])
+def test_group_sizes_fp16(G):
+    w = wl.small_append(300 + G, [7, 70, 129], [9, 500, 129], 16, 2 * G, 2, dtype="fp16",
+                        causal=True)
+    o_ref, l_ref = ora.append_workload(w)
+    o, l = run_append(w, num_workers=13)
+    assert_parity(o, l, o_ref, l_ref, "fp16", what=f"append fp16 G{G}")
+
+
+def test_empty_and_zero_query_requests():
+    """Requests with no queries write nothing; a non-causal request with no keys gives (0, -inf)."""
+    w = wl.small_append(310, [0, 4, 0, 3], [10, 0, 5, 7], 16, 8, 2, causal=False)
+    o_ref, l_ref = ora.append_workload(w)
+    o, l = run_append(w, num_workers=5)
+    assert_parity(o, l, o_ref, l_ref, "bf16", what="empty requests")
+
+
+def test_ragged_append_sampled():
+    """Full ragged causal append (16 requests, qo U{128..1024} onto kv U{1024..8192},
+    GQA 32/8, bf16) in the launch configuration the benchmark times, compared on
+    sampled query tokens of every request (first, last, and random ones)."""
+    w = wl.ragged_append_causal()
+    say(f"[case] {w.name}")
+    o, l = run_append(w)
+    rng = np.random.Generator(np.random.PCG64(9))
+    toks = []
+    for b in range(w.batch):
+        q0, q1 = int(w.qo_indptr[b]), int(w.qo_indptr[b + 1])
+        toks += [q0, q1 - 1] + list(rng.integers(q0, q1, size=6))
+    toks = sorted(set(toks))
+    o_ref, l_ref = ora.append_workload(w, token_ids=toks)
+    assert_parity(o, l, o_ref, l_ref, "bf16", rows=toks, what="ragged append sampled")
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
+
+
+def test_append_worker_invariance_and_determinism():
+    w = wl.small_append(320, [100, 257], [900, 2000], 16, 32, 8, causal=True)
+    o_ref, l_ref = ora.append_workload(w)
+    prev = None
+    for W in (1, 3, 64, 256):
+        o, l = run_append(w, num_workers=W)
+        assert_parity(o, l, o_ref, l_ref, "bf16", what=f"W{W}")
+    o1, l1 = run_append(w, num_workers=64)
+    o2, l2 = run_append(w, num_workers=64)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+# ----------------------------------------------------------------------------
+# fused RoPE
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("P", [3, 16])
+def test_rope_decode_parity(P):
+    w = wl.small_decode(330 + P, [1, 40, 700, 3000], P, 8, 2)
+    w.rope_theta = 500000.0
+    rng = np.random.Generator(np.random.PCG64(331))
+    w.kv_pos_offset = rng.integers(0, 9000, size=w.batch).astype(np.int32)
+    w.q_pos = (w.kv_pos_offset + w.kv.kv_len + rng.integers(-5, 5, size=w.batch)).astype(np.int32)
+    o_ref, l_ref = ora.decode_workload(w)
+    o, l = run_decode(w, num_workers=11)
+    assert_parity(o, l, o_ref, l_ref, "bf16", what=f"rope decode P{P}")
+    # defaults: q at kv_len - 1, keys from 0
+    w.q_pos = None
+    w.kv_pos_offset = None
+    o_ref, l_ref = ora.decode_workload(w)
+    o, l = run_decode(w, num_workers=11)
+    assert_parity(o, l, o_ref, l_ref, "bf16", what=f"rope decode defaults P{P}")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_rope_append_parity(causal):
+    w = wl.small_append(340, [3, 90, 200], [50, 400, 900], 16, 8, 2, causal=causal)
+    w.rope_theta = 500000.0
+    o_ref, l_ref = ora.append_workload(w)
+    o, l = run_append(w, num_workers=7)
+    assert_parity(o, l, o_ref, l_ref, "bf16", what=f"rope append c{int(causal)}")
+
+
+# ----------------------------------------------------------------------------
+# cascade / composable formats
+# ----------------------------------------------------------------------------
+def run_cascade(w, num_workers=0, prefix_workers=0):
+    import torch
+    pre, kv = w.prefix, w.kv
+    cas = abp.CascadeDecode(w.num_qo_heads, w.num_kv_heads, w.head_dim, pre.page_size,
+                            kv.page_size, torch.bfloat16 if w.dtype == "bf16" else torch.float16,
+                            max_batch=w.batch, rope_theta=w.rope_theta, num_workers=num_workers,
+                            prefix_workers=prefix_workers)
+    cas.plan(w.batch, pre.kv_indptr, pre.kv_last_page_len, kv.kv_indptr, kv.kv_last_page_len)
+    dp, ds = upload_kv(pre), upload_kv(kv)
+    q = wl.to_torch(w.q, w.dtype, "cuda")
+    o, l = cas.run(q, dp["k"], dp["v"], i32([0, w.batch]), dp["indptr"], dp["indices"], dp["lpl"],
+                   ds["k"], ds["v"], ds["indptr"], ds["indices"], ds["lpl"],
+                   q_pos=i32(w.q_pos), kv_pos_offset=i32(w.kv_pos_offset))
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), l.cpu().numpy()
+
+
+def small_cascade(seed, theta):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    B, pre_len = 5, 700
+    prefix = wl.make_paged_kv(rng, np.array([pre_len]), 256, 2, 128, "bf16", extra_pages=1)
+    suf = rng.integers(1, 300, size=B)
+    kv = wl.make_paged_kv(rng, suf, 16, 2, 128, "bf16", extra_pages=3)
+    q = wl.normal_bits(rng, (B, 8, 128), "bf16")
+    w = wl.Workload("small_cascade", "cascade", seed, "bf16", 8, 2, 128, kv, q,
+                    rope_theta=theta, prefix=prefix)
+    if theta:
+        w.kv_pos_offset = np.full(B, pre_len, np.int32)
+        w.q_pos = (pre_len + suf - 1).astype(np.int32)
+    return w
+
+
+@pytest.mark.parametrize("theta", [0.0, 500000.0])
+def test_small_cascade_parity(theta):
+    w = small_cascade(350, theta)
+    o_ref, l_ref = ora.decode_workload(w)
+    o, l = run_cascade(w, num_workers=9, prefix_workers=4)
+    assert_parity(o, l, o_ref, l_ref, "bf16", what=f"cascade theta={theta}")
+
+
+def test_cascade_rope_full_sampled():
+    """64 requests sharing an 8192-token prefix (pages of 256) plus suffixes of
+    256..1024 tokens (pages of 16), GQA 32/8, bf16, RoPE theta 500000, in the
+    default launch configuration; compared on sampled requests."""
+    w = wl.cascade_rope()
+    say(f"[case] {w.name}")
+    o, l = run_cascade(w)
+    ids = [0, 17, 40, 63]
+    o_ref, l_ref = ora.decode_workload(w, batch_ids=ids)
+    assert_parity(o, l, o_ref, l_ref, "bf16", rows=ids, what="cascade rope sampled")
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
