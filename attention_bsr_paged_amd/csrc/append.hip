@@ -40,10 +40,11 @@ namespace abp {
 namespace {
 
 constexpr int kD = 128;
-constexpr int kRows = kAppendRows;   // 128
 constexpr int kTk = kAppendTileKv;   // 64
 constexpr int kKStride = 136;        // sK row stride (uint16): 128 + 8 pad
 constexpr int kVStride = 68;         // sVt row stride (uint16): 64 + 4 pad
+constexpr float kRescaleLog2 = 8.f;  // lazy rescale threshold (log2 of the max p)
+
 
 template <typename T>
 __device__ __forceinline__ f32x4_t mfma(const uint4& a, const uint4& b, f32x4_t c);
@@ -123,14 +124,18 @@ __device__ __forceinline__ void rope_k(const uint4& u, float pos, int c,
   }
 }
 
-// RoPE variants carry hi/lo parts of q and k and run one workgroup per CU.
+// Waves per workgroup: 8 (256 rows, waves 0-3 stage K and 4-7 stage V), or 4
+// for RoPE (128 rows, every wave stages both; hi/lo operands need 512 regs).
+// One workgroup per CU either way.
 template <bool ROPE>
-constexpr int append_wg_per_cu() {
-  return ROPE ? 1 : 2;
+constexpr int append_waves() {
+  return ROPE ? 4 : 8;
 }
 
 template <typename T, int G, bool CAUSAL, bool ROPE, bool FASTPAGE>
-__global__ __launch_bounds__(256, append_wg_per_cu<ROPE>()) void append_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * append_waves<ROPE>(), 1) void append_kernel(AttnArgs a) {
+  constexpr int NW = append_waves<ROPE>();
+  constexpr int kRows = 32 * NW;
   constexpr int TQ = kRows / G;
   __shared__ __align__(16) uint16_t sK[kTk * kKStride];
   __shared__ __align__(16) uint16_t sKlo[ROPE ? kTk * kKStride : 8];  // RoPE: low parts of K
@@ -162,11 +167,17 @@ __global__ __launch_bounds__(256, append_wg_per_cu<ROPE>()) void append_kernel(A
   const uint16_t* __restrict__ kp = static_cast<const uint16_t*>(a.k_pages);
   const uint16_t* __restrict__ vp = static_cast<const uint16_t*>(a.v_pages);
 
-  // staging thread mappings
-  const int kc_chunk = tid & 15;      // K: 16-byte chunk of head_dim
-  const int k_row = tid >> 4;         // K: keys k_row + 16 i
-  const int v_kg = tid & 15;          // V: keys 4 v_kg .. 4 v_kg + 3
-  const int v_chunk = tid >> 4;       // V: 16-byte chunk of head_dim
+  const float thr = kRescaleLog2 / cl2;  // lazy rescale threshold, raw score units
+  // staging (256 threads per operand): K rows k_row + 16 i (i = 16-key group),
+  // 16-byte chunk kc_chunk; V keys 16 vw + 4 v_kg + i (16-key group vw), chunk
+  // v_chunk. With 8 waves, waves 0-3 stage K and waves 4-7 stage V.
+  const int kc_chunk = tid & 15;
+  const int k_row = (tid & 255) >> 4;
+  const int v_kg = lane & 3;
+  const int v_chunk = lane >> 2;
+  const int vw = wave & 3;
+  const bool stage_k = NW == 4 || wave < 4;
+  const bool stage_v = NW == 4 || wave >= 4;
 
   for (int s = s_begin; s < s_end; ++s) {
     const int tile = segs[4 * s];
@@ -178,6 +189,8 @@ __global__ __launch_bounds__(256, append_wg_per_cu<ROPE>()) void append_kernel(A
     const int npg = kv_indptr[b + 1] - ip0;
     const int kv_len = npg > 0 ? (npg - 1) * P + a.kv_last_page_len[b] : 0;
     const int kv_pos0 = (ROPE && a.kv_pos_offset) ? a.kv_pos_offset[b] : 0;
+    const int koff_lane = k_row * tstride + h * kD + kc_chunk * 8;       // elements
+    const int voff_lane = (4 * v_kg) * tstride + h * kD + v_chunk * 8;   // + i * tstride
 
     // ---- Q fragments (B operand of S^T = K Q^T) for this wave's 32 rows
     uint4 qf[2][4];
@@ -216,95 +229,101 @@ __global__ __launch_bounds__(256, append_wg_per_cu<ROPE>()) void append_kernel(A
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) O[md][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // ---- staging: global -> registers (next block) and registers -> LDS
-    uint4 kreg[4], vreg[4];
+    // ---- staging: global -> registers (block kb) and registers -> LDS
+    // with 8 waves a wave stages either K or V, so V reuses the K registers
+    uint4 kreg[4], vreg[NW == 4 ? 4 : 1];
+    auto vr = [&](int i) -> uint4& {
+      if constexpr (NW == 4) return vreg[i];
+      else return kreg[i];
+    };
     auto gload = [&](int kb) {
       if constexpr (FASTPAGE) {
-        // one page id per 16-key group (scalar), clamped to the last valid group
+        // one page id per 16-key group, on the scalar unit; groups past the
+        // segment end re-read the last valid group (in bounds, masked)
         const int last16 = (kv_end - 1) & ~15;
-        int pid[4], kk[4];
+        if (stage_k) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          kk[i] = min(kb + 16 * i, last16);
-          pid[i] = kv_indices[ip0 + (kk[i] >> shift)];
+          for (int i = 0; i < 4; ++i) {
+            const int kk = min(kb + 16 * i, last16);
+            const int64_t base = (int64_t)kv_indices[ip0 + (kk >> shift)] * a.page_stride +
+                                 (int64_t)(kk & (P - 1)) * tstride;
+            kreg[i] = *reinterpret_cast<const uint4*>(kp + base + koff_lane);
+          }
         }
+        if (stage_v) {
+          const int kk = min(kb + 16 * vw, last16);  // wave-uniform
+          const int64_t vb = (int64_t)kv_indices[ip0 + (kk >> shift)] * a.page_stride +
+                             (int64_t)(kk & (P - 1)) * tstride;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t at = (int64_t)pid[i] * a.page_stride +
-                             (int64_t)((kk[i] & (P - 1)) + k_row) * tstride + h * kD + kc_chunk * 8;
-          kreg[i] = *reinterpret_cast<const uint4*>(kp + at);
-        }
-        const int gi = v_kg >> 2;  // 16-key group of this thread's V keys
-        const int vpid = gi == 0 ? pid[0] : gi == 1 ? pid[1] : gi == 2 ? pid[2] : pid[3];
-        const int vkk = gi == 0 ? kk[0] : gi == 1 ? kk[1] : gi == 2 ? kk[2] : kk[3];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t at = (int64_t)vpid * a.page_stride +
-                             (int64_t)((vkk & (P - 1)) + (4 * v_kg & 15) + i) * tstride + h * kD +
-                             v_chunk * 8;
-          vreg[i] = *reinterpret_cast<const uint4*>(vp + at);
+          for (int i = 0; i < 4; ++i)
+            vr(i) = *reinterpret_cast<const uint4*>(vp + vb + voff_lane + i * tstride);
         }
       } else {
+        if (stage_k) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = min(kb + k_row + 16 * i, kv_end - 1);
-          int page, off;
-          if (shift >= 0) {
-            page = key >> shift;
-            off = key & (P - 1);
-          } else {
-            page = key / P;
-            off = key - page * P;
+          for (int i = 0; i < 4; ++i) {
+            const int key = min(kb + k_row + 16 * i, kv_end - 1);
+            int page, off;
+            if (shift >= 0) {
+              page = key >> shift;
+              off = key & (P - 1);
+            } else {
+              page = key / P;
+              off = key - page * P;
+            }
+            const int64_t pg = a.kv_indices[ip0 + page];
+            kreg[i] = *reinterpret_cast<const uint4*>(kp + pg * a.page_stride +
+                                                      (int64_t)off * tstride + h * kD + kc_chunk * 8);
           }
-          const int64_t pg = a.kv_indices[ip0 + page];
-          kreg[i] = *reinterpret_cast<const uint4*>(kp + pg * a.page_stride +
-                                                    (int64_t)off * tstride + h * kD + kc_chunk * 8);
         }
+        if (stage_v) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = min(kb + 4 * v_kg + i, kv_end - 1);
-          int page, off;
-          if (shift >= 0) {
-            page = key >> shift;
-            off = key & (P - 1);
-          } else {
-            page = key / P;
-            off = key - page * P;
-          }
-          const int64_t pg = a.kv_indices[ip0 + page];
-          vreg[i] = *reinterpret_cast<const uint4*>(vp + pg * a.page_stride +
+          for (int i = 0; i < 4; ++i) {
+            const int key = min(kb + 16 * vw + 4 * v_kg + i, kv_end - 1);
+            int page, off;
+            if (shift >= 0) {
+              page = key >> shift;
+              off = key & (P - 1);
+            } else {
+              page = key / P;
+              off = key - page * P;
+            }
+            const int64_t pg = a.kv_indices[ip0 + page];
+            vr(i) = *reinterpret_cast<const uint4*>(vp + pg * a.page_stride +
                                                     (int64_t)off * tstride + h * kD + v_chunk * 8);
+          }
         }
       }
     };
     auto swrite = [&](int kb) {
+      if (stage_k) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int at = (k_row + 16 * i) * kKStride + kc_chunk * 8;
-        if constexpr (ROPE) {
-          float kr[8];
-          rope_k<T>(kreg[i], (float)(kv_pos0 + kb + k_row + 16 * i), kc_chunk, rope, kr);
-          uint4 hi, lo;
-          split8<T>(kr, hi, lo);
-          *reinterpret_cast<uint4*>(&sK[at]) = hi;
-          *reinterpret_cast<uint4*>(&sKlo[at]) = lo;
-        } else {
-          *reinterpret_cast<uint4*>(&sK[at]) = kreg[i];
+        for (int i = 0; i < 4; ++i) {
+          const int at = (k_row + 16 * i) * kKStride + kc_chunk * 8;
+          if constexpr (ROPE) {
+            float kr[8];
+            rope_k<T>(kreg[i], (float)(kv_pos0 + kb + k_row + 16 * i), kc_chunk, rope, kr);
+            uint4 hi, lo;
+            split8<T>(kr, hi, lo);
+            *reinterpret_cast<uint4*>(&sK[at]) = hi;
+            *reinterpret_cast<uint4*>(&sKlo[at]) = lo;
+          } else {
+            *reinterpret_cast<uint4*>(&sK[at]) = kreg[i];
+          }
         }
       }
-      // V^T: element e of the 4 keys 4 v_kg .. 4 v_kg + 3 as one 8-byte row piece
+      if (stage_v) {
+        // V^T: element d of the 4 keys 16 vw + 4 v_kg + 0..3 as one 8-byte piece
+        uint16_t* V = sVt + 16 * vw + 4 * v_kg;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t w0 = word(vreg[0], j), w1 = word(vreg[1], j);
-        const uint32_t w2 = word(vreg[2], j), w3 = word(vreg[3], j);
-        uint2 lo, hi;
-        lo.x = pair_lo(w0, w1);
-        lo.y = pair_lo(w2, w3);
-        hi.x = pair_hi(w0, w1);
-        hi.y = pair_hi(w2, w3);
-        const int d = v_chunk * 8 + 2 * j;
-        *reinterpret_cast<uint2*>(&sVt[d * kVStride + 4 * v_kg]) = lo;
-        *reinterpret_cast<uint2*>(&sVt[(d + 1) * kVStride + 4 * v_kg]) = hi;
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t w0 = word(vr(0), j), w1 = word(vr(1), j);
+          const uint32_t w2 = word(vr(2), j), w3 = word(vr(3), j);
+          const int d = v_chunk * 8 + 2 * j;
+          *reinterpret_cast<uint2*>(&V[d * kVStride]) = make_uint2(pair_lo(w0, w1), pair_lo(w2, w3));
+          *reinterpret_cast<uint2*>(&V[(d + 1) * kVStride]) =
+              make_uint2(pair_hi(w0, w1), pair_hi(w2, w3));
+        }
       }
     };
 
@@ -353,42 +372,50 @@ __global__ __launch_bounds__(256, append_wg_per_cu<ROPE>()) void append_kernel(A
             }
           }
       }
-      // ---- online softmax per row; P packed as the B operand of the PV product
+      // ---- online softmax per row (lazy rescale); P packed as the PV B operand
+      float mx[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        float x = kNegInf;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+          x = __builtin_fmaxf(x, __builtin_fmaxf(__builtin_fmaxf(S[mb][nb][0], S[mb][nb][1]),
+                                                 __builtin_fmaxf(S[mb][nb][2], S[mb][nb][3])));
+        x = __builtin_fmaxf(x, __shfl_xor(x, 16));
+        mx[nb] = __builtin_fmaxf(x, __shfl_xor(x, 32));
+      }
+      // the reference max moves only when a score exceeds it by more than thr
+      if (__builtin_amdgcn_ballot_w64((mx[0] > m[0] + thr) || (mx[1] > m[1] + thr))) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const float mn = __builtin_fmaxf(m[nb], mx[nb]);
+          const float alpha = mn == kNegInf ? 1.f : fast_exp2((m[nb] - mn) * cl2);
+          m[nb] = mn;
+          lsum[nb] *= alpha;
+#pragma unroll
+          for (int md = 0; md < 8; ++md) O[md][nb] *= alpha;
+        }
+      }
       uint4 pB[2][2];  // [kc2][nb]
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        float mx = kNegInf;
+        const float mc = (m[nb] == kNegInf ? 0.f : m[nb]) * cl2;
+        float p[4][4];
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
-          mx = __builtin_fmaxf(mx, __builtin_fmaxf(__builtin_fmaxf(S[mb][nb][0], S[mb][nb][1]),
-                                                   __builtin_fmaxf(S[mb][nb][2], S[mb][nb][3])));
-        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16));
-        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
-        const float mn = __builtin_fmaxf(m[nb], mx);
-        const float mu = mn == kNegInf ? 0.f : mn;
-        const float alpha = fast_exp2((m[nb] - mu) * cl2);
-        m[nb] = mn;
-        lsum[nb] *= alpha;
 #pragma unroll
-        for (int md = 0; md < 8; ++md) O[md][nb] *= alpha;
-        const float mc = mu * cl2;
-        float p[4][4];
+          for (int j = 0; j < 4; ++j) p[mb][j] = fast_exp2(__builtin_fmaf(S[mb][nb][j], cl2, -mc));
+        // row sum in fp32 of the unrounded p: lse must not carry P's 16-bit rounding
         float ps = 0.f;
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            p[mb][j] = fast_exp2(__builtin_fmaf(S[mb][nb][j], cl2, -mc));
-            ps += p[mb][j];
-          }
+        for (int mb = 0; mb < 4; ++mb) ps += (p[mb][0] + p[mb][1]) + (p[mb][2] + p[mb][3]);
         lsum[nb] += ps;
 #pragma unroll
-        for (int kc2 = 0; kc2 < 2; ++kc2) {
+        for (int kc2 = 0; kc2 < 2; ++kc2)
           pB[kc2][nb] = make_uint4(pack2<T>(p[2 * kc2][0], p[2 * kc2][1]),
                                    pack2<T>(p[2 * kc2][2], p[2 * kc2][3]),
                                    pack2<T>(p[2 * kc2 + 1][0], p[2 * kc2 + 1][1]),
                                    pack2<T>(p[2 * kc2 + 1][2], p[2 * kc2 + 1][3]));
-        }
       }
       // ---- O^T += V^T P^T: K-slots of lane group g16 are keys 4 g16..+3 and 16 + 4 g16..+3
 #pragma unroll
@@ -458,9 +485,9 @@ __global__ __launch_bounds__(256, append_wg_per_cu<ROPE>()) void append_kernel(A
 template <typename T, int G, bool CAUSAL, bool ROPE>
 hipError_t launch_f(const AttnArgs& a, hipStream_t s) {
   if (a.page_shift >= 4)
-    append_kernel<T, G, CAUSAL, ROPE, true><<<a.workers, 256, 0, s>>>(a);
+    append_kernel<T, G, CAUSAL, ROPE, true><<<a.workers, 64 * append_waves<ROPE>(), 0, s>>>(a);
   else
-    append_kernel<T, G, CAUSAL, ROPE, false><<<a.workers, 256, 0, s>>>(a);
+    append_kernel<T, G, CAUSAL, ROPE, false><<<a.workers, 64 * append_waves<ROPE>(), 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -495,9 +522,9 @@ int append_blocks_per_cu(const Config& cfg) {
   // the tile shape is shared by all variants; RoPE ones are built for one per CU
   hipError_t e =
       cfg.rope ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                     &n, append_kernel<BF16, 4, true, true, true>, 256, 0)
+                     &n, append_kernel<BF16, 4, true, true, true>, 64 * append_waves<true>(), 0)
                : hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                     &n, append_kernel<BF16, 4, true, false, true>, 256, 0);
+                     &n, append_kernel<BF16, 4, true, false, true>, 64 * append_waves<false>(), 0);
   return e == hipSuccess && n > 0 ? n : 1;
 }
 

@@ -69,7 +69,9 @@ struct Layout {
 
 // Tile sizes of the kernels.
 constexpr int kDecodeTileKv = 64;   // keys per work block (decode)
-constexpr int kAppendRows = 128;    // MFMA rows per append tile = tile_q * group
+// MFMA rows per append tile (= tile_q * group): 8 waves x 32 rows, or 4 waves
+// for the RoPE variant (its hi/lo operands need the registers of 1 wave/SIMD)
+constexpr int append_rows(bool rope) { return rope ? 128 : 256; }
 constexpr int kAppendTileKv = 64;   // keys per work block (append)
 
 }  // namespace abp

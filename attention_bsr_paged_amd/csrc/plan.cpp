@@ -114,9 +114,9 @@ int make_layout_caps(const Config& cfg, int64_t max_tiles, int32_t workers, Layo
     L.tile_kv = kDecodeTileKv;
     L.rows = cfg.group;
   } else {
-    L.tile_q = kAppendRows / cfg.group;
+    L.rows = append_rows(cfg.rope != 0);
+    L.tile_q = L.rows / cfg.group;
     L.tile_kv = kAppendTileKv;
-    L.rows = kAppendRows;
   }
   const int64_t max_segs = max_tiles + workers - 1;
   // a tile cut k >= 2 times uses k slots and k - 1 of the W - 1 inner worker boundaries
@@ -161,7 +161,7 @@ int make_layout(const Config& cfg, int32_t max_batch, int32_t max_qo_tokens, int
     max_tiles = int64_t(max_batch) * cfg.hkv;
   } else {
     // sum_b ceil(qo_b / tile_q) <= sum_qo / tile_q + batch
-    const int64_t tile_q = kAppendRows / cfg.group;
+    const int64_t tile_q = append_rows(cfg.rope != 0) / cfg.group;
     max_tiles = (ceil_div(max_qo_tokens, tile_q) + max_batch) * int64_t(cfg.hkv);
   }
   return make_layout_caps(cfg, max_tiles, workers, out, err);

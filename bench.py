@@ -84,6 +84,8 @@ def main(argv=None) -> int:
     ap.add_argument("--workers", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-append", action="store_true")
+    ap.add_argument("--part", choices=["all", "decode", "append"], default="all",
+                    help="decode or append alone (profiling); 'all' is the benchmark line")
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the paged attention path has no multi-GPU "
@@ -99,6 +101,9 @@ def main(argv=None) -> int:
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     abp.load_library()
+    if args.part == "append":
+        print(json.dumps(bench_append(abp, wl, torch, dev, args.steps, args.warmup)), flush=True)
+        return 0
 
     # ------------------------------------------------------------------ decode
     w = wl.batch_decode_gqa()
@@ -199,7 +204,7 @@ def main(argv=None) -> int:
     }
 
     # ------------------------------------------------------------------ append
-    if not args.no_append:
+    if not args.no_append and args.part == "all":
         try:
             out["append"] = bench_append(abp, wl, torch, dev, max(20, K // 4), 5)
         except abp.AbpError as e:

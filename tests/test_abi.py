@@ -121,7 +121,7 @@ def _compare(kind, p, B, qo_indptr, kv_indptr, lpl, W, G, max_qo=0):
         ref = plan_ref(KIND_DECODE, B, kv_indptr, lpl, p.page_size, p.num_kv_heads, W, 64)
     else:
         ref = plan_ref(KIND_APPEND, B, kv_indptr, lpl, p.page_size, p.num_kv_heads, W, 64,
-                       qo_indptr=qo_indptr, tile_q=128 // G, causal=bool(p.causal))
+                       qo_indptr=qo_indptr, tile_q=256 // G, causal=bool(p.causal))
     for k, v in ref.items():
         assert np.array_equal(got[k], v), k
     assert plan.num_segments == len(ref["seg_tile"])
