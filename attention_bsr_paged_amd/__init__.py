@@ -194,13 +194,13 @@ def decode_plan_arrays(blob: np.ndarray, plan: AbpPlan):
     H = {k: i for i, k in enumerate(
         ["MAGIC", "KIND", "BATCH", "WORKERS", "NUM_TILES", "NUM_SEGS", "NUM_PARTIALS",
          "NUM_MERGES", "TILE_Q", "TILE_KV", "ROWS", "GROUP", "NUM_KV_HEADS", "PAGE_SIZE",
-         "NUM_BLOCKS", "QUOTA", "OFF_WSEG", "OFF_SEG", "OFF_TILE", "OFF_MERGE", "OFF_ROPE"])}
+         "NUM_BLOCKS", "QUOTA", "OFF_WSEG", "OFF_SEG", "OFF_TILE", "OFF_MERGE", "OFF_ROPE",
+         "MAX_TILES", "MAX_SEGS", "MAX_PARTIALS", "CAUSAL", "OFF_CNT", "OFF_NTILE"])}
     W, T, S, M = b[H["WORKERS"]], b[H["NUM_TILES"]], b[H["NUM_SEGS"]], b[H["NUM_MERGES"]]
     seg = b[b[H["OFF_SEG"]]: b[H["OFF_SEG"]] + 4 * S].reshape(S, 4)
     tile = b[b[H["OFF_TILE"]]: b[H["OFF_TILE"]] + 4 * T].reshape(T, 4)
     mrg = b[b[H["OFF_MERGE"]]: b[H["OFF_MERGE"]] + 4 * M].reshape(M, 4)
-    num_partials = np.zeros(T, np.int32)
-    num_partials[mrg[:, 0]] = mrg[:, 2]
+    num_partials = b[b[H["OFF_NTILE"]]: b[H["OFF_NTILE"]] + T].copy()
     return {
         "num_blocks": b[H["NUM_BLOCKS"]: H["NUM_BLOCKS"] + 1].copy(),
         "quota": b[H["QUOTA"]: H["QUOTA"] + 1].copy(),

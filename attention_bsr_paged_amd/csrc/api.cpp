@@ -156,8 +156,6 @@ void fill_args(const abp::Config& cfg, const abp::Layout& L, const abp_plan* pla
   a->lse_part = a->o_part + int64_t(L.max_partials) * L.rows * cfg.head_dim;
 }
 
-int merge_grid(const abp_plan* plan) { return plan->num_workers; }
-
 }  // namespace
 
 extern "C" {
@@ -292,7 +290,9 @@ int abp_decode_run(const abp_plan* plan, const abp_params* params, const void* q
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     hipError_t e = abp::launch_decode(cfg, a, s);
     if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
-    e = abp::launch_plan_merge(cfg, a, merge_grid(plan), s);
+    // decode tiles are split often and are cheap: a second launch merges them
+    // (append merges its few split tiles inside the kernel)
+    e = abp::launch_plan_merge(cfg, a, plan->num_workers, s);
     if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
     return ABP_OK;
   } catch (...) {
@@ -332,8 +332,6 @@ int abp_append_run(const abp_plan* plan, const abp_params* params, const void* q
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     hipError_t e = abp::launch_append(cfg, a, s);
     if (e != hipSuccess) return hip_fail(e, "append kernel launch");
-    e = abp::launch_plan_merge(cfg, a, merge_grid(plan), s);
-    if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
     return ABP_OK;
   } catch (...) {
     return fail(ABP_ERR_HIP, "exception");

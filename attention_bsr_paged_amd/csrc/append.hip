@@ -34,6 +34,7 @@
 #include "common.h"
 #include "kernels.h"
 #include "layout.h"
+#include "tile_merge.h"
 
 namespace abp {
 
@@ -140,6 +141,7 @@ __global__ __launch_bounds__(64 * append_waves<ROPE>(), 1) void append_kernel(At
   __shared__ __align__(16) uint16_t sK[kTk * kKStride];
   __shared__ __align__(16) uint16_t sKlo[ROPE ? kTk * kKStride : 8];  // RoPE: low parts of K
   __shared__ __align__(16) uint16_t sVt[kD * kVStride];
+  __shared__ int s_last;
 
   const ABP_CONST_AS int32_t* plan = const_as(a.plan);
   const ABP_CONST_AS int32_t* wseg = plan + plan[H_OFF_WSEG];
@@ -478,6 +480,14 @@ __global__ __launch_bounds__(64 * append_waves<ROPE>(), 1) void append_kernel(At
           if (g16 == 0) a.lse_part[prow] = lse;
         }
       }
+    }
+    if (slot >= 0) {
+      merge_if_last(a, tile, kRows, &s_last, [&](int r, int64_t* orow) {
+        const int tloc = qt * TQ + r / G;
+        if (tloc >= qo_len) return false;
+        *orow = (int64_t)(q0 + tloc) * a.num_qo_heads + h * G + (r % G);
+        return true;
+      });
     }
   }
 }

@@ -40,7 +40,8 @@ hipError_t launch_decode(const Config& cfg, const AttnArgs& a, hipStream_t strea
 int decode_blocks_per_cu(const Config& cfg);
 int append_blocks_per_cu(const Config& cfg);
 hipError_t launch_append(const Config& cfg, const AttnArgs& a, hipStream_t stream);
-// merges the split tiles of a plan into o / lse (fixed grid, reads counts from the plan)
+// merges the split tiles of a decode plan into o / lse after the decode kernel
+// (fixed grid; counts are read from the plan at run time)
 hipError_t launch_plan_merge(const Config& cfg, const AttnArgs& a, int32_t grid,
                              hipStream_t stream);
 

@@ -36,16 +36,21 @@ enum Header : int {
   H_MAX_SEGS,
   H_MAX_PARTIALS,
   H_CAUSAL,
+  H_OFF_CNT,     // per-tile arrival counters of split tiles (zero in every upload)
+  H_OFF_NTILE,   // per-tile number of partials
   HEADER_INTS = 32
 };
 
 constexpr int32_t kMagic = 0x41425031;  // "ABP1"
 constexpr int kMaxRopePairs = 64;        // head_dim 128
 
-// Records (int32 x 4 each, 16-byte aligned in the blob):
-//   seg   {tile, kv_begin, kv_end, partial_slot or -1}
-//   tile  {b, kv_head, q_tile, first_partial or -1}
-//   merge {tile, first_partial, num_partials, 0}
+// Records (16-byte aligned in the blob):
+//   seg   int32 x 4 {tile, kv_begin, kv_end, partial_slot or -1}
+//   tile  int32 x 4 {b, kv_head, q_tile, first_partial or -1}
+//   ntile int32 x 1 number of partials of the tile (0 if not split)
+//   merge int32 x 4 {tile, first_partial, num_partials, 0}
+//   cnt   int32 x 1 per tile: segments of a split tile that have written their
+//         partial; the last one merges the tile and resets it to 0
 // worker_seg_indptr has num_workers + 1 entries.
 // rope: kMaxRopePairs x {hi, lo} float32 bit patterns of theta^(-2j/d) / (2 pi)
 //       (revolutions per position), split so hi + lo carries ~48 bits.
@@ -59,7 +64,8 @@ struct Layout {
   int32_t tile_q = 1;
   int32_t tile_kv = 64;
   int32_t rows = 1;
-  int64_t off_wseg = 0, off_seg = 0, off_tile = 0, off_merge = 0, off_rope = 0;
+  int64_t off_wseg = 0, off_seg = 0, off_tile = 0, off_ntile = 0, off_merge = 0, off_rope = 0,
+          off_cnt = 0;
   int64_t plan_ints = 0;       // total int32 of the blob
   uint64_t plan_bytes = 0;
   uint64_t partial_offset = 0; // bytes, 256-aligned

@@ -78,18 +78,19 @@ __global__ __launch_bounds__(256) void merge_two_kernel(const void* o_a, const f
   if (lse_out && e0 == 0) lse_out[row] = lse;
 }
 
-// Merge the split tiles of a plan. Grid is fixed; work items are
-// (merge entry, block of 16 tile rows), read from the plan header at run time.
+// Merge the split tiles of a decode plan after the decode kernel (the kernel
+// boundary orders the partial stores before these loads). Grid is fixed; work
+// items are (merge entry, block of 16 tile rows), read from the plan header.
 template <int OUT_DT>
 __global__ __launch_bounds__(256) void plan_merge_kernel(AttnArgs a) {
-  const int32_t* plan = a.plan;
+  const ABP_CONST_AS int32_t* plan = const_as(a.plan);
   const int kind = plan[H_KIND];
   const int rows = plan[H_ROWS];
   const int G = plan[H_GROUP];
   const int Tq = plan[H_TILE_Q];
   const int num_merges = plan[H_NUM_MERGES];
-  const int4* tiles = reinterpret_cast<const int4*>(plan + plan[H_OFF_TILE]);
-  const int4* merges = reinterpret_cast<const int4*>(plan + plan[H_OFF_MERGE]);
+  const ABP_CONST_AS int32_t* tiles = plan + plan[H_OFF_TILE];
+  const ABP_CONST_AS int32_t* merges = plan + plan[H_OFF_MERGE];
   const int row_blocks = (rows + 15) / 16;
   const int items = num_merges * row_blocks;
   const int e0 = (threadIdx.x & 15) * 8;
@@ -97,24 +98,24 @@ __global__ __launch_bounds__(256) void plan_merge_kernel(AttnArgs a) {
     const int m = item / row_blocks;
     const int r = (item % row_blocks) * 16 + (threadIdx.x >> 4);
     if (r >= rows) continue;
-    const int4 mr = merges[m];
-    const int4 tl = tiles[mr.x];
+    const int mtile = merges[4 * m], mfirst = merges[4 * m + 1], mnum = merges[4 * m + 2];
+    const int tb = tiles[4 * mtile], th = tiles[4 * mtile + 1], tq = tiles[4 * mtile + 2];
     int64_t token;
     int head;
     if (kind == ABP_KIND_DECODE) {
-      token = tl.x;
-      head = tl.y * G + r;
+      token = tb;
+      head = th * G + r;
     } else {
-      const int q0 = a.qo_indptr[tl.x];
-      const int qo_len = a.qo_indptr[tl.x + 1] - q0;
-      const int tloc = tl.z * Tq + r / G;
+      const int q0 = a.qo_indptr[tb];
+      const int qo_len = a.qo_indptr[tb + 1] - q0;
+      const int tloc = tq * Tq + r / G;
       if (tloc >= qo_len) continue;
       token = q0 + tloc;
-      head = tl.y * G + (r % G);
+      head = th * G + (r % G);
     }
-    const int n = mr.z;
+    const int n = mnum;
     float M = kNegInf;
-    for (int i = 0; i < n; ++i) M = __builtin_fmaxf(M, a.lse_part[int64_t(mr.y + i) * rows + r]);
+    for (int i = 0; i < n; ++i) M = __builtin_fmaxf(M, a.lse_part[int64_t(mfirst + i) * rows + r]);
     float out[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) out[e] = 0.f;
@@ -122,10 +123,10 @@ __global__ __launch_bounds__(256) void plan_merge_kernel(AttnArgs a) {
     if (M != kNegInf) {
       float tot = 0.f;
       for (int i = 0; i < n; ++i)
-        tot += fast_exp2((a.lse_part[int64_t(mr.y + i) * rows + r] - M) * kLog2e);
+        tot += fast_exp2((a.lse_part[int64_t(mfirst + i) * rows + r] - M) * kLog2e);
       lse = M + fast_log2(tot) * kLn2;
       for (int i = 0; i < n; ++i) {
-        const int64_t sr = int64_t(mr.y + i) * rows + r;
+        const int64_t sr = int64_t(mfirst + i) * rows + r;
         const float w = fast_exp2((a.lse_part[sr] - lse) * kLog2e);
         float v[8];
         load8<ABP_F32>(a.o_part, sr * 128 + e0, v);

@@ -137,10 +137,14 @@ int make_layout_caps(const Config& cfg, int64_t max_tiles, int32_t workers, Layo
   off += 4 * max_segs;
   L.off_tile = off;
   off += 4 * max_tiles;
+  L.off_ntile = off;
+  off += align4(max_tiles);
   L.off_merge = off;
   off += 4 * max_merges;
   L.off_rope = off;
   off += 2 * kMaxRopePairs;
+  L.off_cnt = off;
+  off += align4(max_tiles);
   L.plan_ints = off;
   L.plan_bytes = uint64_t(off) * 4;
   L.partial_offset = (L.plan_bytes + 255) & ~uint64_t(255);
@@ -259,6 +263,7 @@ int plan_compute(const Config& cfg, const Layout& L, int32_t batch, const int32_
   int32_t* wseg = blob + L.off_wseg;
   int32_t* seg = blob + L.off_seg;
   int32_t* tile = blob + L.off_tile;
+  int32_t* ntile = blob + L.off_ntile;
   int32_t* mrg = blob + L.off_merge;
 
   // tiles, segments, partial slots, merge list (pass 2)
@@ -279,6 +284,7 @@ int plan_compute(const Config& cfg, const Layout& L, int32_t batch, const int32_
         tr[1] = h;
         tr[2] = (int32_t)qt;
         tr[3] = nseg > 1 ? (int32_t)slot : -1;
+        ntile[t] = nseg > 1 ? (int32_t)nseg : 0;
         if (nseg > 1) {
           int32_t* mr = mrg + 4 * m++;
           mr[0] = (int32_t)t;
@@ -338,6 +344,8 @@ int plan_compute(const Config& cfg, const Layout& L, int32_t batch, const int32_
   blob[H_MAX_SEGS] = L.max_segs;
   blob[H_MAX_PARTIALS] = L.max_partials;
   blob[H_CAUSAL] = cfg.causal;
+  blob[H_OFF_CNT] = (int32_t)L.off_cnt;  // counters stay zero (memset above)
+  blob[H_OFF_NTILE] = (int32_t)L.off_ntile;
 
   plan->kind = cfg.kind;
   plan->batch = batch;
