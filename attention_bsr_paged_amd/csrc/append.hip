@@ -11,9 +11,11 @@
 // section (动态负载均衡调度). Unlike decode, each K/V element is reused by up
 // to 128 query rows, so this path is bound by matrix-core throughput.
 //
-// Tiles: 128 rows = tile_q tokens x G qo heads of one kv head (row r is token
-// r / G, head r % G), against blocks of 64 keys. A 256-thread workgroup is one
-// worker; wave w owns rows [32 w, 32 w + 32) (two 16-row column blocks).
+// Tiles: 256 rows = tile_q tokens x G qo heads of one kv head (row r is token
+// r / G, head r % G), against blocks of 64 keys. A 512-thread workgroup (8
+// waves) is one worker; wave w owns rows [32 w, 32 w + 32) (two 16-row column
+// blocks). The RoPE variant uses 128-row tiles and 4 waves: its split q
+// operands need the registers of one wave per SIMD.
 //
 //   S^T = K Q^T    v_mfma_f32_16x16x32 with A = K rows (LDS, row-major,
 //                  padded) and B = Q^T (registers). The accumulator gives each
@@ -27,7 +29,9 @@
 //                  the order in which S holds the keys, so no lane exchange.
 //
 // The next block's K/V are loaded into registers while the current block is
-// computed, then stored to LDS. With a power-of-two page size >= 16, a block's
+// computed, then stored to LDS (K by the first half of the waves, V transposed
+// by the second half). A tile split over several workers is merged by the
+// workgroup whose partial state arrives last (per-tile arrival counters). With a power-of-two page size >= 16, a block's
 // page ids are scalar loads (one per 16-key group). Workers are mapped to
 // workgroup ids XCD-major, so consecutive workers (which usually share the
 // same request and kv head) run on the same XCD and share its L2.

@@ -2,27 +2,37 @@
 """Benchmark of paged BSR attention on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--part all|decode|append|single|skewed|cascade|copy]
 
 A step is one pass of the hot path over one batch of the batch paged decode
 workload (64 requests, GQA 32/8, head_dim 128, page 16, bf16, kv_len uniform on
-[512, 4096]): the CPU plan of the batch, its upload, the persistent decode
-kernel and the merge of split tiles. Inputs are resident in HBM before the timed
-region; the K/V pools are replicated and rotated so that no step can hit data
-a previous step left in the 256 MB last-level cache.
+[512, 4096]): the CPU plan of the batch (validation, kv lengths, Stream-K
+partition), its upload, the persistent decode kernel and the merge of split
+tiles. Inputs are resident in HBM before the timed region; the K/V pools are
+replicated and rotated (at least 2 GiB in all) so that no step reads data a
+previous step left in the 256 MB last-level cache.
 
-Prints one JSON line. ``value`` is achieved HBM throughput of the step in TB/s
-(algorithmic bytes: valid K/V tokens + q + o + lse + page indices).
-``roofline`` is the decode kernel(s) alone, timed with HIP events on their
-stream. ``append`` is the ragged causal append workload (16 requests, qo
-U{128..1024} onto kv U{1024..8192}, GQA 32/8, bf16) in TFLOP/s of causal
-algorithmic work. ``cpu_baseline`` is the fp64 oracle on a bounded sample.
+Prints one JSON line. ``value`` is achieved HBM throughput of the whole step in
+TB/s (algorithmic bytes: each valid K/V token once, plus q, o, lse and the
+page indices). ``roofline`` is the decode run alone (decode kernel + merge
+kernel), timed with HIP events on the stream it is launched on. ``append`` is
+the ragged causal append workload (16 requests, qo U{128..1024} onto kv
+U{1024..8192}, GQA 32/8, bf16) in TFLOP/s of visible (unmasked) work;
+``configs`` holds the single-request, skewed-batch and cascade+RoPE decode
+workloads. ``cpu_baseline`` is the fp64 oracle on a bounded sample of the batch
+decode workload, on the host cores of the same machine.
+
+``--part copy`` times a plain 1 GiB device copy (read + write of known size);
+its counter readings calibrate FETCH_SIZE / WRITE_SIZE for the traffic figure.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -31,51 +41,386 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_TBS = 8.0           # MI355X HBM3E, TB/s
-MFMA_BF16_PEAK_TFLOPS = 2516.6  # dense bf16 MFMA, 256 CU x 4096 flop/clk x 2.4 GHz
+HBM_PEAK_TBS = 8.0              # MI355X HBM3E, TB/s
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+FLUSH_BYTES = 2 * 2 ** 30       # K/V replicas rotated per step (>> 256 MB MALL)
+
+# Counter readings (FETCH_SIZE / WRITE_SIZE) of the decode run and of a plain
+# copy, recorded by rocprofv3; valid only while the kernel sources hash the same.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_run_batch_decode_traffic.txt")
+DECODE_SOURCES = ["decode.hip", "merge.hip", "common.h", "kernels.h", "layout.h"]
 
 
+def decode_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in DECODE_SOURCES:
+        with open(os.path.join(ROOT, "attention_bsr_paged_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """Bytes per decode run from the committed counter summary, or None when the
+    summary is absent or the kernel sources changed since it was taken."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    m = re.search(r"^TRAFFIC (\{.*\})\s*$", text, re.M)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("source_sha256_16") != decode_source_hash():
+        return None
+    return rec
+
+
+# ----------------------------------------------------------------------------
+# algorithmic work
+# ----------------------------------------------------------------------------
 def decode_bytes(w, batch_ids=None) -> int:
     """Algorithmic bytes of a decode batch: each valid K/V token once, q, o, lse, indices."""
     kv = w.kv
-    ids = range(w.batch) if batch_ids is None else batch_ids
+    ids = list(range(w.batch) if batch_ids is None else batch_ids)
     tokens = int(sum(int(kv.kv_len[b]) for b in ids))
     pages = int(sum(int(kv.kv_indptr[b + 1] - kv.kv_indptr[b]) for b in ids))
-    n = len(list(ids))
+    n = len(ids)
     elt = 2
     kvb = tokens * w.num_kv_heads * w.head_dim * 2 * elt
     qo = 2 * n * w.num_qo_heads * w.head_dim * elt
     return kvb + qo + n * w.num_qo_heads * 4 + pages * 4 + (n + 1) * 4 + n * 4
 
 
-def append_flops(w) -> float:
+def cascade_bytes(w) -> int:
+    """The shared prefix once, every suffix token once, q, o, lse and indices."""
+    pre = w.prefix
+    pre_tokens = int(pre.kv_len.sum())
+    kv_row = w.num_kv_heads * w.head_dim * 2 * 2
+    return decode_bytes(w) + pre_tokens * kv_row + int(pre.kv_indptr[-1]) * 4
+
+
+def append_flops(w, token_ids=None) -> float:
     """Causal algorithmic FLOP: 4 * d * Hq per visible (query, key) pair."""
-    qo = np.diff(w.qo_indptr).astype(np.float64)
-    kv = w.kv.kv_len.astype(np.float64)
-    pairs = (qo * (kv - qo) + qo * (qo + 1) / 2).sum() if w.causal else (qo * kv).sum()
-    return 4.0 * w.head_dim * w.num_qo_heads * pairs
+    qo = np.diff(w.qo_indptr).astype(np.int64)
+    kv = w.kv.kv_len.astype(np.int64)
+    if token_ids is None:
+        if w.causal:
+            pairs = (qo * (kv - qo) + qo * (qo + 1) // 2).sum()
+        else:
+            pairs = (qo * kv).sum()
+    else:
+        pairs = 0
+        for t in token_ids:
+            b = int(np.searchsorted(w.qo_indptr, t, side="right") - 1)
+            i = t - int(w.qo_indptr[b])
+            pairs += int(kv[b] - qo[b] + i + 1) if w.causal else int(kv[b])
+    return 4.0 * w.head_dim * w.num_qo_heads * float(pairs)
 
 
-def cpu_baseline_decode(w, budget_s: float = 12.0):
-    """The fp64 oracle on whole requests until ~budget_s of CPU work (1 BLAS thread)."""
+# ----------------------------------------------------------------------------
+# timing helpers
+# ----------------------------------------------------------------------------
+def _stats_ms(ms: np.ndarray) -> dict:
+    return {"avg_us": round(float(ms.mean()) * 1e3, 2),
+            "median_us": round(float(np.median(ms)) * 1e3, 2),
+            "p10_us": round(float(np.percentile(ms, 10)) * 1e3, 2),
+            "p90_us": round(float(np.percentile(ms, 90)) * 1e3, 2)}
+
+
+def timed_steps(torch, stream, step, K, Wm):
+    """Wm untimed steps, then K timed ones; step(i, (ev0, ev1) or None) records the
+    events around the GPU run. Returns (wall ms per step, run ms per step)."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    for i in range(Wm):
+        step(i, None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(Wm + i, ev[i])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / K
+    return wall, np.array([a.elapsed_time(b) for a, b in ev])
+
+
+def replicas(t, torch, total_bytes):
+    n = max(2, math.ceil(FLUSH_BYTES / max(total_bytes, 1)))
+    return [t] + [t.clone() for _ in range(n - 1)], n
+
+
+def plan_time_us(fn, n=50) -> float:
+    t0 = time.perf_counter()
+    for _ in range(n):
+        fn()
+    return (time.perf_counter() - t0) / n * 1e6
+
+
+# ----------------------------------------------------------------------------
+# decode (single, batch, skewed)
+# ----------------------------------------------------------------------------
+def bench_decode(abp, wl, torch, dev, w, K, Wm, workers=0) -> dict:
+    kv = w.kv
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float16
+    by = decode_bytes(w)
+    k0 = wl.to_torch(kv.k_pages, w.dtype, dev)
+    v0 = wl.to_torch(kv.v_pages, w.dtype, dev)
+    ks, copies = replicas(k0, torch, k0.nbytes + v0.nbytes)
+    vs, _ = replicas(v0, torch, k0.nbytes + v0.nbytes)
+    q = wl.to_torch(w.q, w.dtype, dev)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
+    indptr, indices, lpl = i32(kv.kv_indptr), i32(kv.kv_indices), i32(kv.kv_last_page_len)
+    params = abp.make_params(w.num_qo_heads, w.num_kv_heads, w.head_dim, kv.page_size, dt)
+    dec = abp.BatchDecode(params, max_batch=w.batch, num_workers=workers, device=dev)
+    o = torch.empty(q.shape, dtype=dt, device=dev)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, evs):
+        dec.plan(kv.kv_indptr, kv.kv_last_page_len, stream=stream)
+        if evs:
+            evs[0].record(stream)
+        dec.run(q, ks[i % copies], vs[i % copies], indptr, indices, lpl, o=o, lse=lse,
+                stream=stream)
+        if evs:
+            evs[1].record(stream)
+
+    wall, run_ms = timed_steps(torch, stream, step, K, Wm)
+    plan = dec.plan_struct
+    plan_us = plan_time_us(lambda: dec.plan(kv.kv_indptr, kv.kv_last_page_len, stream=stream))
+    torch.cuda.synchronize()
+    avg = float(run_ms.mean())
+    return {
+        "workload": w.name,
+        "step_TBps": round(by / (wall * 1e-3) / 1e12, 4),
+        "ms_per_step": round(wall, 5),
+        "run_TBps": round(by / (avg * 1e-3) / 1e12, 4),
+        "run": _stats_ms(run_ms),
+        "algorithmic_bytes": by,
+        "plan_us": round(plan_us, 2),
+        "batch": w.batch,
+        "kv_tokens": int(kv.kv_len.sum()),
+        "page_size": kv.page_size,
+        "num_qo_heads": w.num_qo_heads,
+        "num_kv_heads": w.num_kv_heads,
+        "dtype": w.dtype,
+        "workers": plan.num_workers,
+        "segments": plan.num_segments,
+        "merged_tiles": plan.num_merges,
+        "kv_pool_copies": copies,
+    }
+
+
+# ----------------------------------------------------------------------------
+# causal append
+# ----------------------------------------------------------------------------
+def bench_append(abp, wl, torch, dev, K, Wm) -> dict:
+    w = wl.ragged_append_causal()
+    kv = w.kv
+    flops = append_flops(w)
+    q = wl.to_torch(w.q, w.dtype, dev)
+    k0 = wl.to_torch(kv.k_pages, w.dtype, dev)
+    v0 = wl.to_torch(kv.v_pages, w.dtype, dev)
+    ks, copies = replicas(k0, torch, k0.nbytes + v0.nbytes)
+    vs, _ = replicas(v0, torch, k0.nbytes + v0.nbytes)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
+    qo, indptr, indices, lpl = i32(w.qo_indptr), i32(kv.kv_indptr), i32(kv.kv_indices), \
+        i32(kv.kv_last_page_len)
+    params = abp.make_params(w.num_qo_heads, w.num_kv_heads, w.head_dim, kv.page_size,
+                             torch.bfloat16, causal=True)
+    app = abp.BatchAppend(params, max_batch=w.batch, max_qo_tokens=int(w.qo_indptr[-1]),
+                          device=dev)
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    s = torch.cuda.current_stream(dev)
+
+    def step(i, evs):
+        app.plan(w.qo_indptr, kv.kv_indptr, kv.kv_last_page_len, stream=s)
+        if evs:
+            evs[0].record(s)
+        app.run(q, ks[i % copies], vs[i % copies], qo, indptr, indices, lpl, o=o, lse=lse,
+                stream=s)
+        if evs:
+            evs[1].record(s)
+
+    wall, run_ms = timed_steps(torch, s, step, K, Wm)
+    plan_us = plan_time_us(lambda: app.plan(w.qo_indptr, kv.kv_indptr, kv.kv_last_page_len,
+                                            stream=s))
+    torch.cuda.synchronize()
+    avg = float(run_ms.mean())
+    tf = flops / (avg * 1e-3) / 1e12
+    return {
+        "workload": w.name,
+        "value": round(tf, 2),
+        "unit": "TFLOP/s",
+        "step_TFLOPs": round(flops / (wall * 1e-3) / 1e12, 2),
+        "ms_per_step": round(wall, 5),
+        "causal_flop": flops,
+        "run": _stats_ms(run_ms),
+        "plan_us": round(plan_us, 2),
+        "qo_tokens": int(w.qo_indptr[-1]),
+        "kv_tokens": int(kv.kv_len.sum()),
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel": "append_kernel (split tiles merged in-kernel)",
+                     "avg_launch_us": round(avg * 1e3, 2)},
+        "workers": app.plan_struct.num_workers,
+        "segments": app.plan_struct.num_segments,
+        "merged_tiles": app.plan_struct.num_merges,
+        "kv_pool_copies": copies,
+    }
+
+
+# ----------------------------------------------------------------------------
+# cascade (shared prefix + suffixes, RoPE)
+# ----------------------------------------------------------------------------
+def bench_cascade(abp, wl, torch, dev, K, Wm) -> dict:
+    w = wl.cascade_rope()
+    pre, kv = w.prefix, w.kv
+    by = cascade_bytes(w)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
+    tot = pre.k_pages.nbytes * 2 + kv.k_pages.nbytes * 2
+    pk, copies = replicas(wl.to_torch(pre.k_pages, w.dtype, dev), torch, tot)
+    pv, _ = replicas(wl.to_torch(pre.v_pages, w.dtype, dev), torch, tot)
+    sk, _ = replicas(wl.to_torch(kv.k_pages, w.dtype, dev), torch, tot)
+    sv, _ = replicas(wl.to_torch(kv.v_pages, w.dtype, dev), torch, tot)
+    q = wl.to_torch(w.q, w.dtype, dev)
+    cas = abp.CascadeDecode(w.num_qo_heads, w.num_kv_heads, w.head_dim, pre.page_size,
+                            kv.page_size, torch.bfloat16, max_batch=w.batch,
+                            rope_theta=w.rope_theta, device=dev)
+    pqo = i32([0, w.batch])
+    p_ind, p_idx, p_lpl = i32(pre.kv_indptr), i32(pre.kv_indices), i32(pre.kv_last_page_len)
+    s_ind, s_idx, s_lpl = i32(kv.kv_indptr), i32(kv.kv_indices), i32(kv.kv_last_page_len)
+    qpos, kvoff = i32(w.q_pos), i32(w.kv_pos_offset)
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    bufs = cas.buffers(q)
+    s = torch.cuda.current_stream(dev)
+
+    def plan():
+        cas.plan(w.batch, pre.kv_indptr, pre.kv_last_page_len, kv.kv_indptr,
+                 kv.kv_last_page_len, stream=s)
+
+    def step(i, evs):
+        plan()
+        if evs:
+            evs[0].record(s)
+        c = i % copies
+        cas.run(q, pk[c], pv[c], pqo, p_ind, p_idx, p_lpl, sk[c], sv[c], s_ind, s_idx, s_lpl,
+                q_pos=qpos, kv_pos_offset=kvoff, o=o, lse=lse, stream=s, bufs=bufs)
+        if evs:
+            evs[1].record(s)
+
+    wall, run_ms = timed_steps(torch, s, step, K, Wm)
+    plan_us = plan_time_us(plan)
+    torch.cuda.synchronize()
+    avg = float(run_ms.mean())
+    return {
+        "workload": w.name,
+        "step_TBps": round(by / (wall * 1e-3) / 1e12, 4),
+        "ms_per_step": round(wall, 5),
+        "run_TBps": round(by / (avg * 1e-3) / 1e12, 4),
+        "run": _stats_ms(run_ms),
+        "algorithmic_bytes": by,
+        "plan_us": round(plan_us, 2),
+        "batch": w.batch,
+        "prefix_tokens": int(pre.kv_len.sum()),
+        "suffix_tokens": int(kv.kv_len.sum()),
+        "rope_theta": w.rope_theta,
+        "launches": "prefix append (RoPE) + suffix decode (RoPE) + its merge + merge_state",
+        "kv_pool_copies": copies,
+    }
+
+
+# ----------------------------------------------------------------------------
+# plain copy (context and counter calibration)
+# ----------------------------------------------------------------------------
+def bench_copy(torch, dev, K, Wm, nbytes=2 ** 30) -> dict:
+    a = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev).normal_()
+    b = torch.empty_like(a)
+    s = torch.cuda.current_stream(dev)
+
+    def step(i, evs):
+        if evs:
+            evs[0].record(s)
+        b.copy_(a)
+        if evs:
+            evs[1].record(s)
+
+    _, ms = timed_steps(torch, s, step, K, Wm)
+    avg = float(ms.mean())
+    return {"bytes_read": nbytes, "bytes_written": nbytes,
+            "read_plus_write_TBps": round(2 * nbytes / (avg * 1e-3) / 1e12, 4),
+            "run": _stats_ms(ms)}
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the oracle, bounded sample
+# ----------------------------------------------------------------------------
+def _cpu_info():
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return model, len(os.sched_getaffinity(0))
+
+
+def cpu_baseline_decode(w, budget_s: float = 12.0) -> dict:
+    """The fp64 oracle over whole requests of the batch, repeated passes, until
+    about budget_s of CPU time (one BLAS thread)."""
     from threadpoolctl import threadpool_limits
 
     from oracle import attention as ora
+    t_used, by, n_req = 0.0, 0, 0
+    with threadpool_limits(limits=1):
+        while t_used < budget_s:
+            for b in range(w.batch):
+                t0 = time.perf_counter()
+                ora.decode_workload(w, batch_ids=[b])
+                t_used += time.perf_counter() - t0
+                by += decode_bytes(w, [b])
+                n_req += 1
+                if t_used >= budget_s:
+                    break
+    model, avail = _cpu_info()
+    return {"value": round(by / t_used / 1e12, 6), "unit": "TB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_req} request evaluations ({n_req / w.batch:.2f} passes over the "
+                      f"{w.batch}-request batch, {by / 1e9:.2f} GB algorithmic) in "
+                      f"{t_used:.1f} s; fp64 NumPy, 1 BLAS thread",
+            "host_cpu": model, "host_cores_available": avail}
+
+
+def cpu_baseline_append(w, budget_s: float = 8.0) -> dict:
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention as ora
+    rng = np.random.Generator(np.random.PCG64(7))
+    qo = np.diff(w.qo_indptr)
     done, t_used = [], 0.0
     with threadpool_limits(limits=1):
-        for b in range(w.batch):
+        while t_used < budget_s:
+            b = int(rng.integers(0, w.batch))
+            n = min(32, int(qo[b]))
+            i0 = int(w.qo_indptr[b]) + int(rng.integers(0, int(qo[b]) - n + 1))
+            ids = list(range(i0, i0 + n))
             t0 = time.perf_counter()
-            ora.decode_workload(w, batch_ids=[b])
+            ora.append_workload(w, token_ids=ids)
             t_used += time.perf_counter() - t0
-            done.append(b)
-            if t_used >= budget_s:
-                break
-    by = decode_bytes(w, done)
-    return {"value": by / t_used / 1e12, "unit": "TB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(done)} of {w.batch} requests of the same batch "
-                      f"({by / 1e6:.1f} MB algorithmic) in {t_used:.1f} s, fp64 NumPy, 1 thread"}
+            done += ids
+    fl = append_flops(w, done)
+    model, avail = _cpu_info()
+    return {"value": round(fl / t_used / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{len(done)} of {int(w.qo_indptr[-1])} query tokens (runs of 32 at random "
+                      f"places, all heads; "
+                      f"{fl / 1e9:.1f} GFLOP visible) in {t_used:.1f} s; fp64 NumPy, 1 BLAS "
+                      f"thread", "host_cpu": model, "host_cores_available": avail}
 
 
+# ----------------------------------------------------------------------------
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -84,12 +429,15 @@ def main(argv=None) -> int:
     ap.add_argument("--workers", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-append", action="store_true")
-    ap.add_argument("--part", choices=["all", "decode", "append"], default="all",
-                    help="decode or append alone (profiling); 'all' is the benchmark line")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the single, skewed and cascade workloads")
+    ap.add_argument("--part", default="all",
+                    choices=["all", "decode", "append", "single", "skewed", "cascade", "copy"],
+                    help="one workload alone (profiling); 'all' is the benchmark line")
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the paged attention path has no multi-GPU "
-              "component (each GPU would run its own share with no exchange); use --gpus 1",
+        print("bench.py measures one GPU only: this build has no multi-GPU path (each GPU "
+              "would run its own share of requests or kv heads with no exchange); use --gpus 1",
               file=sys.stderr)
         return 2
 
@@ -101,164 +449,91 @@ def main(argv=None) -> int:
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     abp.load_library()
-    if args.part == "append":
-        print(json.dumps(bench_append(abp, wl, torch, dev, args.steps, args.warmup)), flush=True)
+    K, Wm = args.steps, args.warmup
+    part = args.part
+    if part == "append":
+        print(json.dumps(bench_append(abp, wl, torch, dev, K, Wm)), flush=True)
+        return 0
+    if part == "copy":
+        print(json.dumps(bench_copy(torch, dev, K, Wm)), flush=True)
+        return 0
+    if part == "cascade":
+        print(json.dumps(bench_cascade(abp, wl, torch, dev, K, Wm)), flush=True)
+        return 0
+    if part in ("single", "skewed"):
+        w = wl.single_decode_mha() if part == "single" else wl.skewed_decode_gqa()
+        print(json.dumps(bench_decode(abp, wl, torch, dev, w, K, Wm, args.workers)), flush=True)
         return 0
 
-    # ------------------------------------------------------------------ decode
+    # --------------------------------------------------- batch decode (the line)
     w = wl.batch_decode_gqa()
-    kv = w.kv
-    by = decode_bytes(w)
-    pool_bytes = kv.k_pages.nbytes + kv.v_pages.nbytes
-    copies = max(2, math.ceil(2 * 2 ** 30 / pool_bytes))
-    k0 = wl.to_torch(kv.k_pages, w.dtype, dev)
-    v0 = wl.to_torch(kv.v_pages, w.dtype, dev)
-    ks = [k0] + [k0.clone() for _ in range(copies - 1)]
-    vs = [v0] + [v0.clone() for _ in range(copies - 1)]
-    q = wl.to_torch(w.q, w.dtype, dev)
-    indptr = torch.from_numpy(kv.kv_indptr).to(dev)
-    indices = torch.from_numpy(kv.kv_indices).to(dev)
-    lpl = torch.from_numpy(kv.kv_last_page_len).to(dev)
-    params = abp.make_params(w.num_qo_heads, w.num_kv_heads, w.head_dim, kv.page_size,
-                             torch.bfloat16)
-    dec = abp.BatchDecode(params, max_batch=w.batch, num_workers=args.workers, device=dev)
-    o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
-    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream(dev)
-    K, Wm = args.steps, args.warmup
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
-
-    def step(i, evs=None):
-        dec.plan(kv.kv_indptr, kv.kv_last_page_len, stream=stream)
-        if evs:
-            evs[0].record(stream)
-        dec.run(q, ks[i % copies], vs[i % copies], indptr, indices, lpl, o=o, lse=lse,
-                stream=stream)
-        if evs:
-            evs[1].record(stream)
-
-    for i in range(Wm):
-        step(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        step(i, ev[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / K
-    kern_ms = np.array([a.elapsed_time(b) for a, b in ev])
-    kern_avg = float(kern_ms.mean())
-    plan = dec.plan_struct
-
-    t_plan0 = time.perf_counter()
-    for _ in range(50):
-        dec.plan(kv.kv_indptr, kv.kv_last_page_len, stream=stream)
-    plan_us = (time.perf_counter() - t_plan0) / 50 * 1e6
-    torch.cuda.synchronize()
-
-    value = by / (ms_step * 1e-3) / 1e12
-    achieved = by / (kern_avg * 1e-3) / 1e9
+    d = bench_decode(abp, wl, torch, dev, w, K, Wm, args.workers)
+    by = d["algorithmic_bytes"]
+    avg_s = d["run"]["avg_us"] * 1e-6
+    achieved = by / avg_s / 1e9
+    tr = recorded_traffic()
     out = {
         "metric": "paged-decode achieved HBM TB/s (% of peak) + causal-append TFLOPS, bf16 GQA",
-        "value": round(value, 4),
+        "value": d["step_TBps"],
         "unit": "TB/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": Wm,
-        "ms_per_step": round(ms_step, 5),
+        "ms_per_step": d["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic",
+        "data": "synthetic: seeded N(0,1) values rounded to bf16, uniform kv_len, shuffled "
+                "page pool",
         "config": {
-            "workload": w.name,
-            "batch": w.batch,
-            "num_qo_heads": w.num_qo_heads,
-            "num_kv_heads": w.num_kv_heads,
-            "head_dim": w.head_dim,
-            "page_size": kv.page_size,
-            "kv_tokens": int(kv.kv_len.sum()),
+            "workload": "batch paged decode: 64 requests, kv_len U{512..4096}, GQA 32/8, "
+                        "head_dim 128, page_size 16, bf16",
+            "batch": d["batch"],
+            "num_qo_heads": d["num_qo_heads"],
+            "num_kv_heads": d["num_kv_heads"],
+            "head_dim": 128,
+            "page_size": d["page_size"],
+            "kv_tokens": d["kv_tokens"],
             "algorithmic_bytes": by,
-            "workers": plan.num_workers,
-            "segments": plan.num_segments,
-            "merged_tiles": plan.num_merges,
-            "kv_pool_copies": copies,
+            "workers": d["workers"],
+            "segments": d["segments"],
+            "merged_tiles": d["merged_tiles"],
+            "kv_pool_copies": d["kv_pool_copies"],
             "parallelism": "single GPU",
         },
-        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_TBS, 2),
-        "plan_us": round(plan_us, 2),
+        "pct_of_hbm_peak": round(100 * d["step_TBps"] / HBM_PEAK_TBS, 2),
+        "plan_us": d["plan_us"],
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_TBS * 1e3,
             "unit": "GB/s",
             "frac": round(achieved / (HBM_PEAK_TBS * 1e3), 4),
-            "traffic": None,
-            "kernel": "decode_kernel + plan_merge_kernel (one run() call)",
-            "avg_launch_us": round(kern_avg * 1e3, 2),
-            "p10_us": round(float(np.percentile(kern_ms, 10)) * 1e3, 2),
-            "p90_us": round(float(np.percentile(kern_ms, 90)) * 1e3, 2),
+            "traffic": tr["traffic_bytes_per_run"] if tr else None,
+            "kernel": "decode run: decode_kernel + plan_merge_kernel (one run() call)",
+            "avg_launch_us": d["run"]["avg_us"],
+            "median_us": d["run"]["median_us"],
+            "p10_us": d["run"]["p10_us"],
+            "p90_us": d["run"]["p90_us"],
         },
     }
-
-    # ------------------------------------------------------------------ append
-    if not args.no_append and args.part == "all":
-        try:
-            out["append"] = bench_append(abp, wl, torch, dev, max(20, K // 4), 5)
-        except abp.AbpError as e:
-            out["append"] = {"error": str(e)}
-
-    # ------------------------------------------------------------- CPU baseline
+    if part == "all" and not args.no_append:
+        out["append"] = bench_append(abp, wl, torch, dev, max(20, K // 4), 5)
+    if part == "all" and not args.no_configs:
+        Kc = max(20, K // 2)
+        out["configs"] = {
+            "single_decode": bench_decode(abp, wl, torch, dev, wl.single_decode_mha(), Kc, 5),
+            "skewed_decode": bench_decode(abp, wl, torch, dev, wl.skewed_decode_gqa(), Kc, 5),
+            "cascade_rope": bench_cascade(abp, wl, torch, dev, Kc, 5),
+        }
+        out["copy_context"] = bench_copy(torch, dev, 20, 3)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_decode(w)
+        if "append" in out:
+            out["append"]["cpu_baseline"] = cpu_baseline_append(wl.ragged_append_causal())
     print(json.dumps(out), flush=True)
     return 0
-
-
-def bench_append(abp, wl, torch, dev, K, Wm):
-    w = wl.ragged_append_causal()
-    kv = w.kv
-    flops = append_flops(w)
-    q = wl.to_torch(w.q, w.dtype, dev)
-    k = wl.to_torch(kv.k_pages, w.dtype, dev)
-    v = wl.to_torch(kv.v_pages, w.dtype, dev)
-    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
-    qo, indptr, indices, lpl = i32(w.qo_indptr), i32(kv.kv_indptr), i32(kv.kv_indices), \
-        i32(kv.kv_last_page_len)
-    params = abp.make_params(w.num_qo_heads, w.num_kv_heads, w.head_dim, kv.page_size,
-                             torch.bfloat16, causal=True)
-    app = abp.BatchAppend(params, max_batch=w.batch, max_qo_tokens=int(w.qo_indptr[-1]),
-                          device=dev)
-    o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
-    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
-    s = torch.cuda.current_stream(dev)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(K)]
-    for i in range(Wm + K):
-        app.plan(w.qo_indptr, kv.kv_indptr, kv.kv_last_page_len, stream=s)
-        e = evs[i - Wm] if i >= Wm else None
-        if e:
-            e[0].record(s)
-        app.run(q, k, v, qo, indptr, indices, lpl, o=o, lse=lse, stream=s)
-        if e:
-            e[1].record(s)
-    torch.cuda.synchronize()
-    ms = np.array([a.elapsed_time(b) for a, b in evs])
-    avg = float(ms.mean())
-    tf = flops / (avg * 1e-3) / 1e12
-    return {
-        "workload": w.name,
-        "value": round(tf, 2),
-        "unit": "TFLOP/s",
-        "causal_flop": flops,
-        "avg_run_us": round(avg * 1e3, 2),
-        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": None},
-        "workers": app.plan_struct.num_workers,
-    }
 
 
 if __name__ == "__main__":

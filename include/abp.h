@@ -122,7 +122,7 @@ typedef struct abp_plan {
   int32_t num_tiles;
   int32_t num_segments;
   int32_t num_partials;  /* partial (o, lse) slots used by split tiles */
-  int32_t num_merges;    /* tiles merged after the main kernel */
+  int32_t num_merges;    /* tiles whose partial states are merged */
   int32_t max_tiles;     /* capacities fixed by (max_batch, max_qo_tokens, workers) */
   int32_t max_segments;
   int32_t max_partials;
@@ -171,8 +171,9 @@ int abp_decode_plan(const abp_params* params, int32_t batch, const int32_t* kv_i
 /* Batch decode over the paged cache (one query token per request).
  * q [batch, Hq, d]; o [batch, Hq, d] (out_dtype); lse [batch, Hq] float32 or NULL.
  * q_pos_d [batch] and kv_pos_offset_d [batch] are read only with RoPE (NULL =
- * defaults). Launches the persistent decode kernel (grid = num_workers) and the
- * merge of split tiles. */
+ * defaults). Launches the persistent decode kernel (grid = num_workers), then a
+ * merge kernel (same grid) that combines the partial states of split tiles.
+ * Partial states live in dev_ws: runs that share one dev_ws must not overlap. */
 int abp_decode_run(const abp_plan* plan, const abp_params* params, const void* q,
                    const void* k_pages, const void* v_pages, const int32_t* kv_indptr_d,
                    const int32_t* kv_indices_d, const int32_t* kv_last_page_len_d,
@@ -188,7 +189,12 @@ int abp_append_plan(const abp_params* params, int32_t batch, const int32_t* qo_i
 
 /* Append / prefill attention (MFMA): q [total_qo, Hq, d] ragged by qo_indptr_d;
  * o [total_qo, Hq, d]; lse [total_qo, Hq] or NULL. Causal per params.causal.
- * q_pos_d [total_qo] and kv_pos_offset_d [batch] are read only with RoPE. */
+ * q_pos_d [total_qo] and kv_pos_offset_d [batch] are read only with RoPE.
+ * Launches the persistent append kernel (grid = num_workers) alone: a tile split
+ * over several workers is merged by the workgroup whose partial arrives last,
+ * counted with per-tile counters in dev_ws that the merging workgroup resets to
+ * zero (every plan upload also zeroes them). Runs that share one dev_ws must
+ * not overlap. */
 int abp_append_run(const abp_plan* plan, const abp_params* params, const void* q,
                    const void* k_pages, const void* v_pages, const int32_t* qo_indptr_d,
                    const int32_t* kv_indptr_d, const int32_t* kv_indices_d,
