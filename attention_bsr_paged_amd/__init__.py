@@ -76,7 +76,7 @@ class AbpPlan(ctypes.Structure):
         ("max_tiles", ctypes.c_int32),
         ("max_segments", ctypes.c_int32),
         ("max_partials", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("upload_path", ctypes.c_int32),
         ("fingerprint", ctypes.c_uint64),
         ("plan_bytes", ctypes.c_uint64),
         ("partial_offset", ctypes.c_uint64),

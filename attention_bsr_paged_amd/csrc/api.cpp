@@ -213,6 +213,19 @@ int abp_plan_host(int kind, const abp_params* params, int32_t batch, const int32
   }
 }
 
+// True when `p` is pinned host memory that the GPU addresses at the same
+// virtual address (hipHostMalloc memory), 16-byte aligned, so a kernel may read
+// it. Pageable or unknown memory gives false (and leaves no sticky HIP error).
+static bool mapped_pinned(const void* p, uint64_t bytes) {
+  if ((reinterpret_cast<uintptr_t>(p) & 15) || (bytes & 3)) return false;
+  hipPointerAttribute_t attr{};
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return attr.type == hipMemoryTypeHost && !attr.isManaged && attr.devicePointer == p;
+}
+
 static int plan_and_upload(int kind, const abp_params* params, int32_t batch,
                            const int32_t* qo_indptr_h, const int32_t* kv_indptr_h,
                            const int32_t* lpl_h, int32_t max_batch, int32_t max_qo,
@@ -226,9 +239,17 @@ static int plan_and_upload(int kind, const abp_params* params, int32_t batch,
   if (!dev_ws) return fail(ABP_ERR_INVALID_ARG, "device workspace is NULL");
   if (dev_bytes < L.dev_bytes)
     return fail(ABP_ERR_WORKSPACE_TOO_SMALL, "device workspace smaller than abp_workspace_size");
-  hipError_t e = hipMemcpyAsync(dev_ws, host_ws, L.plan_bytes, hipMemcpyHostToDevice,
-                                reinterpret_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(plan)");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (mapped_pinned(host_ws, L.plan_bytes)) {
+    // pinned host memory: a small kernel on the same queue reads it directly
+    hipError_t e = abp::launch_upload(dev_ws, host_ws, L.plan_bytes, s);
+    if (e != hipSuccess) return hip_fail(e, "plan upload kernel");
+    plan->upload_path = 1;
+  } else {
+    hipError_t e = hipMemcpyAsync(dev_ws, host_ws, L.plan_bytes, hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(plan)");
+    plan->upload_path = 0;
+  }
   return ABP_OK;
 }
 

@@ -486,7 +486,7 @@ __global__ __launch_bounds__(64 * append_waves<ROPE>(), 1) void append_kernel(At
       }
     }
     if (slot >= 0) {
-      merge_if_last(a, tile, kRows, &s_last, [&](int r, int64_t* orow) {
+      merge_if_last<kRows, 64 * NW>(a, tile, &s_last, [&](int r, int64_t* orow) {
         const int tloc = qt * TQ + r / G;
         if (tloc >= qo_len) return false;
         *orow = (int64_t)(q0 + tloc) * a.num_qo_heads + h * G + (r % G);

@@ -40,6 +40,10 @@ hipError_t launch_decode(const Config& cfg, const AttnArgs& a, hipStream_t strea
 int decode_blocks_per_cu(const Config& cfg);
 int append_blocks_per_cu(const Config& cfg);
 hipError_t launch_append(const Config& cfg, const AttnArgs& a, hipStream_t stream);
+// copies `bytes` (multiple of 4, 16-byte aligned pointers) from pinned host
+// memory mapped into the GPU's address space to device memory
+hipError_t launch_upload(void* dev_dst, const void* host_src_mapped, size_t bytes,
+                         hipStream_t stream);
 // merges the split tiles of a decode plan into o / lse after the decode kernel
 // (fixed grid; counts are read from the plan at run time)
 hipError_t launch_plan_merge(const Config& cfg, const AttnArgs& a, int32_t grid,

@@ -79,8 +79,10 @@ __global__ __launch_bounds__(256) void merge_two_kernel(const void* o_a, const f
 }
 
 // Merge the split tiles of a decode plan after the decode kernel (the kernel
-// boundary orders the partial stores before these loads). Grid is fixed; work
-// items are (merge entry, block of 16 tile rows), read from the plan header.
+// boundary orders the partial stores before these loads). Grid is fixed; 16
+// lanes take one (merge entry, tile row) and 8 head-dim elements each; counts
+// come from the plan header at run time. Partials are folded in slot order
+// with a running maximum, four at a time so their loads are in flight together.
 template <int OUT_DT>
 __global__ __launch_bounds__(256) void plan_merge_kernel(AttnArgs a) {
   const ABP_CONST_AS int32_t* plan = const_as(a.plan);
@@ -91,14 +93,12 @@ __global__ __launch_bounds__(256) void plan_merge_kernel(AttnArgs a) {
   const int num_merges = plan[H_NUM_MERGES];
   const ABP_CONST_AS int32_t* tiles = plan + plan[H_OFF_TILE];
   const ABP_CONST_AS int32_t* merges = plan + plan[H_OFF_MERGE];
-  const int row_blocks = (rows + 15) / 16;
-  const int items = num_merges * row_blocks;
+  const int total = num_merges * rows;
   const int e0 = (threadIdx.x & 15) * 8;
-  for (int item = blockIdx.x; item < items; item += gridDim.x) {
-    const int m = item / row_blocks;
-    const int r = (item % row_blocks) * 16 + (threadIdx.x >> 4);
-    if (r >= rows) continue;
-    const int mtile = merges[4 * m], mfirst = merges[4 * m + 1], mnum = merges[4 * m + 2];
+  for (int ri = blockIdx.x * 16 + (threadIdx.x >> 4); ri < total; ri += gridDim.x * 16) {
+    const int m = ri / rows;
+    const int r = ri - m * rows;
+    const int mtile = merges[4 * m], mfirst = merges[4 * m + 1], n = merges[4 * m + 2];
     const int tb = tiles[4 * mtile], th = tiles[4 * mtile + 1], tq = tiles[4 * mtile + 2];
     int64_t token;
     int head;
@@ -113,26 +113,45 @@ __global__ __launch_bounds__(256) void plan_merge_kernel(AttnArgs a) {
       token = q0 + tloc;
       head = th * G + (r % G);
     }
-    const int n = mnum;
-    float M = kNegInf;
-    for (int i = 0; i < n; ++i) M = __builtin_fmaxf(M, a.lse_part[int64_t(mfirst + i) * rows + r]);
-    float out[8];
+    float M = kNegInf, tot = 0.f;
+    float acc[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) out[e] = 0.f;
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    for (int i0 = 0; i0 < n; i0 += 4) {
+      float l[4], v[4][8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (i0 + j < n) {
+          const int64_t sr = int64_t(mfirst + i0 + j) * rows + r;
+          l[j] = a.lse_part[sr];
+          load8<ABP_F32>(a.o_part, sr * 128 + e0, v[j]);
+        } else {
+          l[j] = kNegInf;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[j][e] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float nm = __builtin_fmaxf(M, l[j]);
+        const float sc = nm == M ? 1.f : fast_exp2((M - nm) * kLog2e);
+        const float wt = l[j] == kNegInf ? 0.f : fast_exp2((l[j] - nm) * kLog2e);
+        M = nm;
+        tot = __builtin_fmaf(tot, sc, wt);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(acc[e], sc, wt * v[j][e]);
+      }
+    }
+    float out[8];
     float lse = kNegInf;
     if (M != kNegInf) {
-      float tot = 0.f;
-      for (int i = 0; i < n; ++i)
-        tot += fast_exp2((a.lse_part[int64_t(mfirst + i) * rows + r] - M) * kLog2e);
-      lse = M + fast_log2(tot) * kLn2;
-      for (int i = 0; i < n; ++i) {
-        const int64_t sr = int64_t(mfirst + i) * rows + r;
-        const float w = fast_exp2((a.lse_part[sr] - lse) * kLog2e);
-        float v[8];
-        load8<ABP_F32>(a.o_part, sr * 128 + e0, v);
+      const float inv = 1.f / tot;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) out[e] = __builtin_fmaf(w, v[e], out[e]);
-      }
+      for (int e = 0; e < 8; ++e) out[e] = acc[e] * inv;
+      lse = M + fast_log2(tot) * kLn2;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out[e] = 0.f;
     }
     const int64_t orow = token * a.num_qo_heads + head;
     store8<OUT_DT>(a.o, orow * 128 + e0, out);

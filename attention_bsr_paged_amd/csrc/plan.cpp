@@ -360,7 +360,7 @@ int plan_compute(const Config& cfg, const Layout& L, int32_t batch, const int32_
   plan->max_tiles = L.max_tiles;
   plan->max_segments = L.max_segs;
   plan->max_partials = L.max_partials;
-  plan->reserved = 0;
+  plan->upload_path = 0;
   plan->fingerprint = fingerprint(cfg, L);
   plan->plan_bytes = L.plan_bytes;
   plan->partial_offset = L.partial_offset;

@@ -10,7 +10,8 @@ workload (64 requests, GQA 32/8, head_dim 128, page 16, bf16, kv_len uniform on
 partition), its upload, the persistent decode kernel and the merge of split
 tiles. Inputs are resident in HBM before the timed region; the K/V pools are
 replicated and rotated (at least 2 GiB in all) so that no step reads data a
-previous step left in the 256 MB last-level cache.
+previous step left in the 256 MB last-level cache. Every 4th run of the timed
+steps is bracketed by HIP events on its stream for the per-run figures.
 
 Prints one JSON line. ``value`` is achieved HBM throughput of the whole step in
 TB/s (algorithmic bytes: each valid K/V token once, plus q, o, lse and the
@@ -127,17 +128,23 @@ def _stats_ms(ms: np.ndarray) -> dict:
             "p90_us": round(float(np.percentile(ms, 90)) * 1e3, 2)}
 
 
+EVENT_EVERY = 4   # bracket every 4th run of the timed region with HIP events
+
+
 def timed_steps(torch, stream, step, K, Wm):
     """Wm untimed steps, then K timed ones; step(i, (ev0, ev1) or None) records the
-    events around the GPU run. Returns (wall ms per step, run ms per step)."""
+    events around the GPU run. Every EVENT_EVERY-th timed run is bracketed: a pair
+    of timing events costs several microseconds of GPU idle time on this stack,
+    so bracketing every run would slow the very steps being timed. Returns (wall
+    ms per step, run ms of the bracketed runs)."""
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
+          for _ in range(0, K, EVENT_EVERY)]
     for i in range(Wm):
         step(i, None)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        step(Wm + i, ev[i])
+        step(Wm + i, ev[i // EVENT_EVERY] if i % EVENT_EVERY == 0 else None)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / K
     return wall, np.array([a.elapsed_time(b) for a, b in ev])
@@ -186,7 +193,10 @@ def bench_decode(abp, wl, torch, dev, w, K, Wm, workers=0) -> dict:
 
     wall, run_ms = timed_steps(torch, stream, step, K, Wm)
     plan = dec.plan_struct
-    plan_us = plan_time_us(lambda: dec.plan(kv.kv_indptr, kv.kv_last_page_len, stream=stream))
+    hws = np.zeros(dec.host_ws.numel(), np.uint8)
+    plan_us = plan_time_us(lambda: abp.abp_plan_host(
+        abp.ABP_KIND_DECODE, params, w.batch, None, kv.kv_indptr, kv.kv_last_page_len, w.batch,
+        0, plan.num_workers, hws))
     torch.cuda.synchronize()
     avg = float(run_ms.mean())
     return {
@@ -196,7 +206,7 @@ def bench_decode(abp, wl, torch, dev, w, K, Wm, workers=0) -> dict:
         "run_TBps": round(by / (avg * 1e-3) / 1e12, 4),
         "run": _stats_ms(run_ms),
         "algorithmic_bytes": by,
-        "plan_us": round(plan_us, 2),
+        "plan_host_us": round(plan_us, 2),
         "batch": w.batch,
         "kv_tokens": int(kv.kv_len.sum()),
         "page_size": kv.page_size,
@@ -243,8 +253,11 @@ def bench_append(abp, wl, torch, dev, K, Wm) -> dict:
             evs[1].record(s)
 
     wall, run_ms = timed_steps(torch, s, step, K, Wm)
-    plan_us = plan_time_us(lambda: app.plan(w.qo_indptr, kv.kv_indptr, kv.kv_last_page_len,
-                                            stream=s))
+    hws = np.zeros(app.host_ws.numel(), np.uint8)
+    nq = int(w.qo_indptr[-1])
+    plan_us = plan_time_us(lambda: abp.abp_plan_host(
+        abp.ABP_KIND_APPEND, params, w.batch, w.qo_indptr, kv.kv_indptr, kv.kv_last_page_len,
+        w.batch, nq, app.plan_struct.num_workers, hws))
     torch.cuda.synchronize()
     avg = float(run_ms.mean())
     tf = flops / (avg * 1e-3) / 1e12
@@ -256,7 +269,7 @@ def bench_append(abp, wl, torch, dev, K, Wm) -> dict:
         "ms_per_step": round(wall, 5),
         "causal_flop": flops,
         "run": _stats_ms(run_ms),
-        "plan_us": round(plan_us, 2),
+        "plan_host_us": round(plan_us, 2),
         "qo_tokens": int(w.qo_indptr[-1]),
         "kv_tokens": int(kv.kv_len.sum()),
         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
@@ -311,7 +324,6 @@ def bench_cascade(abp, wl, torch, dev, K, Wm) -> dict:
             evs[1].record(s)
 
     wall, run_ms = timed_steps(torch, s, step, K, Wm)
-    plan_us = plan_time_us(plan)
     torch.cuda.synchronize()
     avg = float(run_ms.mean())
     return {
@@ -321,7 +333,6 @@ def bench_cascade(abp, wl, torch, dev, K, Wm) -> dict:
         "run_TBps": round(by / (avg * 1e-3) / 1e12, 4),
         "run": _stats_ms(run_ms),
         "algorithmic_bytes": by,
-        "plan_us": round(plan_us, 2),
         "batch": w.batch,
         "prefix_tokens": int(pre.kv_len.sum()),
         "suffix_tokens": int(kv.kv_len.sum()),
@@ -503,7 +514,7 @@ def main(argv=None) -> int:
             "parallelism": "single GPU",
         },
         "pct_of_hbm_peak": round(100 * d["step_TBps"] / HBM_PEAK_TBS, 2),
-        "plan_us": d["plan_us"],
+        "plan_host_us": d["plan_host_us"],
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 1),

@@ -126,7 +126,7 @@ typedef struct abp_plan {
   int32_t max_tiles;     /* capacities fixed by (max_batch, max_qo_tokens, workers) */
   int32_t max_segments;
   int32_t max_partials;
-  int32_t reserved;
+  int32_t upload_path;   /* 1: a kernel read the pinned host_ws; 0: hipMemcpyAsync */
   uint64_t fingerprint;  /* hash of kind, params, capacities and tiling */
   uint64_t plan_bytes;   /* bytes uploaded from the host workspace */
   uint64_t partial_offset; /* byte offset of the partial-state region in dev_ws */
@@ -161,8 +161,12 @@ int abp_plan_host(int kind, const abp_params* params, int32_t batch, const int32
                   int32_t max_batch, int32_t max_qo_tokens, int32_t num_workers, void* host_ws,
                   size_t host_bytes, abp_plan* plan);
 
-/* Decode plan: abp_plan_host for ABP_KIND_DECODE, then one hipMemcpyAsync of the
- * plan from host_ws to dev_ws on `stream`. */
+/* Decode plan: abp_plan_host for ABP_KIND_DECODE, then the upload of the plan
+ * from host_ws to dev_ws on `stream`. If host_ws is pinned host memory mapped at
+ * the same address on the GPU (hipHostMalloc), a small kernel on `stream` reads
+ * it directly (plan->upload_path = 1); otherwise hipMemcpyAsync copies it
+ * (upload_path = 0). Either way host_ws must stay unchanged until the upload
+ * has executed on the stream. */
 int abp_decode_plan(const abp_params* params, int32_t batch, const int32_t* kv_indptr_h,
                     const int32_t* kv_last_page_len_h, int32_t max_batch, int32_t num_workers,
                     void* host_ws, size_t host_bytes, void* dev_ws, size_t dev_bytes,
@@ -180,7 +184,8 @@ int abp_decode_run(const abp_plan* plan, const abp_params* params, const void* q
                    const int32_t* q_pos_d, const int32_t* kv_pos_offset_d, void* o, float* lse,
                    void* dev_ws, size_t dev_bytes, abp_stream_t stream);
 
-/* Append / prefill plan for ragged queries (qo_indptr_h [batch + 1]). */
+/* Append / prefill plan for ragged queries (qo_indptr_h [batch + 1]); uploads
+ * like abp_decode_plan. */
 int abp_append_plan(const abp_params* params, int32_t batch, const int32_t* qo_indptr_h,
                     const int32_t* kv_indptr_h, const int32_t* kv_last_page_len_h,
                     int32_t max_batch, int32_t max_qo_tokens, int32_t num_workers,

@@ -186,6 +186,47 @@ def test_graph_replay_after_replan():
                   what="replanned")
 
 
+def test_plan_upload_paths_and_replan_sequence():
+    """The plan reaches the device workspace either through a kernel that reads
+    the pinned host workspace (the binding's) or through hipMemcpyAsync (a
+    pageable host workspace). Both give the same bits, and a sequence of
+    different plans through one workspace each gives the oracle's result."""
+    import ctypes
+    import torch
+    lib = abp.load_library()
+    params = abp.make_params(8, 2, 128, 16, torch.bfloat16)
+    dec = abp.BatchDecode(params, max_batch=3, num_workers=24)
+    stream = torch.cuda.current_stream().cuda_stream
+    for i, lens in enumerate(([700, 5, 64], [17, 2000, 0], [300, 301, 302], [1, 1, 1])):
+        w = wl.small_decode(31 + i, lens, 16, 8, 2)
+        say(f"[case] upload paths, lengths {lens}")
+        kv = w.kv
+        dev = upload_kv(kv)
+        q = wl.to_torch(w.q, "bf16", "cuda")
+        plan = dec.plan(kv.kv_indptr, kv.kv_last_page_len)
+        assert plan.upload_path == 1, "pinned host workspace should be read by the upload kernel"
+        o, l = dec.run(q, dev["k"], dev["v"], dev["indptr"], dev["indices"], dev["lpl"])
+        torch.cuda.synchronize()
+        o_ref, l_ref = ora.decode_workload(w)
+        assert_parity(o.float().cpu().numpy(), l.cpu().numpy(), o_ref, l_ref, "bf16",
+                      what=f"pinned upload {lens}")
+        host = np.zeros(dec.host_ws.numel(), np.uint8)   # pageable
+        indptr = np.ascontiguousarray(kv.kv_indptr, np.int32)
+        lpl = np.ascontiguousarray(kv.kv_last_page_len, np.int32)
+        p2 = abp.AbpPlan()
+        st = lib.abp_decode_plan(ctypes.byref(params), 3, indptr.ctypes.data, lpl.ctypes.data, 3,
+                                 24, host.ctypes.data, host.nbytes, dec.dev_ws.data_ptr(),
+                                 dec.dev_ws.numel(), stream, ctypes.byref(p2))
+        assert st == 0, abp.abp_last_error()
+        torch.cuda.synchronize()
+        assert p2.upload_path == 0
+        assert p2.fingerprint == plan.fingerprint and p2.num_segments == plan.num_segments
+        dec.plan_struct = p2
+        o2, l2 = dec.run(q, dev["k"], dev["v"], dev["indptr"], dev["indices"], dev["lpl"])
+        torch.cuda.synchronize()
+        assert torch.equal(o2, o) and torch.equal(l2, l)
+
+
 @pytest.mark.parametrize("in_dt,out_dt", [("fp32", "bf16"), ("bf16", "bf16"), ("fp16", "fp32")])
 def test_merge_state_kernel(in_dt, out_dt):
     import torch
