@@ -31,6 +31,9 @@ COMMON = [
 DEVICE = [
     "--offload-arch=" + ARCH,
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # kernels never produce NaN on purpose: max/min need no NaN quieting
+    # (infinities keep their meaning: masked scores are -inf)
+    "-fno-honor-nans",
 ]
 
 

@@ -129,6 +129,18 @@ __device__ __forceinline__ void rope_k(const uint4& u, float pos, int c,
   }
 }
 
+// Maximum over the 4 lane groups (lanes l, l ^ 16, l ^ 32, l ^ 48) without
+// LDS: each swap exchanges halves (32 lanes) or rows (16 lanes) between two
+// copies of x, so the two results hold both partners of every lane.
+__device__ __forceinline__ float max_over_groups(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto h = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  x = __builtin_fmaxf(__builtin_bit_cast(float, h[0]), __builtin_bit_cast(float, h[1]));
+  const uint32_t w = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  return __builtin_fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+}
+
 // Waves per workgroup: 8 (256 rows, waves 0-3 stage K and 4-7 stage V), or 4
 // for RoPE (128 rows, every wave stages both; hi/lo operands need 512 regs).
 // One workgroup per CU either way.
@@ -142,9 +154,11 @@ __global__ __launch_bounds__(64 * append_waves<ROPE>(), 1) void append_kernel(At
   constexpr int NW = append_waves<ROPE>();
   constexpr int kRows = 32 * NW;
   constexpr int TQ = kRows / G;
-  __shared__ __align__(16) uint16_t sK[kTk * kKStride];
-  __shared__ __align__(16) uint16_t sKlo[ROPE ? kTk * kKStride : 8];  // RoPE: low parts of K
-  __shared__ __align__(16) uint16_t sVt[kD * kVStride];
+  // two stages: block j is read from stage j & 1 while block j + 1 is stored
+  // into the other
+  __shared__ __align__(16) uint16_t sKs[2][kTk * kKStride];
+  __shared__ __align__(16) uint16_t sKlos[2][ROPE ? kTk * kKStride : 8];  // RoPE: low parts of K
+  __shared__ __align__(16) uint16_t sVts[2][kD * kVStride];
   __shared__ int s_last;
 
   const ABP_CONST_AS int32_t* plan = const_as(a.plan);
@@ -301,7 +315,10 @@ __global__ __launch_bounds__(64 * append_waves<ROPE>(), 1) void append_kernel(At
         }
       }
     };
-    auto swrite = [&](int kb) {
+    auto swrite = [&](int kb, int stage) {
+      uint16_t* sK = sKs[stage];
+      uint16_t* sKlo = sKlos[stage];
+      uint16_t* sVt = sVts[stage];
       if (stage_k) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -335,12 +352,16 @@ __global__ __launch_bounds__(64 * append_waves<ROPE>(), 1) void append_kernel(At
 
     if (kv_begin < kv_end) {
       gload(kv_begin);
-      swrite(kv_begin);
-      __syncthreads();
+      swrite(kv_begin, 0);
     }
-    for (int kb = kv_begin; kb < kv_end; kb += kTk) {
+    __syncthreads();
+    int stage = 0;
+    for (int kb = kv_begin; kb < kv_end; kb += kTk, stage ^= 1) {
       const bool has_next = kb + kTk < kv_end;
       if (has_next) gload(kb + kTk);
+      const uint16_t* sK = sKs[stage];
+      const uint16_t* sKlo = sKlos[stage];
+      const uint16_t* sVt = sVts[stage];
 
       // ---- S^T = K Q^T: S[mb][nb] holds keys kb + 16 mb + 4 g16 + j, row nb*16 + l16
       f32x4_t S[4][2];
@@ -387,8 +408,7 @@ __global__ __launch_bounds__(64 * append_waves<ROPE>(), 1) void append_kernel(At
         for (int mb = 0; mb < 4; ++mb)
           x = __builtin_fmaxf(x, __builtin_fmaxf(__builtin_fmaxf(S[mb][nb][0], S[mb][nb][1]),
                                                  __builtin_fmaxf(S[mb][nb][2], S[mb][nb][3])));
-        x = __builtin_fmaxf(x, __shfl_xor(x, 16));
-        mx[nb] = __builtin_fmaxf(x, __shfl_xor(x, 32));
+        mx[nb] = max_over_groups(x);
       }
       // the reference max moves only when a score exceeds it by more than thr
       if (__builtin_amdgcn_ballot_w64((mx[0] > m[0] + thr) || (mx[1] > m[1] + thr))) {
@@ -436,11 +456,10 @@ __global__ __launch_bounds__(64 * append_waves<ROPE>(), 1) void append_kernel(At
           O[md][1] = mfma<T>(va, pB[kc2][1], O[md][1]);
         }
       }
-      __syncthreads();  // all waves are done with this block's LDS tiles
-      if (has_next) {
-        swrite(kb + kTk);
-        __syncthreads();
-      }
+      // the other stage held block j - 1, which every wave finished before the
+      // barrier that ended the previous iteration
+      if (has_next) swrite(kb + kTk, stage ^ 1);
+      __syncthreads();
     }
 
     // ---- finalize rows: o = O / l, lse = m * scale + ln l

@@ -57,60 +57,64 @@ __device__ __forceinline__ void merge_if_last(const AttnArgs& a, int tile, int* 
   __syncthreads();
   if (!*s_last) return;
 
-  float M[K], tot[K], acc[K][8];
-#pragma unroll
-  for (int k = 0; k < K; ++k) {
-    M[k] = kNegInf;
-    tot[k] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[k][e] = 0.f;
-  }
   const int tid = threadIdx.x;
-  for (int i = 0; i < np; ++i) {
-    const int64_t slot_row = int64_t(first + i) * ROWS;
-    float l[K];
-    float4 v[K][2];
+  constexpr int KC = K < 8 ? K : 8;  // items per pass (bounds the registers)
+  for (int k0 = 0; k0 < K; k0 += KC) {
+    float M[KC], tot[KC], acc[KC][8];
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const int item = tid + k * NT;
-      const int64_t sr = slot_row + (item >> 4);
-      l[k] = a.lse_part[sr];
-      const float4* src = reinterpret_cast<const float4*>(a.o_part + sr * 128 + (item & 15) * 8);
-      v[k][0] = src[0];
-      v[k][1] = src[1];
+    for (int k = 0; k < KC; ++k) {
+      M[k] = kNegInf;
+      tot[k] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[k][e] = 0.f;
+    }
+    for (int i = 0; i < np; ++i) {
+      const int64_t slot_row = int64_t(first + i) * ROWS;
+      float l[KC];
+      float4 v[KC][2];
+#pragma unroll
+      for (int k = 0; k < KC; ++k) {
+        const int item = tid + (k0 + k) * NT;
+        const int64_t sr = slot_row + (item >> 4);
+        l[k] = a.lse_part[sr];
+        const float4* src =
+            reinterpret_cast<const float4*>(a.o_part + sr * 128 + (item & 15) * 8);
+        v[k][0] = src[0];
+        v[k][1] = src[1];
+      }
+#pragma unroll
+      for (int k = 0; k < KC; ++k) {
+        const float nm = __builtin_fmaxf(M[k], l[k]);
+        // rescale of the running sums; no change (and no -inf - -inf) when M holds
+        const float sc = nm == M[k] ? 1.f : fast_exp2((M[k] - nm) * kLog2e);
+        const float wt = l[k] == kNegInf ? 0.f : fast_exp2((l[k] - nm) * kLog2e);
+        M[k] = nm;
+        tot[k] = __builtin_fmaf(tot[k], sc, wt);
+        const float x[8] = {v[k][0].x, v[k][0].y, v[k][0].z, v[k][0].w,
+                            v[k][1].x, v[k][1].y, v[k][1].z, v[k][1].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[k][e] = __builtin_fmaf(acc[k][e], sc, wt * x[e]);
+      }
     }
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const float nm = __builtin_fmaxf(M[k], l[k]);
-      // rescale of the running sums; no change (and no -inf - -inf) when M holds
-      const float sc = nm == M[k] ? 1.f : fast_exp2((M[k] - nm) * kLog2e);
-      const float wt = l[k] == kNegInf ? 0.f : fast_exp2((l[k] - nm) * kLog2e);
-      M[k] = nm;
-      tot[k] = __builtin_fmaf(tot[k], sc, wt);
-      const float x[8] = {v[k][0].x, v[k][0].y, v[k][0].z, v[k][0].w,
-                          v[k][1].x, v[k][1].y, v[k][1].z, v[k][1].w};
+    for (int k = 0; k < KC; ++k) {
+      const int item = tid + (k0 + k) * NT;
+      int64_t orow;
+      if (!row_out(item >> 4, &orow)) continue;
+      float out[8];
+      float lse = kNegInf;
+      if (M[k] != kNegInf) {
+        const float inv = 1.f / tot[k];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[k][e] = __builtin_fmaf(acc[k][e], sc, wt * x[e]);
+        for (int e = 0; e < 8; ++e) out[e] = acc[k][e] * inv;
+        lse = M[k] + fast_log2(tot[k]) * kLn2;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) out[e] = 0.f;
+      }
+      store8_out(a.o, orow * 128 + (item & 15) * 8, out, a.out_dtype);
+      if (a.lse && (item & 15) == 0) a.lse[orow] = lse;
     }
-  }
-#pragma unroll
-  for (int k = 0; k < K; ++k) {
-    const int item = tid + k * NT;
-    int64_t orow;
-    if (!row_out(item >> 4, &orow)) continue;
-    float out[8];
-    float lse = kNegInf;
-    if (M[k] != kNegInf) {
-      const float inv = 1.f / tot[k];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) out[e] = acc[k][e] * inv;
-      lse = M[k] + fast_log2(tot[k]) * kLn2;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) out[e] = 0.f;
-    }
-    store8_out(a.o, orow * 128 + (item & 15) * 8, out, a.out_dtype);
-    if (a.lse && (item & 15) == 0) a.lse[orow] = lse;
   }
   if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
