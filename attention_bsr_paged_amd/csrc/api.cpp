@@ -353,6 +353,11 @@ int abp_append_run(const abp_plan* plan, const abp_params* params, const void* q
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     hipError_t e = abp::launch_append(cfg, a, s);
     if (e != hipSuccess) return hip_fail(e, "append kernel launch");
+    // tiles split into many partials are merged across all CUs (the plan says
+    // which; the kernel returns at once otherwise, so the launch sequence does
+    // not depend on the plan)
+    e = abp::launch_plan_merge(cfg, a, plan->num_workers, s);
+    if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
     return ABP_OK;
   } catch (...) {
     return fail(ABP_ERR_HIP, "exception");

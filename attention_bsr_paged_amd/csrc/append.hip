@@ -504,7 +504,7 @@ __global__ __launch_bounds__(64 * append_waves<ROPE>(), 1) void append_kernel(At
         }
       }
     }
-    if (slot >= 0) {
+    if (slot >= 0 && plan[H_MERGE_KERNEL] == 0) {
       merge_if_last<kRows, 64 * NW>(a, tile, &s_last, [&](int r, int64_t* orow) {
         const int tloc = qt * TQ + r / G;
         if (tloc >= qo_len) return false;

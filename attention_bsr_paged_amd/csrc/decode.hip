@@ -146,6 +146,21 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
     }
   }
 
+  // Chunk buffers, page ids and q live across segments: on the page-aligned
+  // path the end of a segment's chunk loop issues the loads of the next
+  // segment (q, page ids, first chunk), so they are in flight while the
+  // segment's states are merged and written.
+  KVRegs<S> A, B;
+  int pidA[S] = {}, pidB[S] = {};
+  uint4 qn[G];
+  bool pre = false;  // the loads of segment s were issued by segment s - 1
+  auto load_q = [&](int b, int h, uint4* q) {
+    const uint16_t* qb = static_cast<const uint16_t*>(a.q) +
+                         (int64_t(b) * a.num_qo_heads + int64_t(h) * G) * kD + sub * 8;
+#pragma unroll
+    for (int g = 0; g < G; ++g) q[g] = *reinterpret_cast<const uint4*>(qb + g * kD);
+  };
+
   for (int s = s_begin; s < s_end; ++s) {
     const int tile = segs[4 * s];
     const int kv_begin = segs[4 * s + 1], kv_end = segs[4 * s + 2], slot = segs[4 * s + 3];
@@ -155,17 +170,17 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
 
     // ---- q of the G rows of this kv head: words of elements [8 sub, 8 sub + 8)
     uint4 qv[G];
-    {
-      const uint16_t* qb = static_cast<const uint16_t*>(a.q) +
-                           (int64_t(b) * a.num_qo_heads + int64_t(h) * G) * kD + sub * 8;
+    if (pre) {
 #pragma unroll
-      for (int g = 0; g < G; ++g) qv[g] = *reinterpret_cast<const uint4*>(qb + g * kD);
-      // Consume q here so its load is waited for before the chunk loop; else the
-      // loop's first use of q waits for every load in flight (the next chunk too).
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-        asm volatile("" : "+v"(qv[g].x), "+v"(qv[g].y), "+v"(qv[g].z), "+v"(qv[g].w));
+      for (int g = 0; g < G; ++g) qv[g] = qn[g];
+    } else {
+      load_q(b, h, qv);
     }
+    // Consume q here so its load is waited for before the chunk loop; else the
+    // loop's first use of q waits for every load in flight (the next chunk too).
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      asm volatile("" : "+v"(qv[g].x), "+v"(qv[g].y), "+v"(qv[g].z), "+v"(qv[g].w));
     float kv_pos0 = 0.f;
     float qr[ROPE ? G : 1][8];  // rotated q in fp32 (RoPE only)
     if constexpr (ROPE) {
@@ -329,17 +344,17 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
     // The steady-state body issues its loads unconditionally (the last one or
     // two chunks are peeled), so each compute waits only for its own chunk.
     {
-      KVRegs<S> A, B;
       const int c0 = kv_begin + wave * kChunk;
       const int n = c0 < kv_end ? (kv_end - c0 + kStep - 1) / kStep : 0;
       auto cpos = [&](int i) { return c0 + i * kStep; };
       if (n > 0) {
-        int pidA[S] = {}, pidB[S] = {};
-        if constexpr (FASTPAGE) {
-          chunk_pids(cpos(0), pidA);
-          if (n > 1) chunk_pids(cpos(1), pidB);
+        if (!pre) {
+          if constexpr (FASTPAGE) {
+            chunk_pids(cpos(0), pidA);
+            if (n > 1) chunk_pids(cpos(1), pidB);
+          }
+          load_chunk(A, cpos(0), pidA);
         }
-        load_chunk(A, cpos(0), pidA);
         int i = 0;
         for (; i + 2 < n; i += 2) {
           load_chunk(B, cpos(i + 1), pidB);
@@ -358,6 +373,49 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
         } else {
           compute_chunk(A, cpos(i));
         }
+      }
+    }
+    // ---- issue the next segment's loads (page-aligned path); both chunk
+    // buffers are free here
+    pre = false;
+    if constexpr (FASTPAGE) {
+      if (s + 1 < s_end) {
+        const int nt = segs[4 * (s + 1)];
+        const int nbeg = segs[4 * (s + 1) + 1], nend = segs[4 * (s + 1) + 2];
+        const int nb_ = tiles[4 * nt], nh = tiles[4 * nt + 1];
+        const int nip0 = kv_indptr[nb_];
+        load_q(nb_, nh, qn);
+        const int nc0 = nbeg + wave * kChunk;
+        const int nn = nc0 < nend ? (nend - nc0 + kStep - 1) / kStep : 0;
+        if (nn > 0) {
+          // the same page ids and addresses as chunk_pids / load_chunk compute
+          // for that segment
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            if (c == 1 && nn < 2) break;
+#pragma unroll
+            for (int u = 0; u < S; ++u) {
+              const int cc = nc0 + c * kStep;
+              const int cu = cc + kSub * u < nend ? cc + kSub * u : cc;
+              (c == 0 ? pidA : pidB)[u] = kv_indices[nip0 + (cu >> shift)];
+            }
+          }
+          const uint32_t nhead = uint32_t(nh * kD + sub * 8);
+#pragma unroll
+          for (int u = 0; u < S; ++u) {
+            const int cu = nc0 + kSub * u < nend ? nc0 + kSub * u : nc0;
+            const int64_t base = int64_t(pidA[u]) * a.page_stride + int64_t(cu & (P - 1)) * tstride;
+            const char* kb = reinterpret_cast<const char*>(kp + base);
+            const char* vb = reinterpret_cast<const char*>(vp + base);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const uint32_t off = uint32_t((4 * i + grp) * tstride + nhead) * 2u;
+              A.k[4 * u + i] = *reinterpret_cast<const uint4*>(kb + off);
+              A.v[4 * u + i] = *reinterpret_cast<const uint4*>(vb + off);
+            }
+          }
+        }
+        pre = true;
       }
     }
 

@@ -44,8 +44,8 @@ hipError_t launch_append(const Config& cfg, const AttnArgs& a, hipStream_t strea
 // memory mapped into the GPU's address space to device memory
 hipError_t launch_upload(void* dev_dst, const void* host_src_mapped, size_t bytes,
                          hipStream_t stream);
-// merges the split tiles of a decode plan into o / lse after the decode kernel
-// (fixed grid; counts are read from the plan at run time)
+// merges the split tiles of a plan into o / lse after its main kernel (fixed
+// grid; counts and the merge mode are read from the plan at run time)
 hipError_t launch_plan_merge(const Config& cfg, const AttnArgs& a, int32_t grid,
                              hipStream_t stream);
 

@@ -38,6 +38,8 @@ enum Header : int {
   H_CAUSAL,
   H_OFF_CNT,     // per-tile arrival counters of split tiles (zero in every upload)
   H_OFF_NTILE,   // per-tile number of partials
+  H_MERGE_KERNEL,  // 1: split tiles are merged by the merge kernel after the
+                   // main kernel; 0: by the last arriving workgroup (append)
   HEADER_INTS = 32
 };
 
@@ -79,5 +81,8 @@ constexpr int kDecodeTileKv = 64;   // keys per work block (decode)
 // for the RoPE variant (its hi/lo operands need the registers of 1 wave/SIMD)
 constexpr int append_rows(bool rope) { return rope ? 128 : 256; }
 constexpr int kAppendTileKv = 64;   // keys per work block (append)
+// An append tile split into more partials than this is merged by the merge
+// kernel (spread over all CUs) rather than by one workgroup inside the kernel.
+constexpr int kInKernelMergeMax = 4;
 
 }  // namespace abp

@@ -78,14 +78,16 @@ __global__ __launch_bounds__(256) void merge_two_kernel(const void* o_a, const f
   if (lse_out && e0 == 0) lse_out[row] = lse;
 }
 
-// Merge the split tiles of a decode plan after the decode kernel (the kernel
-// boundary orders the partial stores before these loads). Grid is fixed; 16
+// Merge the split tiles of a plan after its main kernel (the kernel boundary
+// orders the partial stores before these loads); a no-op when the append
+// kernel merged them itself. Grid is fixed; 16
 // lanes take one (merge entry, tile row) and 8 head-dim elements each; counts
 // come from the plan header at run time. Partials are folded in slot order
 // with a running maximum, four at a time so their loads are in flight together.
 template <int OUT_DT>
 __global__ __launch_bounds__(256) void plan_merge_kernel(AttnArgs a) {
   const ABP_CONST_AS int32_t* plan = const_as(a.plan);
+  if (plan[H_MERGE_KERNEL] == 0) return;  // merged inside the append kernel
   const int kind = plan[H_KIND];
   const int rows = plan[H_ROWS];
   const int G = plan[H_GROUP];

@@ -267,7 +267,7 @@ int plan_compute(const Config& cfg, const Layout& L, int32_t batch, const int32_
   int32_t* mrg = blob + L.off_merge;
 
   // tiles, segments, partial slots, merge list (pass 2)
-  int64_t t = 0, s = 0, g0 = 0, slot = 0, m = 0;
+  int64_t t = 0, s = 0, g0 = 0, slot = 0, m = 0, max_nseg = 0;
   for (int32_t b = 0; b < batch; ++b) {
     const int64_t n = int64_t(kv_indptr[b + 1]) - kv_indptr[b];
     const int64_t kv_len = n > 0 ? (n - 1) * P + lpl[b] : 0;
@@ -279,6 +279,7 @@ int plan_compute(const Config& cfg, const Layout& L, int32_t batch, const int32_
         const int64_t g1 = g0 + std::max<int64_t>(1, ceil_div(e, Tk));
         const int64_t w_first = g0 / quota, w_last = (g1 - 1) / quota;
         const int64_t nseg = w_last - w_first + 1;
+        max_nseg = std::max(max_nseg, nseg);
         int32_t* tr = tile + 4 * t;
         tr[0] = b;
         tr[1] = h;
@@ -346,6 +347,7 @@ int plan_compute(const Config& cfg, const Layout& L, int32_t batch, const int32_
   blob[H_CAUSAL] = cfg.causal;
   blob[H_OFF_CNT] = (int32_t)L.off_cnt;  // counters stay zero (memset above)
   blob[H_OFF_NTILE] = (int32_t)L.off_ntile;
+  blob[H_MERGE_KERNEL] = (!append || max_nseg > kInKernelMergeMax) ? 1 : 0;
 
   plan->kind = cfg.kind;
   plan->batch = batch;

@@ -195,11 +195,13 @@ int abp_append_plan(const abp_params* params, int32_t batch, const int32_t* qo_i
 /* Append / prefill attention (MFMA): q [total_qo, Hq, d] ragged by qo_indptr_d;
  * o [total_qo, Hq, d]; lse [total_qo, Hq] or NULL. Causal per params.causal.
  * q_pos_d [total_qo] and kv_pos_offset_d [batch] are read only with RoPE.
- * Launches the persistent append kernel (grid = num_workers) alone: a tile split
- * over several workers is merged by the workgroup whose partial arrives last,
- * counted with per-tile counters in dev_ws that the merging workgroup resets to
- * zero (every plan upload also zeroes them). Runs that share one dev_ws must
- * not overlap. */
+ * Launches the persistent append kernel (grid = num_workers), then a merge
+ * kernel (same grid). A tile split over at most 4 workers is merged inside the
+ * append kernel by the workgroup whose partial arrives last, counted with
+ * per-tile counters in dev_ws that the merging workgroup resets to zero (every
+ * plan upload also zeroes them); when some tile has more partials, the plan
+ * leaves all merges to the merge kernel, which otherwise returns at once. Runs
+ * that share one dev_ws must not overlap. */
 int abp_append_run(const abp_plan* plan, const abp_params* params, const void* q,
                    const void* k_pages, const void* v_pages, const int32_t* qo_indptr_d,
                    const int32_t* kv_indptr_d, const int32_t* kv_indices_d,
