@@ -110,21 +110,21 @@ __device__ __forceinline__ void rope_pair(uint4& lo, uint4& hi, uint4& lo_r, uin
 
 // Rotate a K row chunk (elements 8c..8c+7) held by lane t; its partner chunk
 // (c ^ 8) is held by lane t ^ 8 of the same 16-lane row. Wave-uniform call.
+// f holds the chunk's 8 frequencies as (hi, lo) pairs, loaded once per kernel.
 template <typename T>
-__device__ __forceinline__ void rope_k(const uint4& u, float pos, int c,
-                                       const ABP_CONST_AS float* rope, float out[8]) {
+__device__ __forceinline__ void rope_k(const uint4& u, float pos, int c, const float (&f)[16],
+                                       float out[8]) {
   uint32_t w[4], pw[4];
   w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
 #pragma unroll
   for (int j = 0; j < 4; ++j) pw[j] = dpp_u<kDppRor8>(w[j]);
   const bool hi = c >= 8;
-  const int j0 = (c & 7) * 8;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const float own = (e & 1) ? hi_f32<T>(w[e >> 1]) : lo_f32<T>(w[e >> 1]);
     const float par = (e & 1) ? hi_f32<T>(pw[e >> 1]) : lo_f32<T>(pw[e >> 1]);
     float sn, cs;
-    rope_sincos(pos, rope[2 * (j0 + e)], rope[2 * (j0 + e) + 1], &sn, &cs);
+    rope_sincos(pos, f[2 * e], f[2 * e + 1], &sn, &cs);
     out[e] = __builtin_fmaf(par, hi ? sn : -sn, own * cs);
   }
 }
@@ -192,6 +192,12 @@ __global__ __launch_bounds__(64 * append_waves<ROPE>(), 1) void append_kernel(At
   // 16-byte chunk kc_chunk; V keys 16 vw + 4 v_kg + i (16-key group vw), chunk
   // v_chunk. With 8 waves, waves 0-3 stage K and waves 4-7 stage V.
   const int kc_chunk = tid & 15;
+  // RoPE: this thread's 8 K frequencies (chunk kc_chunk), read once
+  float kfreq[ROPE ? 16 : 1];
+  if constexpr (ROPE) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) kfreq[e] = rope[2 * (kc_chunk & 7) * 8 + e];
+  }
   const int k_row = (tid & 255) >> 4;
   const int v_kg = lane & 3;
   const int v_chunk = lane >> 2;
@@ -325,7 +331,7 @@ __global__ __launch_bounds__(64 * append_waves<ROPE>(), 1) void append_kernel(At
           const int at = (k_row + 16 * i) * kKStride + kc_chunk * 8;
           if constexpr (ROPE) {
             float kr[8];
-            rope_k<T>(kreg[i], (float)(kv_pos0 + kb + k_row + 16 * i), kc_chunk, rope, kr);
+            rope_k<T>(kreg[i], (float)(kv_pos0 + kb + k_row + 16 * i), kc_chunk, kfreq, kr);
             uint4 hi, lo;
             split8<T>(kr, hi, lo);
             *reinterpret_cast<uint4*>(&sK[at]) = hi;

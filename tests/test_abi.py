@@ -124,6 +124,11 @@ def _compare(kind, p, B, qo_indptr, kv_indptr, lpl, W, G, max_qo=0):
                        qo_indptr=qo_indptr, tile_q=256 // G, causal=bool(p.causal))
     for k, v in ref.items():
         assert np.array_equal(got[k], v), k
+    # merge placement: decode always uses the merge kernel; append merges inside
+    # the kernel unless some tile has more than 4 partials
+    np_max = int(ref["tile_num_partials"].max()) if len(ref["tile_num_partials"]) else 0
+    expect = 1 if kind == KIND_DECODE or np_max > 4 else 0
+    assert int(got["merge_kernel"][0]) == expect
     assert plan.num_segments == len(ref["seg_tile"])
     assert plan.num_merges == len(ref["merge_list"])
 

@@ -83,6 +83,72 @@ def test_append_worker_invariance_and_determinism():
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
+def test_merge_modes_and_graph_replay_across_them():
+    """A tile split into more than 4 partials is merged by the merge kernel, at
+    most 4 inside the append kernel. Both give the oracle's result, and a run
+    captured in a graph under one mode replays correctly after a re-plan that
+    selects the other (the launch sequence does not depend on the plan)."""
+    import torch
+    w = wl.small_append(325, [40, 7], [3000, 50], 16, 8, 2, causal=True, extra_pages=64)
+    kv = w.kv
+    dev = upload_kv(kv)
+    q = wl.to_torch(w.q, "bf16", "cuda")
+    params = abp.make_params(8, 2, 128, 16, torch.bfloat16, causal=True)
+    app = abp.BatchAppend(params, max_batch=2, max_qo_tokens=64, num_workers=64)
+    plan = app.plan(w.qo_indptr, kv.kv_indptr, kv.kv_last_page_len)
+    torch.cuda.synchronize()
+    arr = abp.decode_plan_arrays(app.host_ws.numpy(), plan)
+    assert int(arr["merge_kernel"][0]) == 1 and int(arr["tile_num_partials"].max()) > 4
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
+    qo = i32(w.qo_indptr)
+    app.run(q, dev["k"], dev["v"], qo, dev["indptr"], dev["indices"], dev["lpl"], o=o, lse=lse)
+    torch.cuda.synchronize()
+    o_ref, l_ref = ora.append_workload(w)
+    assert_parity(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, "bf16",
+                  what="merge kernel mode")
+    eager1 = (o.clone(), lse.clone())
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            app.run(q, dev["k"], dev["v"], qo, dev["indptr"], dev["indices"], dev["lpl"], o=o,
+                    lse=lse, stream=s)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        o.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, eager1[0]) and torch.equal(lse, eager1[1])
+    # re-plan with short keys: every tile fits in a few blocks, merged in place
+    lens = np.array([64, 20])
+    indptr, _, lpl = wl.page_table(lens, 16, np.arange(10 ** 6))
+    indices = kv.kv_indices[: indptr[-1]].copy()
+    dev["indptr"].copy_(i32(indptr))
+    dev["lpl"].copy_(i32(lpl))
+    dev["indices"][: len(indices)].copy_(i32(indices))
+    qo_b = np.array([0, 40, 47], np.int32)
+    plan = app.plan(qo_b, indptr, lpl)
+    torch.cuda.synchronize()
+    arr = abp.decode_plan_arrays(app.host_ws.numpy(), plan)
+    assert int(arr["merge_kernel"][0]) == 0
+    qo.copy_(i32(qo_b))
+    app.run(q, dev["k"], dev["v"], qo, dev["indptr"], dev["indices"], dev["lpl"], o=o, lse=lse)
+    torch.cuda.synchronize()
+    eager2 = (o.clone(), lse.clone())
+    for _ in range(2):
+        o.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, eager2[0]) and torch.equal(lse, eager2[1])
+    kv2 = wl.PagedKV(16, 2, 128, "bf16", lens, indptr, indices, lpl, kv.k_pages, kv.v_pages)
+    o_ref2, l_ref2 = ora.paged_append(w.q, qo_b, kv2.k_pages, kv2.v_pages, indptr, indices, lpl,
+                                      16, "bf16", 2, causal=True)
+    assert_parity(eager2[0].float().cpu().numpy(), eager2[1].cpu().numpy(), o_ref2, l_ref2,
+                  "bf16", what="merged in place after re-plan")
+
+
 # ----------------------------------------------------------------------------
 # fused RoPE
 # ----------------------------------------------------------------------------
@@ -111,6 +177,29 @@ def test_rope_append_parity(causal):
     o_ref, l_ref = ora.append_workload(w)
     o, l = run_append(w, num_workers=7)
     assert_parity(o, l, o_ref, l_ref, "bf16", what=f"rope append c{int(causal)}")
+
+
+@pytest.mark.parametrize("dtype,G", [("fp16", 8), ("bf16", 1)])
+def test_rope_decode_dtype_and_group(dtype, G):
+    """RoPE decode in fp16 and at the largest and smallest groups (G = 8 is the
+    variant with the most registers)."""
+    w = wl.small_decode(360 + G, [2, 63, 500, 1300], 16, 2 * G, 2, dtype=dtype)
+    w.rope_theta = 500000.0
+    w.kv_pos_offset = np.array([0, 100, 7000, 3], np.int32)
+    w.q_pos = (w.kv_pos_offset + w.kv.kv_len - 1).astype(np.int32)
+    o_ref, l_ref = ora.decode_workload(w)
+    o, l = run_decode(w, num_workers=17)
+    assert_parity(o, l, o_ref, l_ref, dtype, what=f"rope decode {dtype} G{G}")
+
+
+@pytest.mark.parametrize("P", [3, 256])
+def test_rope_append_page_sizes(P):
+    """RoPE append on the per-token page path (P = 3) and with large pages."""
+    w = wl.small_append(370 + P, [5, 64, 150], [70, 64, 600], P, 8, 2, causal=True)
+    w.rope_theta = 500000.0
+    o_ref, l_ref = ora.append_workload(w)
+    o, l = run_append(w, num_workers=10)
+    assert_parity(o, l, o_ref, l_ref, "bf16", what=f"rope append P{P}")
 
 
 # ----------------------------------------------------------------------------
