@@ -154,12 +154,29 @@ __global__ __launch_bounds__(64 * append_waves<ROPE>(), 1) void append_kernel(At
   constexpr int NW = append_waves<ROPE>();
   constexpr int kRows = 32 * NW;
   constexpr int TQ = kRows / G;
-  // two stages: block j is read from stage j & 1 while block j + 1 is stored
-  // into the other
-  __shared__ __align__(16) uint16_t sKs[2][kTk * kKStride];
-  __shared__ __align__(16) uint16_t sKlos[2][ROPE ? kTk * kKStride : 8];  // RoPE: low parts of K
-  __shared__ __align__(16) uint16_t sVts[2][kD * kVStride];
+  // Two stages: block j is read from stage j & 1 while block j + 1 is stored
+  // into the other. Without RoPE a stage is K [64][128] and V [64][128] as in
+  // memory (rows of 256 bytes whose 16-byte chunks are XOR-swizzled by row),
+  // loaded straight from global memory into LDS; with RoPE it is the rotated
+  // K as hi and lo parts and V^T, padded, written from registers.
+  constexpr int kKElems = ROPE ? kTk * kKStride : kTk * kD;
+  constexpr int kKloElems = ROPE ? kTk * kKStride : 0;
+  constexpr int kVElems = ROPE ? kD * kVStride : kTk * kD;
+  constexpr int kStageElems = kKElems + kKloElems + kVElems;
+  // one array per stage, each named at compile time where used, so the
+  // compiler sees that loads into one stage never alias reads of the other
+  __shared__ __align__(16) uint16_t lds0[kStageElems];
+  __shared__ __align__(16) uint16_t lds1[kStageElems];
   __shared__ int s_last;
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  auto stage_base = [&](auto st) -> uint16_t* {
+    if constexpr (decltype(st)::value == 0) return lds0;
+    else return lds1;
+  };
+  auto sK_of = [&](auto st) { return stage_base(st); };
+  auto sKlo_of = [&](auto st) { return stage_base(st) + kKElems; };
+  auto sV_of = [&](auto st) { return stage_base(st) + kKElems + kKloElems; };
 
   const ABP_CONST_AS int32_t* plan = const_as(a.plan);
   const ABP_CONST_AS int32_t* wseg = plan + plan[H_OFF_WSEG];
@@ -321,10 +338,10 @@ __global__ __launch_bounds__(64 * append_waves<ROPE>(), 1) void append_kernel(At
         }
       }
     };
-    auto swrite = [&](int kb, int stage) {
-      uint16_t* sK = sKs[stage];
-      uint16_t* sKlo = sKlos[stage];
-      uint16_t* sVt = sVts[stage];
+    auto swrite = [&](int kb, auto stage) {
+      uint16_t* sK = sK_of(stage);
+      uint16_t* sKlo = sKlo_of(stage);
+      uint16_t* sVt = sV_of(stage);
       if (stage_k) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -356,116 +373,201 @@ __global__ __launch_bounds__(64 * append_waves<ROPE>(), 1) void append_kernel(At
       }
     };
 
+    // Without RoPE: block kb straight into LDS stage `stage`. Each wave
+    // instruction fills 4 rows (1 KB, lane l at byte 16 l); wave w owns rows
+    // 8 w .. 8 w + 7 of K and of V. Lane l stores row r = r0 + l / 16 at chunk
+    // position l % 16, which holds the row's logical chunk (l % 16) ^ swz(r).
+    // Rows past the segment end re-read the last valid rows (in bounds, masked).
+    auto dload = [&](int kb, auto stage) {
+      uint16_t* sK = sK_of(stage);
+      uint16_t* sV = sV_of(stage);
+      const int pos = lane & 15;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r0 = 4 * (2 * wave + i);
+        const int r = r0 + (lane >> 4);
+        const int qk = pos ^ (r & 15);        // K chunk held at this position
+        const int qv = pos ^ (2 * (r & 7));   // V chunk held at this position
+        int64_t row_base;                      // element offset of key kb + r (head h)
+        if constexpr (FASTPAGE) {
+          const int last4 = (kv_end - 1) & ~3;
+          const int kk = min(kb + r0, last4);  // 4-row group, one page
+          row_base = (int64_t)kv_indices[ip0 + (kk >> shift)] * a.page_stride +
+                     (int64_t)((kk & (P - 1)) + (lane >> 4)) * tstride + h * kD;
+        } else {
+          const int key = min(kb + r, kv_end - 1);
+          int page, off;
+          if (shift >= 0) {
+            page = key >> shift;
+            off = key & (P - 1);
+          } else {
+            page = key / P;
+            off = key - page * P;
+          }
+          row_base = (int64_t)a.kv_indices[ip0 + page] * a.page_stride + (int64_t)off * tstride +
+                     h * kD;
+        }
+        __builtin_amdgcn_global_load_lds(kp + row_base + qk * 8, (ABP_LDS void*)(sK + r0 * kD),
+                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vp + row_base + qv * 8, (ABP_LDS void*)(sV + r0 * kD),
+                                         16, 0, 0);
+      }
+    };
+
     if (kv_begin < kv_end) {
-      gload(kv_begin);
-      swrite(kv_begin, 0);
+      if constexpr (ROPE) {
+        gload(kv_begin);
+        swrite(kv_begin, S0{});
+      } else {
+        dload(kv_begin, S0{});
+      }
     }
     __syncthreads();
-    int stage = 0;
-    for (int kb = kv_begin; kb < kv_end; kb += kTk, stage ^= 1) {
+    // one block on stage `st` (blocks alternate between the two stages)
+    auto block = [&](auto st, int kb) __attribute__((always_inline)) {
+      constexpr int ST = decltype(st)::value;
+      using Other = std::integral_constant<int, 1 - ST>;
       const bool has_next = kb + kTk < kv_end;
-      if (has_next) gload(kb + kTk);
-      const uint16_t* sK = sKs[stage];
-      const uint16_t* sKlo = sKlos[stage];
-      const uint16_t* sVt = sVts[stage];
-
-      // ---- S^T = K Q^T: S[mb][nb] holds keys kb + 16 mb + 4 g16 + j, row nb*16 + l16
-      f32x4_t S[4][2];
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        S[mb][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        S[mb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-          const int at = (mb * 16 + l16) * kKStride + kc * 32 + g16 * 8;
-          const uint4 ka = *reinterpret_cast<const uint4*>(&sK[at]);
-          S[mb][0] = mfma<T>(ka, qf[0][kc], S[mb][0]);
-          S[mb][1] = mfma<T>(ka, qf[1][kc], S[mb][1]);
-          if constexpr (ROPE) {  // + Kh Ql + Kl Qh
-            const uint4 kl = *reinterpret_cast<const uint4*>(&sKlo[at]);
-            S[mb][0] = mfma<T>(ka, qfl[0][kc], S[mb][0]);
-            S[mb][1] = mfma<T>(ka, qfl[1][kc], S[mb][1]);
-            S[mb][0] = mfma<T>(kl, qf[0][kc], S[mb][0]);
-            S[mb][1] = mfma<T>(kl, qf[1][kc], S[mb][1]);
-          }
-        }
+      if (has_next) {
+        if constexpr (ROPE) gload(kb + kTk);
+        else dload(kb + kTk, Other{});  // completes before the barrier ending this block
       }
-      // ---- masks: keys past the segment end, causal limit per row
-      const bool edge = (kb + kTk > kv_end) || (CAUSAL && kb + kTk - 1 > tile_min_lim);
-      if (edge) {
+      const uint16_t* sK = sK_of(st);
+      const uint16_t* sKlo = sKlo_of(st);
+      const uint16_t* sVt = sV_of(st);
+
+      // The block is taken as two 32-key halves h, each one step of the online
+      // softmax. Both halves' S products are issued first; the softmax of half
+      // 0 can then run beside the products of half 1, and the P.V products of
+      // half 0 beside the softmax of half 1 (O takes half 0's contribution
+      // before any rescale that half 1 makes).
+      // S^T = K Q^T: S[mb][nb] holds keys kb + 16 mb + 4 g16 + j, row nb*16 + l16
+      f32x4_t S[4][2];
+      auto qk_half = [&](int h) __attribute__((always_inline)) {
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
+        for (int mb = 2 * h; mb < 2 * h + 2; ++mb) {
+          S[mb][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          S[mb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int key = kb + mb * 16 + g16 * 4 + j;
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-              const bool dead = key >= kv_end || (CAUSAL && key > lim[nb]);
-              if (dead) S[mb][nb][j] = kNegInf;
+          for (int kc = 0; kc < 4; ++kc) {
+            // swizzled rows without RoPE: chunk kc * 4 + g16 of row mb * 16 + l16
+            const int at = ROPE ? (mb * 16 + l16) * kKStride + kc * 32 + g16 * 8
+                                : (mb * 16 + l16) * kD + (((kc * 4 + g16) ^ l16) * 8);
+            const uint4 ka = *reinterpret_cast<const uint4*>(&sK[at]);
+            S[mb][0] = mfma<T>(ka, qf[0][kc], S[mb][0]);
+            S[mb][1] = mfma<T>(ka, qf[1][kc], S[mb][1]);
+            if constexpr (ROPE) {  // + Kh Ql + Kl Qh
+              const uint4 kl = *reinterpret_cast<const uint4*>(&sKlo[at]);
+              S[mb][0] = mfma<T>(ka, qfl[0][kc], S[mb][0]);
+              S[mb][1] = mfma<T>(ka, qfl[1][kc], S[mb][1]);
+              S[mb][0] = mfma<T>(kl, qf[0][kc], S[mb][0]);
+              S[mb][1] = mfma<T>(kl, qf[1][kc], S[mb][1]);
             }
           }
-      }
-      // ---- online softmax per row (lazy rescale); P packed as the PV B operand
-      float mx[2];
+        }
+      };
+      // masks of a half (keys past the segment end, causal limit per row),
+      // online softmax with lazy rescale, P of the half packed as the PV B
+      // operand: K-slots of lane group g16 are keys 4 g16..+3 and 16 + 4 g16..+3
+      uint4 pB[2][2];  // [h][nb]
+      auto softmax_half = [&](int h) __attribute__((always_inline)) {
+        const int kbh = kb + 32 * h;
+        const bool edge = (kbh + 32 > kv_end) || (CAUSAL && kbh + 31 > tile_min_lim);
+        if (edge) {
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        float x = kNegInf;
+          for (int mb = 2 * h; mb < 2 * h + 2; ++mb)
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-          x = __builtin_fmaxf(x, __builtin_fmaxf(__builtin_fmaxf(S[mb][nb][0], S[mb][nb][1]),
-                                                 __builtin_fmaxf(S[mb][nb][2], S[mb][nb][3])));
-        mx[nb] = max_over_groups(x);
-      }
-      // the reference max moves only when a score exceeds it by more than thr
-      if (__builtin_amdgcn_ballot_w64((mx[0] > m[0] + thr) || (mx[1] > m[1] + thr))) {
+            for (int j = 0; j < 4; ++j) {
+              const int key = kb + mb * 16 + g16 * 4 + j;
+#pragma unroll
+              for (int nb = 0; nb < 2; ++nb) {
+                const bool dead = key >= kv_end || (CAUSAL && key > lim[nb]);
+                if (dead) S[mb][nb][j] = kNegInf;
+              }
+            }
+        }
+        float mx[2];
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
-          const float mn = __builtin_fmaxf(m[nb], mx[nb]);
-          const float alpha = mn == kNegInf ? 1.f : fast_exp2((m[nb] - mn) * cl2);
-          m[nb] = mn;
-          lsum[nb] *= alpha;
+          float x = kNegInf;
 #pragma unroll
-          for (int md = 0; md < 8; ++md) O[md][nb] *= alpha;
+          for (int mb = 2 * h; mb < 2 * h + 2; ++mb)
+            x = __builtin_fmaxf(x, __builtin_fmaxf(__builtin_fmaxf(S[mb][nb][0], S[mb][nb][1]),
+                                                   __builtin_fmaxf(S[mb][nb][2], S[mb][nb][3])));
+          mx[nb] = max_over_groups(x);
         }
-      }
-      uint4 pB[2][2];  // [kc2][nb]
+        // the reference max moves only when a score exceeds it by more than thr
+        if (__builtin_amdgcn_ballot_w64((mx[0] > m[0] + thr) || (mx[1] > m[1] + thr))) {
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const float mc = (m[nb] == kNegInf ? 0.f : m[nb]) * cl2;
-        float p[4][4];
+          for (int nb = 0; nb < 2; ++nb) {
+            const float mn = __builtin_fmaxf(m[nb], mx[nb]);
+            const float alpha = mn == kNegInf ? 1.f : fast_exp2((m[nb] - mn) * cl2);
+            m[nb] = mn;
+            lsum[nb] *= alpha;
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) p[mb][j] = fast_exp2(__builtin_fmaf(S[mb][nb][j], cl2, -mc));
-        // row sum in fp32 of the unrounded p: lse must not carry P's 16-bit rounding
-        float ps = 0.f;
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) ps += (p[mb][0] + p[mb][1]) + (p[mb][2] + p[mb][3]);
-        lsum[nb] += ps;
-#pragma unroll
-        for (int kc2 = 0; kc2 < 2; ++kc2)
-          pB[kc2][nb] = make_uint4(pack2<T>(p[2 * kc2][0], p[2 * kc2][1]),
-                                   pack2<T>(p[2 * kc2][2], p[2 * kc2][3]),
-                                   pack2<T>(p[2 * kc2 + 1][0], p[2 * kc2 + 1][1]),
-                                   pack2<T>(p[2 * kc2 + 1][2], p[2 * kc2 + 1][3]));
-      }
-      // ---- O^T += V^T P^T: K-slots of lane group g16 are keys 4 g16..+3 and 16 + 4 g16..+3
-#pragma unroll
-      for (int md = 0; md < 8; ++md) {
-#pragma unroll
-        for (int kc2 = 0; kc2 < 2; ++kc2) {
-          const uint16_t* vrow = &sVt[(md * 16 + l16) * kVStride + kc2 * 32 + g16 * 4];
-          const uint2 v0 = *reinterpret_cast<const uint2*>(vrow);
-          const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 16);
-          const uint4 va = make_uint4(v0.x, v0.y, v1.x, v1.y);
-          O[md][0] = mfma<T>(va, pB[kc2][0], O[md][0]);
-          O[md][1] = mfma<T>(va, pB[kc2][1], O[md][1]);
+            for (int md = 0; md < 8; ++md) O[md][nb] *= alpha;
+          }
         }
-      }
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const float mc = (m[nb] == kNegInf ? 0.f : m[nb]) * cl2;
+          float p[2][4];
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              p[i][j] = fast_exp2(__builtin_fmaf(S[2 * h + i][nb][j], cl2, -mc));
+          // row sum in fp32 of the unrounded p: lse must not carry P's 16-bit rounding
+          lsum[nb] += ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) +
+                      ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
+          pB[h][nb] = make_uint4(pack2<T>(p[0][0], p[0][1]), pack2<T>(p[0][2], p[0][3]),
+                                 pack2<T>(p[1][0], p[1][1]), pack2<T>(p[1][2], p[1][3]));
+        }
+      };
+      // O^T += V^T P^T over half h
+      auto pv_half = [&](int h) __attribute__((always_inline)) {
+#pragma unroll
+        for (int md = 0; md < 8; ++md) {
+          uint4 va;
+          if constexpr (ROPE) {
+            const uint16_t* vrow = &sVt[(md * 16 + l16) * kVStride + h * 32 + g16 * 4];
+            const uint2 v0 = *reinterpret_cast<const uint2*>(vrow);
+            const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 16);
+            va = make_uint4(v0.x, v0.y, v1.x, v1.y);
+          } else {
+            // V^T fragment by transpose reads of V: in each 16-lane group,
+            // lane c points at V[key 4 g16 + c / 4 (+ 16)][d 16 md + 4 (c % 4)]
+            // and receives V[4 keys][d 16 md + c] (keys 4 g16..+3, 16 + ..)
+            const int d0 = md * 16 + 4 * (l16 & 3);
+            const int kA = h * 32 + 4 * g16 + (l16 >> 2);
+            const int kB = kA + 16;
+            const int offA = kA * kD + (((d0 >> 3) ^ (2 * (kA & 7))) * 8) + (d0 & 7);
+            const int offB = kB * kD + (((d0 >> 3) ^ (2 * (kB & 7))) * 8) + (d0 & 7);
+            const v4i16_t a4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ABP_LDS v4i16_t*)(sVt + offA));
+            const v4i16_t b4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ABP_LDS v4i16_t*)(sVt + offB));
+            const uint2 av = __builtin_bit_cast(uint2, a4), bv = __builtin_bit_cast(uint2, b4);
+            va = make_uint4(av.x, av.y, bv.x, bv.y);
+          }
+          O[md][0] = mfma<T>(va, pB[h][0], O[md][0]);
+          O[md][1] = mfma<T>(va, pB[h][1], O[md][1]);
+        }
+      };
+      qk_half(0);
+      qk_half(1);
+      softmax_half(0);
+      pv_half(0);
+      softmax_half(1);
+      pv_half(1);
       // the other stage held block j - 1, which every wave finished before the
       // barrier that ended the previous iteration
-      if (has_next) swrite(kb + kTk, stage ^ 1);
+      if constexpr (ROPE) {
+        if (has_next) swrite(kb + kTk, Other{});
+      }
       __syncthreads();
+    };
+    for (int kb = kv_begin; kb < kv_end; kb += 2 * kTk) {
+      block(S0{}, kb);
+      if (kb + kTk < kv_end) block(S1{}, kb + kTk);
     }
 
     // ---- finalize rows: o = O / l, lse = m * scale + ln l

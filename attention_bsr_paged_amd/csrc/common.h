@@ -16,6 +16,9 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+// LDS (group segment) address space, for the gfx950 LDS load / transpose builtins
+#define ABP_LDS __attribute__((address_space(3)))
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // Read-only arrays whose loads at wave-uniform addresses should go through the
