@@ -162,21 +162,24 @@ __global__ __launch_bounds__(64 * append_waves<ROPE>(), 1) void append_kernel(At
   constexpr int kKElems = ROPE ? kTk * kKStride : kTk * kD;
   constexpr int kKloElems = ROPE ? kTk * kKStride : 0;
   constexpr int kVElems = ROPE ? kD * kVStride : kTk * kD;
-  constexpr int kStageElems = kKElems + kKloElems + kVElems;
   // one array per stage, each named at compile time where used, so the
   // compiler sees that loads into one stage never alias reads of the other
-  __shared__ __align__(16) uint16_t lds0[kStageElems];
-  __shared__ __align__(16) uint16_t lds1[kStageElems];
+  __shared__ __align__(16) uint16_t ldsK0[kKElems + kKloElems];
+  __shared__ __align__(16) uint16_t ldsK1[kKElems + kKloElems];
+  __shared__ __align__(16) uint16_t ldsV0[kVElems];
+  __shared__ __align__(16) uint16_t ldsV1[kVElems];
   __shared__ int s_last;
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
-  auto stage_base = [&](auto st) -> uint16_t* {
-    if constexpr (decltype(st)::value == 0) return lds0;
-    else return lds1;
+  auto sK_of = [&](auto st) -> uint16_t* {
+    if constexpr (decltype(st)::value == 0) return ldsK0;
+    else return ldsK1;
   };
-  auto sK_of = [&](auto st) { return stage_base(st); };
-  auto sKlo_of = [&](auto st) { return stage_base(st) + kKElems; };
-  auto sV_of = [&](auto st) { return stage_base(st) + kKElems + kKloElems; };
+  auto sKlo_of = [&](auto st) { return sK_of(st) + kKElems; };
+  auto sV_of = [&](auto st) -> uint16_t* {
+    if constexpr (decltype(st)::value == 0) return ldsV0;
+    else return ldsV1;
+  };
 
   const ABP_CONST_AS int32_t* plan = const_as(a.plan);
   const ABP_CONST_AS int32_t* wseg = plan + plan[H_OFF_WSEG];
