@@ -291,7 +291,7 @@ int abp_decode_run(const abp_plan* plan, const abp_params* params, const void* q
     abp::Layout L;
     int st = prepare_run(ABP_KIND_DECODE, plan, params, dev_ws, dev_bytes, &cfg, &L);
     if (st != ABP_OK) return st;
-    if (plan->batch > 0 && (!q || !k_pages || !v_pages || !kv_indptr_d || !kv_indices_d ||
+    if (plan->num_tiles > 0 && (!q || !k_pages || !v_pages || !kv_indptr_d || !kv_indices_d ||
                             !kv_last_page_len_d || !o))
       return fail(ABP_ERR_INVALID_ARG, "NULL tensor pointer");
     if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o))
@@ -332,7 +332,7 @@ int abp_append_run(const abp_plan* plan, const abp_params* params, const void* q
     abp::Layout L;
     int st = prepare_run(ABP_KIND_APPEND, plan, params, dev_ws, dev_bytes, &cfg, &L);
     if (st != ABP_OK) return st;
-    if (plan->batch > 0 && (!q || !k_pages || !v_pages || !qo_indptr_d || !kv_indptr_d ||
+    if (plan->num_tiles > 0 && (!q || !k_pages || !v_pages || !qo_indptr_d || !kv_indptr_d ||
                             !kv_indices_d || !kv_last_page_len_d || !o))
       return fail(ABP_ERR_INVALID_ARG, "NULL tensor pointer");
     if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o))

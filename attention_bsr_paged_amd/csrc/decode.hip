@@ -63,27 +63,24 @@ __device__ __forceinline__ void set_word(uint4& u, int j, uint32_t v) {
   else u.w = v;
 }
 
-// Rotate this lane's 8 elements (pairs (j, j + 64) split across lanes sub and
-// sub ^ 8) at position `pos`, into fp32. All lanes of the wave must call it
-// together. The rotated values stay in fp32: rounding them back to 16 bits
-// would put ~1e-3 of noise on every logit, which short key ranges do not
-// average out.
+// RoPE (rotate-half): element j pairs with j + 64. With RoPE on, a lane's K
+// (and q) register holds elements [4 sub, 4 sub + 4) in words 0-1 and
+// [64 + 4 sub, 64 + 4 sub + 4) in words 2-3, so both halves of its 4 pairs are
+// local and each angle is needed by one lane only. Rotate them by the angles
+// whose cosines and sines are cs / sn, into fp32: rounding the rotated values
+// back to 16 bits would put ~1e-3 of noise on every logit, which short key
+// ranges do not average out.
 template <typename T>
-__device__ __forceinline__ void rope_rotate8(const uint4& u, float pos, const float* fhi,
-                                             const float* flo, bool hi_half, float out[8]) {
-  uint32_t w[4], pw[4];
+__device__ __forceinline__ void rope_rotate_pairs(const uint4& u, const float cs[4],
+                                                  const float sn[4], float out[8]) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    w[j] = word(u, j);
-    pw[j] = dpp_u<kDppRor8>(w[j]);
-  }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float own = (e & 1) ? hi_f32<T>(w[e >> 1]) : lo_f32<T>(w[e >> 1]);
-    const float par = (e & 1) ? hi_f32<T>(pw[e >> 1]) : lo_f32<T>(pw[e >> 1]);
-    float sn, cs;
-    rope_sincos(pos, fhi[e], flo[e], &sn, &cs);
-    out[e] = __builtin_fmaf(par, hi_half ? sn : -sn, own * cs);
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t wl = (e < 2) ? u.x : u.y;
+    const uint32_t wh = (e < 2) ? u.z : u.w;
+    const float x = (e & 1) ? hi_f32<T>(wl) : lo_f32<T>(wl);
+    const float y = (e & 1) ? hi_f32<T>(wh) : lo_f32<T>(wh);
+    out[e] = __builtin_fmaf(-y, sn[e], x * cs[e]);
+    out[4 + e] = __builtin_fmaf(x, sn[e], y * cs[e]);
   }
 }
 
@@ -121,7 +118,6 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = lane >> 4;
   const int sub = lane & 15;
-  const bool hi_half = sub >= 8;
   const float cl2 = a.sm_scale_log2;
   const float thr = kRescaleLog2 / cl2;  // threshold in raw score units
 
@@ -135,16 +131,32 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
   __shared__ float s_m[kWaves][G];
   __shared__ float s_l[kWaves][G];
 
-  float fhi[8], flo[8];
+  // RoPE: frequencies (revolutions per position, split hi + lo) of this lane's
+  // 4 pairs j = 4 sub + e, and the rotation by 4 positions (c4, s4): a lane's
+  // tokens in a sub-chunk are 4 apart, so only the first one's angles are
+  // evaluated and the next three follow by angle addition
+  float fhi[ROPE ? 4 : 1], flo[ROPE ? 4 : 1], c4[ROPE ? 4 : 1], s4[ROPE ? 4 : 1];
   if constexpr (ROPE) {
     const ABP_CONST_AS float* rope = (const ABP_CONST_AS float*)(plan + plan[H_OFF_ROPE]);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int j = (sub & 7) * 8 + e;
+    for (int e = 0; e < 4; ++e) {
+      const int j = 4 * sub + e;
       fhi[e] = rope[2 * j];
       flo[e] = rope[2 * j + 1];
+      rope_sincos(4.f, fhi[e], flo[e], &s4[e], &c4[e]);
     }
   }
+  // byte offset of this lane's K words from its V words (RoPE layout above)
+  const uint32_t kdel = ROPE ? 8u * sub : 0u;
+  auto load_k = [&](const char* p) -> uint4 {
+    if constexpr (ROPE) {
+      const uint2 lo = *reinterpret_cast<const uint2*>(p);
+      const uint2 hi = *reinterpret_cast<const uint2*>(p + 128);
+      return make_uint4(lo.x, lo.y, hi.x, hi.y);
+    } else {
+      return *reinterpret_cast<const uint4*>(p);
+    }
+  };
 
   // Chunk buffers, page ids and q live across segments: on the page-aligned
   // path the end of a segment's chunk loop issues the loads of the next
@@ -158,7 +170,8 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
     const uint16_t* qb = static_cast<const uint16_t*>(a.q) +
                          (int64_t(b) * a.num_qo_heads + int64_t(h) * G) * kD + sub * 8;
 #pragma unroll
-    for (int g = 0; g < G; ++g) q[g] = *reinterpret_cast<const uint4*>(qb + g * kD);
+    for (int g = 0; g < G; ++g)
+      q[g] = load_k(reinterpret_cast<const char*>(qb + g * kD) - kdel);
   };
 
   for (int s = s_begin; s < s_end; ++s) {
@@ -188,8 +201,11 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
       const int kv_len = n > 0 ? (n - 1) * P + a.kv_last_page_len[b] : 0;
       const int qpos = a.q_pos ? a.q_pos[b] : kv_len - 1;
       kv_pos0 = a.kv_pos_offset ? (float)a.kv_pos_offset[b] : 0.f;
+      float cs[4], sn[4];
 #pragma unroll
-      for (int g = 0; g < G; ++g) rope_rotate8<T>(qv[g], (float)qpos, fhi, flo, hi_half, qr[g]);
+      for (int e = 0; e < 4; ++e) rope_sincos((float)qpos, fhi[e], flo[e], &sn[e], &cs[e]);
+#pragma unroll
+      for (int g = 0; g < G; ++g) rope_rotate_pairs<T>(qv[g], cs, sn, qr[g]);
     }
 
     float m[G], l[G], o[G][8];
@@ -227,7 +243,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
           const char* vb = reinterpret_cast<const char*>(vp + base);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            X.k[4 * u + i] = *reinterpret_cast<const uint4*>(kb + lane_off[i]);
+            X.k[4 * u + i] = load_k(kb + lane_off[i] - kdel);
             X.v[4 * u + i] = *reinterpret_cast<const uint4*>(vb + lane_off[i]);
           }
         } else {
@@ -244,7 +260,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
             }
             const int64_t pg = a.kv_indices[ip0 + page];  // per-lane (vector) load
             const int64_t at = pg * a.page_stride + int64_t(off) * tstride + head_off;
-            X.k[4 * u + i] = *reinterpret_cast<const uint4*>(kp + at);
+            X.k[4 * u + i] = load_k(reinterpret_cast<const char*>(kp + at) - kdel);
             X.v[4 * u + i] = *reinterpret_cast<const uint4*>(vp + at);
           }
         }
@@ -255,11 +271,25 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
     auto compute_sub = [&](const uint4* k4, const uint4* v4, int c) {
       // scores of 4 tokens x G rows, summed over the 16 lanes of the token's row
       float sc[4 * G];
+      float cs[ROPE ? 4 : 1], sn[ROPE ? 4 : 1];
+      if constexpr (ROPE) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          rope_sincos(kv_pos0 + (float)(c + grp), fhi[e], flo[e], &sn[e], &cs[e]);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if constexpr (ROPE) {
+          if (i > 0) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float cn = __builtin_fmaf(-sn[e], s4[e], cs[e] * c4[e]);
+              sn[e] = __builtin_fmaf(cs[e], s4[e], sn[e] * c4[e]);
+              cs[e] = cn;
+            }
+          }
           float kr[8];
-          rope_rotate8<T>(k4[i], kv_pos0 + (float)(c + 4 * i + grp), fhi, flo, hi_half, kr);
+          rope_rotate_pairs<T>(k4[i], cs, sn, kr);
 #pragma unroll
           for (int g = 0; g < G; ++g) {
             float acc = qr[g][0] * kr[0];
@@ -410,7 +440,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const uint32_t off = uint32_t((4 * i + grp) * tstride + nhead) * 2u;
-              A.k[4 * u + i] = *reinterpret_cast<const uint4*>(kb + off);
+              A.k[4 * u + i] = load_k(kb + off - kdel);
               A.v[4 * u + i] = *reinterpret_cast<const uint4*>(vb + off);
             }
           }

@@ -177,7 +177,9 @@ int abp_decode_plan(const abp_params* params, int32_t batch, const int32_t* kv_i
  * q_pos_d [batch] and kv_pos_offset_d [batch] are read only with RoPE (NULL =
  * defaults). Launches the persistent decode kernel (grid = num_workers), then a
  * merge kernel (same grid) that combines the partial states of split tiles.
- * Partial states live in dev_ws: runs that share one dev_ws must not overlap. */
+ * Partial states live in dev_ws: runs that share one dev_ws must not overlap.
+ * The tensor pointers may be NULL only when the plan has no tiles (batch 0);
+ * otherwise NULL gives ABP_ERR_INVALID_ARG. */
 int abp_decode_run(const abp_plan* plan, const abp_params* params, const void* q,
                    const void* k_pages, const void* v_pages, const int32_t* kv_indptr_d,
                    const int32_t* kv_indices_d, const int32_t* kv_last_page_len_d,
@@ -201,7 +203,8 @@ int abp_append_plan(const abp_params* params, int32_t batch, const int32_t* qo_i
  * per-tile counters in dev_ws that the merging workgroup resets to zero (every
  * plan upload also zeroes them); when some tile has more partials, the plan
  * leaves all merges to the merge kernel, which otherwise returns at once. Runs
- * that share one dev_ws must not overlap. */
+ * that share one dev_ws must not overlap. The tensor pointers may be NULL only
+ * when the plan has no tiles (no query tokens in the batch). */
 int abp_append_run(const abp_plan* plan, const abp_params* params, const void* q,
                    const void* k_pages, const void* v_pages, const int32_t* qo_indptr_d,
                    const int32_t* kv_indptr_d, const int32_t* kv_indices_d,

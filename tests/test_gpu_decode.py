@@ -267,3 +267,38 @@ def test_merge_states_kernel():
     assert np.max(np.abs(om.double().cpu().numpy() - o_ref)) <= 1e-5
     assert np.max(np.abs(lm.cpu().numpy()[fin] - l_ref[fin])) <= 1e-5
     assert np.all(np.isneginf(lm.cpu().numpy()[~fin]))
+
+
+def test_empty_batches():
+    """batch 0 plans and runs (no work, nothing written); a batch whose requests
+    all have no pages gives (0, -inf) for every row."""
+    import torch
+    params = abp.make_params(8, 2, 128, 16, torch.bfloat16)
+    dec = abp.BatchDecode(params, max_batch=4, num_workers=8)
+    plan = dec.plan(np.zeros(1, np.int32), np.zeros(0, np.int32))
+    assert plan.num_tiles == 0
+    dev = torch.zeros(1, dtype=torch.int32, device="cuda")
+    kp = torch.zeros((1, 16, 2, 128), dtype=torch.bfloat16, device="cuda")
+    q0 = torch.zeros((0, 8, 128), dtype=torch.bfloat16, device="cuda")
+    o, l = dec.run(q0, kp, kp, dev, dev, dev)
+    torch.cuda.synchronize()
+    assert o.shape == (0, 8, 128)
+    # three requests without pages
+    plan = dec.plan(np.zeros(4, np.int32), np.zeros(3, np.int32))
+    q = torch.randn((3, 8, 128), device="cuda").to(torch.bfloat16)
+    o, l = dec.run(q, kp, kp, torch.zeros(4, dtype=torch.int32, device="cuda"), dev,
+                   torch.zeros(3, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(l))
+    # append with no query tokens at all
+    pa = abp.make_params(8, 2, 128, 16, torch.bfloat16, causal=True)
+    app = abp.BatchAppend(pa, max_batch=2, max_qo_tokens=8, num_workers=8)
+    plan = app.plan(np.zeros(3, np.int32), np.array([0, 1, 2], np.int32), np.array([5, 9], np.int32))
+    assert plan.num_tiles == 0
+    qa = torch.zeros((0, 8, 128), dtype=torch.bfloat16, device="cuda")
+    o, l = app.run(qa, kp, kp, torch.zeros(3, dtype=torch.int32, device="cuda"),
+                   torch.tensor([0, 1, 2], dtype=torch.int32, device="cuda"),
+                   torch.zeros(2, dtype=torch.int32, device="cuda"),
+                   torch.tensor([5, 9], dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert o.shape == (0, 8, 128)
