@@ -196,7 +196,7 @@ def decode_plan_arrays(blob: np.ndarray, plan: AbpPlan):
          "NUM_MERGES", "TILE_Q", "TILE_KV", "ROWS", "GROUP", "NUM_KV_HEADS", "PAGE_SIZE",
          "NUM_BLOCKS", "QUOTA", "OFF_WSEG", "OFF_SEG", "OFF_TILE", "OFF_MERGE", "OFF_ROPE",
          "MAX_TILES", "MAX_SEGS", "MAX_PARTIALS", "CAUSAL", "OFF_CNT", "OFF_NTILE",
-         "MERGE_KERNEL"])}
+         "MERGE_KERNEL", "TILE_HEADS"])}
     W, T, S, M = b[H["WORKERS"]], b[H["NUM_TILES"]], b[H["NUM_SEGS"]], b[H["NUM_MERGES"]]
     seg = b[b[H["OFF_SEG"]]: b[H["OFF_SEG"]] + 4 * S].reshape(S, 4)
     tile = b[b[H["OFF_TILE"]]: b[H["OFF_TILE"]] + 4 * T].reshape(T, 4)
@@ -213,6 +213,7 @@ def decode_plan_arrays(blob: np.ndarray, plan: AbpPlan):
         "tile_first_partial": tile[:, 3].copy(), "tile_num_partials": num_partials,
         "merge_list": mrg[:, 0].copy(),
         "merge_kernel": b[H["MERGE_KERNEL"]: H["MERGE_KERNEL"] + 1].copy(),
+        "tile_heads": b[H["TILE_HEADS"]: H["TILE_HEADS"] + 1].copy(),
     }
 
 

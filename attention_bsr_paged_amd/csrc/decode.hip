@@ -8,12 +8,17 @@
 // bound by HBM bandwidth; the design goal is to keep enough bytes in flight
 // while spending few instructions per byte.
 //
-// Work split: the host planner cuts the (request, kv head) tiles into segments
-// of whole 64-key blocks spread evenly over a fixed grid of workers (section
-// 动态负载均衡调度); one 256-thread workgroup is one worker and walks its
-// segments in order.
+// Work split: the host planner cuts the (request, kv-head group) tiles into
+// segments of whole 64-key blocks spread evenly over a fixed grid of workers
+// (section 动态负载均衡调度); one 256-thread workgroup is one worker and walks
+// its segments in order. When the kv head count is a multiple of 4, a tile
+// holds 4 consecutive kv heads and each wave takes one of them: the workgroup
+// then reads 1 KB runs of every token row together (4 heads x 256 bytes), which
+// the HBM serves faster than 256-byte pieces at the token stride, and each
+// wave owns its head's state, so no workgroup barrier is needed. Otherwise a
+// tile is one head and the 4 waves take its 16-token chunks round-robin.
 //
-// Inside a segment the 4 waves take 16-token chunks round-robin. In a chunk,
+// In a chunk,
 // lane (grp = lane / 16, sub = lane % 16) holds head-dim elements
 // [8 sub, 8 sub + 8) of tokens c + 4 i + grp for i = 0..3: each load
 // instruction reads 4 whole 256-byte head rows (coalesced 128-bit lanes). All
@@ -32,8 +37,9 @@
 // ahead) and all K/V addresses are a uniform page base plus fixed per-lane
 // offsets. Other page sizes translate every token.
 // Chunks are double-buffered in registers. At the end of a segment the states
-// of the 4 token groups and 4 waves are merged, and the tile's rows are written
-// either as the final o / lse or as an fp32 partial state.
+// of the 4 token groups (and of the waves sharing a head) are merged, and the
+// tile's rows are written either as the final o / lse or as an fp32 partial
+// state.
 #include "common.h"
 #include "kernels.h"
 #include "layout.h"
@@ -102,10 +108,11 @@ __device__ __forceinline__ void row16_sum_all(float* x) {
   for (int n = 0; n < N; ++n) x[n] += dpp<kDppMirror>(x[n]);
 }
 
-template <typename T, int G, bool ROPE, bool FASTPAGE, int S>
+template <typename T, int G, bool ROPE, bool FASTPAGE, int S, int HT>
 __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
-  constexpr int kChunk = kSub * S;       // tokens per wave per buffered chunk
-  constexpr int kStep = kWaves * kChunk;  // tokens per workgroup step
+  constexpr int TW = kWaves / HT;     // waves per kv head (they split its keys)
+  constexpr int kChunk = kSub * S;    // tokens per wave per buffered chunk
+  constexpr int kStep = TW * kChunk;  // tokens per step of one head
   const ABP_CONST_AS int32_t* plan = const_as(a.plan);
   const ABP_CONST_AS int32_t* wseg = plan + plan[H_OFF_WSEG];
   const ABP_CONST_AS int32_t* segs = plan + plan[H_OFF_SEG];    // 4 ints per record
@@ -118,6 +125,8 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = lane >> 4;
   const int sub = lane & 15;
+  const int hw = wave % HT;  // this wave's kv head within the tile
+  const int tw = wave / HT;  // this wave's share of the head's keys
   const float cl2 = a.sm_scale_log2;
   const float thr = kRescaleLog2 / cl2;  // threshold in raw score units
 
@@ -127,9 +136,10 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
   const int shift = a.page_shift;
   const int tstride = a.token_stride;
 
-  __shared__ float s_o[kWaves][G][kD];
-  __shared__ float s_m[kWaves][G];
-  __shared__ float s_l[kWaves][G];
+  // cross-wave merge of a head's key shares (only when TW > 1)
+  __shared__ float s_o[TW > 1 ? kWaves : 1][G][kD];
+  __shared__ float s_m[TW > 1 ? kWaves : 1][G];
+  __shared__ float s_l[TW > 1 ? kWaves : 1][G];
 
   // RoPE: frequencies (revolutions per position, split hi + lo) of this lane's
   // 4 pairs j = 4 sub + e, and the rotation by 4 positions (c4, s4): a lane's
@@ -177,7 +187,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
   for (int s = s_begin; s < s_end; ++s) {
     const int tile = segs[4 * s];
     const int kv_begin = segs[4 * s + 1], kv_end = segs[4 * s + 2], slot = segs[4 * s + 3];
-    const int b = tiles[4 * tile], h = tiles[4 * tile + 1];
+    const int b = tiles[4 * tile], h = tiles[4 * tile + 1] + hw;
     const int ip0 = kv_indptr[b];
     const int head_off = h * kD + sub * 8;
 
@@ -374,7 +384,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
     // The steady-state body issues its loads unconditionally (the last one or
     // two chunks are peeled), so each compute waits only for its own chunk.
     {
-      const int c0 = kv_begin + wave * kChunk;
+      const int c0 = kv_begin + tw * kChunk;
       const int n = c0 < kv_end ? (kv_end - c0 + kStep - 1) / kStep : 0;
       auto cpos = [&](int i) { return c0 + i * kStep; };
       if (n > 0) {
@@ -412,10 +422,10 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
       if (s + 1 < s_end) {
         const int nt = segs[4 * (s + 1)];
         const int nbeg = segs[4 * (s + 1) + 1], nend = segs[4 * (s + 1) + 2];
-        const int nb_ = tiles[4 * nt], nh = tiles[4 * nt + 1];
+        const int nb_ = tiles[4 * nt], nh = tiles[4 * nt + 1] + hw;
         const int nip0 = kv_indptr[nb_];
         load_q(nb_, nh, qn);
-        const int nc0 = nbeg + wave * kChunk;
+        const int nc0 = nbeg + tw * kChunk;
         const int nn = nc0 < nend ? (nend - nc0 + kStep - 1) / kStep : 0;
         if (nn > 0) {
           // the same page ids and addresses as chunk_pids / load_chunk compute
@@ -468,55 +478,87 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
       m[g] = M;
       l[g] = lg;
     }
-    if (grp == 0) {
+    if constexpr (TW == 1) {
+      // the wave holds its head's whole state: lanes of token group g % 4
+      // write row g (16 lanes x 8 elements), no workgroup barrier
 #pragma unroll
       for (int g = 0; g < G; ++g) {
+        if ((g & 3) != grp) continue;
+        float out[8];
+        float lse = kNegInf;
+        if (m[g] != kNegInf) {
+          const float inv = 1.f / l[g];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s_o[wave][g][sub * 8 + e] = o[g][e];
-        if (sub == 0) {
-          s_m[wave][g] = m[g];
-          s_l[wave][g] = l[g];
+          for (int e = 0; e < 8; ++e) out[e] = o[g][e] * inv;
+          lse = m[g] * a.sm_scale + fast_log2(l[g]) * kLn2;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) out[e] = 0.f;
+        }
+        if (slot < 0) {
+          const int64_t row = int64_t(b) * a.num_qo_heads + int64_t(h) * G + g;
+          store8_dt(a.o, row * kD + sub * 8, out, a.out_dtype);
+          if (a.lse && sub == 0) a.lse[row] = lse;
+        } else {
+          const int64_t row = int64_t(slot) * (HT * G) + hw * G + g;
+          store8<ABP_F32>(a.o_part, row * kD + sub * 8, out);
+          if (sub == 0) a.lse_part[row] = lse;
         }
       }
-    }
-    __syncthreads();
+    } else {
+      if (grp == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) s_o[wave][g][sub * 8 + e] = o[g][e];
+          if (sub == 0) {
+            s_m[wave][g] = m[g];
+            s_l[wave][g] = l[g];
+          }
+        }
+      }
+      __syncthreads();
 
-    // ---- merge the 4 waves and write the tile's G rows
-    if (threadIdx.x < G * 16) {
-      const int g = threadIdx.x >> 4;
-      const int e0 = (threadIdx.x & 15) * 8;
-      float M = kNegInf;
+      // ---- merge the TW waves of each head and write the tile's HT * G rows
+      if (threadIdx.x < HT * G * 16) {
+        const int rr = threadIdx.x >> 4;  // row within the tile
+        const int hr = rr / G, g = rr - hr * G;
+        const int e0 = (threadIdx.x & 15) * 8;
+        float M = kNegInf;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) M = __builtin_fmaxf(M, s_m[w][g]);
-      float out[8];
-      float lse = kNegInf;
+        for (int j = 0; j < TW; ++j) M = __builtin_fmaxf(M, s_m[hr + HT * j][g]);
+        float out[8];
+        float lse = kNegInf;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) out[e] = 0.f;
-      if (M != kNegInf) {
-        float L = 0.f;
+        for (int e = 0; e < 8; ++e) out[e] = 0.f;
+        if (M != kNegInf) {
+          float L = 0.f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-          const float f = s_m[w][g] == kNegInf ? 0.f : fast_exp2((s_m[w][g] - M) * cl2);
-          L = __builtin_fmaf(f, s_l[w][g], L);
+          for (int j = 0; j < TW; ++j) {
+            const int w = hr + HT * j;
+            const float f = s_m[w][g] == kNegInf ? 0.f : fast_exp2((s_m[w][g] - M) * cl2);
+            L = __builtin_fmaf(f, s_l[w][g], L);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) out[e] = __builtin_fmaf(f, s_o[w][g][e0 + e], out[e]);
+            for (int e = 0; e < 8; ++e) out[e] = __builtin_fmaf(f, s_o[w][g][e0 + e], out[e]);
+          }
+          const float inv = 1.f / L;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) out[e] *= inv;
+          lse = M * a.sm_scale + fast_log2(L) * kLn2;
         }
-        const float inv = 1.f / L;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) out[e] *= inv;
-        lse = M * a.sm_scale + fast_log2(L) * kLn2;
+        if (slot < 0) {
+          const int64_t row =
+              int64_t(b) * a.num_qo_heads + int64_t(tiles[4 * tile + 1] + hr) * G + g;
+          store8_dt(a.o, row * kD + e0, out, a.out_dtype);
+          if (a.lse && e0 == 0) a.lse[row] = lse;
+        } else {
+          const int64_t row = int64_t(slot) * (HT * G) + rr;
+          store8<ABP_F32>(a.o_part, row * kD + e0, out);
+          if (e0 == 0) a.lse_part[row] = lse;
+        }
       }
-      if (slot < 0) {
-        const int64_t row = int64_t(b) * a.num_qo_heads + int64_t(h) * G + g;
-        store8_dt(a.o, row * kD + e0, out, a.out_dtype);
-        if (a.lse && e0 == 0) a.lse[row] = lse;
-      } else {
-        const int64_t row = int64_t(slot) * G + g;
-        store8<ABP_F32>(a.o_part, row * kD + e0, out);
-        if (e0 == 0) a.lse_part[row] = lse;
-      }
+      __syncthreads();
     }
-    __syncthreads();
   }
 }
 
@@ -528,19 +570,26 @@ constexpr int sub_fast() {
   return (G <= 4 && !ROPE) ? 2 : 1;
 }
 
-template <typename T, int G, bool ROPE>
+template <typename T, int G, bool ROPE, int HT>
 hipError_t launch_r(const AttnArgs& a, hipStream_t s) {
   const bool fast = a.page_shift >= 4;  // power of two and a multiple of 16
   if (fast)
-    decode_kernel<T, G, ROPE, true, sub_fast<G, ROPE>()><<<a.workers, 256, 0, s>>>(a);
+    decode_kernel<T, G, ROPE, true, sub_fast<G, ROPE>(), HT><<<a.workers, 256, 0, s>>>(a);
   else
-    decode_kernel<T, G, ROPE, false, 1><<<a.workers, 256, 0, s>>>(a);
+    decode_kernel<T, G, ROPE, false, 1, HT><<<a.workers, 256, 0, s>>>(a);
   return hipGetLastError();
+}
+
+template <typename T, int G, int HT>
+hipError_t launch_h(const Config& cfg, const AttnArgs& a, hipStream_t s) {
+  return cfg.rope ? launch_r<T, G, true, HT>(a, s) : launch_r<T, G, false, HT>(a, s);
 }
 
 template <typename T, int G>
 hipError_t launch_g(const Config& cfg, const AttnArgs& a, hipStream_t s) {
-  return cfg.rope ? launch_r<T, G, true>(a, s) : launch_r<T, G, false>(a, s);
+  static_assert(decode_tile_heads(4) == 4 && decode_tile_heads(2) == 1, "tile heads are 4 or 1");
+  return decode_tile_heads(cfg.hkv) == 4 ? launch_h<T, G, 4>(cfg, a, s)
+                                          : launch_h<T, G, 1>(cfg, a, s);
 }
 
 template <typename T>
@@ -554,21 +603,27 @@ hipError_t launch_t(const Config& cfg, const AttnArgs& a, hipStream_t s) {
   }
 }
 
-template <typename T, int G>
-int occupancy_g(const Config& cfg, bool fast) {
+template <typename T, int G, int HT>
+int occupancy_h(const Config& cfg, bool fast) {
   int n = 0;
   hipError_t e;
   if (cfg.rope)
     e = fast ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                   &n, decode_kernel<T, G, true, true, sub_fast<G, true>()>, 256, 0)
+                   &n, decode_kernel<T, G, true, true, sub_fast<G, true>(), HT>, 256, 0)
              : hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                   &n, decode_kernel<T, G, true, false, 1>, 256, 0);
+                   &n, decode_kernel<T, G, true, false, 1, HT>, 256, 0);
   else
     e = fast ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                   &n, decode_kernel<T, G, false, true, sub_fast<G, false>()>, 256, 0)
+                   &n, decode_kernel<T, G, false, true, sub_fast<G, false>(), HT>, 256, 0)
              : hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                   &n, decode_kernel<T, G, false, false, 1>, 256, 0);
+                   &n, decode_kernel<T, G, false, false, 1, HT>, 256, 0);
   return e == hipSuccess ? n : 0;
+}
+
+template <typename T, int G>
+int occupancy_g(const Config& cfg, bool fast) {
+  return decode_tile_heads(cfg.hkv) == 4 ? occupancy_h<T, G, 4>(cfg, fast)
+                                          : occupancy_h<T, G, 1>(cfg, fast);
 }
 
 template <typename T>

@@ -40,6 +40,7 @@ enum Header : int {
   H_OFF_NTILE,   // per-tile number of partials
   H_MERGE_KERNEL,  // 1: split tiles are merged by the merge kernel after the
                    // main kernel; 0: by the last arriving workgroup (append)
+  H_TILE_HEADS,    // consecutive kv heads per tile
   HEADER_INTS = 32
 };
 
@@ -48,7 +49,7 @@ constexpr int kMaxRopePairs = 64;        // head_dim 128
 
 // Records (16-byte aligned in the blob):
 //   seg   int32 x 4 {tile, kv_begin, kv_end, partial_slot or -1}
-//   tile  int32 x 4 {b, kv_head, q_tile, first_partial or -1}
+//   tile  int32 x 4 {b, first kv_head, q_tile, first_partial or -1}
 //   ntile int32 x 1 number of partials of the tile (0 if not split)
 //   merge int32 x 4 {tile, first_partial, num_partials, 0}
 //   cnt   int32 x 1 per tile: segments of a split tile that have written their
@@ -66,6 +67,7 @@ struct Layout {
   int32_t tile_q = 1;
   int32_t tile_kv = 64;
   int32_t rows = 1;
+  int32_t tile_heads = 1;
   int64_t off_wseg = 0, off_seg = 0, off_tile = 0, off_ntile = 0, off_merge = 0, off_rope = 0,
           off_cnt = 0;
   int64_t plan_ints = 0;       // total int32 of the blob
@@ -77,6 +79,11 @@ struct Layout {
 
 // Tile sizes of the kernels.
 constexpr int kDecodeTileKv = 64;   // keys per work block (decode)
+// kv heads per decode tile: the 4 waves of a decode workgroup take 4
+// consecutive kv heads of one request when the head count allows it, so the
+// workgroup reads 1 KB runs of each token row instead of 256-byte pieces;
+// otherwise one head, with its keys split over the 4 waves
+constexpr int decode_tile_heads(int hkv) { return hkv % 4 == 0 ? 4 : 1; }
 // MFMA rows per append tile (= tile_q * group): 8 waves x 32 rows, or 4 waves
 // for the RoPE variant (its hi/lo operands need the registers of 1 wave/SIMD)
 constexpr int append_rows(bool rope) { return rope ? 128 : 256; }

@@ -112,7 +112,8 @@ int make_layout_caps(const Config& cfg, int64_t max_tiles, int32_t workers, Layo
   if (cfg.kind == ABP_KIND_DECODE) {
     L.tile_q = 1;
     L.tile_kv = kDecodeTileKv;
-    L.rows = cfg.group;
+    L.tile_heads = decode_tile_heads(cfg.hkv);
+    L.rows = cfg.group * L.tile_heads;
   } else {
     L.rows = append_rows(cfg.rope != 0);
     L.tile_q = L.rows / cfg.group;
@@ -162,7 +163,7 @@ int make_layout(const Config& cfg, int32_t max_batch, int32_t max_qo_tokens, int
   }
   int64_t max_tiles;
   if (cfg.kind == ABP_KIND_DECODE) {
-    max_tiles = int64_t(max_batch) * cfg.hkv;
+    max_tiles = int64_t(max_batch) * (cfg.hkv / decode_tile_heads(cfg.hkv));
   } else {
     // sum_b ceil(qo_b / tile_q) <= sum_qo / tile_q + batch
     const int64_t tile_q = append_rows(cfg.rope != 0) / cfg.group;
@@ -213,6 +214,7 @@ int plan_compute(const Config& cfg, const Layout& L, int32_t batch, const int32_
   }
   const int32_t P = cfg.page_size;
   const int32_t Tq = L.tile_q, Tk = L.tile_kv, W = L.workers;
+  const int32_t ngroups = cfg.hkv / L.tile_heads;  // kv-head groups (tiles) per query tile
 
   // validation and the block count N (pass 1)
   int64_t N = 0, T = 0;
@@ -249,9 +251,9 @@ int plan_compute(const Config& cfg, const Layout& L, int32_t batch, const int32_
     }
     for (int64_t qt = 0; qt < nqt; ++qt) {
       const int64_t e = cfg.causal ? kv_len - qo_len + std::min((qt + 1) * Tq, qo_len) : kv_len;
-      N += int64_t(cfg.hkv) * std::max<int64_t>(1, ceil_div(e, Tk));
+      N += int64_t(ngroups) * std::max<int64_t>(1, ceil_div(e, Tk));
     }
-    T += nqt * cfg.hkv;
+    T += nqt * ngroups;
   }
   if (T > L.max_tiles) {
     *err = "batch exceeds the workspace capacities (max_batch / max_qo_tokens)";
@@ -273,7 +275,7 @@ int plan_compute(const Config& cfg, const Layout& L, int32_t batch, const int32_
     const int64_t kv_len = n > 0 ? (n - 1) * P + lpl[b] : 0;
     const int64_t qo_len = append ? int64_t(qo_indptr[b + 1]) - qo_indptr[b] : 1;
     const int64_t nqt = append ? ceil_div(qo_len, Tq) : 1;
-    for (int32_t h = 0; h < cfg.hkv; ++h) {
+    for (int32_t h = 0; h < cfg.hkv; h += L.tile_heads) {
       for (int64_t qt = 0; qt < nqt; ++qt, ++t) {
         const int64_t e = cfg.causal ? kv_len - qo_len + std::min((qt + 1) * Tq, qo_len) : kv_len;
         const int64_t g1 = g0 + std::max<int64_t>(1, ceil_div(e, Tk));
@@ -333,6 +335,7 @@ int plan_compute(const Config& cfg, const Layout& L, int32_t batch, const int32_
   blob[H_ROWS] = L.rows;
   blob[H_GROUP] = cfg.group;
   blob[H_NUM_KV_HEADS] = cfg.hkv;
+  blob[H_TILE_HEADS] = L.tile_heads;
   blob[H_PAGE_SIZE] = P;
   blob[H_NUM_BLOCKS] = (int32_t)std::min<int64_t>(N, INT32_MAX);
   blob[H_QUOTA] = (int32_t)std::min<int64_t>(quota, INT32_MAX);

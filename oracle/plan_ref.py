@@ -13,12 +13,16 @@ The concrete rule below is the plainest Stream-K reading of that passage:
 1. Validate. kv_len_b = (n_b - 1) * page_size + last_page_len_b when request b
    owns n_b > 0 pages (last_page_len_b in [1, page_size]), else 0; indptr must
    be non-decreasing and start at 0; a causal append needs qo_len_b <= kv_len_b.
-2. Tiles, in order: request b, then kv head h, then query tile qt. Decode has one
-   tile per (b, h) (its rows are the qo-head group of h). Append has
-   ceil(qo_len_b / tile_q) query tiles per (b, h). A tile's extent is the number
+2. Tiles, in order: request b, then kv-head group, then query tile qt. A group
+   is heads_per_tile consecutive kv heads starting at h (a property of the
+   kernel that runs the plan: how many heads one worker covers at once; the
+   pages leave it open). Decode has one tile per (b, group) (its rows are the
+   qo heads of the group's kv heads). Append has ceil(qo_len_b / tile_q) query
+   tiles per (b, group). A tile's extent is the number
    of keys its last row may see: kv_len_b - qo_len_b + min((qt + 1) * tile_q,
    qo_len_b) when causal, else kv_len_b. It costs nblk = max(1,
-   ceil(extent / tile_kv)) blocks (an empty tile still writes its (0, -inf)).
+   ceil(extent / tile_kv)) blocks of tile_kv keys of all the group's heads (an
+   empty tile still writes its (0, -inf)).
 3. Partition. N = sum of nblk; quota = ceil(N / W); worker w owns the global
    block range [w * quota, min((w + 1) * quota, N)).
 4. Segments are the intersections of a worker's range with one tile's blocks, in
@@ -70,10 +74,13 @@ def kv_lengths(kv_indptr: Sequence[int], kv_last_page_len: Sequence[int], page_s
 
 def plan_ref(kind: int, batch: int, kv_indptr, kv_last_page_len, page_size: int,
              num_kv_heads: int, num_workers: int, tile_kv: int, qo_indptr=None,
-             tile_q: int = 1, causal: bool = False) -> Dict[str, np.ndarray]:
+             tile_q: int = 1, causal: bool = False,
+             heads_per_tile: int = 1) -> Dict[str, np.ndarray]:
     """Return the plan as int32 arrays (see the module docstring for the rule)."""
     if num_workers < 1 or tile_kv < 1 or tile_q < 1 or num_kv_heads < 1 or batch < 0:
         raise PlanError("bad sizes")
+    if heads_per_tile < 1 or num_kv_heads % heads_per_tile:
+        raise PlanError("heads_per_tile must divide num_kv_heads")
     kv_len = kv_lengths(kv_indptr, kv_last_page_len, page_size, batch)
     if kind == KIND_DECODE:
         qo_len = [1] * batch
@@ -94,7 +101,7 @@ def plan_ref(kind: int, batch: int, kv_indptr, kv_last_page_len, page_size: int,
 
     tile_b, tile_h, tile_qt, extent, nblk = [], [], [], [], []
     for b in range(batch):
-        for h in range(num_kv_heads):
+        for h in range(0, num_kv_heads, heads_per_tile):
             for qt in range(n_qt[b]):
                 if causal:
                     e = kv_len[b] - qo_len[b] + min((qt + 1) * tile_q, qo_len[b])

@@ -118,7 +118,12 @@ def _compare(kind, p, B, qo_indptr, kv_indptr, lpl, W, G, max_qo=0):
     plan = abp.abp_plan_host(kind, p, B, qo_indptr, kv_indptr, lpl, B, max_qo, W, ws)
     got = abp.decode_plan_arrays(ws, plan)
     if kind == KIND_DECODE:
-        ref = plan_ref(KIND_DECODE, B, kv_indptr, lpl, p.page_size, p.num_kv_heads, W, 64)
+        # decode tiles take 4 consecutive kv heads when the count allows, else 1
+        hpt = 4 if p.num_kv_heads % 4 == 0 else 1
+        assert int(got["tile_heads"][0]) == hpt
+        assert plan.rows_per_tile == hpt * G
+        ref = plan_ref(KIND_DECODE, B, kv_indptr, lpl, p.page_size, p.num_kv_heads, W, 64,
+                       heads_per_tile=hpt)
     else:
         ref = plan_ref(KIND_APPEND, B, kv_indptr, lpl, p.page_size, p.num_kv_heads, W, 64,
                        qo_indptr=qo_indptr, tile_q=256 // G, causal=bool(p.causal))
@@ -140,7 +145,7 @@ def test_cpp_planner_matches_reference(data):
     B = data.draw(st.integers(0, 12))
     page = data.draw(st.sampled_from([1, 3, 16, 256]))
     G = data.draw(st.sampled_from([1, 2, 4, 8]))
-    hkv = data.draw(st.integers(1, 3))
+    hkv = data.draw(st.sampled_from([1, 2, 3, 4, 8]))
     W = data.draw(st.integers(1, 70))
     kv_len = data.draw(st.lists(st.integers(0, 3000), min_size=B, max_size=B))
     npg = [-(-n // page) for n in kv_len]

@@ -39,6 +39,22 @@ def test_append_causal_hand_example():
     assert p["tile_first_partial"].tolist() == [-1, 0, -1, 2, -1, -1]
 
 
+def test_decode_head_groups_hand_example():
+    # 2 requests of 10 and 4 keys, 4 kv heads in groups of 2, tile_kv 4, W 3.
+    # Tiles (b, h): (0, 0) (0, 2) cost 3 blocks each, (1, 0) (1, 2) cost 1: N = 8,
+    # quota 3. Worker 0: tile 0 whole. Worker 1: tile 1 whole. Worker 2: tiles 2, 3.
+    p = plan_ref(KIND_DECODE, 2, [0, 3, 4], [2, 4], 4, 4, 3, 4, heads_per_tile=2)
+    assert p["tile_b"].tolist() == [0, 0, 1, 1]
+    assert p["tile_h"].tolist() == [0, 2, 0, 2]
+    assert p["quota"].tolist() == [3]
+    assert p["worker_seg_indptr"].tolist() == [0, 1, 2, 4]
+    assert p["seg_kv_end"].tolist() == [10, 10, 4, 4]
+    assert p["seg_partial"].tolist() == [-1, -1, -1, -1]
+    assert p["merge_list"].tolist() == []
+    with pytest.raises(PlanError):
+        plan_ref(KIND_DECODE, 2, [0, 3, 4], [2, 4], 4, 4, 3, 4, heads_per_tile=3)
+
+
 def test_empty_request_still_gets_a_block():
     p = plan_ref(KIND_DECODE, 3, [0, 0, 2, 2], [0, 3, 0], 4, 1, 8, 64)
     assert p["num_blocks"].tolist() == [3]
@@ -100,7 +116,8 @@ def check_invariants(p, W, Tk, extents):
 def test_invariants_random(data):
     B = data.draw(st.integers(0, 9))
     P = data.draw(st.sampled_from([1, 3, 16, 256]))
-    Hkv = data.draw(st.integers(1, 3))
+    Hkv = data.draw(st.integers(1, 4))
+    hpt = data.draw(st.sampled_from([d for d in (1, 2, 4) if Hkv % d == 0]))
     W = data.draw(st.integers(1, 40))
     Tk = data.draw(st.sampled_from([1, 16, 64]))
     kv_len = data.draw(st.lists(st.integers(0, 700), min_size=B, max_size=B))
@@ -109,18 +126,18 @@ def test_invariants_random(data):
     lpl = [n - (k - 1) * P if k else 0 for n, k in zip(kv_len, npg)]
     append = data.draw(st.booleans())
     if not append:
-        p = plan_ref(KIND_DECODE, B, indptr, lpl, P, Hkv, W, Tk)
-        ext = [n for n in kv_len for _ in range(Hkv)]
+        p = plan_ref(KIND_DECODE, B, indptr, lpl, P, Hkv, W, Tk, heads_per_tile=hpt)
+        ext = [n for n in kv_len for _ in range(Hkv // hpt)]
     else:
         causal = data.draw(st.booleans())
         Tq = data.draw(st.sampled_from([1, 4, 32]))
         qo = [data.draw(st.integers(0, n if causal else 90)) for n in kv_len]
         qo_indptr = np.concatenate([[0], np.cumsum(qo)]).astype(int)
         p = plan_ref(KIND_APPEND, B, indptr, lpl, P, Hkv, W, Tk, qo_indptr=qo_indptr,
-                     tile_q=Tq, causal=causal)
+                     tile_q=Tq, causal=causal, heads_per_tile=hpt)
         ext = []
         for n, m in zip(kv_len, qo):
-            for _ in range(Hkv):
+            for _ in range(Hkv // hpt):
                 for qt in range(-(-m // Tq)):
                     ext.append(n - m + min((qt + 1) * Tq, m) if causal else n)
     check_invariants(p, W, Tk, ext)
