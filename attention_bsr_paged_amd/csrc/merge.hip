@@ -80,10 +80,13 @@ __global__ __launch_bounds__(256) void merge_two_kernel(const void* o_a, const f
 
 // Merge the split tiles of a plan after its main kernel (the kernel boundary
 // orders the partial stores before these loads); a no-op when the append
-// kernel merged them itself. Grid is fixed; 16
-// lanes take one (merge entry, tile row) and 8 head-dim elements each; counts
-// come from the plan header at run time. Partials are folded in slot order
-// with a running maximum, four at a time so their loads are in flight together.
+// kernel merged them itself. Grid is fixed; counts come from the plan header
+// at run time. One wave takes one (merge entry, tile row): its 4 groups of 16
+// lanes fold every 4th partial (8 head-dim elements per lane) with a running
+// maximum, loading 4 partials per group at a time, so 16 partials are in
+// flight per round trip; the groups' states are then combined by lane
+// exchange. Rows with many partials (a long request split over many workers)
+// thus take few dependent memory round trips.
 template <int OUT_DT>
 __global__ __launch_bounds__(256) void plan_merge_kernel(AttnArgs a) {
   const ABP_CONST_AS int32_t* plan = const_as(a.plan);
@@ -96,8 +99,11 @@ __global__ __launch_bounds__(256) void plan_merge_kernel(AttnArgs a) {
   const ABP_CONST_AS int32_t* tiles = plan + plan[H_OFF_TILE];
   const ABP_CONST_AS int32_t* merges = plan + plan[H_OFF_MERGE];
   const int total = num_merges * rows;
-  const int e0 = (threadIdx.x & 15) * 8;
-  for (int ri = blockIdx.x * 16 + (threadIdx.x >> 4); ri < total; ri += gridDim.x * 16) {
+  const int lane = threadIdx.x & 63;
+  const int q = lane >> 4;  // lane group: partials q, q + 4, q + 8, ...
+  const int e0 = (lane & 15) * 8;
+  const int nwaves = gridDim.x * 4;
+  for (int ri = blockIdx.x * 4 + (threadIdx.x >> 6); ri < total; ri += nwaves) {
     const int m = ri / rows;
     const int r = ri - m * rows;
     const int mtile = merges[4 * m], mfirst = merges[4 * m + 1], n = merges[4 * m + 2];
@@ -111,7 +117,7 @@ __global__ __launch_bounds__(256) void plan_merge_kernel(AttnArgs a) {
       const int q0 = a.qo_indptr[tb];
       const int qo_len = a.qo_indptr[tb + 1] - q0;
       const int tloc = tq * Tq + r / G;
-      if (tloc >= qo_len) continue;
+      if (tloc >= qo_len) continue;  // uniform over the wave
       token = q0 + tloc;
       head = th * G + (r % G);
     }
@@ -119,12 +125,12 @@ __global__ __launch_bounds__(256) void plan_merge_kernel(AttnArgs a) {
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-    for (int i0 = 0; i0 < n; i0 += 4) {
+    for (int i0 = q; i0 < n; i0 += 16) {
       float l[4], v[4][8];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        if (i0 + j < n) {
-          const int64_t sr = int64_t(mfirst + i0 + j) * rows + r;
+        if (i0 + 4 * j < n) {
+          const int64_t sr = int64_t(mfirst + i0 + 4 * j) * rows + r;
           l[j] = a.lse_part[sr];
           load8<ABP_F32>(a.o_part, sr * 128 + e0, v[j]);
         } else {
@@ -144,13 +150,28 @@ __global__ __launch_bounds__(256) void plan_merge_kernel(AttnArgs a) {
         for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(acc[e], sc, wt * v[j][e]);
       }
     }
+    // combine the 4 lane groups (lanes xor 16, xor 32)
+    float Mall = __builtin_fmaxf(M, __shfl_xor(M, 16));
+    Mall = __builtin_fmaxf(Mall, __shfl_xor(Mall, 32));
+    const float f = M == kNegInf ? 0.f : fast_exp2((M - Mall) * kLog2e);
+    tot *= f;
+    tot += __shfl_xor(tot, 16);
+    tot += __shfl_xor(tot, 32);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = acc[e] * f;
+      x += __shfl_xor(x, 16);
+      x += __shfl_xor(x, 32);
+      acc[e] = x;
+    }
+    if (q != 0) continue;
     float out[8];
     float lse = kNegInf;
-    if (M != kNegInf) {
+    if (Mall != kNegInf) {
       const float inv = 1.f / tot;
 #pragma unroll
       for (int e = 0; e < 8; ++e) out[e] = acc[e] * inv;
-      lse = M + fast_log2(tot) * kLn2;
+      lse = Mall + fast_log2(tot) * kLn2;
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) out[e] = 0.f;

@@ -6,9 +6,10 @@
 // spread them over the compute units; on the GPU, a persistent kernel with a
 // fixed grid follows the plan. The rule implemented here:
 //
-//  * tiles in order (request, kv head, query tile); a tile's extent is the
-//    number of keys its last row may see, and it costs max(1, ceil(extent /
-//    tile_kv)) blocks;
+//  * tiles in order (request, kv-head group, query tile); a group is the
+//    kernel's heads per tile (decode: 4 consecutive kv heads when the count is
+//    a multiple of 4, else 1; append: 1); a tile's extent is the number of keys
+//    its last row may see, and it costs max(1, ceil(extent / tile_kv)) blocks;
 //  * the N blocks are split into equal contiguous ranges of quota = ceil(N / W)
 //    blocks, one per worker;
 //  * a segment is one tile's share of one worker's range; a tile cut into
