@@ -145,7 +145,7 @@ def test_cpp_planner_matches_reference(data):
     B = data.draw(st.integers(0, 12))
     page = data.draw(st.sampled_from([1, 3, 16, 256]))
     G = data.draw(st.sampled_from([1, 2, 4, 8]))
-    hkv = data.draw(st.sampled_from([1, 2, 3, 4, 8]))
+    hkv = data.draw(st.sampled_from([1, 2, 3, 4, 8, 12, 16]))
     W = data.draw(st.integers(1, 70))
     kv_len = data.draw(st.lists(st.integers(0, 3000), min_size=B, max_size=B))
     npg = [-(-n // page) for n in kv_len]

@@ -35,6 +35,28 @@ def test_small_decode_parity(P, G):
         assert_parity(o, l, o_ref, l_ref, "bf16", what=f"P{P} G{G} W{W}")
 
 
+@pytest.mark.parametrize("hkv", [4, 8, 12, 16])
+@pytest.mark.parametrize("G", [1, 4])
+@pytest.mark.parametrize("rope", [False, True])
+def test_head_group_tiles(hkv, G, rope):
+    """kv head counts that are multiples of 4, where a decode tile holds 4
+    consecutive heads and every wave of a workgroup owns one of them (1, 2, 3
+    or 4 tiles per request). Page sizes 3 (per-token path) and 16, grids of 1,
+    7 and 64 workers, with and without RoPE."""
+    for P in (3, 16):
+        say(f"[case] head groups hkv={hkv} G={G} rope={rope} P={P}")
+        w = wl.small_decode(400 + 10 * hkv + G + P, [0, 1, 17, 64, 65, 700, 1500], P, hkv * G,
+                            hkv, dtype="bf16")
+        if rope:
+            w.rope_theta = 500000.0
+            w.kv_pos_offset = np.array([0, 5, 100, 7000, 3, 0, 64], np.int32)
+            w.q_pos = (w.kv_pos_offset + w.kv.kv_len - 1).astype(np.int32)
+        o_ref, l_ref = ora.decode_workload(w)
+        for W in (1, 7, 64):
+            o, l = run_decode(w, num_workers=W)
+            assert_parity(o, l, o_ref, l_ref, "bf16", what=f"hkv{hkv} G{G} rope{rope} P{P} W{W}")
+
+
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("out", [None, "fp32"])
 def test_dtypes(dtype, out):
