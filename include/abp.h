@@ -118,7 +118,9 @@ typedef struct abp_plan {
   int32_t num_workers;   /* grid size of the persistent kernel */
   int32_t tile_q;        /* query tokens per tile (1 for decode) */
   int32_t tile_kv;       /* keys per work block */
-  int32_t rows_per_tile; /* tile_q * group */
+  int32_t rows_per_tile; /* append: tile_q * group; decode: group * kv heads per
+                            tile (4 consecutive kv heads when num_kv_heads is a
+                            multiple of 4, else 1) */
   int32_t num_tiles;
   int32_t num_segments;
   int32_t num_partials;  /* partial (o, lse) slots used by split tiles */
