@@ -108,24 +108,21 @@ __device__ __forceinline__ void rope_pair(uint4& lo, uint4& hi, uint4& lo_r, uin
   split8<T>(rb, hi, hi_r);
 }
 
-// Rotate a K row chunk (elements 8c..8c+7) held by lane t; its partner chunk
-// (c ^ 8) is held by lane t ^ 8 of the same 16-lane row. Wave-uniform call.
-// f holds the chunk's 8 frequencies as (hi, lo) pairs, loaded once per kernel.
+// Rotate the 4 rotary pairs a lane holds for one K row: u has elements
+// 4c..4c+3 in words 0-1 and their partners 64+4c.. in words 2-3; cs / sn are
+// the cosines and sines of the pairs' angles. out[e] / out[4 + e] are the
+// rotated elements 4c + e and 64 + 4c + e.
 template <typename T>
-__device__ __forceinline__ void rope_k(const uint4& u, float pos, int c, const float (&f)[16],
-                                       float out[8]) {
-  uint32_t w[4], pw[4];
-  w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
+__device__ __forceinline__ void rope_k_pairs(const uint4& u, const float (&cs)[4],
+                                             const float (&sn)[4], float out[8]) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) pw[j] = dpp_u<kDppRor8>(w[j]);
-  const bool hi = c >= 8;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float own = (e & 1) ? hi_f32<T>(w[e >> 1]) : lo_f32<T>(w[e >> 1]);
-    const float par = (e & 1) ? hi_f32<T>(pw[e >> 1]) : lo_f32<T>(pw[e >> 1]);
-    float sn, cs;
-    rope_sincos(pos, f[2 * e], f[2 * e + 1], &sn, &cs);
-    out[e] = __builtin_fmaf(par, hi ? sn : -sn, own * cs);
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t wl = (e < 2) ? u.x : u.y;
+    const uint32_t wh = (e < 2) ? u.z : u.w;
+    const float x = (e & 1) ? hi_f32<T>(wl) : lo_f32<T>(wl);
+    const float y = (e & 1) ? hi_f32<T>(wh) : lo_f32<T>(wh);
+    out[e] = __builtin_fmaf(-y, sn[e], x * cs[e]);
+    out[4 + e] = __builtin_fmaf(x, sn[e], y * cs[e]);
   }
 }
 
@@ -212,11 +209,19 @@ __global__ __launch_bounds__(64 * append_waves<ROPE>(), 1) void append_kernel(At
   // 16-byte chunk kc_chunk; V keys 16 vw + 4 v_kg + i (16-key group vw), chunk
   // v_chunk. With 8 waves, waves 0-3 stage K and waves 4-7 stage V.
   const int kc_chunk = tid & 15;
-  // RoPE: this thread's 8 K frequencies (chunk kc_chunk), read once
-  float kfreq[ROPE ? 16 : 1];
+  // RoPE: a thread stages both halves of the rotary pairs j = 4 kc_chunk + e
+  // (e < 4) of its K rows, so each angle is computed once. Its rows are 16
+  // keys apart: the first row's angles are evaluated and the next follow by
+  // angle addition with the rotation by 16 positions (c16, s16).
+  float kfhi[ROPE ? 4 : 1], kflo[ROPE ? 4 : 1], c16[ROPE ? 4 : 1], s16[ROPE ? 4 : 1];
   if constexpr (ROPE) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) kfreq[e] = rope[2 * (kc_chunk & 7) * 8 + e];
+    for (int e = 0; e < 4; ++e) {
+      const int j = 4 * kc_chunk + e;
+      kfhi[e] = rope[2 * j];
+      kflo[e] = rope[2 * j + 1];
+      rope_sincos(16.f, kfhi[e], kflo[e], &s16[e], &c16[e]);
+    }
   }
   const int k_row = (tid & 255) >> 4;
   const int v_kg = lane & 3;
@@ -235,7 +240,8 @@ __global__ __launch_bounds__(64 * append_waves<ROPE>(), 1) void append_kernel(At
     const int npg = kv_indptr[b + 1] - ip0;
     const int kv_len = npg > 0 ? (npg - 1) * P + a.kv_last_page_len[b] : 0;
     const int kv_pos0 = (ROPE && a.kv_pos_offset) ? a.kv_pos_offset[b] : 0;
-    const int koff_lane = k_row * tstride + h * kD + kc_chunk * 8;       // elements
+    // elements; with RoPE the first piece of the lane's pairs (see above)
+    const int koff_lane = k_row * tstride + h * kD + kc_chunk * (ROPE ? 4 : 8);
     const int voff_lane = (4 * v_kg) * tstride + h * kD + v_chunk * 8;   // + i * tstride
 
     // ---- Q fragments (B operand of S^T = K Q^T) for this wave's 32 rows
@@ -282,6 +288,15 @@ __global__ __launch_bounds__(64 * append_waves<ROPE>(), 1) void append_kernel(At
       if constexpr (NW == 4) return vreg[i];
       else return kreg[i];
     };
+    auto kload = [&](const uint16_t* p) -> uint4 {
+      if constexpr (ROPE) {
+        const uint2 lo = *reinterpret_cast<const uint2*>(p);
+        const uint2 hi = *reinterpret_cast<const uint2*>(p + 64);
+        return make_uint4(lo.x, lo.y, hi.x, hi.y);
+      } else {
+        return *reinterpret_cast<const uint4*>(p);
+      }
+    };
     auto gload = [&](int kb) {
       if constexpr (FASTPAGE) {
         // one page id per 16-key group, on the scalar unit; groups past the
@@ -293,7 +308,7 @@ __global__ __launch_bounds__(64 * append_waves<ROPE>(), 1) void append_kernel(At
             const int kk = min(kb + 16 * i, last16);
             const int64_t base = (int64_t)kv_indices[ip0 + (kk >> shift)] * a.page_stride +
                                  (int64_t)(kk & (P - 1)) * tstride;
-            kreg[i] = *reinterpret_cast<const uint4*>(kp + base + koff_lane);
+            kreg[i] = kload(kp + base + koff_lane);
           }
         }
         if (stage_v) {
@@ -318,8 +333,8 @@ __global__ __launch_bounds__(64 * append_waves<ROPE>(), 1) void append_kernel(At
               off = key - page * P;
             }
             const int64_t pg = a.kv_indices[ip0 + page];
-            kreg[i] = *reinterpret_cast<const uint4*>(kp + pg * a.page_stride +
-                                                      (int64_t)off * tstride + h * kD + kc_chunk * 8);
+            kreg[i] = kload(kp + pg * a.page_stride + (int64_t)off * tstride + h * kD +
+                            kc_chunk * (ROPE ? 4 : 8));
           }
         }
         if (stage_v) {
@@ -346,17 +361,34 @@ __global__ __launch_bounds__(64 * append_waves<ROPE>(), 1) void append_kernel(At
       uint16_t* sKlo = sKlo_of(stage);
       uint16_t* sVt = sV_of(stage);
       if (stage_k) {
+        float cs[ROPE ? 4 : 1], sn[ROPE ? 4 : 1];
+        if constexpr (ROPE) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            rope_sincos((float)(kv_pos0 + kb + k_row), kfhi[e], kflo[e], &sn[e], &cs[e]);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int at = (k_row + 16 * i) * kKStride + kc_chunk * 8;
           if constexpr (ROPE) {
+            if (i > 0) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float cn = __builtin_fmaf(-sn[e], s16[e], cs[e] * c16[e]);
+                sn[e] = __builtin_fmaf(cs[e], s16[e], sn[e] * c16[e]);
+                cs[e] = cn;
+              }
+            }
             float kr[8];
-            rope_k<T>(kreg[i], (float)(kv_pos0 + kb + k_row + 16 * i), kc_chunk, kfreq, kr);
+            rope_k_pairs<T>(kreg[i], cs, sn, kr);
             uint4 hi, lo;
             split8<T>(kr, hi, lo);
-            *reinterpret_cast<uint4*>(&sK[at]) = hi;
-            *reinterpret_cast<uint4*>(&sKlo[at]) = lo;
+            const int at = (k_row + 16 * i) * kKStride + kc_chunk * 4;
+            *reinterpret_cast<uint2*>(&sK[at]) = make_uint2(hi.x, hi.y);
+            *reinterpret_cast<uint2*>(&sK[at + 64]) = make_uint2(hi.z, hi.w);
+            *reinterpret_cast<uint2*>(&sKlo[at]) = make_uint2(lo.x, lo.y);
+            *reinterpret_cast<uint2*>(&sKlo[at + 64]) = make_uint2(lo.z, lo.w);
           } else {
+            const int at = (k_row + 16 * i) * kKStride + kc_chunk * 8;
             *reinterpret_cast<uint4*>(&sK[at]) = kreg[i];
           }
         }
