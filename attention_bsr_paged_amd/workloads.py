@@ -152,6 +152,7 @@ class Workload:
     qo_indptr: Optional[np.ndarray] = None   # int32 [B+1], append only
     causal: bool = False
     rope_theta: float = 0.0        # 0 -> no RoPE
+    rope_llama31: Optional[tuple] = None  # (factor, low_freq_factor, high_freq_factor, old_ctx)
     q_pos: Optional[np.ndarray] = None       # int32, per query token
     kv_pos_offset: Optional[np.ndarray] = None  # int32 [B]
     prefix: Optional[PagedKV] = None         # cascade: the shared prefix (one "request")
@@ -279,3 +280,137 @@ def small_append(seed: int, qo_lens: List[int], kv_lens: List[int], page_size: i
     q = normal_bits(rng, (int(qo_indptr[-1]), num_qo_heads, head_dim), dtype)
     return Workload(f"small_append_s{seed}", "append", seed, dtype, num_qo_heads, num_kv_heads,
                     head_dim, kv, q, qo_indptr=qo_indptr, causal=causal)
+
+
+# ----------------------------------------------------------------------------
+# block-sparse attention over a dense K/V
+# ----------------------------------------------------------------------------
+@dataclass
+class BsrWorkload:
+    """q [M, Hq, d], k / v [N, Hkv, d] (storage bits) and a block-sparse-row mask:
+    row block i (R queries) sees column blocks indices[indptr[i]:indptr[i+1]] (C keys each)."""
+
+    name: str
+    seed: int
+    dtype: str
+    num_qo_heads: int
+    num_kv_heads: int
+    head_dim: int
+    R: int
+    C: int
+    indptr: np.ndarray    # int32 [ceil(M / R) + 1]
+    indices: np.ndarray   # int32 [nnz blocks]
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+
+    @property
+    def M(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def N(self) -> int:
+        return int(self.k.shape[0])
+
+    @property
+    def sm_scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.head_dim))
+
+
+def bsr_pattern(rng: np.random.Generator, num_row_blocks: int, num_col_blocks: int,
+                density: float, empty_rows=()):
+    """Each row block lists round(density * num_col_blocks) (at least 1) distinct
+    column blocks drawn uniformly without replacement, sorted; rows in
+    ``empty_rows`` list none."""
+    k = max(1, int(round(density * num_col_blocks)))
+    indptr = np.zeros(num_row_blocks + 1, dtype=np.int32)
+    rows = []
+    for i in range(num_row_blocks):
+        if i in empty_rows or num_col_blocks == 0:
+            cols = np.zeros(0, dtype=np.int32)
+        else:
+            cols = np.sort(rng.choice(num_col_blocks, size=min(k, num_col_blocks), replace=False))
+        rows.append(cols.astype(np.int32))
+        indptr[i + 1] = indptr[i] + len(cols)
+    indices = np.concatenate(rows) if rows else np.zeros(0, np.int32)
+    return indptr, indices.astype(np.int32)
+
+
+def small_bsr(seed: int, M: int, N: int, R: int, C: int, num_qo_heads: int, num_kv_heads: int,
+              density: float = 0.3, dtype: str = BF16, head_dim: int = 128,
+              empty_rows=()) -> BsrWorkload:
+    rng = np.random.Generator(np.random.PCG64(seed))
+    nrb = -(-M // R) if M else 0
+    indptr, indices = bsr_pattern(rng, nrb, N // C, density, empty_rows)
+    q = normal_bits(rng, (M, num_qo_heads, head_dim), dtype)
+    k = normal_bits(rng, (N, num_kv_heads, head_dim), dtype)
+    v = normal_bits(rng, (N, num_kv_heads, head_dim), dtype)
+    return BsrWorkload(f"small_bsr_s{seed}", seed, dtype, num_qo_heads, num_kv_heads, head_dim,
+                       R, C, indptr, indices, q, k, v)
+
+
+def bsr_sparse(seed: int = 1006, M: int = 8192, N: int = 8192, R: int = 64, C: int = 16,
+               density: float = 0.25) -> BsrWorkload:
+    """Block-sparse attention: one 8192-token sequence, GQA 32/8, d 128, bf16;
+    row blocks of 64 queries, column blocks of 16 keys, each row block seeing a
+    random quarter of the column blocks."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    Hq, Hkv, d = 32, 8, 128
+    indptr, indices = bsr_pattern(rng, M // R, N // C, density)
+    q = normal_bits(rng, (M, Hq, d), BF16)
+    k = normal_bits(rng, (N, Hkv, d), BF16)
+    v = normal_bits(rng, (N, Hkv, d), BF16)
+    return BsrWorkload(f"bsr_M{M}_N{N}_R{R}_C{C}_density{density}_gqa32x8_d128_bf16", seed,
+                       BF16, Hq, Hkv, d, R, C, indptr, indices, q, k, v)
+
+
+# ----------------------------------------------------------------------------
+# new tokens for a paged cache
+# ----------------------------------------------------------------------------
+@dataclass
+class PageAppendWorkload:
+    """New K/V rows ``[nnz, Hkv, d]`` ragged by ``append_indptr`` and the paged
+    cache (page table already extended to hold them) they are written into."""
+
+    name: str
+    seed: int
+    kv: PagedKV
+    append_indptr: np.ndarray   # int32 [B + 1]
+    k_new: np.ndarray
+    v_new: np.ndarray
+
+    @property
+    def nnz(self) -> int:
+        return int(self.append_indptr[-1])
+
+
+def page_append(seed: int, kv_lens, append_lens, page_size: int, num_kv_heads: int,
+                head_dim: int = 128, dtype: str = BF16, extra_pages: int = 2,
+                name: str = "") -> PageAppendWorkload:
+    """A paged cache of ``kv_lens`` tokens (the last ``append_lens[b]`` of each
+    request are the new ones) and the new rows to write."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    kv = make_paged_kv(rng, np.asarray(kv_lens), page_size, num_kv_heads, head_dim, dtype,
+                       extra_pages=extra_pages)
+    ai = np.zeros(len(append_lens) + 1, dtype=np.int32)
+    ai[1:] = np.cumsum(append_lens)
+    k_new = normal_bits(rng, (int(ai[-1]), num_kv_heads, head_dim), dtype)
+    v_new = normal_bits(rng, (int(ai[-1]), num_kv_heads, head_dim), dtype)
+    return PageAppendWorkload(name or f"page_append_s{seed}", seed, kv, ai, k_new, v_new)
+
+
+def ragged_page_append(seed: int = 1007, batch: int = 16) -> PageAppendWorkload:
+    """The new tokens of the ragged append shape: 16 requests, qo_len ~ U{128..1024}
+    new tokens after an existing kv_len ~ U{1024..8192}; GQA 32/8 (8 kv heads),
+    d 128, page 16, bf16."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    qo_len = rng.integers(128, 1024, size=batch, endpoint=True)
+    existing = rng.integers(1024, 8192, size=batch, endpoint=True)
+    return page_append(seed + 1, existing + qo_len, qo_len, 16, 8,
+                       name=f"page_append_{batch}req_new128-1024_kv1024-8192_hkv8_d128_bf16_p16")
+
+
+WORKLOADS_NEXT = {
+    "bsr_sparse": bsr_sparse,
+    "page_append": ragged_page_append,
+}

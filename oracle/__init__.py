@@ -5,13 +5,15 @@ leg may import this package. It shares no code with the HIP library: the
 attention oracle is the fp64 definition evaluated by walking the page table,
 and ``plan_ref`` is the reference of the work-unit planner.
 """
-from .attention import (append_workload, attend, cascade_decode, decode_workload, merge,
-                        paged_append, paged_decode, request_kv_len, rope_rotate, storage_to_f64,
+from .attention import (append_paged_kv, append_workload, attend, attend_masked, bsr_attention,
+                        bsr_mask, cascade_decode, decode_workload, merge, paged_append,
+                        paged_decode, request_kv_len, rope_inv_freq, rope_rotate, storage_to_f64,
                         walk_pages)
 from .plan_ref import KIND_APPEND, KIND_DECODE, PlanError, plan_ref
 
 __all__ = [
-    "append_workload", "attend", "cascade_decode", "decode_workload", "merge", "paged_append",
+    "append_paged_kv", "append_workload", "attend", "attend_masked", "bsr_attention", "bsr_mask",
+    "cascade_decode", "rope_inv_freq", "decode_workload", "merge", "paged_append",
     "paged_decode", "request_kv_len", "rope_rotate", "storage_to_f64", "walk_pages",
     "KIND_APPEND", "KIND_DECODE", "PlanError", "plan_ref",
 ]

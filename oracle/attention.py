@@ -89,16 +89,42 @@ def walk_pages(pages: np.ndarray, kv_indptr, kv_indices, kv_last_page_len, page_
 # ----------------------------------------------------------------------------
 # RoPE (LLaMA style, rotate-half)
 # ----------------------------------------------------------------------------
-def rope_inv_freq(head_dim: int, theta: float) -> np.ndarray:
-    """theta^(-2j/d) for j in [0, d/2), in float64."""
+def rope_inv_freq(head_dim: int, theta: float, llama31=None) -> np.ndarray:
+    """theta^(-2j/d) for j in [0, d/2), in float64.
+
+    ``llama31 = (factor, low_freq_factor, high_freq_factor, old_context_len)``
+    applies the LLaMA 3.1 frequency scaling (the README page lists LLaMA 3.1
+    RoPE among its operators, section 其他算子; the rule is the one published
+    with the LLaMA 3.1 models): with wavelength w = 2 pi / f, a frequency whose
+    wavelength is shorter than old_context_len / high_freq_factor is kept, one
+    whose wavelength is longer than old_context_len / low_freq_factor is divided
+    by factor, and in between the two are blended with weight
+    s = (old_context_len / w - low_freq_factor) / (high_freq_factor - low_freq_factor)
+    on the kept frequency: f' = (1 - s) f / factor + s f.
+    """
     j = np.arange(head_dim // 2, dtype=np.float64)
-    return np.power(float(theta), -2.0 * j / head_dim)
+    f = np.power(float(theta), -2.0 * j / head_dim)
+    if llama31 is None:
+        return f
+    factor, low, high, old = (float(x) for x in llama31)
+    out = np.empty_like(f)
+    for i, fi in enumerate(f):
+        w = 2.0 * math.pi / fi
+        if w < old / high:
+            out[i] = fi
+        elif w > old / low:
+            out[i] = fi / factor
+        else:
+            s = (old / w - low) / (high - low)
+            out[i] = (1.0 - s) * fi / factor + s * fi
+    return out
 
 
-def rope_rotate(x: np.ndarray, pos, theta: float) -> np.ndarray:
+def rope_rotate(x: np.ndarray, pos, theta: float, llama31=None) -> np.ndarray:
     """Rotate the last axis of ``x`` (length d) at position(s) ``pos``.
 
-    Pair (j, j + d/2) is turned by the angle pos * theta^(-2j/d):
+    Pair (j, j + d/2) is turned by the angle pos * f_j, f_j = theta^(-2j/d)
+    (optionally LLaMA 3.1 scaled, see ``rope_inv_freq``):
         x'_j       = x_j cos a - x_{j+d/2} sin a
         x'_{j+d/2} = x_{j+d/2} cos a + x_j sin a
     ``pos`` broadcasts against ``x.shape[:-1]``.
@@ -106,7 +132,7 @@ def rope_rotate(x: np.ndarray, pos, theta: float) -> np.ndarray:
     x = np.asarray(x, dtype=np.float64)
     d = x.shape[-1]
     h = d // 2
-    ang = np.asarray(pos, dtype=np.float64)[..., None] * rope_inv_freq(d, theta)
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * rope_inv_freq(d, theta, llama31)
     c, s = np.cos(ang), np.sin(ang)
     lo, hi = x[..., :h], x[..., h:]
     return np.concatenate([lo * c - hi * s, hi * c + lo * s], axis=-1)
@@ -183,7 +209,7 @@ def _group(num_qo_heads: int, num_kv_heads: int) -> int:
 def paged_decode(q, k_pages, v_pages, kv_indptr, kv_indices, kv_last_page_len, page_size: int,
                  dtype: str, num_kv_heads: int, sm_scale: Optional[float] = None,
                  rope_theta: float = 0.0, q_pos=None, kv_pos_offset=None,
-                 batch_ids: Optional[Iterable[int]] = None):
+                 batch_ids: Optional[Iterable[int]] = None, rope_llama31=None):
     """Decode attention: one query token per request against its paged KV.
 
     q ``[B, Hq, d]`` (storage bits); returns float64 ``o [B, Hq, d]``,
@@ -204,8 +230,8 @@ def paged_decode(q, k_pages, v_pages, kv_indptr, kv_indices, kv_last_page_len, p
         if rope_theta:
             qp = (kv_len - 1) if q_pos is None else int(q_pos[b])
             off = 0 if kv_pos_offset is None else int(kv_pos_offset[b])
-            qb = rope_rotate(qb, qp, rope_theta)
-            K = rope_rotate(K, (off + np.arange(kv_len))[:, None], rope_theta)
+            qb = rope_rotate(qb, qp, rope_theta, rope_llama31)
+            K = rope_rotate(K, (off + np.arange(kv_len))[:, None], rope_theta, rope_llama31)
         for h in range(num_kv_heads):
             ob, lb = attend(qb[h * G:(h + 1) * G], K[:, h], V[:, h], scale)
             o[b, h * G:(h + 1) * G] = ob
@@ -217,7 +243,7 @@ def paged_append(q, qo_indptr, k_pages, v_pages, kv_indptr, kv_indices, kv_last_
                  page_size: int, dtype: str, num_kv_heads: int, causal: bool = True,
                  sm_scale: Optional[float] = None, rope_theta: float = 0.0, q_pos=None,
                  kv_pos_offset=None, batch_ids: Optional[Iterable[int]] = None,
-                 token_ids: Optional[Iterable[int]] = None):
+                 token_ids: Optional[Iterable[int]] = None, rope_llama31=None):
     """Append / prefill attention for ragged queries ``q [sum qo, Hq, d]``.
 
     Query i (0-based within request b, qo_len_b queries) sees keys
@@ -249,8 +275,8 @@ def paged_append(q, qo_indptr, k_pages, v_pages, kv_indptr, kv_indices, kv_last_
         if rope_theta:
             qp = (kv_len - qo_len + ii) if q_pos is None else np.asarray(q_pos)[rows]
             off = 0 if kv_pos_offset is None else int(kv_pos_offset[b])
-            Q = rope_rotate(Q, np.asarray(qp)[:, None], rope_theta)
-            K = rope_rotate(K, (off + np.arange(kv_len))[:, None], rope_theta)
+            Q = rope_rotate(Q, np.asarray(qp)[:, None], rope_theta, rope_llama31)
+            K = rope_rotate(K, (off + np.arange(kv_len))[:, None], rope_theta, rope_llama31)
         vis = (kv_len - qo_len + ii + 1) if causal else np.full(len(rows), kv_len)
         for hq in range(Hq):
             h = hq // G
@@ -264,7 +290,8 @@ def cascade_decode(q, prefix_k, prefix_v, prefix_indptr, prefix_indices, prefix_
                    prefix_page_size: int, k_pages, v_pages, kv_indptr, kv_indices,
                    kv_last_page_len, page_size: int, dtype: str, num_kv_heads: int,
                    sm_scale: Optional[float] = None, rope_theta: float = 0.0, q_pos=None,
-                   kv_pos_offset=None, batch_ids: Optional[Iterable[int]] = None):
+                   kv_pos_offset=None, batch_ids: Optional[Iterable[int]] = None,
+                   rope_llama31=None):
     """Decode over a shared prefix (one BSR row in large pages) plus per-request
     suffixes (small pages), combined through their attention states.
 
@@ -290,11 +317,13 @@ def cascade_decode(q, prefix_k, prefix_v, prefix_indptr, prefix_indices, prefix_
     rep_lpl = np.full(B, int(prefix_last_page_len[0]))
     o_p, l_p = paged_decode(q, prefix_k, prefix_v, rep_indptr, rep_indices, rep_lpl,
                             prefix_page_size, dtype, num_kv_heads, sm_scale, rope_theta,
-                            q_pos=q_pos, kv_pos_offset=np.zeros(B, np.int64), batch_ids=batch_ids)
+                            q_pos=q_pos, kv_pos_offset=np.zeros(B, np.int64), batch_ids=batch_ids,
+                            rope_llama31=rope_llama31)
     # suffix level
     o_s, l_s = paged_decode(q, k_pages, v_pages, kv_indptr, kv_indices, kv_last_page_len,
                             page_size, dtype, num_kv_heads, sm_scale, rope_theta, q_pos=q_pos,
-                            kv_pos_offset=kv_pos_offset, batch_ids=batch_ids)
+                            kv_pos_offset=kv_pos_offset, batch_ids=batch_ids,
+                            rope_llama31=rope_llama31)
     ids = list(range(B) if batch_ids is None else batch_ids)
     o = np.full(q.shape, np.nan)
     lse = np.full(q.shape[:2], np.nan)
@@ -311,10 +340,11 @@ def decode_workload(w, batch_ids=None):
                               p.kv_last_page_len, p.page_size, kv.k_pages, kv.v_pages,
                               kv.kv_indptr, kv.kv_indices, kv.kv_last_page_len, kv.page_size,
                               w.dtype, w.num_kv_heads, w.sm_scale, w.rope_theta, w.q_pos,
-                              w.kv_pos_offset, batch_ids)
+                              w.kv_pos_offset, batch_ids, rope_llama31=w.rope_llama31)
     return paged_decode(w.q, kv.k_pages, kv.v_pages, kv.kv_indptr, kv.kv_indices,
                         kv.kv_last_page_len, kv.page_size, w.dtype, w.num_kv_heads, w.sm_scale,
-                        w.rope_theta, w.q_pos, w.kv_pos_offset, batch_ids)
+                        w.rope_theta, w.q_pos, w.kv_pos_offset, batch_ids,
+                        rope_llama31=w.rope_llama31)
 
 
 def append_workload(w, batch_ids=None, token_ids=None):
@@ -322,4 +352,107 @@ def append_workload(w, batch_ids=None, token_ids=None):
     kv = w.kv
     return paged_append(w.q, w.qo_indptr, kv.k_pages, kv.v_pages, kv.kv_indptr, kv.kv_indices,
                         kv.kv_last_page_len, kv.page_size, w.dtype, w.num_kv_heads, w.causal,
-                        w.sm_scale, w.rope_theta, w.q_pos, w.kv_pos_offset, batch_ids, token_ids)
+                        w.sm_scale, w.rope_theta, w.q_pos, w.kv_pos_offset, batch_ids, token_ids,
+                        rope_llama31=w.rope_llama31)
+
+
+# ----------------------------------------------------------------------------
+# block-sparse attention (a BSR mask over a dense K/V)
+# ----------------------------------------------------------------------------
+def bsr_mask(M: int, N: int, R: int, C: int, indptr, indices) -> np.ndarray:
+    """Dense boolean mask ``[M, N]`` of a block-sparse-row pattern.
+
+    Row block i (queries i*R .. min((i+1)*R, M) - 1) lists its column blocks in
+    ``indices[indptr[i]:indptr[i+1]]``; column block j covers keys j*C ..
+    (j+1)*C - 1. Query r may see key t exactly when the block (r // R, t // C)
+    is listed. This is the block-sparse attention of the README page (section
+    核心功能, 稀疏注意力机制) on the BSR format of the paper summary (section
+    统一的 KV 缓存存储格式).
+    """
+    mask = np.zeros((M, N), dtype=bool)
+    nrb = -(-M // R) if M else 0
+    for i in range(nrb):
+        r0, r1 = i * R, min((i + 1) * R, M)
+        for j in indices[int(indptr[i]):int(indptr[i + 1])]:
+            j = int(j)
+            mask[r0:r1, j * C:(j + 1) * C] = True
+    return mask
+
+
+def attend_masked(qrows: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,
+                  mask: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Softmax attention of ``qrows [r, d]`` over the keys ``mask[i]`` lets row i
+    see (``mask [r, n]`` boolean). A row with no visible key gives o = 0, lse = -inf."""
+    qrows = np.asarray(qrows, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    r = qrows.shape[0]
+    o = np.zeros((r, V.shape[1]), dtype=np.float64)
+    lse = np.full(r, NEG_INF, dtype=np.float64)
+    has = mask.any(axis=1)
+    if r == 0 or not has.any():
+        return o, lse
+    s = np.where(mask, scale * (qrows @ K.T), NEG_INF)[has]
+    m = s.max(axis=1, keepdims=True)
+    lse_h = m[:, 0] + np.log(np.exp(s - m).sum(axis=1))
+    o[has] = np.exp(s - lse_h[:, None]) @ V
+    lse[has] = lse_h
+    return o, lse
+
+
+def bsr_attention(q, k, v, R: int, C: int, indptr, indices, dtype: str, num_kv_heads: int,
+                  sm_scale: Optional[float] = None, rows: Optional[Iterable[int]] = None):
+    """Block-sparse attention: q ``[M, Hq, d]``, k / v ``[N, Hkv, d]`` (storage
+    bits), mask from ``bsr_mask``. Returns float64 ``o [M, Hq, d]``, ``lse [M, Hq]``;
+    rows not in ``rows`` (query indices) are NaN."""
+    M, Hq, d = q.shape
+    N = k.shape[0]
+    G = _group(Hq, num_kv_heads)
+    scale = (1.0 / math.sqrt(d)) if not sm_scale or sm_scale <= 0 else float(sm_scale)
+    ids = np.arange(M) if rows is None else np.asarray(sorted(set(int(r) for r in rows)))
+    o = np.full((M, Hq, d), np.nan)
+    lse = np.full((M, Hq), np.nan)
+    if len(ids) == 0:
+        return o, lse
+    mask = bsr_mask(M, N, R, C, indptr, indices)[ids]
+    K = storage_to_f64(k, dtype)
+    V = storage_to_f64(v, dtype)
+    Q = storage_to_f64(q[ids], dtype)
+    for hq in range(Hq):
+        h = hq // G
+        ob, lb = attend_masked(Q[:, hq], K[:, h], V[:, h], scale, mask)
+        o[ids, hq] = ob
+        lse[ids, hq] = lb
+    return o, lse
+
+
+# ----------------------------------------------------------------------------
+# appending new tokens to a paged cache
+# ----------------------------------------------------------------------------
+def append_paged_kv(k_new, v_new, append_indptr, k_pages, v_pages, kv_indptr, kv_indices,
+                    kv_last_page_len, page_size: int):
+    """Write new K/V rows into copies of the page pools and return them.
+
+    The page table already covers the new tokens (they are the last ones of
+    each request): new row i of request b (rows append_indptr[b] ..
+    append_indptr[b+1] - 1) is logical token kv_len_b - append_len_b + i, which
+    lives in slot (t % page_size) of page kv_indices[kv_indptr[b] + t // page_size].
+    This is the step that fills the paged cache before decode / append read it
+    (README page, section 核心功能: paged KV caches for dynamic batching).
+    Rows whose position would fall outside [0, kv_len_b) are not written.
+    """
+    kp = np.array(k_pages, copy=True)
+    vp = np.array(v_pages, copy=True)
+    B = len(append_indptr) - 1
+    for b in range(B):
+        a0, a1 = int(append_indptr[b]), int(append_indptr[b + 1])
+        n = a1 - a0
+        kv_len = request_kv_len(kv_indptr, kv_last_page_len, page_size, b)
+        for i in range(n):
+            t = kv_len - n + i
+            if t < 0 or t >= kv_len:
+                continue
+            page = int(kv_indices[int(kv_indptr[b]) + t // page_size])
+            kp[page, t % page_size] = k_new[a0 + i]
+            vp[page, t % page_size] = v_new[a0 + i]
+    return kp, vp
