@@ -24,9 +24,10 @@ import numpy as np
 __all__ = [
     "ABP_OK", "ABP_ERR_INVALID_ARG", "ABP_ERR_UNSUPPORTED", "ABP_ERR_WORKSPACE_TOO_SMALL",
     "ABP_ERR_PLAN_MISMATCH", "ABP_ERR_HIP", "ABP_F16", "ABP_BF16", "ABP_F32",
-    "ABP_KIND_DECODE", "ABP_KIND_APPEND", "AbpParams", "AbpPlan", "AbpError", "load_library",
-    "library_path", "make_params", "BatchDecode", "BatchAppend", "merge_state", "merge_states",
-    "single_decode_with_kv_cache", "CascadeDecode", "EXPORTED_SYMBOLS",
+    "ABP_KIND_DECODE", "ABP_KIND_APPEND", "ABP_KIND_BSR", "AbpParams", "AbpPlan", "AbpError",
+    "load_library", "library_path", "make_params", "BatchDecode", "BatchAppend", "merge_state",
+    "merge_states", "single_decode_with_kv_cache", "CascadeDecode", "BlockSparseAttention",
+    "append_paged_kv_cache", "LLAMA31_ROPE", "EXPORTED_SYMBOLS",
 ]
 
 ABP_OK = 0
@@ -37,7 +38,11 @@ ABP_ERR_PLAN_MISMATCH = -4
 ABP_ERR_HIP = -5
 
 ABP_F16, ABP_BF16, ABP_F32 = 0, 1, 2
-ABP_KIND_DECODE, ABP_KIND_APPEND = 0, 1
+ABP_KIND_DECODE, ABP_KIND_APPEND, ABP_KIND_BSR = 0, 1, 2
+
+# LLaMA 3.1 RoPE frequency scaling: (factor, low_freq_factor, high_freq_factor,
+# old_context_len) as published with those models
+LLAMA31_ROPE = (8.0, 1.0, 4.0, 8192.0)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -58,6 +63,10 @@ class AbpParams(ctypes.Structure):
         ("causal", ctypes.c_int32),
         ("rope", ctypes.c_int32),
         ("rope_theta", ctypes.c_float),
+        ("rope_factor", ctypes.c_float),
+        ("rope_low_freq_factor", ctypes.c_float),
+        ("rope_high_freq_factor", ctypes.c_float),
+        ("rope_old_context_len", ctypes.c_float),
     ]
 
 
@@ -116,6 +125,11 @@ _SIGNATURES = {
                                _vp, _planp]),
     "abp_append_run": (_int, [_planp, _pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                               _vp, _vp, _sz, _vp]),
+    "abp_bsr_plan_host": (_int, [_pp, _i32, _i32, _i32, _vp, _i32, _i32, _i32, _vp, _sz, _planp]),
+    "abp_bsr_plan": (_int, [_pp, _i32, _i32, _i32, _vp, _i32, _i32, _i32, _vp, _sz, _vp, _sz, _vp,
+                            _planp]),
+    "abp_bsr_run": (_int, [_planp, _pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "abp_append_paged_kv": (_int, [_pp, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "abp_merge_state": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _int, _int, _vp]),
     "abp_merge_states": (_int, [_vp, _vp, _i32, _i64, _i32, _int, _int, _vp, _vp, _vp]),
 }
@@ -188,6 +202,18 @@ def abp_plan_host(kind: int, params: AbpParams, batch: int, qo_indptr, kv_indptr
     return plan
 
 
+def abp_bsr_plan_host(params: AbpParams, M: int, N: int, R: int, indptr, max_row_blocks: int,
+                      max_M: int, num_workers: int, host_ws: np.ndarray) -> AbpPlan:
+    """Host-only block-sparse planner into a numpy buffer (for inspection and tests)."""
+    plan = AbpPlan()
+    ip = np.ascontiguousarray(indptr, dtype=np.int32)
+    _check(load_library().abp_bsr_plan_host(ctypes.byref(params), M, N, R, ip.ctypes.data,
+                                            max_row_blocks, max_M, num_workers,
+                                            host_ws.ctypes.data, host_ws.nbytes,
+                                            ctypes.byref(plan)))
+    return plan
+
+
 def decode_plan_arrays(blob: np.ndarray, plan: AbpPlan):
     """Read the plan arrays back out of a plan blob (int32 view), for inspection."""
     b = blob.view(np.int32)
@@ -196,7 +222,7 @@ def decode_plan_arrays(blob: np.ndarray, plan: AbpPlan):
          "NUM_MERGES", "TILE_Q", "TILE_KV", "ROWS", "GROUP", "NUM_KV_HEADS", "PAGE_SIZE",
          "NUM_BLOCKS", "QUOTA", "OFF_WSEG", "OFF_SEG", "OFF_TILE", "OFF_MERGE", "OFF_ROPE",
          "MAX_TILES", "MAX_SEGS", "MAX_PARTIALS", "CAUSAL", "OFF_CNT", "OFF_NTILE",
-         "MERGE_KERNEL", "TILE_HEADS"])}
+         "MERGE_KERNEL", "TILE_HEADS", "OFF_AUX"])}
     W, T, S, M = b[H["WORKERS"]], b[H["NUM_TILES"]], b[H["NUM_SEGS"]], b[H["NUM_MERGES"]]
     seg = b[b[H["OFF_SEG"]]: b[H["OFF_SEG"]] + 4 * S].reshape(S, 4)
     tile = b[b[H["OFF_TILE"]]: b[H["OFF_TILE"]] + 4 * T].reshape(T, 4)
@@ -214,6 +240,8 @@ def decode_plan_arrays(blob: np.ndarray, plan: AbpPlan):
         "merge_list": mrg[:, 0].copy(),
         "merge_kernel": b[H["MERGE_KERNEL"]: H["MERGE_KERNEL"] + 1].copy(),
         "tile_heads": b[H["TILE_HEADS"]: H["TILE_HEADS"] + 1].copy(),
+        "rope": blob.view(np.float32)[b[H["OFF_ROPE"]]: b[H["OFF_ROPE"]] + 128].copy(),
+        "off_aux": int(b[H["OFF_AUX"]]),
     }
 
 
@@ -243,12 +271,16 @@ def _torch_dtype(code: int):
 
 def make_params(num_qo_heads: int, num_kv_heads: int, head_dim: int, page_size: int, dtype,
                 out_dtype=None, sm_scale: float = 0.0, causal: bool = False,
-                rope_theta: float = 0.0) -> AbpParams:
-    """abp_params; ``rope_theta`` > 0 turns on the fused LLaMA RoPE."""
+                rope_theta: float = 0.0, rope_llama31=None) -> AbpParams:
+    """abp_params; ``rope_theta`` > 0 turns on the fused LLaMA RoPE, and
+    ``rope_llama31 = (factor, low_freq_factor, high_freq_factor, old_context_len)``
+    (e.g. ``LLAMA31_ROPE``) its LLaMA 3.1 frequency scaling."""
     q = _dtype_code(dtype)
     o = q if out_dtype is None else _dtype_code(out_dtype)
+    rope = 0 if rope_theta <= 0 else (2 if rope_llama31 is not None else 1)
+    l31 = tuple(float(x) for x in rope_llama31) if rope_llama31 is not None else (0.0,) * 4
     return AbpParams(num_qo_heads, num_kv_heads, head_dim, page_size, q, o, float(sm_scale),
-                     int(bool(causal)), int(rope_theta > 0), float(rope_theta))
+                     int(bool(causal)), rope, float(rope_theta), *l31)
 
 
 def _ptr(t) -> Optional[int]:
@@ -482,3 +514,79 @@ class CascadeDecode:
         B, H, d = q.shape
         mk = lambda *s: torch.empty(s, dtype=torch.float32, device=q.device)
         return mk(B, H, d), mk(B, H), mk(B, H, d), mk(B, H)
+
+
+class BlockSparseAttention:
+    """Attention under a block-sparse-row mask over a dense K/V.
+
+    Row block i (queries i*R .. (i+1)*R - 1) sees the column blocks
+    ``indices[indptr[i]:indptr[i+1]]`` of C keys each (C = ``params.page_size``).
+    The planner turns each row block into an append request whose pages are its
+    column blocks, so the run is the MFMA append kernel (``abp_bsr_*``).
+    """
+
+    def __init__(self, params: AbpParams, max_row_blocks: int, max_M: int, num_workers: int = 0,
+                 device=None):
+        torch = _torch()
+        self.params = params
+        self.max_row_blocks = int(max_row_blocks)
+        self.max_M = int(max_M)
+        self.device = torch.device("cuda", torch.cuda.current_device()) if device is None \
+            else torch.device(device)
+        with torch.cuda.device(self.device):
+            hb, db = abp_workspace_size(ABP_KIND_BSR, params, self.max_row_blocks, self.max_M,
+                                        num_workers)
+            self.num_workers = int(num_workers)
+            self.host_ws = torch.empty(max(hb, 16), dtype=torch.uint8, pin_memory=True)
+            self.dev_ws = torch.empty(max(db, 256), dtype=torch.uint8, device=self.device)
+        self.plan_struct = None
+        self._upload_done = None
+
+    def plan(self, M: int, N: int, R: int, indptr, stream=None) -> AbpPlan:
+        torch = _torch()
+        ip = _i32_host(indptr)
+        if self._upload_done is not None:
+            self._upload_done.synchronize()
+        plan = AbpPlan()
+        _check(load_library().abp_bsr_plan(
+            ctypes.byref(self.params), int(M), int(N), int(R), ip.ctypes.data,
+            self.max_row_blocks, self.max_M, self.num_workers, self.host_ws.data_ptr(),
+            self.host_ws.numel(), self.dev_ws.data_ptr(), self.dev_ws.numel(), _stream(stream),
+            ctypes.byref(plan)))
+        ev = torch.cuda.Event()
+        ev.record(stream if stream is not None else torch.cuda.current_stream(self.device))
+        self._upload_done = ev
+        self.plan_struct = plan
+        return plan
+
+    def run(self, q, k, v, indptr, indices, o=None, lse=None, stream=None,
+            return_lse: bool = True):
+        """q [M, Hq, d], k / v [N, Hkv, d]; indptr / indices on the device."""
+        torch = _torch()
+        if self.plan_struct is None:
+            raise RuntimeError("plan() must be called before run()")
+        if o is None:
+            o = torch.empty(q.shape, dtype=_torch_dtype(self.params.out_dtype), device=q.device)
+        if lse is None and return_lse:
+            lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+        _check(load_library().abp_bsr_run(
+            ctypes.byref(self.plan_struct), ctypes.byref(self.params), _ptr(q), _ptr(k), _ptr(v),
+            _ptr(indptr), _ptr(indices), _ptr(o), _ptr(lse), self.dev_ws.data_ptr(),
+            self.dev_ws.numel(), _stream(stream)))
+        return o, lse
+
+
+def append_paged_kv_cache(k_new, v_new, append_indptr, k_pages, v_pages, kv_indptr, kv_indices,
+                          kv_last_page_len, nnz: Optional[int] = None, stream=None) -> None:
+    """Write new rows ``k_new / v_new [nnz, Hkv, d]`` (ragged by ``append_indptr``,
+    device int32) into the pages, at the last positions of each request of the
+    page table (which must already cover them). ``nnz`` defaults to
+    ``k_new.shape[0]``."""
+    num_pages, page_size, hkv, d = k_pages.shape
+    params = make_params(hkv, hkv, d, page_size, k_pages.dtype)
+    batch = append_indptr.shape[0] - 1
+    n = int(k_new.shape[0] if nnz is None else nnz)
+    _check(load_library().abp_append_paged_kv(
+        ctypes.byref(params), batch, n, _ptr(k_new), _ptr(v_new), _ptr(append_indptr),
+        _ptr(k_pages), _ptr(v_pages), _ptr(kv_indptr), _ptr(kv_indices), _ptr(kv_last_page_len),
+        _stream(stream)))

@@ -22,7 +22,8 @@ LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libabp.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "plan.cpp", "merge.hip", "decode.hip", "append.hip", "upload.hip"]
+SOURCES = ["api.cpp", "plan.cpp", "merge.hip", "decode.hip", "append.hip", "upload.hip",
+           "page_append.hip"]
 
 COMMON = [
     "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

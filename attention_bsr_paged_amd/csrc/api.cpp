@@ -206,6 +206,8 @@ int abp_plan_host(int kind, const abp_params* params, int32_t batch, const int32
                   size_t host_bytes, abp_plan* plan) {
   try {
     if (num_workers <= 0) return fail(ABP_ERR_INVALID_ARG, "abp_plan_host needs num_workers > 0");
+    if (kind == ABP_KIND_BSR)
+      return fail(ABP_ERR_INVALID_ARG, "block-sparse plans are made by abp_bsr_plan_host");
     return do_plan(kind, params, batch, qo_indptr_h, kv_indptr_h, kv_last_page_len_h, max_batch,
                    max_qo_tokens, num_workers, host_ws, host_bytes, plan, nullptr, nullptr);
   } catch (...) {
@@ -226,6 +228,34 @@ static bool mapped_pinned(const void* p, uint64_t bytes) {
   return attr.type == hipMemoryTypeHost && !attr.isManaged && attr.devicePointer == p;
 }
 
+// Block-sparse plan on the host: the BSR pattern becomes append requests (one
+// per row block) whose query ranges and page counts the planner writes into
+// the blob's aux region.
+static int do_bsr_plan(const abp_params* params, int32_t M, int32_t N, int32_t R,
+                       const int32_t* indptr_h, int32_t max_rb, int32_t max_M, int32_t workers,
+                       void* host_ws, size_t host_bytes, abp_plan* plan, abp::Layout* lay_out) {
+  if (!plan) return fail(ABP_ERR_INVALID_ARG, "plan is NULL");
+  if (!host_ws) return fail(ABP_ERR_INVALID_ARG, "host workspace is NULL");
+  if (M > max_M) return fail(ABP_ERR_WORKSPACE_TOO_SMALL, "M > max_M");
+  if (R >= 1 && M >= 0 && (int64_t(M) + R - 1) / R > max_rb)
+    return fail(ABP_ERR_WORKSPACE_TOO_SMALL, "ceil(M / R) > max_row_blocks");
+  abp::Config cfg;
+  abp::Layout L;
+  int st = resolve_layout(ABP_KIND_BSR, params, max_rb, max_M, workers, &cfg, &L);
+  if (st != ABP_OK) return st;
+  if (host_bytes < L.plan_bytes)
+    return fail(ABP_ERR_WORKSPACE_TOO_SMALL, "host workspace smaller than abp_workspace_size");
+  std::string err;
+  st = abp::bsr_plan_compute(cfg, L, M, N, R, indptr_h, static_cast<int32_t*>(host_ws), plan,
+                             &err);
+  if (st != ABP_OK) return fail(st, err);
+  if (lay_out) *lay_out = L;
+  return ABP_OK;
+}
+
+static int upload_plan(const abp::Layout& L, void* host_ws, void* dev_ws, size_t dev_bytes,
+                       abp_stream_t stream, abp_plan* plan);
+
 static int plan_and_upload(int kind, const abp_params* params, int32_t batch,
                            const int32_t* qo_indptr_h, const int32_t* kv_indptr_h,
                            const int32_t* lpl_h, int32_t max_batch, int32_t max_qo,
@@ -236,6 +266,12 @@ static int plan_and_upload(int kind, const abp_params* params, int32_t batch,
   int st = do_plan(kind, params, batch, qo_indptr_h, kv_indptr_h, lpl_h, max_batch, max_qo,
                    workers, host_ws, host_bytes, plan, &cfg, &L);
   if (st != ABP_OK) return st;
+  return upload_plan(L, host_ws, dev_ws, dev_bytes, stream, plan);
+}
+
+// Copy the plan blob to the start of dev_ws on `stream`.
+static int upload_plan(const abp::Layout& L, void* host_ws, void* dev_ws, size_t dev_bytes,
+                       abp_stream_t stream, abp_plan* plan) {
   if (!dev_ws) return fail(ABP_ERR_INVALID_ARG, "device workspace is NULL");
   if (dev_bytes < L.dev_bytes)
     return fail(ABP_ERR_WORKSPACE_TOO_SMALL, "device workspace smaller than abp_workspace_size");
@@ -358,6 +394,101 @@ int abp_append_run(const abp_plan* plan, const abp_params* params, const void* q
     // not depend on the plan)
     e = abp::launch_plan_merge(cfg, a, plan->num_workers, s);
     if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+    return ABP_OK;
+  } catch (...) {
+    return fail(ABP_ERR_HIP, "exception");
+  }
+}
+
+int abp_bsr_plan_host(const abp_params* params, int32_t M, int32_t N, int32_t R,
+                      const int32_t* indptr_h, int32_t max_row_blocks, int32_t max_M,
+                      int32_t num_workers, void* host_ws, size_t host_bytes, abp_plan* plan) {
+  try {
+    if (num_workers <= 0)
+      return fail(ABP_ERR_INVALID_ARG, "abp_bsr_plan_host needs num_workers > 0");
+    return do_bsr_plan(params, M, N, R, indptr_h, max_row_blocks, max_M, num_workers, host_ws,
+                       host_bytes, plan, nullptr);
+  } catch (...) {
+    return fail(ABP_ERR_INVALID_ARG, "exception");
+  }
+}
+
+int abp_bsr_plan(const abp_params* params, int32_t M, int32_t N, int32_t R,
+                 const int32_t* indptr_h, int32_t max_row_blocks, int32_t max_M,
+                 int32_t num_workers, void* host_ws, size_t host_bytes, void* dev_ws,
+                 size_t dev_bytes, abp_stream_t stream, abp_plan* plan) {
+  try {
+    abp::Layout L;
+    int st = do_bsr_plan(params, M, N, R, indptr_h, max_row_blocks, max_M, num_workers, host_ws,
+                         host_bytes, plan, &L);
+    if (st != ABP_OK) return st;
+    return upload_plan(L, host_ws, dev_ws, dev_bytes, stream, plan);
+  } catch (...) {
+    return fail(ABP_ERR_INVALID_ARG, "exception");
+  }
+}
+
+int abp_bsr_run(const abp_plan* plan, const abp_params* params, const void* q, const void* k,
+                const void* v, const int32_t* indptr_d, const int32_t* indices_d, void* o,
+                float* lse, void* dev_ws, size_t dev_bytes, abp_stream_t stream) {
+  try {
+    abp::Config cfg;
+    abp::Layout L;
+    int st = prepare_run(ABP_KIND_BSR, plan, params, dev_ws, dev_bytes, &cfg, &L);
+    if (st != ABP_OK) return st;
+    if (plan->num_tiles > 0 && (!q || !k || !v || !indptr_d || !indices_d || !o))
+      return fail(ABP_ERR_INVALID_ARG, "NULL tensor pointer");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+      return fail(ABP_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+    // row block i is append request i; its query range and page count come
+    // from the aux region the planner filled (k / v viewed as [N / C, C, Hkv, d])
+    const int32_t* aux = reinterpret_cast<const int32_t*>(dev_ws) + L.off_aux;
+    abp::AttnArgs a = {};
+    a.q = q;
+    a.k_pages = k;
+    a.v_pages = v;
+    a.qo_indptr = aux;
+    a.kv_indptr = indptr_d;
+    a.kv_indices = indices_d;
+    a.kv_last_page_len = aux + ((int64_t(L.aux_cap) + 1 + 3) & ~int64_t(3));
+    a.o = o;
+    a.lse = lse;
+    fill_args(cfg, L, plan, dev_ws, &a);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = abp::launch_append(cfg, a, s);
+    if (e != hipSuccess) return hip_fail(e, "append kernel launch (block-sparse)");
+    e = abp::launch_plan_merge(cfg, a, plan->num_workers, s);
+    if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+    return ABP_OK;
+  } catch (...) {
+    return fail(ABP_ERR_HIP, "exception");
+  }
+}
+
+int abp_append_paged_kv(const abp_params* params, int32_t batch, int64_t nnz, const void* k_new,
+                        const void* v_new, const int32_t* append_indptr_d, void* k_pages,
+                        void* v_pages, const int32_t* kv_indptr_d, const int32_t* kv_indices_d,
+                        const int32_t* kv_last_page_len_d, abp_stream_t stream) {
+  try {
+    if (!params) return fail(ABP_ERR_INVALID_ARG, "params is NULL");
+    if (params->head_dim != 128) return fail(ABP_ERR_UNSUPPORTED, "only head_dim 128 is built");
+    if (params->num_kv_heads < 1 || params->page_size < 1)
+      return fail(ABP_ERR_INVALID_ARG, "num_kv_heads and page_size must be >= 1");
+    if (params->qkv_dtype != ABP_F16 && params->qkv_dtype != ABP_BF16)
+      return fail(ABP_ERR_UNSUPPORTED, "qkv_dtype must be ABP_F16 or ABP_BF16");
+    if (batch < 0 || nnz < 0) return fail(ABP_ERR_INVALID_ARG, "batch and nnz must be >= 0");
+    if (nnz == 0 || batch == 0) return ABP_OK;
+    if (nnz > (int64_t(1) << 31) - 1) return fail(ABP_ERR_INVALID_ARG, "nnz must be < 2^31");
+    if (!k_new || !v_new || !append_indptr_d || !k_pages || !v_pages || !kv_indptr_d ||
+        !kv_indices_d || !kv_last_page_len_d)
+      return fail(ABP_ERR_INVALID_ARG, "NULL pointer");
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pages) || !aligned16(v_pages))
+      return fail(ABP_ERR_INVALID_ARG, "K/V pointers must be 16-byte aligned");
+    hipError_t e = abp::launch_page_append(
+        k_new, v_new, append_indptr_d, k_pages, v_pages, kv_indptr_d, kv_indices_d,
+        kv_last_page_len_d, batch, nnz, params->num_kv_heads, params->page_size,
+        reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "page append launch");
     return ABP_OK;
   } catch (...) {
     return fail(ABP_ERR_HIP, "exception");

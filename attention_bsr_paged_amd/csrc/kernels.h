@@ -49,6 +49,14 @@ hipError_t launch_upload(void* dev_dst, const void* host_src_mapped, size_t byte
 hipError_t launch_plan_merge(const Config& cfg, const AttnArgs& a, int32_t grid,
                              hipStream_t stream);
 
+// writes nnz new K/V rows [nnz, hkv, 128] into the pages at the last
+// positions of their requests (rows outside a request are skipped)
+hipError_t launch_page_append(const void* k_new, const void* v_new, const int32_t* append_indptr,
+                              void* k_pages, void* v_pages, const int32_t* kv_indptr,
+                              const int32_t* kv_indices, const int32_t* kv_last_page_len,
+                              int32_t batch, int64_t nnz, int32_t hkv, int32_t page_size,
+                              hipStream_t stream);
+
 hipError_t launch_merge_two(const void* o_a, const float* lse_a, const void* o_b,
                             const float* lse_b, void* o_out, float* lse_out, int64_t rows,
                             int in_dtype, int out_dtype, hipStream_t stream);

@@ -41,6 +41,7 @@ enum Header : int {
   H_MERGE_KERNEL,  // 1: split tiles are merged by the merge kernel after the
                    // main kernel; 0: by the last arriving workgroup (append)
   H_TILE_HEADS,    // consecutive kv heads per tile
+  H_OFF_AUX,       // block-sparse plans: derived qo_indptr then kv_last_page_len
   HEADER_INTS = 32
 };
 
@@ -55,8 +56,12 @@ constexpr int kMaxRopePairs = 64;        // head_dim 128
 //   cnt   int32 x 1 per tile: segments of a split tile that have written their
 //         partial; the last one merges the tile and resets it to 0
 // worker_seg_indptr has num_workers + 1 entries.
-// rope: kMaxRopePairs x {hi, lo} float32 bit patterns of theta^(-2j/d) / (2 pi)
-//       (revolutions per position), split so hi + lo carries ~48 bits.
+// rope: kMaxRopePairs x {hi, lo} float32 bit patterns of f_j / (2 pi)
+//       (revolutions per position; f_j = theta^(-2j/d), LLaMA 3.1-scaled when
+//       asked), split so hi + lo carries ~48 bits.
+// aux (block-sparse plans only, at the end): int32 qo_indptr [aux_cap + 1]
+//       then kv_last_page_len [aux_cap], aux_cap = max_tiles / num_kv_heads
+//       (every row block has at least one tile per kv head).
 
 struct Layout {
   int32_t workers = 0;
@@ -70,6 +75,8 @@ struct Layout {
   int32_t tile_heads = 1;
   int64_t off_wseg = 0, off_seg = 0, off_tile = 0, off_ntile = 0, off_merge = 0, off_rope = 0,
           off_cnt = 0;
+  int64_t off_aux = 0;         // == plan_ints when there is no aux region
+  int32_t aux_cap = 0;         // row blocks the aux region holds
   int64_t plan_ints = 0;       // total int32 of the blob
   uint64_t plan_bytes = 0;
   uint64_t partial_offset = 0; // bytes, 256-aligned

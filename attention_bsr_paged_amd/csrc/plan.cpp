@@ -42,8 +42,8 @@ int check_params(int kind, const abp_params* p, Config* cfg, std::string* err) {
     *err = "params is NULL";
     return ABP_ERR_INVALID_ARG;
   }
-  if (kind != ABP_KIND_DECODE && kind != ABP_KIND_APPEND) {
-    *err = "kind must be ABP_KIND_DECODE or ABP_KIND_APPEND";
+  if (kind != ABP_KIND_DECODE && kind != ABP_KIND_APPEND && kind != ABP_KIND_BSR) {
+    *err = "kind must be ABP_KIND_DECODE, ABP_KIND_APPEND or ABP_KIND_BSR";
     return ABP_ERR_INVALID_ARG;
   }
   if (p->num_qo_heads < 1 || p->num_kv_heads < 1) {
@@ -75,17 +75,28 @@ int check_params(int kind, const abp_params* p, Config* cfg, std::string* err) {
     *err = "out_dtype must be ABP_F16, ABP_BF16 or ABP_F32";
     return ABP_ERR_UNSUPPORTED;
   }
-  if (p->rope != 0 && p->rope != 1) {
-    *err = "rope must be 0 or 1";
+  if (p->rope < 0 || p->rope > 2) {
+    *err = "rope must be 0, 1 or 2";
     return ABP_ERR_INVALID_ARG;
   }
-  if (p->rope == 1 && !(p->rope_theta > 1.f)) {
+  if (p->rope != 0 && !(p->rope_theta > 1.f)) {
     *err = "rope_theta must be > 1";
+    return ABP_ERR_INVALID_ARG;
+  }
+  if (p->rope == 2 && !(p->rope_factor > 0.f && p->rope_low_freq_factor > 0.f &&
+                        p->rope_high_freq_factor > p->rope_low_freq_factor &&
+                        p->rope_old_context_len > 0.f)) {
+    *err = "LLaMA 3.1 RoPE needs factor > 0, low_freq_factor > 0, high_freq_factor > "
+           "low_freq_factor and old_context_len > 0";
     return ABP_ERR_INVALID_ARG;
   }
   if (p->causal != 0 && p->causal != 1) {
     *err = "causal must be 0 or 1";
     return ABP_ERR_INVALID_ARG;
+  }
+  if (kind == ABP_KIND_BSR && (p->causal != 0 || p->rope != 0)) {
+    *err = "block-sparse attention takes its mask from the BSR pattern: causal and rope must be 0";
+    return ABP_ERR_UNSUPPORTED;
   }
   cfg->kind = kind;
   cfg->hq = p->num_qo_heads;
@@ -99,6 +110,12 @@ int check_params(int kind, const abp_params* p, Config* cfg, std::string* err) {
   cfg->causal = kind == ABP_KIND_APPEND ? p->causal : 0;
   cfg->rope = p->rope;
   cfg->rope_theta = p->rope_theta;
+  if (p->rope == 2) {
+    cfg->rope_factor = p->rope_factor;
+    cfg->rope_low = p->rope_low_freq_factor;
+    cfg->rope_high = p->rope_high_freq_factor;
+    cfg->rope_old_ctx = p->rope_old_context_len;
+  }
   return ABP_OK;
 }
 
@@ -147,6 +164,11 @@ int make_layout_caps(const Config& cfg, int64_t max_tiles, int32_t workers, Layo
   off += 2 * kMaxRopePairs;
   L.off_cnt = off;
   off += align4(max_tiles);
+  L.off_aux = off;
+  if (cfg.kind == ABP_KIND_BSR) {
+    L.aux_cap = (int32_t)(max_tiles / cfg.hkv);
+    off += align4(int64_t(L.aux_cap) + 1) + align4(L.aux_cap);
+  }
   L.plan_ints = off;
   L.plan_bytes = uint64_t(off) * 4;
   L.partial_offset = (L.plan_bytes + 255) & ~uint64_t(255);
@@ -158,7 +180,7 @@ int make_layout_caps(const Config& cfg, int64_t max_tiles, int32_t workers, Layo
 
 int make_layout(const Config& cfg, int32_t max_batch, int32_t max_qo_tokens, int32_t workers,
                 Layout* out, std::string* err) {
-  if (max_batch < 0 || workers < 1 || (cfg.kind == ABP_KIND_APPEND && max_qo_tokens < 0)) {
+  if (max_batch < 0 || workers < 1 || (cfg.kind != ABP_KIND_DECODE && max_qo_tokens < 0)) {
     *err = "max_batch and max_qo_tokens must be >= 0 and num_workers >= 1";
     return ABP_ERR_INVALID_ARG;
   }
@@ -181,14 +203,19 @@ uint64_t fingerprint(const Config& c, const Layout& L) {
       h *= 1099511628211ull;
     }
   };
-  uint32_t scale_bits, theta_bits;
+  uint32_t scale_bits, theta_bits, l31[4];
   memcpy(&scale_bits, &c.sm_scale, 4);
   memcpy(&theta_bits, &c.rope_theta, 4);
+  memcpy(&l31[0], &c.rope_factor, 4);
+  memcpy(&l31[1], &c.rope_low, 4);
+  memcpy(&l31[2], &c.rope_high, 4);
+  memcpy(&l31[3], &c.rope_old_ctx, 4);
   const int64_t vals[] = {c.kind,      c.hq,          c.hkv,          c.head_dim,   c.page_size,
                           c.qkv_dtype, c.out_dtype,   scale_bits,     c.causal,     c.rope,
                           theta_bits,  L.workers,     L.max_tiles,    L.max_segs,   L.max_partials,
                           L.max_merges, L.tile_q,     L.tile_kv,      L.rows,       L.plan_ints,
-                          (int64_t)L.partial_offset};
+                          (int64_t)L.partial_offset, l31[0], l31[1], l31[2], l31[3],
+                          L.off_aux, L.aux_cap};
   for (int64_t v : vals) mix((uint64_t)v);
   return h;
 }
@@ -196,7 +223,7 @@ uint64_t fingerprint(const Config& c, const Layout& L) {
 int plan_compute(const Config& cfg, const Layout& L, int32_t batch, const int32_t* qo_indptr,
                  const int32_t* kv_indptr, const int32_t* lpl, int32_t* blob, abp_plan* plan,
                  std::string* err) {
-  const bool append = cfg.kind == ABP_KIND_APPEND;
+  const bool append = cfg.kind != ABP_KIND_DECODE;
   if (batch < 0) {
     *err = "batch must be >= 0";
     return ABP_ERR_INVALID_ARG;
@@ -262,7 +289,8 @@ int plan_compute(const Config& cfg, const Layout& L, int32_t batch, const int32_
   }
   const int64_t quota = N > 0 ? ceil_div(N, W) : 1;
 
-  memset(blob, 0, sizeof(int32_t) * size_t(L.plan_ints));
+  // the aux region (block-sparse plans) holds inputs of this call: keep it
+  memset(blob, 0, sizeof(int32_t) * size_t(L.off_aux));
   int32_t* wseg = blob + L.off_wseg;
   int32_t* seg = blob + L.off_seg;
   int32_t* tile = blob + L.off_tile;
@@ -316,8 +344,22 @@ int plan_compute(const Config& cfg, const Layout& L, int32_t batch, const int32_
   const int half = cfg.head_dim / 2;
   for (int j = 0; j < kMaxRopePairs; ++j) {
     double f = 0.0;
-    if (cfg.rope && j < half)
-      f = pow((double)cfg.rope_theta, -2.0 * j / cfg.head_dim) / (2.0 * M_PI);
+    if (cfg.rope && j < half) {
+      f = pow((double)cfg.rope_theta, -2.0 * j / cfg.head_dim);
+      if (cfg.rope == 2) {
+        // LLaMA 3.1: keep short wavelengths, divide long ones by the factor,
+        // blend linearly in old_context_len / wavelength between the two
+        const double w = 2.0 * M_PI / f;
+        const double old = cfg.rope_old_ctx, lo = cfg.rope_low, hi = cfg.rope_high;
+        if (w > old / lo) {
+          f = f / cfg.rope_factor;
+        } else if (w >= old / hi) {
+          const double sm = (old / w - lo) / (hi - lo);
+          f = (1.0 - sm) * f / cfg.rope_factor + sm * f;
+        }
+      }
+      f /= 2.0 * M_PI;
+    }
     const float hi = (float)f;
     rope[2 * j] = hi;
     rope[2 * j + 1] = (float)(f - (double)hi);
@@ -352,6 +394,7 @@ int plan_compute(const Config& cfg, const Layout& L, int32_t batch, const int32_
   blob[H_OFF_CNT] = (int32_t)L.off_cnt;  // counters stay zero (memset above)
   blob[H_OFF_NTILE] = (int32_t)L.off_ntile;
   blob[H_MERGE_KERNEL] = (!append || max_nseg > kInKernelMergeMax) ? 1 : 0;
+  blob[H_OFF_AUX] = (int32_t)L.off_aux;
 
   plan->kind = cfg.kind;
   plan->batch = batch;
@@ -372,6 +415,52 @@ int plan_compute(const Config& cfg, const Layout& L, int32_t batch, const int32_
   plan->partial_offset = L.partial_offset;
   plan->dev_bytes = L.dev_bytes;
   return ABP_OK;
+}
+
+int bsr_plan_compute(const Config& cfg, const Layout& L, int32_t M, int32_t N, int32_t R,
+                     const int32_t* indptr, int32_t* blob, abp_plan* plan, std::string* err) {
+  if (cfg.kind != ABP_KIND_BSR) {
+    *err = "not a block-sparse configuration";
+    return ABP_ERR_INVALID_ARG;
+  }
+  if (M < 0 || N < 0 || R < 1) {
+    *err = "block-sparse attention needs M >= 0, N >= 0 and R >= 1";
+    return ABP_ERR_INVALID_ARG;
+  }
+  const int32_t C = cfg.page_size;
+  if (N % C != 0) {
+    *err = "N must be a multiple of the column block size (page_size)";
+    return ABP_ERR_INVALID_ARG;
+  }
+  if (!blob || !plan || (M > 0 && !indptr)) {
+    *err = "NULL array";
+    return ABP_ERR_INVALID_ARG;
+  }
+  const int64_t nrb = ceil_div(M, R);
+  if (nrb > L.aux_cap) {
+    *err = "row blocks exceed the workspace capacity (max_row_blocks / max_M)";
+    return ABP_ERR_WORKSPACE_TOO_SMALL;
+  }
+  const int64_t ncb = N / C;
+  for (int64_t i = 0; i < nrb; ++i) {
+    const int64_t n = int64_t(indptr[i + 1]) - indptr[i];
+    if (indptr[0] != 0 || n < 0) {
+      *err = "indptr must start at 0 and be non-decreasing";
+      return ABP_ERR_INVALID_ARG;
+    }
+    if (n > ncb) {
+      *err = "a row block lists more column blocks than N / C";
+      return ABP_ERR_INVALID_ARG;
+    }
+  }
+  // row block i = append request i: queries [i R, min((i+1) R, M)), its
+  // pages are its column blocks, all full (kv_len = n_i C)
+  int32_t* qo = blob + L.off_aux;
+  int32_t* lpl = qo + align4(int64_t(L.aux_cap) + 1);
+  for (int64_t i = 0; i <= nrb; ++i) qo[i] = (int32_t)std::min<int64_t>(i * R, M);
+  for (int64_t i = 0; i < nrb; ++i) lpl[i] = C;
+  const int32_t zero = 0;
+  return plan_compute(cfg, L, (int32_t)nrb, qo, nrb > 0 ? indptr : &zero, lpl, blob, plan, err);
 }
 
 }  // namespace abp

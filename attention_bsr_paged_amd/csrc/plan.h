@@ -18,6 +18,8 @@ struct Config {
   float sm_scale = 0.f;
   int32_t causal = 0, rope = 0;
   float rope_theta = 0.f;
+  // LLaMA 3.1 frequency scaling (rope == 2)
+  float rope_factor = 1.f, rope_low = 1.f, rope_high = 1.f, rope_old_ctx = 1.f;
 };
 
 // Returns ABP_OK or an error status with `err` set.
@@ -36,6 +38,12 @@ int make_layout(const Config& cfg, int32_t max_batch, int32_t max_qo_tokens, int
 int plan_compute(const Config& cfg, const Layout& lay, int32_t batch, const int32_t* qo_indptr,
                  const int32_t* kv_indptr, const int32_t* kv_last_page_len, int32_t* blob,
                  abp_plan* plan, std::string* err);
+
+// Block-sparse attention plan: validates the BSR row pointer, writes the
+// derived per-row-block query ranges and page counts into the blob's aux
+// region and plans them as append requests over the column blocks.
+int bsr_plan_compute(const Config& cfg, const Layout& lay, int32_t M, int32_t N, int32_t R,
+                     const int32_t* indptr, int32_t* blob, abp_plan* plan, std::string* err);
 
 uint64_t fingerprint(const Config& cfg, const Layout& lay);
 

@@ -40,7 +40,14 @@
  *  Causal append: query i (0-based) of a request with qo_len queries sees keys
  *  t <= kv_len - qo_len + i (aligned to the end of the KV).
  *  RoPE (params.rope = 1): LLaMA rotate-half; pair (j, j + head_dim/2) of q and k
- *  is turned by pos * rope_theta^(-2j/head_dim). Key t of request b sits at
+ *  is turned by pos * f_j, f_j = rope_theta^(-2j/head_dim). params.rope = 2 uses
+ *  the LLaMA 3.1 frequencies instead (README page, section 其他算子, lists
+ *  LLaMA 3.1 RoPE; the rule is the one published with those models): with
+ *  wavelength w = 2 pi / f_j, f_j is kept if w < old_context_len /
+ *  high_freq_factor, divided by factor if w > old_context_len / low_freq_factor,
+ *  and otherwise blended as (1 - s) f_j / factor + s f_j with s =
+ *  (old_context_len / w - low_freq_factor) / (high_freq_factor - low_freq_factor).
+ *  Key t of request b sits at
  *  kv_pos_offset[b] + t (default 0). A decode query sits at q_pos[b] (default
  *  kv_len - 1); append query i at q_pos[token] (default kv_len - qo_len + i).
  *  K is stored un-rotated; v is never rotated.
@@ -95,7 +102,7 @@ typedef enum abp_status {
 } abp_status;
 
 typedef enum abp_dtype { ABP_F16 = 0, ABP_BF16 = 1, ABP_F32 = 2 } abp_dtype;
-typedef enum abp_kind { ABP_KIND_DECODE = 0, ABP_KIND_APPEND = 1 } abp_kind;
+typedef enum abp_kind { ABP_KIND_DECODE = 0, ABP_KIND_APPEND = 1, ABP_KIND_BSR = 2 } abp_kind;
 
 typedef struct abp_params {
   int32_t num_qo_heads;
@@ -106,8 +113,14 @@ typedef struct abp_params {
   int32_t out_dtype;  /* ABP_F16, ABP_BF16 or ABP_F32 */
   float sm_scale;     /* <= 0 selects 1/sqrt(head_dim) */
   int32_t causal;     /* append only: 1 = causal mask aligned to the end of the KV */
-  int32_t rope;       /* 0 = none, 1 = LLaMA rotate-half RoPE on q and k at load */
+  int32_t rope;       /* 0 = none, 1 = LLaMA rotate-half RoPE on q and k at load,
+                         2 = the same with LLaMA 3.1 frequency scaling */
   float rope_theta;   /* RoPE base, e.g. 500000 */
+  /* rope = 2 only (LLaMA 3.1 settings: 8, 1, 4, 8192); ignored otherwise */
+  float rope_factor;            /* > 0 */
+  float rope_low_freq_factor;   /* > 0 */
+  float rope_high_freq_factor;  /* > rope_low_freq_factor */
+  float rope_old_context_len;   /* > 0 */
 } abp_params;
 
 /* Result of a plan: plain data, copied by value. Fields are informative; only
@@ -213,6 +226,61 @@ int abp_append_run(const abp_plan* plan, const abp_params* params, const void* q
                    const int32_t* kv_last_page_len_d, const int32_t* q_pos_d,
                    const int32_t* kv_pos_offset_d, void* o, float* lse, void* dev_ws,
                    size_t dev_bytes, abp_stream_t stream);
+
+/* Block-sparse attention (README page, section 核心功能: block-sparse and
+ * variable block-sparse attention; paper summary, section 统一的 KV 缓存存储格式:
+ * one BSR format with a configurable block size serves every layout).
+ *
+ * A mask over q [M, Hq, d] and a dense k / v [N, Hkv, d] (qkv_dtype) in block-
+ * sparse-row form: row block i holds queries [i R, min((i+1) R, M)) and sees the
+ * column blocks indices[indptr[i] .. indptr[i+1]) of C = params->page_size keys
+ * each (key block j = keys [j C, (j+1) C)); query r sees key t exactly when the
+ * block (r / R, t / C) is listed. indptr has ceil(M / R) + 1 entries, indptr[0] = 0,
+ * non-decreasing; indices are column block ids in [0, N / C) in any order, each
+ * at most once per row (a repeated block would count its keys twice). A query
+ * whose row block lists nothing gets o = 0, lse = -inf. Requires N % C == 0,
+ * params->causal = 0 and params->rope = 0.
+ *
+ * Each row block is run as one append request whose pages are its column
+ * blocks (k viewed as [N / C, C, Hkv, d]); the planner writes the derived
+ * query ranges and page counts into the plan blob, so the run needs only the
+ * caller's indptr / indices on the device.
+ *
+ * Workspace: abp_workspace_size(ABP_KIND_BSR, params, max_row_blocks, max_M,
+ * num_workers, ...). abp_bsr_plan_host plans on the host only; abp_bsr_plan
+ * also uploads like abp_decode_plan. */
+int abp_bsr_plan_host(const abp_params* params, int32_t M, int32_t N, int32_t R,
+                      const int32_t* indptr_h, int32_t max_row_blocks, int32_t max_M,
+                      int32_t num_workers, void* host_ws, size_t host_bytes, abp_plan* plan);
+int abp_bsr_plan(const abp_params* params, int32_t M, int32_t N, int32_t R,
+                 const int32_t* indptr_h, int32_t max_row_blocks, int32_t max_M,
+                 int32_t num_workers, void* host_ws, size_t host_bytes, void* dev_ws,
+                 size_t dev_bytes, abp_stream_t stream, abp_plan* plan);
+
+/* Block-sparse attention run (the append MFMA kernel, then the merge kernel):
+ * q [M, Hq, d], k / v [N, Hkv, d], indptr_d / indices_d as planned (device
+ * copies); o [M, Hq, d] (out_dtype), lse [M, Hq] float32 or NULL. Tensor
+ * pointers may be NULL only when M = 0. Same workspace rules as abp_append_run. */
+int abp_bsr_run(const abp_plan* plan, const abp_params* params, const void* q, const void* k,
+                const void* v, const int32_t* indptr_d, const int32_t* indices_d, void* o,
+                float* lse, void* dev_ws, size_t dev_bytes, abp_stream_t stream);
+
+/* Write new tokens into a paged KV cache (the step that fills the pages before
+ * decode / append read them; README page, section 核心功能: paged KV caches).
+ * k_new / v_new [nnz, Hkv, d] (params->qkv_dtype) are ragged by
+ * append_indptr_d [batch + 1] (append_indptr[batch] = nnz). The page table
+ * (kv_indptr_d, kv_indices_d, kv_last_page_len_d, as in abp_decode_run) must
+ * already cover the new tokens, which are the last ones of each request: new
+ * row i of request b is logical token kv_len_b - append_len_b + i, stored in
+ * slot t % page_size of page kv_indices[kv_indptr[b] + t / page_size]. Rows whose
+ * position falls outside [0, kv_len_b) are skipped. Only num_kv_heads,
+ * head_dim, page_size and qkv_dtype of params are used. One kernel on `stream`,
+ * no allocation, graph-capturable. All arrays are device memory; nnz = 0 is a
+ * no-op. */
+int abp_append_paged_kv(const abp_params* params, int32_t batch, int64_t nnz, const void* k_new,
+                        const void* v_new, const int32_t* append_indptr_d, void* k_pages,
+                        void* v_pages, const int32_t* kv_indptr_d, const int32_t* kv_indices_d,
+                        const int32_t* kv_last_page_len_d, abp_stream_t stream);
 
 /* Merge two attention states over disjoint key sets (cascade: prefix and suffix).
  * o_a, o_b [num_rows, head_dim] in in_dtype; lse_a, lse_b [num_rows] float32;

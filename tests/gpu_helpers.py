@@ -47,7 +47,7 @@ def run_decode(w, num_workers=0, out_dtype=None, dev=None, return_runner=False):
     q = wl.to_torch(w.q, w.dtype, "cuda")
     params = abp.make_params(w.num_qo_heads, w.num_kv_heads, w.head_dim, kv.page_size,
                              torch_dtype(w.dtype), out_dtype=out_dtype,
-                             rope_theta=w.rope_theta)
+                             rope_theta=w.rope_theta, rope_llama31=w.rope_llama31)
     dec = abp.BatchDecode(params, max_batch=max(w.batch, 1), num_workers=num_workers)
     dec.plan(kv.kv_indptr, kv.kv_last_page_len)
     o, lse = dec.run(q, dev["k"], dev["v"], dev["indptr"], dev["indices"], dev["lpl"],
@@ -66,7 +66,7 @@ def run_append(w, num_workers=0, out_dtype=None, dev=None):
     q = wl.to_torch(w.q, w.dtype, "cuda")
     params = abp.make_params(w.num_qo_heads, w.num_kv_heads, w.head_dim, kv.page_size,
                              torch_dtype(w.dtype), out_dtype=out_dtype, causal=w.causal,
-                             rope_theta=w.rope_theta)
+                             rope_theta=w.rope_theta, rope_llama31=w.rope_llama31)
     app = abp.BatchAppend(params, max_batch=max(w.batch, 1),
                           max_qo_tokens=max(int(w.qo_indptr[-1]), 1), num_workers=num_workers)
     app.plan(w.qo_indptr, kv.kv_indptr, kv.kv_last_page_len)
@@ -89,3 +89,21 @@ def assert_parity(o, lse, o_ref, lse_ref, dtype, rows=None, what=""):
     assert do <= O_TOL[dtype], f"{what}: max|o - o_ref| = {do}"
     assert dl <= LSE_TOL, f"{what}: max|lse - lse_ref| = {dl}"
     assert np.all(o[inf_ref] == 0), f"{what}: empty rows must be 0"
+
+
+def run_bsr(w, num_workers=0, out_dtype=None, runner=None):
+    """Block-sparse attention of a BsrWorkload through the C ABI."""
+    import torch
+    q = wl.to_torch(w.q, w.dtype, "cuda")
+    k = wl.to_torch(w.k, w.dtype, "cuda")
+    v = wl.to_torch(w.v, w.dtype, "cuda")
+    if runner is None:
+        params = abp.make_params(w.num_qo_heads, w.num_kv_heads, w.head_dim, w.C,
+                                 torch_dtype(w.dtype), out_dtype=out_dtype)
+        nrb = len(w.indptr) - 1
+        runner = abp.BlockSparseAttention(params, max_row_blocks=max(nrb, 1),
+                                          max_M=max(w.M, 1), num_workers=num_workers)
+    runner.plan(w.M, w.N, w.R, w.indptr)
+    o, lse = runner.run(q, k, v, i32(w.indptr), i32(w.indices))
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy()

@@ -175,3 +175,101 @@ def test_planner_on_named_decode_workloads(lib, name):
     indptr, _, lpl = wl.page_table(kv_len, 16, np.arange(10 ** 6))
     for W in (256, 512, 1024):
         _compare(KIND_DECODE, P(), len(kv_len), None, indptr, lpl, W, 4)
+
+
+# ----------------------------------------------------------------------------
+# block-sparse plans, LLaMA 3.1 frequency table, page append argument checks
+# ----------------------------------------------------------------------------
+@settings(max_examples=60, deadline=None)
+@given(st.data())
+def test_bsr_plan_matches_reference_over_row_blocks(data):
+    """A block-sparse plan is the append plan of its row blocks (queries
+    [i R, min((i+1) R, M)), pages = listed column blocks, all full)."""
+    abp.load_library()
+    C = data.draw(st.sampled_from([1, 3, 16, 64]))
+    R = data.draw(st.sampled_from([1, 5, 16, 64, 100]))
+    G = data.draw(st.sampled_from([1, 4, 8]))
+    hkv = data.draw(st.sampled_from([1, 2, 8]))
+    W = data.draw(st.integers(1, 70))
+    ncb = data.draw(st.integers(0, 40))
+    M = data.draw(st.integers(0, 700))
+    nrb = -(-M // R)
+    counts = [data.draw(st.integers(0, ncb)) for _ in range(nrb)]
+    indptr = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    p = P(num_qo_heads=hkv * G, num_kv_heads=hkv, page_size=C)
+    h, _ = abp.abp_workspace_size(abp.ABP_KIND_BSR, p, nrb, M, W)
+    ws = np.zeros(h, np.uint8)
+    plan = abp.abp_bsr_plan_host(p, M, ncb * C, R, indptr, nrb, M, W, ws)
+    assert plan.kind == abp.ABP_KIND_BSR
+    got = abp.decode_plan_arrays(ws, plan)
+    qo_indptr = np.minimum(np.arange(nrb + 1) * R, M)
+    ref = plan_ref(KIND_APPEND, nrb, indptr, np.full(nrb, C), C, hkv, W, 64,
+                   qo_indptr=qo_indptr, tile_q=256 // G, causal=False)
+    for k, v in ref.items():
+        assert np.array_equal(got[k], v), k
+    # the derived query ranges and page counts the run reads from the blob
+    b = ws.view(np.int32)
+    aux = got["off_aux"]
+    cap = (len(b) - aux) // 2
+    assert np.array_equal(b[aux:aux + nrb + 1], qo_indptr)
+    lpl_at = aux + ((plan.max_tiles // hkv + 1 + 3) & ~3)
+    assert np.all(b[lpl_at:lpl_at + nrb] == C)
+    assert cap >= nrb
+
+
+def test_bsr_plan_validation(lib):
+    p = P(page_size=16)
+    h, _ = abp.abp_workspace_size(abp.ABP_KIND_BSR, p, 4, 256, 8)
+    ws = np.zeros(h, np.uint8)
+    for args, status in [
+        ((256, 100, 64, [0, 1, 2, 3, 4]), abp.ABP_ERR_INVALID_ARG),      # N % C != 0
+        ((256, 128, 64, [0, 1, 2, 1, 4]), abp.ABP_ERR_INVALID_ARG),      # decreasing indptr
+        ((256, 128, 64, [1, 1, 2, 3, 4]), abp.ABP_ERR_INVALID_ARG),      # indptr[0] != 0
+        ((256, 128, 64, [0, 9, 9, 9, 9]), abp.ABP_ERR_INVALID_ARG),      # 9 > N / C blocks
+        ((320, 128, 64, [0] * 6), abp.ABP_ERR_WORKSPACE_TOO_SMALL),      # M > max_M
+        ((256, 128, 32, [0] * 9), abp.ABP_ERR_WORKSPACE_TOO_SMALL),      # 8 row blocks > 4
+    ]:
+        with pytest.raises(abp.AbpError) as e:
+            abp.abp_bsr_plan_host(p, *args, 4, 256, 8, ws)
+        assert e.value.status == status, args
+    for bad in (P(causal=True), P(rope_theta=1e4)):
+        with pytest.raises(abp.AbpError) as e:
+            abp.abp_workspace_size(abp.ABP_KIND_BSR, bad, 4, 256, 8)
+        assert e.value.status == abp.ABP_ERR_UNSUPPORTED
+    with pytest.raises(abp.AbpError):              # the generic planner refuses BSR plans
+        abp.abp_plan_host(abp.ABP_KIND_BSR, p, 1, [0, 4], [0, 1], [16], 1, 4, 8, ws)
+
+
+@pytest.mark.parametrize("l31", [None, abp.LLAMA31_ROPE, (4.0, 2.0, 8.0, 4096.0)])
+def test_rope_frequency_table_matches_oracle(lib, l31):
+    """The host table (revolutions per position, fp32 hi + lo) against the
+    oracle's float64 frequencies, LLaMA 3.1-scaled or not."""
+    from oracle import attention as ora
+    p = P(rope_theta=500000.0, rope_llama31=l31)
+    ws = _ws(0, p, 2, 0, 8)
+    plan = abp.abp_plan_host(0, p, 2, None, [0, 1, 2], [3, 4], 2, 0, 8, ws)
+    t = abp.decode_plan_arrays(ws, plan)["rope"].astype(np.float64)
+    rev = t[0::2] + t[1::2]
+    want = ora.rope_inv_freq(128, 500000.0, l31) / (2 * np.pi)
+    assert np.max(np.abs(rev - want) / want) < 1e-13
+
+
+def test_llama31_params_validated(lib):
+    for bad in [(8.0, 1.0, 1.0, 8192.0), (0.0, 1.0, 4.0, 8192.0), (8.0, 1.0, 4.0, 0.0)]:
+        with pytest.raises(abp.AbpError) as e:
+            abp.abp_workspace_size(0, P(rope_theta=5e5, rope_llama31=bad), 2, 0, 8)
+        assert e.value.status == abp.ABP_ERR_INVALID_ARG
+
+
+def test_page_append_argument_checks(lib):
+    p = P()
+    # nothing to write: returns before touching any device
+    assert lib.abp_append_paged_kv(ctypes.byref(p), 3, 0, *([None] * 8), None) == abp.ABP_OK
+    assert lib.abp_append_paged_kv(ctypes.byref(p), 0, 5, *([None] * 8), None) == abp.ABP_OK
+    assert lib.abp_append_paged_kv(ctypes.byref(p), 2, 4, *([None] * 8), None) == \
+        abp.ABP_ERR_INVALID_ARG
+    assert lib.abp_append_paged_kv(ctypes.byref(p), -1, 4, *([None] * 8), None) == \
+        abp.ABP_ERR_INVALID_ARG
+    q = P(head_dim=64)
+    assert lib.abp_append_paged_kv(ctypes.byref(q), 2, 4, *([None] * 8), None) == \
+        abp.ABP_ERR_UNSUPPORTED
