@@ -2,7 +2,7 @@
 """Benchmark of paged BSR attention on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--part all|decode|append|single|skewed|cascade|copy]
+                    [--part all|decode|append|single|skewed|cascade|copy|bsr|page_append]
 
 A step is one pass of the hot path over one batch of the batch paged decode
 workload (64 requests, GQA 32/8, head_dim 128, page 16, bf16, kv_len uniform on
@@ -20,8 +20,11 @@ kernel), timed with HIP events on the stream it is launched on. ``append`` is
 the ragged causal append workload (16 requests, qo U{128..1024} onto kv
 U{1024..8192}, GQA 32/8, bf16) in TFLOP/s of visible (unmasked) work;
 ``configs`` holds the single-request, skewed-batch and cascade+RoPE decode
-workloads. ``cpu_baseline`` is the fp64 oracle on a bounded sample of the batch
-decode workload, on the host cores of the same machine.
+workloads; ``next`` holds block-sparse attention (8192 x 8192, row blocks of
+64, column blocks of 16, a quarter of the blocks, TFLOP/s of unmasked work)
+and the page append of 16 requests' new tokens (TB/s of rows read + written).
+``cpu_baseline`` is the fp64 oracle on a bounded sample of the batch decode
+workload, on the host cores of the same machine (and of each other leg).
 
 ``--part copy`` times a plain 1 GiB device copy (read + write of known size);
 its counter readings calibrate FETCH_SIZE / WRITE_SIZE for the traffic figure.
@@ -52,26 +55,31 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_run_batch_decode_traffic.t
 DECODE_SOURCES = ["decode.hip", "merge.hip", "common.h", "kernels.h", "layout.h"]
 
 
-def decode_source_hash() -> str:
+PAGE_APPEND_TRAFFIC_FILE = os.path.join(ROOT, "profiles",
+                                        "page_append_kernel_ragged_page_append_traffic.txt")
+PAGE_APPEND_SOURCES = ["page_append.hip"]
+
+
+def source_hash(names=DECODE_SOURCES) -> str:
     h = hashlib.sha256()
-    for name in DECODE_SOURCES:
+    for name in names:
         with open(os.path.join(ROOT, "attention_bsr_paged_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def recorded_traffic():
-    """Bytes per decode run from the committed counter summary, or None when the
-    summary is absent or the kernel sources changed since it was taken."""
+def recorded_traffic(path=TRAFFIC_FILE, sources=DECODE_SOURCES):
+    """Bytes per run from a committed counter summary, or None when the summary
+    is absent or the kernel sources changed since it was taken."""
     try:
-        text = open(TRAFFIC_FILE).read()
+        text = open(path).read()
     except OSError:
         return None
     m = re.search(r"^TRAFFIC (\{.*\})\s*$", text, re.M)
     if not m:
         return None
     rec = json.loads(m.group(1))
-    if rec.get("source_sha256_16") != decode_source_hash():
+    if rec.get("source_sha256_16") != source_hash(sources):
         return None
     return rec
 
@@ -343,6 +351,134 @@ def bench_cascade(abp, wl, torch, dev, K, Wm) -> dict:
 
 
 # ----------------------------------------------------------------------------
+# block-sparse attention (MFMA) and page append (HBM copy)
+# ----------------------------------------------------------------------------
+def bsr_flops(w, rows=None) -> float:
+    """4 * d * Hq per (query, key) pair the mask lets through."""
+    nrb = len(w.indptr) - 1
+    cnt = np.diff(w.indptr).astype(np.int64)
+    if rows is None:
+        per_block = np.minimum((np.arange(nrb) + 1) * w.R, w.M) - np.arange(nrb) * w.R
+        pairs = int((per_block * cnt).sum()) * w.C
+    else:
+        pairs = int(sum(int(cnt[r // w.R]) for r in rows)) * w.C
+    return 4.0 * w.head_dim * w.num_qo_heads * float(pairs)
+
+
+def bench_bsr(abp, wl, torch, dev, K, Wm) -> dict:
+    w = wl.bsr_sparse()
+    flops = bsr_flops(w)
+    q = wl.to_torch(w.q, w.dtype, dev)
+    k0 = wl.to_torch(w.k, w.dtype, dev)
+    v0 = wl.to_torch(w.v, w.dtype, dev)
+    ks, copies = replicas(k0, torch, k0.nbytes + v0.nbytes)
+    vs, _ = replicas(v0, torch, k0.nbytes + v0.nbytes)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
+    ip, idx = i32(w.indptr), i32(w.indices)
+    params = abp.make_params(w.num_qo_heads, w.num_kv_heads, w.head_dim, w.C, torch.bfloat16)
+    nrb = len(w.indptr) - 1
+    bsr = abp.BlockSparseAttention(params, max_row_blocks=nrb, max_M=w.M, device=dev)
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    s = torch.cuda.current_stream(dev)
+
+    def step(i, evs):
+        bsr.plan(w.M, w.N, w.R, w.indptr, stream=s)
+        if evs:
+            evs[0].record(s)
+        bsr.run(q, ks[i % copies], vs[i % copies], ip, idx, o=o, lse=lse, stream=s)
+        if evs:
+            evs[1].record(s)
+
+    wall, run_ms = timed_steps(torch, s, step, K, Wm)
+    torch.cuda.synchronize()
+    avg = float(run_ms.mean())
+    tf = flops / (avg * 1e-3) / 1e12
+    nnz = int(w.indptr[-1])
+    return {
+        "workload": w.name,
+        "value": round(tf, 2),
+        "unit": "TFLOP/s",
+        "step_TFLOPs": round(flops / (wall * 1e-3) / 1e12, 2),
+        "ms_per_step": round(wall, 5),
+        "mask_flop": flops,
+        "density": round(nnz / (nrb * (w.N // w.C)), 4),
+        "run": _stats_ms(run_ms),
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel": "append_kernel over BSR row blocks (+ merge)",
+                     "avg_launch_us": round(avg * 1e3, 2)},
+        "workers": bsr.plan_struct.num_workers,
+        "segments": bsr.plan_struct.num_segments,
+        "kv_copies": copies,
+    }
+
+
+def page_append_bytes(w) -> int:
+    """Each new K/V row read once and written once, plus append_indptr, the page
+    table entries read (kv_indptr, last_page_len, one index per row)."""
+    kv = w.kv
+    row = kv.num_kv_heads * kv.head_dim * 2
+    B = len(w.append_indptr) - 1
+    return 2 * 2 * w.nnz * row + (B + 1) * 4 + (B + 1) * 4 + B * 4 + w.nnz * 4
+
+
+def bench_page_append(abp, wl, torch, dev, K, Wm) -> dict:
+    w = wl.ragged_page_append()
+    kv = w.kv
+    by = page_append_bytes(w)
+    kn0 = wl.to_torch(w.k_new, kv.dtype, dev)
+    vn0 = wl.to_torch(w.v_new, kv.dtype, dev)
+    kp0 = wl.to_torch(kv.k_pages, kv.dtype, dev)
+    vp0 = wl.to_torch(kv.v_pages, kv.dtype, dev)
+    tot = kn0.nbytes * 2 + kp0.nbytes * 2
+    kns, copies = replicas(kn0, torch, tot)
+    vns, _ = replicas(vn0, torch, tot)
+    kps, _ = replicas(kp0, torch, tot)
+    vps, _ = replicas(vp0, torch, tot)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
+    ai, ip, idx, lpl = i32(w.append_indptr), i32(kv.kv_indptr), i32(kv.kv_indices), \
+        i32(kv.kv_last_page_len)
+    s = torch.cuda.current_stream(dev)
+    # a launch is ~16 us: one event pair per group of GROUP back-to-back launches,
+    # so the events' own idle time is spread over the group
+    GROUP = 8
+
+    def step(i, evs):
+        if evs:
+            evs[0].record(s)
+        for j in range(GROUP):
+            c = (i * GROUP + j) % copies
+            abp.append_paged_kv_cache(kns[c], vns[c], ai, kps[c], vps[c], ip, idx, lpl, stream=s)
+        if evs:
+            evs[1].record(s)
+
+    wall, run_ms = timed_steps(torch, s, step, max(1, K // GROUP), max(1, Wm // GROUP))
+    torch.cuda.synchronize()
+    wall /= GROUP
+    run_ms = run_ms / GROUP
+    avg = float(run_ms.mean())
+    gbs = by / (avg * 1e-3) / 1e9
+    tr = recorded_traffic(PAGE_APPEND_TRAFFIC_FILE, PAGE_APPEND_SOURCES)
+    return {
+        "workload": w.name,
+        "value": round(gbs / 1e3, 4),
+        "unit": "TB/s",
+        "ms_per_step": round(wall, 5),
+        "algorithmic_bytes": by,
+        "new_tokens": w.nnz,
+        "run": _stats_ms(run_ms),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_TBS * 1e3,
+                     "unit": "GB/s", "frac": round(gbs / (HBM_PEAK_TBS * 1e3), 4),
+                     "traffic": tr["traffic_bytes_per_run"] if tr else None,
+                     "kernel": "page_append_kernel",
+                     "avg_launch_us": round(avg * 1e3, 2)},
+        "timing": f"HIP events around groups of {GROUP} back-to-back launches",
+        "copies": copies,
+    }
+
+
+# ----------------------------------------------------------------------------
 # plain copy (context and counter calibration)
 # ----------------------------------------------------------------------------
 def bench_copy(torch, dev, K, Wm, nbytes=2 ** 30) -> dict:
@@ -431,6 +567,50 @@ def cpu_baseline_append(w, budget_s: float = 8.0) -> dict:
                       f"thread", "host_cpu": model, "host_cores_available": avail}
 
 
+def cpu_baseline_bsr(w, budget_s: float = 6.0) -> dict:
+    """The fp64 oracle on runs of 8 query rows at random places (all heads)."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention as ora
+    rng = np.random.Generator(np.random.PCG64(8))
+    done, t_used = [], 0.0
+    with threadpool_limits(limits=1):
+        while t_used < budget_s:
+            r0 = int(rng.integers(0, w.M - 8))
+            rows = list(range(r0, r0 + 8))
+            t0 = time.perf_counter()
+            ora.bsr_attention(w.q, w.k, w.v, w.R, w.C, w.indptr, w.indices, w.dtype,
+                              w.num_kv_heads, rows=rows)
+            t_used += time.perf_counter() - t0
+            done += rows
+    fl = bsr_flops(w, done)
+    model, avail = _cpu_info()
+    return {"value": round(fl / t_used / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{len(done)} of {w.M} query rows (runs of 8, all heads; {fl / 1e9:.1f} "
+                      f"GFLOP in the mask) in {t_used:.1f} s; fp64 NumPy, 1 BLAS thread",
+            "host_cpu": model, "host_cores_available": avail}
+
+
+def cpu_baseline_page_append(w, budget_s: float = 4.0) -> dict:
+    """The oracle's page append over the whole workload, repeated."""
+    from oracle import attention as ora
+    kv = w.kv
+    n, t_used = 0, 0.0
+    while t_used < budget_s:
+        t0 = time.perf_counter()
+        ora.append_paged_kv(w.k_new, w.v_new, w.append_indptr, kv.k_pages, kv.v_pages,
+                            kv.kv_indptr, kv.kv_indices, kv.kv_last_page_len, kv.page_size)
+        t_used += time.perf_counter() - t0
+        n += 1
+    model, avail = _cpu_info()
+    return {"value": round(n * page_append_bytes(w) / t_used / 1e12, 6), "unit": "TB/s",
+            "cores": 1, "kind": "oracle",
+            "sample": f"{n} passes over all {w.nnz} new rows (each pass copies both pools) in "
+                      f"{t_used:.1f} s; NumPy, one thread",
+            "host_cpu": model, "host_cores_available": avail}
+
+
 # ----------------------------------------------------------------------------
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
@@ -443,7 +623,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the single, skewed and cascade workloads")
     ap.add_argument("--part", default="all",
-                    choices=["all", "decode", "append", "single", "skewed", "cascade", "copy"],
+                    choices=["all", "decode", "append", "single", "skewed", "cascade", "copy",
+                             "bsr", "page_append"],
                     help="one workload alone (profiling); 'all' is the benchmark line")
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -470,6 +651,12 @@ def main(argv=None) -> int:
         return 0
     if part == "cascade":
         print(json.dumps(bench_cascade(abp, wl, torch, dev, K, Wm)), flush=True)
+        return 0
+    if part == "bsr":
+        print(json.dumps(bench_bsr(abp, wl, torch, dev, K, Wm)), flush=True)
+        return 0
+    if part == "page_append":
+        print(json.dumps(bench_page_append(abp, wl, torch, dev, K, Wm)), flush=True)
         return 0
     if part in ("single", "skewed"):
         w = wl.single_decode_mha() if part == "single" else wl.skewed_decode_gqa()
@@ -538,11 +725,19 @@ def main(argv=None) -> int:
             "skewed_decode": bench_decode(abp, wl, torch, dev, wl.skewed_decode_gqa(), Kc, 5),
             "cascade_rope": bench_cascade(abp, wl, torch, dev, Kc, 5),
         }
+        out["next"] = {
+            "bsr_sparse": bench_bsr(abp, wl, torch, dev, Kc, 5),
+            "page_append": bench_page_append(abp, wl, torch, dev, Kc, 5),
+        }
         out["copy_context"] = bench_copy(torch, dev, 20, 3)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_decode(w)
         if "append" in out:
             out["append"]["cpu_baseline"] = cpu_baseline_append(wl.ragged_append_causal())
+        if "next" in out:
+            out["next"]["bsr_sparse"]["cpu_baseline"] = cpu_baseline_bsr(wl.bsr_sparse())
+            out["next"]["page_append"]["cpu_baseline"] = \
+                cpu_baseline_page_append(wl.ragged_page_append())
     print(json.dumps(out), flush=True)
     return 0
 
