@@ -63,9 +63,21 @@ def normal_bits(rng: np.random.Generator, shape, dtype: str, chunk: int = 1 << 2
     return out.reshape(shape)
 
 
-def to_torch(bits: np.ndarray, dtype: str, device=None):
-    """Reinterpret uint16 storage bits as a torch fp16 / bf16 tensor."""
+def round_to_fp8_e4m3(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to OCP FP8 E4M3 codes (uint8), nearest-even, with
+    PyTorch's float8_e4m3fn conversion (input generation only; |x| <= 448)."""
     import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def to_torch(bits: np.ndarray, dtype: str, device=None):
+    """Reinterpret uint16 storage bits as a torch fp16 / bf16 tensor, or uint8
+    fp8 e4m3 codes as a torch float8_e4m3fn tensor."""
+    import torch
+    if dtype == "fp8_e4m3":
+        t = torch.from_numpy(np.ascontiguousarray(bits).view(np.uint8)).view(torch.float8_e4m3fn)
+        return t.to(device) if device is not None else t
 
     t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
     t = t.view(torch.bfloat16 if dtype == BF16 else torch.float16)
@@ -153,6 +165,8 @@ class Workload:
     causal: bool = False
     rope_theta: float = 0.0        # 0 -> no RoPE
     rope_llama31: Optional[tuple] = None  # (factor, low_freq_factor, high_freq_factor, old_ctx)
+    k_scale: float = 1.0           # fp8 K/V pages: value = scale * code value
+    v_scale: float = 1.0
     q_pos: Optional[np.ndarray] = None       # int32, per query token
     kv_pos_offset: Optional[np.ndarray] = None  # int32 [B]
     prefix: Optional[PagedKV] = None         # cascade: the shared prefix (one "request")
@@ -414,3 +428,42 @@ WORKLOADS_NEXT = {
     "bsr_sparse": bsr_sparse,
     "page_append": ragged_page_append,
 }
+
+
+# ----------------------------------------------------------------------------
+# fp8 (e4m3) KV pages
+# ----------------------------------------------------------------------------
+FP8 = "fp8_e4m3"
+
+
+def to_fp8_kv(rng: np.random.Generator, kv: PagedKV, scale: float) -> PagedKV:
+    """The same page table with fresh N(0, 1) K/V stored as e4m3 codes of
+    value / scale (so value ~ scale * code)."""
+    shape = kv.k_pages.shape
+    k = round_to_fp8_e4m3(rng.standard_normal(shape, dtype=np.float32) / np.float32(scale))
+    v = round_to_fp8_e4m3(rng.standard_normal(shape, dtype=np.float32) / np.float32(scale))
+    return PagedKV(kv.page_size, kv.num_kv_heads, kv.head_dim, FP8, kv.kv_len, kv.kv_indptr,
+                   kv.kv_indices, kv.kv_last_page_len, k, v)
+
+
+def small_decode_fp8(seed: int, kv_lens, page_size: int, num_qo_heads: int, num_kv_heads: int,
+                     dtype: str = BF16, k_scale: float = 0.25, v_scale: float = 0.5) -> Workload:
+    """A small decode batch whose K/V pages hold e4m3 codes (q in ``dtype``)."""
+    w = small_decode(seed, kv_lens, page_size, num_qo_heads, num_kv_heads, dtype=dtype)
+    rng = np.random.Generator(np.random.PCG64(seed + 7919))
+    w.kv = to_fp8_kv(rng, w.kv, 1.0)
+    w.k_scale, w.v_scale = float(k_scale), float(v_scale)
+    w.name = f"small_decode_fp8_s{seed}"
+    return w
+
+
+def batch_decode_fp8(seed: int = 1009) -> Workload:
+    """Batch paged decode with an fp8 KV cache: the batch decode shape (64
+    requests, kv_len U{512..4096}, GQA 32/8, d 128, page 16), q bf16, K/V e4m3
+    codes of N(0, 1) / 0.25 with k_scale = v_scale = 0.25."""
+    w = batch_decode_gqa(seed)
+    rng = np.random.Generator(np.random.PCG64(seed + 1))
+    w.kv = to_fp8_kv(rng, w.kv, 0.25)
+    w.k_scale = w.v_scale = 0.25
+    w.name = "batch_decode_fp8kv_b64_gqa32x8_d128_p16_kv512-4096"
+    return w

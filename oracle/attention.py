@@ -45,8 +45,24 @@ NEG_INF = -math.inf
 # ----------------------------------------------------------------------------
 # storage decoding (exact)
 # ----------------------------------------------------------------------------
+def fp8_e4m3_to_f64(codes) -> np.ndarray:
+    """Exact float64 values of OCP FP8 E4M3 codes (uint8): 1 sign bit, 4 exponent
+    bits with bias 7, 3 mantissa bits; exponent 0 is subnormal (m/8 * 2^-6);
+    S.1111.111 is NaN and there is no infinity (largest finite value 448)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    val = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    val = np.where((e == 15) & ((c & 0x7) == 7), np.nan, val)
+    return sign * val
+
+
 def storage_to_f64(bits: np.ndarray, dtype: str) -> np.ndarray:
-    """Exact float64 values of fp16 / bf16 bit patterns (uint16 arrays)."""
+    """Exact float64 values of fp16 / bf16 bit patterns (uint16 arrays) or of
+    fp8 e4m3 codes (uint8 arrays, dtype "fp8_e4m3")."""
+    if dtype == "fp8_e4m3":
+        return fp8_e4m3_to_f64(bits)
     b = np.asarray(bits, dtype=np.uint16)
     if dtype == "fp16":
         return b.view(np.float16).astype(np.float64)
@@ -209,14 +225,21 @@ def _group(num_qo_heads: int, num_kv_heads: int) -> int:
 def paged_decode(q, k_pages, v_pages, kv_indptr, kv_indices, kv_last_page_len, page_size: int,
                  dtype: str, num_kv_heads: int, sm_scale: Optional[float] = None,
                  rope_theta: float = 0.0, q_pos=None, kv_pos_offset=None,
-                 batch_ids: Optional[Iterable[int]] = None, rope_llama31=None):
+                 batch_ids: Optional[Iterable[int]] = None, rope_llama31=None,
+                 kv_dtype: Optional[str] = None, k_scale: float = 1.0, v_scale: float = 1.0):
     """Decode attention: one query token per request against its paged KV.
 
     q ``[B, Hq, d]`` (storage bits); returns float64 ``o [B, Hq, d]``,
     ``lse [B, Hq]``. Rows of requests not in ``batch_ids`` are NaN.
     With RoPE, q of request b sits at ``q_pos[b]`` (default kv_len_b - 1) and
     key t at ``kv_pos_offset[b] + t`` (default offset 0).
+
+    ``kv_dtype`` (default ``dtype``) is the storage of the pages; for
+    "fp8_e4m3" the keys are k_scale times their codes' values and the values
+    v_scale times theirs (one scale per tensor; the README page names FP8
+    attention, section 特性, without a scaling scheme).
     """
+    kvd = dtype if kv_dtype is None else kv_dtype
     B, Hq, d = q.shape
     G = _group(Hq, num_kv_heads)
     scale = (1.0 / math.sqrt(d)) if not sm_scale or sm_scale <= 0 else float(sm_scale)
@@ -224,8 +247,10 @@ def paged_decode(q, k_pages, v_pages, kv_indptr, kv_indices, kv_last_page_len, p
     lse = np.full((B, Hq), np.nan)
     for b in (range(B) if batch_ids is None else batch_ids):
         kv_len = request_kv_len(kv_indptr, kv_last_page_len, page_size, b)
-        K = storage_to_f64(walk_pages(k_pages, kv_indptr, kv_indices, kv_last_page_len, page_size, b), dtype)
-        V = storage_to_f64(walk_pages(v_pages, kv_indptr, kv_indices, kv_last_page_len, page_size, b), dtype)
+        K = float(k_scale) * storage_to_f64(
+            walk_pages(k_pages, kv_indptr, kv_indices, kv_last_page_len, page_size, b), kvd)
+        V = float(v_scale) * storage_to_f64(
+            walk_pages(v_pages, kv_indptr, kv_indices, kv_last_page_len, page_size, b), kvd)
         qb = storage_to_f64(q[b], dtype)
         if rope_theta:
             qp = (kv_len - 1) if q_pos is None else int(q_pos[b])
@@ -344,7 +369,8 @@ def decode_workload(w, batch_ids=None):
     return paged_decode(w.q, kv.k_pages, kv.v_pages, kv.kv_indptr, kv.kv_indices,
                         kv.kv_last_page_len, kv.page_size, w.dtype, w.num_kv_heads, w.sm_scale,
                         w.rope_theta, w.q_pos, w.kv_pos_offset, batch_ids,
-                        rope_llama31=w.rope_llama31)
+                        rope_llama31=w.rope_llama31, kv_dtype=kv.dtype,
+                        k_scale=w.k_scale, v_scale=w.v_scale)
 
 
 def append_workload(w, batch_ids=None, token_ids=None):

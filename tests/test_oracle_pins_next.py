@@ -250,3 +250,47 @@ def test_llama31_rotation_keeps_norms_and_relative_positions():
     b = (ora.rope_rotate(x, 5010, 5e5, L31) * ora.rope_rotate(y, 5003, 5e5, L31)).sum(-1)
     assert np.allclose(a, b, rtol=1e-9, atol=1e-9)
     assert np.array_equal(ora.rope_rotate(x, 0, 5e5, L31), x)
+
+
+# ----------------------------------------------------------------------------
+# fp8 (OCP e4m3) KV cache
+# ----------------------------------------------------------------------------
+def test_fp8_e4m3_constants():
+    # values fixed by the OCP FP8 E4M3 definition (bias 7, no infinity)
+    codes = [0x00, 0x01, 0x07, 0x08, 0x38, 0x3C, 0xB8, 0xC0, 0x7E, 0xFE, 0x77]
+    want = [0.0, 2.0 ** -9, 7 * 2.0 ** -9, 2.0 ** -6, 1.0, 1.5, -1.0, -2.0, 448.0, -448.0,
+            240.0]
+    got = ora.fp8_e4m3_to_f64(np.array(codes, np.uint8))
+    assert list(got) == want
+    assert np.isnan(ora.fp8_e4m3_to_f64(np.array([0x7F, 0xFF], np.uint8))).all()
+
+
+def test_fp8_e4m3_all_codes_match_torch():
+    # library special case: torch's float8_e4m3fn over all 256 codes
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = ora.fp8_e4m3_to_f64(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(got[~np.isnan(got)], ref[~np.isnan(ref)])
+
+
+def test_fp8_decode_equals_decode_on_the_same_values():
+    # fp8 pages with scales equal a 16-bit cache holding scale * value exactly
+    # (e4m3 values times a power of two are exact in bf16)
+    w = wl.small_decode_fp8(50, [1, 33, 300], 16, 8, 2, k_scale=0.25, v_scale=2.0)
+    o, lse = ora.decode_workload(w)
+    kv = w.kv
+    kb = wl.round_to_bf16_bits(
+        (0.25 * ora.fp8_e4m3_to_f64(kv.k_pages)).astype(np.float32))
+    vb = wl.round_to_bf16_bits((2.0 * ora.fp8_e4m3_to_f64(kv.v_pages)).astype(np.float32))
+    assert np.array_equal(ora.storage_to_f64(kb, "bf16"), 0.25 * ora.fp8_e4m3_to_f64(kv.k_pages))
+    o2, lse2 = ora.paged_decode(w.q, kb, vb, kv.kv_indptr, kv.kv_indices, kv.kv_last_page_len,
+                                16, "bf16", 2)
+    assert np.max(np.abs(o - o2)) < 1e-12 and np.max(np.abs(lse - lse2)) < 1e-12
+    # the scales act as stated: k_scale multiplies every logit, v_scale every output
+    w1 = wl.small_decode_fp8(50, [1, 33, 300], 16, 8, 2, k_scale=1.0, v_scale=1.0)
+    o1, _ = ora.decode_workload(w1)
+    w3 = wl.small_decode_fp8(50, [1, 33, 300], 16, 8, 2, k_scale=1.0, v_scale=3.0)
+    o3, _ = ora.decode_workload(w3)
+    assert np.max(np.abs(3.0 * o1 - o3)) < 1e-12
