@@ -67,6 +67,9 @@ class AbpParams(ctypes.Structure):
         ("rope_low_freq_factor", ctypes.c_float),
         ("rope_high_freq_factor", ctypes.c_float),
         ("rope_old_context_len", ctypes.c_float),
+        ("kv_fp8", ctypes.c_int32),
+        ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float),
     ]
 
 
@@ -271,16 +274,19 @@ def _torch_dtype(code: int):
 
 def make_params(num_qo_heads: int, num_kv_heads: int, head_dim: int, page_size: int, dtype,
                 out_dtype=None, sm_scale: float = 0.0, causal: bool = False,
-                rope_theta: float = 0.0, rope_llama31=None) -> AbpParams:
+                rope_theta: float = 0.0, rope_llama31=None, kv_fp8: bool = False,
+                k_scale: float = 1.0, v_scale: float = 1.0) -> AbpParams:
     """abp_params; ``rope_theta`` > 0 turns on the fused LLaMA RoPE, and
     ``rope_llama31 = (factor, low_freq_factor, high_freq_factor, old_context_len)``
-    (e.g. ``LLAMA31_ROPE``) its LLaMA 3.1 frequency scaling."""
+    (e.g. ``LLAMA31_ROPE``) its LLaMA 3.1 frequency scaling. ``kv_fp8`` selects
+    K/V pages of e4m3 codes worth ``k_scale`` / ``v_scale`` times their values."""
     q = _dtype_code(dtype)
     o = q if out_dtype is None else _dtype_code(out_dtype)
     rope = 0 if rope_theta <= 0 else (2 if rope_llama31 is not None else 1)
     l31 = tuple(float(x) for x in rope_llama31) if rope_llama31 is not None else (0.0,) * 4
     return AbpParams(num_qo_heads, num_kv_heads, head_dim, page_size, q, o, float(sm_scale),
-                     int(bool(causal)), rope, float(rope_theta), *l31)
+                     int(bool(causal)), rope, float(rope_theta), *l31, int(bool(kv_fp8)),
+                     float(k_scale), float(v_scale))
 
 
 def _ptr(t) -> Optional[int]:
@@ -582,8 +588,11 @@ def append_paged_kv_cache(k_new, v_new, append_indptr, k_pages, v_pages, kv_indp
     device int32) into the pages, at the last positions of each request of the
     page table (which must already cover them). ``nnz`` defaults to
     ``k_new.shape[0]``."""
+    torch = _torch()
     num_pages, page_size, hkv, d = k_pages.shape
-    params = make_params(hkv, hkv, d, page_size, k_pages.dtype)
+    fp8 = k_pages.dtype == torch.float8_e4m3fn
+    params = make_params(hkv, hkv, d, page_size, torch.bfloat16 if fp8 else k_pages.dtype,
+                         kv_fp8=fp8)
     batch = append_indptr.shape[0] - 1
     n = int(k_new.shape[0] if nnz is None else nnz)
     _check(load_library().abp_append_paged_kv(

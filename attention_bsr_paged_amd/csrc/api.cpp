@@ -147,8 +147,11 @@ void fill_args(const abp::Config& cfg, const abp::Layout& L, const abp_plan* pla
   a->token_stride = cfg.hkv * cfg.head_dim;
   a->page_stride = int64_t(cfg.page_size) * a->token_stride;
   a->out_dtype = cfg.out_dtype;
-  a->sm_scale = cfg.sm_scale;
-  a->sm_scale_log2 = cfg.sm_scale * 1.4426950408889634f;
+  // fp8 keys are k_scale times their codes: the logit scale absorbs k_scale
+  const float qk_scale = cfg.kv_fp8 ? cfg.sm_scale * cfg.k_scale : cfg.sm_scale;
+  a->sm_scale = qk_scale;
+  a->sm_scale_log2 = qk_scale * 1.4426950408889634f;
+  a->v_scale = cfg.kv_fp8 ? cfg.v_scale : 1.f;
   a->workers = plan->num_workers;
   char* ws = static_cast<char*>(dev_ws);
   a->plan = reinterpret_cast<const int32_t*>(ws);
@@ -476,6 +479,8 @@ int abp_append_paged_kv(const abp_params* params, int32_t batch, int64_t nnz, co
       return fail(ABP_ERR_INVALID_ARG, "num_kv_heads and page_size must be >= 1");
     if (params->qkv_dtype != ABP_F16 && params->qkv_dtype != ABP_BF16)
       return fail(ABP_ERR_UNSUPPORTED, "qkv_dtype must be ABP_F16 or ABP_BF16");
+    if (params->kv_fp8 != 0 && params->kv_fp8 != 1)
+      return fail(ABP_ERR_INVALID_ARG, "kv_fp8 must be 0 or 1");
     if (batch < 0 || nnz < 0) return fail(ABP_ERR_INVALID_ARG, "batch and nnz must be >= 0");
     if (nnz == 0 || batch == 0) return ABP_OK;
     if (nnz > (int64_t(1) << 31) - 1) return fail(ABP_ERR_INVALID_ARG, "nnz must be < 2^31");
@@ -486,7 +491,8 @@ int abp_append_paged_kv(const abp_params* params, int32_t batch, int64_t nnz, co
       return fail(ABP_ERR_INVALID_ARG, "K/V pointers must be 16-byte aligned");
     hipError_t e = abp::launch_page_append(
         k_new, v_new, append_indptr_d, k_pages, v_pages, kv_indptr_d, kv_indices_d,
-        kv_last_page_len_d, batch, nnz, params->num_kv_heads, params->page_size,
+        kv_last_page_len_d, batch, nnz, params->num_kv_heads * 128 * (params->kv_fp8 ? 1 : 2),
+        params->page_size,
         reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "page append launch");
     return ABP_OK;

@@ -36,6 +36,11 @@
 // never straddles a page: its page id is one scalar load (issued a chunk
 // ahead) and all K/V addresses are a uniform page base plus fixed per-lane
 // offsets. Other page sizes translate every token.
+// With an fp8 (OCP e4m3) KV cache a lane loads the same 8 elements as 8 bytes
+// and turns each byte pair into the 16-bit pair layout above with one gfx950
+// conversion (exact: every e4m3 value is a bf16 and an fp16 value), so the
+// arithmetic is the 16-bit path's; k_scale is folded into the logit scale and
+// v_scale into the final normalisation.
 // Chunks are double-buffered in registers. At the end of a segment the states
 // of the 4 token groups (and of the waves sharing a head) are merged, and the
 // tile's rows are written either as the final o / lse or as an fp32 partial
@@ -53,11 +58,43 @@ constexpr int kWaves = 4;
 constexpr int kSub = 16;             // tokens per sub-chunk (4 load instructions)
 constexpr float kRescaleLog2 = 8.f;  // lazy rescale threshold (log2 of the max p)
 
-template <int S>
-struct KVRegs {  // S sub-chunks of 16 tokens
-  uint4 k[4 * S];
-  uint4 v[4 * S];
+template <int S, bool KV8>
+struct KVRegs {  // S sub-chunks of 16 tokens; 8 elements per lane and row
+  using W = typename std::conditional<KV8, uint2, uint4>::type;
+  W k[4 * S];
+  W v[4 * S];
 };
+
+// two e4m3 codes (byte pair HI of w) as a 16-bit pair of the query's type
+template <typename T, bool HI>
+__device__ __forceinline__ uint32_t fp8x2(uint32_t w);
+template <>
+__device__ __forceinline__ uint32_t fp8x2<BF16, false>(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, false));
+}
+template <>
+__device__ __forceinline__ uint32_t fp8x2<BF16, true>(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, true));
+}
+template <>
+__device__ __forceinline__ uint32_t fp8x2<F16, false>(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.f, false));
+}
+template <>
+__device__ __forceinline__ uint32_t fp8x2<F16, true>(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.f, true));
+}
+
+// 8 elements of a row as 4 words of 16-bit pairs
+template <typename T>
+__device__ __forceinline__ uint4 widen8(const uint4& u) {
+  return u;
+}
+template <typename T>
+__device__ __forceinline__ uint4 widen8(const uint2& u) {
+  return make_uint4(fp8x2<T, false>(u.x), fp8x2<T, true>(u.x), fp8x2<T, false>(u.y),
+                    fp8x2<T, true>(u.y));
+}
 
 __device__ __forceinline__ uint32_t word(const uint4& u, int j) {
   return j == 0 ? u.x : j == 1 ? u.y : j == 2 ? u.z : u.w;
@@ -108,8 +145,12 @@ __device__ __forceinline__ void row16_sum_all(float* x) {
   for (int n = 0; n < N; ++n) x[n] += dpp<kDppMirror>(x[n]);
 }
 
-template <typename T, int G, bool ROPE, bool FASTPAGE, int S, int HT>
+template <typename T, int G, bool ROPE, bool FASTPAGE, int S, int HT, bool KV8>
 __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
+  static_assert(!(KV8 && ROPE), "fp8 KV pages are read without RoPE");
+  using KE = typename std::conditional<KV8, uint8_t, uint16_t>::type;  // K/V element
+  using KW = typename KVRegs<1, KV8>::W;  // 8 elements of a K/V row
+  constexpr uint32_t kEsz = sizeof(KE);
   constexpr int TW = kWaves / HT;     // waves per kv head (they split its keys)
   constexpr int kChunk = kSub * S;    // tokens per wave per buffered chunk
   constexpr int kStep = TW * kChunk;  // tokens per step of one head
@@ -130,8 +171,8 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
   const float cl2 = a.sm_scale_log2;
   const float thr = kRescaleLog2 / cl2;  // threshold in raw score units
 
-  const uint16_t* __restrict__ kp = static_cast<const uint16_t*>(a.k_pages);
-  const uint16_t* __restrict__ vp = static_cast<const uint16_t*>(a.v_pages);
+  const KE* __restrict__ kp = static_cast<const KE*>(a.k_pages);
+  const KE* __restrict__ vp = static_cast<const KE*>(a.v_pages);
   const int P = a.page_size;
   const int shift = a.page_shift;
   const int tstride = a.token_stride;
@@ -158,13 +199,13 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
   }
   // byte offset of this lane's K words from its V words (RoPE layout above)
   const uint32_t kdel = ROPE ? 8u * sub : 0u;
-  auto load_k = [&](const char* p) -> uint4 {
+  auto load_k = [&](const char* p) -> KW {
     if constexpr (ROPE) {
       const uint2 lo = *reinterpret_cast<const uint2*>(p);
       const uint2 hi = *reinterpret_cast<const uint2*>(p + 128);
       return make_uint4(lo.x, lo.y, hi.x, hi.y);
     } else {
-      return *reinterpret_cast<const uint4*>(p);
+      return *reinterpret_cast<const KW*>(p);
     }
   };
 
@@ -172,7 +213,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
   // path the end of a segment's chunk loop issues the loads of the next
   // segment (q, page ids, first chunk), so they are in flight while the
   // segment's states are merged and written.
-  KVRegs<S> A, B;
+  KVRegs<S, KV8> A, B;
   int pidA[S] = {}, pidB[S] = {};
   uint4 qn[G];
   bool pre = false;  // the loads of segment s were issued by segment s - 1
@@ -180,8 +221,10 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
     const uint16_t* qb = static_cast<const uint16_t*>(a.q) +
                          (int64_t(b) * a.num_qo_heads + int64_t(h) * G) * kD + sub * 8;
 #pragma unroll
-    for (int g = 0; g < G; ++g)
-      q[g] = load_k(reinterpret_cast<const char*>(qb + g * kD) - kdel);
+    for (int g = 0; g < G; ++g) {
+      if constexpr (ROPE) q[g] = load_k(reinterpret_cast<const char*>(qb + g * kD) - kdel);
+      else q[g] = *reinterpret_cast<const uint4*>(qb + g * kD);
+    }
   };
 
   for (int s = s_begin; s < s_end; ++s) {
@@ -230,7 +273,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
     // per-lane byte offsets of the 4 token rows of a sub-chunk (fast path)
     uint32_t lane_off[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lane_off[i] = uint32_t((4 * i + grp) * tstride + head_off) * 2u;
+    for (int i = 0; i < 4; ++i) lane_off[i] = uint32_t((4 * i + grp) * tstride + head_off) * kEsz;
 
     // fast path: one scalar page-table load per sub-chunk, issued a chunk ahead
     // of its use. A sub-chunk that starts past kv_end re-reads the chunk's
@@ -243,7 +286,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
       }
     };
 
-    auto load_chunk = [&](KVRegs<S>& X, int c, const int* pid) {
+    auto load_chunk = [&](KVRegs<S, KV8>& X, int c, const int* pid) {
 #pragma unroll
       for (int u = 0; u < S; ++u) {
         if constexpr (FASTPAGE) {
@@ -254,7 +297,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             X.k[4 * u + i] = load_k(kb + lane_off[i] - kdel);
-            X.v[4 * u + i] = *reinterpret_cast<const uint4*>(vb + lane_off[i]);
+            X.v[4 * u + i] = *reinterpret_cast<const KW*>(vb + lane_off[i]);
           }
         } else {
 #pragma unroll
@@ -271,14 +314,21 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
             const int64_t pg = a.kv_indices[ip0 + page];  // per-lane (vector) load
             const int64_t at = pg * a.page_stride + int64_t(off) * tstride + head_off;
             X.k[4 * u + i] = load_k(reinterpret_cast<const char*>(kp + at) - kdel);
-            X.v[4 * u + i] = *reinterpret_cast<const uint4*>(vp + at);
+            X.v[4 * u + i] = *reinterpret_cast<const KW*>(vp + at);
           }
         }
       }
     };
 
     // one 16-token sub-chunk starting at token c (registers k4[4], v4[4])
-    auto compute_sub = [&](const uint4* k4, const uint4* v4, int c) {
+    auto compute_sub = [&](const KW* k4w, const KW* v4w, int c) {
+      // 16-bit pairs of the 4 K and V rows (fp8 pages are widened here)
+      uint4 k4[4], v4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        k4[i] = widen8<T>(k4w[i]);
+        v4[i] = widen8<T>(v4w[i]);
+      }
       // scores of 4 tokens x G rows, summed over the 16 lanes of the token's row
       float sc[4 * G];
       float cs[ROPE ? 4 : 1], sn[ROPE ? 4 : 1];
@@ -373,7 +423,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
       }
     };
 
-    auto compute_chunk = [&](KVRegs<S>& X, int c) {
+    auto compute_chunk = [&](KVRegs<S, KV8>& X, int c) {
 #pragma unroll
       for (int u = 0; u < S; ++u) {
         if (u == 0 || c + kSub * u < kv_end) compute_sub(&X.k[4 * u], &X.v[4 * u], c + kSub * u);
@@ -449,9 +499,9 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
             const char* vb = reinterpret_cast<const char*>(vp + base);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const uint32_t off = uint32_t((4 * i + grp) * tstride + nhead) * 2u;
+              const uint32_t off = uint32_t((4 * i + grp) * tstride + nhead) * kEsz;
               A.k[4 * u + i] = load_k(kb + off - kdel);
-              A.v[4 * u + i] = *reinterpret_cast<const uint4*>(vb + off);
+              A.v[4 * u + i] = *reinterpret_cast<const KW*>(vb + off);
             }
           }
         }
@@ -487,7 +537,8 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
         float out[8];
         float lse = kNegInf;
         if (m[g] != kNegInf) {
-          const float inv = 1.f / l[g];
+          // fp8: the values are v_scale times their codes
+          const float inv = KV8 ? a.v_scale / l[g] : 1.f / l[g];
 #pragma unroll
           for (int e = 0; e < 8; ++e) out[e] = o[g][e] * inv;
           lse = m[g] * a.sm_scale + fast_log2(l[g]) * kLn2;
@@ -541,7 +592,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) out[e] = __builtin_fmaf(f, s_o[w][g][e0 + e], out[e]);
           }
-          const float inv = 1.f / L;
+          const float inv = KV8 ? a.v_scale / L : 1.f / L;
 #pragma unroll
           for (int e = 0; e < 8; ++e) out[e] *= inv;
           lse = M * a.sm_scale + fast_log2(L) * kLn2;
@@ -570,19 +621,20 @@ constexpr int sub_fast() {
   return (G <= 4 && !ROPE) ? 2 : 1;
 }
 
-template <typename T, int G, bool ROPE, int HT>
+template <typename T, int G, bool ROPE, int HT, bool KV8>
 hipError_t launch_r(const AttnArgs& a, hipStream_t s) {
   const bool fast = a.page_shift >= 4;  // power of two and a multiple of 16
   if (fast)
-    decode_kernel<T, G, ROPE, true, sub_fast<G, ROPE>(), HT><<<a.workers, 256, 0, s>>>(a);
+    decode_kernel<T, G, ROPE, true, sub_fast<G, ROPE>(), HT, KV8><<<a.workers, 256, 0, s>>>(a);
   else
-    decode_kernel<T, G, ROPE, false, 1, HT><<<a.workers, 256, 0, s>>>(a);
+    decode_kernel<T, G, ROPE, false, 1, HT, KV8><<<a.workers, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
 template <typename T, int G, int HT>
 hipError_t launch_h(const Config& cfg, const AttnArgs& a, hipStream_t s) {
-  return cfg.rope ? launch_r<T, G, true, HT>(a, s) : launch_r<T, G, false, HT>(a, s);
+  if (cfg.kv_fp8) return launch_r<T, G, false, HT, true>(a, s);
+  return cfg.rope ? launch_r<T, G, true, HT, false>(a, s) : launch_r<T, G, false, HT, false>(a, s);
 }
 
 template <typename T, int G>
@@ -607,16 +659,21 @@ template <typename T, int G, int HT>
 int occupancy_h(const Config& cfg, bool fast) {
   int n = 0;
   hipError_t e;
-  if (cfg.rope)
+  if (cfg.kv_fp8)
     e = fast ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                   &n, decode_kernel<T, G, true, true, sub_fast<G, true>(), HT>, 256, 0)
+                   &n, decode_kernel<T, G, false, true, sub_fast<G, false>(), HT, true>, 256, 0)
              : hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                   &n, decode_kernel<T, G, true, false, 1, HT>, 256, 0);
+                   &n, decode_kernel<T, G, false, false, 1, HT, true>, 256, 0);
+  else if (cfg.rope)
+    e = fast ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                   &n, decode_kernel<T, G, true, true, sub_fast<G, true>(), HT, false>, 256, 0)
+             : hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                   &n, decode_kernel<T, G, true, false, 1, HT, false>, 256, 0);
   else
     e = fast ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                   &n, decode_kernel<T, G, false, true, sub_fast<G, false>(), HT>, 256, 0)
+                   &n, decode_kernel<T, G, false, true, sub_fast<G, false>(), HT, false>, 256, 0)
              : hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                   &n, decode_kernel<T, G, false, false, 1, HT>, 256, 0);
+                   &n, decode_kernel<T, G, false, false, 1, HT, false>, 256, 0);
   return e == hipSuccess ? n : 0;
 }
 

@@ -33,6 +33,7 @@ struct AttnArgs {
   float sm_scale;
   float sm_scale_log2;           // sm_scale * log2(e)
   int32_t workers;
+  float v_scale;                 // fp8 V pages: value = v_scale * code value (else 1)
 };
 
 hipError_t launch_decode(const Config& cfg, const AttnArgs& a, hipStream_t stream);
@@ -54,7 +55,7 @@ hipError_t launch_plan_merge(const Config& cfg, const AttnArgs& a, int32_t grid,
 hipError_t launch_page_append(const void* k_new, const void* v_new, const int32_t* append_indptr,
                               void* k_pages, void* v_pages, const int32_t* kv_indptr,
                               const int32_t* kv_indices, const int32_t* kv_last_page_len,
-                              int32_t batch, int64_t nnz, int32_t hkv, int32_t page_size,
+                              int32_t batch, int64_t nnz, int32_t row_bytes, int32_t page_size,
                               hipStream_t stream);
 
 hipError_t launch_merge_two(const void* o_a, const float* lse_a, const void* o_b,

@@ -39,7 +39,7 @@ __global__ __launch_bounds__(64 * kWaves) void page_append_kernel(
   const int64_t t = int64_t(blockIdx.x) * kWaves + wave;
   if (t >= nnz) return;
   const int64_t src = t * row_chunks;
-  // pieces lane and lane + 64 of the row (row_chunks = 16 * Hkv)
+  // pieces lane and lane + 64 of the row (row_chunks = Hkv * 128 * element bytes / 16)
   const bool has0 = lane < row_chunks, has1 = lane + 64 < row_chunks;
   u32x4_t k0 = {}, v0 = {}, k1 = {}, v1 = {};
   if (has0) {
@@ -101,14 +101,14 @@ __global__ __launch_bounds__(64 * kWaves) void page_append_kernel(
 hipError_t launch_page_append(const void* k_new, const void* v_new, const int32_t* append_indptr,
                               void* k_pages, void* v_pages, const int32_t* kv_indptr,
                               const int32_t* kv_indices, const int32_t* kv_last_page_len,
-                              int32_t batch, int64_t nnz, int32_t hkv, int32_t page_size,
+                              int32_t batch, int64_t nnz, int32_t row_bytes, int32_t page_size,
                               hipStream_t stream) {
   if (nnz <= 0 || batch <= 0) return hipSuccess;
   const int64_t blocks = (nnz + kWaves - 1) / kWaves;
   page_append_kernel<<<dim3((unsigned)blocks), 64 * kWaves, 0, stream>>>(
       static_cast<const u32x4_t*>(k_new), static_cast<const u32x4_t*>(v_new), append_indptr,
       static_cast<u32x4_t*>(k_pages), static_cast<u32x4_t*>(v_pages), kv_indptr, kv_indices,
-      kv_last_page_len, batch, nnz, hkv * 16, page_size);
+      kv_last_page_len, batch, nnz, row_bytes / 16, page_size);
   return hipGetLastError();
 }
 

@@ -94,6 +94,20 @@ int check_params(int kind, const abp_params* p, Config* cfg, std::string* err) {
     *err = "causal must be 0 or 1";
     return ABP_ERR_INVALID_ARG;
   }
+  if (p->kv_fp8 != 0 && p->kv_fp8 != 1) {
+    *err = "kv_fp8 must be 0 or 1";
+    return ABP_ERR_INVALID_ARG;
+  }
+  if (p->kv_fp8 == 1) {
+    if (kind != ABP_KIND_DECODE || p->rope != 0) {
+      *err = "an fp8 KV cache is supported by decode without RoPE";
+      return ABP_ERR_UNSUPPORTED;
+    }
+    if (!(p->k_scale > 0.f) || !(p->v_scale > 0.f)) {
+      *err = "k_scale and v_scale must be > 0 with an fp8 KV cache";
+      return ABP_ERR_INVALID_ARG;
+    }
+  }
   if (kind == ABP_KIND_BSR && (p->causal != 0 || p->rope != 0)) {
     *err = "block-sparse attention takes its mask from the BSR pattern: causal and rope must be 0";
     return ABP_ERR_UNSUPPORTED;
@@ -110,6 +124,11 @@ int check_params(int kind, const abp_params* p, Config* cfg, std::string* err) {
   cfg->causal = kind == ABP_KIND_APPEND ? p->causal : 0;
   cfg->rope = p->rope;
   cfg->rope_theta = p->rope_theta;
+  if (p->kv_fp8 == 1) {
+    cfg->kv_fp8 = 1;
+    cfg->k_scale = p->k_scale;
+    cfg->v_scale = p->v_scale;
+  }
   if (p->rope == 2) {
     cfg->rope_factor = p->rope_factor;
     cfg->rope_low = p->rope_low_freq_factor;
@@ -203,7 +222,9 @@ uint64_t fingerprint(const Config& c, const Layout& L) {
       h *= 1099511628211ull;
     }
   };
-  uint32_t scale_bits, theta_bits, l31[4];
+  uint32_t scale_bits, theta_bits, l31[4], kvs[2];
+  memcpy(&kvs[0], &c.k_scale, 4);
+  memcpy(&kvs[1], &c.v_scale, 4);
   memcpy(&scale_bits, &c.sm_scale, 4);
   memcpy(&theta_bits, &c.rope_theta, 4);
   memcpy(&l31[0], &c.rope_factor, 4);
@@ -215,7 +236,7 @@ uint64_t fingerprint(const Config& c, const Layout& L) {
                           theta_bits,  L.workers,     L.max_tiles,    L.max_segs,   L.max_partials,
                           L.max_merges, L.tile_q,     L.tile_kv,      L.rows,       L.plan_ints,
                           (int64_t)L.partial_offset, l31[0], l31[1], l31[2], l31[3],
-                          L.off_aux, L.aux_cap};
+                          L.off_aux, L.aux_cap, c.kv_fp8, kvs[0], kvs[1]};
   for (int64_t v : vals) mix((uint64_t)v);
   return h;
 }

@@ -20,6 +20,9 @@ struct Config {
   float rope_theta = 0.f;
   // LLaMA 3.1 frequency scaling (rope == 2)
   float rope_factor = 1.f, rope_low = 1.f, rope_high = 1.f, rope_old_ctx = 1.f;
+  // fp8 e4m3 KV pages with per-tensor scales (decode only)
+  int32_t kv_fp8 = 0;
+  float k_scale = 1.f, v_scale = 1.f;
 };
 
 // Returns ABP_OK or an error status with `err` set.

@@ -2,7 +2,7 @@
 """Benchmark of paged BSR attention on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--part all|decode|append|single|skewed|cascade|copy|bsr|page_append]
+                    [--part all|decode|append|single|skewed|cascade|copy|bsr|page_append|fp8_decode]
 
 A step is one pass of the hot path over one batch of the batch paged decode
 workload (64 requests, GQA 32/8, head_dim 128, page 16, bf16, kv_len uniform on
@@ -22,7 +22,8 @@ U{1024..8192}, GQA 32/8, bf16) in TFLOP/s of visible (unmasked) work;
 ``configs`` holds the single-request, skewed-batch and cascade+RoPE decode
 workloads; ``next`` holds block-sparse attention (8192 x 8192, row blocks of
 64, column blocks of 16, a quarter of the blocks, TFLOP/s of unmasked work)
-and the page append of 16 requests' new tokens (TB/s of rows read + written).
+the page append of 16 requests' new tokens (TB/s of rows read + written) and
+the batch decode shape over an fp8 (e4m3) KV cache (TB/s of its one-byte K/V).
 ``cpu_baseline`` is the fp64 oracle on a bounded sample of the batch decode
 workload, on the host cores of the same machine (and of each other leg).
 
@@ -95,7 +96,8 @@ def decode_bytes(w, batch_ids=None) -> int:
     pages = int(sum(int(kv.kv_indptr[b + 1] - kv.kv_indptr[b]) for b in ids))
     n = len(ids)
     elt = 2
-    kvb = tokens * w.num_kv_heads * w.head_dim * 2 * elt
+    kv_elt = 1 if kv.dtype == "fp8_e4m3" else 2   # e4m3 pages: one byte per element
+    kvb = tokens * w.num_kv_heads * w.head_dim * 2 * kv_elt
     qo = 2 * n * w.num_qo_heads * w.head_dim * elt
     return kvb + qo + n * w.num_qo_heads * 4 + pages * 4 + (n + 1) * 4 + n * 4
 
@@ -177,14 +179,16 @@ def bench_decode(abp, wl, torch, dev, w, K, Wm, workers=0) -> dict:
     kv = w.kv
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float16
     by = decode_bytes(w)
-    k0 = wl.to_torch(kv.k_pages, w.dtype, dev)
-    v0 = wl.to_torch(kv.v_pages, w.dtype, dev)
+    k0 = wl.to_torch(kv.k_pages, kv.dtype, dev)
+    v0 = wl.to_torch(kv.v_pages, kv.dtype, dev)
     ks, copies = replicas(k0, torch, k0.nbytes + v0.nbytes)
     vs, _ = replicas(v0, torch, k0.nbytes + v0.nbytes)
     q = wl.to_torch(w.q, w.dtype, dev)
     i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
     indptr, indices, lpl = i32(kv.kv_indptr), i32(kv.kv_indices), i32(kv.kv_last_page_len)
-    params = abp.make_params(w.num_qo_heads, w.num_kv_heads, w.head_dim, kv.page_size, dt)
+    fp8 = kv.dtype == "fp8_e4m3"
+    params = abp.make_params(w.num_qo_heads, w.num_kv_heads, w.head_dim, kv.page_size, dt,
+                             kv_fp8=fp8, k_scale=w.k_scale, v_scale=w.v_scale)
     dec = abp.BatchDecode(params, max_batch=w.batch, num_workers=workers, device=dev)
     o = torch.empty(q.shape, dtype=dt, device=dev)
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
@@ -221,6 +225,7 @@ def bench_decode(abp, wl, torch, dev, w, K, Wm, workers=0) -> dict:
         "num_qo_heads": w.num_qo_heads,
         "num_kv_heads": w.num_kv_heads,
         "dtype": w.dtype,
+        "kv_dtype": kv.dtype,
         "workers": plan.num_workers,
         "segments": plan.num_segments,
         "merged_tiles": plan.num_merges,
@@ -624,7 +629,7 @@ def main(argv=None) -> int:
                     help="skip the single, skewed and cascade workloads")
     ap.add_argument("--part", default="all",
                     choices=["all", "decode", "append", "single", "skewed", "cascade", "copy",
-                             "bsr", "page_append"],
+                             "bsr", "page_append", "fp8_decode"],
                     help="one workload alone (profiling); 'all' is the benchmark line")
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -658,8 +663,9 @@ def main(argv=None) -> int:
     if part == "page_append":
         print(json.dumps(bench_page_append(abp, wl, torch, dev, K, Wm)), flush=True)
         return 0
-    if part in ("single", "skewed"):
-        w = wl.single_decode_mha() if part == "single" else wl.skewed_decode_gqa()
+    if part in ("single", "skewed", "fp8_decode"):
+        w = {"single": wl.single_decode_mha, "skewed": wl.skewed_decode_gqa,
+             "fp8_decode": wl.batch_decode_fp8}[part]()
         print(json.dumps(bench_decode(abp, wl, torch, dev, w, K, Wm, args.workers)), flush=True)
         return 0
 
@@ -728,7 +734,15 @@ def main(argv=None) -> int:
         out["next"] = {
             "bsr_sparse": bench_bsr(abp, wl, torch, dev, Kc, 5),
             "page_append": bench_page_append(abp, wl, torch, dev, Kc, 5),
+            "fp8_batch_decode": bench_decode(abp, wl, torch, dev, wl.batch_decode_fp8(), Kc, 5),
         }
+        f8 = out["next"]["fp8_batch_decode"]
+        f8["roofline"] = {"bound": "hbm", "achieved": round(f8["run_TBps"] * 1e3, 1),
+                          "peak": HBM_PEAK_TBS * 1e3, "unit": "GB/s",
+                          "frac": round(f8["run_TBps"] / HBM_PEAK_TBS, 4), "traffic": None,
+                          "kernel": "decode run, e4m3 K/V (decode_kernel + plan_merge_kernel)",
+                          "avg_launch_us": f8["run"]["avg_us"]}
+        f8["kv_tokens_per_s"] = round(f8["kv_tokens"] / (f8["run"]["avg_us"] * 1e-6), 1)
         out["copy_context"] = bench_copy(torch, dev, 20, 3)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_decode(w)
@@ -738,6 +752,8 @@ def main(argv=None) -> int:
             out["next"]["bsr_sparse"]["cpu_baseline"] = cpu_baseline_bsr(wl.bsr_sparse())
             out["next"]["page_append"]["cpu_baseline"] = \
                 cpu_baseline_page_append(wl.ragged_page_append())
+            out["next"]["fp8_batch_decode"]["cpu_baseline"] = \
+                cpu_baseline_decode(wl.batch_decode_fp8(), budget_s=4.0)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -53,7 +53,8 @@
  *  K is stored un-rotated; v is never rotated.
  *
  * Supported: head_dim 128; fp16 or bf16 q/k/v; num_qo_heads / num_kv_heads in
- * {1, 2, 4, 8, 16}; page_size >= 1; kv_len < 2^24; batch >= 0.
+ * {1, 2, 4, 8, 16}; page_size >= 1; kv_len < 2^24; batch >= 0. Decode (without
+ * RoPE) and page append also take an fp8 e4m3 KV cache (params.kv_fp8).
  *
  * Ownership and lifetime
  * ----------------------
@@ -121,6 +122,13 @@ typedef struct abp_params {
   float rope_low_freq_factor;   /* > 0 */
   float rope_high_freq_factor;  /* > rope_low_freq_factor */
   float rope_old_context_len;   /* > 0 */
+  /* KV cache storage: 0 = qkv_dtype; 1 = OCP FP8 E4M3 codes (one byte per element,
+     same page layout), whose values are k_scale (keys) or v_scale (values) times
+     the codes' values. Decode and page append only. The README page (section
+     特性) names FP8 attention without a scaling scheme: one scale per tensor. */
+  int32_t kv_fp8;
+  float k_scale;                /* > 0 when kv_fp8 = 1; ignored otherwise */
+  float v_scale;                /* > 0 when kv_fp8 = 1; ignored otherwise */
 } abp_params;
 
 /* Result of a plan: plain data, copied by value. Fields are informative; only
@@ -274,7 +282,8 @@ int abp_bsr_run(const abp_plan* plan, const abp_params* params, const void* q, c
  * row i of request b is logical token kv_len_b - append_len_b + i, stored in
  * slot t % page_size of page kv_indices[kv_indptr[b] + t / page_size]. Rows whose
  * position falls outside [0, kv_len_b) are skipped. Only num_kv_heads,
- * head_dim, page_size and qkv_dtype of params are used. One kernel on `stream`,
+ * head_dim, page_size, qkv_dtype and kv_fp8 of params are used (with kv_fp8 the
+ * rows and pages hold e4m3 codes, one byte per element). One kernel on `stream`,
  * no allocation, graph-capturable. All arrays are device memory; nnz = 0 is a
  * no-op. */
 int abp_append_paged_kv(const abp_params* params, int32_t batch, int64_t nnz, const void* k_new,

@@ -273,3 +273,23 @@ def test_page_append_argument_checks(lib):
     q = P(head_dim=64)
     assert lib.abp_append_paged_kv(ctypes.byref(q), 2, 4, *([None] * 8), None) == \
         abp.ABP_ERR_UNSUPPORTED
+
+
+def test_fp8_kv_params(lib):
+    ok = P(kv_fp8=True, k_scale=0.5, v_scale=2.0)
+    abp.abp_workspace_size(abp.ABP_KIND_DECODE, ok, 4, 0, 8)
+    for kind, bad, status in [
+        (abp.ABP_KIND_APPEND, P(kv_fp8=True), abp.ABP_ERR_UNSUPPORTED),
+        (abp.ABP_KIND_BSR, P(kv_fp8=True), abp.ABP_ERR_UNSUPPORTED),
+        (abp.ABP_KIND_DECODE, P(kv_fp8=True, rope_theta=1e4), abp.ABP_ERR_UNSUPPORTED),
+        (abp.ABP_KIND_DECODE, P(kv_fp8=True, k_scale=0.0), abp.ABP_ERR_INVALID_ARG),
+    ]:
+        with pytest.raises(abp.AbpError) as e:
+            abp.abp_workspace_size(kind, bad, 4, 16, 8)
+        assert e.value.status == status
+    # the scales enter the plan fingerprint: a run with other scales is refused
+    ws = _ws(0, ok, 2, 0, 8)
+    plan = abp.abp_plan_host(0, ok, 2, None, [0, 1, 2], [3, 4], 2, 0, 8, ws)
+    other = P(kv_fp8=True, k_scale=0.5, v_scale=1.0)
+    st_ = lib.abp_decode_run(ctypes.byref(plan), ctypes.byref(other), *([None] * 10), None, 0, None)
+    assert st_ == abp.ABP_ERR_PLAN_MISMATCH

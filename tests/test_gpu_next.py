@@ -170,3 +170,53 @@ def test_llama31_rope_decode_and_append():
     o_ref, l_ref = ora.append_workload(wa)
     o, l = run_append(wa, num_workers=7)
     assert_parity(o, l, o_ref, l_ref, "bf16", what="llama31 rope append")
+
+
+# ----------------------------------------------------------------------------
+# fp8 (e4m3) KV cache decode
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("P,G,hkv,dtype", [(16, 4, 8, "bf16"), (16, 1, 2, "bf16"),
+                                           (3, 4, 2, "fp16"), (16, 8, 4, "fp16"),
+                                           (256, 2, 8, "bf16"), (1, 8, 1, "bf16")])
+def test_fp8_decode_parity(P, G, hkv, dtype):
+    say(f"[case] fp8 decode P={P} G={G} hkv={hkv} q {dtype}")
+    w = wl.small_decode_fp8(700 + P + G + hkv, [0, 1, 16, 63, 700, 3000], P, G * hkv, hkv,
+                            dtype=dtype, k_scale=0.25, v_scale=0.5)
+    o_ref, l_ref = ora.decode_workload(w)
+    for W in (1, 29, 0):
+        o, l = run_decode(w, num_workers=W)
+        assert_parity(o, l, o_ref, l_ref, dtype, what=f"fp8 decode P{P} G{G} hkv{hkv} W{W}")
+
+
+def test_fp8_batch_decode_full_sampled():
+    """The fp8 batch decode shape (64 requests, kv U{512..4096}, GQA 32/8, page 16,
+    q bf16, e4m3 K/V with scales 0.25) in the default launch, sampled requests."""
+    w = wl.batch_decode_fp8()
+    say(f"[case] {w.name}")
+    o, l = run_decode(w)
+    ids = [0, 1, 31, 62, 63]
+    o_ref, l_ref = ora.decode_workload(w, batch_ids=ids)
+    assert_parity(o, l, o_ref, l_ref, "bf16", rows=ids, what="fp8 batch decode sampled")
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
+
+
+def test_page_append_fp8_bit_exact():
+    w = wl.page_append(720, [5, 300, 17, 1000], [5, 37, 1, 999], 16, 8)
+    rng = np.random.Generator(np.random.PCG64(721))
+    w.kv = wl.to_fp8_kv(rng, w.kv, 0.25)
+    w.k_new = wl.round_to_fp8_e4m3(rng.standard_normal(w.k_new.shape, dtype=np.float32) * 4)
+    w.v_new = wl.round_to_fp8_e4m3(rng.standard_normal(w.v_new.shape, dtype=np.float32) * 4)
+    kv = w.kv
+    kp_ref, vp_ref = ora.append_paged_kv(w.k_new, w.v_new, w.append_indptr, kv.k_pages,
+                                         kv.v_pages, kv.kv_indptr, kv.kv_indices,
+                                         kv.kv_last_page_len, 16)
+    import torch
+    dev = upload_kv(kv)
+    kn = wl.to_torch(w.k_new, "fp8_e4m3", "cuda")
+    vn = wl.to_torch(w.v_new, "fp8_e4m3", "cuda")
+    abp.append_paged_kv_cache(kn, vn, i32(w.append_indptr), dev["k"], dev["v"], dev["indptr"],
+                              dev["indices"], dev["lpl"])
+    torch.cuda.synchronize()
+    kp = dev["k"].cpu().view(torch.uint8).numpy()
+    vp = dev["v"].cpu().view(torch.uint8).numpy()
+    assert np.array_equal(kp, kp_ref) and np.array_equal(vp, vp_ref)
