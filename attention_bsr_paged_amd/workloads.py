@@ -165,6 +165,7 @@ class Workload:
     causal: bool = False
     rope_theta: float = 0.0        # 0 -> no RoPE
     rope_llama31: Optional[tuple] = None  # (factor, low_freq_factor, high_freq_factor, old_ctx)
+    rope_interleave: bool = False  # RoPE pairs (2j, 2j+1) instead of (j, j + d/2)
     k_scale: float = 1.0           # fp8 K/V pages: value = scale * code value
     v_scale: float = 1.0
     q_pos: Optional[np.ndarray] = None       # int32, per query token

@@ -136,13 +136,14 @@ def rope_inv_freq(head_dim: int, theta: float, llama31=None) -> np.ndarray:
     return out
 
 
-def rope_rotate(x: np.ndarray, pos, theta: float, llama31=None) -> np.ndarray:
+def rope_rotate(x: np.ndarray, pos, theta: float, llama31=None,
+                interleave: bool = False) -> np.ndarray:
     """Rotate the last axis of ``x`` (length d) at position(s) ``pos``.
 
-    Pair (j, j + d/2) is turned by the angle pos * f_j, f_j = theta^(-2j/d)
-    (optionally LLaMA 3.1 scaled, see ``rope_inv_freq``):
-        x'_j       = x_j cos a - x_{j+d/2} sin a
-        x'_{j+d/2} = x_{j+d/2} cos a + x_j sin a
+    Pair j is turned by the angle pos * f_j, f_j = theta^(-2j/d) (optionally
+    LLaMA 3.1 scaled, see ``rope_inv_freq``). Pair j is (j, j + d/2)
+    (rotate-half) or, with ``interleave``, the adjacent elements (2j, 2j + 1):
+        x'_a = x_a cos - x_b sin,   x'_b = x_b cos + x_a sin   for pair (a, b).
     ``pos`` broadcasts against ``x.shape[:-1]``.
     """
     x = np.asarray(x, dtype=np.float64)
@@ -150,6 +151,12 @@ def rope_rotate(x: np.ndarray, pos, theta: float, llama31=None) -> np.ndarray:
     h = d // 2
     ang = np.asarray(pos, dtype=np.float64)[..., None] * rope_inv_freq(d, theta, llama31)
     c, s = np.cos(ang), np.sin(ang)
+    if interleave:
+        a, b = x[..., 0::2], x[..., 1::2]
+        out = np.empty_like(x)
+        out[..., 0::2] = a * c - b * s
+        out[..., 1::2] = b * c + a * s
+        return out
     lo, hi = x[..., :h], x[..., h:]
     return np.concatenate([lo * c - hi * s, hi * c + lo * s], axis=-1)
 
@@ -226,7 +233,8 @@ def paged_decode(q, k_pages, v_pages, kv_indptr, kv_indices, kv_last_page_len, p
                  dtype: str, num_kv_heads: int, sm_scale: Optional[float] = None,
                  rope_theta: float = 0.0, q_pos=None, kv_pos_offset=None,
                  batch_ids: Optional[Iterable[int]] = None, rope_llama31=None,
-                 kv_dtype: Optional[str] = None, k_scale: float = 1.0, v_scale: float = 1.0):
+                 kv_dtype: Optional[str] = None, k_scale: float = 1.0, v_scale: float = 1.0,
+                 rope_interleave: bool = False):
     """Decode attention: one query token per request against its paged KV.
 
     q ``[B, Hq, d]`` (storage bits); returns float64 ``o [B, Hq, d]``,
@@ -255,8 +263,9 @@ def paged_decode(q, k_pages, v_pages, kv_indptr, kv_indices, kv_last_page_len, p
         if rope_theta:
             qp = (kv_len - 1) if q_pos is None else int(q_pos[b])
             off = 0 if kv_pos_offset is None else int(kv_pos_offset[b])
-            qb = rope_rotate(qb, qp, rope_theta, rope_llama31)
-            K = rope_rotate(K, (off + np.arange(kv_len))[:, None], rope_theta, rope_llama31)
+            qb = rope_rotate(qb, qp, rope_theta, rope_llama31, rope_interleave)
+            K = rope_rotate(K, (off + np.arange(kv_len))[:, None], rope_theta, rope_llama31,
+                            rope_interleave)
         for h in range(num_kv_heads):
             ob, lb = attend(qb[h * G:(h + 1) * G], K[:, h], V[:, h], scale)
             o[b, h * G:(h + 1) * G] = ob
@@ -268,7 +277,8 @@ def paged_append(q, qo_indptr, k_pages, v_pages, kv_indptr, kv_indices, kv_last_
                  page_size: int, dtype: str, num_kv_heads: int, causal: bool = True,
                  sm_scale: Optional[float] = None, rope_theta: float = 0.0, q_pos=None,
                  kv_pos_offset=None, batch_ids: Optional[Iterable[int]] = None,
-                 token_ids: Optional[Iterable[int]] = None, rope_llama31=None):
+                 token_ids: Optional[Iterable[int]] = None, rope_llama31=None,
+                 rope_interleave: bool = False):
     """Append / prefill attention for ragged queries ``q [sum qo, Hq, d]``.
 
     Query i (0-based within request b, qo_len_b queries) sees keys
@@ -300,8 +310,9 @@ def paged_append(q, qo_indptr, k_pages, v_pages, kv_indptr, kv_indices, kv_last_
         if rope_theta:
             qp = (kv_len - qo_len + ii) if q_pos is None else np.asarray(q_pos)[rows]
             off = 0 if kv_pos_offset is None else int(kv_pos_offset[b])
-            Q = rope_rotate(Q, np.asarray(qp)[:, None], rope_theta, rope_llama31)
-            K = rope_rotate(K, (off + np.arange(kv_len))[:, None], rope_theta, rope_llama31)
+            Q = rope_rotate(Q, np.asarray(qp)[:, None], rope_theta, rope_llama31, rope_interleave)
+            K = rope_rotate(K, (off + np.arange(kv_len))[:, None], rope_theta, rope_llama31,
+                            rope_interleave)
         vis = (kv_len - qo_len + ii + 1) if causal else np.full(len(rows), kv_len)
         for hq in range(Hq):
             h = hq // G
@@ -316,7 +327,7 @@ def cascade_decode(q, prefix_k, prefix_v, prefix_indptr, prefix_indices, prefix_
                    kv_last_page_len, page_size: int, dtype: str, num_kv_heads: int,
                    sm_scale: Optional[float] = None, rope_theta: float = 0.0, q_pos=None,
                    kv_pos_offset=None, batch_ids: Optional[Iterable[int]] = None,
-                   rope_llama31=None):
+                   rope_llama31=None, rope_interleave: bool = False):
     """Decode over a shared prefix (one BSR row in large pages) plus per-request
     suffixes (small pages), combined through their attention states.
 
@@ -343,12 +354,12 @@ def cascade_decode(q, prefix_k, prefix_v, prefix_indptr, prefix_indices, prefix_
     o_p, l_p = paged_decode(q, prefix_k, prefix_v, rep_indptr, rep_indices, rep_lpl,
                             prefix_page_size, dtype, num_kv_heads, sm_scale, rope_theta,
                             q_pos=q_pos, kv_pos_offset=np.zeros(B, np.int64), batch_ids=batch_ids,
-                            rope_llama31=rope_llama31)
+                            rope_llama31=rope_llama31, rope_interleave=rope_interleave)
     # suffix level
     o_s, l_s = paged_decode(q, k_pages, v_pages, kv_indptr, kv_indices, kv_last_page_len,
                             page_size, dtype, num_kv_heads, sm_scale, rope_theta, q_pos=q_pos,
                             kv_pos_offset=kv_pos_offset, batch_ids=batch_ids,
-                            rope_llama31=rope_llama31)
+                            rope_llama31=rope_llama31, rope_interleave=rope_interleave)
     ids = list(range(B) if batch_ids is None else batch_ids)
     o = np.full(q.shape, np.nan)
     lse = np.full(q.shape[:2], np.nan)
@@ -365,12 +376,13 @@ def decode_workload(w, batch_ids=None):
                               p.kv_last_page_len, p.page_size, kv.k_pages, kv.v_pages,
                               kv.kv_indptr, kv.kv_indices, kv.kv_last_page_len, kv.page_size,
                               w.dtype, w.num_kv_heads, w.sm_scale, w.rope_theta, w.q_pos,
-                              w.kv_pos_offset, batch_ids, rope_llama31=w.rope_llama31)
+                              w.kv_pos_offset, batch_ids, rope_llama31=w.rope_llama31,
+                              rope_interleave=w.rope_interleave)
     return paged_decode(w.q, kv.k_pages, kv.v_pages, kv.kv_indptr, kv.kv_indices,
                         kv.kv_last_page_len, kv.page_size, w.dtype, w.num_kv_heads, w.sm_scale,
                         w.rope_theta, w.q_pos, w.kv_pos_offset, batch_ids,
                         rope_llama31=w.rope_llama31, kv_dtype=kv.dtype,
-                        k_scale=w.k_scale, v_scale=w.v_scale)
+                        k_scale=w.k_scale, v_scale=w.v_scale, rope_interleave=w.rope_interleave)
 
 
 def append_workload(w, batch_ids=None, token_ids=None):
@@ -379,7 +391,7 @@ def append_workload(w, batch_ids=None, token_ids=None):
     return paged_append(w.q, w.qo_indptr, kv.k_pages, kv.v_pages, kv.kv_indptr, kv.kv_indices,
                         kv.kv_last_page_len, kv.page_size, w.dtype, w.num_kv_heads, w.causal,
                         w.sm_scale, w.rope_theta, w.q_pos, w.kv_pos_offset, batch_ids, token_ids,
-                        rope_llama31=w.rope_llama31)
+                        rope_llama31=w.rope_llama31, rope_interleave=w.rope_interleave)
 
 
 # ----------------------------------------------------------------------------

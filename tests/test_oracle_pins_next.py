@@ -294,3 +294,44 @@ def test_fp8_decode_equals_decode_on_the_same_values():
     w3 = wl.small_decode_fp8(50, [1, 33, 300], 16, 8, 2, k_scale=1.0, v_scale=3.0)
     o3, _ = ora.decode_workload(w3)
     assert np.max(np.abs(3.0 * o1 - o3)) < 1e-12
+
+
+# ----------------------------------------------------------------------------
+# interleaved (adjacent-pair) RoPE
+# ----------------------------------------------------------------------------
+def test_interleaved_rope_is_complex_multiplication():
+    # adjacent pairs as complex numbers, multiplied by exp(i * pos * f_j)
+    x = np.random.Generator(np.random.PCG64(60)).standard_normal((3, 128))
+    pos = np.array([0.0, 7.0, 5000.0])
+    f = ora.rope_inv_freq(128, 5e5)
+    z = (x[:, 0::2] + 1j * x[:, 1::2]) * np.exp(1j * pos[:, None] * f)
+    want = np.empty_like(x)
+    want[:, 0::2], want[:, 1::2] = z.real, z.imag
+    got = ora.rope_rotate(x, pos, 5e5, interleave=True)
+    assert np.max(np.abs(got - want)) < 1e-12
+
+
+def test_interleaved_rope_is_rotate_half_on_deinterleaved_elements():
+    # de-interleaving (evens first, then odds) maps adjacent pairs to (j, j + d/2)
+    x = np.random.Generator(np.random.PCG64(61)).standard_normal((4, 128))
+    perm = np.concatenate([np.arange(0, 128, 2), np.arange(1, 128, 2)])
+    for l31 in (None, (8.0, 1.0, 4.0, 8192.0)):
+        a = ora.rope_rotate(x, 321.0, 5e5, l31, interleave=True)
+        b = ora.rope_rotate(x[:, perm], 321.0, 5e5, l31)
+        assert np.max(np.abs(a[:, perm] - b)) < 1e-12
+
+
+def test_interleaved_rope_attention_equals_rotate_half_on_permuted_heads():
+    # attention with interleaved RoPE == rotate-half RoPE after the same
+    # element permutation of q and k (logits are permutation invariant)
+    w = wl.small_decode(62, [5, 90], 16, 4, 2, head_dim=128)
+    w.rope_theta = 5e5
+    w.rope_interleave = True
+    o1, l1 = ora.decode_workload(w)
+    perm = np.concatenate([np.arange(0, 128, 2), np.arange(1, 128, 2)])
+    w2 = wl.small_decode(62, [5, 90], 16, 4, 2, head_dim=128)
+    w2.rope_theta = 5e5
+    w2.q = w2.q[..., perm]
+    w2.kv.k_pages = w2.kv.k_pages[..., perm]
+    o2, l2 = ora.decode_workload(w2)
+    assert np.max(np.abs(o1 - o2)) < 1e-12 and np.max(np.abs(l1 - l2)) < 1e-12
