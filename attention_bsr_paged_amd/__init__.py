@@ -70,6 +70,7 @@ class AbpParams(ctypes.Structure):
         ("kv_fp8", ctypes.c_int32),
         ("k_scale", ctypes.c_float),
         ("v_scale", ctypes.c_float),
+        ("rope_interleave", ctypes.c_int32),
     ]
 
 
@@ -275,18 +276,20 @@ def _torch_dtype(code: int):
 def make_params(num_qo_heads: int, num_kv_heads: int, head_dim: int, page_size: int, dtype,
                 out_dtype=None, sm_scale: float = 0.0, causal: bool = False,
                 rope_theta: float = 0.0, rope_llama31=None, kv_fp8: bool = False,
-                k_scale: float = 1.0, v_scale: float = 1.0) -> AbpParams:
+                k_scale: float = 1.0, v_scale: float = 1.0,
+                rope_interleave: bool = False) -> AbpParams:
     """abp_params; ``rope_theta`` > 0 turns on the fused LLaMA RoPE, and
     ``rope_llama31 = (factor, low_freq_factor, high_freq_factor, old_context_len)``
     (e.g. ``LLAMA31_ROPE``) its LLaMA 3.1 frequency scaling. ``kv_fp8`` selects
-    K/V pages of e4m3 codes worth ``k_scale`` / ``v_scale`` times their values."""
+    K/V pages of e4m3 codes worth ``k_scale`` / ``v_scale`` times their values;
+    ``rope_interleave`` pairs adjacent elements (2j, 2j + 1) instead of (j, j + d/2)."""
     q = _dtype_code(dtype)
     o = q if out_dtype is None else _dtype_code(out_dtype)
     rope = 0 if rope_theta <= 0 else (2 if rope_llama31 is not None else 1)
     l31 = tuple(float(x) for x in rope_llama31) if rope_llama31 is not None else (0.0,) * 4
     return AbpParams(num_qo_heads, num_kv_heads, head_dim, page_size, q, o, float(sm_scale),
                      int(bool(causal)), rope, float(rope_theta), *l31, int(bool(kv_fp8)),
-                     float(k_scale), float(v_scale))
+                     float(k_scale), float(v_scale), int(bool(rope_interleave)))
 
 
 def _ptr(t) -> Optional[int]:
@@ -478,15 +481,17 @@ class CascadeDecode:
     def __init__(self, num_qo_heads: int, num_kv_heads: int, head_dim: int, prefix_page_size: int,
                  page_size: int, dtype, max_batch: int, sm_scale: float = 0.0,
                  rope_theta: float = 0.0, num_workers: int = 0, prefix_workers: int = 0,
-                 device=None):
+                 device=None, rope_llama31=None, rope_interleave: bool = False):
         torch = _torch()
         self.dtype = dtype
         self.pre_params = make_params(num_qo_heads, num_kv_heads, head_dim, prefix_page_size,
                                       dtype, out_dtype=torch.float32, sm_scale=sm_scale,
-                                      causal=False, rope_theta=rope_theta)
+                                      causal=False, rope_theta=rope_theta,
+                                      rope_llama31=rope_llama31, rope_interleave=rope_interleave)
         self.suf_params = make_params(num_qo_heads, num_kv_heads, head_dim, page_size, dtype,
                                       out_dtype=torch.float32, sm_scale=sm_scale,
-                                      rope_theta=rope_theta)
+                                      rope_theta=rope_theta, rope_llama31=rope_llama31,
+                                      rope_interleave=rope_interleave)
         self.prefix = BatchAppend(self.pre_params, max_batch=1, max_qo_tokens=max_batch,
                                   num_workers=prefix_workers, device=device)
         self.suffix = BatchDecode(self.suf_params, max_batch=max_batch, num_workers=num_workers,

@@ -108,6 +108,36 @@ __device__ __forceinline__ void rope_pair(uint4& lo, uint4& hi, uint4& lo_r, uin
   split8<T>(rb, hi, hi_r);
 }
 
+// Interleaved RoPE for q: `u` holds elements 2 j0 .. 2 j0 + 7, the adjacent
+// pairs j0 .. j0 + 3; rotated in place into (hi, lo) 16-bit parts.
+template <typename T>
+__device__ __forceinline__ void rope_adjacent8(uint4& u, uint4& u_lo, float pos, int j0,
+                                               const ABP_CONST_AS float* rope) {
+  float r[8];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float x = lo_f32<T>(word(u, w)), y = hi_f32<T>(word(u, w));
+    float sn, cs;
+    rope_sincos(pos, rope[2 * (j0 + w)], rope[2 * (j0 + w) + 1], &sn, &cs);
+    r[2 * w] = __builtin_fmaf(x, cs, -y * sn);
+    r[2 * w + 1] = __builtin_fmaf(y, cs, x * sn);
+  }
+  split8<T>(r, u, u_lo);
+}
+
+// Interleaved RoPE for a K row: word w of u is the adjacent pair w of the
+// lane's 4 pairs; out is in element order.
+template <typename T>
+__device__ __forceinline__ void rope_k_adjacent(const uint4& u, const float (&cs)[4],
+                                                const float (&sn)[4], float out[8]) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float x = lo_f32<T>(word(u, w)), y = hi_f32<T>(word(u, w));
+    out[2 * w] = __builtin_fmaf(-y, sn[w], x * cs[w]);
+    out[2 * w + 1] = __builtin_fmaf(x, sn[w], y * cs[w]);
+  }
+}
+
 // Rotate the 4 rotary pairs a lane holds for one K row: u has elements
 // 4c..4c+3 in words 0-1 and their partners 64+4c.. in words 2-3; cs / sn are
 // the cosines and sines of the pairs' angles. out[e] / out[4 + e] are the
@@ -146,8 +176,12 @@ constexpr int append_waves() {
   return ROPE ? 4 : 8;
 }
 
-template <typename T, int G, bool CAUSAL, bool ROPE, bool FASTPAGE>
+template <typename T, int G, bool CAUSAL, bool ROPE, bool FASTPAGE, bool RIL>
 __global__ __launch_bounds__(64 * append_waves<ROPE>(), 1) void append_kernel(AttnArgs a) {
+  static_assert(ROPE || !RIL, "interleaving is a RoPE layout");
+  // K elements a staging thread reads per row: rotate-half RoPE takes 4 + 4
+  // (both halves of its 4 pairs), everything else 8 consecutive ones
+  constexpr int kKPiece = (ROPE && !RIL) ? 4 : 8;
   constexpr int NW = append_waves<ROPE>();
   constexpr int kRows = 32 * NW;
   constexpr int TQ = kRows / G;
@@ -209,8 +243,9 @@ __global__ __launch_bounds__(64 * append_waves<ROPE>(), 1) void append_kernel(At
   // 16-byte chunk kc_chunk; V keys 16 vw + 4 v_kg + i (16-key group vw), chunk
   // v_chunk. With 8 waves, waves 0-3 stage K and waves 4-7 stage V.
   const int kc_chunk = tid & 15;
-  // RoPE: a thread stages both halves of the rotary pairs j = 4 kc_chunk + e
-  // (e < 4) of its K rows, so each angle is computed once. Its rows are 16
+  // RoPE: a thread stages both elements of the rotary pairs j = 4 kc_chunk + e
+  // (e < 4) of its K rows (rotate-half: elements j and j + 64; interleaved:
+  // 2j and 2j + 1, its plain 8 elements), so each angle is computed once. Its rows are 16
   // keys apart: the first row's angles are evaluated and the next follow by
   // angle addition with the rotation by 16 positions (c16, s16).
   float kfhi[ROPE ? 4 : 1], kflo[ROPE ? 4 : 1], c16[ROPE ? 4 : 1], s16[ROPE ? 4 : 1];
@@ -241,7 +276,7 @@ __global__ __launch_bounds__(64 * append_waves<ROPE>(), 1) void append_kernel(At
     const int kv_len = npg > 0 ? (npg - 1) * P + a.kv_last_page_len[b] : 0;
     const int kv_pos0 = (ROPE && a.kv_pos_offset) ? a.kv_pos_offset[b] : 0;
     // elements; with RoPE the first piece of the lane's pairs (see above)
-    const int koff_lane = k_row * tstride + h * kD + kc_chunk * (ROPE ? 4 : 8);
+    const int koff_lane = k_row * tstride + h * kD + kc_chunk * kKPiece;
     const int voff_lane = (4 * v_kg) * tstride + h * kD + v_chunk * 8;   // + i * tstride
 
     // ---- Q fragments (B operand of S^T = K Q^T) for this wave's 32 rows
@@ -262,8 +297,15 @@ __global__ __launch_bounds__(64 * append_waves<ROPE>(), 1) void append_kernel(At
       for (int kc = 0; kc < 4; ++kc) qf[nb][kc] = *reinterpret_cast<const uint4*>(qptr + kc * 32);
       if constexpr (ROPE) {
         const float qpos = a.q_pos ? (float)a.q_pos[q0 + tl] : (float)lim[nb];
-        rope_pair<T>(qf[nb][0], qf[nb][2], qfl[nb][0], qfl[nb][2], qpos, g16 * 8, rope);
-        rope_pair<T>(qf[nb][1], qf[nb][3], qfl[nb][1], qfl[nb][3], qpos, 32 + g16 * 8, rope);
+        if constexpr (RIL) {
+          // chunk kc holds elements g16 * 8 + 32 kc .. + 7: pairs 4 g16 + 16 kc ..
+#pragma unroll
+          for (int kc = 0; kc < 4; ++kc)
+            rope_adjacent8<T>(qf[nb][kc], qfl[nb][kc], qpos, 4 * g16 + 16 * kc, rope);
+        } else {
+          rope_pair<T>(qf[nb][0], qf[nb][2], qfl[nb][0], qfl[nb][2], qpos, g16 * 8, rope);
+          rope_pair<T>(qf[nb][1], qf[nb][3], qfl[nb][1], qfl[nb][3], qpos, 32 + g16 * 8, rope);
+        }
       }
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc)
@@ -289,7 +331,7 @@ __global__ __launch_bounds__(64 * append_waves<ROPE>(), 1) void append_kernel(At
       else return kreg[i];
     };
     auto kload = [&](const uint16_t* p) -> uint4 {
-      if constexpr (ROPE) {
+      if constexpr (ROPE && !RIL) {
         const uint2 lo = *reinterpret_cast<const uint2*>(p);
         const uint2 hi = *reinterpret_cast<const uint2*>(p + 64);
         return make_uint4(lo.x, lo.y, hi.x, hi.y);
@@ -334,7 +376,7 @@ __global__ __launch_bounds__(64 * append_waves<ROPE>(), 1) void append_kernel(At
             }
             const int64_t pg = a.kv_indices[ip0 + page];
             kreg[i] = kload(kp + pg * a.page_stride + (int64_t)off * tstride + h * kD +
-                            kc_chunk * (ROPE ? 4 : 8));
+                            kc_chunk * kKPiece);
           }
         }
         if (stage_v) {
@@ -379,14 +421,23 @@ __global__ __launch_bounds__(64 * append_waves<ROPE>(), 1) void append_kernel(At
               }
             }
             float kr[8];
-            rope_k_pairs<T>(kreg[i], cs, sn, kr);
             uint4 hi, lo;
-            split8<T>(kr, hi, lo);
-            const int at = (k_row + 16 * i) * kKStride + kc_chunk * 4;
-            *reinterpret_cast<uint2*>(&sK[at]) = make_uint2(hi.x, hi.y);
-            *reinterpret_cast<uint2*>(&sK[at + 64]) = make_uint2(hi.z, hi.w);
-            *reinterpret_cast<uint2*>(&sKlo[at]) = make_uint2(lo.x, lo.y);
-            *reinterpret_cast<uint2*>(&sKlo[at + 64]) = make_uint2(lo.z, lo.w);
+            if constexpr (RIL) {
+              // 8 consecutive elements, stored in place as one 16-byte piece
+              rope_k_adjacent<T>(kreg[i], cs, sn, kr);
+              split8<T>(kr, hi, lo);
+              const int at = (k_row + 16 * i) * kKStride + kc_chunk * 8;
+              *reinterpret_cast<uint4*>(&sK[at]) = hi;
+              *reinterpret_cast<uint4*>(&sKlo[at]) = lo;
+            } else {
+              rope_k_pairs<T>(kreg[i], cs, sn, kr);
+              split8<T>(kr, hi, lo);
+              const int at = (k_row + 16 * i) * kKStride + kc_chunk * 4;
+              *reinterpret_cast<uint2*>(&sK[at]) = make_uint2(hi.x, hi.y);
+              *reinterpret_cast<uint2*>(&sK[at + 64]) = make_uint2(hi.z, hi.w);
+              *reinterpret_cast<uint2*>(&sKlo[at]) = make_uint2(lo.x, lo.y);
+              *reinterpret_cast<uint2*>(&sKlo[at + 64]) = make_uint2(lo.z, lo.w);
+            }
           } else {
             const int at = (k_row + 16 * i) * kKStride + kc_chunk * 8;
             *reinterpret_cast<uint4*>(&sK[at]) = kreg[i];
@@ -658,20 +709,27 @@ __global__ __launch_bounds__(64 * append_waves<ROPE>(), 1) void append_kernel(At
   }
 }
 
-template <typename T, int G, bool CAUSAL, bool ROPE>
+template <typename T, int G, bool CAUSAL, bool ROPE, bool RIL>
 hipError_t launch_f(const AttnArgs& a, hipStream_t s) {
   if (a.page_shift >= 4)
-    append_kernel<T, G, CAUSAL, ROPE, true><<<a.workers, 64 * append_waves<ROPE>(), 0, s>>>(a);
+    append_kernel<T, G, CAUSAL, ROPE, true, RIL>
+        <<<a.workers, 64 * append_waves<ROPE>(), 0, s>>>(a);
   else
-    append_kernel<T, G, CAUSAL, ROPE, false><<<a.workers, 64 * append_waves<ROPE>(), 0, s>>>(a);
+    append_kernel<T, G, CAUSAL, ROPE, false, RIL>
+        <<<a.workers, 64 * append_waves<ROPE>(), 0, s>>>(a);
   return hipGetLastError();
+}
+
+template <typename T, int G, bool CAUSAL>
+hipError_t launch_c(const Config& cfg, const AttnArgs& a, hipStream_t s) {
+  if (!cfg.rope) return launch_f<T, G, CAUSAL, false, false>(a, s);
+  return cfg.rope_interleave ? launch_f<T, G, CAUSAL, true, true>(a, s)
+                             : launch_f<T, G, CAUSAL, true, false>(a, s);
 }
 
 template <typename T, int G>
 hipError_t launch_g(const Config& cfg, const AttnArgs& a, hipStream_t s) {
-  if (cfg.causal)
-    return cfg.rope ? launch_f<T, G, true, true>(a, s) : launch_f<T, G, true, false>(a, s);
-  return cfg.rope ? launch_f<T, G, false, true>(a, s) : launch_f<T, G, false, false>(a, s);
+  return cfg.causal ? launch_c<T, G, true>(cfg, a, s) : launch_c<T, G, false>(cfg, a, s);
 }
 
 template <typename T>
@@ -698,9 +756,11 @@ int append_blocks_per_cu(const Config& cfg) {
   // the tile shape is shared by all variants; RoPE ones are built for one per CU
   hipError_t e =
       cfg.rope ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                     &n, append_kernel<BF16, 4, true, true, true>, 64 * append_waves<true>(), 0)
+                     &n, append_kernel<BF16, 4, true, true, true, false>, 64 * append_waves<true>(),
+                     0)
                : hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                     &n, append_kernel<BF16, 4, true, false, true>, 64 * append_waves<false>(), 0);
+                     &n, append_kernel<BF16, 4, true, false, true, false>,
+                     64 * append_waves<false>(), 0);
   return e == hipSuccess && n > 0 ? n : 1;
 }
 

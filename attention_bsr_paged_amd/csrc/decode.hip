@@ -127,6 +127,27 @@ __device__ __forceinline__ void rope_rotate_pairs(const uint4& u, const float cs
   }
 }
 
+// Interleaved RoPE: word w of the lane's 8 elements is the adjacent pair
+// (2w, 2w + 1) of its 4 pairs; rotate each by cs[w] / sn[w] into fp32.
+template <typename T>
+__device__ __forceinline__ void rope_rotate_adjacent(const uint4& u, const float cs[4],
+                                                     const float sn[4], float out[8]) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t wd = w == 0 ? u.x : w == 1 ? u.y : w == 2 ? u.z : u.w;
+    const float x = lo_f32<T>(wd), y = hi_f32<T>(wd);
+    out[2 * w] = __builtin_fmaf(-y, sn[w], x * cs[w]);
+    out[2 * w + 1] = __builtin_fmaf(x, sn[w], y * cs[w]);
+  }
+}
+
+template <typename T, bool RIL>
+__device__ __forceinline__ void rope_rot(const uint4& u, const float cs[4], const float sn[4],
+                                         float out[8]) {
+  if constexpr (RIL) rope_rotate_adjacent<T>(u, cs, sn, out);
+  else rope_rotate_pairs<T>(u, cs, sn, out);
+}
+
 __device__ __forceinline__ void store8_dt(void* base, int64_t off, const float v[8], int dt) {
   if (dt == ABP_F32) store8<ABP_F32>(base, off, v);
   else if (dt == ABP_BF16) store8<ABP_BF16>(base, off, v);
@@ -145,9 +166,10 @@ __device__ __forceinline__ void row16_sum_all(float* x) {
   for (int n = 0; n < N; ++n) x[n] += dpp<kDppMirror>(x[n]);
 }
 
-template <typename T, int G, bool ROPE, bool FASTPAGE, int S, int HT, bool KV8>
+template <typename T, int G, bool ROPE, bool FASTPAGE, int S, int HT, bool KV8, bool RIL>
 __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
   static_assert(!(KV8 && ROPE), "fp8 KV pages are read without RoPE");
+  static_assert(ROPE || !RIL, "interleaving is a RoPE layout");
   using KE = typename std::conditional<KV8, uint8_t, uint16_t>::type;  // K/V element
   using KW = typename KVRegs<1, KV8>::W;  // 8 elements of a K/V row
   constexpr uint32_t kEsz = sizeof(KE);
@@ -183,7 +205,8 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
   __shared__ float s_l[TW > 1 ? kWaves : 1][G];
 
   // RoPE: frequencies (revolutions per position, split hi + lo) of this lane's
-  // 4 pairs j = 4 sub + e, and the rotation by 4 positions (c4, s4): a lane's
+  // 4 pairs j = 4 sub + e (rotate-half: elements 4 sub + e and 64 + 4 sub + e;
+  // interleaved: elements 8 sub + 2e and 8 sub + 2e + 1, the lane's plain 8), and the rotation by 4 positions (c4, s4): a lane's
   // tokens in a sub-chunk are 4 apart, so only the first one's angles are
   // evaluated and the next three follow by angle addition
   float fhi[ROPE ? 4 : 1], flo[ROPE ? 4 : 1], c4[ROPE ? 4 : 1], s4[ROPE ? 4 : 1];
@@ -198,9 +221,9 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
     }
   }
   // byte offset of this lane's K words from its V words (RoPE layout above)
-  const uint32_t kdel = ROPE ? 8u * sub : 0u;
+  const uint32_t kdel = (ROPE && !RIL) ? 8u * sub : 0u;
   auto load_k = [&](const char* p) -> KW {
-    if constexpr (ROPE) {
+    if constexpr (ROPE && !RIL) {
       const uint2 lo = *reinterpret_cast<const uint2*>(p);
       const uint2 hi = *reinterpret_cast<const uint2*>(p + 128);
       return make_uint4(lo.x, lo.y, hi.x, hi.y);
@@ -258,7 +281,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) rope_sincos((float)qpos, fhi[e], flo[e], &sn[e], &cs[e]);
 #pragma unroll
-      for (int g = 0; g < G; ++g) rope_rotate_pairs<T>(qv[g], cs, sn, qr[g]);
+      for (int g = 0; g < G; ++g) rope_rot<T, RIL>(qv[g], cs, sn, qr[g]);
     }
 
     float m[G], l[G], o[G][8];
@@ -349,7 +372,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
             }
           }
           float kr[8];
-          rope_rotate_pairs<T>(k4[i], cs, sn, kr);
+          rope_rot<T, RIL>(k4[i], cs, sn, kr);
 #pragma unroll
           for (int g = 0; g < G; ++g) {
             float acc = qr[g][0] * kr[0];
@@ -621,20 +644,23 @@ constexpr int sub_fast() {
   return (G <= 4 && !ROPE) ? 2 : 1;
 }
 
-template <typename T, int G, bool ROPE, int HT, bool KV8>
+template <typename T, int G, bool ROPE, int HT, bool KV8, bool RIL>
 hipError_t launch_r(const AttnArgs& a, hipStream_t s) {
   const bool fast = a.page_shift >= 4;  // power of two and a multiple of 16
   if (fast)
-    decode_kernel<T, G, ROPE, true, sub_fast<G, ROPE>(), HT, KV8><<<a.workers, 256, 0, s>>>(a);
+    decode_kernel<T, G, ROPE, true, sub_fast<G, ROPE>(), HT, KV8, RIL>
+        <<<a.workers, 256, 0, s>>>(a);
   else
-    decode_kernel<T, G, ROPE, false, 1, HT, KV8><<<a.workers, 256, 0, s>>>(a);
+    decode_kernel<T, G, ROPE, false, 1, HT, KV8, RIL><<<a.workers, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
 template <typename T, int G, int HT>
 hipError_t launch_h(const Config& cfg, const AttnArgs& a, hipStream_t s) {
-  if (cfg.kv_fp8) return launch_r<T, G, false, HT, true>(a, s);
-  return cfg.rope ? launch_r<T, G, true, HT, false>(a, s) : launch_r<T, G, false, HT, false>(a, s);
+  if (cfg.kv_fp8) return launch_r<T, G, false, HT, true, false>(a, s);
+  if (!cfg.rope) return launch_r<T, G, false, HT, false, false>(a, s);
+  return cfg.rope_interleave ? launch_r<T, G, true, HT, false, true>(a, s)
+                             : launch_r<T, G, true, HT, false, false>(a, s);
 }
 
 template <typename T, int G>
@@ -661,19 +687,19 @@ int occupancy_h(const Config& cfg, bool fast) {
   hipError_t e;
   if (cfg.kv_fp8)
     e = fast ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                   &n, decode_kernel<T, G, false, true, sub_fast<G, false>(), HT, true>, 256, 0)
+                   &n, decode_kernel<T, G, false, true, sub_fast<G, false>(), HT, true, false>, 256, 0)
              : hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                   &n, decode_kernel<T, G, false, false, 1, HT, true>, 256, 0);
+                   &n, decode_kernel<T, G, false, false, 1, HT, true, false>, 256, 0);
   else if (cfg.rope)
     e = fast ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                   &n, decode_kernel<T, G, true, true, sub_fast<G, true>(), HT, false>, 256, 0)
+                   &n, decode_kernel<T, G, true, true, sub_fast<G, true>(), HT, false, false>, 256, 0)
              : hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                   &n, decode_kernel<T, G, true, false, 1, HT, false>, 256, 0);
+                   &n, decode_kernel<T, G, true, false, 1, HT, false, false>, 256, 0);
   else
     e = fast ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                   &n, decode_kernel<T, G, false, true, sub_fast<G, false>(), HT, false>, 256, 0)
+                   &n, decode_kernel<T, G, false, true, sub_fast<G, false>(), HT, false, false>, 256, 0)
              : hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                   &n, decode_kernel<T, G, false, false, 1, HT, false>, 256, 0);
+                   &n, decode_kernel<T, G, false, false, 1, HT, false, false>, 256, 0);
   return e == hipSuccess ? n : 0;
 }
 

@@ -94,6 +94,10 @@ int check_params(int kind, const abp_params* p, Config* cfg, std::string* err) {
     *err = "causal must be 0 or 1";
     return ABP_ERR_INVALID_ARG;
   }
+  if (p->rope_interleave != 0 && p->rope_interleave != 1) {
+    *err = "rope_interleave must be 0 or 1";
+    return ABP_ERR_INVALID_ARG;
+  }
   if (p->kv_fp8 != 0 && p->kv_fp8 != 1) {
     *err = "kv_fp8 must be 0 or 1";
     return ABP_ERR_INVALID_ARG;
@@ -124,6 +128,7 @@ int check_params(int kind, const abp_params* p, Config* cfg, std::string* err) {
   cfg->causal = kind == ABP_KIND_APPEND ? p->causal : 0;
   cfg->rope = p->rope;
   cfg->rope_theta = p->rope_theta;
+  cfg->rope_interleave = p->rope != 0 ? p->rope_interleave : 0;
   if (p->kv_fp8 == 1) {
     cfg->kv_fp8 = 1;
     cfg->k_scale = p->k_scale;
@@ -236,7 +241,7 @@ uint64_t fingerprint(const Config& c, const Layout& L) {
                           theta_bits,  L.workers,     L.max_tiles,    L.max_segs,   L.max_partials,
                           L.max_merges, L.tile_q,     L.tile_kv,      L.rows,       L.plan_ints,
                           (int64_t)L.partial_offset, l31[0], l31[1], l31[2], l31[3],
-                          L.off_aux, L.aux_cap, c.kv_fp8, kvs[0], kvs[1]};
+                          L.off_aux, L.aux_cap, c.kv_fp8, kvs[0], kvs[1], c.rope_interleave};
   for (int64_t v : vals) mix((uint64_t)v);
   return h;
 }

@@ -23,6 +23,7 @@ struct Config {
   // fp8 e4m3 KV pages with per-tensor scales (decode only)
   int32_t kv_fp8 = 0;
   float k_scale = 1.f, v_scale = 1.f;
+  int32_t rope_interleave = 0;  // RoPE pairs (2j, 2j+1) instead of (j, j + d/2)
 };
 
 // Returns ABP_OK or an error status with `err` set.

@@ -40,7 +40,7 @@
  *  Causal append: query i (0-based) of a request with qo_len queries sees keys
  *  t <= kv_len - qo_len + i (aligned to the end of the KV).
  *  RoPE (params.rope = 1): LLaMA rotate-half; pair (j, j + head_dim/2) of q and k
- *  is turned by pos * f_j, f_j = rope_theta^(-2j/head_dim). params.rope = 2 uses
+ *  (or (2j, 2j + 1) with params.rope_interleave = 1) is turned by pos * f_j, f_j = rope_theta^(-2j/head_dim). params.rope = 2 uses
  *  the LLaMA 3.1 frequencies instead (README page, section 其他算子, lists
  *  LLaMA 3.1 RoPE; the rule is the one published with those models): with
  *  wavelength w = 2 pi / f_j, f_j is kept if w < old_context_len /
@@ -129,6 +129,9 @@ typedef struct abp_params {
   int32_t kv_fp8;
   float k_scale;                /* > 0 when kv_fp8 = 1; ignored otherwise */
   float v_scale;                /* > 0 when kv_fp8 = 1; ignored otherwise */
+  /* RoPE pairing (rope != 0): 0 = rotate-half pairs (j, j + head_dim/2);
+     1 = adjacent pairs (2j, 2j + 1), the complex-number form */
+  int32_t rope_interleave;
 } abp_params;
 
 /* Result of a plan: plain data, copied by value. Fields are informative; only

@@ -49,7 +49,7 @@ def run_decode(w, num_workers=0, out_dtype=None, dev=None, return_runner=False):
                              torch_dtype(w.dtype), out_dtype=out_dtype,
                              rope_theta=w.rope_theta, rope_llama31=w.rope_llama31,
                              kv_fp8=kv.dtype == "fp8_e4m3", k_scale=w.k_scale,
-                             v_scale=w.v_scale)
+                             v_scale=w.v_scale, rope_interleave=w.rope_interleave)
     dec = abp.BatchDecode(params, max_batch=max(w.batch, 1), num_workers=num_workers)
     dec.plan(kv.kv_indptr, kv.kv_last_page_len)
     o, lse = dec.run(q, dev["k"], dev["v"], dev["indptr"], dev["indices"], dev["lpl"],
@@ -68,7 +68,8 @@ def run_append(w, num_workers=0, out_dtype=None, dev=None):
     q = wl.to_torch(w.q, w.dtype, "cuda")
     params = abp.make_params(w.num_qo_heads, w.num_kv_heads, w.head_dim, kv.page_size,
                              torch_dtype(w.dtype), out_dtype=out_dtype, causal=w.causal,
-                             rope_theta=w.rope_theta, rope_llama31=w.rope_llama31)
+                             rope_theta=w.rope_theta, rope_llama31=w.rope_llama31,
+                             rope_interleave=w.rope_interleave)
     app = abp.BatchAppend(params, max_batch=max(w.batch, 1),
                           max_qo_tokens=max(int(w.qo_indptr[-1]), 1), num_workers=num_workers)
     app.plan(w.qo_indptr, kv.kv_indptr, kv.kv_last_page_len)

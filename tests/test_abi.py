@@ -293,3 +293,18 @@ def test_fp8_kv_params(lib):
     other = P(kv_fp8=True, k_scale=0.5, v_scale=1.0)
     st_ = lib.abp_decode_run(ctypes.byref(plan), ctypes.byref(other), *([None] * 10), None, 0, None)
     assert st_ == abp.ABP_ERR_PLAN_MISMATCH
+
+
+def test_rope_interleave_param(lib):
+    p = P(rope_theta=5e5, rope_interleave=True)
+    ws = _ws(0, p, 2, 0, 8)
+    plan = abp.abp_plan_host(0, p, 2, None, [0, 1, 2], [3, 4], 2, 0, 8, ws)
+    # the pairing enters the fingerprint: a run with the other pairing is refused
+    other = P(rope_theta=5e5)
+    st_ = lib.abp_decode_run(ctypes.byref(plan), ctypes.byref(other), *([None] * 10), None, 0, None)
+    assert st_ == abp.ABP_ERR_PLAN_MISMATCH
+    bad = P(rope_theta=5e5)
+    bad.rope_interleave = 2
+    with pytest.raises(abp.AbpError) as e:
+        abp.abp_workspace_size(0, bad, 2, 0, 8)
+    assert e.value.status == abp.ABP_ERR_INVALID_ARG

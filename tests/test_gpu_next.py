@@ -220,3 +220,60 @@ def test_page_append_fp8_bit_exact():
     kp = dev["k"].cpu().view(torch.uint8).numpy()
     vp = dev["v"].cpu().view(torch.uint8).numpy()
     assert np.array_equal(kp, kp_ref) and np.array_equal(vp, vp_ref)
+
+
+# ----------------------------------------------------------------------------
+# interleaved (adjacent-pair) RoPE
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("P,G,hkv", [(16, 4, 8), (3, 4, 2), (16, 8, 2), (16, 1, 4)])
+def test_interleaved_rope_decode(P, G, hkv):
+    w = wl.small_decode(800 + P + G, [1, 40, 700, 3000], P, G * hkv, hkv)
+    w.rope_theta = 500000.0
+    w.rope_interleave = True
+    rng = np.random.Generator(np.random.PCG64(801))
+    w.kv_pos_offset = rng.integers(0, 9000, size=w.batch).astype(np.int32)
+    w.q_pos = (w.kv_pos_offset + w.kv.kv_len - 1).astype(np.int32)
+    o_ref, l_ref = ora.decode_workload(w)
+    o, l = run_decode(w, num_workers=19)
+    assert_parity(o, l, o_ref, l_ref, "bf16", what=f"interleaved rope decode P{P} G{G}")
+
+
+@pytest.mark.parametrize("P,causal,l31", [(16, True, False), (3, True, True), (16, False, True)])
+def test_interleaved_rope_append(P, causal, l31):
+    w = wl.small_append(810 + P, [3, 90, 200], [50, 400, 900], P, 8, 2, causal=causal)
+    w.rope_theta = 500000.0
+    w.rope_interleave = True
+    w.rope_llama31 = abp.LLAMA31_ROPE if l31 else None
+    o_ref, l_ref = ora.append_workload(w)
+    o, l = run_append(w, num_workers=7)
+    assert_parity(o, l, o_ref, l_ref, "bf16", what=f"interleaved rope append P{P} c{int(causal)}")
+
+
+def test_interleaved_llama31_cascade():
+    """Cascade (prefix in pages of 256 + suffixes in pages of 16) with interleaved
+    LLaMA 3.1 RoPE: the append (prefix) and decode (suffix) kernels both rotate."""
+    import torch
+    rng = np.random.Generator(np.random.PCG64(820))
+    B, pre_len = 5, 700
+    prefix = wl.make_paged_kv(rng, np.array([pre_len]), 256, 2, 128, "bf16", extra_pages=1)
+    suf = rng.integers(1, 300, size=B)
+    kv = wl.make_paged_kv(rng, suf, 16, 2, 128, "bf16", extra_pages=3)
+    q = wl.normal_bits(rng, (B, 8, 128), "bf16")
+    w = wl.Workload("small_cascade_il", "cascade", 820, "bf16", 8, 2, 128, kv, q,
+                    rope_theta=500000.0, prefix=prefix, rope_llama31=abp.LLAMA31_ROPE,
+                    rope_interleave=True)
+    w.kv_pos_offset = np.full(B, pre_len, np.int32)
+    w.q_pos = (pre_len + suf - 1).astype(np.int32)
+    o_ref, l_ref = ora.decode_workload(w)
+    cas = abp.CascadeDecode(8, 2, 128, 256, 16, torch.bfloat16, max_batch=B,
+                            rope_theta=500000.0, num_workers=9, prefix_workers=4,
+                            rope_llama31=abp.LLAMA31_ROPE, rope_interleave=True)
+    cas.plan(B, prefix.kv_indptr, prefix.kv_last_page_len, kv.kv_indptr, kv.kv_last_page_len)
+    dp, ds = upload_kv(prefix), upload_kv(kv)
+    qt = wl.to_torch(q, "bf16", "cuda")
+    o, l = cas.run(qt, dp["k"], dp["v"], i32([0, B]), dp["indptr"], dp["indices"], dp["lpl"],
+                   ds["k"], ds["v"], ds["indptr"], ds["indices"], ds["lpl"],
+                   q_pos=i32(w.q_pos), kv_pos_offset=i32(w.kv_pos_offset))
+    torch.cuda.synchronize()
+    assert_parity(o.float().cpu().numpy(), l.cpu().numpy(), o_ref, l_ref, "bf16",
+                  what="interleaved llama31 cascade")
