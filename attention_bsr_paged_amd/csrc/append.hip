@@ -638,12 +638,21 @@ __global__ __launch_bounds__(64 * append_waves<ROPE>(), 1) void append_kernel(At
           O[md][1] = mfma<T>(va, pB[h][1], O[md][1]);
         }
       };
+      // matrix-core phases run at raised wave priority: the arbiter then
+      // issues one wave's products back to back while the other wave of the
+      // SIMD runs its softmax on the vector unit
+      __builtin_amdgcn_s_setprio(1);
       qk_half(0);
       qk_half(1);
+      __builtin_amdgcn_s_setprio(0);
       softmax_half(0);
+      __builtin_amdgcn_s_setprio(1);
       pv_half(0);
+      __builtin_amdgcn_s_setprio(0);
       softmax_half(1);
+      __builtin_amdgcn_s_setprio(1);
       pv_half(1);
+      __builtin_amdgcn_s_setprio(0);
       // the other stage held block j - 1, which every wave finished before the
       // barrier that ended the previous iteration
       if constexpr (ROPE) {
