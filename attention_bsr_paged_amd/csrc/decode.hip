@@ -723,11 +723,13 @@ int occupancy_t(const Config& cfg, bool fast) {
 }  // namespace
 
 hipError_t launch_decode(const Config& cfg, const AttnArgs& a, hipStream_t s) {
+  if (decode_mfma_applies(cfg)) return launch_decode_mfma(cfg, a, s);
   if (cfg.qkv_dtype == ABP_BF16) return launch_t<BF16>(cfg, a, s);
   return launch_t<F16>(cfg, a, s);
 }
 
 int decode_blocks_per_cu(const Config& cfg) {
+  if (decode_mfma_applies(cfg)) return decode_mfma_blocks_per_cu(cfg);
   const bool pow2 = (cfg.page_size & (cfg.page_size - 1)) == 0;
   const bool fast = pow2 && cfg.page_size >= 16;
   return cfg.qkv_dtype == ABP_BF16 ? occupancy_t<BF16>(cfg, fast) : occupancy_t<F16>(cfg, fast);

@@ -37,6 +37,11 @@ struct AttnArgs {
 };
 
 hipError_t launch_decode(const Config& cfg, const AttnArgs& a, hipStream_t stream);
+// matrix-core decode (16-bit K/V, no RoPE, power-of-two pages >= 16, kv heads a
+// multiple of 4, group 4 or 8); launch_decode picks it when it applies
+bool decode_mfma_applies(const Config& cfg);
+hipError_t launch_decode_mfma(const Config& cfg, const AttnArgs& a, hipStream_t stream);
+int decode_mfma_blocks_per_cu(const Config& cfg);
 // resident 256-thread workgroups per compute unit of the kernel chosen for cfg
 int decode_blocks_per_cu(const Config& cfg);
 int append_blocks_per_cu(const Config& cfg);

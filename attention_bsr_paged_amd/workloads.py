@@ -198,15 +198,17 @@ def single_decode_mha(seed: int = 1001) -> Workload:
     return Workload("single_decode_mha32_d128_fp16_kv2048_p16", "decode", seed, FP16, Hq, Hkv, d, kv, q)
 
 
-def batch_decode_gqa(seed: int = 1002, batch: int = 64, lo: int = 512, hi: int = 4096) -> Workload:
+def batch_decode_gqa(seed: int = 1002, batch: int = 64, lo: int = 512, hi: int = 4096,
+                     num_qo_heads: int = 32) -> Workload:
     """Batch paged decode: 64 requests, GQA 32/8, d 128, page 16, bf16,
-    kv_len uniform on the integers [512, 4096]."""
+    kv_len uniform on the integers [512, 4096] (``num_qo_heads`` = 64 gives
+    groups of 8 over the same cache)."""
     rng = np.random.Generator(np.random.PCG64(seed))
-    Hq, Hkv, d, P = 32, 8, 128, 16
+    Hq, Hkv, d, P = num_qo_heads, 8, 128, 16
     kv_len = rng.integers(lo, hi, size=batch, endpoint=True)
     q = normal_bits(rng, (batch, Hq, d), BF16)
     kv = make_paged_kv(rng, kv_len, P, Hkv, d, BF16)
-    return Workload(f"batch_decode_b{batch}_gqa32x8_d128_bf16_p16_kv{lo}-{hi}", "decode", seed,
+    return Workload(f"batch_decode_b{batch}_gqa{Hq}x8_d128_bf16_p16_kv{lo}-{hi}", "decode", seed,
                     BF16, Hq, Hkv, d, kv, q)
 
 

@@ -53,7 +53,7 @@ FLUSH_BYTES = 2 * 2 ** 30       # K/V replicas rotated per step (>> 256 MB MALL)
 # Counter readings (FETCH_SIZE / WRITE_SIZE) of the decode run and of a plain
 # copy, recorded by rocprofv3; valid only while the kernel sources hash the same.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_run_batch_decode_traffic.txt")
-DECODE_SOURCES = ["decode.hip", "merge.hip", "common.h", "kernels.h", "layout.h"]
+DECODE_SOURCES = ["decode.hip", "decode_mfma.hip", "merge.hip", "common.h", "kernels.h", "layout.h"]
 
 
 PAGE_APPEND_TRAFFIC_FILE = os.path.join(ROOT, "profiles",
@@ -629,7 +629,7 @@ def main(argv=None) -> int:
                     help="skip the single, skewed and cascade workloads")
     ap.add_argument("--part", default="all",
                     choices=["all", "decode", "append", "single", "skewed", "cascade", "copy",
-                             "bsr", "page_append", "fp8_decode"],
+                             "bsr", "page_append", "fp8_decode", "g8_decode"],
                     help="one workload alone (profiling); 'all' is the benchmark line")
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -663,9 +663,10 @@ def main(argv=None) -> int:
     if part == "page_append":
         print(json.dumps(bench_page_append(abp, wl, torch, dev, K, Wm)), flush=True)
         return 0
-    if part in ("single", "skewed", "fp8_decode"):
+    if part in ("single", "skewed", "fp8_decode", "g8_decode"):
         w = {"single": wl.single_decode_mha, "skewed": wl.skewed_decode_gqa,
-             "fp8_decode": wl.batch_decode_fp8}[part]()
+             "fp8_decode": wl.batch_decode_fp8,
+             "g8_decode": lambda: wl.batch_decode_gqa(num_qo_heads=64)}[part]()
         print(json.dumps(bench_decode(abp, wl, torch, dev, w, K, Wm, args.workers)), flush=True)
         return 0
 

@@ -324,3 +324,17 @@ def test_empty_batches():
                    torch.tensor([5, 9], dtype=torch.int32, device="cuda"))
     torch.cuda.synchronize()
     assert o.shape == (0, 8, 128)
+
+
+@pytest.mark.parametrize("P,G,hkv,dtype", [(16, 4, 4, "bf16"), (32, 8, 4, "fp16"),
+                                           (64, 4, 8, "bf16"), (16, 8, 12, "bf16")])
+def test_matrix_core_decode_chunk_edges(P, G, hkv, dtype):
+    """The matrix-core decode path (power-of-two pages >= 16, kv heads a multiple
+    of 4, G 4 or 8): lengths around its 16-token tiles and 32-token chunks, odd
+    and even chunk counts per segment, and segments cut at every worker count."""
+    lens = [0, 1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 97, 128, 1000]
+    w = wl.small_decode(900 + P + G + hkv, lens, P, G * hkv, hkv, dtype=dtype)
+    o_ref, l_ref = ora.decode_workload(w)
+    for W in (1, 7, 64, 0):
+        o, l = run_decode(w, num_workers=W)
+        assert_parity(o, l, o_ref, l_ref, dtype, what=f"mfma decode P{P} G{G} hkv{hkv} W{W}")
