@@ -236,7 +236,7 @@ def bench_decode(abp, wl, torch, dev, w, K, Wm, workers=0) -> dict:
 # ----------------------------------------------------------------------------
 # causal append
 # ----------------------------------------------------------------------------
-def bench_append(abp, wl, torch, dev, K, Wm) -> dict:
+def bench_append(abp, wl, torch, dev, K, Wm, workers=0) -> dict:
     w = wl.ragged_append_causal()
     kv = w.kv
     flops = append_flops(w)
@@ -251,7 +251,7 @@ def bench_append(abp, wl, torch, dev, K, Wm) -> dict:
     params = abp.make_params(w.num_qo_heads, w.num_kv_heads, w.head_dim, kv.page_size,
                              torch.bfloat16, causal=True)
     app = abp.BatchAppend(params, max_batch=w.batch, max_qo_tokens=int(w.qo_indptr[-1]),
-                          device=dev)
+                          num_workers=workers, device=dev)
     o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
     s = torch.cuda.current_stream(dev)
@@ -649,7 +649,7 @@ def main(argv=None) -> int:
     K, Wm = args.steps, args.warmup
     part = args.part
     if part == "append":
-        print(json.dumps(bench_append(abp, wl, torch, dev, K, Wm)), flush=True)
+        print(json.dumps(bench_append(abp, wl, torch, dev, K, Wm, args.workers)), flush=True)
         return 0
     if part == "copy":
         print(json.dumps(bench_copy(torch, dev, K, Wm)), flush=True)
@@ -716,7 +716,7 @@ def main(argv=None) -> int:
             "unit": "GB/s",
             "frac": round(achieved / (HBM_PEAK_TBS * 1e3), 4),
             "traffic": tr["traffic_bytes_per_run"] if tr else None,
-            "kernel": "decode run: decode_kernel + plan_merge_kernel (one run() call)",
+            "kernel": "decode run: decode_mfma_kernel + plan_merge_kernel (one run() call)",
             "avg_launch_us": d["run"]["avg_us"],
             "median_us": d["run"]["median_us"],
             "p10_us": d["run"]["p10_us"],
