@@ -27,7 +27,7 @@ __all__ = [
     "ABP_KIND_DECODE", "ABP_KIND_APPEND", "ABP_KIND_BSR", "AbpParams", "AbpPlan", "AbpError",
     "load_library", "library_path", "make_params", "BatchDecode", "BatchAppend", "merge_state",
     "merge_states", "single_decode_with_kv_cache", "CascadeDecode", "BlockSparseAttention",
-    "append_paged_kv_cache", "LLAMA31_ROPE", "EXPORTED_SYMBOLS",
+    "append_paged_kv_cache", "LLAMA31_ROPE", "EXPORTED_SYMBOLS", "AbpPodPlan", "PodAttention",
 ]
 
 ABP_OK = 0
@@ -97,6 +97,21 @@ class AbpPlan(ctypes.Structure):
     ]
 
 
+class AbpPodPlan(ctypes.Structure):
+    _fields_ = [
+        ("decode", AbpPlan),
+        ("append", AbpPlan),
+        ("num_groups", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("decode_host_offset", ctypes.c_uint64),
+        ("append_host_offset", ctypes.c_uint64),
+        ("decode_dev_offset", ctypes.c_uint64),
+        ("append_dev_offset", ctypes.c_uint64),
+        ("decode_dev_bytes", ctypes.c_uint64),
+        ("append_dev_bytes", ctypes.c_uint64),
+    ]
+
+
 class AbpError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"abp status {status}: {message}")
@@ -114,6 +129,7 @@ _i64 = ctypes.c_int64
 _int = ctypes.c_int
 _pp = ctypes.POINTER(AbpParams)
 _planp = ctypes.POINTER(AbpPlan)
+_podp = ctypes.POINTER(AbpPodPlan)
 
 # name -> (restype, argtypes); the order and types follow include/abp.h
 _SIGNATURES = {
@@ -134,6 +150,13 @@ _SIGNATURES = {
                             _planp]),
     "abp_bsr_run": (_int, [_planp, _pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "abp_append_paged_kv": (_int, [_pp, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "abp_pod_workspace_size": (_int, [_pp, _i32, _i32, _i32, _i32, _szp, _szp]),
+    "abp_pod_plan_host": (_int, [_pp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32,
+                                 _i32, _i32, _vp, _sz, _podp]),
+    "abp_pod_plan": (_int, [_pp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                            _i32, _vp, _sz, _vp, _sz, _vp, _podp]),
+    "abp_pod_run": (_int, [_podp, _pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                           _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "abp_merge_state": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _int, _int, _vp]),
     "abp_merge_states": (_int, [_vp, _vp, _i32, _i64, _i32, _int, _int, _vp, _vp, _vp]),
 }
@@ -215,6 +238,38 @@ def abp_bsr_plan_host(params: AbpParams, M: int, N: int, R: int, indptr, max_row
                                             max_row_blocks, max_M, num_workers,
                                             host_ws.ctypes.data, host_ws.nbytes,
                                             ctypes.byref(plan)))
+    return plan
+
+
+def abp_pod_workspace_size(params: AbpParams, max_decode_batch: int, max_append_batch: int,
+                           max_qo_tokens: int, num_groups: int):
+    h, d = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(load_library().abp_pod_workspace_size(ctypes.byref(params), max_decode_batch,
+                                                 max_append_batch, max_qo_tokens, num_groups,
+                                                 ctypes.byref(h), ctypes.byref(d)))
+    return h.value, d.value
+
+
+def _pod_arrays(d_kv_indptr, d_kv_last_page_len, qo_indptr, a_kv_indptr, a_kv_last_page_len):
+    arrs = [np.zeros(1, np.int32) if a is None else _i32_host(a)
+            for a in (d_kv_indptr, d_kv_last_page_len, qo_indptr, a_kv_indptr,
+                      a_kv_last_page_len)]
+    return arrs, len(arrs[0]) - 1, len(arrs[3]) - 1
+
+
+def abp_pod_plan_host(params: AbpParams, d_kv_indptr, d_kv_last_page_len, qo_indptr,
+                      a_kv_indptr, a_kv_last_page_len, max_decode_batch: int,
+                      max_append_batch: int, max_qo_tokens: int, num_groups: int,
+                      decode_groups: int, host_ws: np.ndarray) -> AbpPodPlan:
+    """Host-only mixed-batch planner into a numpy buffer (for inspection and tests)."""
+    plan = AbpPodPlan()
+    arrs, nd, na = _pod_arrays(d_kv_indptr, d_kv_last_page_len, qo_indptr, a_kv_indptr,
+                               a_kv_last_page_len)
+    _check(load_library().abp_pod_plan_host(
+        ctypes.byref(params), nd, arrs[0].ctypes.data, arrs[1].ctypes.data, na,
+        arrs[2].ctypes.data, arrs[3].ctypes.data, arrs[4].ctypes.data, max_decode_batch,
+        max_append_batch, max_qo_tokens, num_groups, decode_groups, host_ws.ctypes.data,
+        host_ws.nbytes, ctypes.byref(plan)))
     return plan
 
 
@@ -415,6 +470,75 @@ class BatchAppend(_Planned):
             _ptr(kv_last_page_len), _ptr(q_pos), _ptr(kv_pos_offset), _ptr(o), _ptr(lse),
             self.dev_ws.data_ptr(), self.dev_ws.numel(), _stream(stream)))
         return o, lse
+
+
+class PodAttention:
+    """Mixed batches: decode requests and append (prefill) requests of one paged
+    KV cache, planned together and run in one launch whose workgroups take the
+    decode or the append role (split chosen by the planner, or decode_groups)."""
+
+    def __init__(self, params: AbpParams, max_decode_batch: int, max_append_batch: int,
+                 max_qo_tokens: int, num_groups: int = 0, device=None):
+        torch = _torch()
+        self.params = params
+        self.max_decode_batch = int(max_decode_batch)
+        self.max_append_batch = int(max_append_batch)
+        self.max_qo_tokens = int(max_qo_tokens)
+        self.num_groups = int(num_groups)
+        self.device = torch.device("cuda", torch.cuda.current_device()) if device is None \
+            else torch.device(device)
+        with torch.cuda.device(self.device):
+            hb, db = abp_pod_workspace_size(params, self.max_decode_batch, self.max_append_batch,
+                                            self.max_qo_tokens, self.num_groups)
+            self.host_ws = torch.empty(max(hb, 16), dtype=torch.uint8, pin_memory=True)
+            self.dev_ws = torch.empty(max(db, 256), dtype=torch.uint8, device=self.device)
+        self.plan_struct = None
+        self._upload_done = None
+
+    def plan(self, d_kv_indptr, d_kv_last_page_len, qo_indptr, a_kv_indptr, a_kv_last_page_len,
+             decode_groups: int = 0, stream=None) -> AbpPodPlan:
+        torch = _torch()
+        arrs, nd, na = _pod_arrays(d_kv_indptr, d_kv_last_page_len, qo_indptr, a_kv_indptr,
+                                   a_kv_last_page_len)
+        if self._upload_done is not None:
+            self._upload_done.synchronize()
+        plan = AbpPodPlan()
+        _check(load_library().abp_pod_plan(
+            ctypes.byref(self.params), nd, arrs[0].ctypes.data, arrs[1].ctypes.data, na,
+            arrs[2].ctypes.data, arrs[3].ctypes.data, arrs[4].ctypes.data, self.max_decode_batch,
+            self.max_append_batch, self.max_qo_tokens, self.num_groups, int(decode_groups),
+            self.host_ws.data_ptr(), self.host_ws.numel(), self.dev_ws.data_ptr(),
+            self.dev_ws.numel(), _stream(stream), ctypes.byref(plan)))
+        ev = torch.cuda.Event()
+        ev.record(stream if stream is not None else torch.cuda.current_stream(self.device))
+        self._upload_done = ev
+        self.plan_struct = plan
+        return plan
+
+    def run(self, q_decode, q_append, k_pages, v_pages, d_kv_indptr, d_kv_indices,
+            d_kv_last_page_len, qo_indptr, a_kv_indptr, a_kv_indices, a_kv_last_page_len,
+            o_decode=None, lse_decode=None, o_append=None, lse_append=None, stream=None):
+        torch = _torch()
+        if self.plan_struct is None:
+            raise RuntimeError("plan() must be called before run()")
+        odt = _torch_dtype(self.params.out_dtype)
+        if q_decode is not None and o_decode is None:
+            o_decode = torch.empty(q_decode.shape, dtype=odt, device=q_decode.device)
+        if q_decode is not None and lse_decode is None:
+            lse_decode = torch.empty(q_decode.shape[:2], dtype=torch.float32,
+                                     device=q_decode.device)
+        if q_append is not None and o_append is None:
+            o_append = torch.empty(q_append.shape, dtype=odt, device=q_append.device)
+        if q_append is not None and lse_append is None:
+            lse_append = torch.empty(q_append.shape[:2], dtype=torch.float32,
+                                     device=q_append.device)
+        _check(load_library().abp_pod_run(
+            ctypes.byref(self.plan_struct), ctypes.byref(self.params), _ptr(q_decode),
+            _ptr(q_append), _ptr(k_pages), _ptr(v_pages), _ptr(d_kv_indptr), _ptr(d_kv_indices),
+            _ptr(d_kv_last_page_len), _ptr(qo_indptr), _ptr(a_kv_indptr), _ptr(a_kv_indices),
+            _ptr(a_kv_last_page_len), _ptr(o_decode), _ptr(lse_decode), _ptr(o_append),
+            _ptr(lse_append), self.dev_ws.data_ptr(), self.dev_ws.numel(), _stream(stream)))
+        return (o_decode, lse_decode), (o_append, lse_append)
 
 
 def merge_state(o_a, lse_a, o_b, lse_b, out_dtype=None, o_out=None, lse_out=None, stream=None):

@@ -7,6 +7,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 
@@ -157,6 +158,156 @@ void fill_args(const abp::Config& cfg, const abp::Layout& L, const abp_plan* pla
   a->plan = reinterpret_cast<const int32_t*>(ws);
   a->o_part = reinterpret_cast<float*>(ws + L.partial_offset);
   a->lse_part = a->o_part + int64_t(L.max_partials) * L.rows * cfg.head_dim;
+}
+
+}  // namespace
+
+// Mixed decode + append batches: worker split and the two sub-plans.
+namespace {
+
+// Decode bandwidth of the matrix-core decode kernel against the compute units
+// it runs on (one 4-wave worker each), measured on MI355X with the batch decode
+// workload (64 requests, GQA 32/8, page 16, bf16): 2.65, 4.23, 5.14 and 5.20
+// TB/s on 64, 128, 192 and 256 compute units.
+double pod_decode_bw(double cus) {
+  static const double x[] = {0.0, 64.0, 128.0, 192.0, 256.0};
+  static const double y[] = {0.0, 2.65e12, 4.23e12, 5.14e12, 5.20e12};
+  if (cus >= x[4]) return y[4];
+  int i = 0;
+  while (cus > x[i + 1]) ++i;
+  return y[i] + (y[i + 1] - y[i]) * (cus - x[i]) / (x[i + 1] - x[i]);
+}
+// append kernel throughput per compute unit (ragged causal append, bf16)
+constexpr double kPodAppendFlopPerCu = 3.0e12;
+
+int64_t pod_kv_len(const int32_t* indptr, const int32_t* lpl, int32_t b, int32_t page) {
+  const int64_t n = int64_t(indptr[b + 1]) - indptr[b];
+  return n > 0 ? (n - 1) * page + lpl[b] : 0;
+}
+
+// Decode workgroups of a launch of `groups` workgroups.
+int32_t pod_split(const abp::Config& cfg, int32_t groups, int32_t decode_batch,
+                  const int32_t* d_indptr, const int32_t* d_lpl, int32_t append_batch,
+                  const int32_t* qo, const int32_t* a_indptr, const int32_t* a_lpl,
+                  int32_t decode_groups) {
+  const bool has_d = decode_batch > 0, has_a = append_batch > 0;
+  if (!has_d) return 0;
+  if (!has_a) return groups;
+  if (decode_groups > 0) return std::min(std::max(decode_groups, 1), groups - 1);
+  double bytes = 0.0;  // decode K/V bytes
+  for (int32_t b = 0; b < decode_batch; ++b)
+    bytes += double(pod_kv_len(d_indptr, d_lpl, b, cfg.page_size)) * cfg.hkv * cfg.head_dim * 4.0;
+  double pairs = 0.0;  // visible (query, key) pairs of the append part
+  for (int32_t b = 0; b < append_batch; ++b) {
+    const double q = std::max(0, qo[b + 1] - qo[b]);
+    const double k = double(pod_kv_len(a_indptr, a_lpl, b, cfg.page_size));
+    pairs += cfg.causal ? q * std::max(0.0, k - q) + q * (q + 1) / 2 : q * k;
+  }
+  const double flop = 4.0 * cfg.head_dim * cfg.hq * pairs;
+  // whole XCD rows (8 workgroups) when the launch is large enough
+  const int32_t step = groups >= 16 ? 8 : 1;
+  int32_t best = step, lo = step, hi = groups - step;
+  double best_t = 1e300;
+  for (int32_t g = lo; g <= hi; g += step) {
+    const double t = std::max(bytes / pod_decode_bw(g), flop / (kPodAppendFlopPerCu * (groups - g)));
+    if (t < best_t) {
+      best_t = t;
+      best = g;
+    }
+  }
+  return best;
+}
+
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct PodLayout {
+  abp_params pd, pa;  // decode part (causal off) and append part
+  abp::Config cd, ca;
+  abp::Layout ld, la;
+  size_t d_host = 0, a_host = 0, d_dev = 0, a_dev = 0;  // region sizes
+  int32_t groups = 0;
+};
+
+int pod_layout(const abp_params* params, int32_t max_d, int32_t max_a, int32_t max_qo,
+               int32_t groups, PodLayout* P) {
+  if (!params) return fail(ABP_ERR_INVALID_ARG, "params is NULL");
+  if (max_d < 0 || max_a < 0) return fail(ABP_ERR_INVALID_ARG, "negative maximum batch");
+  if (groups <= 0) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    int st = num_cus(dev, &groups);
+    if (st != ABP_OK) return st;
+  }
+  if (groups < 2) return fail(ABP_ERR_INVALID_ARG, "a mixed launch needs at least 2 workgroups");
+  P->groups = groups;
+  P->pd = *params;
+  P->pd.causal = 0;
+  P->pa = *params;
+  std::string err;
+  int st = abp::check_params(ABP_KIND_APPEND, &P->pa, &P->ca, &err);
+  if (st != ABP_OK) return fail(st, err);
+  st = abp::check_params(ABP_KIND_DECODE, &P->pd, &P->cd, &err);
+  if (st != ABP_OK) return fail(st, err);
+  if (!abp::pod_applies(P->cd))
+    return fail(ABP_ERR_UNSUPPORTED,
+                "mixed batches need 16-bit K/V, no RoPE, power-of-two pages >= 16, kv heads a "
+                "multiple of 4 and group 4 or 8");
+  if (max_d > 0) {
+    st = resolve_layout(ABP_KIND_DECODE, &P->pd, max_d, 0, groups, &P->cd, &P->ld);
+    if (st != ABP_OK) return st;
+    P->d_host = round256(P->ld.plan_bytes);
+    P->d_dev = round256(P->ld.dev_bytes);
+  }
+  if (max_a > 0) {
+    st = resolve_layout(ABP_KIND_APPEND, &P->pa, max_a, max_qo, groups, &P->ca, &P->la);
+    if (st != ABP_OK) return st;
+    P->a_host = round256(P->la.plan_bytes);
+    P->a_dev = round256(P->la.dev_bytes);
+  }
+  return ABP_OK;
+}
+
+int pod_plan_host(const abp_params* params, int32_t decode_batch, const int32_t* d_indptr,
+                  const int32_t* d_lpl, int32_t append_batch, const int32_t* qo,
+                  const int32_t* a_indptr, const int32_t* a_lpl, int32_t max_d, int32_t max_a,
+                  int32_t max_qo, int32_t groups, int32_t decode_groups, void* host_ws,
+                  size_t host_bytes, abp_pod_plan_t* plan, PodLayout* P) {
+  if (!plan) return fail(ABP_ERR_INVALID_ARG, "plan is NULL");
+  if (!host_ws) return fail(ABP_ERR_INVALID_ARG, "host workspace is NULL");
+  if (decode_batch < 0 || append_batch < 0) return fail(ABP_ERR_INVALID_ARG, "negative batch");
+  if (decode_batch > max_d) return fail(ABP_ERR_WORKSPACE_TOO_SMALL, "decode_batch > max_decode_batch");
+  if (append_batch > max_a) return fail(ABP_ERR_WORKSPACE_TOO_SMALL, "append_batch > max_append_batch");
+  if ((decode_batch > 0 && (!d_indptr || !d_lpl)) ||
+      (append_batch > 0 && (!qo || !a_indptr || !a_lpl)))
+    return fail(ABP_ERR_INVALID_ARG, "NULL index array");
+  int st = pod_layout(params, max_d, max_a, max_qo, groups, P);
+  if (st != ABP_OK) return st;
+  if (host_bytes < P->d_host + P->a_host)
+    return fail(ABP_ERR_WORKSPACE_TOO_SMALL, "host workspace smaller than abp_pod_workspace_size");
+  memset(plan, 0, sizeof(*plan));
+  plan->num_groups = P->groups;
+  plan->decode_host_offset = 0;
+  plan->append_host_offset = P->d_host;
+  plan->decode_dev_offset = 0;
+  plan->append_dev_offset = P->d_dev;
+  plan->decode_dev_bytes = P->d_dev;
+  plan->append_dev_bytes = P->a_dev;
+  const int32_t wd = pod_split(P->ca, P->groups, decode_batch, d_indptr, d_lpl, append_batch, qo,
+                               a_indptr, a_lpl, decode_groups);
+  const int32_t wa = append_batch > 0 ? P->groups - wd : 0;
+  char* hw = static_cast<char*>(host_ws);
+  if (wd > 0) {
+    st = do_plan(ABP_KIND_DECODE, &P->pd, decode_batch, nullptr, d_indptr, d_lpl, max_d, 0, wd,
+                 hw + plan->decode_host_offset, P->d_host, &plan->decode, &P->cd, &P->ld);
+    if (st != ABP_OK) return st;
+  }
+  if (wa > 0) {
+    st = do_plan(ABP_KIND_APPEND, &P->pa, append_batch, qo, a_indptr, a_lpl, max_a, max_qo, wa,
+                 hw + plan->append_host_offset, P->a_host, &plan->append, &P->ca, &P->la);
+    if (st != ABP_OK) return st;
+  }
+  return ABP_OK;
 }
 
 }  // namespace
@@ -495,6 +646,162 @@ int abp_append_paged_kv(const abp_params* params, int32_t batch, int64_t nnz, co
         params->page_size,
         reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "page append launch");
+    return ABP_OK;
+  } catch (...) {
+    return fail(ABP_ERR_HIP, "exception");
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Mixed decode + append batches (one launch, workgroups split by role)
+
+int abp_pod_workspace_size(const abp_params* params, int32_t max_decode_batch,
+                           int32_t max_append_batch, int32_t max_qo_tokens, int32_t num_groups,
+                           size_t* host_bytes, size_t* dev_bytes) {
+  try {
+    if (!host_bytes || !dev_bytes) return fail(ABP_ERR_INVALID_ARG, "NULL output");
+    PodLayout P;
+    int st = pod_layout(params, max_decode_batch, max_append_batch, max_qo_tokens, num_groups, &P);
+    if (st != ABP_OK) return st;
+    *host_bytes = P.d_host + P.a_host;
+    *dev_bytes = P.d_dev + P.a_dev;
+    return ABP_OK;
+  } catch (...) {
+    return fail(ABP_ERR_INVALID_ARG, "exception");
+  }
+}
+
+int abp_pod_plan_host(const abp_params* params, int32_t decode_batch,
+                      const int32_t* d_kv_indptr_h, const int32_t* d_kv_last_page_len_h,
+                      int32_t append_batch, const int32_t* qo_indptr_h,
+                      const int32_t* a_kv_indptr_h, const int32_t* a_kv_last_page_len_h,
+                      int32_t max_decode_batch, int32_t max_append_batch, int32_t max_qo_tokens,
+                      int32_t num_groups, int32_t decode_groups, void* host_ws,
+                      size_t host_bytes, abp_pod_plan_t* plan) {
+  try {
+    PodLayout P;
+    return pod_plan_host(params, decode_batch, d_kv_indptr_h, d_kv_last_page_len_h, append_batch,
+                         qo_indptr_h, a_kv_indptr_h, a_kv_last_page_len_h, max_decode_batch,
+                         max_append_batch, max_qo_tokens, num_groups, decode_groups, host_ws,
+                         host_bytes, plan, &P);
+  } catch (...) {
+    return fail(ABP_ERR_INVALID_ARG, "exception");
+  }
+}
+
+int abp_pod_plan(const abp_params* params, int32_t decode_batch, const int32_t* d_kv_indptr_h,
+                 const int32_t* d_kv_last_page_len_h, int32_t append_batch,
+                 const int32_t* qo_indptr_h, const int32_t* a_kv_indptr_h,
+                 const int32_t* a_kv_last_page_len_h, int32_t max_decode_batch,
+                 int32_t max_append_batch, int32_t max_qo_tokens, int32_t num_groups,
+                 int32_t decode_groups, void* host_ws, size_t host_bytes, void* dev_ws,
+                 size_t dev_bytes, abp_stream_t stream, abp_pod_plan_t* plan) {
+  try {
+    PodLayout P;
+    int st = pod_plan_host(params, decode_batch, d_kv_indptr_h, d_kv_last_page_len_h,
+                           append_batch, qo_indptr_h, a_kv_indptr_h, a_kv_last_page_len_h,
+                           max_decode_batch, max_append_batch, max_qo_tokens, num_groups,
+                           decode_groups, host_ws, host_bytes, plan, &P);
+    if (st != ABP_OK) return st;
+    if (!dev_ws) return fail(ABP_ERR_INVALID_ARG, "device workspace is NULL");
+    if (dev_bytes < P.d_dev + P.a_dev)
+      return fail(ABP_ERR_WORKSPACE_TOO_SMALL, "device workspace smaller than abp_pod_workspace_size");
+    char* hw = static_cast<char*>(host_ws);
+    char* dw = static_cast<char*>(dev_ws);
+    if (plan->decode.num_workers > 0) {
+      st = upload_plan(P.ld, hw + plan->decode_host_offset, dw + plan->decode_dev_offset,
+                       P.d_dev, stream, &plan->decode);
+      if (st != ABP_OK) return st;
+    }
+    if (plan->append.num_workers > 0) {
+      st = upload_plan(P.la, hw + plan->append_host_offset, dw + plan->append_dev_offset,
+                       P.a_dev, stream, &plan->append);
+      if (st != ABP_OK) return st;
+    }
+    return ABP_OK;
+  } catch (...) {
+    return fail(ABP_ERR_INVALID_ARG, "exception");
+  }
+}
+
+int abp_pod_run(const abp_pod_plan_t* plan, const abp_params* params, const void* q_decode,
+                const void* q_append, const void* k_pages, const void* v_pages,
+                const int32_t* d_kv_indptr_d, const int32_t* d_kv_indices_d,
+                const int32_t* d_kv_last_page_len_d, const int32_t* qo_indptr_d,
+                const int32_t* a_kv_indptr_d, const int32_t* a_kv_indices_d,
+                const int32_t* a_kv_last_page_len_d, void* o_decode, float* lse_decode,
+                void* o_append, float* lse_append, void* dev_ws, size_t dev_bytes,
+                abp_stream_t stream) {
+  try {
+    if (!plan || !params) return fail(ABP_ERR_INVALID_ARG, "plan or params is NULL");
+    if (!dev_ws) return fail(ABP_ERR_INVALID_ARG, "device workspace is NULL");
+    if (dev_bytes < plan->decode_dev_bytes + plan->append_dev_bytes ||
+        plan->append_dev_offset < plan->decode_dev_bytes)
+      return fail(ABP_ERR_WORKSPACE_TOO_SMALL, "device workspace smaller than the plan's regions");
+    const int32_t wd = plan->decode.num_workers, wa = plan->append.num_workers;
+    if (wd < 0 || wa < 0 || wd + wa > plan->num_groups)
+      return fail(ABP_ERR_PLAN_MISMATCH, "inconsistent worker split");
+    abp_params pd = *params;
+    pd.causal = 0;
+    char* dw = static_cast<char*>(dev_ws);
+    abp::Config cd, ca;
+    abp::Layout ld, la;
+    abp::AttnArgs dec = {}, app = {};
+    if (wd > 0) {
+      int st = prepare_run(ABP_KIND_DECODE, &plan->decode, &pd, dw + plan->decode_dev_offset,
+                           plan->decode_dev_bytes, &cd, &ld);
+      if (st != ABP_OK) return st;
+      if (!abp::pod_applies(cd)) return fail(ABP_ERR_UNSUPPORTED, "params not supported for mixed batches");
+      if (plan->decode.num_tiles > 0 && (!q_decode || !k_pages || !v_pages || !d_kv_indptr_d ||
+                                         !d_kv_indices_d || !d_kv_last_page_len_d || !o_decode))
+        return fail(ABP_ERR_INVALID_ARG, "NULL decode tensor pointer");
+      if (!aligned16(q_decode) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o_decode))
+        return fail(ABP_ERR_INVALID_ARG, "q, k_pages, v_pages and o must be 16-byte aligned");
+      dec.q = q_decode;
+      dec.k_pages = k_pages;
+      dec.v_pages = v_pages;
+      dec.kv_indptr = d_kv_indptr_d;
+      dec.kv_indices = d_kv_indices_d;
+      dec.kv_last_page_len = d_kv_last_page_len_d;
+      dec.o = o_decode;
+      dec.lse = lse_decode;
+      fill_args(cd, ld, &plan->decode, dw + plan->decode_dev_offset, &dec);
+    }
+    if (wa > 0) {
+      int st = prepare_run(ABP_KIND_APPEND, &plan->append, params, dw + plan->append_dev_offset,
+                           plan->append_dev_bytes, &ca, &la);
+      if (st != ABP_OK) return st;
+      abp::Config cchk = ca;
+      if (!abp::pod_applies(cchk)) return fail(ABP_ERR_UNSUPPORTED, "params not supported for mixed batches");
+      if (plan->append.num_tiles > 0 && (!q_append || !k_pages || !v_pages || !qo_indptr_d ||
+                                         !a_kv_indptr_d || !a_kv_indices_d ||
+                                         !a_kv_last_page_len_d || !o_append))
+        return fail(ABP_ERR_INVALID_ARG, "NULL append tensor pointer");
+      if (!aligned16(q_append) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o_append))
+        return fail(ABP_ERR_INVALID_ARG, "q, k_pages, v_pages and o must be 16-byte aligned");
+      app.q = q_append;
+      app.k_pages = k_pages;
+      app.v_pages = v_pages;
+      app.qo_indptr = qo_indptr_d;
+      app.kv_indptr = a_kv_indptr_d;
+      app.kv_indices = a_kv_indices_d;
+      app.kv_last_page_len = a_kv_last_page_len_d;
+      app.o = o_append;
+      app.lse = lse_append;
+      fill_args(ca, la, &plan->append, dw + plan->append_dev_offset, &app);
+    }
+    if (wd + wa == 0) return ABP_OK;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = abp::launch_pod(wa > 0 ? ca : cd, app, dec, s);
+    if (e != hipSuccess) return hip_fail(e, "mixed kernel launch");
+    if (wd > 0) {
+      e = abp::launch_plan_merge(cd, dec, wd, s);
+      if (e != hipSuccess) return hip_fail(e, "decode merge kernel launch");
+    }
+    if (wa > 0) {
+      e = abp::launch_plan_merge(ca, app, wa, s);
+      if (e != hipSuccess) return hip_fail(e, "append merge kernel launch");
+    }
     return ABP_OK;
   } catch (...) {
     return fail(ABP_ERR_HIP, "exception");

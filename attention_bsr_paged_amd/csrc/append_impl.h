@@ -1,0 +1,692 @@
+// Body of the append kernel, as a device function of one worker, so that a
+// kernel can run it beside other work (the mixed decode + append launch). The
+// kernel itself, and what it computes, are in append.hip.
+#pragma once
+#include "common.h"
+#include "kernels.h"
+#include "layout.h"
+#include "tile_merge.h"
+
+namespace abp {
+namespace {
+namespace appi {
+
+constexpr int kD = 128;
+constexpr int kTk = kAppendTileKv;   // 64
+constexpr int kKStride = 136;        // sK row stride (uint16): 128 + 8 pad
+constexpr int kVStride = 68;         // sVt row stride (uint16): 64 + 4 pad
+constexpr float kRescaleLog2 = 8.f;  // lazy rescale threshold (log2 of the max p)
+
+
+template <typename T>
+__device__ __forceinline__ f32x4_t mfma(const uint4& a, const uint4& b, f32x4_t c);
+template <>
+__device__ __forceinline__ f32x4_t mfma<BF16>(const uint4& a, const uint4& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x4_t mfma<F16>(const uint4& a, const uint4& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t word(const uint4& u, int j) {
+  return j == 0 ? u.x : j == 1 ? u.y : j == 2 ? u.z : u.w;
+}
+
+// Split fp32 values into a 16-bit high part and the 16-bit rounding of the
+// remainder, so that hi + lo carries ~16 significant bits: products of rotated
+// operands keep fp32-level accuracy with three 16-bit matrix products.
+template <typename T>
+__device__ __forceinline__ void split8(const float v[8], uint4& hi, uint4& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    h[w] = pack2<T>(v[2 * w], v[2 * w + 1]);
+    l[w] = pack2<T>(v[2 * w] - lo_f32<T>(h[w]), v[2 * w + 1] - hi_f32<T>(h[w]));
+  }
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+// Rotate q: `lo` holds elements j0..j0+7 (j0 < 64) and `hi` their partners
+// j0+64..; results are split into (hi, lo) 16-bit parts for both halves.
+template <typename T>
+__device__ __forceinline__ void rope_pair(uint4& lo, uint4& hi, uint4& lo_r, uint4& hi_r,
+                                          float pos, int j0, const ABP_CONST_AS float* rope) {
+  float a[8], b[8];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    a[2 * w] = lo_f32<T>(word(lo, w));
+    a[2 * w + 1] = hi_f32<T>(word(lo, w));
+    b[2 * w] = lo_f32<T>(word(hi, w));
+    b[2 * w + 1] = hi_f32<T>(word(hi, w));
+  }
+  float ra[8], rb[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float sn, cs;
+    rope_sincos(pos, rope[2 * (j0 + e)], rope[2 * (j0 + e) + 1], &sn, &cs);
+    ra[e] = __builtin_fmaf(a[e], cs, -b[e] * sn);
+    rb[e] = __builtin_fmaf(b[e], cs, a[e] * sn);
+  }
+  split8<T>(ra, lo, lo_r);
+  split8<T>(rb, hi, hi_r);
+}
+
+// Interleaved RoPE for q: `u` holds elements 2 j0 .. 2 j0 + 7, the adjacent
+// pairs j0 .. j0 + 3; rotated in place into (hi, lo) 16-bit parts.
+template <typename T>
+__device__ __forceinline__ void rope_adjacent8(uint4& u, uint4& u_lo, float pos, int j0,
+                                               const ABP_CONST_AS float* rope) {
+  float r[8];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float x = lo_f32<T>(word(u, w)), y = hi_f32<T>(word(u, w));
+    float sn, cs;
+    rope_sincos(pos, rope[2 * (j0 + w)], rope[2 * (j0 + w) + 1], &sn, &cs);
+    r[2 * w] = __builtin_fmaf(x, cs, -y * sn);
+    r[2 * w + 1] = __builtin_fmaf(y, cs, x * sn);
+  }
+  split8<T>(r, u, u_lo);
+}
+
+// Interleaved RoPE for a K row: word w of u is the adjacent pair w of the
+// lane's 4 pairs; out is in element order.
+template <typename T>
+__device__ __forceinline__ void rope_k_adjacent(const uint4& u, const float (&cs)[4],
+                                                const float (&sn)[4], float out[8]) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float x = lo_f32<T>(word(u, w)), y = hi_f32<T>(word(u, w));
+    out[2 * w] = __builtin_fmaf(-y, sn[w], x * cs[w]);
+    out[2 * w + 1] = __builtin_fmaf(x, sn[w], y * cs[w]);
+  }
+}
+
+// Rotate the 4 rotary pairs a lane holds for one K row: u has elements
+// 4c..4c+3 in words 0-1 and their partners 64+4c.. in words 2-3; cs / sn are
+// the cosines and sines of the pairs' angles. out[e] / out[4 + e] are the
+// rotated elements 4c + e and 64 + 4c + e.
+template <typename T>
+__device__ __forceinline__ void rope_k_pairs(const uint4& u, const float (&cs)[4],
+                                             const float (&sn)[4], float out[8]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t wl = (e < 2) ? u.x : u.y;
+    const uint32_t wh = (e < 2) ? u.z : u.w;
+    const float x = (e & 1) ? hi_f32<T>(wl) : lo_f32<T>(wl);
+    const float y = (e & 1) ? hi_f32<T>(wh) : lo_f32<T>(wh);
+    out[e] = __builtin_fmaf(-y, sn[e], x * cs[e]);
+    out[4 + e] = __builtin_fmaf(x, sn[e], y * cs[e]);
+  }
+}
+
+// Maximum over the 4 lane groups (lanes l, l ^ 16, l ^ 32, l ^ 48) without
+// LDS: each swap exchanges halves (32 lanes) or rows (16 lanes) between two
+// copies of x, so the two results hold both partners of every lane.
+__device__ __forceinline__ float max_over_groups(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto h = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  x = __builtin_fmaxf(__builtin_bit_cast(float, h[0]), __builtin_bit_cast(float, h[1]));
+  const uint32_t w = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  return __builtin_fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+}
+
+// Waves per workgroup: 8 (256 rows, waves 0-3 stage K and 4-7 stage V), or 4
+// for RoPE (128 rows, every wave stages both; hi/lo operands need 512 regs).
+// One workgroup per CU either way.
+template <bool ROPE>
+constexpr int append_waves() {
+  return ROPE ? 4 : 8;
+}
+
+// The work of one append worker (a workgroup of append_waves<ROPE>() waves);
+// bid is the workgroup's index among the launch's append workgroups.
+template <typename T, int G, bool CAUSAL, bool ROPE, bool FASTPAGE, bool RIL>
+__device__ __forceinline__ void append_worker(const AttnArgs& a, int bid) {
+  static_assert(ROPE || !RIL, "interleaving is a RoPE layout");
+  // K elements a staging thread reads per row: rotate-half RoPE takes 4 + 4
+  // (both halves of its 4 pairs), everything else 8 consecutive ones
+  constexpr int kKPiece = (ROPE && !RIL) ? 4 : 8;
+  constexpr int NW = append_waves<ROPE>();
+  constexpr int kRows = 32 * NW;
+  constexpr int TQ = kRows / G;
+  // Two stages: block j is read from stage j & 1 while block j + 1 is stored
+  // into the other. Without RoPE a stage is K [64][128] and V [64][128] as in
+  // memory (rows of 256 bytes whose 16-byte chunks are XOR-swizzled by row),
+  // loaded straight from global memory into LDS; with RoPE it is the rotated
+  // K as hi and lo parts and V^T, padded, written from registers.
+  constexpr int kKElems = ROPE ? kTk * kKStride : kTk * kD;
+  constexpr int kKloElems = ROPE ? kTk * kKStride : 0;
+  constexpr int kVElems = ROPE ? kD * kVStride : kTk * kD;
+  // one array per stage, each named at compile time where used, so the
+  // compiler sees that loads into one stage never alias reads of the other
+  __shared__ __align__(16) uint16_t ldsK0[kKElems + kKloElems];
+  __shared__ __align__(16) uint16_t ldsK1[kKElems + kKloElems];
+  __shared__ __align__(16) uint16_t ldsV0[kVElems];
+  __shared__ __align__(16) uint16_t ldsV1[kVElems];
+  __shared__ int s_last;
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  auto sK_of = [&](auto st) -> uint16_t* {
+    if constexpr (decltype(st)::value == 0) return ldsK0;
+    else return ldsK1;
+  };
+  auto sKlo_of = [&](auto st) { return sK_of(st) + kKElems; };
+  auto sV_of = [&](auto st) -> uint16_t* {
+    if constexpr (decltype(st)::value == 0) return ldsV0;
+    else return ldsV1;
+  };
+
+  const ABP_CONST_AS int32_t* plan = const_as(a.plan);
+  const ABP_CONST_AS int32_t* wseg = plan + plan[H_OFF_WSEG];
+  const ABP_CONST_AS int32_t* segs = plan + plan[H_OFF_SEG];
+  const ABP_CONST_AS int32_t* tiles = plan + plan[H_OFF_TILE];
+  const ABP_CONST_AS float* rope = (const ABP_CONST_AS float*)(plan + plan[H_OFF_ROPE]);
+  const ABP_CONST_AS int32_t* kv_indptr = const_as(a.kv_indptr);
+  const ABP_CONST_AS int32_t* kv_indices = const_as(a.kv_indices);
+  const ABP_CONST_AS int32_t* qo_indptr = const_as(a.qo_indptr);
+
+  // XCD-major worker id: workgroup i runs on XCD i % 8
+  const int W = a.workers;
+  const int worker = (W % 8 == 0) ? (bid % 8) * (W / 8) + bid / 8 : bid;
+  const int s_begin = wseg[worker], s_end = wseg[worker + 1];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g16 = lane >> 4;   // lane group 0..3
+  const int l16 = lane & 15;
+  const float cl2 = a.sm_scale_log2;
+  const int P = a.page_size;
+  const int shift = a.page_shift;
+  const int tstride = a.token_stride;
+  const uint16_t* __restrict__ kp = static_cast<const uint16_t*>(a.k_pages);
+  const uint16_t* __restrict__ vp = static_cast<const uint16_t*>(a.v_pages);
+
+  const float thr = kRescaleLog2 / cl2;  // lazy rescale threshold, raw score units
+  // staging (256 threads per operand): K rows k_row + 16 i (i = 16-key group),
+  // 16-byte chunk kc_chunk; V keys 16 vw + 4 v_kg + i (16-key group vw), chunk
+  // v_chunk. With 8 waves, waves 0-3 stage K and waves 4-7 stage V.
+  const int kc_chunk = tid & 15;
+  // RoPE: a thread stages both elements of the rotary pairs j = 4 kc_chunk + e
+  // (e < 4) of its K rows (rotate-half: elements j and j + 64; interleaved:
+  // 2j and 2j + 1, its plain 8 elements), so each angle is computed once. Its rows are 16
+  // keys apart: the first row's angles are evaluated and the next follow by
+  // angle addition with the rotation by 16 positions (c16, s16).
+  float kfhi[ROPE ? 4 : 1], kflo[ROPE ? 4 : 1], c16[ROPE ? 4 : 1], s16[ROPE ? 4 : 1];
+  if constexpr (ROPE) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = 4 * kc_chunk + e;
+      kfhi[e] = rope[2 * j];
+      kflo[e] = rope[2 * j + 1];
+      rope_sincos(16.f, kfhi[e], kflo[e], &s16[e], &c16[e]);
+    }
+  }
+  const int k_row = (tid & 255) >> 4;
+  const int v_kg = lane & 3;
+  const int v_chunk = lane >> 2;
+  const int vw = wave & 3;
+  const bool stage_k = NW == 4 || wave < 4;
+  const bool stage_v = NW == 4 || wave >= 4;
+
+  for (int s = s_begin; s < s_end; ++s) {
+    const int tile = segs[4 * s];
+    const int kv_begin = segs[4 * s + 1], kv_end = segs[4 * s + 2], slot = segs[4 * s + 3];
+    const int b = tiles[4 * tile], h = tiles[4 * tile + 1], qt = tiles[4 * tile + 2];
+    const int q0 = qo_indptr[b];
+    const int qo_len = qo_indptr[b + 1] - q0;
+    const int ip0 = kv_indptr[b];
+    const int npg = kv_indptr[b + 1] - ip0;
+    const int kv_len = npg > 0 ? (npg - 1) * P + a.kv_last_page_len[b] : 0;
+    const int kv_pos0 = (ROPE && a.kv_pos_offset) ? a.kv_pos_offset[b] : 0;
+    // elements; with RoPE the first piece of the lane's pairs (see above)
+    const int koff_lane = k_row * tstride + h * kD + kc_chunk * kKPiece;
+    const int voff_lane = (4 * v_kg) * tstride + h * kD + v_chunk * 8;   // + i * tstride
+
+    // ---- Q fragments (B operand of S^T = K Q^T) for this wave's 32 rows
+    uint4 qf[2][4];
+    uint4 qfl[ROPE ? 2 : 1][4];  // RoPE: low parts of the rotated q
+    int lim[2];
+    int tloc_r[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int r = wave * 32 + nb * 16 + l16;
+      const int tloc = qt * TQ + r / G;
+      const int tl = min(tloc, qo_len - 1);
+      tloc_r[nb] = tloc;
+      lim[nb] = kv_len - qo_len + tl;
+      const uint16_t* qptr = static_cast<const uint16_t*>(a.q) +
+                             ((int64_t)(q0 + tl) * a.num_qo_heads + h * G + (r % G)) * kD + g16 * 8;
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) qf[nb][kc] = *reinterpret_cast<const uint4*>(qptr + kc * 32);
+      if constexpr (ROPE) {
+        const float qpos = a.q_pos ? (float)a.q_pos[q0 + tl] : (float)lim[nb];
+        if constexpr (RIL) {
+          // chunk kc holds elements g16 * 8 + 32 kc .. + 7: pairs 4 g16 + 16 kc ..
+#pragma unroll
+          for (int kc = 0; kc < 4; ++kc)
+            rope_adjacent8<T>(qf[nb][kc], qfl[nb][kc], qpos, 4 * g16 + 16 * kc, rope);
+        } else {
+          rope_pair<T>(qf[nb][0], qf[nb][2], qfl[nb][0], qfl[nb][2], qpos, g16 * 8, rope);
+          rope_pair<T>(qf[nb][1], qf[nb][3], qfl[nb][1], qfl[nb][3], qpos, 32 + g16 * 8, rope);
+        }
+      }
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc)
+        asm volatile("" : "+v"(qf[nb][kc].x), "+v"(qf[nb][kc].y), "+v"(qf[nb][kc].z),
+                     "+v"(qf[nb][kc].w));
+    }
+    // first row of the tile sees the fewest keys
+    const int tile_min_lim = kv_len - qo_len + qt * TQ;
+
+    float m[2] = {kNegInf, kNegInf};
+    float lsum[2] = {0.f, 0.f};
+    f32x4_t O[8][2];
+#pragma unroll
+    for (int md = 0; md < 8; ++md)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) O[md][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // ---- staging: global -> registers (block kb) and registers -> LDS
+    // with 8 waves a wave stages either K or V, so V reuses the K registers
+    uint4 kreg[4], vreg[NW == 4 ? 4 : 1];
+    auto vr = [&](int i) -> uint4& {
+      if constexpr (NW == 4) return vreg[i];
+      else return kreg[i];
+    };
+    auto kload = [&](const uint16_t* p) -> uint4 {
+      if constexpr (ROPE && !RIL) {
+        const uint2 lo = *reinterpret_cast<const uint2*>(p);
+        const uint2 hi = *reinterpret_cast<const uint2*>(p + 64);
+        return make_uint4(lo.x, lo.y, hi.x, hi.y);
+      } else {
+        return *reinterpret_cast<const uint4*>(p);
+      }
+    };
+    auto gload = [&](int kb) {
+      if constexpr (FASTPAGE) {
+        // one page id per 16-key group, on the scalar unit; groups past the
+        // segment end re-read the last valid group (in bounds, masked)
+        const int last16 = (kv_end - 1) & ~15;
+        if (stage_k) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int kk = min(kb + 16 * i, last16);
+            const int64_t base = (int64_t)kv_indices[ip0 + (kk >> shift)] * a.page_stride +
+                                 (int64_t)(kk & (P - 1)) * tstride;
+            kreg[i] = kload(kp + base + koff_lane);
+          }
+        }
+        if (stage_v) {
+          const int kk = min(kb + 16 * vw, last16);  // wave-uniform
+          const int64_t vb = (int64_t)kv_indices[ip0 + (kk >> shift)] * a.page_stride +
+                             (int64_t)(kk & (P - 1)) * tstride;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            vr(i) = *reinterpret_cast<const uint4*>(vp + vb + voff_lane + i * tstride);
+        }
+      } else {
+        if (stage_k) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = min(kb + k_row + 16 * i, kv_end - 1);
+            int page, off;
+            if (shift >= 0) {
+              page = key >> shift;
+              off = key & (P - 1);
+            } else {
+              page = key / P;
+              off = key - page * P;
+            }
+            const int64_t pg = a.kv_indices[ip0 + page];
+            kreg[i] = kload(kp + pg * a.page_stride + (int64_t)off * tstride + h * kD +
+                            kc_chunk * kKPiece);
+          }
+        }
+        if (stage_v) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = min(kb + 16 * vw + 4 * v_kg + i, kv_end - 1);
+            int page, off;
+            if (shift >= 0) {
+              page = key >> shift;
+              off = key & (P - 1);
+            } else {
+              page = key / P;
+              off = key - page * P;
+            }
+            const int64_t pg = a.kv_indices[ip0 + page];
+            vr(i) = *reinterpret_cast<const uint4*>(vp + pg * a.page_stride +
+                                                    (int64_t)off * tstride + h * kD + v_chunk * 8);
+          }
+        }
+      }
+    };
+    auto swrite = [&](int kb, auto stage) {
+      uint16_t* sK = sK_of(stage);
+      uint16_t* sKlo = sKlo_of(stage);
+      uint16_t* sVt = sV_of(stage);
+      if (stage_k) {
+        float cs[ROPE ? 4 : 1], sn[ROPE ? 4 : 1];
+        if constexpr (ROPE) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            rope_sincos((float)(kv_pos0 + kb + k_row), kfhi[e], kflo[e], &sn[e], &cs[e]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (ROPE) {
+            if (i > 0) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float cn = __builtin_fmaf(-sn[e], s16[e], cs[e] * c16[e]);
+                sn[e] = __builtin_fmaf(cs[e], s16[e], sn[e] * c16[e]);
+                cs[e] = cn;
+              }
+            }
+            float kr[8];
+            uint4 hi, lo;
+            if constexpr (RIL) {
+              // 8 consecutive elements, stored in place as one 16-byte piece
+              rope_k_adjacent<T>(kreg[i], cs, sn, kr);
+              split8<T>(kr, hi, lo);
+              const int at = (k_row + 16 * i) * kKStride + kc_chunk * 8;
+              *reinterpret_cast<uint4*>(&sK[at]) = hi;
+              *reinterpret_cast<uint4*>(&sKlo[at]) = lo;
+            } else {
+              rope_k_pairs<T>(kreg[i], cs, sn, kr);
+              split8<T>(kr, hi, lo);
+              const int at = (k_row + 16 * i) * kKStride + kc_chunk * 4;
+              *reinterpret_cast<uint2*>(&sK[at]) = make_uint2(hi.x, hi.y);
+              *reinterpret_cast<uint2*>(&sK[at + 64]) = make_uint2(hi.z, hi.w);
+              *reinterpret_cast<uint2*>(&sKlo[at]) = make_uint2(lo.x, lo.y);
+              *reinterpret_cast<uint2*>(&sKlo[at + 64]) = make_uint2(lo.z, lo.w);
+            }
+          } else {
+            const int at = (k_row + 16 * i) * kKStride + kc_chunk * 8;
+            *reinterpret_cast<uint4*>(&sK[at]) = kreg[i];
+          }
+        }
+      }
+      if (stage_v) {
+        // V^T: element d of the 4 keys 16 vw + 4 v_kg + 0..3 as one 8-byte piece
+        uint16_t* V = sVt + 16 * vw + 4 * v_kg;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t w0 = word(vr(0), j), w1 = word(vr(1), j);
+          const uint32_t w2 = word(vr(2), j), w3 = word(vr(3), j);
+          const int d = v_chunk * 8 + 2 * j;
+          *reinterpret_cast<uint2*>(&V[d * kVStride]) = make_uint2(pair_lo(w0, w1), pair_lo(w2, w3));
+          *reinterpret_cast<uint2*>(&V[(d + 1) * kVStride]) =
+              make_uint2(pair_hi(w0, w1), pair_hi(w2, w3));
+        }
+      }
+    };
+
+    // Without RoPE: block kb straight into LDS stage `stage`. Each wave
+    // instruction fills 4 rows (1 KB, lane l at byte 16 l); wave w owns rows
+    // 8 w .. 8 w + 7 of K and of V. Lane l stores row r = r0 + l / 16 at chunk
+    // position l % 16, which holds the row's logical chunk (l % 16) ^ swz(r).
+    // Rows past the segment end re-read the last valid rows (in bounds, masked).
+    auto dload = [&](int kb, auto stage) {
+      uint16_t* sK = sK_of(stage);
+      uint16_t* sV = sV_of(stage);
+      const int pos = lane & 15;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r0 = 4 * (2 * wave + i);
+        const int r = r0 + (lane >> 4);
+        const int qk = pos ^ (r & 15);        // K chunk held at this position
+        const int qv = pos ^ (2 * (r & 7));   // V chunk held at this position
+        int64_t row_base;                      // element offset of key kb + r (head h)
+        if constexpr (FASTPAGE) {
+          const int last4 = (kv_end - 1) & ~3;
+          const int kk = min(kb + r0, last4);  // 4-row group, one page
+          row_base = (int64_t)kv_indices[ip0 + (kk >> shift)] * a.page_stride +
+                     (int64_t)((kk & (P - 1)) + (lane >> 4)) * tstride + h * kD;
+        } else {
+          const int key = min(kb + r, kv_end - 1);
+          int page, off;
+          if (shift >= 0) {
+            page = key >> shift;
+            off = key & (P - 1);
+          } else {
+            page = key / P;
+            off = key - page * P;
+          }
+          row_base = (int64_t)a.kv_indices[ip0 + page] * a.page_stride + (int64_t)off * tstride +
+                     h * kD;
+        }
+        __builtin_amdgcn_global_load_lds(kp + row_base + qk * 8, (ABP_LDS void*)(sK + r0 * kD),
+                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vp + row_base + qv * 8, (ABP_LDS void*)(sV + r0 * kD),
+                                         16, 0, 0);
+      }
+    };
+
+    if (kv_begin < kv_end) {
+      if constexpr (ROPE) {
+        gload(kv_begin);
+        swrite(kv_begin, S0{});
+      } else {
+        dload(kv_begin, S0{});
+      }
+    }
+    __syncthreads();
+    // one block on stage `st` (blocks alternate between the two stages)
+    auto block = [&](auto st, int kb) __attribute__((always_inline)) {
+      constexpr int ST = decltype(st)::value;
+      using Other = std::integral_constant<int, 1 - ST>;
+      const bool has_next = kb + kTk < kv_end;
+      if (has_next) {
+        if constexpr (ROPE) gload(kb + kTk);
+        else dload(kb + kTk, Other{});  // completes before the barrier ending this block
+      }
+      const uint16_t* sK = sK_of(st);
+      const uint16_t* sKlo = sKlo_of(st);
+      const uint16_t* sVt = sV_of(st);
+
+      // The block is taken as two 32-key halves h, each one step of the online
+      // softmax. Both halves' S products are issued first; the softmax of half
+      // 0 can then run beside the products of half 1, and the P.V products of
+      // half 0 beside the softmax of half 1 (O takes half 0's contribution
+      // before any rescale that half 1 makes).
+      // S^T = K Q^T: S[mb][nb] holds keys kb + 16 mb + 4 g16 + j, row nb*16 + l16
+      f32x4_t S[4][2];
+      auto qk_half = [&](int h) __attribute__((always_inline)) {
+#pragma unroll
+        for (int mb = 2 * h; mb < 2 * h + 2; ++mb) {
+          S[mb][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          S[mb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kc = 0; kc < 4; ++kc) {
+            // swizzled rows without RoPE: chunk kc * 4 + g16 of row mb * 16 + l16
+            const int at = ROPE ? (mb * 16 + l16) * kKStride + kc * 32 + g16 * 8
+                                : (mb * 16 + l16) * kD + (((kc * 4 + g16) ^ l16) * 8);
+            const uint4 ka = *reinterpret_cast<const uint4*>(&sK[at]);
+            S[mb][0] = mfma<T>(ka, qf[0][kc], S[mb][0]);
+            S[mb][1] = mfma<T>(ka, qf[1][kc], S[mb][1]);
+            if constexpr (ROPE) {  // + Kh Ql + Kl Qh
+              const uint4 kl = *reinterpret_cast<const uint4*>(&sKlo[at]);
+              S[mb][0] = mfma<T>(ka, qfl[0][kc], S[mb][0]);
+              S[mb][1] = mfma<T>(ka, qfl[1][kc], S[mb][1]);
+              S[mb][0] = mfma<T>(kl, qf[0][kc], S[mb][0]);
+              S[mb][1] = mfma<T>(kl, qf[1][kc], S[mb][1]);
+            }
+          }
+        }
+      };
+      // masks of a half (keys past the segment end, causal limit per row),
+      // online softmax with lazy rescale, P of the half packed as the PV B
+      // operand: K-slots of lane group g16 are keys 4 g16..+3 and 16 + 4 g16..+3
+      uint4 pB[2][2];  // [h][nb]
+      auto softmax_half = [&](int h) __attribute__((always_inline)) {
+        const int kbh = kb + 32 * h;
+        const bool edge = (kbh + 32 > kv_end) || (CAUSAL && kbh + 31 > tile_min_lim);
+        if (edge) {
+#pragma unroll
+          for (int mb = 2 * h; mb < 2 * h + 2; ++mb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int key = kb + mb * 16 + g16 * 4 + j;
+#pragma unroll
+              for (int nb = 0; nb < 2; ++nb) {
+                const bool dead = key >= kv_end || (CAUSAL && key > lim[nb]);
+                if (dead) S[mb][nb][j] = kNegInf;
+              }
+            }
+        }
+        float mx[2];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          float x = kNegInf;
+#pragma unroll
+          for (int mb = 2 * h; mb < 2 * h + 2; ++mb)
+            x = __builtin_fmaxf(x, __builtin_fmaxf(__builtin_fmaxf(S[mb][nb][0], S[mb][nb][1]),
+                                                   __builtin_fmaxf(S[mb][nb][2], S[mb][nb][3])));
+          mx[nb] = max_over_groups(x);
+        }
+        // the reference max moves only when a score exceeds it by more than thr
+        if (__builtin_amdgcn_ballot_w64((mx[0] > m[0] + thr) || (mx[1] > m[1] + thr))) {
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            const float mn = __builtin_fmaxf(m[nb], mx[nb]);
+            const float alpha = mn == kNegInf ? 1.f : fast_exp2((m[nb] - mn) * cl2);
+            m[nb] = mn;
+            lsum[nb] *= alpha;
+#pragma unroll
+            for (int md = 0; md < 8; ++md) O[md][nb] *= alpha;
+          }
+        }
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const float mc = (m[nb] == kNegInf ? 0.f : m[nb]) * cl2;
+          float p[2][4];
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              p[i][j] = fast_exp2(__builtin_fmaf(S[2 * h + i][nb][j], cl2, -mc));
+          // row sum in fp32 of the unrounded p: lse must not carry P's 16-bit rounding
+          lsum[nb] += ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) +
+                      ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
+          pB[h][nb] = make_uint4(pack2<T>(p[0][0], p[0][1]), pack2<T>(p[0][2], p[0][3]),
+                                 pack2<T>(p[1][0], p[1][1]), pack2<T>(p[1][2], p[1][3]));
+        }
+      };
+      // O^T += V^T P^T over half h
+      auto pv_half = [&](int h) __attribute__((always_inline)) {
+#pragma unroll
+        for (int md = 0; md < 8; ++md) {
+          uint4 va;
+          if constexpr (ROPE) {
+            const uint16_t* vrow = &sVt[(md * 16 + l16) * kVStride + h * 32 + g16 * 4];
+            const uint2 v0 = *reinterpret_cast<const uint2*>(vrow);
+            const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 16);
+            va = make_uint4(v0.x, v0.y, v1.x, v1.y);
+          } else {
+            // V^T fragment by transpose reads of V: in each 16-lane group,
+            // lane c points at V[key 4 g16 + c / 4 (+ 16)][d 16 md + 4 (c % 4)]
+            // and receives V[4 keys][d 16 md + c] (keys 4 g16..+3, 16 + ..)
+            const int d0 = md * 16 + 4 * (l16 & 3);
+            const int kA = h * 32 + 4 * g16 + (l16 >> 2);
+            const int kB = kA + 16;
+            const int offA = kA * kD + (((d0 >> 3) ^ (2 * (kA & 7))) * 8) + (d0 & 7);
+            const int offB = kB * kD + (((d0 >> 3) ^ (2 * (kB & 7))) * 8) + (d0 & 7);
+            const v4i16_t a4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ABP_LDS v4i16_t*)(sVt + offA));
+            const v4i16_t b4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ABP_LDS v4i16_t*)(sVt + offB));
+            const uint2 av = __builtin_bit_cast(uint2, a4), bv = __builtin_bit_cast(uint2, b4);
+            va = make_uint4(av.x, av.y, bv.x, bv.y);
+          }
+          O[md][0] = mfma<T>(va, pB[h][0], O[md][0]);
+          O[md][1] = mfma<T>(va, pB[h][1], O[md][1]);
+        }
+      };
+      // matrix-core phases run at raised wave priority: the arbiter then
+      // issues one wave's products back to back while the other wave of the
+      // SIMD runs its softmax on the vector unit
+      __builtin_amdgcn_s_setprio(1);
+      qk_half(0);
+      qk_half(1);
+      __builtin_amdgcn_s_setprio(0);
+      softmax_half(0);
+      __builtin_amdgcn_s_setprio(1);
+      pv_half(0);
+      __builtin_amdgcn_s_setprio(0);
+      softmax_half(1);
+      __builtin_amdgcn_s_setprio(1);
+      pv_half(1);
+      __builtin_amdgcn_s_setprio(0);
+      // the other stage held block j - 1, which every wave finished before the
+      // barrier that ended the previous iteration
+      if constexpr (ROPE) {
+        if (has_next) swrite(kb + kTk, Other{});
+      }
+      __syncthreads();
+    };
+    for (int kb = kv_begin; kb < kv_end; kb += 2 * kTk) {
+      block(S0{}, kb);
+      if (kb + kTk < kv_end) block(S1{}, kb + kTk);
+    }
+
+    // ---- finalize rows: o = O / l, lse = m * scale + ln l
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      float L = lsum[nb];
+      L += __shfl_xor(L, 16);
+      L += __shfl_xor(L, 32);
+      const int r = wave * 32 + nb * 16 + l16;
+      const bool valid = tloc_r[nb] < qo_len;
+      const bool empty = !(L > 0.f);
+      const float inv = empty ? 0.f : 1.f / L;
+      const float lse = empty ? kNegInf : m[nb] * a.sm_scale + fast_log2(L) * kLn2;
+      if (valid) {
+        if (slot < 0) {
+          const int64_t orow = (int64_t)(q0 + tloc_r[nb]) * a.num_qo_heads + h * G + (r % G);
+#pragma unroll
+          for (int md = 0; md < 8; ++md) {
+            const int64_t off = orow * kD + md * 16 + g16 * 4;
+            const f32x4_t v = O[md][nb] * inv;
+            if (a.out_dtype == ABP_F32) {
+              *reinterpret_cast<float4*>(static_cast<float*>(a.o) + off) =
+                  make_float4(v[0], v[1], v[2], v[3]);
+            } else if (a.out_dtype == ABP_BF16) {
+              *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.o) + off) =
+                  make_uint2(pack2<BF16>(v[0], v[1]), pack2<BF16>(v[2], v[3]));
+            } else {
+              *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.o) + off) =
+                  make_uint2(pack2<F16>(v[0], v[1]), pack2<F16>(v[2], v[3]));
+            }
+          }
+          if (a.lse && g16 == 0) a.lse[orow] = lse;
+        } else {
+          const int64_t prow = (int64_t)slot * kRows + r;
+#pragma unroll
+          for (int md = 0; md < 8; ++md) {
+            const f32x4_t v = O[md][nb] * inv;
+            *reinterpret_cast<float4*>(a.o_part + prow * kD + md * 16 + g16 * 4) =
+                make_float4(v[0], v[1], v[2], v[3]);
+          }
+          if (g16 == 0) a.lse_part[prow] = lse;
+        }
+      }
+    }
+    if (slot >= 0 && plan[H_MERGE_KERNEL] == 0) {
+      merge_if_last<kRows, 64 * NW>(a, tile, &s_last, [&](int r, int64_t* orow) {
+        const int tloc = qt * TQ + r / G;
+        if (tloc >= qo_len) return false;
+        *orow = (int64_t)(q0 + tloc) * a.num_qo_heads + h * G + (r % G);
+        return true;
+      });
+    }
+  }
+}
+
+}  // namespace appi
+}  // namespace
+}  // namespace abp

@@ -25,512 +25,20 @@
 // Scope (the dispatcher falls back to decode_kernel otherwise): 16-bit or fp8
 // (e4m3, in decode_mfma_fp8_kernel below) K/V, no RoPE, power-of-two page size >= 16 (a 16-token tile never straddles a page),
 // kv head count a multiple of 4, group size 4 or 8 (rows padded to 16).
-#include "common.h"
-#include "kernels.h"
-#include "layout.h"
+#include "decode_mfma_impl.h"
 
 namespace abp {
 
 namespace {
 
-constexpr int kD = 128;
-constexpr int kC = 32;               // tokens per chunk
-constexpr float kRescaleLog2 = 8.f;  // lazy rescale threshold (log2 of the max p)
-
-template <typename T>
-__device__ __forceinline__ f32x4_t mfma16(const uint4& a, const uint4& b, f32x4_t c);
-template <>
-__device__ __forceinline__ f32x4_t mfma16<BF16>(const uint4& a, const uint4& b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
-template <>
-__device__ __forceinline__ f32x4_t mfma16<F16>(const uint4& a, const uint4& b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
-                                                __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
-}
-
-// maximum over the 4 lane groups (lanes l, l ^ 16, l ^ 32, l ^ 48)
-__device__ __forceinline__ float max4groups(float x) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, x);
-  const auto h = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  x = __builtin_fmaxf(__builtin_bit_cast(float, h[0]), __builtin_bit_cast(float, h[1]));
-  const uint32_t w = __builtin_bit_cast(uint32_t, x);
-  const auto r = __builtin_amdgcn_permlane16_swap(w, w, false, false);
-  return __builtin_fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
-}
-
-__device__ __forceinline__ void store4_dt(void* base, int64_t off, const f32x4_t& v, int dt) {
-  if (dt == ABP_F32) {
-    *reinterpret_cast<float4*>(static_cast<float*>(base) + off) = make_float4(v[0], v[1], v[2], v[3]);
-  } else if (dt == ABP_BF16) {
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + off) =
-        make_uint2(pack2<BF16>(v[0], v[1]), pack2<BF16>(v[2], v[3]));
-  } else {
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + off) =
-        make_uint2(pack2<F16>(v[0], v[1]), pack2<F16>(v[2], v[3]));
-  }
-}
-
-// two e4m3 codes (byte pair HI of w) as a 16-bit pair of the query's type;
-// exact: every e4m3 value is a bf16 and an fp16 value
-template <typename T, bool HI>
-__device__ __forceinline__ uint32_t fp8x2(uint32_t w);
-template <>
-__device__ __forceinline__ uint32_t fp8x2<BF16, false>(uint32_t w) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, false));
-}
-template <>
-__device__ __forceinline__ uint32_t fp8x2<BF16, true>(uint32_t w) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, true));
-}
-template <>
-__device__ __forceinline__ uint32_t fp8x2<F16, false>(uint32_t w) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.f, false));
-}
-template <>
-__device__ __forceinline__ uint32_t fp8x2<F16, true>(uint32_t w) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.f, true));
-}
-// 8 codes (two words) as 8 16-bit elements (four words), in order
-template <typename T>
-__device__ __forceinline__ uint4 widen8(uint32_t w0, uint32_t w1) {
-  return make_uint4(fp8x2<T, false>(w0), fp8x2<T, true>(w0), fp8x2<T, false>(w1),
-                    fp8x2<T, true>(w1));
-}
-
 template <typename T, int G>
 __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(AttnArgs a) {
-  static_assert(G == 4 || G == 8, "rows of one kv head fill at most one 16-row tile");
-  constexpr int HT = 4;  // kv heads per tile = waves per workgroup
-  // per-wave V ring: two stages of 32 rows x 128 head dims, each a separately
-  // named array so loads into one stage are seen not to alias reads of the other
-  __shared__ __align__(16) uint16_t sV0[HT][kC * kD];
-  __shared__ __align__(16) uint16_t sV1[HT][kC * kD];
-
-  const ABP_CONST_AS int32_t* plan = const_as(a.plan);
-  const ABP_CONST_AS int32_t* wseg = plan + plan[H_OFF_WSEG];
-  const ABP_CONST_AS int32_t* segs = plan + plan[H_OFF_SEG];
-  const ABP_CONST_AS int32_t* tiles = plan + plan[H_OFF_TILE];
-  const ABP_CONST_AS int32_t* kv_indptr = const_as(a.kv_indptr);
-  const ABP_CONST_AS int32_t* kv_indices = const_as(a.kv_indices);
-  const int s_begin = wseg[blockIdx.x], s_end = wseg[blockIdx.x + 1];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g16 = lane >> 4;
-  const int l16 = lane & 15;
-  const float cl2 = a.sm_scale_log2;
-  const float thr = kRescaleLog2 / cl2;
-  const uint16_t* __restrict__ kp = static_cast<const uint16_t*>(a.k_pages);
-  const uint16_t* __restrict__ vp = static_cast<const uint16_t*>(a.v_pages);
-  const int P = a.page_size;
-  const int shift = a.page_shift;
-  const int tstride = a.token_stride;
-  uint16_t* const myV0 = sV0[wave];
-  uint16_t* const myV1 = sV1[wave];
-
-  for (int s = s_begin; s < s_end; ++s) {
-    const int tile = segs[4 * s];
-    const int kv_begin = segs[4 * s + 1], kv_end = segs[4 * s + 2], slot = segs[4 * s + 3];
-    const int b = tiles[4 * tile], h = tiles[4 * tile + 1] + wave;
-    const int ip0 = kv_indptr[b];
-
-    // q of row l16 (< G), head dims 32 kc + 8 g16 .. + 7: the B operand of S^T = K Q^T
-    // (branch-free: lanes of rows >= G load row G - 1 and zero it)
-    uint4 qf[4];
-    {
-      const int qr = l16 < G ? l16 : G - 1;
-      const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
-                             (int64_t(b) * a.num_qo_heads + int64_t(h) * G + qr) * kD + 8 * g16;
-      const uint32_t keep = l16 < G ? 0xffffffffu : 0u;
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        const uint4 v = *reinterpret_cast<const uint4*>(qrow + 32 * kc);
-        qf[kc] = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
-      }
-    }
-
-    float m = kNegInf, lsum = 0.f;
-    f32x4_t O[8];
-#pragma unroll
-    for (int md = 0; md < 8; ++md) O[md] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    // element offset of token t (< the tile's page end) of head h
-    auto row_base = [&](int t) -> int64_t {
-      return int64_t(kv_indices[ip0 + (t >> shift)]) * a.page_stride +
-             int64_t(t & (P - 1)) * tstride + int64_t(h) * kD;
-    };
-    // K of chunk c: tile mb = tokens c + 16 mb .. + 15 (a tile past kv_end re-reads
-    // tile 0, in bounds and masked); lane: token l16 of the tile, window kc
-    auto load_k = [&](int c, uint4 (&kr)[2][4]) {
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const int t0 = (c + 16 * mb < kv_end) ? c + 16 * mb : c;
-        const uint16_t* rp = kp + row_base(t0) + int64_t(l16) * tstride + 8 * g16;
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) kr[mb][kc] = *reinterpret_cast<const uint4*>(rp + 32 * kc);
-      }
-    };
-    // V of chunk c into this wave's LDS stage: instruction i fills rows 4 i ..
-    // 4 i + 3 (1 KB); lane l writes row 4 i + l / 16 at chunk position l % 16,
-    // which holds the row's logical chunk (l % 16) ^ (2 (row & 7)) (the swizzle
-    // that makes the transpose reads conflict-free)
-    auto load_v = [&](int c, uint16_t* dst) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int mb = i >> 2;
-        const int t0 = (c + 16 * mb < kv_end) ? c + 16 * mb : c;
-        const int r = 4 * i + (lane >> 4);
-        const int qv = (lane & 15) ^ (2 * (r & 7));
-        const uint16_t* src = vp + row_base(t0) + int64_t(r & 15) * tstride + qv * 8;
-        __builtin_amdgcn_global_load_lds(src, (ABP_LDS void*)(dst + 4 * i * kD), 16, 0, 0);
-      }
-    };
-
-    auto compute = [&](int c, const uint4 (&kr)[2][4], const uint16_t* sv)
-                       __attribute__((always_inline)) {
-      // S^T: S[mb] holds keys c + 16 mb + 4 g16 + j of row l16
-      f32x4_t S[2];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        S[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) S[mb] = mfma16<T>(kr[mb][kc], qf[kc], S[mb]);
-      }
-      if (c + kC > kv_end) {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (c + 16 * mb + 4 * g16 + j >= kv_end) S[mb][j] = kNegInf;
-      }
-      float mx = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(S[0][0], S[0][1]),
-                                                 __builtin_fmaxf(S[0][2], S[0][3])),
-                                 __builtin_fmaxf(__builtin_fmaxf(S[1][0], S[1][1]),
-                                                 __builtin_fmaxf(S[1][2], S[1][3])));
-      mx = max4groups(mx);
-      if (__builtin_amdgcn_ballot_w64(mx > m + thr)) {
-        const float mn = __builtin_fmaxf(m, mx);
-        const float alpha = mn == kNegInf ? 1.f : fast_exp2((m - mn) * cl2);
-        m = mn;
-        lsum *= alpha;
-#pragma unroll
-        for (int md = 0; md < 8; ++md) O[md] *= alpha;
-      }
-      const float mc = (m == kNegInf ? 0.f : m) * cl2;
-      float p[2][4];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) p[mb][j] = fast_exp2(__builtin_fmaf(S[mb][j], cl2, -mc));
-      lsum += ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) +
-              ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
-      // P^T: K-slots of lane group g16 are keys 4 g16 .. + 3 and 16 + 4 g16 .. + 3
-      const uint4 pB = make_uint4(pack2<T>(p[0][0], p[0][1]), pack2<T>(p[0][2], p[0][3]),
-                                  pack2<T>(p[1][0], p[1][1]), pack2<T>(p[1][2], p[1][3]));
-      // O^T += V^T P^T: lane c of a 16-lane group points at V[key 4 g16 + c / 4
-      // (+ 16)][d 16 md + 4 (c % 4)] and receives V[4 keys][d 16 md + c]
-      const int kA = 4 * g16 + (l16 >> 2);
-      const int kB = kA + 16;
-#pragma unroll
-      for (int md = 0; md < 8; ++md) {
-        const int d0 = md * 16 + 4 * (l16 & 3);
-        const int offA = kA * kD + (((d0 >> 3) ^ (2 * (kA & 7))) * 8) + (d0 & 7);
-        const int offB = kB * kD + (((d0 >> 3) ^ (2 * (kB & 7))) * 8) + (d0 & 7);
-        const v4i16_t a4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ABP_LDS v4i16_t*)(sv + offA));
-        const v4i16_t b4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ABP_LDS v4i16_t*)(sv + offB));
-        const uint2 av = __builtin_bit_cast(uint2, a4), bv = __builtin_bit_cast(uint2, b4);
-        O[md] = mfma16<T>(make_uint4(av.x, av.y, bv.x, bv.y), pB, O[md]);
-      }
-    };
-
-    // chunks c = kv_begin + 32 n in pairs, alternating between the two LDS
-    // stages and two K register sets, two chunks in flight per wave: the
-    // prologue loads chunks 0 and 1; each half-step waits for its chunk,
-    // computes it and then refills its stage and registers with the chunk two
-    // ahead (clamped to the last chunk of the segment, so trailing loads
-    // re-read that chunk in bounds; a chunk past kv_end is fully masked).
-    // A chunk's V (written to LDS by the memory unit) and K were issued before
-    // the 16 loads of the chunk after it, so vmcnt(16) covers both; a stage is
-    // refilled only after the transpose reads of its chunk have completed
-    // (lgkmcnt(0)). Scheduling barriers keep each wait, compute and refill in
-    // that order.
-    // chunks c = kv_begin + 32 n in pairs, alternating between the two LDS
-    // stages and two K register sets; chunk n + 1 is loaded while chunk n is
-    // computed, and only chunks that exist are loaded. Waits are explicit: a
-    // chunk's V (written to LDS by the memory unit) and K were issued before
-    // the 16 loads of the next chunk, so vmcnt(16) covers both (vmcnt(0) when
-    // nothing follows); a stage is refilled only after the transpose reads of
-    // its previous chunk have completed (lgkmcnt(0)). (Keeping two chunks in
-    // flight, with clamped trailing loads, measured 2.5 % slower.)
-    const int nch = kv_begin < kv_end ? (kv_end - kv_begin + kC - 1) / kC : 0;
-    uint4 KA[2][4], KB[2][4];
-    if (nch > 0) {
-      load_v(kv_begin, myV0);
-      load_k(kv_begin, KA);
-    }
-    for (int n = 0; n < nch; n += 2) {
-      const int c = kv_begin + n * kC;
-      const bool has1 = n + 1 < nch;
-      if (has1) {
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): stage 1 reads of chunk n - 1
-        load_v(c + kC, myV1);
-        load_k(c + kC, KB);
-        __builtin_amdgcn_s_waitcnt(0x4f70);  // vmcnt(16)
-      } else {
-        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-      }
-      compute(c, KA, myV0);
-      if (has1) {
-        if (n + 2 < nch) {
-          __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): stage 0 reads of chunk n
-          load_v(c + 2 * kC, myV0);
-          load_k(c + 2 * kC, KA);
-          __builtin_amdgcn_s_waitcnt(0x4f70);  // vmcnt(16)
-        } else {
-          __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-        }
-        compute(c + kC, KB, myV1);
-      }
-    }
-
-    // ---- rows: o = O / L, lse = m * scale + ln L (L summed over the lane groups)
-    float L = lsum;
-    L += __shfl_xor(L, 16);
-    L += __shfl_xor(L, 32);
-    const bool empty = !(L > 0.f);
-    const float inv = empty ? 0.f : 1.f / L;
-    const float lse = empty ? kNegInf : m * a.sm_scale + fast_log2(L) * kLn2;
-    if (l16 < G) {
-      if (slot < 0) {
-        const int64_t row = int64_t(b) * a.num_qo_heads + int64_t(h) * G + l16;
-#pragma unroll
-        for (int md = 0; md < 8; ++md) store4_dt(a.o, row * kD + md * 16 + 4 * g16, O[md] * inv,
-                                                 a.out_dtype);
-        if (a.lse && g16 == 0) a.lse[row] = lse;
-      } else {
-        const int64_t row = int64_t(slot) * (HT * G) + int64_t(wave) * G + l16;
-#pragma unroll
-        for (int md = 0; md < 8; ++md) {
-          const f32x4_t v = O[md] * inv;
-          *reinterpret_cast<float4*>(a.o_part + row * kD + md * 16 + 4 * g16) =
-              make_float4(v[0], v[1], v[2], v[3]);
-        }
-        if (g16 == 0) a.lse_part[row] = lse;
-      }
-    }
-    // this wave's next segment refills its LDS stages: finish reading them first
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-  }
+  dmi::decode_mfma_worker<T, G>(a, blockIdx.x);
 }
 
-// The same decode for an fp8 (OCP e4m3) KV cache. K and V rows are half as
-// wide, so each lane's share is loaded into registers as codes and widened
-// to the query's 16-bit type on the way to the matrix cores:
-//   * K: lane group g16 holds head dims [32 g16, 32 g16 + 32) of its token
-//     (32 contiguous bytes, two 16-byte loads per 16-token tile); piece kc of
-//     that range is the lane's 8 K-slots of product kc, and q is loaded with
-//     the same head-dim map (any map serves a dot product if q and K share it);
-//   * V: lane l loads 16 codes of row 8 i + l / 8 (four loads per chunk),
-//     widens them to two 16-byte chunks and writes them into its wave's LDS
-//     slice in the layout the transpose reads of the 16-bit kernel expect.
-// k_scale is folded into the logit scale on the host; v_scale multiplies the
-// final normalisation. With 16 VGPRs of K and V codes per chunk, both register
-// sets fit, so every wait is a register dependency.
 template <typename T, int G>
 __global__ __launch_bounds__(256, 2) void decode_mfma_fp8_kernel(AttnArgs a) {
-  static_assert(G == 4 || G == 8, "rows of one kv head fill at most one 16-row tile");
-  constexpr int HT = 4;
-  __shared__ __align__(16) uint16_t sV[HT][kC * kD];  // widened V of a wave's chunk
-
-  const ABP_CONST_AS int32_t* plan = const_as(a.plan);
-  const ABP_CONST_AS int32_t* wseg = plan + plan[H_OFF_WSEG];
-  const ABP_CONST_AS int32_t* segs = plan + plan[H_OFF_SEG];
-  const ABP_CONST_AS int32_t* tiles = plan + plan[H_OFF_TILE];
-  const ABP_CONST_AS int32_t* kv_indptr = const_as(a.kv_indptr);
-  const ABP_CONST_AS int32_t* kv_indices = const_as(a.kv_indices);
-  const int s_begin = wseg[blockIdx.x], s_end = wseg[blockIdx.x + 1];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g16 = lane >> 4;
-  const int l16 = lane & 15;
-  const float cl2 = a.sm_scale_log2;
-  const float thr = kRescaleLog2 / cl2;
-  const uint8_t* __restrict__ kp = static_cast<const uint8_t*>(a.k_pages);
-  const uint8_t* __restrict__ vp = static_cast<const uint8_t*>(a.v_pages);
-  const int P = a.page_size;
-  const int shift = a.page_shift;
-  const int tstride = a.token_stride;  // elements = bytes
-  uint16_t* const sv = sV[wave];
-
-  for (int s = s_begin; s < s_end; ++s) {
-    const int tile = segs[4 * s];
-    const int kv_begin = segs[4 * s + 1], kv_end = segs[4 * s + 2], slot = segs[4 * s + 3];
-    const int b = tiles[4 * tile], h = tiles[4 * tile + 1] + wave;
-    const int ip0 = kv_indptr[b];
-
-    // q of row l16 (< G), head dims 32 g16 + 8 kc .. + 7 for product kc
-    uint4 qf[4];
-    {
-      const int qr = l16 < G ? l16 : G - 1;
-      const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
-                             (int64_t(b) * a.num_qo_heads + int64_t(h) * G + qr) * kD + 32 * g16;
-      const uint32_t keep = l16 < G ? 0xffffffffu : 0u;
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        const uint4 v = *reinterpret_cast<const uint4*>(qrow + 8 * kc);
-        qf[kc] = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
-      }
-    }
-
-    float m = kNegInf, lsum = 0.f;
-    f32x4_t O[8];
-#pragma unroll
-    for (int md = 0; md < 8; ++md) O[md] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    auto row_base = [&](int t) -> int64_t {
-      return int64_t(kv_indices[ip0 + (t >> shift)]) * a.page_stride +
-             int64_t(t & (P - 1)) * tstride + int64_t(h) * kD;
-    };
-    // K codes of chunk c: tile mb (a tile past kv_end re-reads tile 0, in
-    // bounds and masked); lane: token l16, bytes 32 g16 .. 32 g16 + 31
-    auto load_k = [&](int c, uint4 (&kr)[2][2]) {
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const int t0 = (c + 16 * mb < kv_end) ? c + 16 * mb : c;
-        const uint8_t* rp = kp + row_base(t0) + int64_t(l16) * tstride + 32 * g16;
-        kr[mb][0] = *reinterpret_cast<const uint4*>(rp);
-        kr[mb][1] = *reinterpret_cast<const uint4*>(rp + 16);
-      }
-    };
-    // V codes of chunk c: piece i is row 8 i + l / 8, bytes 16 (l % 8) .. + 15
-    auto load_v = [&](int c, uint4 (&vr)[4]) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 8 * i + (lane >> 3);
-        const int t0 = (c + 16 * (r >> 4) < kv_end) ? c + 16 * (r >> 4) : c;
-        vr[i] = *reinterpret_cast<const uint4*>(vp + row_base(t0) + int64_t(r & 15) * tstride +
-                                                16 * (lane & 7));
-      }
-    };
-
-    auto compute = [&](int c, const uint4 (&kr)[2][2], const uint4 (&vr)[4])
-                       __attribute__((always_inline)) {
-      // widened V into the wave's LDS slice: the 16 codes of a lane are the
-      // row's logical 16-byte chunks q0 = 2 (l % 8) and q0 + 1, held at
-      // positions q0 ^ (2 (row & 7)) and the one after (the swizzle is even)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 8 * i + (lane >> 3);
-        const int p0 = (2 * (lane & 7)) ^ (2 * (r & 7));
-        uint16_t* dst = sv + r * kD + p0 * 8;
-        *reinterpret_cast<uint4*>(dst) = widen8<T>(vr[i].x, vr[i].y);
-        *reinterpret_cast<uint4*>(dst + 8) = widen8<T>(vr[i].z, vr[i].w);
-      }
-      f32x4_t S[2];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        S[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        S[mb] = mfma16<T>(widen8<T>(kr[mb][0].x, kr[mb][0].y), qf[0], S[mb]);
-        S[mb] = mfma16<T>(widen8<T>(kr[mb][0].z, kr[mb][0].w), qf[1], S[mb]);
-        S[mb] = mfma16<T>(widen8<T>(kr[mb][1].x, kr[mb][1].y), qf[2], S[mb]);
-        S[mb] = mfma16<T>(widen8<T>(kr[mb][1].z, kr[mb][1].w), qf[3], S[mb]);
-      }
-      if (c + kC > kv_end) {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (c + 16 * mb + 4 * g16 + j >= kv_end) S[mb][j] = kNegInf;
-      }
-      float mx = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(S[0][0], S[0][1]),
-                                                 __builtin_fmaxf(S[0][2], S[0][3])),
-                                 __builtin_fmaxf(__builtin_fmaxf(S[1][0], S[1][1]),
-                                                 __builtin_fmaxf(S[1][2], S[1][3])));
-      mx = max4groups(mx);
-      if (__builtin_amdgcn_ballot_w64(mx > m + thr)) {
-        const float mn = __builtin_fmaxf(m, mx);
-        const float alpha = mn == kNegInf ? 1.f : fast_exp2((m - mn) * cl2);
-        m = mn;
-        lsum *= alpha;
-#pragma unroll
-        for (int md = 0; md < 8; ++md) O[md] *= alpha;
-      }
-      const float mc = (m == kNegInf ? 0.f : m) * cl2;
-      float p[2][4];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) p[mb][j] = fast_exp2(__builtin_fmaf(S[mb][j], cl2, -mc));
-      lsum += ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) +
-              ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
-      const uint4 pB = make_uint4(pack2<T>(p[0][0], p[0][1]), pack2<T>(p[0][2], p[0][3]),
-                                  pack2<T>(p[1][0], p[1][1]), pack2<T>(p[1][2], p[1][3]));
-      const int kA = 4 * g16 + (l16 >> 2);
-      const int kB = kA + 16;
-#pragma unroll
-      for (int md = 0; md < 8; ++md) {
-        const int d0 = md * 16 + 4 * (l16 & 3);
-        const int offA = kA * kD + (((d0 >> 3) ^ (2 * (kA & 7))) * 8) + (d0 & 7);
-        const int offB = kB * kD + (((d0 >> 3) ^ (2 * (kB & 7))) * 8) + (d0 & 7);
-        const v4i16_t a4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ABP_LDS v4i16_t*)(sv + offA));
-        const v4i16_t b4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ABP_LDS v4i16_t*)(sv + offB));
-        const uint2 av = __builtin_bit_cast(uint2, a4), bv = __builtin_bit_cast(uint2, b4);
-        O[md] = mfma16<T>(make_uint4(av.x, av.y, bv.x, bv.y), pB, O[md]);
-      }
-    };
-
-    // chunk n + 1 is loaded while chunk n is computed; only chunks that exist
-    const int nch = kv_begin < kv_end ? (kv_end - kv_begin + kC - 1) / kC : 0;
-    uint4 KA[2][2], KB[2][2], VA[4], VB[4];
-    if (nch > 0) {
-      load_k(kv_begin, KA);
-      load_v(kv_begin, VA);
-    }
-    for (int n = 0; n < nch; n += 2) {
-      const int c = kv_begin + n * kC;
-      const bool has1 = n + 1 < nch;
-      if (has1) {
-        load_k(c + kC, KB);
-        load_v(c + kC, VB);
-      }
-      compute(c, KA, VA);
-      if (has1) {
-        if (n + 2 < nch) {
-          load_k(c + 2 * kC, KA);
-          load_v(c + 2 * kC, VA);
-        }
-        compute(c + kC, KB, VB);
-      }
-    }
-
-    float L = lsum;
-    L += __shfl_xor(L, 16);
-    L += __shfl_xor(L, 32);
-    const bool empty = !(L > 0.f);
-    const float inv = empty ? 0.f : a.v_scale / L;  // the values are v_scale times their codes
-    const float lse = empty ? kNegInf : m * a.sm_scale + fast_log2(L) * kLn2;
-    if (l16 < G) {
-      if (slot < 0) {
-        const int64_t row = int64_t(b) * a.num_qo_heads + int64_t(h) * G + l16;
-#pragma unroll
-        for (int md = 0; md < 8; ++md) store4_dt(a.o, row * kD + md * 16 + 4 * g16, O[md] * inv,
-                                                 a.out_dtype);
-        if (a.lse && g16 == 0) a.lse[row] = lse;
-      } else {
-        const int64_t row = int64_t(slot) * (HT * G) + int64_t(wave) * G + l16;
-#pragma unroll
-        for (int md = 0; md < 8; ++md) {
-          const f32x4_t v = O[md] * inv;
-          *reinterpret_cast<float4*>(a.o_part + row * kD + md * 16 + 4 * g16) =
-              make_float4(v[0], v[1], v[2], v[3]);
-        }
-        if (g16 == 0) a.lse_part[row] = lse;
-      }
-    }
-  }
+  dmi::decode_mfma_fp8_worker<T, G>(a, blockIdx.x);
 }
 
 template <typename T>

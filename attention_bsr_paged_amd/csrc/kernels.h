@@ -46,6 +46,11 @@ int decode_mfma_blocks_per_cu(const Config& cfg);
 int decode_blocks_per_cu(const Config& cfg);
 int append_blocks_per_cu(const Config& cfg);
 hipError_t launch_append(const Config& cfg, const AttnArgs& a, hipStream_t stream);
+// mixed batch: workgroups [0, app.workers) run append workers, the next
+// dec.workers run matrix-core decode workers (cfg: the append part's config)
+bool pod_applies(const Config& cfg);
+hipError_t launch_pod(const Config& cfg, const AttnArgs& app, const AttnArgs& dec,
+                      hipStream_t stream);
 // copies `bytes` (multiple of 4, 16-byte aligned pointers) from pinned host
 // memory mapped into the GPU's address space to device memory
 hipError_t launch_upload(void* dev_dst, const void* host_src_mapped, size_t bytes,

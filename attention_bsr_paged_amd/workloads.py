@@ -470,3 +470,52 @@ def batch_decode_fp8(seed: int = 1009) -> Workload:
     w.k_scale = w.v_scale = 0.25
     w.name = "batch_decode_fp8kv_b64_gqa32x8_d128_p16_kv512-4096"
     return w
+
+
+# ----------------------------------------------------------------------------
+# mixed batches: decode and append requests over one page pool
+# ----------------------------------------------------------------------------
+@dataclass
+class PodWorkload:
+    """Decode requests and append requests of one KV cache: both parts' page
+    tables index the same pools (k_pages, v_pages)."""
+    name: str
+    dec: Workload                 # kv.k_pages / kv.v_pages are the shared pools
+    app: Workload                 # its kv_indices index the shared pools too
+    meta: Dict[str, object] = field(default_factory=dict)
+
+
+def mixed_batch(dec: Workload, app: Workload, name: str) -> PodWorkload:
+    """Put the pages of an append workload after those of a decode workload in
+    one pool and shift the append page table accordingly."""
+    assert dec.kv.page_size == app.kv.page_size and dec.dtype == app.dtype
+    n = dec.kv.k_pages.shape[0]
+    k = np.concatenate([dec.kv.k_pages, app.kv.k_pages])
+    v = np.concatenate([dec.kv.v_pages, app.kv.v_pages])
+    dkv = PagedKV(dec.kv.page_size, dec.kv.num_kv_heads, dec.kv.head_dim, dec.kv.dtype,
+                  dec.kv.kv_len, dec.kv.kv_indptr, dec.kv.kv_indices, dec.kv.kv_last_page_len,
+                  k, v)
+    akv = PagedKV(app.kv.page_size, app.kv.num_kv_heads, app.kv.head_dim, app.kv.dtype,
+                  app.kv.kv_len, app.kv.kv_indptr, (app.kv.kv_indices + n).astype(np.int32),
+                  app.kv.kv_last_page_len, k, v)
+    dec.kv, app.kv = dkv, akv
+    return PodWorkload(name, dec, app)
+
+
+def pod_mixed(seed: int = 1010) -> PodWorkload:
+    """A mixed batch: the batch decode shape (64 requests, kv_len U{512..4096},
+    GQA 32/8, d 128, page 16, bf16; seed 1010) beside a chunked prefill of 4
+    requests, each appending a 512-token chunk causally onto existing kv_len
+    U{1024..4096} (seed 1011), in one page pool."""
+    dec = batch_decode_gqa(seed)
+    rng = np.random.Generator(np.random.PCG64(seed + 1))
+    Hq, Hkv, d, P, B = 32, 8, 128, 16, 4
+    qo_len = np.full(B, 512)
+    existing = rng.integers(1024, 4096, size=B, endpoint=True)
+    qo_indptr = np.zeros(B + 1, dtype=np.int32)
+    qo_indptr[1:] = np.cumsum(qo_len)
+    q = normal_bits(rng, (int(qo_indptr[-1]), Hq, d), BF16)
+    kv = make_paged_kv(rng, existing + qo_len, P, Hkv, d, BF16)
+    app = Workload("chunked_prefill_4x512", "append", seed + 1, BF16, Hq, Hkv, d, kv, q,
+                   qo_indptr=qo_indptr, causal=True)
+    return mixed_batch(dec, app, "pod_decode64_kv512-4096_prefill4x512_gqa32x8_d128_bf16_p16")

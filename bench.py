@@ -53,7 +53,7 @@ FLUSH_BYTES = 2 * 2 ** 30       # K/V replicas rotated per step (>> 256 MB MALL)
 # Counter readings (FETCH_SIZE / WRITE_SIZE) of the decode run and of a plain
 # copy, recorded by rocprofv3; valid only while the kernel sources hash the same.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_run_batch_decode_traffic.txt")
-DECODE_SOURCES = ["decode.hip", "decode_mfma.hip", "merge.hip", "common.h", "kernels.h", "layout.h"]
+DECODE_SOURCES = ["decode.hip", "decode_mfma.hip", "decode_mfma_impl.h", "merge.hip", "common.h", "kernels.h", "layout.h"]
 
 
 PAGE_APPEND_TRAFFIC_FILE = os.path.join(ROOT, "profiles",
@@ -292,6 +292,76 @@ def bench_append(abp, wl, torch, dev, K, Wm, workers=0) -> dict:
         "workers": app.plan_struct.num_workers,
         "segments": app.plan_struct.num_segments,
         "merged_tiles": app.plan_struct.num_merges,
+        "kv_pool_copies": copies,
+    }
+
+
+# ----------------------------------------------------------------------------
+# mixed batch: decode + append in one launch, against the two runs in turn
+# ----------------------------------------------------------------------------
+def bench_pod(abp, wl, torch, dev, K, Wm) -> dict:
+    w = wl.pod_mixed()
+    d, a = w.dec, w.app
+    by = decode_bytes(d)
+    flops = append_flops(a)
+    k0 = wl.to_torch(d.kv.k_pages, d.dtype, dev)
+    v0 = wl.to_torch(d.kv.v_pages, d.dtype, dev)
+    ks, copies = replicas(k0, torch, k0.nbytes + v0.nbytes)
+    vs, _ = replicas(v0, torch, k0.nbytes + v0.nbytes)
+    i32 = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.int32)).to(dev)
+    qd, qa = wl.to_torch(d.q, d.dtype, dev), wl.to_torch(a.q, a.dtype, dev)
+    d_ip, d_ix, d_lp = i32(d.kv.kv_indptr), i32(d.kv.kv_indices), i32(d.kv.kv_last_page_len)
+    qo, a_ip, a_ix, a_lp = (i32(a.qo_indptr), i32(a.kv.kv_indptr), i32(a.kv.kv_indices),
+                            i32(a.kv.kv_last_page_len))
+    nd, na, nq = d.batch, len(a.kv.kv_indptr) - 1, int(a.qo_indptr[-1])
+    pd = abp.make_params(32, 8, 128, 16, torch.bfloat16)
+    pa = abp.make_params(32, 8, 128, 16, torch.bfloat16, causal=True)
+    dec = abp.BatchDecode(pd, max_batch=nd, device=dev)
+    app = abp.BatchAppend(pa, max_batch=na, max_qo_tokens=nq, device=dev)
+    pod = abp.PodAttention(pa, nd, na, nq, device=dev)
+    od, ld = torch.empty_like(qd), torch.empty(qd.shape[:2], dtype=torch.float32, device=dev)
+    oa, la = torch.empty_like(qa), torch.empty(qa.shape[:2], dtype=torch.float32, device=dev)
+    s = torch.cuda.current_stream(dev)
+    dec.plan(d.kv.kv_indptr, d.kv.kv_last_page_len, stream=s)
+    app.plan(a.qo_indptr, a.kv.kv_indptr, a.kv.kv_last_page_len, stream=s)
+    plan = pod.plan(d.kv.kv_indptr, d.kv.kv_last_page_len, a.qo_indptr, a.kv.kv_indptr,
+                    a.kv.kv_last_page_len, stream=s)
+
+    def seq(i, evs):
+        if evs:
+            evs[0].record(s)
+        dec.run(qd, ks[i % copies], vs[i % copies], d_ip, d_ix, d_lp, o=od, lse=ld, stream=s)
+        app.run(qa, ks[i % copies], vs[i % copies], qo, a_ip, a_ix, a_lp, o=oa, lse=la, stream=s)
+        if evs:
+            evs[1].record(s)
+
+    def mixed(i, evs):
+        if evs:
+            evs[0].record(s)
+        pod.run(qd, qa, ks[i % copies], vs[i % copies], d_ip, d_ix, d_lp, qo, a_ip, a_ix, a_lp,
+                o_decode=od, lse_decode=ld, o_append=oa, lse_append=la, stream=s)
+        if evs:
+            evs[1].record(s)
+
+    _, seq_ms = timed_steps(torch, s, seq, K, Wm)
+    wall, pod_ms = timed_steps(torch, s, mixed, K, Wm)
+    torch.cuda.synchronize()
+    t_seq, t_pod = float(seq_ms.mean()), float(pod_ms.mean())
+    return {
+        "workload": w.name,
+        "value": round(t_seq / t_pod, 4),
+        "unit": "speedup over the decode run then the append run",
+        "run": _stats_ms(pod_ms),
+        "sequential_run": _stats_ms(seq_ms),
+        "ms_per_step": round(wall, 5),
+        "decode_bytes": by,
+        "append_causal_flop": flops,
+        "decode_TBps_over_run": round(by / (t_pod * 1e-3) / 1e12, 4),
+        "append_TFLOPs_over_run": round(flops / (t_pod * 1e-3) / 1e12, 2),
+        "split": {"groups": plan.num_groups, "decode": plan.decode.num_workers,
+                  "append": plan.append.num_workers},
+        "sequential_workers": {"decode": dec.plan_struct.num_workers,
+                               "append": app.plan_struct.num_workers},
         "kv_pool_copies": copies,
     }
 
@@ -629,7 +699,7 @@ def main(argv=None) -> int:
                     help="skip the single, skewed and cascade workloads")
     ap.add_argument("--part", default="all",
                     choices=["all", "decode", "append", "single", "skewed", "cascade", "copy",
-                             "bsr", "page_append", "fp8_decode", "g8_decode"],
+                             "bsr", "page_append", "fp8_decode", "g8_decode", "pod"],
                     help="one workload alone (profiling); 'all' is the benchmark line")
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -662,6 +732,9 @@ def main(argv=None) -> int:
         return 0
     if part == "page_append":
         print(json.dumps(bench_page_append(abp, wl, torch, dev, K, Wm)), flush=True)
+        return 0
+    if part == "pod":
+        print(json.dumps(bench_pod(abp, wl, torch, dev, K, Wm)), flush=True)
         return 0
     if part in ("single", "skewed", "fp8_decode", "g8_decode"):
         w = {"single": wl.single_decode_mha, "skewed": wl.skewed_decode_gqa,
@@ -736,12 +809,13 @@ def main(argv=None) -> int:
             "bsr_sparse": bench_bsr(abp, wl, torch, dev, Kc, 5),
             "page_append": bench_page_append(abp, wl, torch, dev, Kc, 5),
             "fp8_batch_decode": bench_decode(abp, wl, torch, dev, wl.batch_decode_fp8(), Kc, 5),
+            "pod_mixed": bench_pod(abp, wl, torch, dev, Kc, 5),
         }
         f8 = out["next"]["fp8_batch_decode"]
         f8["roofline"] = {"bound": "hbm", "achieved": round(f8["run_TBps"] * 1e3, 1),
                           "peak": HBM_PEAK_TBS * 1e3, "unit": "GB/s",
                           "frac": round(f8["run_TBps"] / HBM_PEAK_TBS, 4), "traffic": None,
-                          "kernel": "decode run, e4m3 K/V (decode_kernel + plan_merge_kernel)",
+                          "kernel": "decode run, e4m3 K/V (decode_mfma_fp8_kernel + plan_merge_kernel)",
                           "avg_launch_us": f8["run"]["avg_us"]}
         f8["kv_tokens_per_s"] = round(f8["kv_tokens"] / (f8["run"]["avg_us"] * 1e-6), 1)
         out["copy_context"] = bench_copy(torch, dev, 20, 3)

@@ -294,6 +294,80 @@ int abp_append_paged_kv(const abp_params* params, int32_t batch, int64_t nnz, co
                         void* v_pages, const int32_t* kv_indptr_d, const int32_t* kv_indices_d,
                         const int32_t* kv_last_page_len_d, abp_stream_t stream);
 
+/* Mixed batches: decode requests and append (prefill) requests in one plan and
+ * one persistent launch (the POD kernels of the README page, section 核心功能 /
+ * 注意力机制内核). Decode is bound by HBM bandwidth and append by the matrix
+ * cores; the launch gives num_groups workgroups (one per compute unit) one
+ * role each, decode or append, so both run at the same time.
+ *
+ * The plan holds two sub-plans, each exactly what abp_plan_host makes for its
+ * kind with its own worker count: decode.num_workers decode workers and
+ * append.num_workers = num_groups - decode.num_workers append workers (0 when
+ * that part has no request). The split is decode_groups if > 0 (clamped so
+ * each part with requests keeps at least one workgroup); otherwise the planner
+ * chooses it so that both parts are predicted to end together, from the
+ * decode part's K/V bytes against a measured curve of decode bandwidth over
+ * compute units and the append part's visible (query, key) pairs at the
+ * append kernel's measured rate per compute unit. Outputs are those of
+ * abp_decode_run and abp_append_run on the two parts.
+ *
+ * Requires: no RoPE, 16-bit K/V (no kv_fp8), a power-of-two page_size >= 16,
+ * num_kv_heads a multiple of 4, group 4 or 8 (ABP_ERR_UNSUPPORTED otherwise).
+ * params->causal applies to the append part. Both parts read the same page
+ * pools (k_pages, v_pages) through their own page tables.
+ *
+ * Workspace: abp_pod_workspace_size; the host and device workspaces hold the
+ * decode sub-plan, then the append one, at the offsets the plan records.
+ * num_groups <= 0 means the compute units of the current device. */
+typedef struct abp_pod_plan_t {
+  abp_plan decode;             /* decode sub-plan (num_workers 0: no decode part) */
+  abp_plan append;             /* append sub-plan (num_workers 0: no append part) */
+  int32_t num_groups;          /* workgroups of the launch */
+  int32_t reserved;
+  uint64_t decode_host_offset, append_host_offset; /* byte offsets in host_ws */
+  uint64_t decode_dev_offset, append_dev_offset;   /* byte offsets in dev_ws */
+  uint64_t decode_dev_bytes, append_dev_bytes;     /* device region sizes */
+} abp_pod_plan_t;
+
+int abp_pod_workspace_size(const abp_params* params, int32_t max_decode_batch,
+                           int32_t max_append_batch, int32_t max_qo_tokens, int32_t num_groups,
+                           size_t* host_bytes, size_t* dev_bytes);
+
+/* Host-only planning (no HIP call when num_groups > 0): validates both parts'
+ * index arrays as abp_plan_host does. The decode part has decode_batch
+ * requests (d_*), the append part append_batch requests (qo_indptr_h, a_*). */
+int abp_pod_plan_host(const abp_params* params, int32_t decode_batch,
+                      const int32_t* d_kv_indptr_h, const int32_t* d_kv_last_page_len_h,
+                      int32_t append_batch, const int32_t* qo_indptr_h,
+                      const int32_t* a_kv_indptr_h, const int32_t* a_kv_last_page_len_h,
+                      int32_t max_decode_batch, int32_t max_append_batch, int32_t max_qo_tokens,
+                      int32_t num_groups, int32_t decode_groups, void* host_ws,
+                      size_t host_bytes, abp_pod_plan_t* plan);
+
+/* abp_pod_plan_host, then the upload of both sub-plans to dev_ws on `stream`
+ * (as abp_decode_plan). */
+int abp_pod_plan(const abp_params* params, int32_t decode_batch, const int32_t* d_kv_indptr_h,
+                 const int32_t* d_kv_last_page_len_h, int32_t append_batch,
+                 const int32_t* qo_indptr_h, const int32_t* a_kv_indptr_h,
+                 const int32_t* a_kv_last_page_len_h, int32_t max_decode_batch,
+                 int32_t max_append_batch, int32_t max_qo_tokens, int32_t num_groups,
+                 int32_t decode_groups, void* host_ws, size_t host_bytes, void* dev_ws,
+                 size_t dev_bytes, abp_stream_t stream, abp_pod_plan_t* plan);
+
+/* One launch of num_groups workgroups runs both parts, then the plan-merge
+ * launches of each part merge their split tiles. q_decode [decode_batch, Hq,
+ * d] -> o_decode / lse_decode as abp_decode_run; q_append [total_qo_tokens,
+ * Hq, d] -> o_append / lse_append as abp_append_run (lse pointers may be
+ * NULL). Device index arrays as planned. No allocation; graph-capturable. */
+int abp_pod_run(const abp_pod_plan_t* plan, const abp_params* params, const void* q_decode,
+                const void* q_append, const void* k_pages, const void* v_pages,
+                const int32_t* d_kv_indptr_d, const int32_t* d_kv_indices_d,
+                const int32_t* d_kv_last_page_len_d, const int32_t* qo_indptr_d,
+                const int32_t* a_kv_indptr_d, const int32_t* a_kv_indices_d,
+                const int32_t* a_kv_last_page_len_d, void* o_decode, float* lse_decode,
+                void* o_append, float* lse_append, void* dev_ws, size_t dev_bytes,
+                abp_stream_t stream);
+
 /* Merge two attention states over disjoint key sets (cascade: prefix and suffix).
  * o_a, o_b [num_rows, head_dim] in in_dtype; lse_a, lse_b [num_rows] float32;
  * writes o_out [num_rows, head_dim] in out_dtype and lse_out (may be NULL).

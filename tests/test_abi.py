@@ -308,3 +308,101 @@ def test_rope_interleave_param(lib):
     with pytest.raises(abp.AbpError) as e:
         abp.abp_workspace_size(0, bad, 2, 0, 8)
     assert e.value.status == abp.ABP_ERR_INVALID_ARG
+
+
+# ----------------------------------------------------------------------------
+# mixed decode + append batches (one plan, two sub-plans)
+# ----------------------------------------------------------------------------
+def _pod_ws(p, md, ma, mq, groups):
+    h, _ = abp.abp_pod_workspace_size(p, md, ma, mq, groups)
+    return np.zeros(h, np.uint8)
+
+
+def _pod_case(rng, B, P_, causal):
+    kv_len = rng.integers(0 if not causal else 1, 3000, size=B)
+    pages = (kv_len + P_ - 1) // P_
+    indptr = np.concatenate([[0], np.cumsum(pages)]).astype(np.int32)
+    lpl = np.where(pages > 0, kv_len - (pages - 1) * P_, 1).astype(np.int32)
+    return kv_len, indptr, lpl
+
+
+@pytest.mark.parametrize("groups,decode_groups", [(256, 0), (256, 40), (16, 0), (2, 0), (9, 3)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_pod_subplans_match_reference(lib, groups, decode_groups, causal):
+    """Each sub-plan is the reference plan of its part with the split's worker counts."""
+    rng = np.random.default_rng(groups + decode_groups + causal)
+    p = P(causal=causal)
+    _, d_indptr, d_lpl = _pod_case(rng, 9, 16, False)
+    a_len, a_indptr, a_lpl = _pod_case(rng, 5, 16, True)
+    qo_len = np.minimum(rng.integers(1, 600, size=5), a_len)
+    qo = np.concatenate([[0], np.cumsum(qo_len)]).astype(np.int32)
+    ws = _pod_ws(p, 9, 5, int(qo[-1]), groups)
+    plan = abp.abp_pod_plan_host(p, d_indptr, d_lpl, qo, a_indptr, a_lpl, 9, 5, int(qo[-1]),
+                                 groups, decode_groups, ws)
+    wd, wa = plan.decode.num_workers, plan.append.num_workers
+    assert plan.num_groups == groups and wd + wa == groups and wd >= 1 and wa >= 1
+    if decode_groups:
+        assert wd == decode_groups
+    elif groups >= 16:
+        assert wd % 8 == 0
+    dblob = ws[plan.decode_host_offset:plan.append_host_offset]
+    ablob = ws[plan.append_host_offset:]
+    got_d = abp.decode_plan_arrays(dblob, plan.decode)
+    ref_d = plan_ref(KIND_DECODE, 9, d_indptr, d_lpl, 16, 8, wd, 64, heads_per_tile=4)
+    for k, v in ref_d.items():
+        assert np.array_equal(got_d[k], v), k
+    got_a = abp.decode_plan_arrays(ablob, plan.append)
+    ref_a = plan_ref(KIND_APPEND, 5, a_indptr, a_lpl, 16, 8, wa, 64, qo_indptr=qo,
+                     tile_q=256 // 4, causal=causal)
+    for k, v in ref_a.items():
+        assert np.array_equal(got_a[k], v), k
+    assert int(got_d["merge_kernel"][0]) == 1
+
+
+def test_pod_split_follows_the_work(lib):
+    """More decode bytes against the same append work gets more decode groups;
+    a part with no request gets no group."""
+    p = P(causal=True)
+    qo = np.array([0, 512], np.int32)
+    a_indptr, a_lpl = np.array([0, 160], np.int32), np.array([16], np.int32)
+    splits = []
+    for n in (4, 64, 512):
+        d_indptr = (np.arange(n + 1) * 128).astype(np.int32)   # 2048 tokens each
+        d_lpl = np.full(n, 16, np.int32)
+        ws = _pod_ws(p, n, 1, 512, 256)
+        plan = abp.abp_pod_plan_host(p, d_indptr, d_lpl, qo, a_indptr, a_lpl, n, 1, 512, 256,
+                                     0, ws)
+        splits.append(plan.decode.num_workers)
+    assert splits[0] < splits[1] < splits[2] <= 248, splits
+    ws = _pod_ws(p, 4, 1, 512, 256)
+    only_a = abp.abp_pod_plan_host(p, None, None, qo, a_indptr, a_lpl, 4, 1, 512, 256, 0, ws)
+    assert (only_a.decode.num_workers, only_a.append.num_workers) == (0, 256)
+    only_d = abp.abp_pod_plan_host(p, [0, 1], [5], None, None, None, 4, 1, 512, 256, 0, ws)
+    assert (only_d.decode.num_workers, only_d.append.num_workers) == (256, 0)
+
+
+@pytest.mark.parametrize("kw", [dict(rope_theta=1e4), dict(page_size=8), dict(num_qo_heads=16),
+                                dict(num_kv_heads=2, num_qo_heads=8),
+                                dict(kv_fp8=True, k_scale=1.0, v_scale=1.0)])
+def test_pod_rejects_unsupported_params(lib, kw):
+    with pytest.raises(abp.AbpError) as e:
+        abp.abp_pod_workspace_size(P(**kw), 4, 4, 64, 256)
+    assert e.value.status == abp.ABP_ERR_UNSUPPORTED
+
+
+def test_pod_plan_errors(lib):
+    p = P()
+    ws = _pod_ws(p, 2, 1, 8, 256)
+    qo = np.array([0, 4], np.int32)
+    with pytest.raises(abp.AbpError) as e:      # more decode requests than planned for
+        abp.abp_pod_plan_host(p, [0, 1, 2, 3], [1, 1, 1], qo, [0, 1], [4], 2, 1, 8, 256, 0, ws)
+    assert e.value.status == abp.ABP_ERR_WORKSPACE_TOO_SMALL
+    with pytest.raises(abp.AbpError) as e:      # host workspace too small
+        abp.abp_pod_plan_host(p, [0, 1], [1], qo, [0, 1], [4], 2, 1, 8, 256, 0, ws[:100])
+    assert e.value.status == abp.ABP_ERR_WORKSPACE_TOO_SMALL
+    with pytest.raises(abp.AbpError) as e:      # a bad decode page table
+        abp.abp_pod_plan_host(p, [0, 1], [0], qo, [0, 1], [4], 2, 1, 8, 256, 0, ws)
+    assert e.value.status == abp.ABP_ERR_INVALID_ARG
+    with pytest.raises(abp.AbpError) as e:      # one workgroup cannot hold both roles
+        abp.abp_pod_workspace_size(p, 2, 1, 8, 1)
+    assert e.value.status == abp.ABP_ERR_INVALID_ARG
