@@ -179,6 +179,11 @@ double pod_decode_bw(double cus) {
 }
 // append kernel throughput per compute unit (ragged causal append, bf16)
 constexpr double kPodAppendFlopPerCu = 3.0e12;
+// Decode beside a running append is slower than on the same compute units
+// alone: the append's K/V traffic competes for the memory system. Measured on
+// the mixed benchmark batch (64 decode requests, 4 x 512-token prefill
+// chunks), the launch took 1.08 to 1.24 times the slower part's time alone.
+constexpr double kPodDecodeSlowdown = 1.2;
 
 int64_t pod_kv_len(const int32_t* indptr, const int32_t* lpl, int32_t b, int32_t page) {
   const int64_t n = int64_t(indptr[b + 1]) - indptr[b];
@@ -209,7 +214,8 @@ int32_t pod_split(const abp::Config& cfg, int32_t groups, int32_t decode_batch,
   int32_t best = step, lo = step, hi = groups - step;
   double best_t = 1e300;
   for (int32_t g = lo; g <= hi; g += step) {
-    const double t = std::max(bytes / pod_decode_bw(g), flop / (kPodAppendFlopPerCu * (groups - g)));
+    const double t = std::max(kPodDecodeSlowdown * bytes / pod_decode_bw(g),
+                              flop / (kPodAppendFlopPerCu * (groups - g)));
     if (t < best_t) {
       best_t = t;
       best = g;
