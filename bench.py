@@ -358,6 +358,15 @@ def bench_pod(abp, wl, torch, dev, K, Wm) -> dict:
         "append_causal_flop": flops,
         "decode_TBps_over_run": round(by / (t_pod * 1e-3) / 1e12, 4),
         "append_TFLOPs_over_run": round(flops / (t_pod * 1e-3) / 1e12, 2),
+        # the decode part's HBM bytes bound the batch (at peak they take longer
+        # than the append part's flop at the dense bf16 peak)
+        "roofline": {"bound": "hbm", "achieved": round(by / (t_pod * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_TBS * 1e3, "unit": "GB/s",
+                     "frac": round(by / (t_pod * 1e-3) / 1e12 / HBM_PEAK_TBS, 4),
+                     "traffic": None,
+                     "kernel": "pod_kernel + the two plan merges (one run; it also does the "
+                               "append part's flop)",
+                     "avg_launch_us": round(t_pod * 1e3, 2)},
         "split": {"groups": plan.num_groups, "decode": plan.decode.num_workers,
                   "append": plan.append.num_workers},
         "sequential_workers": {"decode": dec.plan_struct.num_workers,
@@ -642,6 +651,19 @@ def cpu_baseline_append(w, budget_s: float = 8.0) -> dict:
                       f"thread", "host_cpu": model, "host_cores_available": avail}
 
 
+def cpu_baseline_pod(w, budget_s: float = 3.0) -> dict:
+    """The oracle on the mixed batch: its decode and append rates, each measured
+    as in the decode and append baselines on that part, give the time of the
+    whole batch."""
+    d = cpu_baseline_decode(w.dec, budget_s)
+    a = cpu_baseline_append(w.app, budget_s)
+    t = decode_bytes(w.dec) / (d["value"] * 1e12) + append_flops(w.app) / (a["value"] * 1e12)
+    return {"value": round(t, 3), "unit": "s per mixed batch", "cores": 1, "kind": "oracle",
+            "sample": f"decode part: {d['sample']}; append part: {a['sample']}; the batch's "
+                      f"decode bytes and append flop at those rates",
+            "host_cpu": d["host_cpu"], "host_cores_available": d["host_cores_available"]}
+
+
 def cpu_baseline_bsr(w, budget_s: float = 6.0) -> dict:
     """The fp64 oracle on runs of 8 query rows at random places (all heads)."""
     from threadpoolctl import threadpool_limits
@@ -829,6 +851,7 @@ def main(argv=None) -> int:
                 cpu_baseline_page_append(wl.ragged_page_append())
             out["next"]["fp8_batch_decode"]["cpu_baseline"] = \
                 cpu_baseline_decode(wl.batch_decode_fp8(), budget_s=4.0)
+            out["next"]["pod_mixed"]["cpu_baseline"] = cpu_baseline_pod(wl.pod_mixed())
     print(json.dumps(out), flush=True)
     return 0
 
