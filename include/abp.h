@@ -358,7 +358,11 @@ int abp_pod_plan(const abp_params* params, int32_t decode_batch, const int32_t* 
  * launches of each part merge their split tiles. q_decode [decode_batch, Hq,
  * d] -> o_decode / lse_decode as abp_decode_run; q_append [total_qo_tokens,
  * Hq, d] -> o_append / lse_append as abp_append_run (lse pointers may be
- * NULL). Device index arrays as planned. No allocation; graph-capturable. */
+ * NULL). Device index arrays as planned. No allocation; graph-capturable. A
+ * captured run keeps the worker counts of the plan it was captured with, so it
+ * may be replayed after a re-plan only if both sub-plans keep theirs: pass the
+ * same decode_groups and num_groups, keep both parts non-empty and keep the
+ * capacities. */
 int abp_pod_run(const abp_pod_plan_t* plan, const abp_params* params, const void* q_decode,
                 const void* q_append, const void* k_pages, const void* v_pages,
                 const int32_t* d_kv_indptr_d, const int32_t* d_kv_indices_d,

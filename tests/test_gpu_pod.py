@@ -127,3 +127,70 @@ def test_pod_benchmark_batch_sampled():
     oa_ref, la_ref = ora.append_workload(w.app, token_ids=toks)
     assert_parity(oa, la, oa_ref, la_ref, "bf16", rows=toks, what="pod bench append sample")
     assert np.all(np.isfinite(od)) and np.all(np.isfinite(oa))
+
+
+def test_pod_graph_replay_with_fixed_split():
+    """run() captured in a hipGraph: every replay equals the eager result, also
+    after a re-plan that keeps the split (decode_groups) and the capacities."""
+    import torch
+    w = small_mixed(740, 4, True)
+    d, a = w.dec, w.app
+    k = wl.to_torch(d.kv.k_pages, "bf16", "cuda")
+    v = wl.to_torch(d.kv.v_pages, "bf16", "cuda")
+    params = abp.make_params(16, 4, 128, 16, torch.bfloat16, causal=True)
+    nd, na, nq = len(d.kv.kv_indptr) - 1, len(a.kv.kv_indptr) - 1, int(a.qo_indptr[-1])
+    pod = abp.PodAttention(params, nd, na, nq, num_groups=32)
+    qd, qa = wl.to_torch(d.q, "bf16", "cuda"), wl.to_torch(a.q, "bf16", "cuda")
+    D = [i32(d.kv.kv_indptr), i32(d.kv.kv_indices), i32(d.kv.kv_last_page_len)]
+    A = [i32(a.qo_indptr), i32(a.kv.kv_indptr), i32(a.kv.kv_indices), i32(a.kv.kv_last_page_len)]
+    od, oa = torch.empty_like(qd), torch.empty_like(qa)
+    ld = torch.empty(qd.shape[:2], dtype=torch.float32, device="cuda")
+    la = torch.empty(qa.shape[:2], dtype=torch.float32, device="cuda")
+
+    def run(stream=None):
+        pod.run(qd, qa, k, v, *D, *A, o_decode=od, lse_decode=ld, o_append=oa, lse_append=la,
+                stream=stream)
+
+    def outs():
+        return [t.clone() for t in (od, ld, oa, la)]
+
+    pod.plan(d.kv.kv_indptr, d.kv.kv_last_page_len, a.qo_indptr, a.kv.kv_indptr,
+             a.kv.kv_last_page_len, decode_groups=12)
+    run()
+    torch.cuda.synchronize()
+    eager1 = outs()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            run(s)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for t in (od, oa):
+            t.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert all(torch.equal(x, y) for x, y in zip(outs(), eager1))
+    # re-plan with shorter last pages of the decode requests (same page table
+    # arrays, same capacities, same split)
+    lpl2 = np.where(np.diff(d.kv.kv_indptr) > 0, np.maximum(1, d.kv.kv_last_page_len // 2),
+                    d.kv.kv_last_page_len).astype(np.int32)
+    D[2].copy_(i32(lpl2))
+    plan = pod.plan(d.kv.kv_indptr, lpl2, a.qo_indptr, a.kv.kv_indptr, a.kv.kv_last_page_len,
+                    decode_groups=12)
+    assert plan.decode.num_workers == 12
+    run()
+    torch.cuda.synchronize()
+    eager2 = outs()
+    assert not torch.equal(eager2[0], eager1[0])
+    for _ in range(3):
+        for t in (od, oa):
+            t.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert all(torch.equal(x, y) for x, y in zip(outs(), eager2))
+    d.kv.kv_last_page_len = lpl2
+    od_ref, ld_ref = ora.decode_workload(d)
+    assert_parity(eager2[0].float().cpu().numpy(), eager2[1].cpu().numpy(), od_ref, ld_ref,
+                  "bf16", what="pod decode after re-plan")
