@@ -777,8 +777,7 @@ int abp_pod_run(const abp_pod_plan_t* plan, const abp_params* params, const void
       int st = prepare_run(ABP_KIND_APPEND, &plan->append, params, dw + plan->append_dev_offset,
                            plan->append_dev_bytes, &ca, &la);
       if (st != ABP_OK) return st;
-      abp::Config cchk = ca;
-      if (!abp::pod_applies(cchk)) return fail(ABP_ERR_UNSUPPORTED, "params not supported for mixed batches");
+      if (!abp::pod_applies(ca)) return fail(ABP_ERR_UNSUPPORTED, "params not supported for mixed batches");
       if (plan->append.num_tiles > 0 && (!q_append || !k_pages || !v_pages || !qo_indptr_d ||
                                          !a_kv_indptr_d || !a_kv_indices_d ||
                                          !a_kv_last_page_len_d || !o_append))
