@@ -406,3 +406,20 @@ def test_pod_plan_errors(lib):
     with pytest.raises(abp.AbpError) as e:      # one workgroup cannot hold both roles
         abp.abp_pod_workspace_size(p, 2, 1, 8, 1)
     assert e.value.status == abp.ABP_ERR_INVALID_ARG
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """The product path has no fallback: a missing library is an error."""
+    with pytest.raises(RuntimeError, match="no fallback"):
+        abp.load_library(str(tmp_path / "libabp.so"))
+
+
+def test_product_code_does_not_reach_the_oracle():
+    """Nothing in the package imports the oracle (it is test infrastructure)."""
+    pkg = os.path.join(os.path.dirname(os.path.dirname(__file__)), "attention_bsr_paged_amd")
+    for root, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(root, f), encoding="utf-8").read()
+                assert not re.search(r"^\s*(from|import)\s+oracle\b", text, re.M), f
+                assert "oracle/" not in text, f
