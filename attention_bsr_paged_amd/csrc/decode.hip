@@ -224,11 +224,11 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
   const uint32_t kdel = (ROPE && !RIL) ? 8u * sub : 0u;
   auto load_k = [&](const char* p) -> KW {
     if constexpr (ROPE && !RIL) {
-      const uint2 lo = *reinterpret_cast<const uint2*>(p);
-      const uint2 hi = *reinterpret_cast<const uint2*>(p + 128);
+      const uint2 lo = load_once(reinterpret_cast<const uint2*>(p));
+      const uint2 hi = load_once(reinterpret_cast<const uint2*>(p + 128));
       return make_uint4(lo.x, lo.y, hi.x, hi.y);
     } else {
-      return *reinterpret_cast<const KW*>(p);
+      return load_once(reinterpret_cast<const KW*>(p));
     }
   };
 
@@ -320,7 +320,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             X.k[4 * u + i] = load_k(kb + lane_off[i] - kdel);
-            X.v[4 * u + i] = *reinterpret_cast<const KW*>(vb + lane_off[i]);
+            X.v[4 * u + i] = load_once(reinterpret_cast<const KW*>(vb + lane_off[i]));
           }
         } else {
 #pragma unroll
@@ -337,7 +337,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
             const int64_t pg = a.kv_indices[ip0 + page];  // per-lane (vector) load
             const int64_t at = pg * a.page_stride + int64_t(off) * tstride + head_off;
             X.k[4 * u + i] = load_k(reinterpret_cast<const char*>(kp + at) - kdel);
-            X.v[4 * u + i] = *reinterpret_cast<const KW*>(vp + at);
+            X.v[4 * u + i] = load_once(reinterpret_cast<const KW*>(vp + at));
           }
         }
       }

@@ -149,7 +149,8 @@ __device__ __forceinline__ void decode_mfma_worker(const AttnArgs& a, int worker
         const int t0 = (c + 16 * mb < kv_end) ? c + 16 * mb : c;
         const uint16_t* rp = kp + row_base(t0) + int64_t(l16) * tstride + 8 * g16;
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc) kr[mb][kc] = *reinterpret_cast<const uint4*>(rp + 32 * kc);
+        for (int kc = 0; kc < 4; ++kc)
+          kr[mb][kc] = load_once(reinterpret_cast<const uint4*>(rp + 32 * kc));
       }
     };
     // V of chunk c into this wave's LDS stage: instruction i fills rows 4 i ..
@@ -164,7 +165,8 @@ __device__ __forceinline__ void decode_mfma_worker(const AttnArgs& a, int worker
         const int r = 4 * i + (lane >> 4);
         const int qv = (lane & 15) ^ (2 * (r & 7));
         const uint16_t* src = vp + row_base(t0) + int64_t(r & 15) * tstride + qv * 8;
-        __builtin_amdgcn_global_load_lds(src, (ABP_LDS void*)(dst + 4 * i * kD), 16, 0, 0);
+        // aux 2: non-temporal, as load_once
+        __builtin_amdgcn_global_load_lds(src, (ABP_LDS void*)(dst + 4 * i * kD), 16, 0, 2);
       }
     };
 
@@ -381,8 +383,8 @@ __device__ __forceinline__ void decode_mfma_fp8_worker(const AttnArgs& a, int wo
       for (int mb = 0; mb < 2; ++mb) {
         const int t0 = (c + 16 * mb < kv_end) ? c + 16 * mb : c;
         const uint8_t* rp = kp + row_base(t0) + int64_t(l16) * tstride + 32 * g16;
-        kr[mb][0] = *reinterpret_cast<const uint4*>(rp);
-        kr[mb][1] = *reinterpret_cast<const uint4*>(rp + 16);
+        kr[mb][0] = load_once(reinterpret_cast<const uint4*>(rp));
+        kr[mb][1] = load_once(reinterpret_cast<const uint4*>(rp + 16));
       }
     };
     // V codes of chunk c: piece i is row 8 i + l / 8, bytes 16 (l % 8) .. + 15
@@ -391,8 +393,9 @@ __device__ __forceinline__ void decode_mfma_fp8_worker(const AttnArgs& a, int wo
       for (int i = 0; i < 4; ++i) {
         const int r = 8 * i + (lane >> 3);
         const int t0 = (c + 16 * (r >> 4) < kv_end) ? c + 16 * (r >> 4) : c;
-        vr[i] = *reinterpret_cast<const uint4*>(vp + row_base(t0) + int64_t(r & 15) * tstride +
-                                                16 * (lane & 7));
+        vr[i] = load_once(reinterpret_cast<const uint4*>(vp + row_base(t0) +
+                                                         int64_t(r & 15) * tstride +
+                                                         16 * (lane & 7)));
       }
     };
 
