@@ -79,7 +79,11 @@ __device__ __forceinline__ uint4 widen8(uint32_t w0, uint32_t w1) {
 
 // The work of one decode worker (a 256-thread workgroup, or the first four
 // waves of a larger one): segments wseg[worker] .. wseg[worker + 1] of the plan.
-template <typename T, int G>
+// NT: non-temporal K/V loads. They pay when decode holds the whole chip and
+// HBM is the limit; on a few compute units beside other work (the mixed
+// launch) ordinary loads are faster (measured: 160.5 against 182.3 us for the
+// batch decode on 96 compute units).
+template <typename T, int G, bool NT = true>
 __device__ __forceinline__ void decode_mfma_worker(const AttnArgs& a, int worker) {
   static_assert(G == 4 || G == 8, "rows of one kv head fill at most one 16-row tile");
   constexpr int HT = 4;  // kv heads per tile = waves per workgroup
@@ -149,8 +153,10 @@ __device__ __forceinline__ void decode_mfma_worker(const AttnArgs& a, int worker
         const int t0 = (c + 16 * mb < kv_end) ? c + 16 * mb : c;
         const uint16_t* rp = kp + row_base(t0) + int64_t(l16) * tstride + 8 * g16;
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc)
-          kr[mb][kc] = load_once(reinterpret_cast<const uint4*>(rp + 32 * kc));
+        for (int kc = 0; kc < 4; ++kc) {
+          const uint4* p = reinterpret_cast<const uint4*>(rp + 32 * kc);
+          kr[mb][kc] = NT ? load_once(p) : *p;
+        }
       }
     };
     // V of chunk c into this wave's LDS stage: instruction i fills rows 4 i ..
@@ -166,7 +172,8 @@ __device__ __forceinline__ void decode_mfma_worker(const AttnArgs& a, int worker
         const int qv = (lane & 15) ^ (2 * (r & 7));
         const uint16_t* src = vp + row_base(t0) + int64_t(r & 15) * tstride + qv * 8;
         // aux 2: non-temporal, as load_once
-        __builtin_amdgcn_global_load_lds(src, (ABP_LDS void*)(dst + 4 * i * kD), 16, 0, 2);
+        __builtin_amdgcn_global_load_lds(src, (ABP_LDS void*)(dst + 4 * i * kD), 16, 0,
+                                         NT ? 2 : 0);
       }
     };
 

@@ -34,7 +34,7 @@ __global__ __launch_bounds__(512, 1) void pod_kernel(AttnArgs app, AttnArgs dec)
   if (b < app.workers) {
     appi::append_worker<T, G, CAUSAL, false, true, false>(app, b);
   } else if (threadIdx.x < 256) {
-    dmi::decode_mfma_worker<T, G>(dec, b - app.workers);
+    dmi::decode_mfma_worker<T, G, false>(dec, b - app.workers);  // ordinary loads: few CUs
   }
 }
 
