@@ -378,7 +378,7 @@ def bench_pod(abp, wl, torch, dev, K, Wm) -> dict:
 # ----------------------------------------------------------------------------
 # cascade (shared prefix + suffixes, RoPE)
 # ----------------------------------------------------------------------------
-def bench_cascade(abp, wl, torch, dev, K, Wm) -> dict:
+def bench_cascade(abp, wl, torch, dev, K, Wm, workers=0) -> dict:
     w = wl.cascade_rope()
     pre, kv = w.prefix, w.kv
     by = cascade_bytes(w)
@@ -391,7 +391,7 @@ def bench_cascade(abp, wl, torch, dev, K, Wm) -> dict:
     q = wl.to_torch(w.q, w.dtype, dev)
     cas = abp.CascadeDecode(w.num_qo_heads, w.num_kv_heads, w.head_dim, pre.page_size,
                             kv.page_size, torch.bfloat16, max_batch=w.batch,
-                            rope_theta=w.rope_theta, device=dev)
+                            rope_theta=w.rope_theta, num_workers=workers, device=dev)
     pqo = i32([0, w.batch])
     p_ind, p_idx, p_lpl = i32(pre.kv_indptr), i32(pre.kv_indices), i32(pre.kv_last_page_len)
     s_ind, s_idx, s_lpl = i32(kv.kv_indptr), i32(kv.kv_indices), i32(kv.kv_last_page_len)
@@ -747,7 +747,7 @@ def main(argv=None) -> int:
         print(json.dumps(bench_copy(torch, dev, K, Wm)), flush=True)
         return 0
     if part == "cascade":
-        print(json.dumps(bench_cascade(abp, wl, torch, dev, K, Wm)), flush=True)
+        print(json.dumps(bench_cascade(abp, wl, torch, dev, K, Wm, args.workers)), flush=True)
         return 0
     if part == "bsr":
         print(json.dumps(bench_bsr(abp, wl, torch, dev, K, Wm)), flush=True)
