@@ -17,22 +17,30 @@
 // blocks). The RoPE variant uses 128-row tiles and 4 waves: its split q
 // operands need the registers of one wave per SIMD.
 //
-//   S^T = K Q^T    v_mfma_f32_16x16x32 with A = K rows (LDS, row-major,
-//                  padded) and B = Q^T (registers). The accumulator gives each
-//                  lane one query row and 16 of the block's keys, so softmax
-//                  statistics are lane-local except a 4-lane max.
-//   softmax        fp32, base-2 exponentials, running max per row; P is
-//                  rounded to the storage type for the next product.
-//   O^T += V^T P^T v_mfma with A = V^T (LDS, transposed when staged: key pairs
-//                  packed with v_perm) and B = P^T taken directly from the S
-//                  registers: the K-slot order of the product is chosen to be
-//                  the order in which S holds the keys, so no lane exchange.
+//   S^T = K Q^T    v_mfma_f32_16x16x32 with A = K rows from LDS and B = Q^T
+//                  from registers. The accumulator gives each lane one query
+//                  row and 16 of the block's keys, so softmax statistics are
+//                  lane-local except a 4-lane-group max.
+//   softmax        fp32, base-2 exponentials, running max per row with a lazy
+//                  rescale; P is rounded to the storage type for the next product.
+//   O^T += V^T P^T v_mfma with A = V^T from LDS and B = P^T taken directly from
+//                  the S registers: the K-slot order of the product is the
+//                  order in which S holds the keys, so no lane exchange.
 //
-// The next block's K/V are loaded into registers while the current block is
-// computed, then stored to LDS (K by the first half of the waves, V transposed
-// by the second half). A tile split over several workers is merged by the
-// workgroup whose partial state arrives last (per-tile arrival counters). With a power-of-two page size >= 16, a block's
-// page ids are scalar loads (one per 16-key group). Workers are mapped to
+// Staging, two LDS stages (block j + 1 is loaded while block j is computed):
+//   * without RoPE, K and V rows go straight from global memory into LDS with
+//     the gfx950 global-to-LDS loads, rows unpadded with their 16-byte chunks
+//     XOR-swizzled by row (K chunk q of row r at q ^ (r & 15), V at
+//     q ^ 2 (r & 7)); K operands are plain 16-byte reads and V^T operands come
+//     from ds_read_b64_tr_b16 transpose reads, both free of bank conflicts;
+//   * with RoPE, K is loaded into registers, rotated in fp32 and stored as
+//     16-bit hi and lo parts (padded rows), and V is stored transposed (key
+//     pairs packed with v_perm); the waves take K and V rows alike.
+// Rows past the segment end re-read the segment's last key (in bounds; their
+// scores are masked, and their values are finite even where the slot holds no
+// token). A tile split over a few workers is merged by the workgroup whose
+// partial state arrives last (per-tile arrival counters). With a power-of-two
+// page size >= 16, a block's page ids are scalar loads. Workers are mapped to
 // workgroup ids XCD-major, so consecutive workers (which usually share the
 // same request and kv head) run on the same XCD and share its L2.
 #include "append_impl.h"

@@ -246,7 +246,6 @@ __device__ __forceinline__ void append_worker(const AttnArgs& a, int bid) {
     const int kv_pos0 = (ROPE && a.kv_pos_offset) ? a.kv_pos_offset[b] : 0;
     // elements; with RoPE the first piece of the lane's pairs (see above)
     const int koff_lane = k_row * tstride + h * kD + kc_chunk * kKPiece;
-    const int voff_lane = (4 * v_kg) * tstride + h * kD + v_chunk * 8;   // + i * tstride
 
     // ---- Q fragments (B operand of S^T = K Q^T) for this wave's 32 rows
     uint4 qf[2][4];
@@ -326,9 +325,14 @@ __device__ __forceinline__ void append_worker(const AttnArgs& a, int bid) {
           const int kk = min(kb + 16 * vw, last16);  // wave-uniform
           const int64_t vb = (int64_t)kv_indices[ip0 + (kk >> shift)] * a.page_stride +
                              (int64_t)(kk & (P - 1)) * tstride;
+          // a key at or past kv_end takes the last key's values: slots past a
+          // request's last token may hold NaN / inf bits, which p = 0 does not
+          // cancel in P.V (K rows there only reach masked scores)
+          const int rmax = kv_end - 1 - kk;
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            vr(i) = *reinterpret_cast<const uint4*>(vp + vb + voff_lane + i * tstride);
+            vr(i) = *reinterpret_cast<const uint4*>(vp + vb + min(4 * v_kg + i, rmax) * tstride +
+                                                    h * kD + v_chunk * 8);
         }
       } else {
         if (stage_k) {
@@ -447,8 +451,11 @@ __device__ __forceinline__ void append_worker(const AttnArgs& a, int bid) {
         if constexpr (FASTPAGE) {
           const int last4 = (kv_end - 1) & ~3;
           const int kk = min(kb + r0, last4);  // 4-row group, one page
+          // rows at or past kv_end re-read the last key (unwritten slots may
+          // hold NaN / inf bits, which p = 0 does not cancel in P.V)
+          const int rr = min(lane >> 4, kv_end - 1 - kk);
           row_base = (int64_t)kv_indices[ip0 + (kk >> shift)] * a.page_stride +
-                     (int64_t)((kk & (P - 1)) + (lane >> 4)) * tstride + h * kD;
+                     (int64_t)((kk & (P - 1)) + rr) * tstride + h * kD;
         } else {
           const int key = min(kb + r, kv_end - 1);
           int page, off;

@@ -352,6 +352,14 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(AttnArgs a) {
         k4[i] = widen8<T>(k4w[i]);
         v4[i] = widen8<T>(v4w[i]);
       }
+      // tokens at or past kv_end were read from slots that may hold no token
+      // (NaN or inf bits); their p is 0, but 0 * NaN is not, so their values
+      // are zeroed (their scores are masked below)
+      if (c + kSub > kv_end) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (c + 4 * i + grp >= kv_end) v4[i] = make_uint4(0u, 0u, 0u, 0u);
+      }
       // scores of 4 tokens x G rows, summed over the 16 lanes of the token's row
       float sc[4 * G];
       float cs[ROPE ? 4 : 1], sn[ROPE ? 4 : 1];

@@ -162,7 +162,10 @@ __device__ __forceinline__ void decode_mfma_worker(const AttnArgs& a, int worker
     // V of chunk c into this wave's LDS stage: instruction i fills rows 4 i ..
     // 4 i + 3 (1 KB); lane l writes row 4 i + l / 16 at chunk position l % 16,
     // which holds the row's logical chunk (l % 16) ^ (2 (row & 7)) (the swizzle
-    // that makes the transpose reads conflict-free)
+    // that makes the transpose reads conflict-free). A row at or past kv_end
+    // takes the last key's values instead: slots past a request's last valid
+    // token hold undefined bits (possibly NaN or inf), and although their p is
+    // 0, 0 * NaN would still reach o.
     auto load_v = [&](int c, uint16_t* dst) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -170,7 +173,8 @@ __device__ __forceinline__ void decode_mfma_worker(const AttnArgs& a, int worker
         const int t0 = (c + 16 * mb < kv_end) ? c + 16 * mb : c;
         const int r = 4 * i + (lane >> 4);
         const int qv = (lane & 15) ^ (2 * (r & 7));
-        const uint16_t* src = vp + row_base(t0) + int64_t(r & 15) * tstride + qv * 8;
+        const int rs = min(r & 15, kv_end - 1 - t0);  // source row, never past kv_end
+        const uint16_t* src = vp + row_base(t0) + int64_t(rs) * tstride + qv * 8;
         // aux 2: non-temporal, as load_once
         __builtin_amdgcn_global_load_lds(src, (ABP_LDS void*)(dst + 4 * i * kD), 16, 0,
                                          NT ? 2 : 0);
@@ -234,17 +238,6 @@ __device__ __forceinline__ void decode_mfma_worker(const AttnArgs& a, int worker
       }
     };
 
-    // chunks c = kv_begin + 32 n in pairs, alternating between the two LDS
-    // stages and two K register sets, two chunks in flight per wave: the
-    // prologue loads chunks 0 and 1; each half-step waits for its chunk,
-    // computes it and then refills its stage and registers with the chunk two
-    // ahead (clamped to the last chunk of the segment, so trailing loads
-    // re-read that chunk in bounds; a chunk past kv_end is fully masked).
-    // A chunk's V (written to LDS by the memory unit) and K were issued before
-    // the 16 loads of the chunk after it, so vmcnt(16) covers both; a stage is
-    // refilled only after the transpose reads of its chunk have completed
-    // (lgkmcnt(0)). Scheduling barriers keep each wait, compute and refill in
-    // that order.
     // chunks c = kv_begin + 32 n in pairs, alternating between the two LDS
     // stages and two K register sets; chunk n + 1 is loaded while chunk n is
     // computed, and only chunks that exist are loaded. Waits are explicit: a
@@ -394,14 +387,17 @@ __device__ __forceinline__ void decode_mfma_fp8_worker(const AttnArgs& a, int wo
         kr[mb][1] = load_once(reinterpret_cast<const uint4*>(rp + 16));
       }
     };
-    // V codes of chunk c: piece i is row 8 i + l / 8, bytes 16 (l % 8) .. + 15
+    // V codes of chunk c: piece i is row 8 i + l / 8, bytes 16 (l % 8) .. + 15;
+    // a row at or past kv_end takes the last key's codes (unwritten slots may
+    // hold NaN codes, and p = 0 does not cancel them)
     auto load_v = [&](int c, uint4 (&vr)[4]) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 8 * i + (lane >> 3);
         const int t0 = (c + 16 * (r >> 4) < kv_end) ? c + 16 * (r >> 4) : c;
+        const int rs = min(r & 15, kv_end - 1 - t0);
         vr[i] = load_once(reinterpret_cast<const uint4*>(vp + row_base(t0) +
-                                                         int64_t(r & 15) * tstride +
+                                                         int64_t(rs) * tstride +
                                                          16 * (lane & 7)));
       }
     };

@@ -147,6 +147,52 @@ def make_paged_kv(rng: np.random.Generator, kv_len, page_size: int, num_kv_heads
     return PagedKV(page_size, num_kv_heads, head_dim, dtype, kv_len, indptr, indices, lpl, k, v)
 
 
+
+# Non-finite bit patterns of each storage type: quiet NaN, -inf and +inf for the
+# 16-bit types; e4m3 has no infinity, so its two NaN codes (S.1111.111).
+NON_FINITE_BITS = {
+    "bf16": (0x7FC0, 0xFF80, 0x7F80),
+    "fp16": (0x7E00, 0xFC00, 0x7C00),
+    "fp8_e4m3": (0x7F, 0xFF),
+}
+
+
+def poison_unwritten(kv: PagedKV) -> PagedKV:
+    """A copy of ``kv`` whose slots that hold no token are non-finite.
+
+    The page table defines only the first ``kv_last_page_len[b]`` slots of a
+    request's last page and says nothing of pages no request owns; a cache
+    allocated without clearing (or reused) holds arbitrary bits there. This
+    fills every such slot, in both pools, with the storage type's NaN / inf
+    patterns, cycling through them element by element. The valid slots are
+    unchanged, so any correct attention over the table gives the same result.
+    """
+    k = kv.k_pages.copy()
+    v = kv.v_pages.copy()
+    pat = NON_FINITE_BITS[kv.dtype]
+    dt = k.dtype
+    owned = np.zeros(k.shape[0], dtype=bool)
+    owned[np.asarray(kv.kv_indices, dtype=np.int64)] = True
+    P = kv.page_size
+    for b in range(len(kv.kv_indptr) - 1):
+        s, e = int(kv.kv_indptr[b]), int(kv.kv_indptr[b + 1])
+        if e > s:
+            last = int(kv.kv_indices[e - 1])
+            lpl = int(kv.kv_last_page_len[b])
+            if lpl < P:
+                n = k[last, lpl:].size
+                fill = np.resize(np.array(pat, dtype=dt), n).reshape(k[last, lpl:].shape)
+                k[last, lpl:] = fill
+                v[last, lpl:] = fill[..., ::-1]
+    free = ~owned
+    if free.any():
+        n = k[free].size
+        fill = np.resize(np.array(pat, dtype=dt), n).reshape(k[free].shape)
+        k[free] = fill
+        v[free] = fill
+    return PagedKV(kv.page_size, kv.num_kv_heads, kv.head_dim, kv.dtype, kv.kv_len,
+                   kv.kv_indptr, kv.kv_indices, kv.kv_last_page_len, k, v)
+
 # ----------------------------------------------------------------------------
 # the five named workloads
 # ----------------------------------------------------------------------------

@@ -56,7 +56,8 @@ def test_empty_and_zero_query_requests():
 def test_ragged_append_sampled():
     """Full ragged causal append (16 requests, qo U{128..1024} onto kv U{1024..8192},
     GQA 32/8, bf16) in the launch configuration the benchmark times, compared on
-    sampled query tokens of every request (first, last, and random ones)."""
+    at least 64 query tokens of every request: the first and last, both sides
+    of every 64-token query-tile boundary, and random ones."""
     w = wl.ragged_append_causal()
     say(f"[case] {w.name}")
     o, l = run_append(w)
@@ -64,7 +65,11 @@ def test_ragged_append_sampled():
     toks = []
     for b in range(w.batch):
         q0, q1 = int(w.qo_indptr[b]), int(w.qo_indptr[b + 1])
-        toks += [q0, q1 - 1] + list(rng.integers(q0, q1, size=6))
+        mine = {q0, q1 - 1}
+        mine |= {t for j in range(q0 + 64, q1, 64) for t in (j - 1, j)}
+        mine |= set(int(t) for t in rng.choice(np.arange(q0, q1), size=64, replace=False))
+        assert len(mine) >= 64
+        toks += sorted(mine)
     toks = sorted(set(toks))
     o_ref, l_ref = ora.append_workload(w, token_ids=toks)
     assert_parity(o, l, o_ref, l_ref, "bf16", rows=toks, what="ragged append sampled")
@@ -245,14 +250,13 @@ def test_small_cascade_parity(theta):
     assert_parity(o, l, o_ref, l_ref, "bf16", what=f"cascade theta={theta}")
 
 
-def test_cascade_rope_full_sampled():
+def test_cascade_rope_full():
     """64 requests sharing an 8192-token prefix (pages of 256) plus suffixes of
     256..1024 tokens (pages of 16), GQA 32/8, bf16, RoPE theta 500000, in the
-    default launch configuration; compared on sampled requests."""
+    default launch configuration; every request compared."""
     w = wl.cascade_rope()
     say(f"[case] {w.name}")
     o, l = run_cascade(w)
-    ids = [0, 17, 40, 63]
-    o_ref, l_ref = ora.decode_workload(w, batch_ids=ids)
-    assert_parity(o, l, o_ref, l_ref, "bf16", rows=ids, what="cascade rope sampled")
+    o_ref, l_ref = ora.decode_workload(w)
+    assert_parity(o, l, o_ref, l_ref, "bf16", what="cascade rope, all requests")
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))

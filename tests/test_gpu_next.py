@@ -188,15 +188,14 @@ def test_fp8_decode_parity(P, G, hkv, dtype):
         assert_parity(o, l, o_ref, l_ref, dtype, what=f"fp8 decode P{P} G{G} hkv{hkv} W{W}")
 
 
-def test_fp8_batch_decode_full_sampled():
+def test_fp8_batch_decode_full():
     """The fp8 batch decode shape (64 requests, kv U{512..4096}, GQA 32/8, page 16,
-    q bf16, e4m3 K/V with scales 0.25) in the default launch, sampled requests."""
+    q bf16, e4m3 K/V with scales 0.25) in the default launch, every request."""
     w = wl.batch_decode_fp8()
     say(f"[case] {w.name}")
     o, l = run_decode(w)
-    ids = [0, 1, 31, 62, 63]
-    o_ref, l_ref = ora.decode_workload(w, batch_ids=ids)
-    assert_parity(o, l, o_ref, l_ref, "bf16", rows=ids, what="fp8 batch decode sampled")
+    o_ref, l_ref = ora.decode_workload(w)
+    assert_parity(o, l, o_ref, l_ref, "bf16", what="fp8 batch decode, all requests")
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
 
 
