@@ -159,7 +159,11 @@ _SIGNATURES = {
                            _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "abp_merge_state": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _int, _int, _vp]),
     "abp_merge_states": (_int, [_vp, _vp, _i32, _i64, _i32, _int, _int, _vp, _vp, _vp]),
+    "abp_decode_static": (_int, [_pp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                 _vp, _vp, _vp, _vp]),
 }
+ABP_STATIC_SCRATCH_BYTES = 32 << 20
+ABP_STATIC_PLAN_BYTES = 1 << 20
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
 _lib = None

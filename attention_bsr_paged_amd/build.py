@@ -23,7 +23,7 @@ LIB = os.path.join(LIBDIR, "libabp.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "plan.cpp", "merge.hip", "decode.hip", "append.hip", "upload.hip",
-           "page_append.hip", "decode_mfma.hip", "pod.hip"]
+           "page_append.hip", "decode_mfma.hip", "pod.hip", "static_ws.hip"]
 
 COMMON = [
     "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

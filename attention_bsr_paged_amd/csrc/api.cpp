@@ -172,6 +172,20 @@ void fill_args(const abp::Config& cfg, const abp::Layout& L, const abp_plan* pla
 
 }  // namespace
 
+namespace abp {
+
+int default_decode_workers(const abp_params* params, int32_t* out) {
+  Config cfg;
+  std::string err;
+  int st = check_params(ABP_KIND_DECODE, params, &cfg, &err);
+  if (st != ABP_OK) return fail(st, err);
+  return default_workers(cfg, out);
+}
+
+int set_error(int status, const char* msg) { return fail(status, msg); }
+
+}  // namespace abp
+
 // Mixed decode + append batches: worker split and the two sub-plans.
 namespace {
 

@@ -68,6 +68,12 @@ hipError_t launch_page_append(const void* k_new, const void* v_new, const int32_
                               int32_t batch, int64_t nnz, int32_t row_bytes, int32_t page_size,
                               hipStream_t stream);
 
+// Host-side helpers shared with the no-allocation entry point (api.cpp):
+// the default decode worker count of the current device for `params`, and
+// recording a status message for abp_last_error() (returns `status`).
+int default_decode_workers(const abp_params* params, int32_t* out);
+int set_error(int status, const char* msg);
+
 hipError_t launch_merge_two(const void* o_a, const float* lse_a, const void* o_b,
                             const float* lse_b, void* o_out, float* lse_out, int64_t rows,
                             int in_dtype, int out_dtype, hipStream_t stream);

@@ -388,6 +388,35 @@ int abp_merge_states(const void* o_in, const float* lse_in, int32_t num_states,
                      int64_t num_rows, int32_t head_dim, int in_dtype, int out_dtype,
                      void* o_out, float* lse_out, abp_stream_t stream);
 
+/* Batch decode without any allocation, for callers that cannot allocate
+ * (code under graph capture, tight serving loops, harnesses that forbid
+ * allocation). Computes exactly abp_decode_plan followed by abp_decode_run
+ * (same plan, same kernels, bit-identical results), but the caller passes no
+ * workspace: the library keeps a device array of ABP_STATIC_SCRATCH_BYTES on
+ * each GPU it runs on (allocated with the code object, held until the process
+ * ends) for the plan blob and partial states, and a host array of
+ * ABP_STATIC_PLAN_BYTES for the plan. Arguments are those of the two calls:
+ * host kv_indptr_h [batch + 1] and kv_last_page_len_h [batch] for the plan
+ * (validated as in abp_decode_plan), num_workers <= 0 for the device default,
+ * and the device tensors of abp_decode_run. A batch whose plan or workspace
+ * exceeds those sizes returns ABP_ERR_WORKSPACE_TOO_SMALL before any GPU work
+ * (with 8 kv heads, group 4 or 8 and the default 256 workers, up to about
+ * 12,000 requests fit; the device array holds the partial states of up to
+ * 1024 workers at group 8, 2048 at group 4).
+ * The plan is copied from pageable host memory, a copy HIP performs
+ * synchronously with respect to the host; then the decode and merge kernels
+ * are enqueued on `stream`. Not graph-capturable itself (the copy). Every
+ * call on a GPU shares that GPU's scratch: calls on one stream are ordered,
+ * calls that overlap on one GPU (other streams or threads) race. */
+#define ABP_STATIC_SCRATCH_BYTES (32u << 20)
+#define ABP_STATIC_PLAN_BYTES (1u << 20)
+int abp_decode_static(const abp_params* params, int32_t batch, const int32_t* kv_indptr_h,
+                      const int32_t* kv_last_page_len_h, int32_t num_workers, const void* q,
+                      const void* k_pages, const void* v_pages, const int32_t* kv_indptr_d,
+                      const int32_t* kv_indices_d, const int32_t* kv_last_page_len_d,
+                      const int32_t* q_pos_d, const int32_t* kv_pos_offset_d, void* o,
+                      float* lse, abp_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

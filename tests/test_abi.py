@@ -423,3 +423,24 @@ def test_product_code_does_not_reach_the_oracle():
                 text = open(os.path.join(root, f), encoding="utf-8").read()
                 assert not re.search(r"^\s*(from|import)\s+oracle\b", text, re.M), f
                 assert "oracle/" not in text, f
+
+
+def test_decode_static_rejects_batches_beyond_its_arrays(lib):
+    """The no-allocation decode refuses a batch whose plan exceeds its static
+    host array before any GPU work (explicit worker count: no device query)."""
+    import ctypes
+    import torch
+    p = abp.make_params(32, 8, 128, 16, torch.bfloat16)
+    B = 20000
+    indptr = np.arange(B + 1, dtype=np.int32)
+    lpl = np.ones(B, np.int32)
+    st = lib.abp_decode_static(ctypes.byref(p), B, indptr.ctypes.data, lpl.ctypes.data, 256,
+                               *([None] * 10), None)
+    assert st == abp.ABP_ERR_WORKSPACE_TOO_SMALL
+    msg = abp.abp_last_error()
+    assert "abp_decode_static" in msg and str(abp.ABP_STATIC_PLAN_BYTES) in msg
+    # too many workers for the device array
+    st = lib.abp_decode_static(ctypes.byref(p), 4, indptr[:5].ctypes.data, lpl.ctypes.data,
+                               4096, *([None] * 10), None)
+    assert st == abp.ABP_ERR_WORKSPACE_TOO_SMALL
+    assert str(abp.ABP_STATIC_SCRATCH_BYTES) in abp.abp_last_error()
