@@ -143,10 +143,10 @@ constexpr int append_waves() {
   return ROPE ? 4 : 8;
 }
 
-// The work of one append worker (a workgroup of append_waves<ROPE>() waves);
-// bid is the workgroup's index among the launch's append workgroups.
+// The append worker with RoPE (4 waves, 128 rows): K is staged through
+// registers, rotated and split into hi/lo parts before the LDS store.
 template <typename T, int G, bool CAUSAL, bool ROPE, bool FASTPAGE, bool RIL>
-__device__ __forceinline__ void append_worker(const AttnArgs& a, int bid) {
+__device__ __forceinline__ void append_worker_staged(const AttnArgs& a, int bid) {
   static_assert(ROPE || !RIL, "interleaving is a RoPE layout");
   // K elements a staging thread reads per row: rotate-half RoPE takes 4 + 4
   // (both halves of its 4 pairs), everything else 8 consecutive ones
@@ -692,6 +692,499 @@ __device__ __forceinline__ void append_worker(const AttnArgs& a, int bid) {
       });
     }
   }
+}
+
+// Softmax reference of the pipelined worker. A row keeps its reference max m
+// while every p = 2^(s * scale * log2 e - m) of the row stays at or below
+// 2^kSumCheckLog2: a lane's partial row sum bounds each of its p, so one
+// comparison per row and step replaces the row maximum; when it fails the step
+// takes the exact maximum instead. fp32 keeps full relative precision over
+// that range, and O and l stay far below overflow (at most
+// 2^(kSumCheckLog2 + 32) for 2^32 keys of unit size). Before its first key a
+// row's reference is kNoRef, finite and far below any score, so the first p
+// overflows the check and the exact maximum is taken.
+constexpr float kSumCheckLog2 = 16.f;
+constexpr float kNoRef = -1.0e30f;
+
+// The work of one append worker without RoPE: 8 waves, 256 rows (tile_q tokens
+// x G heads), wave w owning rows 32 w .. 32 w + 31, against 64-key blocks.
+//
+// Software pipeline over 32-key half blocks t: step t issues the S products
+// of half t + 1 and the P.V products of half t - 1 on the matrix cores while
+// the vector unit runs the softmax of half t. A step is written as 8 slots,
+// each holding 4 products, the exponentials of 2 of the lane's 16 scores and
+// the operand reads of the slot two ahead, with scheduling fences between the
+// slots, so every wave keeps both units busy and each LDS read has two slots
+// of products to land. S is double-buffered in registers; P of each half
+// waits one step in registers for its P.V products.
+//
+// Staging: K and V blocks go straight from global memory into LDS (global-to-
+// LDS loads, rows of 256 bytes whose 16-byte chunks are XOR-swizzled by row:
+// K chunk q of row r at q ^ (r & 15), V at q ^ 2 (r & 7); K operands are
+// 16-byte reads, V^T operands transpose reads, both free of bank conflicts).
+// K and V have two stages each, V one block behind K: during block j's steps
+// the LDS holds K(j), K(j + 1), V(j - 1) and V(j). After the first step of
+// block j, once every wave is past it (barrier), K(j + 2) and V(j + 1) are
+// loaded into the stages of K(j) and V(j - 1); they have two steps to land.
+template <typename T, int G, bool CAUSAL, bool FASTPAGE, int NS>
+__device__ __forceinline__ void append_worker_pipe(const AttnArgs& a, int bid) {
+  static_assert(NS == 2 || NS == 3, "two or three K/V stages");
+  constexpr int NW = 8;
+  constexpr int kRows = 32 * NW;
+  constexpr int TQ = kRows / G;
+  __shared__ __align__(16) uint16_t ldsK0[kTk * kD];
+  __shared__ __align__(16) uint16_t ldsK1[kTk * kD];
+  __shared__ __align__(16) uint16_t ldsK2[NS > 2 ? kTk * kD : 8];
+  __shared__ __align__(16) uint16_t ldsV0[kTk * kD];
+  __shared__ __align__(16) uint16_t ldsV1[kTk * kD];
+  __shared__ __align__(16) uint16_t ldsV2[NS > 2 ? kTk * kD : 8];
+  __shared__ int s_last;
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  auto sK_of = [&](auto st) -> uint16_t* {
+    if constexpr (decltype(st)::value == 0) return ldsK0;
+    else if constexpr (decltype(st)::value == 1) return ldsK1;
+    else return ldsK2;
+  };
+  auto sV_of = [&](auto st) -> uint16_t* {
+    if constexpr (decltype(st)::value == 0) return ldsV0;
+    else if constexpr (decltype(st)::value == 1) return ldsV1;
+    else return ldsV2;
+  };
+
+  const ABP_CONST_AS int32_t* plan = const_as(a.plan);
+  const ABP_CONST_AS int32_t* wseg = plan + plan[H_OFF_WSEG];
+  const ABP_CONST_AS int32_t* segs = plan + plan[H_OFF_SEG];
+  const ABP_CONST_AS int32_t* tiles = plan + plan[H_OFF_TILE];
+  const ABP_CONST_AS int32_t* kv_indptr = const_as(a.kv_indptr);
+  const ABP_CONST_AS int32_t* kv_indices = const_as(a.kv_indices);
+  const ABP_CONST_AS int32_t* qo_indptr = const_as(a.qo_indptr);
+
+  // XCD-major worker id: workgroup i runs on XCD i % 8
+  const int W = a.workers;
+  const int worker = (W % 8 == 0) ? (bid % 8) * (W / 8) + bid / 8 : bid;
+  const int s_begin = wseg[worker], s_end = wseg[worker + 1];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g16 = lane >> 4;   // lane group 0..3
+  const int l16 = lane & 15;
+  const float cl2 = a.sm_scale_log2;
+  const int P = a.page_size;
+  const int shift = a.page_shift;
+  const int tstride = a.token_stride;
+  const uint16_t* __restrict__ kp = static_cast<const uint16_t*>(a.k_pages);
+  const uint16_t* __restrict__ vp = static_cast<const uint16_t*>(a.v_pages);
+  constexpr float kBig = float(1u << 16);  // 2^kSumCheckLog2
+  static_assert(kSumCheckLog2 == 16.f, "kBig follows the threshold");
+
+  // Per-lane LDS byte offsets, the same for every block and stage:
+  //  * K operand of product kc: row 16 mb + l16 (mb in the immediate offset),
+  //    chunk (4 kc + g16) ^ l16 = (g16 ^ l16) ^ 4 kc;
+  //  * V^T operand of d-tile md: transpose read of keys 4 g16 + l16 / 4 (and
+  //    + 16, + 32 h in the immediate offset) at head dims 16 md + 4 (l16 % 4),
+  //    whose chunk 2 md + (l16 / 2) % 2 sits at position
+  //    2 (md ^ (key & 7)) + (l16 / 2) % 2.
+  uint32_t koff[4], voff[8];
+  {
+    const uint32_t x = uint32_t(g16 ^ l16);
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) koff[kc] = uint32_t(l16) * 256u + ((x ^ uint32_t(4 * kc)) * 16u);
+    const uint32_t key = uint32_t(4 * g16 + (l16 >> 2));
+    const uint32_t c = key & 7u;
+    const uint32_t b = uint32_t(l16 >> 1) & 1u;
+#pragma unroll
+    for (int md = 0; md < 8; ++md)
+      voff[md] = (key * 128u + 16u * (uint32_t(md) ^ c) + 8u * b + 4u * uint32_t(l16 & 1)) * 2u;
+  }
+  // Refill loads: wave w fills rows 8 w .. 8 w + 7 of a stage, 4 rows per
+  // instruction i (1 KB, lane l at byte 16 l): lane l takes row
+  // r = 8 w + 4 i + l / 16 at chunk position l % 16, which holds the row's
+  // logical chunk (l % 16) ^ swz(r). Element offsets within the wave's rows:
+  uint32_t goffK[2], goffV[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 8 * wave + 4 * i + (lane >> 4);
+    const int pos = lane & 15;
+    goffK[i] = uint32_t((4 * i + (lane >> 4)) * tstride + ((pos ^ (r & 15)) * 8));
+    goffV[i] = uint32_t((4 * i + (lane >> 4)) * tstride + ((pos ^ (2 * (r & 7))) * 8));
+  }
+
+  for (int s = s_begin; s < s_end; ++s) {
+    const int tile = segs[4 * s];
+    const int kv_begin = segs[4 * s + 1], kv_end = segs[4 * s + 2], slot = segs[4 * s + 3];
+    const int b = tiles[4 * tile], h = tiles[4 * tile + 1], qt = tiles[4 * tile + 2];
+    const int q0 = qo_indptr[b];
+    const int qo_len = qo_indptr[b + 1] - q0;
+    const int ip0 = kv_indptr[b];
+    const int npg = kv_indptr[b + 1] - ip0;
+    const int kv_len = npg > 0 ? (npg - 1) * P + a.kv_last_page_len[b] : 0;
+
+    // ---- Q fragments (B operand of S^T = K Q^T) for this wave's 32 rows
+    uint4 qf[2][4];
+    int lim[2];
+    int tloc_r[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int r = wave * 32 + nb * 16 + l16;
+      const int tloc = qt * TQ + r / G;
+      const int tl = min(tloc, qo_len - 1);
+      tloc_r[nb] = tloc;
+      lim[nb] = kv_len - qo_len + tl;
+      const uint16_t* qptr = static_cast<const uint16_t*>(a.q) +
+                             ((int64_t)(q0 + tl) * a.num_qo_heads + h * G + (r % G)) * kD + g16 * 8;
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) qf[nb][kc] = *reinterpret_cast<const uint4*>(qptr + kc * 32);
+    }
+    // first row of the tile sees the fewest keys
+    const int tile_min_lim = kv_len - qo_len + qt * TQ;
+
+    float m[2] = {kNoRef, kNoRef};
+    float mc[2] = {kNoRef * cl2, kNoRef * cl2};  // m * scale * log2 e
+    float lsum[2] = {0.f, 0.f};
+    f32x4_t O[8][2];
+#pragma unroll
+    for (int md = 0; md < 8; ++md)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) O[md][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // ---- global -> LDS: K or V rows kb + 8 w .. + 7 of this wave into a
+    // stage. When all 8 rows are keys of the segment they share one page
+    // (pages of >= 16 keys, rows 8-aligned): one page lookup, per-lane offsets
+    // from the table above. Otherwise each lane translates its row, and rows
+    // at or past kv_end re-read the last key (in bounds; their scores are
+    // masked and their values finite even where the slot holds no token).
+    // (fast path: unsigned 32 x 32 -> 64-bit scalar arithmetic on bases
+    // fixed per segment; page ids and strides are non-negative)
+    const char* const kseg = reinterpret_cast<const char*>(kp + h * kD);
+    const char* const vseg = reinterpret_cast<const char*>(vp + h * kD);
+    const ABP_CONST_AS uint32_t* const pids =
+        reinterpret_cast<const ABP_CONST_AS uint32_t*>(kv_indices + ip0);
+    const uint32_t page_bytes = uint32_t(a.page_stride) * 2u;
+    const uint32_t row_bytes = uint32_t(tstride) * 2u;
+    auto dload = [&](const uint16_t* src, uint16_t* dst, int kb, bool is_v) {
+      const int r0 = kb + 8 * wave;
+      if (FASTPAGE && r0 + 7 < kv_end) {
+        const uint32_t pid = pids[uint32_t(r0) >> shift];
+        const char* sb = (is_v ? vseg : kseg) + (uint64_t(pid) * page_bytes +
+                                                 (uint32_t(r0) & uint32_t(P - 1)) * row_bytes);
+        const uint16_t* sbe = reinterpret_cast<const uint16_t*>(sb);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          __builtin_amdgcn_global_load_lds(sbe + (is_v ? goffV[i] : goffK[i]),
+                                           (ABP_LDS void*)(dst + (8 * wave + 4 * i) * kD), 16, 0, 0);
+      } else {
+        const int pos = lane & 15;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int r = 8 * wave + 4 * i + (lane >> 4);
+          const int q = is_v ? (pos ^ (2 * (r & 7))) : (pos ^ (r & 15));
+          const int key = min(kb + r, kv_end - 1);
+          int page, off;
+          if (shift >= 0) {
+            page = key >> shift;
+            off = key & (P - 1);
+          } else {
+            page = key / P;
+            off = key - page * P;
+          }
+          const int64_t rb = (int64_t)a.kv_indices[ip0 + page] * a.page_stride +
+                             (int64_t)off * tstride + h * kD;
+          __builtin_amdgcn_global_load_lds(src + rb + q * 8,
+                                           (ABP_LDS void*)(dst + (8 * wave + 4 * i) * kD), 16, 0, 0);
+        }
+      }
+    };
+
+    // S^T of half hh of the block in stage sK (used outside the slotted steps)
+    auto qk = [&](const uint16_t* sK, int hh, f32x4_t (&S)[2][2]) __attribute__((always_inline)) {
+      const char* base = reinterpret_cast<const char*>(sK);
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          const uint4 ka = *reinterpret_cast<const uint4*>(base + koff[kc] + (2 * hh + mb) * 4096);
+          const f32x4_t z = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          S[mb][0] = mfma<T>(ka, qf[0][kc], kc == 0 ? z : S[mb][0]);
+          S[mb][1] = mfma<T>(ka, qf[1][kc], kc == 0 ? z : S[mb][1]);
+        }
+    };
+    // V^T operand of d-tile md, half hh of the block in stage sV
+    auto vread = [&](const uint16_t* sV, int hh, int md) __attribute__((always_inline)) -> uint4 {
+      const char* base = reinterpret_cast<const char*>(sV) + hh * 8192;
+      const v4i16_t a4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ABP_LDS v4i16_t*)(base + voff[md]));
+      const v4i16_t b4 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((ABP_LDS v4i16_t*)(base + voff[md] + 4096));
+      const uint2 av = __builtin_bit_cast(uint2, a4), bv = __builtin_bit_cast(uint2, b4);
+      return make_uint4(av.x, av.y, bv.x, bv.y);
+    };
+    // O^T += V^T P^T over half hh of the block in stage sV (the last half)
+    auto pv = [&](const uint16_t* sV, int hh, const uint4 (&pB)[2]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int md = 0; md < 8; ++md) {
+        const uint4 va = vread(sV, hh, md);
+        O[md][0] = mfma<T>(va, pB[0], O[md][0]);
+        O[md][1] = mfma<T>(va, pB[1], O[md][1]);
+      }
+    };
+    // Causal and segment-end masks of one half (keys kbh .. kbh + 31), taken
+    // only on halves that cross a limit: kbh > edge_from.
+    const int edge_from = CAUSAL ? min(kv_end - 32, tile_min_lim - 31) : kv_end - 32;
+    auto mask = [&](f32x4_t (&S)[2][2], int kbh) __attribute__((always_inline)) {
+      if (kbh > edge_from) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int key = kbh + mb * 16 + g16 * 4 + j;
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+              if (key >= kv_end || (CAUSAL && key > lim[nb])) S[mb][nb][j] = kNegInf;
+          }
+      }
+    };
+    auto partial_sums = [&](const float (&p)[2][2][4], float (&part)[2]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+        part[nb] = ((p[0][nb][0] + p[0][nb][1]) + (p[0][nb][2] + p[0][nb][3])) +
+                   ((p[1][nb][0] + p[1][nb][1]) + (p[1][nb][2] + p[1][nb][3]));
+    };
+
+    // One pipeline step: the softmax of S_cur (keys kbh ..) beside the S
+    // products of the next half (K half qh of stage sK, into S_nxt) and, with
+    // PV, the P.V products of the previous half (V half vh of stage sV with
+    // P pB_prev). Slot i: products (kc = i / 2, mb = i % 2) of S and d-tile i
+    // of P.V, the scores (mb = i / 4, nb = (i / 2) % 2, j = 2 (i % 2) + 0, 1)
+    // of S_cur, and the operand reads of slot i + 2.
+    auto step = [&](auto with_pv, f32x4_t (&S_cur)[2][2], int kbh, uint4 (&pB_out)[2],
+                    const uint16_t* sK, int qh, f32x4_t (&S_nxt)[2][2], const uint16_t* sV,
+                    int vh, const uint4 (&pB_prev)[2]) __attribute__((always_inline)) {
+      constexpr bool PV = decltype(with_pv)::value;
+      mask(S_cur, kbh);
+      const char* kbase = reinterpret_cast<const char*>(sK) + 2 * qh * 4096;
+      auto kread = [&](int i) __attribute__((always_inline)) -> uint4 {
+        return *reinterpret_cast<const uint4*>(kbase + koff[i >> 1] + (i & 1) * 4096);
+      };
+      uint4 kf[3], vf[3];
+      kf[0] = kread(0);
+      kf[1] = kread(1);
+      if constexpr (PV) {
+        vf[0] = vread(sV, vh, 0);
+        vf[1] = vread(sV, vh, 1);
+      }
+      float p[2][2][4];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + 2 < 8) {
+          kf[(i + 2) % 3] = kread(i + 2);
+          if constexpr (PV) vf[(i + 2) % 3] = vread(sV, vh, i + 2);
+        }
+        const int emb = i >> 2, enb = (i >> 1) & 1, ej = 2 * (i & 1);
+        p[emb][enb][ej] = fast_exp2(__builtin_fmaf(S_cur[emb][enb][ej], cl2, -mc[enb]));
+        p[emb][enb][ej + 1] = fast_exp2(__builtin_fmaf(S_cur[emb][enb][ej + 1], cl2, -mc[enb]));
+        const int kc = i >> 1, qmb = i & 1;
+        const f32x4_t z = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        S_nxt[qmb][0] = mfma<T>(kf[i % 3], qf[0][kc], kc == 0 ? z : S_nxt[qmb][0]);
+        S_nxt[qmb][1] = mfma<T>(kf[i % 3], qf[1][kc], kc == 0 ? z : S_nxt[qmb][1]);
+        if constexpr (PV) {
+          O[i][0] = mfma<T>(vf[i % 3], pB_prev[0], O[i][0]);
+          O[i][1] = mfma<T>(vf[i % 3], pB_prev[1], O[i][1]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      float part[2];
+      partial_sums(p, part);
+      // every p <= the lane's partial sum <= 2^kSumCheckLog2 keeps the
+      // reference; !(x <= kBig) also catches an overflow to inf (and a row
+      // still at kNoRef overflows)
+      const bool moved = __builtin_amdgcn_ballot_w64(!(part[0] <= kBig) | !(part[1] <= kBig)) != 0;
+      float alpha[2];
+      if (moved) {
+        // exact row maximum over the half (4 lane groups), then evaluate again
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          float x = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(S_cur[0][nb][0], S_cur[0][nb][1]),
+                                                    __builtin_fmaxf(S_cur[0][nb][2], S_cur[0][nb][3])),
+                                    __builtin_fmaxf(__builtin_fmaxf(S_cur[1][nb][0], S_cur[1][nb][1]),
+                                                    __builtin_fmaxf(S_cur[1][nb][2], S_cur[1][nb][3])));
+          x = max_over_groups(x);
+          const float mn = __builtin_fmaxf(m[nb], x);
+          alpha[nb] = fast_exp2((m[nb] - mn) * cl2);
+          m[nb] = mn;
+          mc[nb] = mn * cl2;
+          lsum[nb] *= alpha[nb];
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              p[mb][nb][j] = fast_exp2(__builtin_fmaf(S_cur[mb][nb][j], cl2, -mc[nb]));
+        }
+        partial_sums(p, part);
+      }
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        // row sum in fp32 of the unrounded p: lse must not carry P's 16-bit rounding
+        lsum[nb] += part[nb];
+        pB_out[nb] = make_uint4(pack2<T>(p[0][nb][0], p[0][nb][1]), pack2<T>(p[0][nb][2], p[0][nb][3]),
+                                pack2<T>(p[1][nb][0], p[1][nb][1]), pack2<T>(p[1][nb][2], p[1][nb][3]));
+      }
+      // O took the P.V products of the previous half against the old reference
+      if (moved) {
+#pragma unroll
+        for (int md = 0; md < 8; ++md)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) O[md][nb] *= alpha[nb];
+      }
+    };
+
+    const int nblk = kv_begin < kv_end ? (kv_end - kv_begin + kTk - 1) / kTk : 0;
+    f32x4_t Sa[2][2], Sb[2][2];
+    uint4 pB0[2], pB1[2];
+    // Block j's K and V sit in stage j % NS. The prologue loads K(0) ..
+    // K(NS - 1) and V(0) .. V(NS - 2); the barrier in the middle of block j
+    // loads K(j + NS) and V(j + NS - 1) into the stages of K(j) and V(j - 1).
+    if (nblk > 0) {
+      dload(kp, sK_of(S0{}), kv_begin, false);
+      dload(vp, sV_of(S0{}), kv_begin, true);
+      if (nblk > 1) dload(kp, sK_of(S1{}), kv_begin + kTk, false);
+      if constexpr (NS > 2) {
+        if (nblk > 1) dload(vp, sV_of(S1{}), kv_begin + kTk, true);
+        if (nblk > 2) dload(kp, sK_of(S2{}), kv_begin + 2 * kTk, false);
+      }
+    }
+    // The global-to-LDS loads count as loads for the memory model, so a
+    // barrier's release does not wait for them: each wave waits for its own
+    // before the barrier that publishes them.
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    __syncthreads();
+    if (nblk > 0) {
+      // S of (0, h0), then step (0, h0): S of (0, h1), softmax of (0, h0)
+      qk(sK_of(S0{}), 0, Sa);
+      step(std::false_type{}, Sa, kv_begin, pB0, sK_of(S0{}), 1, Sb, sV_of(S0{}), 1, pB1);
+    }
+    // second half of block j (K(j + 1) and V(j) must have landed): barrier,
+    // refills, then step (j, h1): S of (j + 1, h0) (a block past the end
+    // reads a stale stage whose results are never used), softmax of (j, h1),
+    // P.V of (j, h0). st, st1, stm: stages of block j, j + 1 and j - 1.
+    auto half1 = [&](auto st, auto st1, auto stm, int j) __attribute__((always_inline)) {
+      const int kb = kv_begin + j * kTk;
+      // loads still allowed in flight: those of the previous middle barrier
+      // (NS = 3 only; each refill is two instructions per wave)
+      const int pend = (NS > 2 && j >= 1)
+                           ? ((j - 1 + NS < nblk) ? 2 : 0) + ((j - 2 + NS < nblk) ? 2 : 0)
+                           : 0;
+      if (pend == 4) __builtin_amdgcn_s_waitcnt(0x0f74);       // vmcnt(4)
+      else if (pend == 2) __builtin_amdgcn_s_waitcnt(0x0f72);  // vmcnt(2)
+      else __builtin_amdgcn_s_waitcnt(0x0f70);                 // vmcnt(0)
+      __syncthreads();
+      if (j + NS < nblk) dload(kp, sK_of(st), kb + NS * kTk, false);
+      if (j + NS - 1 < nblk) dload(vp, sV_of(stm), kb + (NS - 1) * kTk, true);
+      step(std::true_type{}, Sb, kb + 32, pB1, sK_of(st1), 0, Sa, sV_of(st), 0, pB0);
+    };
+    // first half of block j >= 1: step (j, h0): S of (j, h1), softmax of
+    // (j, h0), P.V of (j - 1, h1)
+    auto half0 = [&](auto st, auto stm, int j) __attribute__((always_inline)) {
+      const int kb = kv_begin + j * kTk;
+      step(std::true_type{}, Sa, kb, pB0, sK_of(st), 1, Sb, sV_of(stm), 1, pB1);
+    };
+    if constexpr (NS == 2) {
+      for (int j = 0; j < nblk; j += 2) {
+        half1(S0{}, S1{}, S1{}, j);
+        if (j + 1 < nblk) {
+          half0(S1{}, S0{}, j + 1);
+          half1(S1{}, S0{}, S0{}, j + 1);
+          if (j + 2 < nblk) half0(S0{}, S1{}, j + 2);
+        }
+      }
+    } else {
+      for (int j = 0; j < nblk; j += 3) {
+        half1(S0{}, S1{}, S2{}, j);
+        if (j + 1 < nblk) {
+          half0(S1{}, S0{}, j + 1);
+          half1(S1{}, S2{}, S0{}, j + 1);
+          if (j + 2 < nblk) {
+            half0(S2{}, S1{}, j + 2);
+            half1(S2{}, S0{}, S1{}, j + 2);
+            if (j + 3 < nblk) half0(S0{}, S2{}, j + 3);
+          }
+        }
+      }
+    }
+    if (nblk > 0) {
+      // P.V of the last half; its stage is that of the last block
+      const int last = (nblk - 1) % NS;
+      if (last == 0) pv(sV_of(S0{}), 1, pB1);
+      else if (NS == 2 || last == 1) pv(sV_of(S1{}), 1, pB1);
+      else pv(sV_of(S2{}), 1, pB1);
+    }
+    // the next segment's loads overwrite the stages: every wave must be done
+    __syncthreads();
+
+    // ---- finalize rows: o = O / l, lse = m * scale + ln l
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      float L = lsum[nb];
+      L += __shfl_xor(L, 16);
+      L += __shfl_xor(L, 32);
+      const int r = wave * 32 + nb * 16 + l16;
+      const bool valid = tloc_r[nb] < qo_len;
+      const bool empty = !(L > 0.f);
+      const float inv = empty ? 0.f : 1.f / L;
+      const float lse = empty ? kNegInf : m[nb] * a.sm_scale + fast_log2(L) * kLn2;
+      if (valid) {
+        if (slot < 0) {
+          const int64_t orow = (int64_t)(q0 + tloc_r[nb]) * a.num_qo_heads + h * G + (r % G);
+#pragma unroll
+          for (int md = 0; md < 8; ++md) {
+            const int64_t off = orow * kD + md * 16 + g16 * 4;
+            const f32x4_t v = O[md][nb] * inv;
+            if (a.out_dtype == ABP_F32) {
+              *reinterpret_cast<float4*>(static_cast<float*>(a.o) + off) =
+                  make_float4(v[0], v[1], v[2], v[3]);
+            } else if (a.out_dtype == ABP_BF16) {
+              *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.o) + off) =
+                  make_uint2(pack2<BF16>(v[0], v[1]), pack2<BF16>(v[2], v[3]));
+            } else {
+              *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.o) + off) =
+                  make_uint2(pack2<F16>(v[0], v[1]), pack2<F16>(v[2], v[3]));
+            }
+          }
+          if (a.lse && g16 == 0) a.lse[orow] = lse;
+        } else {
+          const int64_t prow = (int64_t)slot * kRows + r;
+#pragma unroll
+          for (int md = 0; md < 8; ++md) {
+            const f32x4_t v = O[md][nb] * inv;
+            *reinterpret_cast<float4*>(a.o_part + prow * kD + md * 16 + g16 * 4) =
+                make_float4(v[0], v[1], v[2], v[3]);
+          }
+          if (g16 == 0) a.lse_part[prow] = lse;
+        }
+      }
+    }
+    if (slot >= 0 && plan[H_MERGE_KERNEL] == 0) {
+      merge_if_last<kRows, 64 * NW>(a, tile, &s_last, [&](int r, int64_t* orow) {
+        const int tloc = qt * TQ + r / G;
+        if (tloc >= qo_len) return false;
+        *orow = (int64_t)(q0 + tloc) * a.num_qo_heads + h * G + (r % G);
+        return true;
+      });
+    }
+  }
+}
+
+// The work of one append worker (a workgroup of append_waves<ROPE>() waves);
+// bid is the workgroup's index among the launch's append workgroups.
+// NS: K/V stages of the pipelined worker. Two measured faster than three
+// (716-722 against 733-736 us on the ragged causal append, same box): the
+// refills already land within the two steps they are given.
+template <typename T, int G, bool CAUSAL, bool ROPE, bool FASTPAGE, bool RIL, int NS = 2>
+__device__ __forceinline__ void append_worker(const AttnArgs& a, int bid) {
+  if constexpr (ROPE) append_worker_staged<T, G, CAUSAL, true, FASTPAGE, RIL>(a, bid);
+  else append_worker_pipe<T, G, CAUSAL, FASTPAGE, NS>(a, bid);
 }
 
 }  // namespace appi

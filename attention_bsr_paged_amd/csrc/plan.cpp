@@ -67,6 +67,12 @@ int check_params(int kind, const abp_params* p, Config* cfg, std::string* err) {
     *err = "page_size must be >= 1";
     return ABP_ERR_INVALID_ARG;
   }
+  // one page of K (or V) must stay under 2 GiB: kernels address within a
+  // page with 32-bit byte offsets
+  if (int64_t(p->page_size) * p->num_kv_heads * p->head_dim * 2 >= (int64_t(1) << 31)) {
+    *err = "page_size * num_kv_heads * head_dim * 2 bytes must be below 2 GiB";
+    return ABP_ERR_UNSUPPORTED;
+  }
   if (p->qkv_dtype != ABP_F16 && p->qkv_dtype != ABP_BF16) {
     *err = "qkv_dtype must be ABP_F16 or ABP_BF16";
     return ABP_ERR_UNSUPPORTED;

@@ -32,7 +32,7 @@ __global__ __launch_bounds__(512, 1) void pod_kernel(AttnArgs app, AttnArgs dec)
   static_assert(appi::append_waves<false>() == 8, "append workers are 512-thread workgroups");
   const int b = blockIdx.x;
   if (b < app.workers) {
-    appi::append_worker<T, G, CAUSAL, false, true, false>(app, b);
+    appi::append_worker<T, G, CAUSAL, false, true, false, 2>(app, b);
   } else if (threadIdx.x < 256) {
     dmi::decode_mfma_worker<T, G, false>(dec, b - app.workers);  // ordinary loads: few CUs
   }

@@ -53,7 +53,8 @@
  *  K is stored un-rotated; v is never rotated.
  *
  * Supported: head_dim 128; fp16 or bf16 q/k/v; num_qo_heads / num_kv_heads in
- * {1, 2, 4, 8, 16}; page_size >= 1; kv_len < 2^24; batch >= 0. Decode (without
+ * {1, 2, 4, 8, 16}; page_size >= 1 with one page of K (or V) under 2 GiB;
+ * kv_len < 2^24; batch >= 0. Decode (without
  * RoPE) and page append also take an fp8 e4m3 KV cache (params.kv_fp8).
  *
  * Ownership and lifetime

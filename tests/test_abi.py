@@ -444,3 +444,16 @@ def test_decode_static_rejects_batches_beyond_its_arrays(lib):
                                4096, *([None] * 10), None)
     assert st == abp.ABP_ERR_WORKSPACE_TOO_SMALL
     assert str(abp.ABP_STATIC_SCRATCH_BYTES) in abp.abp_last_error()
+
+
+def test_pages_of_2gib_or_more_are_refused(lib):
+    import ctypes
+    import torch
+    hb, db = ctypes.c_size_t(), ctypes.c_size_t()
+    ok = abp.make_params(32, 8, 128, 1 << 19, torch.bfloat16)        # 1 GiB pages
+    assert lib.abp_workspace_size(0, ctypes.byref(ok), 4, 0, 16, ctypes.byref(hb),
+                                  ctypes.byref(db)) == abp.ABP_OK
+    big = abp.make_params(32, 8, 128, 1 << 20, torch.bfloat16)       # 2 GiB pages
+    assert lib.abp_workspace_size(0, ctypes.byref(big), 4, 0, 16, ctypes.byref(hb),
+                                  ctypes.byref(db)) == abp.ABP_ERR_UNSUPPORTED
+    assert "2 GiB" in abp.abp_last_error()
