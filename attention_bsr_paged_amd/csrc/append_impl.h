@@ -975,6 +975,8 @@ __device__ __forceinline__ void append_worker_pipe(const AttnArgs& a, int bid) {
         vf[1] = vread(sV, vh, 1);
       }
       float p[2][2][4];
+      float part[2] = {0.f, 0.f};
+      uint32_t pk[2][4];  // P of the step, packed pairs, as they are produced
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         __builtin_amdgcn_sched_barrier(0);
@@ -985,6 +987,8 @@ __device__ __forceinline__ void append_worker_pipe(const AttnArgs& a, int bid) {
         const int emb = i >> 2, enb = (i >> 1) & 1, ej = 2 * (i & 1);
         p[emb][enb][ej] = fast_exp2(__builtin_fmaf(S_cur[emb][enb][ej], cl2, -mc[enb]));
         p[emb][enb][ej + 1] = fast_exp2(__builtin_fmaf(S_cur[emb][enb][ej + 1], cl2, -mc[enb]));
+        part[enb] += p[emb][enb][ej] + p[emb][enb][ej + 1];
+        pk[enb][2 * emb + (i & 1)] = pack2<T>(p[emb][enb][ej], p[emb][enb][ej + 1]);
         const int kc = i >> 1, qmb = i & 1;
         const f32x4_t z = f32x4_t{0.f, 0.f, 0.f, 0.f};
         S_nxt[qmb][0] = mfma<T>(kf[i % 3], qf[0][kc], kc == 0 ? z : S_nxt[qmb][0]);
@@ -995,8 +999,6 @@ __device__ __forceinline__ void append_worker_pipe(const AttnArgs& a, int bid) {
         }
       }
       __builtin_amdgcn_sched_barrier(0);
-      float part[2];
-      partial_sums(p, part);
       // every p <= the lane's partial sum <= 2^kSumCheckLog2 keeps the
       // reference; !(x <= kBig) also catches an overflow to inf (and a row
       // still at kNoRef overflows)
@@ -1023,13 +1025,17 @@ __device__ __forceinline__ void append_worker_pipe(const AttnArgs& a, int bid) {
               p[mb][nb][j] = fast_exp2(__builtin_fmaf(S_cur[mb][nb][j], cl2, -mc[nb]));
         }
         partial_sums(p, part);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) pk[nb][w] = pack2<T>(p[w >> 1][nb][2 * (w & 1)], p[w >> 1][nb][2 * (w & 1) + 1]);
       }
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         // row sum in fp32 of the unrounded p: lse must not carry P's 16-bit rounding
         lsum[nb] += part[nb];
-        pB_out[nb] = make_uint4(pack2<T>(p[0][nb][0], p[0][nb][1]), pack2<T>(p[0][nb][2], p[0][nb][3]),
-                                pack2<T>(p[1][nb][0], p[1][nb][1]), pack2<T>(p[1][nb][2], p[1][nb][3]));
+        // K-slots of lane group g16: keys 4 g16 .. + 3, then 16 + 4 g16 .. + 3
+        pB_out[nb] = make_uint4(pk[nb][0], pk[nb][1], pk[nb][2], pk[nb][3]);
       }
       // O took the P.V products of the previous half against the old reference
       if (moved) {
