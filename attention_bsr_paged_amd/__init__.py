@@ -38,6 +38,7 @@ ABP_ERR_PLAN_MISMATCH = -4
 ABP_ERR_HIP = -5
 
 ABP_F16, ABP_BF16, ABP_F32 = 0, 1, 2
+ABP_WORKERS_PER_TILE = -1   # num_workers: one worker per tile, no split (ablation)
 ABP_KIND_DECODE, ABP_KIND_APPEND, ABP_KIND_BSR = 0, 1, 2
 
 # LLaMA 3.1 RoPE frequency scaling: (factor, low_freq_factor, high_freq_factor,

@@ -78,6 +78,15 @@ int resolve_layout(int kind, const abp_params* params, int32_t max_batch, int32_
   if (st != ABP_OK) return fail(st, err);
   if (kind == ABP_KIND_DECODE && cfg->group > 8)
     return fail(ABP_ERR_UNSUPPORTED, "decode supports group sizes 1, 2, 4 and 8");
+  if (workers == ABP_WORKERS_PER_TILE) {
+    // one worker per tile: as many workers as the capacities allow tiles
+    st = abp::make_layout(*cfg, max_batch, max_qo, 1, L, &err);
+    if (st != ABP_OK) return fail(st, err);
+    st = abp::make_layout(*cfg, max_batch, max_qo, std::max<int32_t>(1, L->max_tiles), L, &err);
+    if (st != ABP_OK) return fail(st, err);
+    L->no_split = true;
+    return ABP_OK;
+  }
   if (workers <= 0) {
     st = default_workers(*cfg, &workers);
     if (st != ABP_OK) return st;
@@ -389,7 +398,8 @@ int abp_plan_host(int kind, const abp_params* params, int32_t batch, const int32
                   int32_t max_batch, int32_t max_qo_tokens, int32_t num_workers, void* host_ws,
                   size_t host_bytes, abp_plan* plan) {
   try {
-    if (num_workers <= 0) return fail(ABP_ERR_INVALID_ARG, "abp_plan_host needs num_workers > 0");
+    if (num_workers <= 0 && num_workers != ABP_WORKERS_PER_TILE)
+      return fail(ABP_ERR_INVALID_ARG, "abp_plan_host needs num_workers > 0 or ABP_WORKERS_PER_TILE");
     if (kind == ABP_KIND_BSR)
       return fail(ABP_ERR_INVALID_ARG, "block-sparse plans are made by abp_bsr_plan_host");
     return do_plan(kind, params, batch, qo_indptr_h, kv_indptr_h, kv_last_page_len_h, max_batch,

@@ -82,6 +82,9 @@ struct Layout {
   uint64_t partial_offset = 0; // bytes, 256-aligned
   uint64_t partial_bytes = 0;
   uint64_t dev_bytes = 0;
+  // planning mode (not part of the memory layout): one worker per tile, each
+  // tile one segment, no partial states (workers = the tile capacity)
+  bool no_split = false;
 };
 
 // Tile sizes of the kernels.

@@ -319,6 +319,10 @@ int plan_compute(const Config& cfg, const Layout& L, int32_t batch, const int32_
     *err = "batch exceeds the workspace capacities (max_batch / max_qo_tokens)";
     return ABP_ERR_WORKSPACE_TOO_SMALL;
   }
+  if (L.no_split && T > W) {
+    *err = "one worker per tile needs num_workers >= the number of tiles";
+    return ABP_ERR_INVALID_ARG;
+  }
   const int64_t quota = N > 0 ? ceil_div(N, W) : 1;
 
   // the aux region (block-sparse plans) holds inputs of this call: keep it
@@ -340,7 +344,10 @@ int plan_compute(const Config& cfg, const Layout& L, int32_t batch, const int32_
       for (int64_t qt = 0; qt < nqt; ++qt, ++t) {
         const int64_t e = cfg.causal ? kv_len - qo_len + std::min((qt + 1) * Tq, qo_len) : kv_len;
         const int64_t g1 = g0 + std::max<int64_t>(1, ceil_div(e, Tk));
-        const int64_t w_first = g0 / quota, w_last = (g1 - 1) / quota;
+        // Stream-K: the workers whose block ranges meet [g0, g1); without
+        // splitting, worker t takes tile t whole
+        const int64_t w_first = L.no_split ? t : g0 / quota;
+        const int64_t w_last = L.no_split ? t : (g1 - 1) / quota;
         const int64_t nseg = w_last - w_first + 1;
         max_nseg = std::max(max_nseg, nseg);
         int32_t* tr = tile + 4 * t;
@@ -357,7 +364,8 @@ int plan_compute(const Config& cfg, const Layout& L, int32_t batch, const int32_
           mr[3] = 0;
         }
         for (int64_t w = w_first; w <= w_last; ++w, ++s) {
-          const int64_t lo = std::max(g0, w * quota), hi = std::min(g1, (w + 1) * quota);
+          const int64_t lo = L.no_split ? g0 : std::max(g0, w * quota);
+          const int64_t hi = L.no_split ? g1 : std::min(g1, (w + 1) * quota);
           int32_t* sr = seg + 4 * s;
           sr[0] = (int32_t)t;
           sr[1] = (int32_t)((lo - g0) * Tk);

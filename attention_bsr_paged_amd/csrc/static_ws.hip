@@ -70,7 +70,7 @@ extern "C" int abp_decode_static(const abp_params* params, int32_t batch,
     if (batch < 0) return abp::set_error(ABP_ERR_INVALID_ARG, "batch < 0");
     int32_t workers = num_workers;
     int st = ABP_OK;
-    if (workers <= 0) {
+    if (workers <= 0 && workers != ABP_WORKERS_PER_TILE) {
       st = abp::default_decode_workers(params, &workers);
       if (st != ABP_OK) return st;
     }

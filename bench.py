@@ -10,8 +10,9 @@ workload (64 requests, GQA 32/8, head_dim 128, page 16, bf16, kv_len uniform on
 partition), its upload, the persistent decode kernel and the merge of split
 tiles. Inputs are resident in HBM before the timed region; the K/V pools are
 replicated and rotated (at least 2 GiB in all) so that no step reads data a
-previous step left in the 256 MB last-level cache. Every 4th run of the timed
-steps is bracketed by HIP events on its stream for the per-run figures.
+previous step left in the 256 MB last-level cache. After the K timed steps,
+each leg runs max(100, K) more runs bracketed one by one by HIP events on their
+stream (median, p10 and p90 of the run), sampling the engine clock meanwhile.
 
 Prints one JSON line. ``value`` is achieved HBM throughput of the whole step in
 TB/s (algorithmic bytes: each valid K/V token once, plus q, o, lse and the
@@ -138,26 +139,96 @@ def _stats_ms(ms: np.ndarray) -> dict:
             "p90_us": round(float(np.percentile(ms, 90)) * 1e3, 2)}
 
 
-EVENT_EVERY = 4   # bracket every 4th run of the timed region with HIP events
+SAMPLES = 100     # runs bracketed by HIP events per leg, after the timed steps
 
 
-def timed_steps(torch, stream, step, K, Wm):
-    """Wm untimed steps, then K timed ones; step(i, (ev0, ev1) or None) records the
-    events around the GPU run. Every EVENT_EVERY-th timed run is bracketed: a pair
-    of timing events costs several microseconds of GPU idle time on this stack,
-    so bracketing every run would slow the very steps being timed. Returns (wall
-    ms per step, run ms of the bracketed runs)."""
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(0, K, EVENT_EVERY)]
+def _sclk_path():
+    """sysfs file listing the GPU's engine clock levels, the current one marked
+    with '*' (one GPU per box here; None when it cannot be read)."""
+    import glob
+    paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    vis = os.environ.get("HIP_VISIBLE_DEVICES") or os.environ.get("ROCR_VISIBLE_DEVICES")
+    if len(paths) == 1 or (paths and not vis):
+        return paths[0] if len(paths) == 1 else None
+    return None
+
+
+class ClockSampler:
+    """Samples the current engine clock (MHz) from sysfs every `period` seconds
+    on a background thread while a leg's runs execute."""
+
+    def __init__(self, period: float = 0.002):
+        self.path = _sclk_path()
+        self.period = period
+        self.samples = []
+        self._stop = None
+        self._thread = None
+
+    def _read(self):
+        try:
+            with open(self.path) as f:
+                for line in f:
+                    if "*" in line:
+                        m = re.search(r"(\d+)\s*[Mm][Hh]z", line)
+                        return int(m.group(1)) if m else None
+        except OSError:
+            return None
+        return None
+
+    def __enter__(self):
+        import threading
+        if self.path is None:
+            return self
+        self._stop = threading.Event()
+
+        def run():
+            while not self._stop.is_set():
+                v = self._read()
+                if v is not None:
+                    self.samples.append(v)
+                self._stop.wait(self.period)
+
+        self._thread = threading.Thread(target=run, daemon=True)
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+        return False
+
+    def stats(self):
+        if not self.samples:
+            return None
+        a = np.array(self.samples, dtype=np.float64)
+        return {"median": float(np.median(a)), "min": float(a.min()), "max": float(a.max()),
+                "samples": int(a.size), "source": "pp_dpm_sclk (current level), sampled every "
+                f"{self.period * 1e3:.0f} ms during the event-bracketed runs"}
+
+
+def timed_steps(torch, stream, step, K, Wm, samples=SAMPLES):
+    """Wm untimed steps, then K timed steps (wall clock between two
+    synchronizes, no events inside), then max(samples, K) more runs, each
+    bracketed by HIP events on the run's stream (step(i, (ev0, ev1))), with the
+    engine clock sampled meanwhile. Returns (wall ms per step, run ms of every
+    bracketed run, clock stats)."""
     for i in range(Wm):
         step(i, None)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        step(Wm + i, ev[i // EVENT_EVERY] if i % EVENT_EVERY == 0 else None)
+        step(Wm + i, None)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / K
-    return wall, np.array([a.elapsed_time(b) for a, b in ev])
+    n = max(samples, K)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    with ClockSampler() as cs:
+        for i in range(n):
+            step(Wm + K + i, ev[i])
+        torch.cuda.synchronize()
+    return wall, np.array([a.elapsed_time(b) for a, b in ev]), cs.stats()
 
 
 def replicas(t, torch, total_bytes):
@@ -203,7 +274,7 @@ def bench_decode(abp, wl, torch, dev, w, K, Wm, workers=0) -> dict:
         if evs:
             evs[1].record(stream)
 
-    wall, run_ms = timed_steps(torch, stream, step, K, Wm)
+    wall, run_ms, clk = timed_steps(torch, stream, step, K, Wm)
     plan = dec.plan_struct
     hws = np.zeros(dec.host_ws.numel(), np.uint8)
     plan_us = plan_time_us(lambda: abp.abp_plan_host(
@@ -217,6 +288,7 @@ def bench_decode(abp, wl, torch, dev, w, K, Wm, workers=0) -> dict:
         "ms_per_step": round(wall, 5),
         "run_TBps": round(by / (avg * 1e-3) / 1e12, 4),
         "run": _stats_ms(run_ms),
+        "clock_mhz": clk,
         "algorithmic_bytes": by,
         "plan_host_us": round(plan_us, 2),
         "batch": w.batch,
@@ -265,7 +337,7 @@ def bench_append(abp, wl, torch, dev, K, Wm, workers=0) -> dict:
         if evs:
             evs[1].record(s)
 
-    wall, run_ms = timed_steps(torch, s, step, K, Wm)
+    wall, run_ms, clk = timed_steps(torch, s, step, K, Wm)
     hws = np.zeros(app.host_ws.numel(), np.uint8)
     nq = int(w.qo_indptr[-1])
     plan_us = plan_time_us(lambda: abp.abp_plan_host(
@@ -282,6 +354,7 @@ def bench_append(abp, wl, torch, dev, K, Wm, workers=0) -> dict:
         "ms_per_step": round(wall, 5),
         "causal_flop": flops,
         "run": _stats_ms(run_ms),
+        "clock_mhz": clk,
         "plan_host_us": round(plan_us, 2),
         "qo_tokens": int(w.qo_indptr[-1]),
         "kv_tokens": int(kv.kv_len.sum()),
@@ -343,8 +416,8 @@ def bench_pod(abp, wl, torch, dev, K, Wm) -> dict:
         if evs:
             evs[1].record(s)
 
-    _, seq_ms = timed_steps(torch, s, seq, K, Wm)
-    wall, pod_ms = timed_steps(torch, s, mixed, K, Wm)
+    _, seq_ms, _ = timed_steps(torch, s, seq, K, Wm)
+    wall, pod_ms, clk = timed_steps(torch, s, mixed, K, Wm)
     torch.cuda.synchronize()
     t_seq, t_pod = float(seq_ms.mean()), float(pod_ms.mean())
     return {
@@ -352,6 +425,7 @@ def bench_pod(abp, wl, torch, dev, K, Wm) -> dict:
         "value": round(t_seq / t_pod, 4),
         "unit": "speedup over the decode run then the append run",
         "run": _stats_ms(pod_ms),
+        "clock_mhz": clk,
         "sequential_run": _stats_ms(seq_ms),
         "ms_per_step": round(wall, 5),
         "decode_bytes": by,
@@ -415,11 +489,12 @@ def bench_cascade(abp, wl, torch, dev, K, Wm, workers=0) -> dict:
         if evs:
             evs[1].record(s)
 
-    wall, run_ms = timed_steps(torch, s, step, K, Wm)
+    wall, run_ms, clk = timed_steps(torch, s, step, K, Wm)
     torch.cuda.synchronize()
     avg = float(run_ms.mean())
     return {
         "workload": w.name,
+        "clock_mhz": clk,
         "step_TBps": round(by / (wall * 1e-3) / 1e12, 4),
         "ms_per_step": round(wall, 5),
         "run_TBps": round(by / (avg * 1e-3) / 1e12, 4),
@@ -431,6 +506,165 @@ def bench_cascade(abp, wl, torch, dev, K, Wm, workers=0) -> dict:
         "rope_theta": w.rope_theta,
         "launches": "prefix append (RoPE) + suffix decode (RoPE) + its merge + merge_state",
         "kv_pool_copies": copies,
+    }
+
+
+# ----------------------------------------------------------------------------
+# the pages' comparisons on this chip (cascade workload): RoPE fused at load
+# against a separate rotation pass, and the cascade against a flat page table
+# ----------------------------------------------------------------------------
+def _rope_tables(torch, dev, pos, theta, d=128):
+    """cos / sin of pos * theta^(-2j/d), j < d/2, for a position array (fp32;
+    the separate pass's own inputs, built once outside the timed region)."""
+    f = torch.tensor(theta ** (-np.arange(d // 2, dtype=np.float64) * 2.0 / d),
+                     dtype=torch.float64, device=dev)
+    ang = torch.from_numpy(np.asarray(pos, np.float64)).to(dev)[..., None] * f
+    return torch.cos(ang).float(), torch.sin(ang).float()
+
+
+def _slot_positions(kv, offset):
+    """Position of every slot of a pool [num_pages, page_size] under its page
+    table: request b's logical token t sits at offset[b] + t (unused slots: 0)."""
+    pos = np.zeros((kv.num_pages, kv.page_size), np.int64)
+    for b in range(len(kv.kv_indptr) - 1):
+        pages = kv.kv_indices[kv.kv_indptr[b]:kv.kv_indptr[b + 1]]
+        for i, pg in enumerate(pages):
+            pos[pg] = offset[b] + i * kv.page_size + np.arange(kv.page_size)
+    return pos
+
+
+def bench_cascade_separate_rope(abp, wl, torch, dev, K, Wm, fused_us) -> dict:
+    """Rotate-then-attend: a separate pass (PyTorch elementwise ops) writes
+    rotated q and rotated K pools, then the cascade runs without RoPE on them."""
+    w = wl.cascade_rope()
+    pre, kv = w.prefix, w.kv
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
+    theta = w.rope_theta
+    tot = pre.k_pages.nbytes * 2 + kv.k_pages.nbytes * 2
+    pk, copies = replicas(wl.to_torch(pre.k_pages, w.dtype, dev), torch, tot)
+    pv, _ = replicas(wl.to_torch(pre.v_pages, w.dtype, dev), torch, tot)
+    sk, _ = replicas(wl.to_torch(kv.k_pages, w.dtype, dev), torch, tot)
+    sv, _ = replicas(wl.to_torch(kv.v_pages, w.dtype, dev), torch, tot)
+    q = wl.to_torch(w.q, w.dtype, dev)
+    pc, ps = _rope_tables(torch, dev, _slot_positions(pre, [0]), theta)
+    sc, ss = _rope_tables(torch, dev, _slot_positions(kv, w.kv_pos_offset), theta)
+    qc, qs = _rope_tables(torch, dev, w.q_pos, theta)
+    pre_rot = torch.empty_like(pk[0])
+    suf_rot = torch.empty_like(sk[0])
+    q_rot = torch.empty_like(q)
+
+    def rotate(x, c, sn, out):
+        # x [..., H, 128]: rotate-half pairs (j, j + 64); c / sn [..., 64] broadcast over H
+        xf = x.float()
+        a, b = xf[..., :64], xf[..., 64:]
+        c, sn = c.unsqueeze(-2), sn.unsqueeze(-2)
+        out[..., :64] = (a * c - b * sn).to(out.dtype)
+        out[..., 64:] = (b * c + a * sn).to(out.dtype)
+
+    cas = abp.CascadeDecode(w.num_qo_heads, w.num_kv_heads, w.head_dim, pre.page_size,
+                            kv.page_size, torch.bfloat16, max_batch=w.batch, rope_theta=0.0,
+                            device=dev)
+    pqo = i32([0, w.batch])
+    p_ind, p_idx, p_lpl = i32(pre.kv_indptr), i32(pre.kv_indices), i32(pre.kv_last_page_len)
+    s_ind, s_idx, s_lpl = i32(kv.kv_indptr), i32(kv.kv_indices), i32(kv.kv_last_page_len)
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    bufs = cas.buffers(q)
+    s = torch.cuda.current_stream(dev)
+
+    def step(i, evs):
+        cas.plan(w.batch, pre.kv_indptr, pre.kv_last_page_len, kv.kv_indptr,
+                 kv.kv_last_page_len, stream=s)
+        if evs:
+            evs[0].record(s)
+        c = i % copies
+        rotate(q, qc, qs, q_rot)
+        rotate(pk[c], pc, ps, pre_rot)
+        rotate(sk[c], sc, ss, suf_rot)
+        cas.run(q_rot, pre_rot, pv[c], pqo, p_ind, p_idx, p_lpl, suf_rot, sv[c], s_ind, s_idx,
+                s_lpl, o=o, lse=lse, stream=s, bufs=bufs)
+        if evs:
+            evs[1].record(s)
+
+    wall, run_ms, clk = timed_steps(torch, s, step, K, Wm)
+    avg_us = float(run_ms.mean()) * 1e3
+    return {
+        "what": "rotate q and both K pools with PyTorch elementwise ops (fp32 math, bf16 "
+                "results, 12 launches), then the cascade without RoPE; against the cascade "
+                "with RoPE fused at load",
+        "run": _stats_ms(run_ms),
+        "clock_mhz": clk,
+        "fused_run_avg_us": round(fused_us, 2),
+        "value": round(avg_us / fused_us, 3),
+        "unit": "separate-pass run time / fused run time",
+        "note": "the rotated K pools are rounded to bf16, which costs the separate pass "
+                "accuracy the fused path keeps (its scores use fp32 / hi+lo operands)",
+    }
+
+
+def bench_flat_decode(abp, wl, torch, dev, K, Wm, cascade_us) -> dict:
+    """The cascade workload as one flat page table of 16-token pages: every
+    request lists the shared prefix's pages, then its own, so each request
+    reads the prefix again; RoPE decode over prefix || suffix."""
+    w = wl.cascade_rope()
+    pre, kv = w.prefix, w.kv
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
+    P = kv.page_size
+    pl = int(pre.kv_len[0])
+    # the prefix's keys in logical order, cut into pages of P (shared by every request)
+    order = pre.kv_indices[pre.kv_indptr[0]:pre.kv_indptr[1]]
+    klog = pre.k_pages[order].reshape(-1, w.num_kv_heads, w.head_dim)[:pl]
+    vlog = pre.v_pages[order].reshape(-1, w.num_kv_heads, w.head_dim)[:pl]
+    npre = -(-pl // P)
+    pad = npre * P - pl
+    kpre = np.concatenate([klog, np.zeros((pad,) + klog.shape[1:], klog.dtype)]).reshape(
+        npre, P, w.num_kv_heads, w.head_dim)
+    vpre = np.concatenate([vlog, np.zeros((pad,) + vlog.shape[1:], vlog.dtype)]).reshape(
+        npre, P, w.num_kv_heads, w.head_dim)
+    assert pad == 0, "the prefix fills whole 16-token pages"
+    kflat = np.concatenate([kpre, kv.k_pages])
+    vflat = np.concatenate([vpre, kv.v_pages])
+    B = w.batch
+    lens = np.diff(kv.kv_indptr)
+    indptr = np.concatenate([[0], np.cumsum(lens + npre)]).astype(np.int32)
+    idx = np.concatenate([np.concatenate([np.arange(npre),
+                                          kv.kv_indices[kv.kv_indptr[b]:kv.kv_indptr[b + 1]] + npre])
+                          for b in range(B)]).astype(np.int32)
+    lpl = kv.kv_last_page_len
+    k0, v0 = wl.to_torch(kflat, w.dtype, dev), wl.to_torch(vflat, w.dtype, dev)
+    ks, copies = replicas(k0, torch, k0.nbytes + v0.nbytes)
+    vs, _ = replicas(v0, torch, k0.nbytes + v0.nbytes)
+    q = wl.to_torch(w.q, w.dtype, dev)
+    params = abp.make_params(w.num_qo_heads, w.num_kv_heads, w.head_dim, P, torch.bfloat16,
+                             rope_theta=w.rope_theta)
+    dec = abp.BatchDecode(params, max_batch=B, device=dev)
+    d_ind, d_idx, d_lpl = i32(indptr), i32(idx), i32(lpl)
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    s = torch.cuda.current_stream(dev)
+
+    def step(i, evs):
+        dec.plan(indptr, lpl, stream=s)
+        if evs:
+            evs[0].record(s)
+        c = i % copies
+        # default positions: key t at t, the query on the last key (= the cascade's)
+        dec.run(q, ks[c], vs[c], d_ind, d_idx, d_lpl, o=o, lse=lse, stream=s)
+        if evs:
+            evs[1].record(s)
+
+    wall, run_ms, clk = timed_steps(torch, s, step, K, Wm)
+    avg_us = float(run_ms.mean()) * 1e3
+    logical = (B * pl + int(kv.kv_len.sum())) * w.num_kv_heads * w.head_dim * 2 * 2
+    return {
+        "what": "one flat page table (pages of 16): each request lists the prefix's pages and "
+                "then its own; RoPE batch decode; against the cascade",
+        "run": _stats_ms(run_ms),
+        "clock_mhz": clk,
+        "logical_kv_bytes": logical,
+        "cascade_run_avg_us": round(cascade_us, 2),
+        "value": round(avg_us / cascade_us, 3),
+        "unit": "flat run time / cascade run time",
     }
 
 
@@ -474,7 +708,7 @@ def bench_bsr(abp, wl, torch, dev, K, Wm) -> dict:
         if evs:
             evs[1].record(s)
 
-    wall, run_ms = timed_steps(torch, s, step, K, Wm)
+    wall, run_ms, clk = timed_steps(torch, s, step, K, Wm)
     torch.cuda.synchronize()
     avg = float(run_ms.mean())
     tf = flops / (avg * 1e-3) / 1e12
@@ -488,6 +722,7 @@ def bench_bsr(abp, wl, torch, dev, K, Wm) -> dict:
         "mask_flop": flops,
         "density": round(nnz / (nrb * (w.N // w.C)), 4),
         "run": _stats_ms(run_ms),
+        "clock_mhz": clk,
         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": None, "kernel": "append_kernel over BSR row blocks (+ merge)",
@@ -537,7 +772,7 @@ def bench_page_append(abp, wl, torch, dev, K, Wm) -> dict:
         if evs:
             evs[1].record(s)
 
-    wall, run_ms = timed_steps(torch, s, step, max(1, K // GROUP), max(1, Wm // GROUP))
+    wall, run_ms, clk = timed_steps(torch, s, step, max(1, K // GROUP), max(1, Wm // GROUP))
     torch.cuda.synchronize()
     wall /= GROUP
     run_ms = run_ms / GROUP
@@ -552,6 +787,7 @@ def bench_page_append(abp, wl, torch, dev, K, Wm) -> dict:
         "algorithmic_bytes": by,
         "new_tokens": w.nnz,
         "run": _stats_ms(run_ms),
+        "clock_mhz": clk,
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_TBS * 1e3,
                      "unit": "GB/s", "frac": round(gbs / (HBM_PEAK_TBS * 1e3), 4),
                      "traffic": tr["traffic_bytes_per_run"] if tr else None,
@@ -577,7 +813,7 @@ def bench_copy(torch, dev, K, Wm, nbytes=2 ** 30) -> dict:
         if evs:
             evs[1].record(s)
 
-    _, ms = timed_steps(torch, s, step, K, Wm)
+    _, ms, _ = timed_steps(torch, s, step, K, Wm, samples=K)
     avg = float(ms.mean())
     return {"bytes_read": nbytes, "bytes_written": nbytes,
             "read_plus_write_TBps": round(2 * nbytes / (avg * 1e-3) / 1e12, 4),
@@ -709,6 +945,32 @@ def cpu_baseline_page_append(w, budget_s: float = 4.0) -> dict:
 
 
 # ----------------------------------------------------------------------------
+def comparisons(abp, wl, torch, dev, K, configs) -> dict:
+    """The pages' three comparisons, measured here as ratios (> 1: the method wins):
+    the Stream-K split against one worker per tile on skewed lengths (paper
+    summary, 动态负载均衡调度 / 性能提升), RoPE fused at load against a
+    separate rotation pass (可定制的注意力模板 / 性能提升), and the cascade
+    against a flat page table that reads the prefix once per request
+    (统一的 KV 缓存存储格式 / 高级功能)."""
+    sk = configs["skewed_decode"]
+    ns = bench_decode(abp, wl, torch, dev, wl.skewed_decode_gqa(), K, 5,
+                      abp.ABP_WORKERS_PER_TILE)
+    cas_us = configs["cascade_rope"]["run"]["avg_us"]
+    sep = bench_cascade_separate_rope(abp, wl, torch, dev, K, 5, cas_us)
+    flat = bench_flat_decode(abp, wl, torch, dev, K, 5, cas_us)
+    return {
+        "load_balance_skewed": {
+            "value": round(ns["run"]["avg_us"] / sk["run"]["avg_us"], 3),
+            "unit": "one-worker-per-tile run time / Stream-K run time",
+            "no_split_run": ns["run"], "no_split_workers": ns["workers"],
+            "stream_k_run": sk["run"], "stream_k_workers": sk["workers"],
+            "clock_mhz": ns["clock_mhz"],
+        },
+        "rope_fused_vs_separate": sep,
+        "cascade_vs_flat": flat,
+    }
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -721,7 +983,8 @@ def main(argv=None) -> int:
                     help="skip the single, skewed and cascade workloads")
     ap.add_argument("--part", default="all",
                     choices=["all", "decode", "append", "single", "skewed", "cascade", "copy",
-                             "bsr", "page_append", "fp8_decode", "g8_decode", "pod"],
+                             "bsr", "page_append", "fp8_decode", "g8_decode", "pod",
+                             "comparisons"],
                     help="one workload alone (profiling); 'all' is the benchmark line")
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -757,6 +1020,11 @@ def main(argv=None) -> int:
         return 0
     if part == "pod":
         print(json.dumps(bench_pod(abp, wl, torch, dev, K, Wm)), flush=True)
+        return 0
+    if part == "comparisons":
+        cfg = {"skewed_decode": bench_decode(abp, wl, torch, dev, wl.skewed_decode_gqa(), K, Wm),
+               "cascade_rope": bench_cascade(abp, wl, torch, dev, K, Wm)}
+        print(json.dumps(comparisons(abp, wl, torch, dev, K, cfg)), flush=True)
         return 0
     if part in ("single", "skewed", "fp8_decode", "g8_decode"):
         w = {"single": wl.single_decode_mha, "skewed": wl.skewed_decode_gqa,
@@ -827,6 +1095,7 @@ def main(argv=None) -> int:
             "skewed_decode": bench_decode(abp, wl, torch, dev, wl.skewed_decode_gqa(), Kc, 5),
             "cascade_rope": bench_cascade(abp, wl, torch, dev, Kc, 5),
         }
+        out["comparisons"] = comparisons(abp, wl, torch, dev, Kc, out["configs"])
         out["next"] = {
             "bsr_sparse": bench_bsr(abp, wl, torch, dev, Kc, 5),
             "page_append": bench_page_append(abp, wl, torch, dev, Kc, 5),

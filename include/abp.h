@@ -169,10 +169,17 @@ const char* abp_last_error(void);
 /* Number of compute units of HIP device `device` (cached). */
 int abp_device_num_cus(int device, int32_t* num_cus);
 
+/* num_workers value selecting the plan without load balancing, as an ablation
+ * of the Stream-K split (paper summary, section 动态负载均衡调度): one worker
+ * per tile, each tile one segment, no partial states. The grid is then the
+ * tile capacity of the workspace (max_batch x kv-head groups for decode). */
+#define ABP_WORKERS_PER_TILE (-1)
+
 /* Workspace sizes for plans of `kind` with at most `max_batch` requests,
  * `max_qo_tokens` query tokens (append; ignored for decode) and `num_workers`
- * workers (<= 0: one per resident workgroup slot of the current device, i.e.
- * compute units times the workgroups of the selected kernel that fit on one).
+ * workers (ABP_WORKERS_PER_TILE: one per tile, no split; other values <= 0:
+ * one per resident workgroup slot of the current device, i.e. compute units
+ * times the workgroups of the selected kernel that fit on one).
  * Pure host code except the device query for num_workers <= 0. */
 int abp_workspace_size(int kind, const abp_params* params, int32_t max_batch,
                        int32_t max_qo_tokens, int32_t num_workers, size_t* host_bytes,
@@ -180,7 +187,8 @@ int abp_workspace_size(int kind, const abp_params* params, int32_t max_batch,
 
 /* The planner alone (host only, no HIP call): validate the index arrays and
  * write the plan into `host_ws` (>= host_bytes of abp_workspace_size).
- * qo_indptr_h is read for ABP_KIND_APPEND only. num_workers must be > 0.
+ * qo_indptr_h is read for ABP_KIND_APPEND only. num_workers must be > 0 or
+ * ABP_WORKERS_PER_TILE.
  * Work is cut into blocks of tile_kv keys and spread over the workers in equal
  * contiguous ranges (Stream-K), paper summary section 动态负载均衡调度. */
 int abp_plan_host(int kind, const abp_params* params, int32_t batch, const int32_t* qo_indptr_h,

@@ -75,8 +75,12 @@ def kv_lengths(kv_indptr: Sequence[int], kv_last_page_len: Sequence[int], page_s
 def plan_ref(kind: int, batch: int, kv_indptr, kv_last_page_len, page_size: int,
              num_kv_heads: int, num_workers: int, tile_kv: int, qo_indptr=None,
              tile_q: int = 1, causal: bool = False,
-             heads_per_tile: int = 1) -> Dict[str, np.ndarray]:
-    """Return the plan as int32 arrays (see the module docstring for the rule)."""
+             heads_per_tile: int = 1, no_split: bool = False) -> Dict[str, np.ndarray]:
+    """Return the plan as int32 arrays (see the module docstring for the rule).
+
+    ``no_split`` is the ablation without load balancing: worker t takes tile t
+    whole (one segment, no partial states); ``num_workers`` must be at least
+    the number of tiles, and the workers past them get nothing."""
     if num_workers < 1 or tile_kv < 1 or tile_q < 1 or num_kv_heads < 1 or batch < 0:
         raise PlanError("bad sizes")
     if heads_per_tile < 1 or num_kv_heads % heads_per_tile:
@@ -117,8 +121,16 @@ def plan_ref(kind: int, batch: int, kv_indptr, kv_last_page_len, page_size: int,
     quota = _ceil_div(N, num_workers) if N else 1
 
     seg_tile, seg_begin, seg_end, seg_worker = [], [], [], []
+    if no_split and T > num_workers:
+        raise PlanError("one worker per tile needs num_workers >= the number of tiles")
     g0 = 0
     for t in range(T):
+        if no_split:
+            seg_tile.append(t)
+            seg_begin.append(0)
+            seg_end.append(extent[t])
+            seg_worker.append(t)
+            continue
         g1 = g0 + nblk[t]
         w = g0 // quota
         while w * quota < g1:

@@ -117,16 +117,21 @@ def _compare(kind, p, B, qo_indptr, kv_indptr, lpl, W, G, max_qo=0):
     ws = _ws(kind, p, B, max_qo, W)
     plan = abp.abp_plan_host(kind, p, B, qo_indptr, kv_indptr, lpl, B, max_qo, W, ws)
     got = abp.decode_plan_arrays(ws, plan)
+    no_split = W == abp.ABP_WORKERS_PER_TILE
+    if no_split:
+        W = plan.num_workers   # the tile capacity
+        assert W == max(1, plan.max_tiles)
     if kind == KIND_DECODE:
         # decode tiles take 4 consecutive kv heads when the count allows, else 1
         hpt = 4 if p.num_kv_heads % 4 == 0 else 1
         assert int(got["tile_heads"][0]) == hpt
         assert plan.rows_per_tile == hpt * G
         ref = plan_ref(KIND_DECODE, B, kv_indptr, lpl, p.page_size, p.num_kv_heads, W, 64,
-                       heads_per_tile=hpt)
+                       heads_per_tile=hpt, no_split=no_split)
     else:
         ref = plan_ref(KIND_APPEND, B, kv_indptr, lpl, p.page_size, p.num_kv_heads, W, 64,
-                       qo_indptr=qo_indptr, tile_q=256 // G, causal=bool(p.causal))
+                       qo_indptr=qo_indptr, tile_q=256 // G, causal=bool(p.causal),
+                       no_split=no_split)
     for k, v in ref.items():
         assert np.array_equal(got[k], v), k
     # merge placement: decode always uses the merge kernel; append merges inside
@@ -146,7 +151,7 @@ def test_cpp_planner_matches_reference(data):
     page = data.draw(st.sampled_from([1, 3, 16, 256]))
     G = data.draw(st.sampled_from([1, 2, 4, 8]))
     hkv = data.draw(st.sampled_from([1, 2, 3, 4, 8, 12, 16]))
-    W = data.draw(st.integers(1, 70))
+    W = data.draw(st.sampled_from([abp.ABP_WORKERS_PER_TILE]) | st.integers(1, 70))
     kv_len = data.draw(st.lists(st.integers(0, 3000), min_size=B, max_size=B))
     npg = [-(-n // page) for n in kv_len]
     indptr = np.concatenate([[0], np.cumsum(npg)]).astype(np.int32)
@@ -173,7 +178,7 @@ def test_planner_on_named_decode_workloads(lib, name):
         rest = np.clip(np.rint(np.exp(rng.normal(np.log(512.0), 1.0, size=127))), 16, 16384)
         kv_len = np.concatenate([[32768], rest]).astype(np.int64)
     indptr, _, lpl = wl.page_table(kv_len, 16, np.arange(10 ** 6))
-    for W in (256, 512, 1024):
+    for W in (256, 512, 1024, abp.ABP_WORKERS_PER_TILE):
         _compare(KIND_DECODE, P(), len(kv_len), None, indptr, lpl, W, 4)
 
 

@@ -336,3 +336,16 @@ def test_matrix_core_decode_chunk_edges(P, G, hkv, dtype):
     for W in (1, 7, 64, 0):
         o, l = run_decode(w, num_workers=W)
         assert_parity(o, l, o_ref, l_ref, dtype, what=f"mfma decode P{P} G{G} hkv{hkv} W{W}")
+
+
+def test_one_worker_per_tile_plan():
+    """The plan without load balancing (ABP_WORKERS_PER_TILE: one worker per
+    tile, no split, no partial states) gives the same attention."""
+    w = wl.small_decode(13, [0, 1, 17, 700, 3000, 64], 16, 32, 8)
+    o_ref, l_ref = ora.decode_workload(w)
+    o, l = run_decode(w, num_workers=abp.ABP_WORKERS_PER_TILE)
+    assert_parity(o, l, o_ref, l_ref, "bf16", what="one worker per tile")
+    w3 = wl.small_decode(14, [0, 5, 300, 2000], 3, 8, 2)
+    o_ref, l_ref = ora.decode_workload(w3)
+    o, l = run_decode(w3, num_workers=abp.ABP_WORKERS_PER_TILE)
+    assert_parity(o, l, o_ref, l_ref, "bf16", what="one worker per tile, P 3")

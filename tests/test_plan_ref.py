@@ -141,3 +141,36 @@ def test_invariants_random(data):
                 for qt in range(-(-m // Tq)):
                     ext.append(n - m + min((qt + 1) * Tq, m) if causal else n)
     check_invariants(p, W, Tk, ext)
+
+
+def test_no_split_hand_example():
+    # The decode example above without load balancing: worker t takes tile t
+    # whole. Tile 0 (10 keys, 3 blocks) is one segment [0, 10) on worker 0,
+    # tile 1 (4 keys) one segment [0, 4) on worker 1; worker 2 gets nothing;
+    # no partial states and nothing to merge.
+    p = plan_ref(KIND_DECODE, 2, [0, 3, 4], [2, 4], 4, 1, 3, 4, no_split=True)
+    assert p["worker_seg_indptr"].tolist() == [0, 1, 2, 2]
+    assert p["seg_tile"].tolist() == [0, 1]
+    assert p["seg_kv_begin"].tolist() == [0, 0]
+    assert p["seg_kv_end"].tolist() == [10, 4]
+    assert p["seg_partial"].tolist() == [-1, -1]
+    assert p["num_partials"].tolist() == [0]
+    assert p["merge_list"].tolist() == []
+    with pytest.raises(PlanError):
+        plan_ref(KIND_DECODE, 2, [0, 3, 4], [2, 4], 4, 1, 1, 4, no_split=True)
+
+
+def test_no_split_covers_each_tile_once_on_its_own_worker():
+    rng = np.random.Generator(np.random.PCG64(77))
+    kv = rng.integers(0, 500, size=9)
+    npg = -(-kv // 16)
+    indptr = np.concatenate([[0], np.cumsum(npg)])
+    lpl = np.where(npg > 0, kv - (npg - 1) * 16, 0)
+    p = plan_ref(KIND_DECODE, 9, indptr, lpl, 16, 8, 20, 64, heads_per_tile=4, no_split=True)
+    T = len(p["tile_b"])
+    assert T == 18
+    wsi = p["worker_seg_indptr"]
+    assert (np.diff(wsi)[:T] == 1).all() and (np.diff(wsi)[T:] == 0).all()
+    assert p["seg_tile"].tolist() == list(range(T))
+    assert (p["seg_kv_begin"] == 0).all()
+    assert p["seg_kv_end"].tolist() == [int(kv[b]) for b in p["tile_b"]]
