@@ -41,8 +41,29 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_fp8_kernel(AttnArgs a) {
   dmi::decode_mfma_fp8_worker<T, G>(a, blockIdx.x);
 }
 
+// RoPE: the rotation state needs more registers, so one workgroup per CU
+template <typename T, int G, bool RIL>
+__global__ __launch_bounds__(256, 1) void decode_mfma_rope_kernel(AttnArgs a) {
+  dmi::decode_mfma_rope_worker<T, G, RIL>(a, blockIdx.x);
+}
+
 template <typename T>
 hipError_t launch_t(const Config& cfg, const AttnArgs& a, hipStream_t s) {
+  if (cfg.rope) {
+    const bool il = cfg.rope_interleave != 0;
+    switch (cfg.group) {
+      case 4:
+        if (il) decode_mfma_rope_kernel<T, 4, true><<<a.workers, 256, 0, s>>>(a);
+        else decode_mfma_rope_kernel<T, 4, false><<<a.workers, 256, 0, s>>>(a);
+        break;
+      case 8:
+        if (il) decode_mfma_rope_kernel<T, 8, true><<<a.workers, 256, 0, s>>>(a);
+        else decode_mfma_rope_kernel<T, 8, false><<<a.workers, 256, 0, s>>>(a);
+        break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   if (cfg.kv_fp8) {
     switch (cfg.group) {
       case 4: decode_mfma_fp8_kernel<T, 4><<<a.workers, 256, 0, s>>>(a); break;
@@ -63,7 +84,7 @@ hipError_t launch_t(const Config& cfg, const AttnArgs& a, hipStream_t s) {
 
 bool decode_mfma_applies(const Config& cfg) {
   const bool pow2 = (cfg.page_size & (cfg.page_size - 1)) == 0;
-  return !cfg.rope && pow2 && cfg.page_size >= 16 && cfg.hkv % 4 == 0 &&
+  return !(cfg.rope && cfg.kv_fp8) && pow2 && cfg.page_size >= 16 && cfg.hkv % 4 == 0 &&
          (cfg.group == 4 || cfg.group == 8);
 }
 
@@ -78,6 +99,12 @@ hipError_t launch_decode_mfma(const Config& cfg, const AttnArgs& a, hipStream_t 
 // workers beat three (63.5 against 66.4 us).
 int decode_mfma_blocks_per_cu(const Config& cfg) {
   int n = 0;
+  if (cfg.rope) {
+    const hipError_t e = cfg.qkv_dtype == ABP_BF16
+        ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_rope_kernel<BF16, 4, false>, 256, 0)
+        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_rope_kernel<F16, 4, false>, 256, 0);
+    return e == hipSuccess ? (n < 1 ? n : 1) : 0;
+  }
   if (cfg.kv_fp8) {
     const hipError_t e = cfg.qkv_dtype == ABP_BF16
         ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_fp8_kernel<BF16, 4>, 256, 0)

@@ -307,6 +307,321 @@ __device__ __forceinline__ void decode_mfma_worker(const AttnArgs& a, int worker
   }
 }
 
+// 8 fp32 values as 16-bit hi parts and the 16-bit rounding of the remainders
+// (hi + lo carries ~16 significant bits), for products that keep fp32-level
+// accuracy with three 16-bit matrix products
+template <typename T>
+__device__ __forceinline__ void split_hilo(const float v[8], uint4& hi, uint4& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    h[w] = pack2<T>(v[2 * w], v[2 * w + 1]);
+    l[w] = pack2<T>(v[2 * w] - lo_f32<T>(h[w]), v[2 * w + 1] - hi_f32<T>(h[w]));
+  }
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+__device__ __forceinline__ uint32_t word_of(const uint4& u, int j) {
+  return j == 0 ? u.x : j == 1 ? u.y : j == 2 ? u.z : u.w;
+}
+
+// Element e (0..7) of 8 16-bit values as fp32
+template <typename T>
+__device__ __forceinline__ float elem(const uint4& u, int e) {
+  const uint32_t w = word_of(u, e >> 1);
+  return (e & 1) ? hi_f32<T>(w) : lo_f32<T>(w);
+}
+
+// The rotary pairs a lane holds for one token row in the S^T operand layout
+// (windows kc = 0..3, head dims 32 kc + 8 g16 + e): rotate-half pairs
+// (j, j + 64) are elements e of windows kc and kc + 2, i = 8 kc + e for
+// kc < 2 (j = 32 kc + 8 g16 + e); adjacent pairs (2j, 2j + 1) are word w of
+// window kc, i = 4 kc + w (j = 16 kc + 4 g16 + w). Rotates the 16 pairs by
+// the angles whose cosines and sines are cs / sn and returns the 4 windows
+// as hi and lo 16-bit parts.
+template <typename T, bool RIL>
+__device__ __forceinline__ void rope_windows(const uint4 (&k)[4], const float (&cs)[16],
+                                             const float (&sn)[16], uint4 (&hi)[4],
+                                             uint4 (&lo)[4]) {
+  float r[4][8];
+  if constexpr (RIL) {
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int i = 4 * kc + w;
+        const float x = elem<T>(k[kc], 2 * w), y = elem<T>(k[kc], 2 * w + 1);
+        r[kc][2 * w] = __builtin_fmaf(-y, sn[i], x * cs[i]);
+        r[kc][2 * w + 1] = __builtin_fmaf(x, sn[i], y * cs[i]);
+      }
+  } else {
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = 8 * kc + e;
+        const float x = elem<T>(k[kc], e), y = elem<T>(k[kc + 2], e);
+        r[kc][e] = __builtin_fmaf(-y, sn[i], x * cs[i]);
+        r[kc + 2][e] = __builtin_fmaf(x, sn[i], y * cs[i]);
+      }
+  }
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc) split_hilo<T>(r[kc], hi[kc], lo[kc]);
+}
+
+// Decode with LLaMA RoPE fused at load, on the matrix cores: the worker of
+// decode_mfma_worker with q and every K row rotated in fp32 before the
+// products. q (at its position) and K (key t at kv_pos_offset + t) enter
+// S^T = K Q^T as 16-bit hi and lo parts, S^T = Kh Qh + Kh Ql + Kl Qh, so the
+// scores keep fp32-level accuracy (rounding the rotated operands to 16 bits
+// moves lse by up to ~1e-2). A lane's 16 pairs keep the cosine and sine of
+// their angle at the lane's token of the next 16-token tile; each tile steps
+// them by 16 positions (angle addition), and every kAnchorTiles tiles they are
+// evaluated exactly again, so the stepping error stays below ~1e-5 rad. V is
+// not rotated: its path is the one of decode_mfma_worker.
+constexpr int kAnchorTiles = 32;
+
+template <typename T, int G, bool RIL>
+__device__ __forceinline__ void decode_mfma_rope_worker(const AttnArgs& a, int worker) {
+  static_assert(G == 4 || G == 8, "rows of one kv head fill at most one 16-row tile");
+  constexpr int HT = 4;
+  __shared__ __align__(16) uint16_t sV0[HT][kC * kD];
+  __shared__ __align__(16) uint16_t sV1[HT][kC * kD];
+
+  const ABP_CONST_AS int32_t* plan = const_as(a.plan);
+  const ABP_CONST_AS int32_t* wseg = plan + plan[H_OFF_WSEG];
+  const ABP_CONST_AS int32_t* segs = plan + plan[H_OFF_SEG];
+  const ABP_CONST_AS int32_t* tiles = plan + plan[H_OFF_TILE];
+  const float* rope = reinterpret_cast<const float*>(a.plan + plan[H_OFF_ROPE]);
+  const ABP_CONST_AS int32_t* kv_indptr = const_as(a.kv_indptr);
+  const ABP_CONST_AS int32_t* kv_indices = const_as(a.kv_indices);
+  const int s_begin = wseg[worker], s_end = wseg[worker + 1];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g16 = lane >> 4;
+  const int l16 = lane & 15;
+  const float cl2 = a.sm_scale_log2;
+  const float thr = kRescaleLog2 / cl2;
+  const uint16_t* __restrict__ kp = static_cast<const uint16_t*>(a.k_pages);
+  const uint16_t* __restrict__ vp = static_cast<const uint16_t*>(a.v_pages);
+  const int P = a.page_size;
+  const int shift = a.page_shift;
+  const int tstride = a.token_stride;
+  uint16_t* const myV0 = sV0[wave];
+  uint16_t* const myV1 = sV1[wave];
+
+  // pair i of this lane: rotate-half j = 32 (i / 8) + 8 g16 + i % 8,
+  // interleaved j = 16 (i / 4) + 4 g16 + i % 4
+  auto pair_j = [&](int i) {
+    return RIL ? 16 * (i >> 2) + 4 * g16 + (i & 3) : 32 * (i >> 3) + 8 * g16 + (i & 7);
+  };
+  // exact cosines and sines of the lane's 16 pairs at position pos
+  auto anchor = [&](float pos, float (&cs)[16], float (&sn)[16]) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int j = pair_j(i);
+      rope_sincos(pos, rope[2 * j], rope[2 * j + 1], &sn[i], &cs[i]);
+    }
+  };
+  // the rotation by 16 positions
+  float c16[16], s16[16];
+  anchor(16.f, c16, s16);
+
+  for (int s = s_begin; s < s_end; ++s) {
+    const int tile = segs[4 * s];
+    const int kv_begin = segs[4 * s + 1], kv_end = segs[4 * s + 2], slot = segs[4 * s + 3];
+    const int b = tiles[4 * tile], h = tiles[4 * tile + 1] + wave;
+    const int ip0 = kv_indptr[b];
+    const int npg = kv_indptr[b + 1] - ip0;
+    const int kv_len = npg > 0 ? (npg - 1) * P + a.kv_last_page_len[b] : 0;
+    const float qpos = a.q_pos ? (float)a.q_pos[b] : (float)(kv_len - 1);
+    const float kpos0 = a.kv_pos_offset ? (float)a.kv_pos_offset[b] : 0.f;
+
+    // rotated q of row l16 (< G) as hi / lo B operands; rows >= G are zero
+    uint4 qh[4], ql[4];
+    {
+      const int qr = l16 < G ? l16 : G - 1;
+      const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
+                             (int64_t(b) * a.num_qo_heads + int64_t(h) * G + qr) * kD + 8 * g16;
+      const uint32_t keep = l16 < G ? 0xffffffffu : 0u;
+      uint4 qf[4];
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        const uint4 v = *reinterpret_cast<const uint4*>(qrow + 32 * kc);
+        qf[kc] = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
+      }
+      float cs[16], sn[16];
+      anchor(qpos, cs, sn);
+      rope_windows<T, RIL>(qf, cs, sn, qh, ql);
+    }
+    // angles at the lane's token of the next 16-token tile (tile index tcount)
+    float cs[16], sn[16];
+    int tcount = 0;
+
+    float m = kNegInf, lsum = 0.f;
+    f32x4_t O[8];
+#pragma unroll
+    for (int md = 0; md < 8; ++md) O[md] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    auto row_base = [&](int t) -> int64_t {
+      return int64_t(kv_indices[ip0 + (t >> shift)]) * a.page_stride +
+             int64_t(t & (P - 1)) * tstride + int64_t(h) * kD;
+    };
+    // K of chunk c: tile mb = tokens c + 16 mb .. + 15 (a tile past kv_end
+    // re-reads tile 0, in bounds and masked); lane: token l16 of the tile
+    auto load_k = [&](int c, uint4 (&kr)[2][4]) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int t0 = (c + 16 * mb < kv_end) ? c + 16 * mb : c;
+        const uint16_t* rp = kp + row_base(t0) + int64_t(l16) * tstride + 8 * g16;
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) kr[mb][kc] = load_once(reinterpret_cast<const uint4*>(rp + 32 * kc));
+      }
+    };
+    // V of chunk c into this wave's LDS stage, as in decode_mfma_worker (rows
+    // at or past kv_end take the last key's values)
+    auto load_v = [&](int c, uint16_t* dst) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int mb = i >> 2;
+        const int t0 = (c + 16 * mb < kv_end) ? c + 16 * mb : c;
+        const int r = 4 * i + (lane >> 4);
+        const int qv = (lane & 15) ^ (2 * (r & 7));
+        const int rs = min(r & 15, kv_end - 1 - t0);
+        const uint16_t* src = vp + row_base(t0) + int64_t(rs) * tstride + qv * 8;
+        __builtin_amdgcn_global_load_lds(src, (ABP_LDS void*)(dst + 4 * i * kD), 16, 0, 2);
+      }
+    };
+
+    auto compute = [&](int c, const uint4 (&kr)[2][4], const uint16_t* sv)
+                       __attribute__((always_inline)) {
+      f32x4_t S[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        if (tcount % kAnchorTiles == 0) anchor(kpos0 + (float)(c + 16 * mb + l16), cs, sn);
+        uint4 kh[4], kl[4];
+        rope_windows<T, RIL>(kr[mb], cs, sn, kh, kl);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {  // to the next tile: 16 positions further
+          const float cn = __builtin_fmaf(-sn[i], s16[i], cs[i] * c16[i]);
+          sn[i] = __builtin_fmaf(cs[i], s16[i], sn[i] * c16[i]);
+          cs[i] = cn;
+        }
+        ++tcount;
+        S[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+          S[mb] = mfma16<T>(kh[kc], qh[kc], S[mb]);
+          S[mb] = mfma16<T>(kh[kc], ql[kc], S[mb]);
+          S[mb] = mfma16<T>(kl[kc], qh[kc], S[mb]);
+        }
+      }
+      if (c + kC > kv_end) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (c + 16 * mb + 4 * g16 + j >= kv_end) S[mb][j] = kNegInf;
+      }
+      float mx = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(S[0][0], S[0][1]),
+                                                 __builtin_fmaxf(S[0][2], S[0][3])),
+                                 __builtin_fmaxf(__builtin_fmaxf(S[1][0], S[1][1]),
+                                                 __builtin_fmaxf(S[1][2], S[1][3])));
+      mx = max4groups(mx);
+      if (__builtin_amdgcn_ballot_w64(mx > m + thr)) {
+        const float mn = __builtin_fmaxf(m, mx);
+        const float alpha = mn == kNegInf ? 1.f : fast_exp2((m - mn) * cl2);
+        m = mn;
+        lsum *= alpha;
+#pragma unroll
+        for (int md = 0; md < 8; ++md) O[md] *= alpha;
+      }
+      const float mc = (m == kNegInf ? 0.f : m) * cl2;
+      float p[2][4];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) p[mb][j] = fast_exp2(__builtin_fmaf(S[mb][j], cl2, -mc));
+      lsum += ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) +
+              ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
+      const uint4 pB = make_uint4(pack2<T>(p[0][0], p[0][1]), pack2<T>(p[0][2], p[0][3]),
+                                  pack2<T>(p[1][0], p[1][1]), pack2<T>(p[1][2], p[1][3]));
+      const int kA = 4 * g16 + (l16 >> 2);
+      const int kB = kA + 16;
+#pragma unroll
+      for (int md = 0; md < 8; ++md) {
+        const int d0 = md * 16 + 4 * (l16 & 3);
+        const int offA = kA * kD + (((d0 >> 3) ^ (2 * (kA & 7))) * 8) + (d0 & 7);
+        const int offB = kB * kD + (((d0 >> 3) ^ (2 * (kB & 7))) * 8) + (d0 & 7);
+        const v4i16_t a4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ABP_LDS v4i16_t*)(sv + offA));
+        const v4i16_t b4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ABP_LDS v4i16_t*)(sv + offB));
+        const uint2 av = __builtin_bit_cast(uint2, a4), bv = __builtin_bit_cast(uint2, b4);
+        O[md] = mfma16<T>(make_uint4(av.x, av.y, bv.x, bv.y), pB, O[md]);
+      }
+    };
+
+    // chunk n + 1 is loaded while chunk n is computed (as in decode_mfma_worker)
+    const int nch = kv_begin < kv_end ? (kv_end - kv_begin + kC - 1) / kC : 0;
+    uint4 KA[2][4], KB[2][4];
+    if (nch > 0) {
+      load_v(kv_begin, myV0);
+      load_k(kv_begin, KA);
+    }
+    for (int n = 0; n < nch; n += 2) {
+      const int c = kv_begin + n * kC;
+      const bool has1 = n + 1 < nch;
+      if (has1) {
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): stage 1 reads of chunk n - 1
+        load_v(c + kC, myV1);
+        load_k(c + kC, KB);
+        __builtin_amdgcn_s_waitcnt(0x4f70);  // vmcnt(16)
+      } else {
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+      }
+      compute(c, KA, myV0);
+      if (has1) {
+        if (n + 2 < nch) {
+          __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): stage 0 reads of chunk n
+          load_v(c + 2 * kC, myV0);
+          load_k(c + 2 * kC, KA);
+          __builtin_amdgcn_s_waitcnt(0x4f70);  // vmcnt(16)
+        } else {
+          __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+        }
+        compute(c + kC, KB, myV1);
+      }
+    }
+
+    float L = lsum;
+    L += __shfl_xor(L, 16);
+    L += __shfl_xor(L, 32);
+    const bool empty = !(L > 0.f);
+    const float inv = empty ? 0.f : 1.f / L;
+    const float lse = empty ? kNegInf : m * a.sm_scale + fast_log2(L) * kLn2;
+    if (l16 < G) {
+      if (slot < 0) {
+        const int64_t row = int64_t(b) * a.num_qo_heads + int64_t(h) * G + l16;
+#pragma unroll
+        for (int md = 0; md < 8; ++md) store4_dt(a.o, row * kD + md * 16 + 4 * g16, O[md] * inv,
+                                                 a.out_dtype);
+        if (a.lse && g16 == 0) a.lse[row] = lse;
+      } else {
+        const int64_t row = int64_t(slot) * (HT * G) + int64_t(wave) * G + l16;
+#pragma unroll
+        for (int md = 0; md < 8; ++md) {
+          const f32x4_t v = O[md] * inv;
+          *reinterpret_cast<float4*>(a.o_part + row * kD + md * 16 + 4 * g16) =
+              make_float4(v[0], v[1], v[2], v[3]);
+        }
+        if (g16 == 0) a.lse_part[row] = lse;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the next segment refills the stages
+  }
+}
+
 // The same decode for an fp8 (OCP e4m3) KV cache. K and V rows are half as
 // wide, so each lane's share is loaded into registers as codes and widened
 // to the query's 16-bit type on the way to the matrix cores:

@@ -349,3 +349,26 @@ def test_one_worker_per_tile_plan():
     o_ref, l_ref = ora.decode_workload(w3)
     o, l = run_decode(w3, num_workers=abp.ABP_WORKERS_PER_TILE)
     assert_parity(o, l, o_ref, l_ref, "bf16", what="one worker per tile, P 3")
+
+
+@pytest.mark.parametrize("variant", ["rotate_half", "interleaved", "llama31"])
+@pytest.mark.parametrize("G,P,dtype", [(4, 16, "bf16"), (8, 16, "fp16"), (4, 256, "fp16"),
+                                       (8, 64, "bf16")])
+def test_rope_decode_matrix_cores(variant, G, P, dtype):
+    """RoPE decode on the matrix-core path (kv heads a multiple of 4, G 4 or 8,
+    power-of-two pages >= 16): q and K rotated in fp32, hi/lo products. Key
+    offsets and query positions vary per request; slots without a token hold
+    NaN / inf."""
+    say(f"[case] matrix-core rope decode {variant} G={G} P={P} {dtype}")
+    lens = [0, 1, 15, 16, 17, 33, 64, 65, 500, 1000, 2100]
+    w = wl.small_decode(600 + G + P, lens, P, 8 * G, 8, dtype=dtype)
+    w.kv = wl.poison_unwritten(w.kv)
+    w.rope_theta = 500000.0
+    w.rope_interleave = variant == "interleaved"
+    w.rope_llama31 = abp.LLAMA31_ROPE if variant == "llama31" else None
+    w.kv_pos_offset = (np.arange(len(lens)) * 37 % 5000).astype(np.int32)
+    w.q_pos = (w.kv_pos_offset + w.kv.kv_len - 1 + np.arange(len(lens)) % 3).astype(np.int32)
+    o_ref, l_ref = ora.decode_workload(w)
+    for W in (1, 13, 0):
+        o, l = run_decode(w, num_workers=W)
+        assert_parity(o, l, o_ref, l_ref, dtype, what=f"mfma rope {variant} G{G} P{P} W{W}")
