@@ -53,7 +53,8 @@ using appi::append_waves;
 
 template <typename T, int G, bool CAUSAL, bool ROPE, bool FASTPAGE, bool RIL>
 __global__ __launch_bounds__(64 * append_waves<ROPE>(), 1) void append_kernel(AttnArgs a) {
-  appi::append_worker<T, G, CAUSAL, ROPE, FASTPAGE, RIL>(a, blockIdx.x);
+  ABP_APPEND_PIPE_LDS(lds, 2);
+  appi::append_worker<T, G, CAUSAL, ROPE, FASTPAGE, RIL>(a, blockIdx.x, lds);
 }
 
 template <typename T, int G, bool CAUSAL, bool ROPE, bool RIL>

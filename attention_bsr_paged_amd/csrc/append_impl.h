@@ -706,6 +706,27 @@ __device__ __forceinline__ void append_worker_staged(const AttnArgs& a, int bid)
 constexpr float kSumCheckLog2 = 16.f;
 constexpr float kNoRef = -1.0e30f;
 
+// LDS of the pipelined append worker: K and V stages of kTk * kD elements
+// each (the third ones only with three stages) and the merge flag, declared by
+// the kernel as separate arrays (ABP_APPEND_PIPE_LDS), so the compiler sees
+// every stage as its own object; a kernel with other roles may lend it larger
+// arrays of its own.
+struct PipeLds {
+  uint16_t *k0, *k1, *k2, *v0, *v1, *v2;
+  int* last;
+};
+
+#define ABP_APPEND_PIPE_LDS(name, NS)                                                      \
+  __shared__ __align__(16) uint16_t name##_k0[appi::kTk * appi::kD];                      \
+  __shared__ __align__(16) uint16_t name##_k1[appi::kTk * appi::kD];                      \
+  __shared__ __align__(16) uint16_t name##_k2[(NS) > 2 ? appi::kTk * appi::kD : 8];       \
+  __shared__ __align__(16) uint16_t name##_v0[appi::kTk * appi::kD];                      \
+  __shared__ __align__(16) uint16_t name##_v1[appi::kTk * appi::kD];                      \
+  __shared__ __align__(16) uint16_t name##_v2[(NS) > 2 ? appi::kTk * appi::kD : 8];       \
+  __shared__ int name##_last;                                                             \
+  const appi::PipeLds name = {name##_k0, name##_k1, name##_k2, name##_v0,                \
+                              name##_v1, name##_v2, &name##_last}
+
 // The work of one append worker without RoPE: 8 waves, 256 rows (tile_q tokens
 // x G heads), wave w owning rows 32 w .. 32 w + 31, against 64-key blocks.
 //
@@ -727,18 +748,19 @@ constexpr float kNoRef = -1.0e30f;
 // block j, once every wave is past it (barrier), K(j + 2) and V(j + 1) are
 // loaded into the stages of K(j) and V(j - 1); they have two steps to land.
 template <typename T, int G, bool CAUSAL, bool FASTPAGE, int NS>
-__device__ __forceinline__ void append_worker_pipe(const AttnArgs& a, int bid) {
+__device__ __forceinline__ void append_worker_pipe(const AttnArgs& a, int bid,
+                                                   const PipeLds& lds) {
   static_assert(NS == 2 || NS == 3, "two or three K/V stages");
   constexpr int NW = 8;
   constexpr int kRows = 32 * NW;
   constexpr int TQ = kRows / G;
-  __shared__ __align__(16) uint16_t ldsK0[kTk * kD];
-  __shared__ __align__(16) uint16_t ldsK1[kTk * kD];
-  __shared__ __align__(16) uint16_t ldsK2[NS > 2 ? kTk * kD : 8];
-  __shared__ __align__(16) uint16_t ldsV0[kTk * kD];
-  __shared__ __align__(16) uint16_t ldsV1[kTk * kD];
-  __shared__ __align__(16) uint16_t ldsV2[NS > 2 ? kTk * kD : 8];
-  __shared__ int s_last;
+  uint16_t* const ldsK0 = lds.k0;
+  uint16_t* const ldsK1 = lds.k1;
+  uint16_t* const ldsK2 = lds.k2;
+  uint16_t* const ldsV0 = lds.v0;
+  uint16_t* const ldsV1 = lds.v1;
+  uint16_t* const ldsV2 = lds.v2;
+  int& s_last = *lds.last;
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   using S2 = std::integral_constant<int, 2>;
@@ -1183,14 +1205,15 @@ __device__ __forceinline__ void append_worker_pipe(const AttnArgs& a, int bid) {
 }
 
 // The work of one append worker (a workgroup of append_waves<ROPE>() waves);
-// bid is the workgroup's index among the launch's append workgroups.
+// bid is the workgroup's index among the launch's append workgroups; lds is
+// the pipelined worker's LDS (the RoPE worker declares its own).
 // NS: K/V stages of the pipelined worker. Two measured faster than three
 // (716-722 against 733-736 us on the ragged causal append, same box): the
 // refills already land within the two steps they are given.
 template <typename T, int G, bool CAUSAL, bool ROPE, bool FASTPAGE, bool RIL, int NS = 2>
-__device__ __forceinline__ void append_worker(const AttnArgs& a, int bid) {
+__device__ __forceinline__ void append_worker(const AttnArgs& a, int bid, const PipeLds& lds) {
   if constexpr (ROPE) append_worker_staged<T, G, CAUSAL, true, FASTPAGE, RIL>(a, bid);
-  else append_worker_pipe<T, G, CAUSAL, FASTPAGE, NS>(a, bid);
+  else append_worker_pipe<T, G, CAUSAL, FASTPAGE, NS>(a, bid, lds);
 }
 
 }  // namespace appi

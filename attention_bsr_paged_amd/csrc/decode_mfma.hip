@@ -9,22 +9,30 @@
 // exponential per (token, row) in every lane; here both products run on the
 // matrix cores and the vector unit does only the softmax of each score once:
 //
-//   S^T = K Q^T   v_mfma_f32_16x16x32: A = 16 token rows of K straight from
-//                 global memory (lane: token l % 16, 16 bytes of the 64-byte
-//                 window of head dims 32 kc .. 32 kc + 31), B = q of the G rows
-//                 padded to 16 (rows >= G are zero). A 32-token chunk is two
-//                 16-token tiles x 4 head-dim windows = 8 products.
+//   S^T = K Q^T   v_mfma_f32_16x16x32: A = 16 token rows of K (lane: token
+//                 l % 16, 16 bytes of head dims 32 kc + 8 (l / 16) ..), B = q
+//                 of the G rows padded to 16. A 32-token chunk is two 16-token
+//                 tiles x 4 head-dim windows = 8 products. With RoPE, q and K
+//                 are rotated in fp32 and the products are fp32 ones
+//                 (v_mfma_f32_16x16x4_f32, 32 per tile).
 //   softmax       fp32, base 2, lazy rescale; a lane holds 8 scores of one row
 //                 (l % 16); the row maximum is a 4-lane-group exchange.
 //   O^T += V^T P^T  8 products (16 head dims each): B = P^T taken from the S^T
 //                 registers in the order S holds the keys; A = V^T read from
-//                 LDS with transpose reads. V goes from global memory straight
-//                 into a per-wave LDS ring (2 chunks of 32 rows, 16-byte chunks
-//                 of a row XOR-swizzled by row), so no wave waits on another.
+//                 LDS with transpose reads.
 //
-// Scope (the dispatcher falls back to decode_kernel otherwise): 16-bit or fp8
-// (e4m3, in decode_mfma_fp8_kernel below) K/V, no RoPE, power-of-two page size >= 16 (a 16-token tile never straddles a page),
-// kv head count a multiple of 4, group size 4 or 8 (rows padded to 16).
+// K, V and q go from global memory straight into per-wave LDS rings
+// (memory-to-LDS loads, 16-byte pieces of a row XOR-swizzled by row), so no
+// wave waits on another and every wait counts loads of one kind; a worker's
+// chunks stream across its segments, the next segment's first chunk loading
+// while the current segment ends. LDS: 136 or 144 KB (group 4 or 8), 154 KB
+// with RoPE at group 8; one workgroup per compute unit.
+//
+// Scope (the dispatcher falls back to decode_kernel otherwise): 16-bit K/V
+// with or without RoPE, or fp8 (e4m3, in decode_mfma_fp8_kernel below,
+// without RoPE), power-of-two page size >= 16 (a 16-token tile never
+// straddles a page), kv head count a multiple of 4, group size 4 or 8 (rows
+// padded to 16).
 #include "decode_mfma_impl.h"
 
 namespace abp {
@@ -32,8 +40,9 @@ namespace abp {
 namespace {
 
 template <typename T, int G>
-__global__ __launch_bounds__(256, 2) void decode_mfma_kernel(AttnArgs a) {
-  dmi::decode_mfma_worker<T, G>(a, blockIdx.x);
+__global__ __launch_bounds__(256, 1) void decode_mfma_kernel(AttnArgs a) {
+  ABP_DECODE_LDS(lds, G, false);
+  dmi::decode_mfma_worker<T, G, true, false, false>(a, blockIdx.x, lds);
 }
 
 template <typename T, int G>
@@ -41,10 +50,10 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_fp8_kernel(AttnArgs a) {
   dmi::decode_mfma_fp8_worker<T, G>(a, blockIdx.x);
 }
 
-// RoPE: the rotation state needs more registers, so one workgroup per CU
 template <typename T, int G, bool RIL>
 __global__ __launch_bounds__(256, 1) void decode_mfma_rope_kernel(AttnArgs a) {
-  dmi::decode_mfma_rope_worker<T, G, RIL>(a, blockIdx.x);
+  ABP_DECODE_LDS(lds, G, true);
+  dmi::decode_mfma_worker<T, G, true, true, RIL>(a, blockIdx.x, lds);
 }
 
 template <typename T>

@@ -25,16 +25,22 @@ namespace abp {
 
 namespace {
 
-// LDS: the append stages (64 KB) and a decode worker's V rings (64 KB) are
-// separate arrays, 128 KB in all, so one workgroup fits per compute unit.
+// LDS: the decode role's arrays (K and V rings of 32 KB each, q rows); the
+// append role borrows the four rings as its K and V stages (16 KB each), so
+// one workgroup fits per compute unit.
 template <typename T, int G, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void pod_kernel(AttnArgs app, AttnArgs dec) {
   static_assert(appi::append_waves<false>() == 8, "append workers are 512-thread workgroups");
+  static_assert(4 * dmi::kC * dmi::kD >= appi::kTk * appi::kD, "append stages fit the rings");
+  ABP_DECODE_LDS(dlds, G, false);
+  __shared__ int app_last;
   const int b = blockIdx.x;
   if (b < app.workers) {
-    appi::append_worker<T, G, CAUSAL, false, true, false, 2>(app, b);
+    const appi::PipeLds alds = {dlds.k0, dlds.k1, dlds.q, dlds.v0, dlds.v1, dlds.q, &app_last};
+    appi::append_worker<T, G, CAUSAL, false, true, false, 2>(app, b, alds);
   } else if (threadIdx.x < 256) {
-    dmi::decode_mfma_worker<T, G, false>(dec, b - app.workers);  // ordinary loads: few CUs
+    // ordinary loads: few CUs
+    dmi::decode_mfma_worker<T, G, false, false, false>(dec, b - app.workers, dlds);
   }
 }
 
