@@ -1071,6 +1071,7 @@ def main(argv=None) -> int:
             "parallelism": "single GPU",
         },
         "pct_of_hbm_peak": round(100 * d["step_TBps"] / HBM_PEAK_TBS, 2),
+        "clock_mhz": d["clock_mhz"],
         "plan_host_us": d["plan_host_us"],
         "roofline": {
             "bound": "hbm",
