@@ -158,6 +158,9 @@ _SIGNATURES = {
                             _i32, _vp, _sz, _vp, _sz, _vp, _podp]),
     "abp_pod_run": (_int, [_podp, _pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                            _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "abp_cascade_run": (_int, [_planp, _pp, _vp, _sz, _planp, _pp, _vp, _sz, _vp, _vp, _vp, _vp,
+                               _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                               _vp, _vp, _vp, _i32, _vp]),
     "abp_merge_state": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _int, _int, _vp]),
     "abp_merge_states": (_int, [_vp, _vp, _i32, _i64, _i32, _int, _int, _vp, _vp, _vp]),
     "abp_decode_static": (_int, [_pp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -603,8 +606,9 @@ class CascadeDecode:
 
     The prefix level runs the append kernel with every request's query as one
     row block against the shared prefix (each prefix page is read once for all
-    requests); the suffix level runs the decode kernel; ``merge_state`` joins
-    them. Both levels write fp32 states.
+    requests); the suffix level runs the decode kernel; one merge launch folds
+    both levels' states (direct or split-tile partials). Both levels write fp32
+    states.
     """
 
     def __init__(self, num_qo_heads: int, num_kv_heads: int, head_dim: int, prefix_page_size: int,
@@ -636,17 +640,29 @@ class CascadeDecode:
             prefix_last_page_len, k_pages, v_pages, kv_indptr, kv_indices, kv_last_page_len,
             q_pos=None, kv_pos_offset=None, o=None, lse=None, stream=None, bufs=None):
         """q [B, Hq, d]; prefix_qo_indptr = [0, B] on the device. RoPE: query b at
-        q_pos[b], prefix key t at t, suffix key t at kv_pos_offset[b] + t."""
+        q_pos[b], prefix key t at t, suffix key t at kv_pos_offset[b] + t. One
+        ``abp_cascade_run``: both levels' kernels, then one merge of their states."""
         torch = _torch()
+        if self.prefix.plan_struct is None or self.suffix.plan_struct is None:
+            raise RuntimeError("plan() must be called before run()")
         if bufs is None:
             bufs = self.buffers(q)
         o_p, l_p, o_s, l_s = bufs
-        self.prefix.run(q, prefix_k, prefix_v, prefix_qo_indptr, prefix_indptr, prefix_indices,
-                        prefix_last_page_len, o=o_p, lse=l_p, q_pos=q_pos, stream=stream)
-        self.suffix.run(q, k_pages, v_pages, kv_indptr, kv_indices, kv_last_page_len, o=o_s,
-                        lse=l_s, q_pos=q_pos, kv_pos_offset=kv_pos_offset, stream=stream)
-        return merge_state(o_p, l_p, o_s, l_s, out_dtype=self.dtype, o_out=o, lse_out=lse,
-                           stream=stream)
+        if o is None:
+            o = torch.empty(q.shape, dtype=self.dtype, device=q.device)
+        if lse is None:
+            lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+        _check(load_library().abp_cascade_run(
+            ctypes.byref(self.prefix.plan_struct), ctypes.byref(self.pre_params),
+            self.prefix.dev_ws.data_ptr(), self.prefix.dev_ws.numel(),
+            ctypes.byref(self.suffix.plan_struct), ctypes.byref(self.suf_params),
+            self.suffix.dev_ws.data_ptr(), self.suffix.dev_ws.numel(), _ptr(q), _ptr(prefix_k),
+            _ptr(prefix_v), _ptr(prefix_qo_indptr), _ptr(prefix_indptr), _ptr(prefix_indices),
+            _ptr(prefix_last_page_len), _ptr(k_pages), _ptr(v_pages), _ptr(kv_indptr),
+            _ptr(kv_indices), _ptr(kv_last_page_len), _ptr(q_pos), _ptr(kv_pos_offset),
+            _ptr(o_p), _ptr(l_p), _ptr(o_s), _ptr(l_s), _ptr(o), _ptr(lse),
+            _dtype_code(self.dtype), _stream(stream)))
+        return o, lse
 
     @staticmethod
     def buffers(q):

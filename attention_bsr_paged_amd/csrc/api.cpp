@@ -847,6 +847,88 @@ int abp_pod_run(const abp_pod_plan_t* plan, const abp_params* params, const void
   }
 }
 
+int abp_cascade_run(const abp_plan* prefix_plan, const abp_params* prefix_params,
+                    void* prefix_dev_ws, size_t prefix_dev_bytes, const abp_plan* suffix_plan,
+                    const abp_params* suffix_params, void* suffix_dev_ws, size_t suffix_dev_bytes,
+                    const void* q, const void* prefix_k_pages, const void* prefix_v_pages,
+                    const int32_t* prefix_qo_indptr_d, const int32_t* prefix_kv_indptr_d,
+                    const int32_t* prefix_kv_indices_d, const int32_t* prefix_kv_last_page_len_d,
+                    const void* k_pages, const void* v_pages, const int32_t* kv_indptr_d,
+                    const int32_t* kv_indices_d, const int32_t* kv_last_page_len_d,
+                    const int32_t* q_pos_d, const int32_t* kv_pos_offset_d, float* o_prefix,
+                    float* lse_prefix, float* o_suffix, float* lse_suffix, void* o, float* lse,
+                    int32_t out_dtype, abp_stream_t stream) {
+  try {
+    abp::Config cp, cs;
+    abp::Layout lp, ls;
+    int st = prepare_run(ABP_KIND_APPEND, prefix_plan, prefix_params, prefix_dev_ws,
+                         prefix_dev_bytes, &cp, &lp);
+    if (st != ABP_OK) return st;
+    st = prepare_run(ABP_KIND_DECODE, suffix_plan, suffix_params, suffix_dev_ws, suffix_dev_bytes,
+                     &cs, &ls);
+    if (st != ABP_OK) return st;
+    if (cp.out_dtype != ABP_F32 || cs.out_dtype != ABP_F32)
+      return fail(ABP_ERR_UNSUPPORTED, "cascade levels must write fp32 states (out_dtype ABP_F32)");
+    if (cp.hq != cs.hq || cp.hkv != cs.hkv || cp.qkv_dtype != cs.qkv_dtype || cp.causal)
+      return fail(ABP_ERR_PLAN_MISMATCH,
+                  "cascade levels need the same heads and q dtype, and a non-causal prefix");
+    if (out_dtype < ABP_F16 || out_dtype > ABP_F32)
+      return fail(ABP_ERR_UNSUPPORTED, "out_dtype must be ABP_F16, ABP_BF16 or ABP_F32");
+    const int32_t B = suffix_plan->batch;
+    // the prefix is one request whose query tokens are the suffix level's B
+    // queries: its tiles are (kv-head group, query tile), one head per tile
+    const int32_t tq = prefix_plan->tile_q;
+    const int64_t want_tiles = int64_t(cp.hkv) * ((B + tq - 1) / tq);
+    if (prefix_plan->batch != 1 || lp.tile_heads != 1 || prefix_plan->num_tiles != want_tiles)
+      return fail(ABP_ERR_PLAN_MISMATCH,
+                  "prefix plan must be one request with the suffix batch's queries");
+    if (B > 0 && (!q || !prefix_k_pages || !prefix_v_pages || !prefix_qo_indptr_d ||
+                  !prefix_kv_indptr_d || !prefix_kv_indices_d || !prefix_kv_last_page_len_d ||
+                  !k_pages || !v_pages || !kv_indptr_d || !kv_indices_d || !kv_last_page_len_d ||
+                  !o_prefix || !lse_prefix || !o_suffix || !lse_suffix || !o))
+      return fail(ABP_ERR_INVALID_ARG, "NULL tensor pointer");
+    if (!aligned16(q) || !aligned16(prefix_k_pages) || !aligned16(prefix_v_pages) ||
+        !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o_prefix) ||
+        !aligned16(o_suffix) || !aligned16(o))
+      return fail(ABP_ERR_INVALID_ARG, "q, pages and o buffers must be 16-byte aligned");
+    abp::AttnArgs ap = {};
+    ap.q = q;
+    ap.k_pages = prefix_k_pages;
+    ap.v_pages = prefix_v_pages;
+    ap.qo_indptr = prefix_qo_indptr_d;
+    ap.kv_indptr = prefix_kv_indptr_d;
+    ap.kv_indices = prefix_kv_indices_d;
+    ap.kv_last_page_len = prefix_kv_last_page_len_d;
+    ap.q_pos = q_pos_d;
+    ap.kv_pos_offset = nullptr;  // prefix keys sit at 0 .. prefix length - 1
+    ap.o = o_prefix;
+    ap.lse = lse_prefix;
+    fill_args(cp, lp, prefix_plan, prefix_dev_ws, &ap);
+    abp::AttnArgs as = {};
+    as.q = q;
+    as.k_pages = k_pages;
+    as.v_pages = v_pages;
+    as.kv_indptr = kv_indptr_d;
+    as.kv_indices = kv_indices_d;
+    as.kv_last_page_len = kv_last_page_len_d;
+    as.q_pos = q_pos_d;
+    as.kv_pos_offset = kv_pos_offset_d;
+    as.o = o_suffix;
+    as.lse = lse_suffix;
+    fill_args(cs, ls, suffix_plan, suffix_dev_ws, &as);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = abp::launch_append(cp, ap, s);
+    if (e != hipSuccess) return hip_fail(e, "prefix append kernel launch");
+    e = abp::launch_decode(cs, as, s);
+    if (e != hipSuccess) return hip_fail(e, "suffix decode kernel launch");
+    e = abp::launch_cascade_merge(ap, as, B, o, lse, out_dtype, s);
+    if (e != hipSuccess) return hip_fail(e, "cascade merge kernel launch");
+    return ABP_OK;
+  } catch (...) {
+    return fail(ABP_ERR_HIP, "exception");
+  }
+}
+
 int abp_merge_state(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
                     void* o_out, float* lse_out, int64_t num_rows, int32_t head_dim,
                     int in_dtype, int out_dtype, abp_stream_t stream) {

@@ -57,6 +57,10 @@ hipError_t launch_upload(void* dev_dst, const void* host_src_mapped, size_t byte
                          hipStream_t stream);
 // merges the split tiles of a plan into o / lse after its main kernel (fixed
 // grid; counts and the merge mode are read from the plan at run time)
+// Cascade: the final (o, lse) of every (request, qo head) row from the prefix
+// level's and the suffix level's states (direct fp32 outputs or partial slots)
+hipError_t launch_cascade_merge(const AttnArgs& pre, const AttnArgs& suf, int32_t batch,
+                                void* o, float* lse, int out_dtype, hipStream_t stream);
 hipError_t launch_plan_merge(const Config& cfg, const AttnArgs& a, int32_t grid,
                              hipStream_t stream);
 

@@ -182,6 +182,132 @@ __global__ __launch_bounds__(256) void plan_merge_kernel(AttnArgs a) {
   }
 }
 
+// Cascade: the final state of every output row from both levels' states in
+// one pass (paper summary "图谱动态｜学苑周刊 NO.266", section 统一的 KV 缓存存储格式:
+// a shared-prefix level and a per-request level recombined by their attention
+// states). Per level, row (b, head) has either one state in the level's output
+// (fp32; an unsplit tile, or a tile the append kernel merged itself) or the
+// partial slots of its split tile; all of them are folded with a running
+// maximum in the level order of the partial slots, prefix first. One wave per
+// row: its 4 groups of 16 lanes fold every 4th state (8 head dims per lane),
+// then combine by lane exchange.
+struct LevelRow {
+  const float* o;    // first state's row (128 floats)
+  const float* lse;  // first state's lse
+  int64_t so, sl;    // strides between states (floats)
+  int n;             // number of states
+};
+
+__device__ __forceinline__ LevelRow level_row(const AttnArgs& a, int tile, int r, int64_t orow) {
+  const ABP_CONST_AS int32_t* plan = const_as(a.plan);
+  const int np = plan[plan[H_OFF_NTILE] + tile];
+  LevelRow L;
+  if (np == 0 || plan[H_MERGE_KERNEL] == 0) {
+    L.o = static_cast<const float*>(a.o) + orow * 128;
+    L.lse = a.lse + orow;
+    L.so = 0;
+    L.sl = 0;
+    L.n = 1;
+  } else {
+    const int rows = plan[H_ROWS];
+    const int64_t first = plan[plan[H_OFF_TILE] + 4 * tile + 3];
+    L.o = a.o_part + (first * rows + r) * 128;
+    L.lse = a.lse_part + first * rows + r;
+    L.so = int64_t(rows) * 128;
+    L.sl = rows;
+    L.n = np;
+  }
+  return L;
+}
+
+template <int OUT_DT>
+__global__ __launch_bounds__(256) void cascade_merge_kernel(AttnArgs pre, AttnArgs suf, int batch,
+                                                            void* o, float* lse) {
+  const ABP_CONST_AS int32_t* pplan = const_as(pre.plan);
+  const ABP_CONST_AS int32_t* splan = const_as(suf.plan);
+  const int hq = suf.num_qo_heads;
+  const int G = splan[H_GROUP];
+  const int hkv = hq / G;
+  const int hpt_s = splan[H_TILE_HEADS], hpt_p = pplan[H_TILE_HEADS];
+  const int tq = pplan[H_TILE_Q];
+  const int nqt = (batch + tq - 1) / tq;
+  const int lane = threadIdx.x & 63;
+  const int q = lane >> 4;
+  const int e0 = (lane & 15) * 8;
+  const int total = batch * hq;
+  const int nwaves = gridDim.x * 4;
+  for (int row = blockIdx.x * 4 + (threadIdx.x >> 6); row < total; row += nwaves) {
+    const int b = row / hq, head = row - b * hq;
+    const int hk = head / G, g = head - hk * G;
+    // prefix: one request whose query tokens are the batch's queries; tiles
+    // in kv-head-group order, then query tiles. suffix: tiles in request order,
+    // then kv-head groups.
+    const LevelRow P = level_row(pre, (hk / hpt_p) * nqt + b / tq,
+                                 ((b % tq) * hpt_p + hk % hpt_p) * G + g, row);
+    const LevelRow S = level_row(suf, b * (hkv / hpt_s) + hk / hpt_s, (hk % hpt_s) * G + g, row);
+    const int n = P.n + S.n;
+    float M = kNegInf, tot = 0.f;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    for (int i0 = q; i0 < n; i0 += 16) {
+      float l[4], v[4][8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = i0 + 4 * j;
+        if (i < n) {
+          const bool pi = i < P.n;
+          const int k = pi ? i : i - P.n;
+          const LevelRow& X = pi ? P : S;
+          l[j] = X.lse[k * X.sl];
+          load8<ABP_F32>(X.o, k * X.so + e0, v[j]);
+        } else {
+          l[j] = kNegInf;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[j][e] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float nm = __builtin_fmaxf(M, l[j]);
+        const float sc = nm == M ? 1.f : fast_exp2((M - nm) * kLog2e);
+        const float wt = l[j] == kNegInf ? 0.f : fast_exp2((l[j] - nm) * kLog2e);
+        M = nm;
+        tot = __builtin_fmaf(tot, sc, wt);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(acc[e], sc, wt * v[j][e]);
+      }
+    }
+    float Mall = __builtin_fmaxf(M, __shfl_xor(M, 16));
+    Mall = __builtin_fmaxf(Mall, __shfl_xor(Mall, 32));
+    const float f = M == kNegInf ? 0.f : fast_exp2((M - Mall) * kLog2e);
+    tot *= f;
+    tot += __shfl_xor(tot, 16);
+    tot += __shfl_xor(tot, 32);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = acc[e] * f;
+      x += __shfl_xor(x, 16);
+      x += __shfl_xor(x, 32);
+      acc[e] = x;
+    }
+    if (q != 0) continue;
+    float out[8];
+    float lse_r = kNegInf;
+    if (Mall != kNegInf) {
+      const float inv = 1.f / tot;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out[e] = acc[e] * inv;
+      lse_r = Mall + fast_log2(tot) * kLn2;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out[e] = 0.f;
+    }
+    store8<OUT_DT>(o, int64_t(row) * 128 + e0, out);
+    if (lse && e0 == 0) lse[row] = lse_r;
+  }
+}
+
 template <int IN_DT>
 hipError_t merge_two_out(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
                          void* o_out, float* lse_out, int64_t rows, int out_dtype,
@@ -232,6 +358,20 @@ hipError_t launch_merge_states(const void* o_in, const float* lse_in, int32_t n,
   if (in_dtype == ABP_BF16)
     return merge_states_out<ABP_BF16>(o_in, lse_in, n, rows, out_dtype, o_out, lse_out, s);
   return merge_states_out<ABP_F16>(o_in, lse_in, n, rows, out_dtype, o_out, lse_out, s);
+}
+
+hipError_t launch_cascade_merge(const AttnArgs& pre, const AttnArgs& suf, int32_t batch,
+                                void* o, float* lse, int out_dtype, hipStream_t s) {
+  const int64_t rows = int64_t(batch) * suf.num_qo_heads;
+  if (rows == 0) return hipSuccess;
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  if (out_dtype == ABP_F32)
+    cascade_merge_kernel<ABP_F32><<<grid, 256, 0, s>>>(pre, suf, batch, o, lse);
+  else if (out_dtype == ABP_BF16)
+    cascade_merge_kernel<ABP_BF16><<<grid, 256, 0, s>>>(pre, suf, batch, o, lse);
+  else
+    cascade_merge_kernel<ABP_F16><<<grid, 256, 0, s>>>(pre, suf, batch, o, lse);
+  return hipGetLastError();
 }
 
 hipError_t launch_plan_merge(const Config& cfg, const AttnArgs& a, int32_t grid, hipStream_t s) {

@@ -504,7 +504,7 @@ def bench_cascade(abp, wl, torch, dev, K, Wm, workers=0) -> dict:
         "prefix_tokens": int(pre.kv_len.sum()),
         "suffix_tokens": int(kv.kv_len.sum()),
         "rope_theta": w.rope_theta,
-        "launches": "prefix append (RoPE) + suffix decode (RoPE) + its merge + merge_state",
+        "launches": "prefix append (RoPE) + suffix decode (RoPE) + one merge of both levels' states",
         "kv_pool_copies": copies,
     }
 

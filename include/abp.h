@@ -381,6 +381,41 @@ int abp_pod_run(const abp_pod_plan_t* plan, const abp_params* params, const void
                 void* o_append, float* lse_append, void* dev_ws, size_t dev_bytes,
                 abp_stream_t stream);
 
+/* Cascade decode in one call: a shared prefix level and a per-request suffix
+ * level whose attention states are recombined (paper summary "图谱动态｜学苑周刊
+ * NO.266", section 统一的 KV 缓存存储格式, composable formats). Runs the
+ * prefix append kernel (non-causal, one request whose query tokens are the B
+ * decode queries, its own page pool and table), the suffix decode kernel (B
+ * requests, their own pool and table), then one merge launch that folds, for
+ * every (request, qo head) row, the prefix level's state and the suffix
+ * level's state, each read either from the level's fp32 output (an unsplit
+ * tile) or from the level's partial slots (a split tile), so neither level
+ * runs its own plan merge. Equals merge_state(prefix run, suffix run).
+ *
+ * Plans: prefix_plan from abp_append_plan with qo_indptr = [0, B] and
+ * causal 0; suffix_plan from abp_decode_plan over the B suffixes; both params
+ * with out_dtype ABP_F32 (the level states) and the same heads and q dtype
+ * (ABP_ERR_PLAN_MISMATCH / ABP_ERR_UNSUPPORTED otherwise). Each plan keeps
+ * its own device workspace. q [B, Hq, d] is both levels' query; RoPE (when
+ * the params enable it): query b at q_pos_d[b] (NULL: each level's default),
+ * prefix key t at t, suffix key t at kv_pos_offset_d[b] + t. o_prefix /
+ * o_suffix [B, Hq, d] and lse_prefix / lse_suffix [B, Hq] are fp32 scratch
+ * for the levels' direct states (caller-owned, contents undefined after the
+ * call); o [B, Hq, d] in out_dtype and lse [B, Hq] (may be NULL) receive the
+ * result. No allocation; graph-capturable under the same conditions as the
+ * two runs. */
+int abp_cascade_run(const abp_plan* prefix_plan, const abp_params* prefix_params,
+                    void* prefix_dev_ws, size_t prefix_dev_bytes, const abp_plan* suffix_plan,
+                    const abp_params* suffix_params, void* suffix_dev_ws, size_t suffix_dev_bytes,
+                    const void* q, const void* prefix_k_pages, const void* prefix_v_pages,
+                    const int32_t* prefix_qo_indptr_d, const int32_t* prefix_kv_indptr_d,
+                    const int32_t* prefix_kv_indices_d, const int32_t* prefix_kv_last_page_len_d,
+                    const void* k_pages, const void* v_pages, const int32_t* kv_indptr_d,
+                    const int32_t* kv_indices_d, const int32_t* kv_last_page_len_d,
+                    const int32_t* q_pos_d, const int32_t* kv_pos_offset_d, float* o_prefix,
+                    float* lse_prefix, float* o_suffix, float* lse_suffix, void* o, float* lse,
+                    int32_t out_dtype, abp_stream_t stream);
+
 /* Merge two attention states over disjoint key sets (cascade: prefix and suffix).
  * o_a, o_b [num_rows, head_dim] in in_dtype; lse_a, lse_b [num_rows] float32;
  * writes o_out [num_rows, head_dim] in out_dtype and lse_out (may be NULL).

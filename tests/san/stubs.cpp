@@ -24,6 +24,10 @@ hipError_t launch_upload(void*, const void*, size_t, hipStream_t) { return hipEr
 hipError_t launch_plan_merge(const Config&, const AttnArgs&, int32_t, hipStream_t) {
   return hipErrorNotSupported;
 }
+hipError_t launch_cascade_merge(const AttnArgs&, const AttnArgs&, int32_t, void*, float*, int,
+                                hipStream_t) {
+  return hipErrorNotSupported;
+}
 hipError_t launch_page_append(const void*, const void*, const int32_t*, void*, void*,
                               const int32_t*, const int32_t*, const int32_t*, int32_t, int64_t,
                               int32_t, int32_t, hipStream_t) {

@@ -462,3 +462,49 @@ def test_pages_of_2gib_or_more_are_refused(lib):
     assert lib.abp_workspace_size(0, ctypes.byref(big), 4, 0, 16, ctypes.byref(hb),
                                   ctypes.byref(db)) == abp.ABP_ERR_UNSUPPORTED
     assert "2 GiB" in abp.abp_last_error()
+
+
+def test_cascade_run_checks_its_plans(lib):
+    """abp_cascade_run refuses, on the host and before any launch, a prefix
+    plan whose query tiles do not cover the suffix batch, a causal prefix,
+    level params that do not write fp32 states, swapped plans and a bad output
+    dtype (the prefix's exact query count is the caller's contract: the plan
+    does not hold it)."""
+    B = 6
+    pre_p = P(page_size=256, out_dtype="fp32")
+    suf_p = P(out_dtype="fp32")
+    pws = _ws(abp.ABP_KIND_APPEND, pre_p, 1, B, 8)
+    pre = abp.abp_plan_host(abp.ABP_KIND_APPEND, pre_p, 1, [0, B], [0, 2], [256], 1, B, 8, pws)
+    sws = _ws(abp.ABP_KIND_DECODE, suf_p, B, 0, 8)
+    indptr = np.arange(B + 1, dtype=np.int32) * 3
+    suf = abp.abp_plan_host(abp.ABP_KIND_DECODE, suf_p, B, None, indptr, np.full(B, 5, np.int32),
+                            B, 0, 8, sws)
+    fake_ws, big = 1 << 20, 1 << 40   # never dereferenced: every case fails before a launch
+
+    def run(pp, pre_params, sp, suf_params, out=abp.ABP_BF16):
+        return lib.abp_cascade_run(ctypes.byref(pp), ctypes.byref(pre_params), fake_ws, big,
+                                   ctypes.byref(sp), ctypes.byref(suf_params), fake_ws, big,
+                                   *([None] * 20), out, None)
+
+    assert run(pre, pre_p, suf, P()) == abp.ABP_ERR_PLAN_MISMATCH  # params differ from the plan
+    bf_p = P(out_dtype="bf16")
+    sws2 = _ws(abp.ABP_KIND_DECODE, bf_p, B, 0, 8)
+    suf_bf = abp.abp_plan_host(abp.ABP_KIND_DECODE, bf_p, B, None, indptr,
+                               np.full(B, 5, np.int32), B, 0, 8, sws2)
+    assert run(pre, pre_p, suf_bf, bf_p) == abp.ABP_ERR_UNSUPPORTED  # level states must be fp32
+    # a prefix over fewer query tiles than the suffix batch needs (64 queries per tile)
+    B2 = 70
+    indptr2 = np.arange(B2 + 1, dtype=np.int32) * 3
+    sws3 = _ws(abp.ABP_KIND_DECODE, suf_p, B2, 0, 8)
+    suf2 = abp.abp_plan_host(abp.ABP_KIND_DECODE, suf_p, B2, None, indptr2,
+                             np.full(B2, 5, np.int32), B2, 0, 8, sws3)
+    assert run(pre, pre_p, suf2, suf_p) == abp.ABP_ERR_PLAN_MISMATCH
+    # a well-formed pair gets past the plan checks to the tensor checks
+    assert run(pre, pre_p, suf, suf_p) == abp.ABP_ERR_INVALID_ARG
+    causal_p = P(page_size=256, out_dtype="fp32", causal=True)
+    cws = _ws(abp.ABP_KIND_APPEND, causal_p, 1, B, 8)
+    cpre = abp.abp_plan_host(abp.ABP_KIND_APPEND, causal_p, 1, [0, B], [0, 2], [256], 1, B, 8,
+                             cws)
+    assert run(cpre, causal_p, suf, suf_p) == abp.ABP_ERR_PLAN_MISMATCH
+    assert run(suf, suf_p, pre, pre_p) == abp.ABP_ERR_PLAN_MISMATCH  # swapped kinds
+    assert run(pre, pre_p, suf, suf_p, out=abp.ABP_F32 + 7) == abp.ABP_ERR_UNSUPPORTED
