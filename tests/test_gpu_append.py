@@ -260,3 +260,43 @@ def test_cascade_rope_full():
     o_ref, l_ref = ora.decode_workload(w)
     assert_parity(o, l, o_ref, l_ref, "bf16", what="cascade rope, all requests")
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
+
+
+def cascade_case(seed, B, hkv, G, theta, dtype="bf16", pre_len=900, zero_suffix=True):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    prefix = wl.make_paged_kv(rng, np.array([pre_len]), 256, hkv, 128, dtype, extra_pages=1)
+    suf = rng.integers(1, 200, size=B)
+    if zero_suffix:
+        suf[B // 3] = 0
+    kv = wl.make_paged_kv(rng, suf, 16, hkv, 128, dtype, extra_pages=3)
+    q = wl.normal_bits(rng, (B, hkv * G, 128), dtype)
+    w = wl.Workload("cascade_case", "cascade", seed, dtype, hkv * G, hkv, 128, kv, q,
+                    rope_theta=theta, prefix=prefix)
+    if theta:
+        w.kv_pos_offset = np.full(B, pre_len, np.int32)
+        w.q_pos = (pre_len + np.maximum(suf, 1) - 1).astype(np.int32)
+    return w
+
+
+@pytest.mark.parametrize("theta", [0.0, 500000.0])
+@pytest.mark.parametrize("pw,sw", [(1, 1), (3, 7), (0, 0), (40, 300)])
+def test_cascade_single_call_shapes(theta, pw, sw):
+    """abp_cascade_run over query tiles that do not divide the batch (100
+    queries: 64-query tiles without RoPE, 32 with), 8 kv heads (4-head decode
+    tiles on the matrix cores), a suffix of length 0, and worker counts that
+    leave the prefix tiles unsplit (1), merged inside the append kernel (3),
+    or split over many partials (default, 40), and the suffix tiles unsplit,
+    split a few ways or many."""
+    w = cascade_case(700 + pw + sw, 100, 8, 4, theta)
+    say(f"[case] cascade B=100 hkv=8 G=4 theta={theta} prefix W{pw} suffix W{sw}")
+    o_ref, l_ref = ora.decode_workload(w)
+    o, l = run_cascade(w, num_workers=sw, prefix_workers=pw)
+    assert_parity(o, l, o_ref, l_ref, "bf16", what=f"cascade theta={theta} W{pw}/{sw}")
+
+
+def test_cascade_single_call_group8_fp16():
+    """G = 8 (64 qo heads over 8 kv heads), fp16, RoPE."""
+    w = cascade_case(760, 37, 8, 8, 500000.0, dtype="fp16")
+    o_ref, l_ref = ora.decode_workload(w)
+    o, l = run_cascade(w, num_workers=11, prefix_workers=6)
+    assert_parity(o, l, o_ref, l_ref, "fp16", what="cascade G8 fp16")
