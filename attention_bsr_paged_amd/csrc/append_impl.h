@@ -135,37 +135,47 @@ __device__ __forceinline__ float max_over_groups(float x) {
   return __builtin_fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
 }
 
-// Waves per workgroup: 8 (256 rows, waves 0-3 stage K and 4-7 stage V), or 4
-// for RoPE (128 rows, every wave stages both; hi/lo operands need 512 regs).
-// One workgroup per CU either way.
+// Waves per workgroup: 8 for the pipelined worker (256 rows), 4 for the RoPE
+// worker (128 rows: the hi/lo operands need a wave's 512 registers). One
+// workgroup per CU either way.
 template <bool ROPE>
 constexpr int append_waves() {
   return ROPE ? 4 : 8;
 }
 
-// The append worker with RoPE (4 waves, 128 rows): K is staged through
-// registers, rotated and split into hi/lo parts before the LDS store.
-template <typename T, int G, bool CAUSAL, bool ROPE, bool FASTPAGE, bool RIL>
-__device__ __forceinline__ void append_worker_staged(const AttnArgs& a, int bid) {
-  static_assert(ROPE || !RIL, "interleaving is a RoPE layout");
+// The append worker with RoPE: 4 waves, 128 rows (tile_q tokens x G heads),
+// wave w owning rows 32 w .. 32 w + 31, against 64-key blocks.
+//
+// K must be rotated by its position before the score products, so it comes
+// into registers, is rotated there and is split into hi and lo 16-bit parts
+// (S = Kh Qh + Kh Ql + Kl Qh keeps fp32-level accuracy); V is transposed on
+// the way to LDS. Every thread stages 4 K rows and 4 V rows of each block.
+//
+// Staging runs one block ahead of the products and its loads two blocks
+// ahead: while block j's products read LDS stage j & 1, block j + 1's
+// rotation (registers loaded during block j - 1) is interleaved with them and
+// stored into stage (j + 1) & 1, and block j + 2's loads are issued into the
+// registers block j came in. One barrier per block: it ends block j's reads of
+// stage j & 1 and publishes stage (j + 1) & 1. The rotation is vector work and
+// the score products matrix work, so with one wave per SIMD they overlap only
+// inside one wave's instruction stream: the score products of each 16-key
+// group are written beside the rotation of one K row and a quarter of the V
+// transposition, fenced from the next group.
+template <typename T, int G, bool CAUSAL, bool FASTPAGE, bool RIL>
+__device__ __forceinline__ void append_worker_rope(const AttnArgs& a, int bid) {
   // K elements a staging thread reads per row: rotate-half RoPE takes 4 + 4
-  // (both halves of its 4 pairs), everything else 8 consecutive ones
-  constexpr int kKPiece = (ROPE && !RIL) ? 4 : 8;
-  constexpr int NW = append_waves<ROPE>();
-  constexpr int kRows = 32 * NW;
+  // (both halves of its 4 pairs), interleaved RoPE 8 consecutive ones
+  constexpr int kKPiece = RIL ? 8 : 4;
+  constexpr int kRows = 32 * append_waves<true>();
   constexpr int TQ = kRows / G;
-  // Two stages: block j is read from stage j & 1 while block j + 1 is stored
-  // into the other. Without RoPE a stage is K [64][128] and V [64][128] as in
-  // memory (rows of 256 bytes whose 16-byte chunks are XOR-swizzled by row),
-  // loaded straight from global memory into LDS; with RoPE it is the rotated
-  // K as hi and lo parts and V^T, padded, written from registers.
-  constexpr int kKElems = ROPE ? kTk * kKStride : kTk * kD;
-  constexpr int kKloElems = ROPE ? kTk * kKStride : 0;
-  constexpr int kVElems = ROPE ? kD * kVStride : kTk * kD;
-  // one array per stage, each named at compile time where used, so the
-  // compiler sees that loads into one stage never alias reads of the other
-  __shared__ __align__(16) uint16_t ldsK0[kKElems + kKloElems];
-  __shared__ __align__(16) uint16_t ldsK1[kKElems + kKloElems];
+  // a stage: rotated K as hi and lo parts [64][kKStride] each, then V^T
+  // [128][kVStride]; one array per stage, each named at compile time where
+  // used, so the compiler sees that stores into one stage never alias reads
+  // of the other
+  constexpr int kKElems = kTk * kKStride;
+  constexpr int kVElems = kD * kVStride;
+  __shared__ __align__(16) uint16_t ldsK0[2 * kKElems];
+  __shared__ __align__(16) uint16_t ldsK1[2 * kKElems];
   __shared__ __align__(16) uint16_t ldsV0[kVElems];
   __shared__ __align__(16) uint16_t ldsV1[kVElems];
   __shared__ int s_last;
@@ -175,7 +185,6 @@ __device__ __forceinline__ void append_worker_staged(const AttnArgs& a, int bid)
     if constexpr (decltype(st)::value == 0) return ldsK0;
     else return ldsK1;
   };
-  auto sKlo_of = [&](auto st) { return sK_of(st) + kKElems; };
   auto sV_of = [&](auto st) -> uint16_t* {
     if constexpr (decltype(st)::value == 0) return ldsV0;
     else return ldsV1;
@@ -186,7 +195,6 @@ __device__ __forceinline__ void append_worker_staged(const AttnArgs& a, int bid)
   const ABP_CONST_AS int32_t* segs = plan + plan[H_OFF_SEG];
   const ABP_CONST_AS int32_t* tiles = plan + plan[H_OFF_TILE];
   const ABP_CONST_AS float* rope = (const ABP_CONST_AS float*)(plan + plan[H_OFF_ROPE]);
-  const ABP_CONST_AS int32_t* kv_indptr = const_as(a.kv_indptr);
   const ABP_CONST_AS int32_t* kv_indices = const_as(a.kv_indices);
   const ABP_CONST_AS int32_t* qo_indptr = const_as(a.qo_indptr);
 
@@ -208,31 +216,31 @@ __device__ __forceinline__ void append_worker_staged(const AttnArgs& a, int bid)
   const uint16_t* __restrict__ vp = static_cast<const uint16_t*>(a.v_pages);
 
   const float thr = kRescaleLog2 / cl2;  // lazy rescale threshold, raw score units
-  // staging (256 threads per operand): K rows k_row + 16 i (i = 16-key group),
-  // 16-byte chunk kc_chunk; V keys 16 vw + 4 v_kg + i (16-key group vw), chunk
-  // v_chunk. With 8 waves, waves 0-3 stage K and waves 4-7 stage V.
-  const int kc_chunk = tid & 15;
-  // RoPE: a thread stages both elements of the rotary pairs j = 4 kc_chunk + e
+  // staging: K rows k_row + 16 i (i = 16-key group), 16-byte chunk kc_chunk;
+  // V keys 16 wave + 4 v_kg + i, chunk v_chunk.
+  // A thread stages both elements of the rotary pairs j = 4 kc_chunk + e
   // (e < 4) of its K rows (rotate-half: elements j and j + 64; interleaved:
-  // 2j and 2j + 1, its plain 8 elements), so each angle is computed once. Its rows are 16
-  // keys apart: the first row's angles are evaluated and the next follow by
-  // angle addition with the rotation by 16 positions (c16, s16).
-  float kfhi[ROPE ? 4 : 1], kflo[ROPE ? 4 : 1], c16[ROPE ? 4 : 1], s16[ROPE ? 4 : 1];
-  if constexpr (ROPE) {
+  // 2j and 2j + 1, its plain 8 elements), so each angle is computed once. Its
+  // rows are 16 keys apart: the first row's angles are evaluated and the next
+  // follow by angle addition with the rotation by 16 positions (c16, s16).
+  const int kc_chunk = tid & 15;
+  float kfhi[4], kflo[4], c16[4], s16[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int j = 4 * kc_chunk + e;
-      kfhi[e] = rope[2 * j];
-      kflo[e] = rope[2 * j + 1];
-      rope_sincos(16.f, kfhi[e], kflo[e], &s16[e], &c16[e]);
-    }
+  for (int e = 0; e < 4; ++e) {
+    const int j = 4 * kc_chunk + e;
+    kfhi[e] = rope[2 * j];
+    kflo[e] = rope[2 * j + 1];
+    rope_sincos(16.f, kfhi[e], kflo[e], &s16[e], &c16[e]);
   }
-  const int k_row = (tid & 255) >> 4;
+  const int k_row = tid >> 4;
   const int v_kg = lane & 3;
   const int v_chunk = lane >> 2;
-  const int vw = wave & 3;
-  const bool stage_k = NW == 4 || wave < 4;
-  const bool stage_v = NW == 4 || wave >= 4;
+
+  // registers of one staged block
+  struct Regs {
+    uint4 k[4], v[4];
+  };
+  Regs R0, R1;
 
   for (int s = s_begin; s < s_end; ++s) {
     const int tile = segs[4 * s];
@@ -240,18 +248,175 @@ __device__ __forceinline__ void append_worker_staged(const AttnArgs& a, int bid)
     const int b = tiles[4 * tile], h = tiles[4 * tile + 1], qt = tiles[4 * tile + 2];
     const int q0 = qo_indptr[b];
     const int qo_len = qo_indptr[b + 1] - q0;
-    const int ip0 = kv_indptr[b];
-    const int npg = kv_indptr[b + 1] - ip0;
+    const int ip0 = a.kv_indptr[b];
+    const int npg = a.kv_indptr[b + 1] - ip0;
     const int kv_len = npg > 0 ? (npg - 1) * P + a.kv_last_page_len[b] : 0;
-    const int kv_pos0 = (ROPE && a.kv_pos_offset) ? a.kv_pos_offset[b] : 0;
-    // elements; with RoPE the first piece of the lane's pairs (see above)
+    const int kv_pos0 = a.kv_pos_offset ? a.kv_pos_offset[b] : 0;
+    // elements; the first piece of the lane's pairs (see above)
     const int koff_lane = k_row * tstride + h * kD + kc_chunk * kKPiece;
 
-    // ---- Q fragments (B operand of S^T = K Q^T) for this wave's 32 rows
-    uint4 qf[2][4];
-    uint4 qfl[ROPE ? 2 : 1][4];  // RoPE: low parts of the rotated q
+    // ---- staging: global -> registers. Any kb is in bounds: groups past
+    // the segment end re-read its last valid rows (masked, or never read).
+    auto kload = [&](const uint16_t* p) -> uint4 {
+      if constexpr (!RIL) {
+        const uint2 lo = *reinterpret_cast<const uint2*>(p);
+        const uint2 hi = *reinterpret_cast<const uint2*>(p + 64);
+        return make_uint4(lo.x, lo.y, hi.x, hi.y);
+      } else {
+        return *reinterpret_cast<const uint4*>(p);
+      }
+    };
+    auto gload = [&](int kb, Regs& R) __attribute__((always_inline)) {
+      if constexpr (FASTPAGE) {
+        // one page id per 16-key group, on the scalar unit
+        // (the page ids are read first, so their scalar loads overlap)
+        const int last16 = (kv_end - 1) & ~15;
+        int kk[4], pid[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          kk[i] = min(kb + 16 * i, last16);
+          pid[i] = kv_indices[ip0 + (kk[i] >> shift)];
+        }
+        const int kkv = min(kb + 16 * wave, last16);  // wave-uniform
+        const int pidv = kv_indices[ip0 + (kkv >> shift)];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t base = (int64_t)pid[i] * a.page_stride + (int64_t)(kk[i] & (P - 1)) * tstride;
+          R.k[i] = kload(kp + base + koff_lane);
+        }
+        const int64_t vb = (int64_t)pidv * a.page_stride + (int64_t)(kkv & (P - 1)) * tstride;
+        // a key at or past kv_end takes the last key's values: slots past a
+        // request's last token may hold NaN / inf bits, which p = 0 does not
+        // cancel in P.V (K rows there only reach masked scores)
+        const int rmax = kv_end - 1 - kkv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          R.v[i] = *reinterpret_cast<const uint4*>(vp + vb + min(4 * v_kg + i, rmax) * tstride +
+                                                   h * kD + v_chunk * 8);
+      } else {
+        auto row_of = [&](int key) -> int64_t {
+          int page, off;
+          if (shift >= 0) {
+            page = key >> shift;
+            off = key & (P - 1);
+          } else {
+            page = key / P;
+            off = key - page * P;
+          }
+          return (int64_t)a.kv_indices[ip0 + page] * a.page_stride + (int64_t)off * tstride;
+        };
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = min(kb + k_row + 16 * i, kv_end - 1);
+          R.k[i] = kload(kp + row_of(key) + h * kD + kc_chunk * kKPiece);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = min(kb + 16 * wave + 4 * v_kg + i, kv_end - 1);
+          R.v[i] = *reinterpret_cast<const uint4*>(vp + row_of(key) + h * kD + v_chunk * 8);
+        }
+      }
+    };
+    // ---- staging: registers -> LDS, in 4 parts (part i: K row k_row + 16 i,
+    // rotated and split, and V^T dims v_chunk * 8 + 2 i, + 1 of the thread's
+    // 4 keys), each cut into small pieces that the score products are
+    // interleaved with: st_begin sets up the angles of K row k_row, st_step
+    // moves them on by 16 positions, st_rot rotates one pair, st_split splits
+    // one word of the rotated row into hi and lo parts, st_store_k / st_store_v
+    // store the part
+    float cs[4], sn[4];
+    float kr[8];
+    uint32_t hw[4], lw[4];
+    auto st_begin = [&](int kb) __attribute__((always_inline)) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        rope_sincos((float)(kv_pos0 + kb + k_row), kfhi[e], kflo[e], &sn[e], &cs[e]);
+    };
+    auto st_step = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float cn = __builtin_fmaf(-sn[e], s16[e], cs[e] * c16[e]);
+        sn[e] = __builtin_fmaf(cs[e], s16[e], sn[e] * c16[e]);
+        cs[e] = cn;
+      }
+    };
+    // pair e of K row part i: rotate-half holds elements 4c + e (words 0-1)
+    // and 64 + 4c + e (words 2-3), giving kr[e] and kr[4 + e]; interleaved
+    // holds the pair in word e, giving kr[2e] and kr[2e + 1]
+    auto st_rot = [&](const Regs& R, int i, int e) __attribute__((always_inline)) {
+      const uint4& u = R.k[i];
+      if constexpr (RIL) {
+        const float x = lo_f32<T>(word(u, e)), y = hi_f32<T>(word(u, e));
+        kr[2 * e] = __builtin_fmaf(-y, sn[e], x * cs[e]);
+        kr[2 * e + 1] = __builtin_fmaf(x, sn[e], y * cs[e]);
+      } else {
+        const uint32_t wl = (e < 2) ? u.x : u.y;
+        const uint32_t wh = (e < 2) ? u.z : u.w;
+        const float x = (e & 1) ? hi_f32<T>(wl) : lo_f32<T>(wl);
+        const float y = (e & 1) ? hi_f32<T>(wh) : lo_f32<T>(wh);
+        kr[e] = __builtin_fmaf(-y, sn[e], x * cs[e]);
+        kr[4 + e] = __builtin_fmaf(x, sn[e], y * cs[e]);
+      }
+    };
+    auto st_split = [&](int w) __attribute__((always_inline)) {
+      hw[w] = pack2<T>(kr[2 * w], kr[2 * w + 1]);
+      lw[w] = pack2<T>(kr[2 * w] - lo_f32<T>(hw[w]), kr[2 * w + 1] - hi_f32<T>(hw[w]));
+    };
+    auto st_store_k = [&](int i, auto stage) __attribute__((always_inline)) {
+      uint16_t* sK = sK_of(stage);
+      uint16_t* sKlo = sK + kKElems;
+      if constexpr (RIL) {
+        // 8 consecutive elements, stored in place as one 16-byte piece
+        const int at = (k_row + 16 * i) * kKStride + kc_chunk * 8;
+        *reinterpret_cast<uint4*>(&sK[at]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        *reinterpret_cast<uint4*>(&sKlo[at]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+      } else {
+        const int at = (k_row + 16 * i) * kKStride + kc_chunk * 4;
+        *reinterpret_cast<uint2*>(&sK[at]) = make_uint2(hw[0], hw[1]);
+        *reinterpret_cast<uint2*>(&sK[at + 64]) = make_uint2(hw[2], hw[3]);
+        *reinterpret_cast<uint2*>(&sKlo[at]) = make_uint2(lw[0], lw[1]);
+        *reinterpret_cast<uint2*>(&sKlo[at + 64]) = make_uint2(lw[2], lw[3]);
+      }
+    };
+    auto st_store_v = [&](const Regs& R, int i, auto stage) __attribute__((always_inline)) {
+      // V^T: element d of the 4 keys 16 wave + 4 v_kg + 0..3 as one 8-byte piece
+      uint16_t* V = sV_of(stage) + 16 * wave + 4 * v_kg;
+      const uint32_t w0 = word(R.v[0], i), w1 = word(R.v[1], i);
+      const uint32_t w2 = word(R.v[2], i), w3 = word(R.v[3], i);
+      const int d = v_chunk * 8 + 2 * i;
+      *reinterpret_cast<uint2*>(&V[d * kVStride]) = make_uint2(pair_lo(w0, w1), pair_lo(w2, w3));
+      *reinterpret_cast<uint2*>(&V[(d + 1) * kVStride]) =
+          make_uint2(pair_hi(w0, w1), pair_hi(w2, w3));
+    };
+    // piece p (0..11) of staging part i
+    auto st_piece = [&](const Regs& R, int i, int p, auto stage) __attribute__((always_inline)) {
+      if (p == 0) {
+        if (i > 0) st_step();
+      } else if (p <= 4) {
+        st_rot(R, i, p - 1);
+      } else if (p <= 8) {
+        st_split(p - 5);
+      } else if (p == 9) {
+        st_store_k(i, stage);
+      } else if (p == 10) {
+        st_store_v(R, i, stage);
+      }
+    };
+    auto st_part = [&](const Regs& R, int i, auto stage) __attribute__((always_inline)) {
+#pragma unroll
+      for (int p = 0; p < 11; ++p) st_piece(R, i, p, stage);
+    };
+
+    const int nblk = kv_end > kv_begin ? (kv_end - kv_begin + kTk - 1) / kTk : 0;
+
+    // ---- Q fragments (B operand of S^T = K Q^T) for this wave's 32 rows,
+    // rotated and split into hi (qf) and lo (qfl) parts. The q loads go out
+    // first and the first two blocks' K/V loads next, so that the q rotation
+    // waits for q alone and the blocks' latency overlaps it.
+    uint4 qf[2][4], qfl[2][4];
     int lim[2];
     int tloc_r[2];
+    float qpos[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const int r = wave * 32 + nb * 16 + l16;
@@ -263,22 +428,23 @@ __device__ __forceinline__ void append_worker_staged(const AttnArgs& a, int bid)
                              ((int64_t)(q0 + tl) * a.num_qo_heads + h * G + (r % G)) * kD + g16 * 8;
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc) qf[nb][kc] = *reinterpret_cast<const uint4*>(qptr + kc * 32);
-      if constexpr (ROPE) {
-        const float qpos = a.q_pos ? (float)a.q_pos[q0 + tl] : (float)lim[nb];
-        if constexpr (RIL) {
-          // chunk kc holds elements g16 * 8 + 32 kc .. + 7: pairs 4 g16 + 16 kc ..
+      qpos[nb] = a.q_pos ? (float)a.q_pos[q0 + tl] : (float)lim[nb];
+    }
+    if (nblk > 0) {
+      gload(kv_begin, R0);
+      gload(kv_begin + kTk, R1);
+    }
 #pragma unroll
-          for (int kc = 0; kc < 4; ++kc)
-            rope_adjacent8<T>(qf[nb][kc], qfl[nb][kc], qpos, 4 * g16 + 16 * kc, rope);
-        } else {
-          rope_pair<T>(qf[nb][0], qf[nb][2], qfl[nb][0], qfl[nb][2], qpos, g16 * 8, rope);
-          rope_pair<T>(qf[nb][1], qf[nb][3], qfl[nb][1], qfl[nb][3], qpos, 32 + g16 * 8, rope);
-        }
+    for (int nb = 0; nb < 2; ++nb) {
+      if constexpr (RIL) {
+        // chunk kc holds elements g16 * 8 + 32 kc .. + 7: pairs 4 g16 + 16 kc ..
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc)
+          rope_adjacent8<T>(qf[nb][kc], qfl[nb][kc], qpos[nb], 4 * g16 + 16 * kc, rope);
+      } else {
+        rope_pair<T>(qf[nb][0], qf[nb][2], qfl[nb][0], qfl[nb][2], qpos[nb], g16 * 8, rope);
+        rope_pair<T>(qf[nb][1], qf[nb][3], qfl[nb][1], qfl[nb][3], qpos[nb], 32 + g16 * 8, rope);
       }
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc)
-        asm volatile("" : "+v"(qf[nb][kc].x), "+v"(qf[nb][kc].y), "+v"(qf[nb][kc].z),
-                     "+v"(qf[nb][kc].w));
     }
     // first row of the tile sees the fewest keys
     const int tile_min_lim = kv_len - qo_len + qt * TQ;
@@ -291,253 +457,77 @@ __device__ __forceinline__ void append_worker_staged(const AttnArgs& a, int bid)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) O[md][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // ---- staging: global -> registers (block kb) and registers -> LDS
-    // with 8 waves a wave stages either K or V, so V reuses the K registers
-    uint4 kreg[4], vreg[NW == 4 ? 4 : 1];
-    auto vr = [&](int i) -> uint4& {
-      if constexpr (NW == 4) return vreg[i];
-      else return kreg[i];
-    };
-    auto kload = [&](const uint16_t* p) -> uint4 {
-      if constexpr (ROPE && !RIL) {
-        const uint2 lo = *reinterpret_cast<const uint2*>(p);
-        const uint2 hi = *reinterpret_cast<const uint2*>(p + 64);
-        return make_uint4(lo.x, lo.y, hi.x, hi.y);
-      } else {
-        return *reinterpret_cast<const uint4*>(p);
-      }
-    };
-    auto gload = [&](int kb) {
-      if constexpr (FASTPAGE) {
-        // one page id per 16-key group, on the scalar unit; groups past the
-        // segment end re-read the last valid group (in bounds, masked)
-        const int last16 = (kv_end - 1) & ~15;
-        if (stage_k) {
+    if (nblk > 0) {
+      st_begin(kv_begin);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int kk = min(kb + 16 * i, last16);
-            const int64_t base = (int64_t)kv_indices[ip0 + (kk >> shift)] * a.page_stride +
-                                 (int64_t)(kk & (P - 1)) * tstride;
-            kreg[i] = kload(kp + base + koff_lane);
-          }
-        }
-        if (stage_v) {
-          const int kk = min(kb + 16 * vw, last16);  // wave-uniform
-          const int64_t vb = (int64_t)kv_indices[ip0 + (kk >> shift)] * a.page_stride +
-                             (int64_t)(kk & (P - 1)) * tstride;
-          // a key at or past kv_end takes the last key's values: slots past a
-          // request's last token may hold NaN / inf bits, which p = 0 does not
-          // cancel in P.V (K rows there only reach masked scores)
-          const int rmax = kv_end - 1 - kk;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            vr(i) = *reinterpret_cast<const uint4*>(vp + vb + min(4 * v_kg + i, rmax) * tstride +
-                                                    h * kD + v_chunk * 8);
-        }
-      } else {
-        if (stage_k) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = min(kb + k_row + 16 * i, kv_end - 1);
-            int page, off;
-            if (shift >= 0) {
-              page = key >> shift;
-              off = key & (P - 1);
-            } else {
-              page = key / P;
-              off = key - page * P;
-            }
-            const int64_t pg = a.kv_indices[ip0 + page];
-            kreg[i] = kload(kp + pg * a.page_stride + (int64_t)off * tstride + h * kD +
-                            kc_chunk * kKPiece);
-          }
-        }
-        if (stage_v) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = min(kb + 16 * vw + 4 * v_kg + i, kv_end - 1);
-            int page, off;
-            if (shift >= 0) {
-              page = key >> shift;
-              off = key & (P - 1);
-            } else {
-              page = key / P;
-              off = key - page * P;
-            }
-            const int64_t pg = a.kv_indices[ip0 + page];
-            vr(i) = *reinterpret_cast<const uint4*>(vp + pg * a.page_stride +
-                                                    (int64_t)off * tstride + h * kD + v_chunk * 8);
-          }
-        }
-      }
-    };
-    auto swrite = [&](int kb, auto stage) {
-      uint16_t* sK = sK_of(stage);
-      uint16_t* sKlo = sKlo_of(stage);
-      uint16_t* sVt = sV_of(stage);
-      if (stage_k) {
-        float cs[ROPE ? 4 : 1], sn[ROPE ? 4 : 1];
-        if constexpr (ROPE) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            rope_sincos((float)(kv_pos0 + kb + k_row), kfhi[e], kflo[e], &sn[e], &cs[e]);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if constexpr (ROPE) {
-            if (i > 0) {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const float cn = __builtin_fmaf(-sn[e], s16[e], cs[e] * c16[e]);
-                sn[e] = __builtin_fmaf(cs[e], s16[e], sn[e] * c16[e]);
-                cs[e] = cn;
-              }
-            }
-            float kr[8];
-            uint4 hi, lo;
-            if constexpr (RIL) {
-              // 8 consecutive elements, stored in place as one 16-byte piece
-              rope_k_adjacent<T>(kreg[i], cs, sn, kr);
-              split8<T>(kr, hi, lo);
-              const int at = (k_row + 16 * i) * kKStride + kc_chunk * 8;
-              *reinterpret_cast<uint4*>(&sK[at]) = hi;
-              *reinterpret_cast<uint4*>(&sKlo[at]) = lo;
-            } else {
-              rope_k_pairs<T>(kreg[i], cs, sn, kr);
-              split8<T>(kr, hi, lo);
-              const int at = (k_row + 16 * i) * kKStride + kc_chunk * 4;
-              *reinterpret_cast<uint2*>(&sK[at]) = make_uint2(hi.x, hi.y);
-              *reinterpret_cast<uint2*>(&sK[at + 64]) = make_uint2(hi.z, hi.w);
-              *reinterpret_cast<uint2*>(&sKlo[at]) = make_uint2(lo.x, lo.y);
-              *reinterpret_cast<uint2*>(&sKlo[at + 64]) = make_uint2(lo.z, lo.w);
-            }
-          } else {
-            const int at = (k_row + 16 * i) * kKStride + kc_chunk * 8;
-            *reinterpret_cast<uint4*>(&sK[at]) = kreg[i];
-          }
-        }
-      }
-      if (stage_v) {
-        // V^T: element d of the 4 keys 16 vw + 4 v_kg + 0..3 as one 8-byte piece
-        uint16_t* V = sVt + 16 * vw + 4 * v_kg;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t w0 = word(vr(0), j), w1 = word(vr(1), j);
-          const uint32_t w2 = word(vr(2), j), w3 = word(vr(3), j);
-          const int d = v_chunk * 8 + 2 * j;
-          *reinterpret_cast<uint2*>(&V[d * kVStride]) = make_uint2(pair_lo(w0, w1), pair_lo(w2, w3));
-          *reinterpret_cast<uint2*>(&V[(d + 1) * kVStride]) =
-              make_uint2(pair_hi(w0, w1), pair_hi(w2, w3));
-        }
-      }
-    };
-
-    // Without RoPE: block kb straight into LDS stage `stage`. Each wave
-    // instruction fills 4 rows (1 KB, lane l at byte 16 l); wave w owns rows
-    // 8 w .. 8 w + 7 of K and of V. Lane l stores row r = r0 + l / 16 at chunk
-    // position l % 16, which holds the row's logical chunk (l % 16) ^ swz(r).
-    // Rows past the segment end re-read the last valid rows (in bounds, masked).
-    auto dload = [&](int kb, auto stage) {
-      uint16_t* sK = sK_of(stage);
-      uint16_t* sV = sV_of(stage);
-      const int pos = lane & 15;
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r0 = 4 * (2 * wave + i);
-        const int r = r0 + (lane >> 4);
-        const int qk = pos ^ (r & 15);        // K chunk held at this position
-        const int qv = pos ^ (2 * (r & 7));   // V chunk held at this position
-        int64_t row_base;                      // element offset of key kb + r (head h)
-        if constexpr (FASTPAGE) {
-          const int last4 = (kv_end - 1) & ~3;
-          const int kk = min(kb + r0, last4);  // 4-row group, one page
-          // rows at or past kv_end re-read the last key (unwritten slots may
-          // hold NaN / inf bits, which p = 0 does not cancel in P.V)
-          const int rr = min(lane >> 4, kv_end - 1 - kk);
-          row_base = (int64_t)kv_indices[ip0 + (kk >> shift)] * a.page_stride +
-                     (int64_t)((kk & (P - 1)) + rr) * tstride + h * kD;
-        } else {
-          const int key = min(kb + r, kv_end - 1);
-          int page, off;
-          if (shift >= 0) {
-            page = key >> shift;
-            off = key & (P - 1);
-          } else {
-            page = key / P;
-            off = key - page * P;
-          }
-          row_base = (int64_t)a.kv_indices[ip0 + page] * a.page_stride + (int64_t)off * tstride +
-                     h * kD;
-        }
-        __builtin_amdgcn_global_load_lds(kp + row_base + qk * 8, (ABP_LDS void*)(sK + r0 * kD),
-                                         16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vp + row_base + qv * 8, (ABP_LDS void*)(sV + r0 * kD),
-                                         16, 0, 0);
-      }
-    };
-
-    if (kv_begin < kv_end) {
-      if constexpr (ROPE) {
-        gload(kv_begin);
-        swrite(kv_begin, S0{});
-      } else {
-        dload(kv_begin, S0{});
-      }
+      for (int i = 0; i < 4; ++i) st_part(R0, i, S0{});
     }
     __syncthreads();
-    // one block on stage `st` (blocks alternate between the two stages)
-    auto block = [&](auto st, int kb) __attribute__((always_inline)) {
+
+    // one block on stage `st`: R holds block j + 1 (rotated and stored into
+    // the other stage beside the score products), Rn takes block j + 2
+    auto block = [&](auto st, int kb, Regs& R, Regs& Rn) __attribute__((always_inline)) {
       constexpr int ST = decltype(st)::value;
       using Other = std::integral_constant<int, 1 - ST>;
-      const bool has_next = kb + kTk < kv_end;
-      if (has_next) {
-        if constexpr (ROPE) gload(kb + kTk);
-        else dload(kb + kTk, Other{});  // completes before the barrier ending this block
-      }
+      // always issued (past the end it re-reads the last rows), so the wait
+      // for R below is the same count on every block
+      gload(kb + 2 * kTk, Rn);
       const uint16_t* sK = sK_of(st);
-      const uint16_t* sKlo = sKlo_of(st);
+      const uint16_t* sKlo = sK + kKElems;
       const uint16_t* sVt = sV_of(st);
-
-      // The block is taken as two 32-key halves h, each one step of the online
-      // softmax. Both halves' S products are issued first; the softmax of half
-      // 0 can then run beside the products of half 1, and the P.V products of
-      // half 0 beside the softmax of half 1 (O takes half 0's contribution
-      // before any rescale that half 1 makes).
-      // S^T = K Q^T: S[mb][nb] holds keys kb + 16 mb + 4 g16 + j, row nb*16 + l16
+      // S^T = K Q^T: S[mb][nb] holds keys kb + 16 mb + 4 g16 + j, row nb*16 + l16.
+      // Product piece kc of 16-key group mb is 6 products (hi/lo parts); its
+      // operands are read one piece ahead. Each fenced slot issues 2 products
+      // and one piece of the next block's staging part mb (the angles first).
       f32x4_t S[4][2];
-      auto qk_half = [&](int h) __attribute__((always_inline)) {
+      uint4 kh[2], kl[2];
+      auto rd = [&](int mb, int kc, int buf) __attribute__((always_inline)) {
+        const int at = (mb * 16 + l16) * kKStride + kc * 32 + g16 * 8;
+        kh[buf] = *reinterpret_cast<const uint4*>(&sK[at]);
+        kl[buf] = *reinterpret_cast<const uint4*>(&sKlo[at]);
+      };
+      auto mf = [&](int mb, int kc, int buf, int t) __attribute__((always_inline)) {
+        const uint4& ka = (t < 4) ? kh[buf] : kl[buf];
+        const uint4& qb = (t < 2 || t >= 4) ? qf[t & 1][kc] : qfl[t & 1][kc];
+        S[mb][t & 1] = mfma<T>(ka, qb, S[mb][t & 1]);
+      };
+      rd(0, 0, 0);
 #pragma unroll
-        for (int mb = 2 * h; mb < 2 * h + 2; ++mb) {
-          S[mb][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          S[mb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int mb = 0; mb < 4; ++mb) {
+        S[mb][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        S[mb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int kc = 0; kc < 4; ++kc) {
-            // swizzled rows without RoPE: chunk kc * 4 + g16 of row mb * 16 + l16
-            const int at = ROPE ? (mb * 16 + l16) * kKStride + kc * 32 + g16 * 8
-                                : (mb * 16 + l16) * kD + (((kc * 4 + g16) ^ l16) * 8);
-            const uint4 ka = *reinterpret_cast<const uint4*>(&sK[at]);
-            S[mb][0] = mfma<T>(ka, qf[0][kc], S[mb][0]);
-            S[mb][1] = mfma<T>(ka, qf[1][kc], S[mb][1]);
-            if constexpr (ROPE) {  // + Kh Ql + Kl Qh
-              const uint4 kl = *reinterpret_cast<const uint4*>(&sKlo[at]);
-              S[mb][0] = mfma<T>(ka, qfl[0][kc], S[mb][0]);
-              S[mb][1] = mfma<T>(ka, qfl[1][kc], S[mb][1]);
-              S[mb][0] = mfma<T>(kl, qf[0][kc], S[mb][0]);
-              S[mb][1] = mfma<T>(kl, qf[1][kc], S[mb][1]);
+        for (int kc = 0; kc < 4; ++kc) {
+          const int buf = kc & 1;
+#pragma unroll
+          for (int sl = 0; sl < 3; ++sl) {
+            if (sl == 0) {
+              if (kc < 3) rd(mb, kc + 1, buf ^ 1);
+              else if (mb < 3) rd(mb + 1, 0, buf ^ 1);
             }
+            mf(mb, kc, buf, 2 * sl);
+            mf(mb, kc, buf, 2 * sl + 1);
+            // the next block's staging (past the last block it fills the idle
+            // stage with values nobody reads)
+            if (mb == 0 && kc == 0 && sl == 0) st_begin(kb + kTk);
+            else st_piece(R, mb, 3 * kc + sl, Other{});
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
-      };
+      }
       // masks of a half (keys past the segment end, causal limit per row),
       // online softmax with lazy rescale, P of the half packed as the PV B
       // operand: K-slots of lane group g16 are keys 4 g16..+3 and 16 + 4 g16..+3
       uint4 pB[2][2];  // [h][nb]
-      auto softmax_half = [&](int h) __attribute__((always_inline)) {
-        const int kbh = kb + 32 * h;
+      auto softmax_half = [&](int hh) __attribute__((always_inline)) {
+        const int kbh = kb + 32 * hh;
         const bool edge = (kbh + 32 > kv_end) || (CAUSAL && kbh + 31 > tile_min_lim);
         if (edge) {
 #pragma unroll
-          for (int mb = 2 * h; mb < 2 * h + 2; ++mb)
+          for (int mb = 2 * hh; mb < 2 * hh + 2; ++mb)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const int key = kb + mb * 16 + g16 * 4 + j;
@@ -553,7 +543,7 @@ __device__ __forceinline__ void append_worker_staged(const AttnArgs& a, int bid)
         for (int nb = 0; nb < 2; ++nb) {
           float x = kNegInf;
 #pragma unroll
-          for (int mb = 2 * h; mb < 2 * h + 2; ++mb)
+          for (int mb = 2 * hh; mb < 2 * hh + 2; ++mb)
             x = __builtin_fmaxf(x, __builtin_fmaxf(__builtin_fmaxf(S[mb][nb][0], S[mb][nb][1]),
                                                    __builtin_fmaxf(S[mb][nb][2], S[mb][nb][3])));
           mx[nb] = max_over_groups(x);
@@ -578,67 +568,36 @@ __device__ __forceinline__ void append_worker_staged(const AttnArgs& a, int bid)
           for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-              p[i][j] = fast_exp2(__builtin_fmaf(S[2 * h + i][nb][j], cl2, -mc));
+              p[i][j] = fast_exp2(__builtin_fmaf(S[2 * hh + i][nb][j], cl2, -mc));
           // row sum in fp32 of the unrounded p: lse must not carry P's 16-bit rounding
           lsum[nb] += ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) +
                       ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
-          pB[h][nb] = make_uint4(pack2<T>(p[0][0], p[0][1]), pack2<T>(p[0][2], p[0][3]),
-                                 pack2<T>(p[1][0], p[1][1]), pack2<T>(p[1][2], p[1][3]));
+          pB[hh][nb] = make_uint4(pack2<T>(p[0][0], p[0][1]), pack2<T>(p[0][2], p[0][3]),
+                                  pack2<T>(p[1][0], p[1][1]), pack2<T>(p[1][2], p[1][3]));
         }
       };
-      // O^T += V^T P^T over half h
-      auto pv_half = [&](int h) __attribute__((always_inline)) {
+      // O^T += V^T P^T over half hh
+      auto pv_half = [&](int hh) __attribute__((always_inline)) {
 #pragma unroll
         for (int md = 0; md < 8; ++md) {
-          uint4 va;
-          if constexpr (ROPE) {
-            const uint16_t* vrow = &sVt[(md * 16 + l16) * kVStride + h * 32 + g16 * 4];
-            const uint2 v0 = *reinterpret_cast<const uint2*>(vrow);
-            const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 16);
-            va = make_uint4(v0.x, v0.y, v1.x, v1.y);
-          } else {
-            // V^T fragment by transpose reads of V: in each 16-lane group,
-            // lane c points at V[key 4 g16 + c / 4 (+ 16)][d 16 md + 4 (c % 4)]
-            // and receives V[4 keys][d 16 md + c] (keys 4 g16..+3, 16 + ..)
-            const int d0 = md * 16 + 4 * (l16 & 3);
-            const int kA = h * 32 + 4 * g16 + (l16 >> 2);
-            const int kB = kA + 16;
-            const int offA = kA * kD + (((d0 >> 3) ^ (2 * (kA & 7))) * 8) + (d0 & 7);
-            const int offB = kB * kD + (((d0 >> 3) ^ (2 * (kB & 7))) * 8) + (d0 & 7);
-            const v4i16_t a4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ABP_LDS v4i16_t*)(sVt + offA));
-            const v4i16_t b4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ABP_LDS v4i16_t*)(sVt + offB));
-            const uint2 av = __builtin_bit_cast(uint2, a4), bv = __builtin_bit_cast(uint2, b4);
-            va = make_uint4(av.x, av.y, bv.x, bv.y);
-          }
-          O[md][0] = mfma<T>(va, pB[h][0], O[md][0]);
-          O[md][1] = mfma<T>(va, pB[h][1], O[md][1]);
+          const uint16_t* vrow = &sVt[(md * 16 + l16) * kVStride + hh * 32 + g16 * 4];
+          const uint2 v0 = *reinterpret_cast<const uint2*>(vrow);
+          const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 16);
+          const uint4 va = make_uint4(v0.x, v0.y, v1.x, v1.y);
+          O[md][0] = mfma<T>(va, pB[hh][0], O[md][0]);
+          O[md][1] = mfma<T>(va, pB[hh][1], O[md][1]);
         }
       };
-      // matrix-core phases run at raised wave priority: the arbiter then
-      // issues one wave's products back to back while the other wave of the
-      // SIMD runs its softmax on the vector unit
-      __builtin_amdgcn_s_setprio(1);
-      qk_half(0);
-      qk_half(1);
-      __builtin_amdgcn_s_setprio(0);
       softmax_half(0);
-      __builtin_amdgcn_s_setprio(1);
       pv_half(0);
-      __builtin_amdgcn_s_setprio(0);
       softmax_half(1);
-      __builtin_amdgcn_s_setprio(1);
       pv_half(1);
-      __builtin_amdgcn_s_setprio(0);
-      // the other stage held block j - 1, which every wave finished before the
-      // barrier that ended the previous iteration
-      if constexpr (ROPE) {
-        if (has_next) swrite(kb + kTk, Other{});
-      }
+      // ends every wave's reads of this stage and publishes the other
       __syncthreads();
     };
     for (int kb = kv_begin; kb < kv_end; kb += 2 * kTk) {
-      block(S0{}, kb);
-      if (kb + kTk < kv_end) block(S1{}, kb + kTk);
+      block(S0{}, kb, R1, R0);
+      if (kb + kTk < kv_end) block(S1{}, kb + kTk, R0, R1);
     }
 
     // ---- finalize rows: o = O / l, lse = m * scale + ln l
@@ -684,7 +643,7 @@ __device__ __forceinline__ void append_worker_staged(const AttnArgs& a, int bid)
       }
     }
     if (slot >= 0 && plan[H_MERGE_KERNEL] == 0) {
-      merge_if_last<kRows, 64 * NW>(a, tile, &s_last, [&](int r, int64_t* orow) {
+      merge_if_last<kRows, 64 * append_waves<true>()>(a, tile, &s_last, [&](int r, int64_t* orow) {
         const int tloc = qt * TQ + r / G;
         if (tloc >= qo_len) return false;
         *orow = (int64_t)(q0 + tloc) * a.num_qo_heads + h * G + (r % G);
@@ -1212,7 +1171,7 @@ __device__ __forceinline__ void append_worker_pipe(const AttnArgs& a, int bid,
 // refills already land within the two steps they are given.
 template <typename T, int G, bool CAUSAL, bool ROPE, bool FASTPAGE, bool RIL, int NS = 2>
 __device__ __forceinline__ void append_worker(const AttnArgs& a, int bid, const PipeLds& lds) {
-  if constexpr (ROPE) append_worker_staged<T, G, CAUSAL, true, FASTPAGE, RIL>(a, bid);
+  if constexpr (ROPE) append_worker_rope<T, G, CAUSAL, FASTPAGE, RIL>(a, bid);
   else append_worker_pipe<T, G, CAUSAL, FASTPAGE, NS>(a, bid, lds);
 }
 
