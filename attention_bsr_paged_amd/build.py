@@ -22,8 +22,8 @@ LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libabp.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "plan.cpp", "merge.hip", "decode.hip", "append.hip", "upload.hip",
-           "page_append.hip", "decode_mfma.hip", "pod.hip", "static_ws.hip"]
+SOURCES = ["api.cpp", "plan.cpp", "merge.hip", "decode.hip", "append.hip", "append_rope.hip",
+           "upload.hip", "page_append.hip", "decode_mfma.hip", "pod.hip", "static_ws.hip"]
 
 COMMON = [
     "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
@@ -36,6 +36,9 @@ DEVICE = [
     # (infinities keep their meaning: masked scores are -inf)
     "-fno-honor-nans",
 ]
+# per-source device flags: the RoPE append kernels keep their matrix-product
+# accumulators in VGPRs (see the header of append_rope.hip)
+EXTRA = {"append_rope.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:
@@ -49,7 +52,7 @@ def compile_one(src: str, opt: list, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     cmd = [hipcc(), "-c", os.path.join(CSRC, src), "-o", obj] + COMMON + opt
     if src.endswith(".hip"):
-        cmd += DEVICE + ["-x", "hip"]
+        cmd += DEVICE + EXTRA.get(src, []) + ["-x", "hip"]
     else:
         # host-only translation units: no device code object
         cmd += ["--offload-arch=" + ARCH, "-x", "hip", "--cuda-host-only"]

@@ -14,8 +14,8 @@
 // Tiles: 256 rows = tile_q tokens x G qo heads of one kv head (row r is token
 // r / G, head r % G), against blocks of 64 keys. A 512-thread workgroup (8
 // waves) is one worker; wave w owns rows [32 w, 32 w + 32) (two 16-row column
-// blocks). The RoPE variant uses 128-row tiles and 4 waves: its split q
-// operands need the registers of one wave per SIMD.
+// blocks). The RoPE variant (append_rope.hip) uses 128-row tiles and 4 waves:
+// its split q operands need the registers of one wave per SIMD.
 //
 //   S^T = K Q^T    v_mfma_f32_16x16x32 with A = K rows from LDS and B = Q^T
 //                  from registers. The accumulator gives each lane one query
@@ -51,28 +51,20 @@ namespace {
 
 using appi::append_waves;
 
-template <typename T, int G, bool CAUSAL, bool ROPE, bool FASTPAGE, bool RIL>
-__global__ __launch_bounds__(64 * append_waves<ROPE>(), 1) void append_kernel(AttnArgs a) {
+template <typename T, int G, bool CAUSAL, bool FASTPAGE>
+__global__ __launch_bounds__(64 * append_waves<false>(), 1) void append_kernel(AttnArgs a) {
   ABP_APPEND_PIPE_LDS(lds, 2);
-  appi::append_worker<T, G, CAUSAL, ROPE, FASTPAGE, RIL>(a, blockIdx.x, lds);
-}
-
-template <typename T, int G, bool CAUSAL, bool ROPE, bool RIL>
-hipError_t launch_f(const AttnArgs& a, hipStream_t s) {
-  if (a.page_shift >= 4)
-    append_kernel<T, G, CAUSAL, ROPE, true, RIL>
-        <<<a.workers, 64 * append_waves<ROPE>(), 0, s>>>(a);
-  else
-    append_kernel<T, G, CAUSAL, ROPE, false, RIL>
-        <<<a.workers, 64 * append_waves<ROPE>(), 0, s>>>(a);
-  return hipGetLastError();
+  appi::append_worker<T, G, CAUSAL, false, FASTPAGE, false>(a, blockIdx.x, lds);
 }
 
 template <typename T, int G, bool CAUSAL>
 hipError_t launch_c(const Config& cfg, const AttnArgs& a, hipStream_t s) {
-  if (!cfg.rope) return launch_f<T, G, CAUSAL, false, false>(a, s);
-  return cfg.rope_interleave ? launch_f<T, G, CAUSAL, true, true>(a, s)
-                             : launch_f<T, G, CAUSAL, true, false>(a, s);
+  if (cfg.rope) return launch_append_rope(cfg, a, s);
+  if (a.page_shift >= 4)
+    append_kernel<T, G, CAUSAL, true><<<a.workers, 64 * append_waves<false>(), 0, s>>>(a);
+  else
+    append_kernel<T, G, CAUSAL, false><<<a.workers, 64 * append_waves<false>(), 0, s>>>(a);
+  return hipGetLastError();
 }
 
 template <typename T, int G>
@@ -100,15 +92,11 @@ hipError_t launch_append(const Config& cfg, const AttnArgs& a, hipStream_t s) {
 }
 
 int append_blocks_per_cu(const Config& cfg) {
+  if (cfg.rope) return append_rope_blocks_per_cu();
   int n = 0;
-  // the tile shape is shared by all variants; RoPE ones are built for one per CU
-  hipError_t e =
-      cfg.rope ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                     &n, append_kernel<BF16, 4, true, true, true, false>, 64 * append_waves<true>(),
-                     0)
-               : hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                     &n, append_kernel<BF16, 4, true, false, true, false>,
-                     64 * append_waves<false>(), 0);
+  // the tile shape is shared by all variants, each built for one per CU
+  const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      &n, append_kernel<BF16, 4, true, true>, 64 * append_waves<false>(), 0);
   return e == hipSuccess && n > 0 ? n : 1;
 }
 

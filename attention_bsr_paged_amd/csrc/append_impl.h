@@ -448,6 +448,17 @@ __device__ __forceinline__ void append_worker_rope(const AttnArgs& a, int bid) {
     }
     // first row of the tile sees the fewest keys
     const int tile_min_lim = kv_len - qo_len + qt * TQ;
+    // the q operands live in AGPRs, which the score products read in place:
+    // the VGPRs are left to the accumulators and the staging
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        asm volatile("" : "+a"(qf[nb][kc].x), "+a"(qf[nb][kc].y), "+a"(qf[nb][kc].z),
+                     "+a"(qf[nb][kc].w));
+        asm volatile("" : "+a"(qfl[nb][kc].x), "+a"(qfl[nb][kc].y), "+a"(qfl[nb][kc].z),
+                     "+a"(qfl[nb][kc].w));
+      }
 
     float m[2] = {kNegInf, kNegInf};
     float lsum[2] = {0.f, 0.f};

@@ -46,6 +46,10 @@ int decode_mfma_blocks_per_cu(const Config& cfg);
 int decode_blocks_per_cu(const Config& cfg);
 int append_blocks_per_cu(const Config& cfg);
 hipError_t launch_append(const Config& cfg, const AttnArgs& a, hipStream_t stream);
+// the RoPE variants of the append kernel (append_rope.hip; launch_append
+// dispatches to them)
+int append_rope_blocks_per_cu();
+hipError_t launch_append_rope(const Config& cfg, const AttnArgs& a, hipStream_t stream);
 // mixed batch: workgroups [0, app.workers) run append workers, the next
 // dec.workers run matrix-core decode workers (cfg: the append part's config)
 bool pod_applies(const Config& cfg);
