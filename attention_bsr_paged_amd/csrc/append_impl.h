@@ -529,32 +529,32 @@ __device__ __forceinline__ void append_worker_rope(const AttnArgs& a, int bid) {
           }
         }
       }
-      // masks of a half (keys past the segment end, causal limit per row),
-      // online softmax with lazy rescale, P of the half packed as the PV B
-      // operand: K-slots of lane group g16 are keys 4 g16..+3 and 16 + 4 g16..+3
-      uint4 pB[2][2];  // [h][nb]
-      auto softmax_half = [&](int hh) __attribute__((always_inline)) {
-        const int kbh = kb + 32 * hh;
-        const bool edge = (kbh + 32 > kv_end) || (CAUSAL && kbh + 31 > tile_min_lim);
-        if (edge) {
+      // ---- online softmax over the block's 64 keys: masks (keys past the
+      // segment end, causal limit per row), one reference check per row with
+      // a lazy rescale, then the exponentials of each 32-key half, P packed as
+      // the PV B operand (K-slots of lane group g16 are keys 4 g16..+3 and
+      // 16 + 4 g16..+3 of the half)
+      const bool edge = (kb + kTk > kv_end) || (CAUSAL && kb + kTk - 1 > tile_min_lim);
+      if (edge) {
 #pragma unroll
-          for (int mb = 2 * hh; mb < 2 * hh + 2; ++mb)
+        for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int key = kb + mb * 16 + g16 * 4 + j;
+          for (int j = 0; j < 4; ++j) {
+            const int key = kb + mb * 16 + g16 * 4 + j;
 #pragma unroll
-              for (int nb = 0; nb < 2; ++nb) {
-                const bool dead = key >= kv_end || (CAUSAL && key > lim[nb]);
-                if (dead) S[mb][nb][j] = kNegInf;
-              }
+            for (int nb = 0; nb < 2; ++nb) {
+              const bool dead = key >= kv_end || (CAUSAL && key > lim[nb]);
+              if (dead) S[mb][nb][j] = kNegInf;
             }
-        }
+          }
+      }
+      {
         float mx[2];
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
           float x = kNegInf;
 #pragma unroll
-          for (int mb = 2 * hh; mb < 2 * hh + 2; ++mb)
+          for (int mb = 0; mb < 4; ++mb)
             x = __builtin_fmaxf(x, __builtin_fmaxf(__builtin_fmaxf(S[mb][nb][0], S[mb][nb][1]),
                                                    __builtin_fmaxf(S[mb][nb][2], S[mb][nb][3])));
           mx[nb] = max_over_groups(x);
@@ -571,38 +571,52 @@ __device__ __forceinline__ void append_worker_rope(const AttnArgs& a, int bid) {
             for (int md = 0; md < 8; ++md) O[md][nb] *= alpha;
           }
         }
+      }
+      const float mc[2] = {(m[0] == kNegInf ? 0.f : m[0]) * cl2, (m[1] == kNegInf ? 0.f : m[1]) * cl2};
+      uint4 pB[2][2];  // [half][nb]
+      float p[2][2][4];  // [nb][16-key group of the half][key]
+      // piece k (0..3) of half hh's exponentials: row block nb = k / 2,
+      // 16-key group k % 2; the row sum and the packing follow with the
+      // group's second piece. The row sum is taken in fp32 of the unrounded
+      // p: lse must not carry P's 16-bit rounding.
+      auto exps = [&](int hh, int k) __attribute__((always_inline)) {
+        const int nb = k >> 1, i = k & 1;
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const float mc = (m[nb] == kNegInf ? 0.f : m[nb]) * cl2;
-          float p[2][4];
-#pragma unroll
-          for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              p[i][j] = fast_exp2(__builtin_fmaf(S[2 * hh + i][nb][j], cl2, -mc));
-          // row sum in fp32 of the unrounded p: lse must not carry P's 16-bit rounding
-          lsum[nb] += ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) +
-                      ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
-          pB[hh][nb] = make_uint4(pack2<T>(p[0][0], p[0][1]), pack2<T>(p[0][2], p[0][3]),
-                                  pack2<T>(p[1][0], p[1][1]), pack2<T>(p[1][2], p[1][3]));
+        for (int j = 0; j < 4; ++j)
+          p[nb][i][j] = fast_exp2(__builtin_fmaf(S[2 * hh + i][nb][j], cl2, -mc[nb]));
+        if (i == 1) {
+          lsum[nb] += ((p[nb][0][0] + p[nb][0][1]) + (p[nb][0][2] + p[nb][0][3])) +
+                      ((p[nb][1][0] + p[nb][1][1]) + (p[nb][1][2] + p[nb][1][3]));
+          pB[hh][nb] = make_uint4(pack2<T>(p[nb][0][0], p[nb][0][1]), pack2<T>(p[nb][0][2], p[nb][0][3]),
+                                  pack2<T>(p[nb][1][0], p[nb][1][1]), pack2<T>(p[nb][1][2], p[nb][1][3]));
         }
       };
-      // O^T += V^T P^T over half hh
-      auto pv_half = [&](int hh) __attribute__((always_inline)) {
+      // O^T += V^T P^T over half hh, 16 dims (md) at a time; the V^T operand
+      // of each md is read one slot ahead, and each slot carries a piece of
+      // the next half's exponentials
+      uint4 va[2];
+      auto rdv = [&](int hh, int md, int buf) __attribute__((always_inline)) {
+        const uint16_t* vrow = &sVt[(md * 16 + l16) * kVStride + hh * 32 + g16 * 4];
+        const uint2 v0 = *reinterpret_cast<const uint2*>(vrow);
+        const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 16);
+        va[buf] = make_uint4(v0.x, v0.y, v1.x, v1.y);
+      };
+      rdv(0, 0, 0);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) exps(0, k);
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
         for (int md = 0; md < 8; ++md) {
-          const uint16_t* vrow = &sVt[(md * 16 + l16) * kVStride + hh * 32 + g16 * 4];
-          const uint2 v0 = *reinterpret_cast<const uint2*>(vrow);
-          const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 16);
-          const uint4 va = make_uint4(v0.x, v0.y, v1.x, v1.y);
-          O[md][0] = mfma<T>(va, pB[hh][0], O[md][0]);
-          O[md][1] = mfma<T>(va, pB[hh][1], O[md][1]);
+          const int buf = md & 1;
+          if (md < 7) rdv(hh, md + 1, buf ^ 1);
+          else if (hh == 0) rdv(1, 0, buf ^ 1);
+          O[md][0] = mfma<T>(va[buf], pB[hh][0], O[md][0]);
+          O[md][1] = mfma<T>(va[buf], pB[hh][1], O[md][1]);
+          if (hh == 0 && md < 4) exps(1, md);
+          __builtin_amdgcn_sched_barrier(0);
         }
-      };
-      softmax_half(0);
-      pv_half(0);
-      softmax_half(1);
-      pv_half(1);
+      }
       // ends every wave's reads of this stage and publishes the other
       __syncthreads();
     };
