@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(AttnArgs a) {
 }
 
 template <typename T, int G>
-__global__ __launch_bounds__(256, 2) void decode_mfma_fp8_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 1) void decode_mfma_fp8_kernel(AttnArgs a) {
   dmi::decode_mfma_fp8_worker<T, G>(a, blockIdx.x);
 }
 
@@ -104,8 +104,9 @@ hipError_t launch_decode_mfma(const Config& cfg, const AttnArgs& a, hipStream_t 
 
 // Default workers per compute unit: fewer than fit. With non-temporal K/V
 // loads, one 16-bit worker per compute unit beat two on the batch decode
-// (99.8 against 102.2 us; skewed lengths 89.9 against 92.7 us), and two fp8
-// workers beat three (63.5 against 66.4 us).
+// (99.8 against 102.2 us; skewed lengths 89.9 against 92.7 us). The fp8
+// worker needs a compute unit's registers for its four chunk stages (one
+// workgroup per compute unit: 61.0 us against 62.2 for two with two stages).
 int decode_mfma_blocks_per_cu(const Config& cfg) {
   int n = 0;
   if (cfg.rope) {
@@ -118,7 +119,7 @@ int decode_mfma_blocks_per_cu(const Config& cfg) {
     const hipError_t e = cfg.qkv_dtype == ABP_BF16
         ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_fp8_kernel<BF16, 4>, 256, 0)
         : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_fp8_kernel<F16, 4>, 256, 0);
-    return e == hipSuccess ? (n < 2 ? n : 2) : 0;
+    return e == hipSuccess ? (n < 1 ? n : 1) : 0;
   }
   const hipError_t e = cfg.qkv_dtype == ABP_BF16
       ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<BF16, 4>, 256, 0)

@@ -608,16 +608,20 @@ __device__ __forceinline__ void decode_mfma_worker(const AttnArgs& a, int worker
 // The same decode for an fp8 (OCP e4m3) KV cache. K and V rows are half as
 // wide, so each lane's share is loaded into registers as codes and widened
 // to the query's 16-bit type on the way to the matrix cores:
-//   * K: lane group g16 holds head dims [32 g16, 32 g16 + 32) of its token
-//     (32 contiguous bytes, two 16-byte loads per 16-token tile); piece kc of
-//     that range is the lane's 8 K-slots of product kc, and q is loaded with
-//     the same head-dim map (any map serves a dot product if q and K share it);
+//   * K: lane group g16 holds head dims [16 g16, 16 g16 + 16) and
+//     [64 + 16 g16, 64 + 16 g16 + 16) of its token (two 16-byte loads per
+//     16-token tile, each covering a contiguous 64-byte half of every row);
+//     product kc takes dims 64 (kc / 2) + 16 g16 + 8 (kc % 2) .. + 7 as the
+//     lane's 8 K-slots, and q is loaded with the same head-dim map (any map
+//     serves a dot product if q and K share it);
 //   * V: lane l loads 16 codes of row 8 i + l / 8 (four loads per chunk),
 //     widens them to two 16-byte chunks and writes them into its wave's LDS
 //     slice in the layout the transpose reads of the 16-bit kernel expect.
 // k_scale is folded into the logit scale on the host; v_scale multiplies the
-// final normalisation. With 16 VGPRs of K and V codes per chunk, both register
-// sets fit, so every wait is a register dependency.
+// final normalisation. K and V codes take 32 VGPRs per chunk; with one
+// 4-wave workgroup per compute unit (512 registers a wave) four register sets
+// fit, so three chunks stay in flight per wave and every wait is a register
+// dependency.
 template <typename T, int G>
 __device__ __forceinline__ void decode_mfma_fp8_worker(const AttnArgs& a, int worker) {
   static_assert(G == 4 || G == 8, "rows of one kv head fill at most one 16-row tile");
@@ -651,16 +655,16 @@ __device__ __forceinline__ void decode_mfma_fp8_worker(const AttnArgs& a, int wo
     const int b = tiles[4 * tile], h = tiles[4 * tile + 1] + wave;
     const int ip0 = kv_indptr[b];
 
-    // q of row l16 (< G), head dims 32 g16 + 8 kc .. + 7 for product kc
+    // q of row l16 (< G), head dims dim0(kc) .. + 7 for product kc, the K map
     uint4 qf[4];
     {
       const int qr = l16 < G ? l16 : G - 1;
       const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
-                             (int64_t(b) * a.num_qo_heads + int64_t(h) * G + qr) * kD + 32 * g16;
+                             (int64_t(b) * a.num_qo_heads + int64_t(h) * G + qr) * kD;
       const uint32_t keep = l16 < G ? 0xffffffffu : 0u;
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc) {
-        const uint4 v = *reinterpret_cast<const uint4*>(qrow + 8 * kc);
+        const uint4 v = *reinterpret_cast<const uint4*>(qrow + 64 * (kc >> 1) + 16 * g16 + 8 * (kc & 1));
         qf[kc] = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
       }
     }
@@ -675,14 +679,15 @@ __device__ __forceinline__ void decode_mfma_fp8_worker(const AttnArgs& a, int wo
              int64_t(t & (P - 1)) * tstride + int64_t(h) * kD;
     };
     // K codes of chunk c: tile mb (a tile past kv_end re-reads tile 0, in
-    // bounds and masked); lane: token l16, bytes 32 g16 .. 32 g16 + 31
+    // bounds and masked); lane: token l16, bytes 16 g16 .. + 15 and 64 + 16 g16
+    // .. + 15, so that each load covers a contiguous 64-byte half of every row
     auto load_k = [&](int c, uint4 (&kr)[2][2]) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         const int t0 = (c + 16 * mb < kv_end) ? c + 16 * mb : c;
-        const uint8_t* rp = kp + row_base(t0) + int64_t(l16) * tstride + 32 * g16;
+        const uint8_t* rp = kp + row_base(t0) + int64_t(l16) * tstride + 16 * g16;
         kr[mb][0] = load_once(reinterpret_cast<const uint4*>(rp));
-        kr[mb][1] = load_once(reinterpret_cast<const uint4*>(rp + 16));
+        kr[mb][1] = load_once(reinterpret_cast<const uint4*>(rp + 64));
       }
     };
     // V codes of chunk c: piece i is row 8 i + l / 8, bytes 16 (l % 8) .. + 15;
@@ -766,27 +771,39 @@ __device__ __forceinline__ void decode_mfma_fp8_worker(const AttnArgs& a, int wo
       }
     };
 
-    // chunk n + 1 is loaded while chunk n is computed; only chunks that exist
+    // Four register sets: chunk n is computed while chunks n + 1 .. n + 3 are
+    // in flight. The first three loads are issued unconditionally (a chunk
+    // past the segment's last re-reads it), so every wait in the steady loop,
+    // where all loads are real chunks, is the same register dependency; the
+    // last chunks (fewer than seven) run in a tail with conditional loads.
+    constexpr int NS = 4;
     const int nch = kv_begin < kv_end ? (kv_end - kv_begin + kC - 1) / kC : 0;
-    uint4 KA[2][2], KB[2][2], VA[4], VB[4];
+    uint4 Kr[NS][2][2], Vr[NS][4];
+    auto ch = [&](int n) { return kv_begin + min(n, nch - 1) * kC; };
     if (nch > 0) {
-      load_k(kv_begin, KA);
-      load_v(kv_begin, VA);
-    }
-    for (int n = 0; n < nch; n += 2) {
-      const int c = kv_begin + n * kC;
-      const bool has1 = n + 1 < nch;
-      if (has1) {
-        load_k(c + kC, KB);
-        load_v(c + kC, VB);
+#pragma unroll
+      for (int i = 0; i < NS - 1; ++i) {
+        load_k(ch(i), Kr[i]);
+        load_v(ch(i), Vr[i]);
       }
-      compute(c, KA, VA);
-      if (has1) {
-        if (n + 2 < nch) {
-          load_k(c + 2 * kC, KA);
-          load_v(c + 2 * kC, VA);
+      int n = 0;
+      for (; n + 2 * NS - 1 <= nch; n += NS) {
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {
+          load_k(kv_begin + (n + u + NS - 1) * kC, Kr[(u + NS - 1) % NS]);
+          load_v(kv_begin + (n + u + NS - 1) * kC, Vr[(u + NS - 1) % NS]);
+          compute(kv_begin + (n + u) * kC, Kr[u], Vr[u]);
         }
-        compute(c + kC, KB, VB);
+      }
+      for (; n < nch; n += NS) {
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {
+          if (n + u + NS - 1 < nch) {
+            load_k(kv_begin + (n + u + NS - 1) * kC, Kr[(u + NS - 1) % NS]);
+            load_v(kv_begin + (n + u + NS - 1) * kC, Vr[(u + NS - 1) % NS]);
+          }
+          if (n + u < nch) compute(kv_begin + (n + u) * kC, Kr[u], Vr[u]);
+        }
       }
     }
 
