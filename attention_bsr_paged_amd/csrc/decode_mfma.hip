@@ -33,6 +33,11 @@
 // without RoPE), power-of-two page size >= 16 (a 16-token tile never
 // straddles a page), kv head count a multiple of 4, group size 4 or 8 (rows
 // padded to 16).
+//
+// Built with the matrix products in VGPR form (-mllvm -amdgpu-mfma-vgpr-form):
+// in the default form the compiler kept accumulators and loaded codes in
+// AGPRs and moved them to VGPRs around the vector work (376 moves in the
+// plain kernel, 864 in the fp8 one, 457 with RoPE; 0, 0 and 116 in VGPR form).
 #include "decode_mfma_impl.h"
 
 namespace abp {
