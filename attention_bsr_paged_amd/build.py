@@ -36,10 +36,10 @@ DEVICE = [
     # (infinities keep their meaning: masked scores are -inf)
     "-fno-honor-nans",
 ]
-# per-source device flags: these kernels (one workgroup per compute unit, so
-# up to 512 registers a wave) keep their matrix-product accumulators in VGPRs;
-# in the default form the compiler moves them between AGPRs and VGPRs around
-# the vector work (see the headers of append_rope.hip and decode_mfma.hip)
+# per-source device flags: these kernels keep their matrix-product
+# accumulators in VGPRs; in the default form the compiler moves them between
+# AGPRs and VGPRs around the vector work (see the headers of append_rope.hip
+# and decode_mfma.hip)
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 EXTRA = {"append_rope.hip": VGPR_FORM, "decode_mfma.hip": VGPR_FORM}
 

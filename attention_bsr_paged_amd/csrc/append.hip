@@ -14,8 +14,8 @@
 // Tiles: 256 rows = tile_q tokens x G qo heads of one kv head (row r is token
 // r / G, head r % G), against blocks of 64 keys. A 512-thread workgroup (8
 // waves) is one worker; wave w owns rows [32 w, 32 w + 32) (two 16-row column
-// blocks). The RoPE variant (append_rope.hip) uses 128-row tiles and 4 waves:
-// its split q operands need the registers of one wave per SIMD.
+// blocks). The RoPE variant (append_rope.hip) uses 128-row tiles, 16 rows a
+// wave: its q operands are hi and lo parts.
 //
 //   S^T = K Q^T    v_mfma_f32_16x16x32 with A = K rows from LDS and B = Q^T
 //                  from registers. The accumulator gives each lane one query

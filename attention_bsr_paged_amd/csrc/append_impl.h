@@ -135,39 +135,43 @@ __device__ __forceinline__ float max_over_groups(float x) {
   return __builtin_fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
 }
 
-// Waves per workgroup: 8 for the pipelined worker (256 rows), 4 for the RoPE
-// worker (128 rows: the hi/lo operands need a wave's 512 registers). One
-// workgroup per CU either way.
+// Waves per workgroup: 8 for both workers (one workgroup per CU). The
+// pipelined worker's waves own 32 rows each (256-row tiles), the RoPE worker's
+// 16 (128-row tiles: its q operands are hi and lo parts).
 template <bool ROPE>
 constexpr int append_waves() {
-  return ROPE ? 4 : 8;
+  return 8;
 }
 
-// The append worker with RoPE: 4 waves, 128 rows (tile_q tokens x G heads),
-// wave w owning rows 32 w .. 32 w + 31, against 64-key blocks.
+// The append worker with RoPE: 8 waves, 128 rows (tile_q tokens x G heads),
+// wave w owning rows 16 w .. 16 w + 15, against 64-key blocks.
 //
 // K must be rotated by its position before the score products, so it comes
 // into registers, is rotated there and is split into hi and lo 16-bit parts
 // (S = Kh Qh + Kh Ql + Kl Qh keeps fp32-level accuracy); V is transposed on
-// the way to LDS. Every thread stages 4 K rows and 4 V rows of each block.
+// the way to LDS. Every thread stages 2 K rows (32 keys apart) and 4 V rows
+// (4 head dims) of each block.
 //
 // Staging runs one block ahead of the products and its loads two blocks
 // ahead: while block j's products read LDS stage j & 1, block j + 1's
 // rotation (registers loaded during block j - 1) is interleaved with them and
 // stored into stage (j + 1) & 1, and block j + 2's loads are issued into the
 // registers block j came in. One barrier per block: it ends block j's reads of
-// stage j & 1 and publishes stage (j + 1) & 1. The rotation is vector work and
-// the score products matrix work, so with one wave per SIMD they overlap only
-// inside one wave's instruction stream: the score products of each 16-key
-// group are written beside the rotation of one K row and a quarter of the V
-// transposition, fenced from the next group.
+// stage j & 1 and publishes stage (j + 1) & 1. The score products are written
+// as fenced slots of 2 products and one small piece of the staging work; with
+// two waves per SIMD the other wave's vector work fills the rest.
 template <typename T, int G, bool CAUSAL, bool FASTPAGE, bool RIL>
 __device__ __forceinline__ void append_worker_rope(const AttnArgs& a, int bid) {
   // K elements a staging thread reads per row: rotate-half RoPE takes 4 + 4
   // (both halves of its 4 pairs), interleaved RoPE 8 consecutive ones
   constexpr int kKPiece = RIL ? 8 : 4;
-  constexpr int kRows = 32 * append_waves<true>();
+  constexpr int NW = append_waves<true>();
+  constexpr int NT = 64 * NW;
+  constexpr int kRows = 16 * NW;
   constexpr int TQ = kRows / G;
+  constexpr int KSTEP = NT / 16;           // keys between a thread's K rows
+  constexpr int KI = kTk / KSTEP;          // K rows a thread stages per block
+  static_assert(KI == 2 && NW == 8, "staging map: 2 K rows of 32 keys apart, 8 V keys a wave");
   // a stage: rotated K as hi and lo parts [64][kKStride] each, then V^T
   // [128][kVStride]; one array per stage, each named at compile time where
   // used, so the compiler sees that stores into one stage never alias reads
@@ -216,29 +220,30 @@ __device__ __forceinline__ void append_worker_rope(const AttnArgs& a, int bid) {
   const uint16_t* __restrict__ vp = static_cast<const uint16_t*>(a.v_pages);
 
   const float thr = kRescaleLog2 / cl2;  // lazy rescale threshold, raw score units
-  // staging: K rows k_row + 16 i (i = 16-key group), 16-byte chunk kc_chunk;
-  // V keys 16 wave + 4 v_kg + i, chunk v_chunk.
-  // A thread stages both elements of the rotary pairs j = 4 kc_chunk + e
-  // (e < 4) of its K rows (rotate-half: elements j and j + 64; interleaved:
-  // 2j and 2j + 1, its plain 8 elements), so each angle is computed once. Its
-  // rows are 16 keys apart: the first row's angles are evaluated and the next
-  // follow by angle addition with the rotation by 16 positions (c16, s16).
+  // staging: K rows k_row + 32 i (i < 2), 16-byte chunk kc_chunk. A thread
+  // stages both elements of the rotary pairs j = 4 kc_chunk + e (e < 4) of
+  // its K rows (rotate-half: elements j and j + 64; interleaved: 2j and
+  // 2j + 1, its plain 8 elements), so each angle is computed once; its second
+  // row follows by angle addition with the rotation by 32 positions.
+  // V: wave w stages keys 8 w + 4 v_kg + i (i < 4), head dims 4 v_q .. + 3.
   const int kc_chunk = tid & 15;
-  float kfhi[4], kflo[4], c16[4], s16[4];
+  const int k_row = tid >> 4;
+  const int k_grp = k_row & ~15;  // 16-key group of the row (uniform over the wave)
+  float kfhi[4], kflo[4], cst[4], sst[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int j = 4 * kc_chunk + e;
     kfhi[e] = rope[2 * j];
     kflo[e] = rope[2 * j + 1];
-    rope_sincos(16.f, kfhi[e], kflo[e], &s16[e], &c16[e]);
+    rope_sincos((float)KSTEP, kfhi[e], kflo[e], &sst[e], &cst[e]);
   }
-  const int k_row = tid >> 4;
-  const int v_kg = lane & 3;
-  const int v_chunk = lane >> 2;
+  const int v_kg = lane & 1;
+  const int v_q = lane >> 1;
 
   // registers of one staged block
   struct Regs {
-    uint4 k[4], v[4];
+    uint4 k[KI];
+    uint2 v[4];
   };
   Regs R0, R1;
 
@@ -253,7 +258,7 @@ __device__ __forceinline__ void append_worker_rope(const AttnArgs& a, int bid) {
     const int kv_len = npg > 0 ? (npg - 1) * P + a.kv_last_page_len[b] : 0;
     const int kv_pos0 = a.kv_pos_offset ? a.kv_pos_offset[b] : 0;
     // elements; the first piece of the lane's pairs (see above)
-    const int koff_lane = k_row * tstride + h * kD + kc_chunk * kKPiece;
+    const int koff_lane = (k_row & 15) * tstride + h * kD + kc_chunk * kKPiece;
 
     // ---- staging: global -> registers. Any kb is in bounds: groups past
     // the segment end re-read its last valid rows (masked, or never read).
@@ -268,19 +273,19 @@ __device__ __forceinline__ void append_worker_rope(const AttnArgs& a, int bid) {
     };
     auto gload = [&](int kb, Regs& R) __attribute__((always_inline)) {
       if constexpr (FASTPAGE) {
-        // one page id per 16-key group, on the scalar unit
-        // (the page ids are read first, so their scalar loads overlap)
+        // one page id per 16-key group (uniform over the wave), on the scalar
+        // unit; the page ids are read first, so their scalar loads overlap
         const int last16 = (kv_end - 1) & ~15;
-        int kk[4], pid[4];
+        int kk[KI], pid[KI];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          kk[i] = min(kb + 16 * i, last16);
+        for (int i = 0; i < KI; ++i) {
+          kk[i] = min(kb + k_grp + KSTEP * i, last16);
           pid[i] = kv_indices[ip0 + (kk[i] >> shift)];
         }
-        const int kkv = min(kb + 16 * wave, last16);  // wave-uniform
+        const int kkv = min(kb + 16 * (wave >> 1), last16);
         const int pidv = kv_indices[ip0 + (kkv >> shift)];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < KI; ++i) {
           const int64_t base = (int64_t)pid[i] * a.page_stride + (int64_t)(kk[i] & (P - 1)) * tstride;
           R.k[i] = kload(kp + base + koff_lane);
         }
@@ -291,8 +296,8 @@ __device__ __forceinline__ void append_worker_rope(const AttnArgs& a, int bid) {
         const int rmax = kv_end - 1 - kkv;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          R.v[i] = *reinterpret_cast<const uint4*>(vp + vb + min(4 * v_kg + i, rmax) * tstride +
-                                                   h * kD + v_chunk * 8);
+          R.v[i] = *reinterpret_cast<const uint2*>(
+              vp + vb + min(8 * (wave & 1) + 4 * v_kg + i, rmax) * tstride + h * kD + 4 * v_q);
       } else {
         auto row_of = [&](int key) -> int64_t {
           int page, off;
@@ -306,24 +311,22 @@ __device__ __forceinline__ void append_worker_rope(const AttnArgs& a, int bid) {
           return (int64_t)a.kv_indices[ip0 + page] * a.page_stride + (int64_t)off * tstride;
         };
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = min(kb + k_row + 16 * i, kv_end - 1);
+        for (int i = 0; i < KI; ++i) {
+          const int key = min(kb + k_row + KSTEP * i, kv_end - 1);
           R.k[i] = kload(kp + row_of(key) + h * kD + kc_chunk * kKPiece);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int key = min(kb + 16 * wave + 4 * v_kg + i, kv_end - 1);
-          R.v[i] = *reinterpret_cast<const uint4*>(vp + row_of(key) + h * kD + v_chunk * 8);
+          const int key = min(kb + 8 * wave + 4 * v_kg + i, kv_end - 1);
+          R.v[i] = *reinterpret_cast<const uint2*>(vp + row_of(key) + h * kD + 4 * v_q);
         }
       }
     };
-    // ---- staging: registers -> LDS, in 4 parts (part i: K row k_row + 16 i,
-    // rotated and split, and V^T dims v_chunk * 8 + 2 i, + 1 of the thread's
-    // 4 keys), each cut into small pieces that the score products are
-    // interleaved with: st_begin sets up the angles of K row k_row, st_step
-    // moves them on by 16 positions, st_rot rotates one pair, st_split splits
-    // one word of the rotated row into hi and lo parts, st_store_k / st_store_v
-    // store the part
+    // ---- staging: registers -> LDS, cut into small pieces that the score
+    // products are interleaved with: st_begin sets up the angles of K row
+    // k_row, st_step moves them on by 32 positions, st_rot rotates one pair,
+    // st_split splits one word of the rotated row into hi and lo parts,
+    // st_store_k stores a K row, st_store_v two head dims of the V^T rows
     float cs[4], sn[4];
     float kr[8];
     uint32_t hw[4], lw[4];
@@ -335,14 +338,14 @@ __device__ __forceinline__ void append_worker_rope(const AttnArgs& a, int bid) {
     auto st_step = [&]() __attribute__((always_inline)) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float cn = __builtin_fmaf(-sn[e], s16[e], cs[e] * c16[e]);
-        sn[e] = __builtin_fmaf(cs[e], s16[e], sn[e] * c16[e]);
+        const float cn = __builtin_fmaf(-sn[e], sst[e], cs[e] * cst[e]);
+        sn[e] = __builtin_fmaf(cs[e], sst[e], sn[e] * cst[e]);
         cs[e] = cn;
       }
     };
-    // pair e of K row part i: rotate-half holds elements 4c + e (words 0-1)
-    // and 64 + 4c + e (words 2-3), giving kr[e] and kr[4 + e]; interleaved
-    // holds the pair in word e, giving kr[2e] and kr[2e + 1]
+    // pair e of K row i: rotate-half holds elements 4c + e (words 0-1) and
+    // 64 + 4c + e (words 2-3), giving kr[e] and kr[4 + e]; interleaved holds
+    // the pair in word e, giving kr[2e] and kr[2e + 1]
     auto st_rot = [&](const Regs& R, int i, int e) __attribute__((always_inline)) {
       const uint4& u = R.k[i];
       if constexpr (RIL) {
@@ -367,172 +370,150 @@ __device__ __forceinline__ void append_worker_rope(const AttnArgs& a, int bid) {
       uint16_t* sKlo = sK + kKElems;
       if constexpr (RIL) {
         // 8 consecutive elements, stored in place as one 16-byte piece
-        const int at = (k_row + 16 * i) * kKStride + kc_chunk * 8;
+        const int at = (k_row + KSTEP * i) * kKStride + kc_chunk * 8;
         *reinterpret_cast<uint4*>(&sK[at]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
         *reinterpret_cast<uint4*>(&sKlo[at]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
       } else {
-        const int at = (k_row + 16 * i) * kKStride + kc_chunk * 4;
+        const int at = (k_row + KSTEP * i) * kKStride + kc_chunk * 4;
         *reinterpret_cast<uint2*>(&sK[at]) = make_uint2(hw[0], hw[1]);
         *reinterpret_cast<uint2*>(&sK[at + 64]) = make_uint2(hw[2], hw[3]);
         *reinterpret_cast<uint2*>(&sKlo[at]) = make_uint2(lw[0], lw[1]);
         *reinterpret_cast<uint2*>(&sKlo[at + 64]) = make_uint2(lw[2], lw[3]);
       }
     };
-    auto st_store_v = [&](const Regs& R, int i, auto stage) __attribute__((always_inline)) {
-      // V^T: element d of the 4 keys 16 wave + 4 v_kg + 0..3 as one 8-byte piece
-      uint16_t* V = sV_of(stage) + 16 * wave + 4 * v_kg;
-      const uint32_t w0 = word(R.v[0], i), w1 = word(R.v[1], i);
-      const uint32_t w2 = word(R.v[2], i), w3 = word(R.v[3], i);
-      const int d = v_chunk * 8 + 2 * i;
+    // V^T: head dims 4 v_q + 2 j, + 1 of the 4 keys 8 wave + 4 v_kg + 0..3 as
+    // one 8-byte piece each
+    auto st_store_v = [&](const Regs& R, int j, auto stage) __attribute__((always_inline)) {
+      uint16_t* V = sV_of(stage) + 8 * wave + 4 * v_kg;
+      const uint32_t w0 = j ? R.v[0].y : R.v[0].x, w1 = j ? R.v[1].y : R.v[1].x;
+      const uint32_t w2 = j ? R.v[2].y : R.v[2].x, w3 = j ? R.v[3].y : R.v[3].x;
+      const int d = 4 * v_q + 2 * j;
       *reinterpret_cast<uint2*>(&V[d * kVStride]) = make_uint2(pair_lo(w0, w1), pair_lo(w2, w3));
       *reinterpret_cast<uint2*>(&V[(d + 1) * kVStride]) =
           make_uint2(pair_hi(w0, w1), pair_hi(w2, w3));
     };
-    // piece p (0..11) of staging part i
-    auto st_piece = [&](const Regs& R, int i, int p, auto stage) __attribute__((always_inline)) {
-      if (p == 0) {
-        if (i > 0) st_step();
-      } else if (p <= 4) {
-        st_rot(R, i, p - 1);
-      } else if (p <= 8) {
-        st_split(p - 5);
-      } else if (p == 9) {
-        st_store_k(i, stage);
-      } else if (p == 10) {
-        st_store_v(R, i, stage);
+    // staging piece p of a block (p = 0 is st_begin, placed by the caller):
+    // K row i takes pieces 1 + 10 i .. 10 + 10 i (the step to it, 4 pair
+    // rotations, 4 splits, the store), then the two V^T pieces
+    constexpr int kPieces = 1 + 10 * KI + 2;
+    auto st_piece = [&](const Regs& R, int p, auto stage) __attribute__((always_inline)) {
+      if (p >= 1 && p <= 10 * KI) {
+        const int i = (p - 1) / 10, r = (p - 1) % 10;
+        if (r == 0) {
+          if (i > 0) st_step();
+        } else if (r <= 4) {
+          st_rot(R, i, r - 1);
+        } else if (r <= 8) {
+          st_split(r - 5);
+        } else {
+          st_store_k(i, stage);
+        }
+      } else if (p > 10 * KI && p < kPieces) {
+        st_store_v(R, p - 1 - 10 * KI, stage);
       }
     };
-    auto st_part = [&](const Regs& R, int i, auto stage) __attribute__((always_inline)) {
+    auto st_all = [&](const Regs& R, auto stage) __attribute__((always_inline)) {
 #pragma unroll
-      for (int p = 0; p < 11; ++p) st_piece(R, i, p, stage);
+      for (int p = 1; p < kPieces; ++p) st_piece(R, p, stage);
     };
 
     const int nblk = kv_end > kv_begin ? (kv_end - kv_begin + kTk - 1) / kTk : 0;
 
-    // ---- Q fragments (B operand of S^T = K Q^T) for this wave's 32 rows,
+    // ---- Q fragment (B operand of S^T = K Q^T) for this wave's 16 rows,
     // rotated and split into hi (qf) and lo (qfl) parts. The q loads go out
     // first and the first two blocks' K/V loads next, so that the q rotation
     // waits for q alone and the blocks' latency overlaps it.
-    uint4 qf[2][4], qfl[2][4];
-    int lim[2];
-    int tloc_r[2];
-    float qpos[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int r = wave * 32 + nb * 16 + l16;
-      const int tloc = qt * TQ + r / G;
-      const int tl = min(tloc, qo_len - 1);
-      tloc_r[nb] = tloc;
-      lim[nb] = kv_len - qo_len + tl;
+    uint4 qf[4], qfl[4];
+    const int r_row = wave * 16 + l16;
+    const int tloc_r = qt * TQ + r_row / G;
+    int lim;
+    float qpos;
+    {
+      const int tl = min(tloc_r, qo_len - 1);
+      lim = kv_len - qo_len + tl;
       const uint16_t* qptr = static_cast<const uint16_t*>(a.q) +
-                             ((int64_t)(q0 + tl) * a.num_qo_heads + h * G + (r % G)) * kD + g16 * 8;
+                             ((int64_t)(q0 + tl) * a.num_qo_heads + h * G + (r_row % G)) * kD +
+                             g16 * 8;
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc) qf[nb][kc] = *reinterpret_cast<const uint4*>(qptr + kc * 32);
-      qpos[nb] = a.q_pos ? (float)a.q_pos[q0 + tl] : (float)lim[nb];
+      for (int kc = 0; kc < 4; ++kc) qf[kc] = *reinterpret_cast<const uint4*>(qptr + kc * 32);
+      qpos = a.q_pos ? (float)a.q_pos[q0 + tl] : (float)lim;
     }
     if (nblk > 0) {
       gload(kv_begin, R0);
       gload(kv_begin + kTk, R1);
     }
+    if constexpr (RIL) {
+      // chunk kc holds elements g16 * 8 + 32 kc .. + 7: pairs 4 g16 + 16 kc ..
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      if constexpr (RIL) {
-        // chunk kc holds elements g16 * 8 + 32 kc .. + 7: pairs 4 g16 + 16 kc ..
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc)
-          rope_adjacent8<T>(qf[nb][kc], qfl[nb][kc], qpos[nb], 4 * g16 + 16 * kc, rope);
-      } else {
-        rope_pair<T>(qf[nb][0], qf[nb][2], qfl[nb][0], qfl[nb][2], qpos[nb], g16 * 8, rope);
-        rope_pair<T>(qf[nb][1], qf[nb][3], qfl[nb][1], qfl[nb][3], qpos[nb], 32 + g16 * 8, rope);
-      }
+      for (int kc = 0; kc < 4; ++kc)
+        rope_adjacent8<T>(qf[kc], qfl[kc], qpos, 4 * g16 + 16 * kc, rope);
+    } else {
+      rope_pair<T>(qf[0], qf[2], qfl[0], qfl[2], qpos, g16 * 8, rope);
+      rope_pair<T>(qf[1], qf[3], qfl[1], qfl[3], qpos, 32 + g16 * 8, rope);
     }
     // first row of the tile sees the fewest keys
     const int tile_min_lim = kv_len - qo_len + qt * TQ;
-    // the q operands live in AGPRs, which the score products read in place:
-    // the VGPRs are left to the accumulators and the staging
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        asm volatile("" : "+a"(qf[nb][kc].x), "+a"(qf[nb][kc].y), "+a"(qf[nb][kc].z),
-                     "+a"(qf[nb][kc].w));
-        asm volatile("" : "+a"(qfl[nb][kc].x), "+a"(qfl[nb][kc].y), "+a"(qfl[nb][kc].z),
-                     "+a"(qfl[nb][kc].w));
-      }
 
-    float m[2] = {kNegInf, kNegInf};
-    float lsum[2] = {0.f, 0.f};
-    f32x4_t O[8][2];
+    float m = kNegInf;
+    float lsum = 0.f;
+    f32x4_t O[8];
 #pragma unroll
-    for (int md = 0; md < 8; ++md)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) O[md][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int md = 0; md < 8; ++md) O[md] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     if (nblk > 0) {
       st_begin(kv_begin);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) st_part(R0, i, S0{});
+      st_all(R0, S0{});
     }
     __syncthreads();
 
     // one block on stage `st`: R holds block j + 1 (rotated and stored into
     // the other stage beside the score products), Rn takes block j + 2
     auto block = [&](auto st, int kb, Regs& R, Regs& Rn) __attribute__((always_inline)) {
-      constexpr int ST = decltype(st)::value;
-      using Other = std::integral_constant<int, 1 - ST>;
+      using Other = std::integral_constant<int, 1 - decltype(st)::value>;
       // always issued (past the end it re-reads the last rows), so the wait
       // for R below is the same count on every block
       gload(kb + 2 * kTk, Rn);
       const uint16_t* sK = sK_of(st);
       const uint16_t* sKlo = sK + kKElems;
       const uint16_t* sVt = sV_of(st);
-      // S^T = K Q^T: S[mb][nb] holds keys kb + 16 mb + 4 g16 + j, row nb*16 + l16.
-      // Product piece kc of 16-key group mb is 6 products (hi/lo parts); its
-      // operands are read one piece ahead. Each fenced slot issues 2 products
-      // and one piece of the next block's staging part mb (the angles first).
-      f32x4_t S[4][2];
+      // S^T = K Q^T: S[mb] holds keys kb + 16 mb + 4 g16 + j of row l16. Piece
+      // (mb, kc) is 3 products (hi/lo parts); its operands are read one piece
+      // ahead. Each fenced slot issues 2 products and one staging piece of
+      // the next block (past the last block it fills the idle stage with
+      // values nobody reads).
+      f32x4_t S[4];
       uint4 kh[2], kl[2];
       auto rd = [&](int mb, int kc, int buf) __attribute__((always_inline)) {
         const int at = (mb * 16 + l16) * kKStride + kc * 32 + g16 * 8;
         kh[buf] = *reinterpret_cast<const uint4*>(&sK[at]);
         kl[buf] = *reinterpret_cast<const uint4*>(&sKlo[at]);
       };
-      auto mf = [&](int mb, int kc, int buf, int t) __attribute__((always_inline)) {
-        const uint4& ka = (t < 4) ? kh[buf] : kl[buf];
-        const uint4& qb = (t < 2 || t >= 4) ? qf[t & 1][kc] : qfl[t & 1][kc];
-        S[mb][t & 1] = mfma<T>(ka, qb, S[mb][t & 1]);
-      };
       rd(0, 0, 0);
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        S[mb][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        S[mb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-          const int buf = kc & 1;
-#pragma unroll
-          for (int sl = 0; sl < 3; ++sl) {
-            if (sl == 0) {
-              if (kc < 3) rd(mb, kc + 1, buf ^ 1);
-              else if (mb < 3) rd(mb + 1, 0, buf ^ 1);
-            }
-            mf(mb, kc, buf, 2 * sl);
-            mf(mb, kc, buf, 2 * sl + 1);
-            // the next block's staging (past the last block it fills the idle
-            // stage with values nobody reads)
-            if (mb == 0 && kc == 0 && sl == 0) st_begin(kb + kTk);
-            else st_piece(R, mb, 3 * kc + sl, Other{});
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_barrier(0);
-          }
+      for (int u = 0; u < 48; ++u) {
+        const int pc = u / 3, t = u % 3;  // piece (mb, kc) = (pc / 4, pc % 4)
+        const int mb = pc >> 2, kc = pc & 3, buf = pc & 1;
+        if (t == 0) {
+          if (kc == 0) S[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          if (pc < 15) rd((pc + 1) >> 2, (pc + 1) & 3, buf ^ 1);
+        }
+        const uint4& ka = t < 2 ? kh[buf] : kl[buf];
+        const uint4& qb = t == 1 ? qfl[kc] : qf[kc];
+        S[mb] = mfma<T>(ka, qb, S[mb]);
+        if (u & 1) {
+          const int sl = u >> 1;
+          if (sl == 0) st_begin(kb + kTk);
+          else st_piece(R, sl, Other{});
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
       // ---- online softmax over the block's 64 keys: masks (keys past the
-      // segment end, causal limit per row), one reference check per row with
-      // a lazy rescale, then the exponentials of each 32-key half, P packed as
-      // the PV B operand (K-slots of lane group g16 are keys 4 g16..+3 and
+      // segment end, causal limit), one reference check per row with a lazy
+      // rescale, then the exponentials of each 32-key half, P packed as the
+      // PV B operand (K-slots of lane group g16 are keys 4 g16..+3 and
       // 16 + 4 g16..+3 of the half)
       const bool edge = (kb + kTk > kv_end) || (CAUSAL && kb + kTk - 1 > tile_min_lim);
       if (edge) {
@@ -541,59 +522,46 @@ __device__ __forceinline__ void append_worker_rope(const AttnArgs& a, int bid) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int key = kb + mb * 16 + g16 * 4 + j;
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-              const bool dead = key >= kv_end || (CAUSAL && key > lim[nb]);
-              if (dead) S[mb][nb][j] = kNegInf;
-            }
+            const bool dead = key >= kv_end || (CAUSAL && key > lim);
+            if (dead) S[mb][j] = kNegInf;
           }
       }
       {
-        float mx[2];
+        float x = kNegInf;
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          float x = kNegInf;
-#pragma unroll
-          for (int mb = 0; mb < 4; ++mb)
-            x = __builtin_fmaxf(x, __builtin_fmaxf(__builtin_fmaxf(S[mb][nb][0], S[mb][nb][1]),
-                                                   __builtin_fmaxf(S[mb][nb][2], S[mb][nb][3])));
-          mx[nb] = max_over_groups(x);
-        }
+        for (int mb = 0; mb < 4; ++mb)
+          x = __builtin_fmaxf(x, __builtin_fmaxf(__builtin_fmaxf(S[mb][0], S[mb][1]),
+                                                 __builtin_fmaxf(S[mb][2], S[mb][3])));
+        const float mx = max_over_groups(x);
         // the reference max moves only when a score exceeds it by more than thr
-        if (__builtin_amdgcn_ballot_w64((mx[0] > m[0] + thr) || (mx[1] > m[1] + thr))) {
+        if (__builtin_amdgcn_ballot_w64(mx > m + thr)) {
+          const float mn = __builtin_fmaxf(m, mx);
+          const float alpha = mn == kNegInf ? 1.f : fast_exp2((m - mn) * cl2);
+          m = mn;
+          lsum *= alpha;
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
-            const float mn = __builtin_fmaxf(m[nb], mx[nb]);
-            const float alpha = mn == kNegInf ? 1.f : fast_exp2((m[nb] - mn) * cl2);
-            m[nb] = mn;
-            lsum[nb] *= alpha;
-#pragma unroll
-            for (int md = 0; md < 8; ++md) O[md][nb] *= alpha;
-          }
+          for (int md = 0; md < 8; ++md) O[md] *= alpha;
         }
       }
-      const float mc[2] = {(m[0] == kNegInf ? 0.f : m[0]) * cl2, (m[1] == kNegInf ? 0.f : m[1]) * cl2};
-      uint4 pB[2][2];  // [half][nb]
-      float p[2][2][4];  // [nb][16-key group of the half][key]
-      // piece k (0..3) of half hh's exponentials: row block nb = k / 2,
-      // 16-key group k % 2; the row sum and the packing follow with the
-      // group's second piece. The row sum is taken in fp32 of the unrounded
-      // p: lse must not carry P's 16-bit rounding.
-      auto exps = [&](int hh, int k) __attribute__((always_inline)) {
-        const int nb = k >> 1, i = k & 1;
+      const float mc = (m == kNegInf ? 0.f : m) * cl2;
+      uint4 pB[2];
+      float p[2][4];  // [16-key group of the half][key]
+      // piece i (0..1) of half hh's exponentials: 16-key group i; the row sum
+      // and the packing follow with the second. The row sum is taken in fp32
+      // of the unrounded p: lse must not carry P's 16-bit rounding.
+      auto exps = [&](int hh, int i) __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          p[nb][i][j] = fast_exp2(__builtin_fmaf(S[2 * hh + i][nb][j], cl2, -mc[nb]));
+        for (int j = 0; j < 4; ++j) p[i][j] = fast_exp2(__builtin_fmaf(S[2 * hh + i][j], cl2, -mc));
         if (i == 1) {
-          lsum[nb] += ((p[nb][0][0] + p[nb][0][1]) + (p[nb][0][2] + p[nb][0][3])) +
-                      ((p[nb][1][0] + p[nb][1][1]) + (p[nb][1][2] + p[nb][1][3]));
-          pB[hh][nb] = make_uint4(pack2<T>(p[nb][0][0], p[nb][0][1]), pack2<T>(p[nb][0][2], p[nb][0][3]),
-                                  pack2<T>(p[nb][1][0], p[nb][1][1]), pack2<T>(p[nb][1][2], p[nb][1][3]));
+          lsum += ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) +
+                  ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
+          pB[hh] = make_uint4(pack2<T>(p[0][0], p[0][1]), pack2<T>(p[0][2], p[0][3]),
+                              pack2<T>(p[1][0], p[1][1]), pack2<T>(p[1][2], p[1][3]));
         }
       };
       // O^T += V^T P^T over half hh, 16 dims (md) at a time; the V^T operand
-      // of each md is read one slot ahead, and each slot carries a piece of
-      // the next half's exponentials
+      // of each md is read one slot ahead, and the first half's slots carry
+      // the second half's exponentials
       uint4 va[2];
       auto rdv = [&](int hh, int md, int buf) __attribute__((always_inline)) {
         const uint16_t* vrow = &sVt[(md * 16 + l16) * kVStride + hh * 32 + g16 * 4];
@@ -602,8 +570,8 @@ __device__ __forceinline__ void append_worker_rope(const AttnArgs& a, int bid) {
         va[buf] = make_uint4(v0.x, v0.y, v1.x, v1.y);
       };
       rdv(0, 0, 0);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) exps(0, k);
+      exps(0, 0);
+      exps(0, 1);
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
@@ -611,9 +579,8 @@ __device__ __forceinline__ void append_worker_rope(const AttnArgs& a, int bid) {
           const int buf = md & 1;
           if (md < 7) rdv(hh, md + 1, buf ^ 1);
           else if (hh == 0) rdv(1, 0, buf ^ 1);
-          O[md][0] = mfma<T>(va[buf], pB[hh][0], O[md][0]);
-          O[md][1] = mfma<T>(va[buf], pB[hh][1], O[md][1]);
-          if (hh == 0 && md < 4) exps(1, md);
+          O[md] = mfma<T>(va[buf], pB[hh], O[md]);
+          if (hh == 0 && md < 2) exps(1, md);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -626,23 +593,21 @@ __device__ __forceinline__ void append_worker_rope(const AttnArgs& a, int bid) {
     }
 
     // ---- finalize rows: o = O / l, lse = m * scale + ln l
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      float L = lsum[nb];
+    {
+      float L = lsum;
       L += __shfl_xor(L, 16);
       L += __shfl_xor(L, 32);
-      const int r = wave * 32 + nb * 16 + l16;
-      const bool valid = tloc_r[nb] < qo_len;
+      const bool valid = tloc_r < qo_len;
       const bool empty = !(L > 0.f);
       const float inv = empty ? 0.f : 1.f / L;
-      const float lse = empty ? kNegInf : m[nb] * a.sm_scale + fast_log2(L) * kLn2;
+      const float lse = empty ? kNegInf : m * a.sm_scale + fast_log2(L) * kLn2;
       if (valid) {
         if (slot < 0) {
-          const int64_t orow = (int64_t)(q0 + tloc_r[nb]) * a.num_qo_heads + h * G + (r % G);
+          const int64_t orow = (int64_t)(q0 + tloc_r) * a.num_qo_heads + h * G + (r_row % G);
 #pragma unroll
           for (int md = 0; md < 8; ++md) {
             const int64_t off = orow * kD + md * 16 + g16 * 4;
-            const f32x4_t v = O[md][nb] * inv;
+            const f32x4_t v = O[md] * inv;
             if (a.out_dtype == ABP_F32) {
               *reinterpret_cast<float4*>(static_cast<float*>(a.o) + off) =
                   make_float4(v[0], v[1], v[2], v[3]);
@@ -656,10 +621,10 @@ __device__ __forceinline__ void append_worker_rope(const AttnArgs& a, int bid) {
           }
           if (a.lse && g16 == 0) a.lse[orow] = lse;
         } else {
-          const int64_t prow = (int64_t)slot * kRows + r;
+          const int64_t prow = (int64_t)slot * kRows + r_row;
 #pragma unroll
           for (int md = 0; md < 8; ++md) {
-            const f32x4_t v = O[md][nb] * inv;
+            const f32x4_t v = O[md] * inv;
             *reinterpret_cast<float4*>(a.o_part + prow * kD + md * 16 + g16 * 4) =
                 make_float4(v[0], v[1], v[2], v[3]);
           }
@@ -668,7 +633,7 @@ __device__ __forceinline__ void append_worker_rope(const AttnArgs& a, int bid) {
       }
     }
     if (slot >= 0 && plan[H_MERGE_KERNEL] == 0) {
-      merge_if_last<kRows, 64 * append_waves<true>()>(a, tile, &s_last, [&](int r, int64_t* orow) {
+      merge_if_last<kRows, NT>(a, tile, &s_last, [&](int r, int64_t* orow) {
         const int tloc = qt * TQ + r / G;
         if (tloc >= qo_len) return false;
         *orow = (int64_t)(q0 + tloc) * a.num_qo_heads + h * G + (r % G);

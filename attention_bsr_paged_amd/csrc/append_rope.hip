@@ -4,14 +4,13 @@
 // fusion of the paper summary, "图谱动态｜学苑周刊 NO.266", section
 // 可定制的注意力模板).
 //
-// The worker (append_worker_rope in append_impl.h) runs 4 waves over 128-row
-// tiles; its rotated operands are carried as 16-bit hi and lo parts. This
-// translation unit is built with the matrix products in VGPR form
-// (-mllvm -amdgpu-mfma-vgpr-form): the O and S accumulators then stay in
-// VGPRs, where the softmax and the rare rescale use them directly, and the
-// q hi/lo operands sit in AGPRs, which the products read in place. In the
-// default form the compiler kept O in AGPRs and copied all 64 accumulators to
-// VGPRs on every block for the rescale branch.
+// The worker (append_worker_rope in append_impl.h) runs 8 waves of 16 rows
+// over 128-row tiles; its rotated operands are carried as 16-bit hi and lo
+// parts. This translation unit is built with the matrix products in VGPR form
+// (-mllvm -amdgpu-mfma-vgpr-form): the O and S accumulators stay in VGPRs,
+// where the softmax and the rare rescale use them directly. In the default
+// form the compiler kept O in AGPRs and copied the accumulators to VGPRs on
+// every block for the rescale branch.
 #include "append_impl.h"
 
 namespace abp {
