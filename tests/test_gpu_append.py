@@ -197,6 +197,21 @@ def test_rope_decode_dtype_and_group(dtype, G):
     assert_parity(o, l, o_ref, l_ref, dtype, what=f"rope decode {dtype} G{G}")
 
 
+@pytest.mark.parametrize("G,dtype,causal", [(1, "bf16", True), (2, "fp16", False),
+                                            (8, "fp16", True), (16, "bf16", True)])
+def test_rope_append_groups(G, dtype, causal):
+    """RoPE append at every group size the kernel is built for (a tile's 128
+    rows are 128 / G tokens of G heads) in both 16-bit types; the requests
+    span several tiles, a ragged last tile and a split segment."""
+    say(f"[case] rope append G={G} {dtype} causal={causal}")
+    w = wl.small_append(380 + G, [5, 130 // G + 3, 300], [40, 260, 900], 16, 2 * G, 2,
+                        dtype=dtype, causal=causal)
+    w.rope_theta = 500000.0
+    o_ref, l_ref = ora.append_workload(w)
+    o, l = run_append(w, num_workers=9)
+    assert_parity(o, l, o_ref, l_ref, dtype, what=f"rope append G{G} {dtype}")
+
+
 @pytest.mark.parametrize("P", [3, 256])
 def test_rope_append_page_sizes(P):
     """RoPE append on the per-token page path (P = 3) and with large pages."""
