@@ -94,8 +94,8 @@ constexpr int kDecodeTileKv = 64;   // keys per work block (decode)
 // workgroup reads 1 KB runs of each token row instead of 256-byte pieces;
 // otherwise one head, with its keys split over the 4 waves
 constexpr int decode_tile_heads(int hkv) { return hkv % 4 == 0 ? 4 : 1; }
-// MFMA rows per append tile (= tile_q * group): 8 waves x 32 rows, or 4 waves
-// for the RoPE variant (its hi/lo operands need the registers of 1 wave/SIMD)
+// MFMA rows per append tile (= tile_q * group): 8 waves x 32 rows, or 8 waves
+// x 16 rows for the RoPE variant (its q operands are hi and lo parts)
 constexpr int append_rows(bool rope) { return rope ? 128 : 256; }
 constexpr int kAppendTileKv = 64;   // keys per work block (append)
 // An append tile split into more partials than this is merged by the merge
