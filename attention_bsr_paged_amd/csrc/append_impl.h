@@ -1156,9 +1156,10 @@ __device__ __forceinline__ void append_worker_pipe(const AttnArgs& a, int bid,
 // The work of one append worker (a workgroup of append_waves<ROPE>() waves);
 // bid is the workgroup's index among the launch's append workgroups; lds is
 // the pipelined worker's LDS (the RoPE worker declares its own).
-// NS: K/V stages of the pipelined worker. Two measured faster than three
-// (716-722 against 733-736 us on the ragged causal append, same box): the
-// refills already land within the two steps they are given.
+// NS: K/V stages of the pipelined worker. Two measured faster than three on
+// the ragged causal append, also with the barriers' drain of in-flight refills
+// taken out (734-738 against 693-708 us, same box): what the refills cost is
+// their HBM traffic (it lowers the engine clock), not their latency.
 template <typename T, int G, bool CAUSAL, bool ROPE, bool FASTPAGE, bool RIL, int NS = 2>
 __device__ __forceinline__ void append_worker(const AttnArgs& a, int bid, const PipeLds& lds) {
   if constexpr (ROPE) append_worker_rope<T, G, CAUSAL, FASTPAGE, RIL>(a, bid);
