@@ -188,6 +188,19 @@ def test_fp8_decode_parity(P, G, hkv, dtype):
         assert_parity(o, l, o_ref, l_ref, dtype, what=f"fp8 decode P{P} G{G} hkv{hkv} W{W}")
 
 
+def test_fp8_decode_stage_tails():
+    """fp8 decode segments of 1 to 9 whole 32-token chunks and partial ones, each
+    request one unsplit segment (one worker per tile), so the four-stage loop
+    runs its prologue, steady part and tail at every length."""
+    lens = [32, 64, 96, 128, 160, 192, 224, 256, 288, 31, 33, 225]
+    say(f"[case] fp8 decode stage tails {lens}")
+    w = wl.small_decode_fp8(777, lens, 16, 4 * 4, 4, k_scale=0.5, v_scale=0.25)
+    o_ref, l_ref = ora.decode_workload(w)
+    for W in (abp.ABP_WORKERS_PER_TILE, 0):
+        o, l = run_decode(w, num_workers=W)
+        assert_parity(o, l, o_ref, l_ref, "bf16", what=f"fp8 decode stage tails W{W}")
+
+
 def test_fp8_batch_decode_full():
     """The fp8 batch decode shape (64 requests, kv U{512..4096}, GQA 32/8, page 16,
     q bf16, e4m3 K/V with scales 0.25) in the default launch, every request."""
