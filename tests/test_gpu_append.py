@@ -212,6 +212,31 @@ def test_rope_append_groups(G, dtype, causal):
     assert_parity(o, l, o_ref, l_ref, dtype, what=f"rope append G{G} {dtype}")
 
 
+def test_rope_append_many_way_splits():
+    """RoPE append with tiles split over more than 4 workers, so the plan merge
+    kernel (not the in-kernel merge) combines the 128-row partial states; the
+    plan's mode is checked."""
+    import torch
+    say("[case] rope append, many-way splits")
+    w = wl.small_append(391, [40, 128, 7], [2000, 1500, 900], 16, 8, 2, causal=True)
+    w.rope_theta = 500000.0
+    kv = w.kv
+    dev = upload_kv(kv)
+    q = wl.to_torch(w.q, "bf16", "cuda")
+    params = abp.make_params(8, 2, 128, 16, torch.bfloat16, causal=True, rope_theta=w.rope_theta)
+    app = abp.BatchAppend(params, max_batch=3, max_qo_tokens=256, num_workers=96)
+    plan = app.plan(w.qo_indptr, kv.kv_indptr, kv.kv_last_page_len)
+    torch.cuda.synchronize()
+    arr = abp.decode_plan_arrays(app.host_ws.numpy(), plan)
+    assert int(arr["merge_kernel"][0]) == 1 and int(arr["tile_num_partials"].max()) > 4
+    o, lse = app.run(q, dev["k"], dev["v"], i32(w.qo_indptr), dev["indptr"], dev["indices"],
+                     dev["lpl"])
+    torch.cuda.synchronize()
+    o_ref, l_ref = ora.append_workload(w)
+    assert_parity(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, "bf16",
+                  what="rope append, many-way splits")
+
+
 @pytest.mark.parametrize("P", [3, 256])
 def test_rope_append_page_sizes(P):
     """RoPE append on the per-token page path (P = 3) and with large pages."""
