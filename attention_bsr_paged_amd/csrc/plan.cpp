@@ -16,6 +16,19 @@
 //    several segments writes fp32 partial states to consecutive slots (in key
 //    order) and is merged afterwards.
 //
+// Append plans with load balancing co-schedule query tiles that read the same
+// keys: K workers of one XCD (K = the largest of 8, 4, 2 dividing the workers
+// per XCD) form a group, and the Stream-K split runs over groups and K-tile
+// units instead of workers and tiles. A unit is K consecutive query tiles of
+// one (request, kv head) (the tiles of a (request, kv head) left over after
+// its whole units are queued, and every K queued tiles form a unit, so those
+// mix kv heads); lane i of the unit is worker K g + i of group g. A unit
+// costs the blocks of its longest tile; a group's range [g q, (g + 1) q) of
+// unit blocks (q = ceil(units' blocks / (W / K))) gives lane i the same block
+// range of its own tile, clipped to that tile's blocks. The lanes of a unit
+// start its tiles together and walk the same keys at the same pace, so one
+// read from HBM serves them all through the XCD's L2.
+//
 // The planner writes straight into the caller's host workspace and allocates
 // nothing.
 #include "plan.h"
@@ -32,6 +45,19 @@ namespace {
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 inline int64_t align4(int64_t x) { return (x + 3) & ~int64_t(3); }
+
+constexpr int kCoLanesMax = 8;  // workers per co-scheduled group, at most
+
+// Workers per co-scheduled group for this plan (1: plain Stream-K). The
+// kernels place worker w on XCD w / (W / 8) when W is a multiple of 8, so a
+// group of K consecutive workers shares one L2 when K divides W / 8.
+int co_lanes(const Config& cfg, const Layout& L) {
+  if (cfg.kind != ABP_KIND_APPEND || L.no_split || L.workers % 8 != 0) return 1;
+  const int32_t per_xcd = L.workers / 8;
+  for (int k = kCoLanesMax; k > 1; k >>= 1)
+    if (per_xcd % k == 0) return k;
+  return 1;
+}
 
 constexpr int32_t kMaxKvLen = 1 << 24;
 
@@ -252,6 +278,142 @@ uint64_t fingerprint(const Config& c, const Layout& L) {
   return h;
 }
 
+namespace {
+
+// The co-scheduled split of an append plan over groups of K workers (file
+// header): writes the tile records, the segments grouped by worker with their
+// partial slots, wseg, the per-tile partial counts and the merge list into the
+// zeroed blob. The arrival counters serve as scratch and are zero again on
+// return.
+void co_schedule(const Config& cfg, const Layout& L, int32_t K, int32_t batch,
+                 const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* lpl,
+                 int32_t* blob, int64_t* n_seg, int64_t* n_slot, int64_t* n_merge,
+                 int64_t* max_nseg, int64_t* quota_out) {
+  const int64_t P = cfg.page_size, Tq = L.tile_q, Tk = L.tile_kv;
+  const int32_t W = L.workers;
+  int32_t* wseg = blob + L.off_wseg;
+  int32_t* seg = blob + L.off_seg;
+  int32_t* tile = blob + L.off_tile;
+  int32_t* ntile = blob + L.off_ntile;
+  int32_t* mrg = blob + L.off_merge;
+  int32_t* used = blob + L.off_cnt;
+
+  int64_t T = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t nqt = ceil_div(int64_t(qo_indptr[b + 1]) - qo_indptr[b], Tq);
+    for (int32_t h = 0; h < cfg.hkv; h += L.tile_heads)
+      for (int64_t qt = 0; qt < nqt; ++qt, ++T) {
+        int32_t* tr = tile + 4 * T;
+        tr[0] = b;
+        tr[1] = h;
+        tr[2] = (int32_t)qt;
+        tr[3] = -1;
+      }
+  }
+  auto extent = [&](int64_t t) -> int64_t {
+    const int32_t b = tile[4 * t];
+    const int64_t n = int64_t(kv_indptr[b + 1]) - kv_indptr[b];
+    const int64_t kv_len = n > 0 ? (n - 1) * P + lpl[b] : 0;
+    const int64_t qo_len = int64_t(qo_indptr[b + 1]) - qo_indptr[b];
+    return cfg.causal ? kv_len - qo_len + std::min((int64_t(tile[4 * t + 2]) + 1) * Tq, qo_len)
+                      : kv_len;
+  };
+  auto blocks = [&](int64_t t) { return std::max<int64_t>(1, ceil_div(extent(t), Tk)); };
+
+  // the units in order: fn(tiles of lanes 0 .. K - 1 (-1: idle lane), cost)
+  auto walk = [&](auto&& fn) {
+    int64_t u[kCoLanesMax], q[kCoLanesMax];
+    int nq = 0;
+    auto unit = [&](const int64_t* v) {
+      int64_t c = 0;
+      for (int j = 0; j < K; ++j)
+        if (v[j] >= 0) c = std::max(c, blocks(v[j]));
+      fn(v, c);
+    };
+    for (int64_t t0 = 0, t1; t0 < T; t0 = t1) {
+      t1 = t0 + 1;
+      while (t1 < T && tile[4 * t1] == tile[4 * t0] && tile[4 * t1 + 1] == tile[4 * t0 + 1]) ++t1;
+      const int64_t whole = t0 + (t1 - t0) / K * K;
+      for (int64_t i = t0; i < whole; i += K) {
+        for (int j = 0; j < K; ++j) u[j] = i + j;
+        unit(u);
+      }
+      for (int64_t i = whole; i < t1; ++i) {
+        q[nq++] = i;
+        if (nq == K) {
+          unit(q);
+          nq = 0;
+        }
+      }
+    }
+    if (nq > 0) {
+      for (int j = nq; j < K; ++j) q[j] = -1;
+      unit(q);
+    }
+  };
+  int64_t N2 = 0;
+  walk([&](const int64_t*, int64_t c) { N2 += c; });
+  const int64_t groups = W / K;
+  const int64_t quota = N2 > 0 ? ceil_div(N2, groups) : 1;
+  // every (worker, tile, kv range) in unit order: fn(w, t, kv_begin, kv_end)
+  auto split = [&](auto&& fn) {
+    int64_t g0 = 0;
+    walk([&](const int64_t* v, int64_t c) {
+      const int64_t g1 = g0 + c;
+      for (int64_t grp = g0 / quota; grp * quota < g1; ++grp) {
+        const int64_t lo = std::max(g0, grp * quota) - g0;
+        const int64_t hi = std::min(g1, (grp + 1) * quota) - g0;
+        for (int j = 0; j < K; ++j) {
+          if (v[j] < 0) continue;
+          const int64_t nb = blocks(v[j]);
+          if (lo >= nb) continue;
+          fn(grp * K + j, v[j], lo * Tk, std::min(std::min(hi, nb) * Tk, extent(v[j])));
+        }
+      }
+      g0 = g1;
+    });
+  };
+  split([&](int64_t w, int64_t t, int64_t, int64_t) {
+    wseg[w + 1] += 1;
+    ntile[t] += 1;
+  });
+  for (int32_t w = 0; w < W; ++w) wseg[w + 1] += wseg[w];
+  int64_t slot = 0, m = 0, mx = 0;
+  for (int64_t t = 0; t < T; ++t) {
+    const int64_t n = ntile[t];
+    mx = std::max(mx, n);
+    if (n > 1) {
+      tile[4 * t + 3] = (int32_t)slot;
+      int32_t* mr = mrg + 4 * m++;
+      mr[0] = (int32_t)t;
+      mr[1] = (int32_t)slot;
+      mr[2] = (int32_t)n;
+      mr[3] = 0;
+      slot += n;
+    } else {
+      ntile[t] = 0;
+    }
+  }
+  // fill: wseg[w] walks worker w's records, ending at the next worker's start
+  split([&](int64_t w, int64_t t, int64_t kb, int64_t ke) {
+    int32_t* sr = seg + 4 * int64_t(wseg[w]++);
+    sr[0] = (int32_t)t;
+    sr[1] = (int32_t)kb;
+    sr[2] = (int32_t)ke;
+    sr[3] = ntile[t] > 1 ? tile[4 * t + 3] + used[t]++ : -1;
+  });
+  for (int32_t w = W; w > 0; --w) wseg[w] = wseg[w - 1];
+  wseg[0] = 0;
+  for (int64_t t = 0; t < T; ++t) used[t] = 0;
+  *n_seg = wseg[W];
+  *n_slot = slot;
+  *n_merge = m;
+  *max_nseg = mx;
+  *quota_out = quota;
+}
+
+}  // namespace
+
 int plan_compute(const Config& cfg, const Layout& L, int32_t batch, const int32_t* qo_indptr,
                  const int32_t* kv_indptr, const int32_t* lpl, int32_t* blob, abp_plan* plan,
                  std::string* err) {
@@ -335,7 +497,14 @@ int plan_compute(const Config& cfg, const Layout& L, int32_t batch, const int32_
 
   // tiles, segments, partial slots, merge list (pass 2)
   int64_t t = 0, s = 0, g0 = 0, slot = 0, m = 0, max_nseg = 0;
-  for (int32_t b = 0; b < batch; ++b) {
+  int64_t plan_quota = quota;
+  const int32_t lanes = co_lanes(cfg, L);
+  if (lanes > 1) {
+    co_schedule(cfg, L, lanes, batch, qo_indptr, kv_indptr, lpl, blob, &s, &slot, &m, &max_nseg,
+                &plan_quota);
+    t = T;
+  }
+  for (int32_t b = 0; b < batch && lanes == 1; ++b) {
     const int64_t n = int64_t(kv_indptr[b + 1]) - kv_indptr[b];
     const int64_t kv_len = n > 0 ? (n - 1) * P + lpl[b] : 0;
     const int64_t qo_len = append ? int64_t(qo_indptr[b + 1]) - qo_indptr[b] : 1;
@@ -377,7 +546,8 @@ int plan_compute(const Config& cfg, const Layout& L, int32_t batch, const int32_
       }
     }
   }
-  for (int32_t w = 0; w < W; ++w) wseg[w + 1] += wseg[w];
+  if (lanes == 1)
+    for (int32_t w = 0; w < W; ++w) wseg[w + 1] += wseg[w];
 
   // RoPE frequencies in revolutions per position, as fp32 hi + lo
   float* rope = reinterpret_cast<float*>(blob + L.off_rope);
@@ -421,7 +591,7 @@ int plan_compute(const Config& cfg, const Layout& L, int32_t batch, const int32_
   blob[H_TILE_HEADS] = L.tile_heads;
   blob[H_PAGE_SIZE] = P;
   blob[H_NUM_BLOCKS] = (int32_t)std::min<int64_t>(N, INT32_MAX);
-  blob[H_QUOTA] = (int32_t)std::min<int64_t>(quota, INT32_MAX);
+  blob[H_QUOTA] = (int32_t)std::min<int64_t>(plan_quota, INT32_MAX);
   blob[H_OFF_WSEG] = (int32_t)L.off_wseg;
   blob[H_OFF_SEG] = (int32_t)L.off_seg;
   blob[H_OFF_TILE] = (int32_t)L.off_tile;

@@ -30,8 +30,25 @@ The concrete rule below is the plainest Stream-K reading of that passage:
    first local block * tile_kv, kv_end = min((last local block + 1) * tile_kv,
    extent).
 5. A tile covered by one segment writes its output directly (partial = -1).
-   Otherwise its segments get consecutive partial slots in global order (so in
-   kv order) and the tile enters the merge list, in tile order.
+   Otherwise the tile enters the merge list, and the split tiles, in tile
+   order, take consecutive runs of partial slots; a tile's segments fill its
+   run in the order they are listed (kv order).
+6. Co-scheduling (append plans with load balancing whose worker count W is a
+   multiple of 8; the pages leave the order of the work units open, and this
+   rule serves the kernels' placement of worker w on XCD w / (W / 8)): K = the
+   largest of 8, 4, 2 dividing W / 8 (none: K = 1, steps 3-4 as written). K
+   consecutive workers form a group; units of K tiles replace tiles and groups
+   replace workers in steps 3-4. Walking the (request, kv-head group) runs of
+   tiles in order, each run gives its whole K-tile units (consecutive query
+   tiles) and queues its remaining tiles; every K queued tiles form a unit at
+   that point, and a last incomplete one is padded with idle lanes. A unit
+   costs the largest nblk of its tiles; quota = ceil(sum of unit costs / (W /
+   K)); group g owns [g * quota, (g + 1) * quota) of unit blocks. Where group
+   g meets a unit in its local blocks [lo, hi), lane j's tile t gets the
+   segment [lo * tile_kv, min(min(hi, nblk_t) * tile_kv, extent_t)) on worker
+   K g + j, unless lo >= nblk_t. Segments are listed worker by worker, each
+   worker's in unit order; partial slots follow that listing (so each tile's
+   slots are consecutive and in kv order).
 """
 from __future__ import annotations
 
@@ -72,15 +89,28 @@ def kv_lengths(kv_indptr: Sequence[int], kv_last_page_len: Sequence[int], page_s
     return out
 
 
+def co_lanes(kind: int, num_workers: int, no_split: bool = False) -> int:
+    """Workers per co-scheduled group (rule 6 of the module docstring)."""
+    if kind != KIND_APPEND or no_split or num_workers % 8:
+        return 1
+    for k in (8, 4, 2):
+        if (num_workers // 8) % k == 0:
+            return k
+    return 1
+
+
 def plan_ref(kind: int, batch: int, kv_indptr, kv_last_page_len, page_size: int,
              num_kv_heads: int, num_workers: int, tile_kv: int, qo_indptr=None,
              tile_q: int = 1, causal: bool = False,
-             heads_per_tile: int = 1, no_split: bool = False) -> Dict[str, np.ndarray]:
+             heads_per_tile: int = 1, no_split: bool = False,
+             lanes: Optional[int] = None) -> Dict[str, np.ndarray]:
     """Return the plan as int32 arrays (see the module docstring for the rule).
 
     ``no_split`` is the ablation without load balancing: worker t takes tile t
     whole (one segment, no partial states); ``num_workers`` must be at least
-    the number of tiles, and the workers past them get nothing."""
+    the number of tiles, and the workers past them get nothing. ``lanes`` is
+    the co-scheduling group size K (None: rule 6's choice; 1: plain Stream-K,
+    as block-sparse plans use)."""
     if num_workers < 1 or tile_kv < 1 or tile_q < 1 or num_kv_heads < 1 or batch < 0:
         raise PlanError("bad sizes")
     if heads_per_tile < 1 or num_kv_heads % heads_per_tile:
@@ -123,8 +153,49 @@ def plan_ref(kind: int, batch: int, kv_indptr, kv_last_page_len, page_size: int,
     seg_tile, seg_begin, seg_end, seg_worker = [], [], [], []
     if no_split and T > num_workers:
         raise PlanError("one worker per tile needs num_workers >= the number of tiles")
+    K = co_lanes(kind, num_workers, no_split) if lanes is None else int(lanes)
+    if K > 1:
+        if no_split or num_workers % K:
+            raise PlanError("co-scheduling needs load balancing and K | num_workers")
+        units, queued = [], []
+        t0 = 0
+        while t0 < T:
+            t1 = t0 + 1
+            while t1 < T and (tile_b[t1], tile_h[t1]) == (tile_b[t0], tile_h[t0]):
+                t1 += 1
+            whole = t0 + (t1 - t0) // K * K
+            units += [list(range(i, i + K)) for i in range(t0, whole, K)]
+            for i in range(whole, t1):
+                queued.append(i)
+                if len(queued) == K:
+                    units.append(queued)
+                    queued = []
+            t0 = t1
+        if queued:
+            units.append(queued + [-1] * (K - len(queued)))
+        cost = [max(nblk[t] for t in u if t >= 0) for u in units]
+        quota = _ceil_div(sum(cost), num_workers // K) if units else 1
+        per_worker = [[] for _ in range(num_workers)]
+        g0 = 0
+        for u, c in zip(units, cost):
+            g1 = g0 + c
+            grp = g0 // quota
+            while grp * quota < g1:
+                lo, hi = max(g0, grp * quota) - g0, min(g1, (grp + 1) * quota) - g0
+                for j, t in enumerate(u):
+                    if t >= 0 and lo < nblk[t]:
+                        per_worker[grp * K + j].append(
+                            (t, lo * tile_kv, min(min(hi, nblk[t]) * tile_kv, extent[t])))
+                grp += 1
+            g0 = g1
+        for w, lst in enumerate(per_worker):
+            for t, kb, ke in lst:
+                seg_tile.append(t)
+                seg_begin.append(kb)
+                seg_end.append(ke)
+                seg_worker.append(w)
     g0 = 0
-    for t in range(T):
+    for t in range(T if K == 1 else 0):
         if no_split:
             seg_tile.append(t)
             seg_begin.append(0)
@@ -147,20 +218,23 @@ def plan_ref(kind: int, batch: int, kv_indptr, kv_last_page_len, page_size: int,
     nseg = [0] * T
     for t in seg_tile:
         nseg[t] += 1
-    seg_partial = []
     first_partial = [-1] * T
     num_partials = [0] * T
     slot = 0
+    for t in range(T):
+        if nseg[t] > 1:
+            first_partial[t] = slot
+            num_partials[t] = nseg[t]
+            slot += nseg[t]
+    seg_partial = []
+    used = [0] * T
     for s in range(S):
         t = seg_tile[s]
         if nseg[t] == 1:
             seg_partial.append(-1)
         else:
-            if first_partial[t] < 0:
-                first_partial[t] = slot
-                num_partials[t] = nseg[t]
-            seg_partial.append(slot)
-            slot += 1
+            seg_partial.append(first_partial[t] + used[t])
+            used[t] += 1
     merge_list = [t for t in range(T) if nseg[t] > 1]
 
     worker_seg_indptr = [0] * (num_workers + 1)

@@ -130,7 +130,8 @@ def _compare(kind, p, B, qo_indptr, kv_indptr, lpl, W, G, max_qo=0):
                        heads_per_tile=hpt, no_split=no_split)
     else:
         ref = plan_ref(KIND_APPEND, B, kv_indptr, lpl, p.page_size, p.num_kv_heads, W, 64,
-                       qo_indptr=qo_indptr, tile_q=256 // G, causal=bool(p.causal),
+                       qo_indptr=qo_indptr, tile_q=plan.rows_per_tile // G,
+                       causal=bool(p.causal),
                        no_split=no_split)
     for k, v in ref.items():
         assert np.array_equal(got[k], v), k
@@ -182,6 +183,21 @@ def test_planner_on_named_decode_workloads(lib, name):
         _compare(KIND_DECODE, P(), len(kv_len), None, indptr, lpl, W, 4)
 
 
+@pytest.mark.parametrize("rope", [0, 1])
+def test_planner_on_ragged_append(lib, rope):
+    """The ragged causal append's page table (lengths only) at worker counts
+    that co-schedule 8, 4 and 2 query tiles and at one that does not."""
+    from attention_bsr_paged_amd import workloads as wl
+    rng = np.random.Generator(np.random.PCG64(1004))
+    qo_len = rng.integers(128, 1024, size=16, endpoint=True)
+    kv_len = rng.integers(1024, 8192, size=16, endpoint=True) + qo_len
+    qo_indptr = np.concatenate([[0], np.cumsum(qo_len)]).astype(np.int32)
+    indptr, _, lpl = wl.page_table(kv_len, 16, np.arange(10 ** 6))
+    p = P(causal=True, rope_theta=5e5 if rope else 0.0)
+    for W in (256, 224, 208, 200):
+        _compare(KIND_APPEND, p, 16, qo_indptr, indptr, lpl, W, 4, max_qo=int(qo_indptr[-1]))
+
+
 # ----------------------------------------------------------------------------
 # block-sparse plans, LLaMA 3.1 frequency table, page append argument checks
 # ----------------------------------------------------------------------------
@@ -209,7 +225,7 @@ def test_bsr_plan_matches_reference_over_row_blocks(data):
     got = abp.decode_plan_arrays(ws, plan)
     qo_indptr = np.minimum(np.arange(nrb + 1) * R, M)
     ref = plan_ref(KIND_APPEND, nrb, indptr, np.full(nrb, C), C, hkv, W, 64,
-                   qo_indptr=qo_indptr, tile_q=256 // G, causal=False)
+                   qo_indptr=qo_indptr, tile_q=256 // G, causal=False, lanes=1)
     for k, v in ref.items():
         assert np.array_equal(got[k], v), k
     # the derived query ranges and page counts the run reads from the blob

@@ -88,6 +88,23 @@ def test_append_worker_invariance_and_determinism():
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
+@pytest.mark.parametrize("W", [16, 32, 64, 224])
+@pytest.mark.parametrize("rope", [False, True])
+def test_co_scheduled_plans(W, rope):
+    """Worker counts whose plans run K = 2, 4, 8, 4 consecutive query tiles of
+    one (request, kv head) side by side: ragged query tails, causal requests of
+    different lengths (idle lanes, units mixing kv heads), with and without
+    RoPE."""
+    say(f"[case] co-scheduled append W={W} rope={rope}")
+    w = wl.small_append(330 + W, [300, 7, 129, 64, 33], [2100, 70, 900, 64, 1000], 16, 8, 2,
+                        causal=True)
+    if rope:
+        w.rope_theta = 500000.0
+    o_ref, l_ref = ora.append_workload(w)
+    o, l = run_append(w, num_workers=W)
+    assert_parity(o, l, o_ref, l_ref, "bf16", what=f"co-scheduled W{W} rope{int(rope)}")
+
+
 def test_merge_modes_and_graph_replay_across_them():
     """A tile split into more than 4 partials is merged by the merge kernel, at
     most 4 inside the append kernel. Both give the oracle's result, and a run

@@ -3,7 +3,7 @@ import numpy as np
 import pytest
 from hypothesis import given, settings, strategies as st
 
-from oracle.plan_ref import KIND_APPEND, KIND_DECODE, PlanError, plan_ref
+from oracle.plan_ref import KIND_APPEND, KIND_DECODE, PlanError, co_lanes, plan_ref
 
 
 def test_decode_hand_example():
@@ -79,7 +79,9 @@ def test_causal_needs_qo_not_above_kv():
     plan_ref(KIND_APPEND, 1, [0, 1], [3], 4, 1, 4, 16, qo_indptr=[0, 4], tile_q=2, causal=False)
 
 
-def check_invariants(p, W, Tk, extents):
+def check_invariants(p, W, Tk, extents, contiguous=True):
+    """contiguous: a tile's segments are adjacent in the listing (plain
+    Stream-K); co-scheduled plans list them worker by worker."""
     T = len(extents)
     S = len(p["seg_tile"])
     quota = int(p["quota"][0])
@@ -89,7 +91,9 @@ def check_invariants(p, W, Tk, extents):
     # exact cover of every tile's blocks, in kv order
     for t in range(T):
         segs = np.nonzero(p["seg_tile"] == t)[0]
-        assert len(segs) >= 1 and np.all(np.diff(segs) == 1)
+        assert len(segs) >= 1
+        if contiguous:
+            assert np.all(np.diff(segs) == 1)
         b = p["seg_kv_begin"][segs]
         e = p["seg_kv_end"][segs]
         assert b[0] == 0 and e[-1] == extents[t]
@@ -100,6 +104,9 @@ def check_invariants(p, W, Tk, extents):
             slots = p["seg_partial"][segs]
             assert np.all(np.diff(slots) == 1) and slots[0] == p["tile_first_partial"][t]
             assert p["tile_num_partials"][t] == len(segs)
+    # split tiles take consecutive slot runs in tile order
+    firsts = [int(p["tile_first_partial"][t]) for t in range(T) if p["tile_num_partials"][t] > 1]
+    assert firsts == sorted(firsts)
     # worker loads stay within the quota
     for w in range(W):
         blocks = 0
@@ -118,7 +125,7 @@ def test_invariants_random(data):
     P = data.draw(st.sampled_from([1, 3, 16, 256]))
     Hkv = data.draw(st.integers(1, 4))
     hpt = data.draw(st.sampled_from([d for d in (1, 2, 4) if Hkv % d == 0]))
-    W = data.draw(st.integers(1, 40))
+    W = data.draw(st.integers(1, 40) | st.sampled_from([64, 96, 128]))
     Tk = data.draw(st.sampled_from([1, 16, 64]))
     kv_len = data.draw(st.lists(st.integers(0, 700), min_size=B, max_size=B))
     npg = [-(-n // P) for n in kv_len]
@@ -140,7 +147,74 @@ def test_invariants_random(data):
             for _ in range(Hkv // hpt):
                 for qt in range(-(-m // Tq)):
                     ext.append(n - m + min((qt + 1) * Tq, m) if causal else n)
-    check_invariants(p, W, Tk, ext)
+    check_invariants(p, W, Tk, ext, contiguous=co_lanes(KIND_APPEND if append else KIND_DECODE, W) == 1)
+
+
+def test_co_scheduled_append_hand_example():
+    # The causal append example above on W = 16 workers: 2 per XCD, so units of
+    # K = 2 tiles. Head 0's tiles 0, 1 form a unit and tile 2 is queued; head
+    # 1's tiles 3, 4 form a unit, and its tile 5 completes the queued unit
+    # (2, 5). Units [0, 1], [3, 4], [2, 5] cost 3 blocks each: 9 blocks over 8
+    # groups -> quota 2. Group 0 (workers 0, 1): unit 0 blocks 0-1. Group 1
+    # (workers 2, 3): unit 0 block 2, unit 1 block 0. Group 2: unit 1 blocks
+    # 1-2. Group 3: unit 2 blocks 0-1; group 4: its block 2. Every tile is cut
+    # in two; slots run in tile order (tile t takes 2t, 2t + 1).
+    p = plan_ref(KIND_APPEND, 1, [0, 2], [4], 16, 2, 16, 8, qo_indptr=[0, 5], tile_q=2,
+                 causal=True)
+    assert co_lanes(KIND_APPEND, 16) == 2
+    assert p["quota"].tolist() == [2]
+    assert p["worker_seg_indptr"].tolist() == [0, 1, 2, 4, 6, 7, 8, 9, 10, 11, 12] + [12] * 6
+    assert p["seg_tile"].tolist() == [0, 1, 0, 3, 1, 4, 3, 4, 2, 5, 2, 5]
+    assert p["seg_kv_begin"].tolist() == [0, 0, 16, 0, 16, 0, 8, 8, 0, 0, 16, 16]
+    assert p["seg_kv_end"].tolist() == [16, 16, 17, 8, 19, 8, 17, 19, 16, 16, 20, 20]
+    assert p["seg_partial"].tolist() == [0, 2, 1, 6, 3, 8, 7, 9, 4, 10, 5, 11]
+    assert p["tile_first_partial"].tolist() == [0, 2, 4, 6, 8, 10]
+    assert p["merge_list"].tolist() == [0, 1, 2, 3, 4, 5]
+    # the same plan without co-scheduling is the plain Stream-K split
+    q = plan_ref(KIND_APPEND, 1, [0, 2], [4], 16, 2, 16, 8, qo_indptr=[0, 5], tile_q=2,
+                 causal=True, lanes=1)
+    assert q["quota"].tolist() == [2]
+    assert q["seg_tile"].tolist() == [0, 0, 1, 1, 2, 2, 3, 3, 4, 4, 5, 5]
+
+
+def test_co_lanes_rule():
+    assert [co_lanes(KIND_APPEND, w) for w in (8, 16, 24, 32, 48, 64, 96, 224, 256, 512)] == \
+        [1, 2, 1, 4, 2, 8, 4, 4, 8, 8]
+    assert co_lanes(KIND_APPEND, 20) == 1 and co_lanes(KIND_DECODE, 256) == 1
+    assert co_lanes(KIND_APPEND, 256, no_split=True) == 1
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.data())
+def test_co_scheduled_lanes_share_keys(data):
+    """Non-causal requests whose query tiles come in whole units: the K workers
+    of each group (within one XCD's block of workers) walk the same key ranges,
+    segment by segment, of tiles of one (request, kv head), and the plan
+    covers every tile exactly once."""
+    W = data.draw(st.sampled_from([16, 32, 64, 128, 256]))
+    K = co_lanes(KIND_APPEND, W)
+    assert K > 1 and (W // 8) % K == 0
+    B = data.draw(st.integers(1, 6))
+    Hkv = data.draw(st.integers(1, 3))
+    Tq = data.draw(st.sampled_from([4, 32]))
+    kv_len = data.draw(st.lists(st.integers(1, 900), min_size=B, max_size=B))
+    qo = [K * Tq * data.draw(st.integers(0, 3)) for _ in kv_len]
+    indptr = np.concatenate([[0], np.cumsum([-(-n // 16) for n in kv_len])]).astype(int)
+    lpl = [n - (-(-n // 16) - 1) * 16 for n in kv_len]
+    qo_indptr = np.concatenate([[0], np.cumsum(qo)]).astype(int)
+    p = plan_ref(KIND_APPEND, B, indptr, lpl, 16, Hkv, W, 64, qo_indptr=qo_indptr, tile_q=Tq,
+                 causal=False)
+    ind = p["worker_seg_indptr"]
+    for g in range(W // K):
+        lanes = [range(ind[g * K + j], ind[g * K + j + 1]) for j in range(K)]
+        assert len({len(r) for r in lanes}) == 1
+        for segs in zip(*lanes):
+            t = [int(p["seg_tile"][i]) for i in segs]
+            assert len({(int(p["tile_b"][x]), int(p["tile_h"][x])) for x in t}) == 1
+            assert len({int(p["tile_qt"][x]) for x in t}) == K
+            assert len({(int(p["seg_kv_begin"][i]), int(p["seg_kv_end"][i])) for i in segs}) == 1
+    ext = [n for n, m in zip(kv_len, qo) for _ in range(Hkv) for _ in range(m // Tq)]
+    check_invariants(p, W, 64, ext, contiguous=False)
 
 
 def test_no_split_hand_example():
