@@ -89,6 +89,9 @@ void check_plan(const std::vector<int32_t>& blob, const abp_plan& plan, bool app
     CHECK(next[t] == e, "tile %d covered to %lld, extent %lld", t, (long long)next[t],
           (long long)e);
     CHECK((nseg[t] > 1) == (tile[4 * t + 3] >= 0), "split tiles own partial slots");
+    // the arrival counters start every run at zero (co-scheduled plans use
+    // them as scratch while planning)
+    CHECK(h[h[H_OFF_CNT] + t] == 0, "tile %d: arrival counter %d", t, h[h[H_OFF_CNT] + t]);
   }
 }
 
