@@ -190,7 +190,11 @@ int abp_workspace_size(int kind, const abp_params* params, int32_t max_batch,
  * qo_indptr_h is read for ABP_KIND_APPEND only. num_workers must be > 0 or
  * ABP_WORKERS_PER_TILE.
  * Work is cut into blocks of tile_kv keys and spread over the workers in equal
- * contiguous ranges (Stream-K), paper summary section 动态负载均衡调度. */
+ * contiguous ranges (Stream-K), paper summary section 动态负载均衡调度. Append
+ * plans whose num_workers is a multiple of 8 spread it over groups of K
+ * workers instead (K = the largest of 8, 4, 2 dividing num_workers / 8), each
+ * group running K query tiles of one (request, kv head) side by side on one
+ * XCD; the outputs are the same up to rounding order. */
 int abp_plan_host(int kind, const abp_params* params, int32_t batch, const int32_t* qo_indptr_h,
                   const int32_t* kv_indptr_h, const int32_t* kv_last_page_len_h,
                   int32_t max_batch, int32_t max_qo_tokens, int32_t num_workers, void* host_ws,
