@@ -51,6 +51,12 @@ void check_plan(const std::vector<int32_t>& blob, const abp_plan& plan, bool app
   const int W = h[H_WORKERS], T = h[H_NUM_TILES], S = h[H_NUM_SEGS];
   const int Tk = h[H_TILE_KV], Tq = h[H_TILE_Q];
   CHECK(W == plan.num_workers && T == plan.num_tiles && S == plan.num_segments, "counts");
+  // the plan fits the capacities the workspace was sized for
+  CHECK(T <= h[H_MAX_TILES] && S <= h[H_MAX_SEGS] && h[H_NUM_PARTIALS] <= h[H_MAX_PARTIALS],
+        "capacities: tiles %d/%d segs %d/%d partials %d/%d", T, h[H_MAX_TILES], S, h[H_MAX_SEGS],
+        h[H_NUM_PARTIALS], h[H_MAX_PARTIALS]);
+  CHECK(h[H_NUM_MERGES] <= std::max(0, std::min(h[H_MAX_TILES], W - 1)), "merges %d",
+        h[H_NUM_MERGES]);
   const int32_t* wseg = h + h[H_OFF_WSEG];
   const int32_t* seg = h + h[H_OFF_SEG];
   const int32_t* tile = h + h[H_OFF_TILE];
