@@ -41,8 +41,9 @@
 // token). A tile split over a few workers is merged by the workgroup whose
 // partial state arrives last (per-tile arrival counters). With a power-of-two
 // page size >= 16, a block's page ids are scalar loads. Workers are mapped to
-// workgroup ids XCD-major, so consecutive workers (which usually share the
-// same request and kv head) run on the same XCD and share its L2.
+// workgroup ids XCD-major, so consecutive workers run on the same XCD and
+// share its L2; the planner gives groups of them query tiles of one (request,
+// kv head) to run side by side, and their K/V reads meet in that L2.
 #include "append_impl.h"
 
 namespace abp {
