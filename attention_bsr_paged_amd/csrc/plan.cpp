@@ -22,12 +22,15 @@
 // units instead of workers and tiles. A unit is K consecutive query tiles of
 // one (request, kv head) (the tiles of a (request, kv head) left over after
 // its whole units are queued, and every K queued tiles form a unit, so those
-// mix kv heads); lane i of the unit is worker K g + i of group g. A unit
-// costs the blocks of its longest tile; a group's range [g q, (g + 1) q) of
-// unit blocks (q = ceil(units' blocks / (W / K))) gives lane i the same block
-// range of its own tile, clipped to that tile's blocks. The lanes of a unit
-// start its tiles together and walk the same keys at the same pace, so one
-// read from HBM serves them all through the XCD's L2.
+// mix kv heads); slot i of an even unit, and slot K - 1 - i of an odd one, is
+// lane i, worker K g + i of group g (under a causal mask a unit's tiles grow
+// by one block per slot; mirrored, every lane runs about as many blocks over
+// two units, so the lanes of a group stay close together in time).
+// A unit costs the blocks of its longest tile; a group's range [g q, (g + 1) q)
+// of unit blocks (q = ceil(units' blocks / (W / K))) gives each lane the same
+// block range of its own tile, clipped to that tile's blocks. The lanes of a
+// unit start its tiles together and walk the same keys at the same pace, so
+// one read from HBM serves them all through the XCD's L2.
 //
 // The planner writes straight into the caller's host workspace and allocates
 // nothing.
@@ -355,19 +358,22 @@ void co_schedule(const Config& cfg, const Layout& L, int32_t K, int32_t batch,
   walk([&](const int64_t*, int64_t c) { N2 += c; });
   const int64_t groups = W / K;
   const int64_t quota = N2 > 0 ? ceil_div(N2, groups) : 1;
-  // every (worker, tile, kv range) in unit order: fn(w, t, kv_begin, kv_end)
+  // every (worker, tile, kv range) in unit order: fn(w, t, kv_begin, kv_end);
+  // odd units give their slots to the lanes in reverse
   auto split = [&](auto&& fn) {
-    int64_t g0 = 0;
+    int64_t g0 = 0, ui = 0;
     walk([&](const int64_t* v, int64_t c) {
       const int64_t g1 = g0 + c;
+      const bool odd = (ui++ & 1) != 0;
       for (int64_t grp = g0 / quota; grp * quota < g1; ++grp) {
         const int64_t lo = std::max(g0, grp * quota) - g0;
         const int64_t hi = std::min(g1, (grp + 1) * quota) - g0;
         for (int j = 0; j < K; ++j) {
-          if (v[j] < 0) continue;
-          const int64_t nb = blocks(v[j]);
+          const int64_t t = v[odd ? K - 1 - j : j];
+          if (t < 0) continue;
+          const int64_t nb = blocks(t);
           if (lo >= nb) continue;
-          fn(grp * K + j, v[j], lo * Tk, std::min(std::min(hi, nb) * Tk, extent(v[j])));
+          fn(grp * K + j, t, lo * Tk, std::min(std::min(hi, nb) * Tk, extent(t)));
         }
       }
       g0 = g1;

@@ -43,8 +43,9 @@ The concrete rule below is the plainest Stream-K reading of that passage:
    tiles) and queues its remaining tiles; every K queued tiles form a unit at
    that point, and a last incomplete one is padded with idle lanes. A unit
    costs the largest nblk of its tiles; quota = ceil(sum of unit costs / (W /
-   K)); group g owns [g * quota, (g + 1) * quota) of unit blocks. Where group
-   g meets a unit in its local blocks [lo, hi), lane j's tile t gets the
+   K)); group g owns [g * quota, (g + 1) * quota) of unit blocks. Lane j of
+   unit i is slot j when i is even and slot K - 1 - j when i is odd. Where
+   group g meets unit i in its local blocks [lo, hi), lane j's tile t gets the
    segment [lo * tile_kv, min(min(hi, nblk_t) * tile_kv, extent_t)) on worker
    K g + j, unless lo >= nblk_t. Segments are listed worker by worker, each
    worker's in unit order; partial slots follow that listing (so each tile's
@@ -177,12 +178,13 @@ def plan_ref(kind: int, batch: int, kv_indptr, kv_last_page_len, page_size: int,
         quota = _ceil_div(sum(cost), num_workers // K) if units else 1
         per_worker = [[] for _ in range(num_workers)]
         g0 = 0
-        for u, c in zip(units, cost):
+        for i, (u, c) in enumerate(zip(units, cost)):
             g1 = g0 + c
             grp = g0 // quota
             while grp * quota < g1:
                 lo, hi = max(g0, grp * quota) - g0, min(g1, (grp + 1) * quota) - g0
-                for j, t in enumerate(u):
+                for j in range(K):
+                    t = u[K - 1 - j] if i % 2 else u[j]
                     if t >= 0 and lo < nblk[t]:
                         per_worker[grp * K + j].append(
                             (t, lo * tile_kv, min(min(hi, nblk[t]) * tile_kv, extent[t])))

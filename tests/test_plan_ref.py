@@ -152,22 +152,23 @@ def test_invariants_random(data):
 
 def test_co_scheduled_append_hand_example():
     # The causal append example above on W = 16 workers: 2 per XCD, so units of
-    # K = 2 tiles. Head 0's tiles 0, 1 form a unit and tile 2 is queued; head
-    # 1's tiles 3, 4 form a unit, and its tile 5 completes the queued unit
-    # (2, 5). Units [0, 1], [3, 4], [2, 5] cost 3 blocks each: 9 blocks over 8
-    # groups -> quota 2. Group 0 (workers 0, 1): unit 0 blocks 0-1. Group 1
-    # (workers 2, 3): unit 0 block 2, unit 1 block 0. Group 2: unit 1 blocks
-    # 1-2. Group 3: unit 2 blocks 0-1; group 4: its block 2. Every tile is cut
-    # in two; slots run in tile order (tile t takes 2t, 2t + 1).
+    # K = 2 tiles. Head 0's tiles 0, 1 form unit 0 and tile 2 is queued; head
+    # 1's tiles 3, 4 form unit 1, and its tile 5 completes the queued unit 2
+    # (2, 5). Unit 1 is odd, so its slots go to the lanes in reverse: lane 0
+    # runs tiles 0, 4, 2 and lane 1 tiles 1, 3, 5. Units cost 3 blocks each:
+    # 9 blocks over 8 groups -> quota 2. Group 0 (workers 0, 1): unit 0 blocks
+    # 0-1. Group 1 (workers 2, 3): unit 0 block 2, unit 1 block 0. Group 2:
+    # unit 1 blocks 1-2. Group 3: unit 2 blocks 0-1; group 4: its block 2.
+    # Every tile is cut in two; slots run in tile order (tile t takes 2t, 2t + 1).
     p = plan_ref(KIND_APPEND, 1, [0, 2], [4], 16, 2, 16, 8, qo_indptr=[0, 5], tile_q=2,
                  causal=True)
     assert co_lanes(KIND_APPEND, 16) == 2
     assert p["quota"].tolist() == [2]
     assert p["worker_seg_indptr"].tolist() == [0, 1, 2, 4, 6, 7, 8, 9, 10, 11, 12] + [12] * 6
-    assert p["seg_tile"].tolist() == [0, 1, 0, 3, 1, 4, 3, 4, 2, 5, 2, 5]
+    assert p["seg_tile"].tolist() == [0, 1, 0, 4, 1, 3, 4, 3, 2, 5, 2, 5]
     assert p["seg_kv_begin"].tolist() == [0, 0, 16, 0, 16, 0, 8, 8, 0, 0, 16, 16]
-    assert p["seg_kv_end"].tolist() == [16, 16, 17, 8, 19, 8, 17, 19, 16, 16, 20, 20]
-    assert p["seg_partial"].tolist() == [0, 2, 1, 6, 3, 8, 7, 9, 4, 10, 5, 11]
+    assert p["seg_kv_end"].tolist() == [16, 16, 17, 8, 19, 8, 19, 17, 16, 16, 20, 20]
+    assert p["seg_partial"].tolist() == [0, 2, 1, 8, 3, 6, 9, 7, 4, 10, 5, 11]
     assert p["tile_first_partial"].tolist() == [0, 2, 4, 6, 8, 10]
     assert p["merge_list"].tolist() == [0, 1, 2, 3, 4, 5]
     # the same plan without co-scheduling is the plain Stream-K split
